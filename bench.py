@@ -1,0 +1,303 @@
+#!/usr/bin/env python3
+"""Benchmark: paged grouped-query decode steps at batch 200 on one MI355X.
+
+Workload (synthetic, seeded): the pages' 24-layer model shape (14 query heads, 2 KV heads,
+head_dim 64, fp16), a paged cache of 16-token blocks, 200 requests with context lengths
+uniform on 128..2048, groups of 8 consecutive requests sharing a 512-token prefix
+(copy-on-write), block ids scattered by a seeded shuffle of the free list.
+
+One step = the host block manager reserves one slot per request (copy-on-write pairs
+included), the copy-on-write block copies run, the block table / context lengths / slots
+are uploaded, then for each of the 24 layers: kv_append of the new token's K/V and
+paged_decode_attention over the whole cache.  Contexts grow by one token per step.
+
+Printed: one JSON line with the decode-attention KV throughput (unique bytes), steps/s,
+the roofline of the dominant kernel (the paged decode call: split-K partial + merge),
+and the fp64 CPU oracle timed on a bounded sample of the same workload.
+"""
+import argparse
+import ctypes
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+HQ, HKV, D, BLOCK = 14, 2, 64, 16
+KV_TOKEN_LAYER_BYTES = 2 * HKV * D * 2  # K and V, fp16: 512 B per token per layer
+
+
+def unique_and_logical_tokens(table, ctx):
+    """Distinct cache slots read by one decode call (a block's readers each read a prefix
+    of it, so a block contributes the longest prefix read) and the per-request sum."""
+    import numpy as np
+    blocks, counts = [], []
+    for i, c in enumerate(ctx):
+        nb = (c + BLOCK - 1) // BLOCK
+        cnt = np.full(nb, BLOCK, dtype=np.int64)
+        cnt[-1] = c - BLOCK * (nb - 1)
+        blocks.append(table[i, :nb])
+        counts.append(cnt)
+    blocks = np.concatenate(blocks)
+    counts = np.concatenate(counts)
+    order = np.lexsort((counts, blocks))
+    b_sorted, c_sorted = blocks[order], counts[order]
+    last = np.r_[b_sorted[1:] != b_sorted[:-1], True]
+    unique = int(c_sorted[last].sum())
+    return unique, int(sum(ctx))
+
+
+def decode_call_bytes(table, ctx, B):
+    """Algorithmic bytes of one paged_decode_attention call (one layer): unique K/V bytes,
+    q in, out, the block-table entries and the context lengths."""
+    uniq, logical = unique_and_logical_tokens(table, ctx)
+    blocks_read = sum((c + BLOCK - 1) // BLOCK for c in ctx)
+    qo = 2 * B * HQ * D * 2
+    return uniq * KV_TOKEN_LAYER_BYTES + qo + 4 * blocks_read + 4 * B, uniq, logical
+
+
+def build_state(kvp, torch, W, B, layers, total_steps, seed):
+    pb = W.paged_batch(B)
+    dev = "cuda"
+    ngroups = len(set(pb.group))
+    need = sum(math.ceil((c + total_steps + 1) / BLOCK) for c in pb.ctx_before)
+    need += ngroups * math.ceil(pb.prefix / BLOCK) + B + 64
+    num_blocks = need
+    max_blocks = math.ceil((max(pb.ctx_before) + total_steps + 1) / BLOCK)
+    pool = kvp.BlockPool(num_blocks)
+    pool.set_free_order(W.free_list_permutation(num_blocks, seed + 1).tolist())
+    cache = kvp.PagedKVCache(layers, num_blocks, HQ, HKV, torch.float16, dev)
+    for l in range(layers):  # cache contents: seeded N(0,1) in every slot
+        cache.k_pool[l].copy_(W.randn_device(cache.k_pool[l].shape, seed + 10 + 2 * l, torch.float16, dev))
+        cache.v_pool[l].copy_(W.randn_device(cache.v_pool[l].shape, seed + 11 + 2 * l, torch.float16, dev))
+    seqs = [None] * B
+    for gi in sorted(set(pb.group)):
+        pre = pool.alloc(pb.prefix)
+        for i in [i for i in range(B) if pb.group[i] == gi]:
+            s = pool.fork(pre)
+            L = pb.ctx_before[i]
+            if L < pb.prefix:
+                pool.truncate(s, L)
+            elif L > pb.prefix:
+                pool.reserve(s, L - pb.prefix)
+            seqs[i] = s
+        pool.free(pre)
+    return pb, pool, cache, seqs, max_blocks
+
+
+def cpu_baseline(W, B_sample_layers=2, seed=42):
+    """The fp64 oracle, as it is, on a bounded sample of the same workload: all 200
+    requests of `B_sample_layers` layers, one thread per request in flight."""
+    import concurrent.futures as cf
+
+    import numpy as np
+
+    import oracle
+    pb = W.paged_batch(200)
+    lmax = max(pb.ctx_before) + 1
+    threads = min(16, len(os.sched_getaffinity(0)))
+    ctx = np.array([c + 1 for c in pb.ctx_before], dtype=np.int32)
+    total_bytes = 0
+    elapsed = 0.0
+    for layer in range(B_sample_layers):
+        K, V = W.logical_kv(pb, HKV, lmax, seed, layer=layer)
+        q = W.decode_q(pb.batch, HQ, seed, layer=layer)
+        K64, V64, q64 = K.double().numpy(), V.double().numpy(), q.double().numpy()
+
+        def one(i):
+            n = int(ctx[i])
+            return oracle.decode_gqa(q64[i:i + 1], np.ascontiguousarray(K64[i:i + 1, :, :n]),
+                                     np.ascontiguousarray(V64[i:i + 1, :, :n]), ctx[i:i + 1])
+
+        t0 = time.perf_counter()
+        with cf.ThreadPoolExecutor(threads) as ex:
+            list(ex.map(one, range(pb.batch)))
+        elapsed += time.perf_counter() - t0
+        total_bytes += int(ctx.sum()) * KV_TOKEN_LAYER_BYTES
+    return {"value": round(total_bytes / elapsed / 1e9, 4), "unit": "GB/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{B_sample_layers} of 24 layers x all 200 requests of the batch-200 step "
+                      f"(logical KV bytes / wall time, fp64 scalar C, {threads} threads)"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--batch", type=int, default=200)
+    ap.add_argument("--layers", type=int, default=24)
+    ap.add_argument("--kernel-reps", type=int, default=4, help="rounds of per-layer decode timing")
+    ap.add_argument("--no-graph", action="store_true", help="launch the 24 layers eagerly")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--seed", type=int, default=42)
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}). "
+              "Requests would be sharded across GPUs by whole sharing groups; see DESIGN.md.", flush=True)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import kv_cache_decode_paged_amd as kvp
+    import workloads as W
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    dev = "cuda"
+    B, L = args.batch, args.layers
+    total_steps = args.warmup + args.steps + 1
+    t_setup = time.perf_counter()
+    pb, pool, cache, seqs, max_blocks = build_state(kvp, torch, W, B, L, total_steps, args.seed)
+    print(f"[bench] setup: B={B} layers={L} blocks={cache.num_blocks} max_blocks={max_blocks} "
+          f"({time.perf_counter() - t_setup:.1f}s)", file=sys.stderr, flush=True)
+
+    # static per-layer inputs of the step
+    q = W.randn_device((L, B, HQ, D), args.seed + 500, torch.float16, dev)
+    knew = W.randn_device((L, B, HKV, D), args.seed + 501, torch.float16, dev)
+    vnew = W.randn_device((L, B, HKV, D), args.seed + 502, torch.float16, dev)
+    out = torch.empty((L, B, HQ, D), dtype=torch.float16, device=dev)
+    ws = kvp.make_workspace(HQ, HKV, torch.float16, B, max_blocks * BLOCK, dev)
+    table_d = torch.empty((B, max_blocks), dtype=torch.int32, device=dev)
+    ctx_d = torch.empty((B,), dtype=torch.int32, device=dev)
+    slots_d = torch.empty((B,), dtype=torch.int64, device=dev)
+    pairs_d = torch.empty((B, 2), dtype=torch.int32, device=dev)
+    ids = torch.tensor(seqs, dtype=torch.int32)
+    hb = [dict(table=torch.empty((B, max_blocks), dtype=torch.int32).pin_memory(),
+               ctx=torch.empty((B,), dtype=torch.int32).pin_memory(),
+               slots=torch.empty((B,), dtype=torch.int64).pin_memory(),
+               pairs=torch.empty((B, 2), dtype=torch.int32).pin_memory()) for _ in range(2)]
+    done = [torch.cuda.Event(), torch.cuda.Event()]
+    cows = (kvp.kvp_copy * B)()
+    stream = torch.cuda.current_stream()
+
+    def layers_body():
+        for l in range(L):
+            kvp.kv_append(cache, l, knew[l], vnew[l], slots_d)
+            kvp.paged_decode_attention(cache, l, q[l], table_d, ctx_d, out=out[l], workspace=ws)
+
+    graph = None
+    record = []
+
+    def step(k, keep=False):
+        h = hb[k % 2]
+        done[k % 2].synchronize()  # the copies that last read these pinned buffers are done
+        pool.append_slots_raw(ids.data_ptr(), B, h["slots"].data_ptr(), cows)
+        npairs = 0
+        for i in range(B):
+            if cows[i].src >= 0:
+                h["pairs"][npairs, 0] = cows[i].src
+                h["pairs"][npairs, 1] = cows[i].dst
+                npairs += 1
+        pool.export_raw(ids.data_ptr(), B, max_blocks, h["table"].data_ptr(), h["ctx"].data_ptr())
+        if keep:
+            record.append((h["table"].numpy().copy(), h["ctx"].numpy().copy(), npairs))
+        table_d.copy_(h["table"], non_blocking=True)
+        ctx_d.copy_(h["ctx"], non_blocking=True)
+        slots_d.copy_(h["slots"], non_blocking=True)
+        if npairs:
+            pairs_d[:npairs].copy_(h["pairs"][:npairs], non_blocking=True)
+            kvp.kv_copy_blocks(cache, pairs_d[:npairs])
+        if graph is not None:
+            graph.replay()
+        else:
+            layers_body()
+        done[k % 2].record(stream)
+
+    # first step eagerly (loads code objects), then capture the 24-layer body
+    step(0)
+    torch.cuda.synchronize()
+    if not args.no_graph:
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            layers_body()
+        torch.cuda.synchronize()
+    k = 1
+    for _ in range(args.warmup):
+        step(k)
+        k += 1
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(k, keep=True)
+        k += 1
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+
+    # bytes of the timed steps
+    uniq_tok = [unique_and_logical_tokens(t, c) for t, c, _ in record]
+    uniq_bytes_step = np.mean([u for u, _ in uniq_tok]) * KV_TOKEN_LAYER_BYTES * L
+    logical_bytes_step = np.mean([lg for _, lg in uniq_tok]) * KV_TOKEN_LAYER_BYTES * L
+    cow_blocks = sum(n for _, _, n in record)
+    value = uniq_bytes_step / (ms_per_step * 1e-3) / 1e9
+    logical_gbps = logical_bytes_step / (ms_per_step * 1e-3) / 1e9
+    print(f"[bench] {ms_per_step:.4f} ms/step, unique {uniq_bytes_step / 1e9:.3f} GB/step -> {value:.1f} GB/s, "
+          f"logical {logical_gbps:.1f} GB/s, COW blocks in timed steps {cow_blocks}", file=sys.stderr, flush=True)
+
+    # ---- dominant kernel: the paged decode call, timed per call with HIP events on the
+    # stream it runs on; layers are cycled so each call reads cold data (the 24-layer
+    # working set is far larger than the on-chip caches) ----
+    table_last, ctx_last, _ = record[-1]
+    call_bytes, call_uniq, call_logical = decode_call_bytes(table_last, ctx_last, B)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.kernel_reps * L)]
+    torch.cuda.synchronize()
+    i = 0
+    for r in range(args.kernel_reps):
+        for l in range(L):
+            evs[i][0].record(stream)
+            kvp.paged_decode_attention(cache, l, q[l], table_d, ctx_d, out=out[l], workspace=ws)
+            evs[i][1].record(stream)
+            i += 1
+    torch.cuda.synchronize()
+    durs = [a.elapsed_time(b) for a, b in evs]
+    avg_ms = float(np.mean(durs[L:])) if len(durs) > L else float(np.mean(durs))  # skip the first round
+    achieved = call_bytes / (avg_ms * 1e-3) / 1e9
+    print(f"[bench] decode call avg {avg_ms * 1e3:.2f} us over {len(durs) - L} calls, {call_bytes / 1e6:.2f} MB "
+          f"-> {achieved:.1f} GB/s ({achieved / HBM_PEAK_GBPS * 100:.1f}% of peak)", file=sys.stderr, flush=True)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(W)
+        print(f"[bench] cpu oracle {cpu}", file=sys.stderr, flush=True)
+
+    line = {
+        "metric": "decode attention KV GB/s (% of HBM peak) + decode steps/sec at batch 200",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": f"paged GQA decode step, batch {B}, 24 layers x (kv_append + paged decode), "
+                               "14q/2kv heads d64 fp16, 16-token blocks, contexts U{128..2048}, "
+                               "groups of 8 sharing a 512-token prefix (copy-on-write)",
+                   "batch": B, "layers": L, "graph": graph is not None},
+        "steps_per_sec": round(1e3 / ms_per_step, 2),
+        "hbm_pct": round(value / HBM_PEAK_GBPS * 100, 2),
+        "logical_GBps": round(logical_gbps, 2),
+        "unique_GB_per_step": round(uniq_bytes_step / 1e9, 4),
+        "logical_GB_per_step": round(logical_bytes_step / 1e9, 4),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "kernel": "paged_decode_attention (decode_partial_kernel + decode_reduce_kernel)",
+                     "bytes_per_launch": int(call_bytes), "avg_launch_us": round(avg_ms * 1e3, 3)},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,263 @@
+/*
+ * kvp.h -- C ABI of the MI355X (gfx950) paged key-value-cache attention library.
+ *
+ * What the library computes (pages cited by title and section):
+ *   [CHAP]  neuralialabs "Tornar a inferencia barata: KV cache, batching e quantizacao":
+ *           the KV cache (keys/values of earlier positions never change under the causal
+ *           mask, so they are stored), prefill vs decode, the per-token cache size
+ *           2*L*H_kv*d*bytes, grouped-query attention, PagedAttention (fixed-size blocks
+ *           plus a per-sequence block table; shared-prefix blocks).
+ *   [KVES]  gustavoai "La cache de claves y valores: cuanto cuesta cada token": the four
+ *           steps of one cached token (append k_t, v_t to each head's cache, then attend
+ *           over the whole cache including itself).
+ *   [XF]    chatgpz.de "Aufmerksamkeit", xformers demo sections 4 (packed variable-length
+ *           batch with a block-diagonal, optionally causal, mask) and 5 (grouped-query
+ *           attention in the (B, M, G, Hq/G, K) layout).
+ *   [PAGED] same feed, paged-attention article: SECTION 2 (page pool with a free list
+ *           and reference counts, block table per request) and SECTION 3 (copy-on-write
+ *           shared system prompts).
+ *   [FLASH] same feed, FlashAttention post: blocks of keys/values processed on chip with
+ *           a partial softmax, merged by rescaling with e^(block max - global max).
+ *   [LIN]   same feed, linear-attention post: TraditionalAttention, softmax(QK^T/sqrt(d))V.
+ *
+ * Conventions for every call
+ *   - Every function returns kvp_status (0 = KVP_OK, negative = error).  On error nothing
+ *     has changed: no host state and no device memory; kvp_last_error() describes it.
+ *   - Device memory is always owned by the caller.  Arguments documented "device" are
+ *     device pointers (e.g. from torch tensors); the library never allocates device memory.
+ *   - Work is enqueued asynchronously on the given stream (NULL = the null stream); the
+ *     host returns before the kernels run.  Errors detected on the host are reported
+ *     before anything is enqueued.
+ *   - Host objects (kvp_pool) are owned by the library and freed by block_pool_destroy.
+ *     A pool is not thread-safe: one owner thread at a time.
+ *   - Layouts: head_dim d = 64.  dtype is fp16 (KVP_F16) or fp32 (KVP_F32).
+ *       paged K/V pool, one per K and V:  [num_layers][num_blocks][H_kv][block_size][d]
+ *       contiguous cache (one layer):       [B][H_kv][Lmax][d]
+ *       decode q / out:                     [B][H_q][d]
+ *       packed prefill q / out:             [T][H_q][d];  k, v: [T][H_kv][d]
+ *       block table:                        int32 [B][max_blocks], logical block -> block id
+ *       slot:                               int64 block_id * block_size + offset
+ *   - Query head h reads key-value head h / (H_q / H_kv)  ([CHAP] GQA passage, [XF] 5).
+ */
+#ifndef KVP_H
+#define KVP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* HIP stream handle without including the HIP headers (same type as hipStream_t). */
+struct ihipStream_t;
+typedef struct ihipStream_t *kvp_stream;
+
+typedef int32_t kvp_status;
+#define KVP_OK 0
+#define KVP_ERR_INVALID (-1)     /* bad argument, shape or state                    */
+#define KVP_ERR_OOM (-2)         /* block pool has no free block                    */
+#define KVP_ERR_NOT_FOUND (-3)   /* unknown sequence id                             */
+#define KVP_ERR_HIP (-4)         /* the HIP runtime reported an error on launch     */
+#define KVP_ERR_UNSUPPORTED (-5) /* valid request this build does not implement     */
+
+enum { KVP_F16 = 0, KVP_F32 = 1 };
+
+typedef struct {
+    int32_t num_layers;
+    int32_t num_q_heads;
+    int32_t num_kv_heads; /* num_q_heads % num_kv_heads == 0            */
+    int32_t head_dim;     /* 64                                         */
+    int32_t dtype;        /* KVP_F16 or KVP_F32                          */
+} kvp_dims;
+
+typedef struct {
+    kvp_dims dims;
+    int32_t block_size; /* tokens per block: 16                          */
+    int32_t num_blocks;
+    void *k_pool; /* device [num_layers][num_blocks][H_kv][block_size][d] */
+    void *v_pool; /* device, same shape                                   */
+} kvp_cache_desc;
+
+/* Thread-local description of the last error on this thread ("" if none). */
+const char *kvp_last_error(void);
+/* Library version string. */
+const char *kvp_version(void);
+
+/* ======================================================================================
+ * Host block manager  ([PAGED] SECTION 2 and 3; [CHAP] PagedAttention passage)
+ * ==================================================================================== */
+typedef struct kvp_pool kvp_pool;
+
+typedef struct {
+    int32_t src; /* block copied from, -1 if no copy was needed */
+    int32_t dst; /* block copied to,   -1 if no copy was needed */
+} kvp_copy;
+
+typedef struct {
+    int32_t total_blocks;
+    int32_t used_blocks;
+    int32_t free_blocks;
+    int32_t shared_blocks; /* blocks with reference count > 1 */
+    int32_t num_seqs;
+    double utilisation_pct; /* used / total * 100 ([PAGED] SECTION 2) */
+} kvp_pool_stats;
+
+/* Create a pool of num_blocks blocks of block_size tokens.  The free list starts as
+ * 0..num_blocks-1; allocation takes the front, release appends to the back ([PAGED] 2).
+ * INVALID if num_blocks <= 0 or block_size <= 0.  *out receives the pool. */
+kvp_status block_pool_create(int32_t num_blocks, int32_t block_size, kvp_pool **out);
+void block_pool_destroy(kvp_pool *pool);
+
+/* Reorder the free list (only while every block is free): perm is a permutation of
+ * 0..num_blocks-1 giving the new front-to-back order.  Used to obtain scattered tables.
+ * INVALID if blocks are in use or perm is not a permutation. */
+kvp_status block_pool_set_free_order(kvp_pool *pool, const int32_t *perm, int32_t n);
+
+/* New sequence holding n_tokens tokens: ceil(n_tokens / block_size) fresh blocks, each
+ * with reference count 1.  OOM (and no change) if too few blocks are free. */
+kvp_status block_table_alloc(kvp_pool *pool, int32_t n_tokens, int32_t *seq_id);
+
+/* Reserve the position of sequence `seq`'s next token and return its slot.  At a block
+ * boundary a new block is taken ([PAGED] 2, generate_token).  If the target block is
+ * shared (reference count > 1) it is first made private by copy-on-write and *cow gets
+ * {src, dst}: the caller must copy block src to dst on the device (kv_copy_blocks) before
+ * writing the slot; otherwise *cow = {-1, -1}.  OOM / NOT_FOUND leave everything as is. */
+kvp_status block_table_append_slot(kvp_pool *pool, int32_t seq, int64_t *slot, kvp_copy *cow);
+
+/* One decode step for a batch: block_table_append_slot for seqs[0..n-1] in order (each id
+ * at most once); slots[i] and cows[i] receive that call's results.  All or nothing:
+ * capacity for every new and copied block is checked first, so OOM changes nothing. */
+kvp_status block_table_append_slots(kvp_pool *pool, const int32_t *seqs, int32_t n,
+                                    int64_t *slots, kvp_copy *cows);
+
+/* Reserve the positions of the next n tokens of `seq` (e.g. a prompt appended after a
+ * shared prefix) and write their slots to slots[n].  Same rules as n calls of
+ * block_table_append_slot; at most the first, partially filled block can need
+ * copy-on-write, reported in *cow as above.  All or nothing: OOM changes nothing. */
+kvp_status block_table_reserve(kvp_pool *pool, int32_t seq, int32_t n, int64_t *slots,
+                               kvp_copy *cow);
+
+/* Fork: the child gets a copy of the parent's block table and token count, and every
+ * block's reference count goes up by one ([PAGED] 3, share). */
+kvp_status block_table_fork(kvp_pool *pool, int32_t parent, int32_t *child);
+
+/* Copy-on-write of one logical block: if its block is shared, take a new block, release
+ * the old one and point the table at the new one; *src/*dst report the pair to copy on the
+ * device.  If the block is private, *src = *dst = that block (nothing to do). */
+kvp_status block_table_cow(kvp_pool *pool, int32_t seq, int32_t logical_block, int32_t *src,
+                           int32_t *dst);
+
+/* Shorten a sequence to n_tokens (<= its current count): blocks past
+ * ceil(n_tokens / block_size) are released; a kept block that is shared stays shared, so the
+ * next append into it copies it first.  Used to give a forked request a shorter view of a
+ * shared prefix, and to roll back tokens that were reserved but rejected. */
+kvp_status block_table_truncate(kvp_pool *pool, int32_t seq, int32_t n_tokens);
+
+/* Release every block of the sequence (a block returns to the free list when its
+ * reference count reaches 0) and forget the sequence. */
+kvp_status block_table_free(kvp_pool *pool, int32_t seq);
+
+/* Host export of n sequences' tables into host_table [n][max_blocks] (unused entries -1)
+ * and their token counts into context_lens [n].  INVALID if a table is longer than
+ * max_blocks.  The caller uploads both to the device for the attention calls. */
+kvp_status block_table_export(const kvp_pool *pool, const int32_t *seqs, int32_t n,
+                              int32_t max_blocks, int32_t *host_table, int32_t *context_lens);
+
+/* Slots of tokens [start, start+n) of a sequence (all already reserved) into slots[n]. */
+kvp_status block_table_slots(const kvp_pool *pool, int32_t seq, int32_t start, int32_t n,
+                             int64_t *slots);
+
+/* One sequence's table: *n_tokens, *n_blocks, and up to cap block ids into blocks. */
+kvp_status block_table_get(const kvp_pool *pool, int32_t seq, int32_t *n_tokens,
+                           int32_t *n_blocks, int32_t *blocks, int32_t cap);
+
+kvp_status block_pool_stats(const kvp_pool *pool, kvp_pool_stats *stats);
+/* Reference count of a block (0 if free). */
+kvp_status block_pool_refcount(const kvp_pool *pool, int32_t block, int32_t *refcount);
+
+/* Bytes of cache per token: 2 * L * H_kv * d * elem_bytes ([CHAP] cache-size passage). */
+int64_t kv_bytes_per_token(int32_t num_layers, int32_t num_kv_heads, int32_t head_dim,
+                           int32_t elem_bytes);
+
+/* ======================================================================================
+ * Device operations (HIP kernels for gfx950)
+ * ==================================================================================== */
+
+/* Copy whole blocks for copy-on-write: for each pair p < n, block d_pairs[2p] is copied to
+ * block d_pairs[2p+1] in every layer, in both K and V pools, bit for bit ([PAGED] 3).
+ * d_pairs: device int32 [n][2].  n == 0 is a no-op. */
+kvp_status kv_copy_blocks(const kvp_cache_desc *cache, const int32_t *d_pairs, int32_t n,
+                          kvp_stream stream);
+
+/* Write n new tokens' keys and values of one layer into their slots ([KVES] step 2:
+ * k_t, v_t go to the end of each head's cache).  k, v: device [n][H_kv][d] in the cache
+ * dtype; d_slots: device int64 [n] (slot = block * block_size + offset, every slot
+ * < num_blocks * block_size, distinct).  Bit-exact copy. */
+kvp_status kv_append(const kvp_cache_desc *cache, int32_t layer, const void *k, const void *v,
+                     const int64_t *d_slots, int32_t n, kvp_stream stream);
+
+/* Contiguous-layout append: for each b < B, writes k[b], v[b] ([B][H_kv][d]) at position
+ * d_pos[b] (< Lmax) of k_cache / v_cache ([B][H_kv][Lmax][d], one layer). */
+kvp_status contiguous_kv_append(const kvp_dims *dims, void *k_cache, void *v_cache,
+                                int32_t Lmax, const void *k, const void *v,
+                                const int32_t *d_pos, int32_t B, kvp_stream stream);
+
+/* Workspace bytes for decode with B requests and contexts up to max_context tokens
+ * (split-K partials).  0 if the arguments are invalid. */
+size_t decode_workspace_bytes(const kvp_dims *dims, int32_t B, int32_t max_context);
+
+/* Number of split-K partitions the decode uses for a request of context_len tokens.
+ * A pure function of context_len (the same for paged and contiguous layouts). */
+int32_t decode_num_splits(int32_t context_len);
+
+/* Paged grouped-query decode attention for one layer ([CHAP] decode loop; [KVES] the new
+ * position attends over every cached position and itself; [LIN] softmax(q k^T * scale) v;
+ * [FLASH] block partials merged by rescaling).  For request b < B and query head h:
+ *   out[b][h] = sum_j softmax_j(scale * q[b][h] . k_j) v_j over j < d_context_lens[b],
+ * k_j / v_j read from block d_block_table[b][j / block_size], offset j % block_size, KV
+ * head h / (H_q / H_kv).  The token of this step must already be appended.
+ *   q, out: device [B][H_q][d] in the cache dtype.  d_block_table: device int32
+ *   [B][max_blocks].  d_context_lens: device int32 [B], each in 1..max_blocks*block_size.
+ *   scale: 0 means 1/sqrt(d).  workspace: device, at least
+ *   decode_workspace_bytes(dims, B, max_blocks * block_size) bytes (may be NULL if that is
+ *   0).  Long contexts are split across CUs (decode_num_splits) and merged by a second
+ *   kernel in split order; results are deterministic.  fp32 softmax and accumulation, one
+ *   rounding to the output dtype. */
+kvp_status paged_decode_attention(const kvp_cache_desc *cache, int32_t layer, void *out,
+                                  const void *q, const int32_t *d_block_table,
+                                  int32_t max_blocks, const int32_t *d_context_lens, int32_t B,
+                                  float scale, void *workspace, size_t ws_bytes,
+                                  kvp_stream stream);
+
+/* The same decode over a contiguous cache k_cache / v_cache [B][H_kv][Lmax][d] (one layer;
+ * the layout of the cache tensors in [CHAP]'s allocator check).  Same kernels, same split
+ * policy and the same arithmetic order as the paged call, so the outputs of the two are
+ * bit-identical for the same logical data. */
+kvp_status contiguous_decode_attention(const kvp_dims *dims, void *out, const void *q,
+                                       const void *k_cache, const void *v_cache, int32_t Lmax,
+                                       const int32_t *d_context_lens, int32_t B, float scale,
+                                       void *workspace, size_t ws_bytes, kvp_stream stream);
+
+/* Packed variable-length prefill ([XF] section 4, [XF] 5 for the head map).  Segment s
+ * covers packed rows d_cu_seqlens[s] .. d_cu_seqlens[s+1]-1.  Row i of a segment attends
+ * to rows j <= i of the same segment (causal = 1) or to every row of its segment
+ * (causal = 0, block-diagonal mask).  q/out: device [T][H_q][d]; k, v: device [T][H_kv][d];
+ * d_cu_seqlens: device int32 [nseg+1], non-decreasing, starting at 0; max_seqlen >= every
+ * segment length (sizes the grid).  fp16 uses MFMA tiles with fp32 accumulation. */
+kvp_status varlen_causal_prefill(const kvp_dims *dims, void *out, const void *q, const void *k,
+                                 const void *v, const int32_t *d_cu_seqlens, int32_t nseg,
+                                 int32_t max_seqlen, int32_t causal, float scale,
+                                 kvp_stream stream);
+
+/* Gather one layer of the paged cache back to the contiguous layout: positions
+ * j < d_context_lens[b] of k_out / v_out [B][H_kv][Lmax][d] receive the paged rows, bit for
+ * bit; other positions are left untouched. */
+kvp_status kv_gather(const kvp_cache_desc *cache, int32_t layer, const int32_t *d_block_table,
+                     int32_t max_blocks, const int32_t *d_context_lens, int32_t B, int32_t Lmax,
+                     void *k_out, void *v_out, kvp_stream stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* KVP_H */

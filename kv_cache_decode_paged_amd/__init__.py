@@ -1,0 +1,441 @@
+"""Python binding of the MI355X paged KV-cache attention library (libkvp.so).
+
+Argument marshalling only: every computation runs in the library's HIP kernels (device
+work) or its C++ block manager (host bookkeeping).  PyTorch tensors supply device memory
+and the current HIP stream.  There is no fallback: if libkvp.so is missing, importing the
+module raises.
+
+The C functions keep their names; see include/kvp.h for layouts and error behaviour.
+"""
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libkvp.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is missing: build it with `python -m kv_cache_decode_paged_amd._build` "
+                      "(or __graft_entry__.build()) before using the library")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+KVP_OK = 0
+KVP_ERR_INVALID = -1
+KVP_ERR_OOM = -2
+KVP_ERR_NOT_FOUND = -3
+KVP_ERR_HIP = -4
+KVP_ERR_UNSUPPORTED = -5
+_STATUS = {KVP_ERR_INVALID: "INVALID", KVP_ERR_OOM: "OOM", KVP_ERR_NOT_FOUND: "NOT_FOUND",
+           KVP_ERR_HIP: "HIP", KVP_ERR_UNSUPPORTED: "UNSUPPORTED"}
+KVP_F16 = 0
+KVP_F32 = 1
+BLOCK = 16
+HEAD_DIM = 64
+
+
+class KvpError(RuntimeError):
+    def __init__(self, status, msg):
+        super().__init__(f"kvp status {status} ({_STATUS.get(status, '?')}): {msg}")
+        self.status = status
+
+
+class KvpOOM(KvpError):
+    pass
+
+
+class kvp_dims(ctypes.Structure):
+    _fields_ = [("num_layers", ctypes.c_int32), ("num_q_heads", ctypes.c_int32),
+                ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("dtype", ctypes.c_int32)]
+
+
+class kvp_cache_desc(ctypes.Structure):
+    _fields_ = [("dims", kvp_dims), ("block_size", ctypes.c_int32), ("num_blocks", ctypes.c_int32),
+                ("k_pool", ctypes.c_void_p), ("v_pool", ctypes.c_void_p)]
+
+
+class kvp_copy(ctypes.Structure):
+    _fields_ = [("src", ctypes.c_int32), ("dst", ctypes.c_int32)]
+
+
+class kvp_pool_stats(ctypes.Structure):
+    _fields_ = [("total_blocks", ctypes.c_int32), ("used_blocks", ctypes.c_int32),
+                ("free_blocks", ctypes.c_int32), ("shared_blocks", ctypes.c_int32),
+                ("num_seqs", ctypes.c_int32), ("utilisation_pct", ctypes.c_double)]
+
+
+_i32 = ctypes.c_int32
+_i64 = ctypes.c_int64
+_p = ctypes.c_void_p
+_pi32 = ctypes.POINTER(ctypes.c_int32)
+_pi64 = ctypes.POINTER(ctypes.c_int64)
+_f32 = ctypes.c_float
+_sz = ctypes.c_size_t
+
+
+def _sig(name, res, args):
+    f = getattr(_lib, name)
+    f.restype = res
+    f.argtypes = args
+    return f
+
+
+_lib.kvp_last_error.restype = ctypes.c_char_p
+_lib.kvp_version.restype = ctypes.c_char_p
+_sig("block_pool_create", _i32, [_i32, _i32, ctypes.POINTER(_p)])
+_sig("block_pool_destroy", None, [_p])
+_sig("block_pool_set_free_order", _i32, [_p, _pi32, _i32])
+_sig("block_table_alloc", _i32, [_p, _i32, _pi32])
+_sig("block_table_append_slot", _i32, [_p, _i32, _pi64, ctypes.POINTER(kvp_copy)])
+_sig("block_table_append_slots", _i32, [_p, _pi32, _i32, _pi64, ctypes.POINTER(kvp_copy)])
+_sig("block_table_reserve", _i32, [_p, _i32, _i32, _pi64, ctypes.POINTER(kvp_copy)])
+_sig("block_table_fork", _i32, [_p, _i32, _pi32])
+_sig("block_table_cow", _i32, [_p, _i32, _i32, _pi32, _pi32])
+_sig("block_table_free", _i32, [_p, _i32])
+_sig("block_table_truncate", _i32, [_p, _i32, _i32])
+_sig("block_table_export", _i32, [_p, _pi32, _i32, _i32, _pi32, _pi32])
+_sig("block_table_slots", _i32, [_p, _i32, _i32, _i32, _pi64])
+_sig("block_table_get", _i32, [_p, _i32, _pi32, _pi32, _pi32, _i32])
+_sig("block_pool_stats", _i32, [_p, ctypes.POINTER(kvp_pool_stats)])
+_sig("block_pool_refcount", _i32, [_p, _i32, _pi32])
+_sig("kv_bytes_per_token", _i64, [_i32, _i32, _i32, _i32])
+_sig("kv_copy_blocks", _i32, [ctypes.POINTER(kvp_cache_desc), _p, _i32, _p])
+_sig("kv_append", _i32, [ctypes.POINTER(kvp_cache_desc), _i32, _p, _p, _p, _i32, _p])
+_sig("contiguous_kv_append", _i32, [ctypes.POINTER(kvp_dims), _p, _p, _i32, _p, _p, _p, _i32, _p])
+_sig("decode_workspace_bytes", _sz, [ctypes.POINTER(kvp_dims), _i32, _i32])
+_sig("decode_num_splits", _i32, [_i32])
+_sig("paged_decode_attention", _i32, [ctypes.POINTER(kvp_cache_desc), _i32, _p, _p, _p, _i32, _p,
+                                      _i32, _f32, _p, _sz, _p])
+_sig("contiguous_decode_attention", _i32, [ctypes.POINTER(kvp_dims), _p, _p, _p, _p, _i32, _p, _i32,
+                                           _f32, _p, _sz, _p])
+_sig("varlen_causal_prefill", _i32, [ctypes.POINTER(kvp_dims), _p, _p, _p, _p, _p, _i32, _i32, _i32,
+                                     _f32, _p])
+_sig("kv_gather", _i32, [ctypes.POINTER(kvp_cache_desc), _i32, _p, _i32, _p, _i32, _i32, _p, _p, _p])
+
+
+def last_error():
+    return _lib.kvp_last_error().decode()
+
+
+def version():
+    return _lib.kvp_version().decode()
+
+
+def _check(st):
+    if st != KVP_OK:
+        cls = KvpOOM if st == KVP_ERR_OOM else KvpError
+        raise cls(st, last_error())
+
+
+def lib():
+    """The raw ctypes handle (for tests of the C ABI itself)."""
+    return _lib
+
+
+# ---------------------------------------------------------------------------------------
+# tensors and streams
+# ---------------------------------------------------------------------------------------
+_DT = {torch.float16: KVP_F16, torch.float32: KVP_F32}
+
+
+def _dtype_code(dt):
+    if dt not in _DT:
+        raise TypeError(f"unsupported dtype {dt} (float16 or float32)")
+    return _DT[dt]
+
+
+def _stream(stream=None):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _dev(t, name, dtype=None, ndim=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got {tuple(t.shape)}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def dims(num_layers, num_q_heads, num_kv_heads, dtype, head_dim=HEAD_DIM):
+    return kvp_dims(num_layers, num_q_heads, num_kv_heads, head_dim, _dtype_code(dtype))
+
+
+class PagedKVCache:
+    """K and V pools of shape [num_layers][num_blocks][H_kv][16][64] in device memory
+    (owned by the torch tensors held here)."""
+
+    def __init__(self, num_layers, num_blocks, num_q_heads, num_kv_heads, dtype=torch.float16,
+                 device="cuda", k_pool=None, v_pool=None):
+        shape = (num_layers, num_blocks, num_kv_heads, BLOCK, HEAD_DIM)
+        self.k_pool = torch.empty(shape, dtype=dtype, device=device) if k_pool is None else k_pool
+        self.v_pool = torch.empty(shape, dtype=dtype, device=device) if v_pool is None else v_pool
+        for t, n in ((self.k_pool, "k_pool"), (self.v_pool, "v_pool")):
+            if tuple(t.shape) != shape:
+                raise ValueError(f"{n} must have shape {shape}")
+            _dev(t, n, dtype)
+        self.num_layers, self.num_blocks = num_layers, num_blocks
+        self.num_q_heads, self.num_kv_heads, self.dtype = num_q_heads, num_kv_heads, dtype
+        self.desc = kvp_cache_desc(dims(num_layers, num_q_heads, num_kv_heads, dtype), BLOCK,
+                                   num_blocks, self.k_pool.data_ptr(), self.v_pool.data_ptr())
+
+    @property
+    def dims(self):
+        return self.desc.dims
+
+
+# ---------------------------------------------------------------------------------------
+# host block manager
+# ---------------------------------------------------------------------------------------
+class BlockPool:
+    """Wrapper of the C++ block manager (pool, block tables, fork, copy-on-write)."""
+
+    def __init__(self, num_blocks, block_size=BLOCK):
+        h = _p()
+        _check(_lib.block_pool_create(num_blocks, block_size, ctypes.byref(h)))
+        self._h = h
+        self.num_blocks, self.block_size = num_blocks, block_size
+
+    def close(self):
+        if self._h:
+            _lib.block_pool_destroy(self._h)
+            self._h = _p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def set_free_order(self, perm):
+        arr = (ctypes.c_int32 * len(perm))(*[int(x) for x in perm])
+        _check(_lib.block_pool_set_free_order(self._h, arr, len(perm)))
+
+    def alloc(self, n_tokens):
+        sid = ctypes.c_int32()
+        _check(_lib.block_table_alloc(self._h, int(n_tokens), ctypes.byref(sid)))
+        return sid.value
+
+    def append_slot(self, seq):
+        """-> (slot, (src, dst) or None)"""
+        slot = ctypes.c_int64()
+        cp = kvp_copy()
+        _check(_lib.block_table_append_slot(self._h, int(seq), ctypes.byref(slot), ctypes.byref(cp)))
+        return slot.value, (None if cp.src < 0 else (cp.src, cp.dst))
+
+    def append_slots(self, seqs):
+        """One step for a batch: -> (slots int64 [n] host tensor, [(src, dst) or None] * n)."""
+        n = len(seqs)
+        ids = torch.tensor([int(x) for x in seqs] or [0], dtype=torch.int32)
+        slots = torch.empty((max(n, 1),), dtype=torch.int64)
+        cows = (kvp_copy * max(n, 1))()
+        _check(_lib.block_table_append_slots(self._h, ctypes.cast(ids.data_ptr(), _pi32), n,
+                                             ctypes.cast(slots.data_ptr(), _pi64), cows))
+        return slots[:n], [None if cows[i].src < 0 else (cows[i].src, cows[i].dst) for i in range(n)]
+
+    def append_slots_raw(self, ids_ptr, n, slots_ptr, cows):
+        """Zero-copy variant for hot loops: caller-owned int32 ids / int64 slots buffers
+        (addresses) and a (kvp_copy * n) array."""
+        _check(_lib.block_table_append_slots(self._h, ctypes.cast(ids_ptr, _pi32), int(n),
+                                             ctypes.cast(slots_ptr, _pi64), cows))
+
+    def export_raw(self, ids_ptr, n, max_blocks, table_ptr, ctx_ptr):
+        _check(_lib.block_table_export(self._h, ctypes.cast(ids_ptr, _pi32), int(n), int(max_blocks),
+                                       ctypes.cast(table_ptr, _pi32), ctypes.cast(ctx_ptr, _pi32)))
+
+    def reserve(self, seq, n):
+        """-> (slots int64 [n] on the host, (src, dst) or None)"""
+        out = torch.empty((max(int(n), 1),), dtype=torch.int64)
+        cp = kvp_copy()
+        _check(_lib.block_table_reserve(self._h, int(seq), int(n), ctypes.cast(out.data_ptr(), _pi64),
+                                        ctypes.byref(cp)))
+        return out[:int(n)], (None if cp.src < 0 else (cp.src, cp.dst))
+
+    def fork(self, parent):
+        c = ctypes.c_int32()
+        _check(_lib.block_table_fork(self._h, int(parent), ctypes.byref(c)))
+        return c.value
+
+    def cow(self, seq, logical_block):
+        s, d = ctypes.c_int32(), ctypes.c_int32()
+        _check(_lib.block_table_cow(self._h, int(seq), int(logical_block), ctypes.byref(s), ctypes.byref(d)))
+        return s.value, d.value
+
+    def free(self, seq):
+        _check(_lib.block_table_free(self._h, int(seq)))
+
+    def truncate(self, seq, n_tokens):
+        _check(_lib.block_table_truncate(self._h, int(seq), int(n_tokens)))
+
+    def export(self, seqs, max_blocks):
+        """-> (table int32 [n, max_blocks] (pad -1), context_lens int32 [n]) on the host."""
+        n = len(seqs)
+        table = torch.empty((n, max_blocks), dtype=torch.int32)
+        ctx = torch.empty((n,), dtype=torch.int32)
+        arr = (ctypes.c_int32 * max(n, 1))(*[int(s) for s in seqs])
+        _check(_lib.block_table_export(self._h, arr, n, int(max_blocks),
+                                       ctypes.cast(table.data_ptr(), _pi32), ctypes.cast(ctx.data_ptr(), _pi32)))
+        return table, ctx
+
+    def slots(self, seq, start, n):
+        out = torch.empty((n,), dtype=torch.int64)
+        _check(_lib.block_table_slots(self._h, int(seq), int(start), int(n), ctypes.cast(out.data_ptr(), _pi64)))
+        return out
+
+    def table(self, seq):
+        nt, nb = ctypes.c_int32(), ctypes.c_int32()
+        _check(_lib.block_table_get(self._h, int(seq), ctypes.byref(nt), ctypes.byref(nb), None, 0))
+        buf = (ctypes.c_int32 * max(nb.value, 1))()
+        _check(_lib.block_table_get(self._h, int(seq), ctypes.byref(nt), ctypes.byref(nb), buf, nb.value))
+        return list(buf)[:nb.value]
+
+    def tokens(self, seq):
+        nt, nb = ctypes.c_int32(), ctypes.c_int32()
+        _check(_lib.block_table_get(self._h, int(seq), ctypes.byref(nt), ctypes.byref(nb), None, 0))
+        return nt.value
+
+    def stats(self):
+        st = kvp_pool_stats()
+        _check(_lib.block_pool_stats(self._h, ctypes.byref(st)))
+        return {f: getattr(st, f) for f, _ in kvp_pool_stats._fields_}
+
+    def refcount(self, block):
+        r = ctypes.c_int32()
+        _check(_lib.block_pool_refcount(self._h, int(block), ctypes.byref(r)))
+        return r.value
+
+
+def kv_bytes_per_token(num_layers, num_kv_heads, head_dim, elem_bytes):
+    return int(_lib.kv_bytes_per_token(num_layers, num_kv_heads, head_dim, elem_bytes))
+
+
+# ---------------------------------------------------------------------------------------
+# device operations
+# ---------------------------------------------------------------------------------------
+def kv_copy_blocks(cache: PagedKVCache, pairs, stream=None):
+    """pairs: device int32 [n, 2] (src, dst)."""
+    n = pairs.shape[0] if pairs.numel() else 0
+    if n == 0:
+        return
+    _check(_lib.kv_copy_blocks(ctypes.byref(cache.desc), _dev(pairs, "pairs", torch.int32), n,
+                               _stream(stream)))
+
+
+def kv_append(cache: PagedKVCache, layer, k, v, slots, stream=None):
+    """k, v: device [n, H_kv, 64] in the cache dtype; slots: device int64 [n]."""
+    n = k.shape[0]
+    if v.shape != k.shape or k.shape[1:] != (cache.num_kv_heads, HEAD_DIM) or slots.shape != (n,):
+        raise ValueError("kv_append: shape mismatch")
+    _check(_lib.kv_append(ctypes.byref(cache.desc), int(layer), _dev(k, "k", cache.dtype),
+                          _dev(v, "v", cache.dtype), _dev(slots, "slots", torch.int64), n,
+                          _stream(stream)))
+
+
+def contiguous_kv_append(k_cache, v_cache, k, v, pos, num_q_heads=None, stream=None):
+    """k_cache, v_cache: [B, H_kv, Lmax, 64]; k, v: [B, H_kv, 64]; pos: device int32 [B]."""
+    B, hkv, lmax, d = k_cache.shape
+    if v_cache.shape != k_cache.shape or k.shape != (B, hkv, d) or v.shape != k.shape or pos.shape != (B,):
+        raise ValueError("contiguous_kv_append: shape mismatch")
+    dm = dims(1, num_q_heads or hkv, hkv, k_cache.dtype, d)
+    _check(_lib.contiguous_kv_append(ctypes.byref(dm), _dev(k_cache, "k_cache", k.dtype),
+                                     _dev(v_cache, "v_cache", k.dtype), lmax, _dev(k, "k"), _dev(v, "v"),
+                                     _dev(pos, "pos", torch.int32), B, _stream(stream)))
+
+
+def decode_num_splits(context_len):
+    return int(_lib.decode_num_splits(int(context_len)))
+
+
+def decode_workspace_bytes(num_q_heads, num_kv_heads, dtype, B, max_context):
+    dm = dims(1, num_q_heads, num_kv_heads, dtype)
+    return int(_lib.decode_workspace_bytes(ctypes.byref(dm), int(B), int(max_context)))
+
+
+def make_workspace(num_q_heads, num_kv_heads, dtype, B, max_context, device="cuda"):
+    n = decode_workspace_bytes(num_q_heads, num_kv_heads, dtype, B, max_context)
+    return torch.empty((max(n, 16),), dtype=torch.uint8, device=device)
+
+
+def paged_decode_attention(cache: PagedKVCache, layer, q, block_table, context_lens, out=None,
+                           scale=0.0, workspace=None, stream=None):
+    """q: device [B, H_q, 64]; block_table: device int32 [B, max_blocks]; context_lens:
+    device int32 [B].  Returns out [B, H_q, 64]."""
+    B, hq, d = q.shape
+    if hq != cache.num_q_heads or d != HEAD_DIM:
+        raise ValueError("paged_decode_attention: q shape does not match the cache")
+    max_blocks = block_table.shape[1]
+    if block_table.shape[0] != B or context_lens.shape != (B,):
+        raise ValueError("paged_decode_attention: table / context_lens shape mismatch")
+    if out is None:
+        out = torch.empty_like(q)
+    if workspace is None:
+        workspace = make_workspace(hq, cache.num_kv_heads, cache.dtype, B, max_blocks * BLOCK, q.device)
+    _check(_lib.paged_decode_attention(ctypes.byref(cache.desc), int(layer), _dev(out, "out", cache.dtype),
+                                       _dev(q, "q", cache.dtype), _dev(block_table, "block_table", torch.int32),
+                                       max_blocks, _dev(context_lens, "context_lens", torch.int32), B,
+                                       float(scale), _dev(workspace, "workspace"), workspace.numel(),
+                                       _stream(stream)))
+    return out
+
+
+def contiguous_decode_attention(q, k_cache, v_cache, context_lens, out=None, scale=0.0,
+                                workspace=None, stream=None):
+    """q: [B, H_q, 64]; k_cache, v_cache: [B, H_kv, Lmax, 64]; context_lens: int32 [B]."""
+    B, hq, d = q.shape
+    Bk, hkv, lmax, dk = k_cache.shape
+    if Bk != B or dk != d or v_cache.shape != k_cache.shape or context_lens.shape != (B,):
+        raise ValueError("contiguous_decode_attention: shape mismatch")
+    dm = dims(1, hq, hkv, q.dtype, d)
+    if out is None:
+        out = torch.empty_like(q)
+    if workspace is None:
+        workspace = make_workspace(hq, hkv, q.dtype, B, lmax, q.device)
+    _check(_lib.contiguous_decode_attention(ctypes.byref(dm), _dev(out, "out", q.dtype), _dev(q, "q"),
+                                            _dev(k_cache, "k_cache", q.dtype), _dev(v_cache, "v_cache", q.dtype),
+                                            lmax, _dev(context_lens, "context_lens", torch.int32), B,
+                                            float(scale), _dev(workspace, "workspace"), workspace.numel(),
+                                            _stream(stream)))
+    return out
+
+
+def varlen_causal_prefill(q, k, v, cu_seqlens, max_seqlen, causal=True, out=None, scale=0.0,
+                          stream=None):
+    """q: [T, H_q, 64]; k, v: [T, H_kv, 64]; cu_seqlens: device int32 [nseg+1];
+    max_seqlen: host int >= every segment length."""
+    T, hq, d = q.shape
+    hkv = k.shape[1]
+    if k.shape != (T, hkv, d) or v.shape != k.shape:
+        raise ValueError("varlen_causal_prefill: shape mismatch")
+    dm = dims(1, hq, hkv, q.dtype, d)
+    if out is None:
+        out = torch.empty_like(q)
+    nseg = cu_seqlens.numel() - 1
+    _check(_lib.varlen_causal_prefill(ctypes.byref(dm), _dev(out, "out", q.dtype), _dev(q, "q"),
+                                      _dev(k, "k", q.dtype), _dev(v, "v", q.dtype),
+                                      _dev(cu_seqlens, "cu_seqlens", torch.int32), nseg, int(max_seqlen),
+                                      int(bool(causal)), float(scale), _stream(stream)))
+    return out
+
+
+def kv_gather(cache: PagedKVCache, layer, block_table, context_lens, lmax, k_out=None, v_out=None,
+              stream=None):
+    B, max_blocks = block_table.shape
+    shape = (B, cache.num_kv_heads, lmax, HEAD_DIM)
+    if k_out is None:
+        k_out = torch.zeros(shape, dtype=cache.dtype, device=block_table.device)
+    if v_out is None:
+        v_out = torch.zeros(shape, dtype=cache.dtype, device=block_table.device)
+    _check(_lib.kv_gather(ctypes.byref(cache.desc), int(layer), _dev(block_table, "block_table", torch.int32),
+                          max_blocks, _dev(context_lens, "context_lens", torch.int32), B, int(lmax),
+                          _dev(k_out, "k_out", cache.dtype), _dev(v_out, "v_out", cache.dtype),
+                          _stream(stream)))
+    return k_out, v_out

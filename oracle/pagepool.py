@@ -19,7 +19,9 @@ Readings where the article is silent (each is listed with its reason in the desi
     needed); with a count of one the write goes in place;
   * running out of pages raises PoolOOM and leaves every table, count and the free-list
     order exactly as before (capacity is checked before anything is taken);
-  * releasing a page that is not allocated raises PoolError (a double free).
+  * releasing a page that is not allocated raises PoolError (a double free);
+  * truncating a sequence releases the pages past its new length; a kept shared page
+    stays shared (a later append into it is copied first).
 """
 import math
 from collections import deque
@@ -133,6 +135,47 @@ class PagePoolModel:
         slot = table[tokens // ps] * ps + tokens % ps
         self.seqs[sid][1] = tokens + 1
         return slot, copy
+
+    def append_batch(self, sids):
+        """append_slot for each id in order; all or nothing (state restored on OOM)."""
+        import copy as _copy
+        if len(set(sids)) != len(sids):
+            raise PoolError("repeated sequence in batch")
+        saved = (_copy.deepcopy(self.free), dict(self.ref),
+                 {k: [list(v[0]), v[1]] for k, v in self.seqs.items()})
+        try:
+            return [self.append_slot(s) for s in sids]
+        except PoolOOM:
+            self.free, self.ref, self.seqs = saved
+            raise
+
+    def reserve(self, sid, n):
+        """n appends in one call, all or nothing: returns (slots, (src, dst) or None)."""
+        table, tokens = self.seqs[sid]
+        ps = self.page_size
+        need = math.ceil((tokens + n) / ps) - len(table)
+        copy_needed = n > 0 and tokens % ps != 0 and self.ref[table[tokens // ps]] > 1
+        if need + int(copy_needed) > len(self.free):
+            raise PoolOOM("no free pages")
+        slots, copy = [], None
+        for _ in range(n):
+            slot, c = self.append_slot(sid)
+            slots.append(slot)
+            if c is not None:
+                copy = c
+        return slots, copy
+
+    def truncate(self, sid, n_tokens):
+        """Shorten to n_tokens: pages past ceil(n/page_size) are released (in table
+        order); kept pages keep their sharing, so a later append copies a shared one."""
+        table, tokens = self.seqs[sid]
+        if not 0 <= n_tokens <= tokens:
+            raise PoolError("bad truncate length")
+        keep = math.ceil(n_tokens / self.page_size)
+        for pid in table[keep:]:
+            self.release(pid)
+        del table[keep:]
+        self.seqs[sid][1] = n_tokens
 
     def free_seq(self, sid):
         table, _ = self.seqs.pop(sid)

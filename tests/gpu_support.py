@@ -1,0 +1,136 @@
+"""Helpers of the GPU tests: device checks and construction of a paged decode step.
+
+Inputs come from `workloads` (seeded), expected values from `oracle`; the HIP library
+only ever produces the values under test.
+"""
+import math
+import os
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+
+GPU = torch.cuda.is_available()
+
+
+def need_gpu():
+    if not GPU:
+        pytest.skip("no GPU")
+
+
+def say(*a):
+    """Progress line naming the case, flushed before the GPU step runs."""
+    print("[gpu-case]", *a, file=sys.stderr, flush=True)
+
+
+def to64(t):
+    return t.detach().to("cpu").to(torch.float64).numpy()
+
+
+def max_abs(a, b):
+    return float(np.max(np.abs(np.asarray(a, dtype=np.float64) - np.asarray(b, dtype=np.float64))))
+
+
+TOL = {torch.float16: 2e-3, torch.float32: 1e-5}
+
+
+class PagedStep:
+    """One decode step of a batch over a paged cache, built through the block manager:
+    sharing groups fork a prefix sequence (and truncate to shorter contexts), private
+    tokens are reserved after it, then the step appends one token per request (copy-on-
+    write where the target block is shared) and writes its K/V in every layer."""
+
+    def __init__(self, kvp, pb: W.PagedBatch, layers, hq, hkv, dtype, seed, device="cuda",
+                 extra_blocks=64, poison=True, layers_with_data=None):
+        self.kvp, self.pb, self.layers = kvp, pb, layers
+        self.hq, self.hkv, self.dtype, self.seed = hq, hkv, dtype, seed
+        B = pb.batch
+        ctx_after = [c + 1 for c in pb.ctx_before]
+        self.lmax = max(ctx_after)
+        self.max_blocks = math.ceil(self.lmax / W.BLOCK)
+        ngroups = len(set(pb.group))
+        need = sum(math.ceil(c / W.BLOCK) for c in ctx_after) + ngroups * math.ceil(pb.prefix / W.BLOCK)
+        self.num_blocks = need + extra_blocks
+        self.pool = kvp.BlockPool(self.num_blocks)
+        self.pool.set_free_order(W.free_list_permutation(self.num_blocks, seed + 17).tolist())
+        self.cache = kvp.PagedKVCache(layers, self.num_blocks, hq, hkv, dtype, device)
+        if poison:  # never-written rows hold NaN: any read of them shows up in the output
+            self.cache.k_pool.fill_(float("nan"))
+            self.cache.v_pool.fill_(float("nan"))
+        self.layers_with_data = list(range(layers)) if layers_with_data is None else layers_with_data
+        self.logical = {l: W.logical_kv(pb, hkv, self.lmax, seed, dtype, layer=l) for l in self.layers_with_data}
+        prefix = {l: W.group_prefix_kv(pb, hkv, seed, dtype, layer=l) for l in self.layers_with_data}
+
+        seqs = [None] * B
+        for gi in sorted(set(pb.group)):
+            members = [i for i in range(B) if pb.group[i] == gi]
+            if pb.prefix > 0:
+                pre = self.pool.alloc(pb.prefix)
+                sl = self.pool.slots(pre, 0, pb.prefix).to(device)
+                for l in self.layers_with_data:
+                    pk, pv = prefix[l][gi]
+                    kvp.kv_append(self.cache, l, pk.transpose(0, 1).contiguous().to(device),
+                                  pv.transpose(0, 1).contiguous().to(device), sl)
+                for i in members:
+                    s = self.pool.fork(pre)
+                    L = pb.ctx_before[i]
+                    if L < pb.prefix:
+                        self.pool.truncate(s, L)
+                    elif L > pb.prefix:
+                        self._reserve_private(s, i, pb.prefix, L, device)
+                    seqs[i] = s
+                self.pool.free(pre)
+            else:
+                for i in members:
+                    s = self.pool.alloc(0)
+                    self._reserve_private(s, i, 0, pb.ctx_before[i], device)
+                    seqs[i] = s
+        self.seqs = seqs
+        # the decode step: one new token per request
+        pairs, slots = [], []
+        for i in range(B):
+            slot, cp = self.pool.append_slot(seqs[i])
+            slots.append(slot)
+            if cp is not None:
+                pairs.append(cp)
+        self.cow_pairs = pairs
+        if pairs:
+            kvp.kv_copy_blocks(self.cache, torch.tensor(pairs, dtype=torch.int32, device=device))
+        self.new_slots = torch.tensor(slots, dtype=torch.int64, device=device)
+        for l in self.layers_with_data:
+            K, V = self.logical[l]
+            idx = torch.tensor(pb.ctx_before)
+            kn = K[torch.arange(B), :, idx].contiguous().to(device)  # [B, hkv, d]
+            vn = V[torch.arange(B), :, idx].contiguous().to(device)
+            kvp.kv_append(self.cache, l, kn, vn, self.new_slots)
+        table, ctx = self.pool.export(seqs, self.max_blocks)
+        self.table = table.to(device)
+        self.ctx = ctx.to(device)
+        self.ctx_host = ctx.tolist()
+        assert self.ctx_host == ctx_after
+
+    def _reserve_private(self, s, i, start, end, device):
+        n = end - start
+        sl, cp = self.pool.reserve(s, n)
+        assert cp is None  # private tokens start on a fresh block
+        sl = sl.to(device)
+        for l in self.layers_with_data:
+            K, V = self.logical[l]
+            self.kvp.kv_append(self.cache, l, K[i, :, start:end].transpose(0, 1).contiguous().to(device),
+                               V[i, :, start:end].transpose(0, 1).contiguous().to(device), sl)
+
+    def q(self, layer):
+        return W.decode_q(self.pb.batch, self.hq, self.seed, self.dtype, layer)
+
+    def oracle(self, layer, rows=None):
+        """Oracle decode output [B, Hq, d] (float64) for the given requests (all if None)."""
+        import oracle
+        K, V = self.logical[layer]
+        q = self.q(layer)
+        rows = list(range(self.pb.batch)) if rows is None else rows
+        out = oracle.decode_gqa(to64(q[rows]), to64(K[rows]), to64(V[rows]),
+                                np.array([self.ctx_host[r] for r in rows]))
+        return out

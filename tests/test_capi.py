@@ -1,0 +1,91 @@
+"""The C ABI library: it loads without a GPU, exports every symbol kvp.h declares, and its
+host-side calls validate arguments (CPU only; no device work is launched here)."""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kvp.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    names = set()
+    for m in re.finditer(r"\b([A-Za-z_][A-Za-z0-9_]*)\s*\(", text):
+        name = m.group(1)
+        prefix = text[max(0, m.start() - 80):m.start()]
+        # declarations: return type precedes the name on the same statement
+        if name in {"if", "for", "while", "sizeof", "defined"}:
+            continue
+        if re.search(r"(kvp_status|void|size_t|int32_t|int64_t|const char\s*\*)\s*\**\s*$", prefix):
+            names.add(name)
+    return sorted(names)
+
+
+def test_header_declares_the_boundary():
+    names = _declared_functions()
+    for must in ["kv_append", "paged_decode_attention", "varlen_causal_prefill", "block_table_alloc",
+                 "block_table_fork", "block_table_cow", "block_table_free", "block_table_append_slot",
+                 "kv_copy_blocks", "contiguous_decode_attention", "kv_gather", "decode_workspace_bytes",
+                 "kv_bytes_per_token", "kvp_last_error"]:
+        assert must in names
+
+
+def test_library_exports_every_declared_symbol():
+    import kv_cache_decode_paged_amd as kvp
+    lib = kvp.lib()
+    missing = [n for n in _declared_functions() if not hasattr(lib, n)]
+    assert not missing, f"declared in kvp.h but not exported: {missing}"
+
+
+def test_version_and_error_text():
+    import kv_cache_decode_paged_amd as kvp
+    assert "gfx950" in kvp.version()
+    lib = kvp.lib()
+    out = ctypes.c_void_p()
+    assert lib.block_pool_create(0, 16, ctypes.byref(out)) == kvp.KVP_ERR_INVALID
+    assert "num_blocks" in kvp.last_error()
+
+
+def test_kv_bytes_per_token_matches_pages():
+    import kv_cache_decode_paged_amd as kvp
+    assert kvp.kv_bytes_per_token(24, 2, 64, 2) == 12288
+    assert kvp.kv_bytes_per_token(24, 14, 64, 2) == 86016
+
+
+def test_device_calls_reject_bad_arguments_before_launch():
+    import kv_cache_decode_paged_amd as kvp
+    lib = kvp.lib()
+    d = kvp.kvp_dims(1, 14, 4, 64, kvp.KVP_F16)  # 14 % 4 != 0
+    assert lib.decode_workspace_bytes(ctypes.byref(d), 1, 100) == 0
+    st = lib.contiguous_decode_attention(ctypes.byref(d), None, None, None, None, 16, None, 1, 0.0,
+                                         None, 0, None)
+    assert st == kvp.KVP_ERR_INVALID
+    d = kvp.kvp_dims(1, 14, 2, 128, kvp.KVP_F16)  # head_dim 128 not built
+    st = lib.varlen_causal_prefill(ctypes.byref(d), None, None, None, None, None, 1, 8, 1, 0.0, None)
+    assert st == kvp.KVP_ERR_UNSUPPORTED
+    desc = kvp.kvp_cache_desc(kvp.kvp_dims(2, 14, 2, 64, kvp.KVP_F16), 16, 8, None, None)
+    st = lib.kv_append(ctypes.byref(desc), 0, None, None, None, 1, None)
+    assert st == kvp.KVP_ERR_INVALID  # NULL pools
+    st = lib.paged_decode_attention(ctypes.byref(desc), 5, None, None, None, 4, None, 1, 0.0, None, 0, None)
+    assert st == kvp.KVP_ERR_INVALID  # layer out of range
+    # zero-sized work is a valid no-op and launches nothing
+    desc2 = kvp.kvp_cache_desc(kvp.kvp_dims(2, 14, 2, 64, kvp.KVP_F16), 16, 8, 16, 16)
+    assert lib.kv_copy_blocks(ctypes.byref(desc2), None, 0, None) == kvp.KVP_OK
+
+
+def test_workspace_size_and_split_policy():
+    import kv_cache_decode_paged_amd as kvp
+    # policy is a pure function of the context length
+    assert kvp.decode_num_splits(1) == 1
+    assert kvp.decode_num_splits(256) == 1
+    assert kvp.decode_num_splits(257) == 2
+    assert kvp.decode_num_splits(2049) == 9
+    assert kvp.decode_num_splits(32768) == 32
+    ws = kvp.decode_workspace_bytes(14, 2, torch.float16, 32, 32768)
+    assert ws == 32 * 14 * 32 * 66 * 4
+    assert kvp.decode_workspace_bytes(14, 2, torch.float16, 4, 256) == 0

@@ -133,6 +133,18 @@ def free_list_permutation(num_blocks, seed=SEED + 400):
     return torch.randperm(num_blocks, generator=gen(seed)).to(torch.int32)
 
 
+def group_prefix_kv(pb: PagedBatch, hkv, seed, dtype=torch.float16, layer=0):
+    """{group: (K, V)} of shape [hkv, prefix, d]: the rows every member of a sharing group
+    holds in common."""
+    base = seed + 1000 * layer
+    pref = {}
+    if pb.prefix > 0:
+        for gi in sorted(set(pb.group)):
+            pref[gi] = (randn((hkv, pb.prefix, HEAD_DIM), base + 2 * gi, dtype),
+                        randn((hkv, pb.prefix, HEAD_DIM), base + 2 * gi + 1, dtype))
+    return pref
+
+
 def logical_kv(pb: PagedBatch, hkv, lmax, seed, dtype=torch.float16, layer=0):
     """Logical (contiguous) K and V [B, hkv, lmax, d] for one layer: positions below the
     prefix are the group's shared rows, the rest are private to each request; positions
@@ -140,13 +152,8 @@ def logical_kv(pb: PagedBatch, hkv, lmax, seed, dtype=torch.float16, layer=0):
     B = pb.batch
     K = torch.zeros((B, hkv, lmax, HEAD_DIM), dtype=dtype)
     V = torch.zeros_like(K)
-    groups = sorted(set(pb.group))
     base = seed + 1000 * layer
-    pref = {}
-    if pb.prefix > 0:
-        for gi in groups:
-            pref[gi] = (randn((hkv, pb.prefix, HEAD_DIM), base + 2 * gi, dtype),
-                        randn((hkv, pb.prefix, HEAD_DIM), base + 2 * gi + 1, dtype))
+    pref = group_prefix_kv(pb, hkv, seed, dtype, layer)
     for i in range(B):
         n = pb.ctx_before[i] + 1
         shared = min(pb.ctx_before[i], pb.prefix)
