@@ -221,9 +221,12 @@ int32_t decode_num_splits(int32_t context_len);
  *   [B][max_blocks].  d_context_lens: device int32 [B], each in 1..max_blocks*block_size.
  *   scale: 0 means 1/sqrt(d).  workspace: device, at least
  *   decode_workspace_bytes(dims, B, max_blocks * block_size) bytes (may be NULL if that is
- *   0).  Long contexts are split across CUs (decode_num_splits) and merged by a second
- *   kernel in split order; results are deterministic.  fp32 softmax and accumulation, one
- *   rounding to the output dtype. */
+ *   0), ZERO-FILLED before its first use; every call leaves its counters at zero again, so
+ *   a workspace is reused without clearing.  Calls that share a workspace must not overlap
+ *   in time (same stream is fine).  Long contexts are split across CUs
+ *   (decode_num_splits); the last split of a request to finish merges the partials in
+ *   split order, so results are deterministic.  fp32 softmax and accumulation, one rounding
+ *   to the output dtype. */
 kvp_status paged_decode_attention(const kvp_cache_desc *cache, int32_t layer, void *out,
                                   const void *q, const int32_t *d_block_table,
                                   int32_t max_blocks, const int32_t *d_context_lens, int32_t B,

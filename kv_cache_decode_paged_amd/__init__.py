@@ -361,8 +361,9 @@ def decode_workspace_bytes(num_q_heads, num_kv_heads, dtype, B, max_context):
 
 
 def make_workspace(num_q_heads, num_kv_heads, dtype, B, max_context, device="cuda"):
+    """Decode workspace, zero-filled as the C ABI requires before first use."""
     n = decode_workspace_bytes(num_q_heads, num_kv_heads, dtype, B, max_context)
-    return torch.empty((max(n, 16),), dtype=torch.uint8, device=device)
+    return torch.zeros((max(n, 16),), dtype=torch.uint8, device=device)
 
 
 def paged_decode_attention(cache: PagedKVCache, layer, q, block_table, context_lens, out=None,

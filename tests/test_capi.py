@@ -87,5 +87,5 @@ def test_workspace_size_and_split_policy():
     assert kvp.decode_num_splits(2049) == 9
     assert kvp.decode_num_splits(32768) == 32
     ws = kvp.decode_workspace_bytes(14, 2, torch.float16, 32, 32768)
-    assert ws == 32 * 14 * 32 * 66 * 4
+    assert ws == 32 * 14 * 32 * 66 * 4 + 256  # partials + per-(request, KV head) tickets
     assert kvp.decode_workspace_bytes(14, 2, torch.float16, 4, 256) == 0
