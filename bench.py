@@ -7,9 +7,10 @@ uniform on 128..2048, groups of 8 consecutive requests sharing a 512-token prefi
 (copy-on-write), block ids scattered by a seeded shuffle of the free list.
 
 One step = the host block manager reserves one slot per request (copy-on-write pairs
-included), the copy-on-write block copies run, the block table / context lengths / slots
-are uploaded, then for each of the 24 layers: kv_append of the new token's K/V and
-paged_decode_attention over the whole cache.  Contexts grow by one token per step.
+included), the copy-on-write block copies run, the block table / context lengths are
+uploaded, then for each of the 24 layers one fused kernel appends the new token's K/V and
+runs the paged decode attention over the whole cache (paged_decode_append_attention).
+Contexts grow by one token per step.
 
 Printed: one JSON line with the decode-attention KV throughput (unique bytes), steps/s,
 the roofline of the dominant kernel (the paged decode call: split-K partial + merge),
@@ -178,9 +179,11 @@ def main():
     stream = torch.cuda.current_stream()
 
     def layers_body():
+        # per layer: the new token's K/V go into the cache and the decode attends over it,
+        # in one fused kernel (equivalent to kv_append + paged_decode_attention)
         for l in range(L):
-            kvp.kv_append(cache, l, knew[l], vnew[l], slots_d)
-            kvp.paged_decode_attention(cache, l, q[l], table_d, ctx_d, out=out[l], workspace=ws)
+            kvp.paged_decode_append_attention(cache, l, q[l], knew[l], vnew[l], table_d, ctx_d, out=out[l],
+                                              workspace=ws)
 
     graph = None
     record = []
@@ -281,7 +284,7 @@ def main():
         "vs_baseline": None,
         "dtype": "f16",
         "data": "synthetic",
-        "config": {"workload": f"paged GQA decode step, batch {B}, 24 layers x (kv_append + paged decode), "
+        "config": {"workload": f"paged GQA decode step, batch {B}, 24 layers x fused (append + paged decode), "
                                "14q/2kv heads d64 fp16, 16-token blocks, contexts U{128..2048}, "
                                "groups of 8 sharing a 512-token prefix (copy-on-write)",
                    "batch": B, "layers": L, "graph": graph is not None},
@@ -292,7 +295,7 @@ def main():
         "logical_GB_per_step": round(logical_bytes_step / 1e9, 4),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
-                     "kernel": "paged_decode_attention (decode_partial_kernel + decode_reduce_kernel)",
+                     "kernel": "paged_decode_attention (decode_f16_kernel, split merge fused)",
                      "bytes_per_launch": int(call_bytes), "avg_launch_us": round(avg_ms * 1e3, 3)},
         "cpu_baseline": cpu,
     }

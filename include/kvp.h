@@ -207,10 +207,6 @@ kvp_status contiguous_kv_append(const kvp_dims *dims, void *k_cache, void *v_cac
  * (split-K partials).  0 if the arguments are invalid. */
 size_t decode_workspace_bytes(const kvp_dims *dims, int32_t B, int32_t max_context);
 
-/* Number of split-K partitions the decode uses for a request of context_len tokens.
- * A pure function of context_len (the same for paged and contiguous layouts). */
-int32_t decode_num_splits(int32_t context_len);
-
 /* Paged grouped-query decode attention for one layer ([CHAP] decode loop; [KVES] the new
  * position attends over every cached position and itself; [LIN] softmax(q k^T * scale) v;
  * [FLASH] block partials merged by rescaling).  For request b < B and query head h:
@@ -221,17 +217,31 @@ int32_t decode_num_splits(int32_t context_len);
  *   [B][max_blocks].  d_context_lens: device int32 [B], each in 1..max_blocks*block_size.
  *   scale: 0 means 1/sqrt(d).  workspace: device, at least
  *   decode_workspace_bytes(dims, B, max_blocks * block_size) bytes (may be NULL if that is
- *   0), ZERO-FILLED before its first use; every call leaves its counters at zero again, so
- *   a workspace is reused without clearing.  Calls that share a workspace must not overlap
- *   in time (same stream is fine).  Long contexts are split across CUs
- *   (decode_num_splits); the last split of a request to finish merges the partials in
- *   split order, so results are deterministic.  fp32 softmax and accumulation, one rounding
- *   to the output dtype. */
+ *   0), 256-byte aligned and ZERO-FILLED before its first use; every call leaves its
+ *   counters at zero again, so a workspace is reused without clearing.  Calls sharing a
+ *   workspace must not overlap in time (one stream is fine).
+ * Work split (fp16): the 64-token tiles of all (request, KV head) pairs are divided evenly
+ * over a fixed set of worker waves (4 per compute unit, or KVP_DECODE_WORKERS); a pair
+ * spread over several workers is merged by the last of them in a fixed order, so results
+ * are deterministic for a given batch and worker count and identical between the paged and
+ * contiguous layouts.  fp32 softmax and accumulation, one rounding to the output dtype. */
 kvp_status paged_decode_attention(const kvp_cache_desc *cache, int32_t layer, void *out,
                                   const void *q, const int32_t *d_block_table,
                                   int32_t max_blocks, const int32_t *d_context_lens, int32_t B,
                                   float scale, void *workspace, size_t ws_bytes,
                                   kvp_stream stream);
+
+/* paged_decode_attention fused with the append of this step's token ([KVES] step 2 then
+ * step 3 in one pass): for every request b, k_new[b] / v_new[b] (device [B][H_kv][d], fp16)
+ * are written into the cache at position d_context_lens[b] - 1 (through the block table; that
+ * block must be private to the request, i.e. copy-on-write already done) and the attention
+ * of the same call already sees them.  Equivalent to kv_append at those slots followed by
+ * paged_decode_attention, in one kernel.  fp16 only (UNSUPPORTED otherwise). */
+kvp_status paged_decode_append_attention(const kvp_cache_desc *cache, int32_t layer, void *out,
+                                         const void *q, const void *k_new, const void *v_new,
+                                         const int32_t *d_block_table, int32_t max_blocks,
+                                         const int32_t *d_context_lens, int32_t B, float scale,
+                                         void *workspace, size_t ws_bytes, kvp_stream stream);
 
 /* The same decode over a contiguous cache k_cache / v_cache [B][H_kv][Lmax][d] (one layer;
  * the layout of the cache tensors in [CHAP]'s allocator check).  Same kernels, same split

@@ -105,9 +105,10 @@ _sig("kv_copy_blocks", _i32, [ctypes.POINTER(kvp_cache_desc), _p, _i32, _p])
 _sig("kv_append", _i32, [ctypes.POINTER(kvp_cache_desc), _i32, _p, _p, _p, _i32, _p])
 _sig("contiguous_kv_append", _i32, [ctypes.POINTER(kvp_dims), _p, _p, _i32, _p, _p, _p, _i32, _p])
 _sig("decode_workspace_bytes", _sz, [ctypes.POINTER(kvp_dims), _i32, _i32])
-_sig("decode_num_splits", _i32, [_i32])
 _sig("paged_decode_attention", _i32, [ctypes.POINTER(kvp_cache_desc), _i32, _p, _p, _p, _i32, _p,
                                       _i32, _f32, _p, _sz, _p])
+_sig("paged_decode_append_attention", _i32, [ctypes.POINTER(kvp_cache_desc), _i32, _p, _p, _p, _p, _p, _i32,
+                                             _p, _i32, _f32, _p, _sz, _p])
 _sig("contiguous_decode_attention", _i32, [ctypes.POINTER(kvp_dims), _p, _p, _p, _p, _i32, _p, _i32,
                                            _f32, _p, _sz, _p])
 _sig("varlen_causal_prefill", _i32, [ctypes.POINTER(kvp_dims), _p, _p, _p, _p, _p, _i32, _i32, _i32,
@@ -351,19 +352,16 @@ def contiguous_kv_append(k_cache, v_cache, k, v, pos, num_q_heads=None, stream=N
                                      _dev(pos, "pos", torch.int32), B, _stream(stream)))
 
 
-def decode_num_splits(context_len):
-    return int(_lib.decode_num_splits(int(context_len)))
-
-
 def decode_workspace_bytes(num_q_heads, num_kv_heads, dtype, B, max_context):
     dm = dims(1, num_q_heads, num_kv_heads, dtype)
     return int(_lib.decode_workspace_bytes(ctypes.byref(dm), int(B), int(max_context)))
 
 
 def make_workspace(num_q_heads, num_kv_heads, dtype, B, max_context, device="cuda"):
-    """Decode workspace, zero-filled as the C ABI requires before first use."""
+    """Decode workspace, zero-filled as the C ABI requires before first use (torch's
+    allocator returns 256-byte aligned blocks)."""
     n = decode_workspace_bytes(num_q_heads, num_kv_heads, dtype, B, max_context)
-    return torch.zeros((max(n, 16),), dtype=torch.uint8, device=device)
+    return torch.zeros((max(n, 256),), dtype=torch.uint8, device=device)
 
 
 def paged_decode_attention(cache: PagedKVCache, layer, q, block_table, context_lens, out=None,
@@ -385,6 +383,31 @@ def paged_decode_attention(cache: PagedKVCache, layer, q, block_table, context_l
                                        max_blocks, _dev(context_lens, "context_lens", torch.int32), B,
                                        float(scale), _dev(workspace, "workspace"), workspace.numel(),
                                        _stream(stream)))
+    return out
+
+
+def paged_decode_append_attention(cache: PagedKVCache, layer, q, k_new, v_new, block_table, context_lens,
+                                  out=None, scale=0.0, workspace=None, stream=None):
+    """Fused step: k_new / v_new [B, H_kv, 64] go to position context_lens[b] - 1 of each
+    request (through block_table) and the decode of q attends over them in the same call."""
+    B, hq, d = q.shape
+    if hq != cache.num_q_heads or d != HEAD_DIM:
+        raise ValueError("paged_decode_append_attention: q shape does not match the cache")
+    if k_new.shape != (B, cache.num_kv_heads, HEAD_DIM) or v_new.shape != k_new.shape:
+        raise ValueError("paged_decode_append_attention: k_new / v_new shape mismatch")
+    max_blocks = block_table.shape[1]
+    if block_table.shape[0] != B or context_lens.shape != (B,):
+        raise ValueError("paged_decode_append_attention: table / context_lens shape mismatch")
+    if out is None:
+        out = torch.empty_like(q)
+    if workspace is None:
+        workspace = make_workspace(hq, cache.num_kv_heads, cache.dtype, B, max_blocks * BLOCK, q.device)
+    _check(_lib.paged_decode_append_attention(ctypes.byref(cache.desc), int(layer), _dev(out, "out", cache.dtype),
+                                              _dev(q, "q", cache.dtype), _dev(k_new, "k_new", cache.dtype),
+                                              _dev(v_new, "v_new", cache.dtype),
+                                              _dev(block_table, "block_table", torch.int32), max_blocks,
+                                              _dev(context_lens, "context_lens", torch.int32), B, float(scale),
+                                              _dev(workspace, "workspace"), workspace.numel(), _stream(stream)))
     return out
 
 

@@ -245,20 +245,41 @@ def test_deterministic_repeat():
     assert torch.equal(_bits(a.cpu()), _bits(b.cpu()))
 
 
-def test_split_and_unsplit_agree(monkeypatch):
+@pytest.mark.parametrize("workers", ["1", "7", "64", "333"])
+def test_worker_counts_agree(monkeypatch, workers):
+    # different worker counts cut the pairs at different tiles (and 1 worker splits none)
     need_gpu()
-    pb = W.uniform_batch(4, 3000)
+    pb = W.paged_batch(12, lo=1, hi=3000, prefix=0, group_size=1, seed=55)
     step = PagedStep(kvp, pb, layers=1, hq=14, hkv=2, dtype=torch.float16, seed=7000)
     q = step.q(0).cuda()
-    outs = {}
-    for tokens in ("256", "512", "1024"):
-        monkeypatch.setenv("KVP_SPLIT_TOKENS", tokens)
-        assert kvp.decode_num_splits(3001) == math.ceil(3001 / int(tokens))
-        outs[tokens] = to64(kvp.paged_decode_attention(step.cache, 0, q, step.table, step.ctx))
-    want = step.oracle(0)
-    for t, o in outs.items():
-        assert max_abs(o, want) <= 2e-3, t
-    assert max_abs(outs["256"], outs["1024"]) <= 2e-3
+    monkeypatch.setenv("KVP_DECODE_WORKERS", workers)
+    say("workers", workers)
+    out = to64(kvp.paged_decode_attention(step.cache, 0, q, step.table, step.ctx))
+    assert max_abs(out, step.oracle(0)) <= 2e-3
+
+
+def test_fused_append_matches_separate_append():
+    need_gpu()
+    pb = W.paged_batch(40, seed=91)
+    say("fused append", pb.batch)
+    # two identical caches; the step's new rows are appended by the fused call in one and
+    # by kv_append in the other
+    a = PagedStep(kvp, pb, layers=2, hq=14, hkv=2, dtype=torch.float16, seed=8000)
+    b = PagedStep(kvp, pb, layers=2, hq=14, hkv=2, dtype=torch.float16, seed=8000)
+    kn = W.randn((pb.batch, 2, 64), 8101).cuda()
+    vn = W.randn((pb.batch, 2, 64), 8102).cuda()
+    # overwrite the new-token slots of cache a with garbage: the fused call must rewrite them
+    blk, row = a.new_slots // 16, a.new_slots % 16
+    a.cache.k_pool[1][blk, :, row] = float("nan")
+    a.cache.v_pool[1][blk, :, row] = float("nan")
+    q = a.q(1).cuda()
+    oa = kvp.paged_decode_append_attention(a.cache, 1, q, kn, vn, a.table, a.ctx)
+    kvp.kv_append(b.cache, 1, kn, vn, b.new_slots)
+    ob = kvp.paged_decode_attention(b.cache, 1, q, b.table, b.ctx)
+    torch.cuda.synchronize()
+    assert torch.equal(_bits(oa.cpu()), _bits(ob.cpu()))
+    assert torch.equal(_bits(a.cache.k_pool[1].cpu()), _bits(b.cache.k_pool[1].cpu()))
+    assert torch.equal(_bits(a.cache.v_pool[1].cpu()), _bits(b.cache.v_pool[1].cpu()))
 
 
 # ---------------------------------------------------------------------------------------
