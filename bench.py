@@ -7,10 +7,11 @@ uniform on 128..2048, groups of 8 consecutive requests sharing a 512-token prefi
 (copy-on-write), block ids scattered by a seeded shuffle of the free list.
 
 One step = the host block manager reserves one slot per request (copy-on-write pairs
-included), the copy-on-write block copies run, the block table / context lengths are
-uploaded, then for each of the 24 layers one fused kernel appends the new token's K/V and
-runs the paged decode attention over the whole cache (paged_decode_append_attention).
-Contexts grow by one token per step.
+included), the host planner turns the block table into the step's work plan (shared
+prefixes read once per group of members), the plan is uploaded and the copy-on-write block
+copies run, then for each of the 24 layers one kernel appends the new token's K/V and runs
+the paged decode attention over the whole cache (paged_decode_attention_planned, replayed
+as one captured graph).  Contexts grow by one token per step.
 
 Printed: one JSON line with the decode-attention KV throughput (unique bytes), steps/s,
 the roofline of the dominant kernel (the paged decode call: split-K partial + merge),
@@ -135,6 +136,7 @@ def main():
     ap.add_argument("--kernel-reps", type=int, default=4, help="rounds of per-layer decode timing")
     ap.add_argument("--no-graph", action="store_true", help="launch the 24 layers eagerly")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-share", action="store_true", help="plans without shared-prefix items")
     ap.add_argument("--seed", type=int, default=42)
     args = ap.parse_args()
 
@@ -164,26 +166,43 @@ def main():
     knew = W.randn_device((L, B, HKV, D), args.seed + 501, torch.float16, dev)
     vnew = W.randn_device((L, B, HKV, D), args.seed + 502, torch.float16, dev)
     out = torch.empty((L, B, HQ, D), dtype=torch.float16, device=dev)
-    ws = kvp.make_workspace(HQ, HKV, torch.float16, B, max_blocks * BLOCK, dev)
-    table_d = torch.empty((B, max_blocks), dtype=torch.int32, device=dev)
-    ctx_d = torch.empty((B,), dtype=torch.int32, device=dev)
-    slots_d = torch.empty((B,), dtype=torch.int64, device=dev)
     pairs_d = torch.empty((B, 2), dtype=torch.int32, device=dev)
     ids = torch.tensor(seqs, dtype=torch.int32)
+
+    # the step's work plan (host-built from the block table, shared by the 24 layers): the
+    # first plan fixes the item count (with room to grow) so every later plan launches the
+    # same way and one captured graph replays all steps
+    share = not args.no_share
+    t0h = torch.empty((B, max_blocks), dtype=torch.int32)
+    c0h = torch.empty((B,), dtype=torch.int32)
+    probe_slots = torch.empty((B,), dtype=torch.int64)
+    cows = (kvp.kvp_copy * B)()
+    pool.export_raw(ids.data_ptr(), B, max_blocks, t0h.data_ptr(), c0h.data_ptr())
+    c0h += total_steps + 1  # the longest contexts of this run (plan sizing only)
+    plan0, _ = kvp.decode_plan_build(HQ, HKV, t0h, c0h, cache.num_blocks, share_prefix=share)
+    pad_items = plan0.n_items + 64
+    img_bytes = kvp.decode_plan_bytes(HQ, HKV, B, max_blocks, pad_items)
     hb = [dict(table=torch.empty((B, max_blocks), dtype=torch.int32).pin_memory(),
                ctx=torch.empty((B,), dtype=torch.int32).pin_memory(),
                slots=torch.empty((B,), dtype=torch.int64).pin_memory(),
-               pairs=torch.empty((B, 2), dtype=torch.int32).pin_memory()) for _ in range(2)]
+               pairs=torch.empty((B, 2), dtype=torch.int32).pin_memory(),
+               image=torch.empty((img_bytes,), dtype=torch.uint8).pin_memory(),
+               plan=kvp.kvp_decode_plan()) for _ in range(2)]
+    plan_d = torch.empty((img_bytes,), dtype=torch.uint8, device=dev)
+    slot_cap = 2 * plan0.n_slots + B * HKV
+    ws_plan = kvp.kvp_decode_plan()
+    ws_plan.B, ws_plan.num_kv_heads, ws_plan.n_slots = B, HKV, slot_cap
+    ws = torch.zeros((max(kvp.decode_plan_workspace_bytes(ws_plan), 256),), dtype=torch.uint8, device=dev)
     done = [torch.cuda.Event(), torch.cuda.Event()]
-    cows = (kvp.kvp_copy * B)()
     stream = torch.cuda.current_stream()
+    launch_plan = [None]
 
     def layers_body():
         # per layer: the new token's K/V go into the cache and the decode attends over it,
-        # in one fused kernel (equivalent to kv_append + paged_decode_attention)
+        # in one kernel following the step's plan
         for l in range(L):
-            kvp.paged_decode_append_attention(cache, l, q[l], knew[l], vnew[l], table_d, ctx_d, out=out[l],
-                                              workspace=ws)
+            kvp.paged_decode_attention_planned(cache, l, q[l], launch_plan[0], plan_d, k_new=knew[l], v_new=vnew[l],
+                                               out=out[l], workspace=ws)
 
     graph = None
     record = []
@@ -199,11 +218,19 @@ def main():
                 h["pairs"][npairs, 1] = cows[i].dst
                 npairs += 1
         pool.export_raw(ids.data_ptr(), B, max_blocks, h["table"].data_ptr(), h["ctx"].data_ptr())
+        plan, _ = kvp.decode_plan_build(HQ, HKV, h["table"], h["ctx"], cache.num_blocks, share_prefix=share,
+                                        image=h["image"], pad_items=pad_items, plan=h["plan"])
+        if launch_plan[0] is None:  # the launch arguments: this layout, slots up to slot_cap
+            launch_plan[0] = kvp.kvp_decode_plan.from_buffer_copy(plan)
+            launch_plan[0].n_slots = slot_cap
+        lp = launch_plan[0]
+        assert plan.n_slots <= slot_cap, "workspace too small for this step's plan"
+        assert (plan.n_items, plan.off_pair_base, plan.off_req_shared) == (lp.n_items, lp.off_pair_base,
+                                                                           lp.off_req_shared)
         if keep:
-            record.append((h["table"].numpy().copy(), h["ctx"].numpy().copy(), npairs))
-        table_d.copy_(h["table"], non_blocking=True)
-        ctx_d.copy_(h["ctx"], non_blocking=True)
-        slots_d.copy_(h["slots"], non_blocking=True)
+            record.append((h["table"].numpy().copy(), h["ctx"].numpy().copy(), npairs, plan.n_shared,
+                           plan.kv_blocks_read))
+        plan_d[: plan.bytes].copy_(h["image"][: plan.bytes], non_blocking=True)
         if npairs:
             pairs_d[:npairs].copy_(h["pairs"][:npairs], non_blocking=True)
             kvp.kv_copy_blocks(cache, pairs_d[:npairs])
@@ -235,10 +262,10 @@ def main():
     ms_per_step = (t1 - t0) * 1e3 / args.steps
 
     # bytes of the timed steps
-    uniq_tok = [unique_and_logical_tokens(t, c) for t, c, _ in record]
+    uniq_tok = [unique_and_logical_tokens(t, c) for t, c, _, _, _ in record]
     uniq_bytes_step = np.mean([u for u, _ in uniq_tok]) * KV_TOKEN_LAYER_BYTES * L
     logical_bytes_step = np.mean([lg for _, lg in uniq_tok]) * KV_TOKEN_LAYER_BYTES * L
-    cow_blocks = sum(n for _, _, n in record)
+    cow_blocks = sum(r[2] for r in record)
     value = uniq_bytes_step / (ms_per_step * 1e-3) / 1e9
     logical_gbps = logical_bytes_step / (ms_per_step * 1e-3) / 1e9
     print(f"[bench] {ms_per_step:.4f} ms/step, unique {uniq_bytes_step / 1e9:.3f} GB/step -> {value:.1f} GB/s, "
@@ -247,7 +274,7 @@ def main():
     # ---- dominant kernel: the paged decode call, timed per call with HIP events on the
     # stream it runs on; layers are cycled so each call reads cold data (the 24-layer
     # working set is far larger than the on-chip caches) ----
-    table_last, ctx_last, _ = record[-1]
+    table_last, ctx_last, _, n_shared_last, blocks_read_last = record[-1]
     call_bytes, call_uniq, call_logical = decode_call_bytes(table_last, ctx_last, B)
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(args.kernel_reps * L)]
@@ -256,7 +283,8 @@ def main():
     for r in range(args.kernel_reps):
         for l in range(L):
             evs[i][0].record(stream)
-            kvp.paged_decode_attention(cache, l, q[l], table_d, ctx_d, out=out[l], workspace=ws)
+            kvp.paged_decode_attention_planned(cache, l, q[l], launch_plan[0], plan_d, k_new=knew[l],
+                                               v_new=vnew[l], out=out[l], workspace=ws)
             evs[i][1].record(stream)
             i += 1
     torch.cuda.synchronize()
@@ -295,8 +323,11 @@ def main():
         "logical_GB_per_step": round(logical_bytes_step / 1e9, 4),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
-                     "kernel": "paged_decode_attention (decode_f16_kernel, split merge fused)",
+                     "kernel": "paged_decode_attention_planned (decode_f16_kernel: append + attention + "
+                               "split merge)",
                      "bytes_per_launch": int(call_bytes), "avg_launch_us": round(avg_ms * 1e3, 3)},
+        "plan": {"items": int(launch_plan[0].n_items), "shared_items": int(n_shared_last),
+                 "kv_block_reads": int(blocks_read_last), "share_prefix": share},
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

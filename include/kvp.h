@@ -220,11 +220,12 @@ size_t decode_workspace_bytes(const kvp_dims *dims, int32_t B, int32_t max_conte
  *   0), 256-byte aligned and ZERO-FILLED before its first use; every call leaves its
  *   counters at zero again, so a workspace is reused without clearing.  Calls sharing a
  *   workspace must not overlap in time (one stream is fine).
- * Work split (fp16): the 64-token tiles of all (request, KV head) pairs are divided evenly
- * over a fixed set of worker waves (4 per compute unit, or KVP_DECODE_WORKERS); a pair
- * spread over several workers is merged by the last of them in a fixed order, so results
- * are deterministic for a given batch and worker count and identical between the paged and
- * contiguous layouts.  fp32 softmax and accumulation, one rounding to the output dtype. */
+ * Work split (fp16): each (request, KV head) pair is cut into splits of 32 blocks (512
+ * tokens), one wave each; a pair with several splits is merged by the last of its waves in
+ * split order, so results are deterministic and identical between the paged and
+ * contiguous layouts.  fp32 softmax and accumulation; the softmax weights enter the value
+ * product rounded once to fp16 (the normaliser sums the same rounded weights); one
+ * rounding to the output dtype. */
 kvp_status paged_decode_attention(const kvp_cache_desc *cache, int32_t layer, void *out,
                                   const void *q, const int32_t *d_block_table,
                                   int32_t max_blocks, const int32_t *d_context_lens, int32_t B,
@@ -251,6 +252,72 @@ kvp_status contiguous_decode_attention(const kvp_dims *dims, void *out, const vo
                                        const void *k_cache, const void *v_cache, int32_t Lmax,
                                        const int32_t *d_context_lens, int32_t B, float scale,
                                        void *workspace, size_t ws_bytes, kvp_stream stream);
+
+/* --------------------------------------------------------------------------------------
+ * Planned decode: a host-built work plan, built once per step from the host copy of the
+ * block table and shared by every layer of that step.  Requests that are consecutive in
+ * the batch and whose tables start with the same physical blocks (sequences forked from
+ * one prefix, [PAGED] SECTION 3; [CHAP] PagedAttention passage on shared prefixes) get
+ * that prefix read ONCE per KV head: one work item scores the K/V tiles of the shared
+ * blocks against the query rows of every member (up to 16 members and 64 query rows),
+ * each member up to its own limit, and the member's partial joins the partials of its
+ * private blocks in the same merge as any other split.  Same result as
+ * paged_decode_attention up to the order of the fp32 sums; without sharing
+ * (flags = 0) the plan reproduces paged_decode_attention's splits exactly, bit for bit.
+ * ------------------------------------------------------------------------------------ */
+#define KVP_PLAN_SHARE_PREFIX 1u
+
+typedef struct {
+    int32_t B;            /* batch the plan was built for                            */
+    int32_t num_kv_heads;
+    int32_t group;        /* query heads per KV head                                 */
+    int32_t num_blocks;   /* block ids in the plan are < num_blocks                  */
+    int32_t n_items;      /* work items (one wave each)                              */
+    int32_t n_shared;     /* of which read a shared prefix for several requests      */
+    int64_t n_slots;      /* partial slots the workspace must hold                   */
+    int64_t bytes;        /* bytes of the plan image (device copy)                   */
+    int64_t off_pair_base, off_pair_nparts, off_req_shared; /* offsets in the image  */
+    int64_t kv_blocks_read; /* (block, KV head) reads the plan performs               */
+} kvp_decode_plan;
+
+/* Upper bound of the plan image bytes for B requests of at most max_blocks blocks, or for
+ * pad_items items if that is larger (0 if the arguments are invalid). */
+size_t decode_plan_bytes(const kvp_dims *dims, int32_t B, int32_t max_blocks, int32_t pad_items);
+
+/* Build a plan on the host.  h_block_table: host int32 [B][max_blocks]; h_context_lens:
+ * host int32 [B] (the lengths the decode will use, i.e. with this step's token); entries
+ * outside 0..num_blocks-1 are recorded as unusable (their rows are masked).  flags:
+ * KVP_PLAN_SHARE_PREFIX to read shared prefixes once (0: plain per-request splits).
+ * pad_items: 0, or a fixed item count (rounded up to a multiple of 8): the image then has
+ * exactly that many items (the rest are empty) and offsets that depend only on pad_items,
+ * B and the head shape, so that successive steps' plans launch identically (a captured
+ * graph can be replayed with a new image in the same device buffer); INVALID if the step
+ * needs more items.  h_image: host buffer of image_bytes >= decode_plan_bytes(...)
+ * receiving the image; the caller copies plan->bytes of it to device memory (16-byte
+ * aligned) before the decode.  UNSUPPORTED for fp32 (the planned kernel is fp16) or a
+ * group size above 8. */
+kvp_status decode_plan_build(const kvp_dims *dims, const int32_t *h_block_table,
+                             int32_t max_blocks, const int32_t *h_context_lens, int32_t B,
+                             int32_t num_blocks, uint32_t flags, int32_t pad_items,
+                             void *h_image, size_t image_bytes, kvp_decode_plan *plan);
+
+/* Workspace bytes the planned decode needs for this plan (0 if it needs none).  The layout
+ * (per-pair counters first, then partials) depends only on B and the head shape, so a
+ * larger workspace serves later plans of the same batch. */
+size_t decode_plan_workspace_bytes(const kvp_decode_plan *plan);
+
+/* paged_decode_attention (k_new = v_new = NULL) or paged_decode_append_attention (both
+ * given) following a plan.  d_plan: device copy of the plan image; the plan must have
+ * been built from this step's block table and context lengths and for this cache
+ * (num_blocks <= cache->num_blocks, same head shape).  The block table itself is not
+ * read: its entries are in the plan.  workspace: decode_plan_workspace_bytes(plan) bytes,
+ * same rules as paged_decode_attention.  The new token's block must be private (copy-on-
+ * write done) -- the plan never treats a context's last block as shared. */
+kvp_status paged_decode_attention_planned(const kvp_cache_desc *cache, int32_t layer,
+                                          void *out, const void *q, const void *k_new,
+                                          const void *v_new, const kvp_decode_plan *plan,
+                                          const void *d_plan, float scale, void *workspace,
+                                          size_t ws_bytes, kvp_stream stream);
 
 /* Packed variable-length prefill ([XF] section 4, [XF] 5 for the head map).  Segment s
  * covers packed rows d_cu_seqlens[s] .. d_cu_seqlens[s+1]-1.  Row i of a segment attends

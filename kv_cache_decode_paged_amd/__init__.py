@@ -66,6 +66,16 @@ class kvp_pool_stats(ctypes.Structure):
                 ("num_seqs", ctypes.c_int32), ("utilisation_pct", ctypes.c_double)]
 
 
+class kvp_decode_plan(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32), ("group", ctypes.c_int32),
+                ("num_blocks", ctypes.c_int32), ("n_items", ctypes.c_int32), ("n_shared", ctypes.c_int32),
+                ("n_slots", ctypes.c_int64), ("bytes", ctypes.c_int64), ("off_pair_base", ctypes.c_int64),
+                ("off_pair_nparts", ctypes.c_int64), ("off_req_shared", ctypes.c_int64),
+                ("kv_blocks_read", ctypes.c_int64)]
+
+
+PLAN_SHARE_PREFIX = 1
+
 _i32 = ctypes.c_int32
 _i64 = ctypes.c_int64
 _p = ctypes.c_void_p
@@ -109,6 +119,12 @@ _sig("paged_decode_attention", _i32, [ctypes.POINTER(kvp_cache_desc), _i32, _p, 
                                       _i32, _f32, _p, _sz, _p])
 _sig("paged_decode_append_attention", _i32, [ctypes.POINTER(kvp_cache_desc), _i32, _p, _p, _p, _p, _p, _i32,
                                              _p, _i32, _f32, _p, _sz, _p])
+_sig("decode_plan_bytes", _sz, [ctypes.POINTER(kvp_dims), _i32, _i32, _i32])
+_sig("decode_plan_build", _i32, [ctypes.POINTER(kvp_dims), _p, _i32, _p, _i32, _i32, ctypes.c_uint32, _i32, _p, _sz,
+                                 ctypes.POINTER(kvp_decode_plan)])
+_sig("decode_plan_workspace_bytes", _sz, [ctypes.POINTER(kvp_decode_plan)])
+_sig("paged_decode_attention_planned", _i32, [ctypes.POINTER(kvp_cache_desc), _i32, _p, _p, _p, _p,
+                                              ctypes.POINTER(kvp_decode_plan), _p, _f32, _p, _sz, _p])
 _sig("contiguous_decode_attention", _i32, [ctypes.POINTER(kvp_dims), _p, _p, _p, _p, _i32, _p, _i32,
                                            _f32, _p, _sz, _p])
 _sig("varlen_causal_prefill", _i32, [ctypes.POINTER(kvp_dims), _p, _p, _p, _p, _p, _i32, _i32, _i32,
@@ -408,6 +424,78 @@ def paged_decode_append_attention(cache: PagedKVCache, layer, q, k_new, v_new, b
                                               _dev(block_table, "block_table", torch.int32), max_blocks,
                                               _dev(context_lens, "context_lens", torch.int32), B, float(scale),
                                               _dev(workspace, "workspace"), workspace.numel(), _stream(stream)))
+    return out
+
+
+def decode_plan_bytes(num_q_heads, num_kv_heads, B, max_blocks, pad_items=0):
+    dm = dims(1, num_q_heads, num_kv_heads, torch.float16)
+    return int(_lib.decode_plan_bytes(ctypes.byref(dm), int(B), int(max_blocks), int(pad_items)))
+
+
+def _host_i32(t, name):
+    if t.device.type != "cpu" or t.dtype != torch.int32 or not t.is_contiguous():
+        raise ValueError(f"{name}: expected a contiguous host int32 tensor")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def decode_plan_build(num_q_heads, num_kv_heads, block_table, context_lens, num_blocks, share_prefix=True,
+                      image=None, pin=False, pad_items=0, plan=None):
+    """Build a decode plan on the host from the HOST block table [B, max_blocks] and context
+    lengths [B] (int32 CPU tensors).  Returns (plan, image): plan is a kvp_decode_plan, image
+    a uint8 CPU tensor whose first plan.bytes bytes are to be copied to the device.
+    pad_items > 0 fixes the item count (see decode_plan_build in kvp.h)."""
+    B, max_blocks = block_table.shape
+    if context_lens.shape != (B,):
+        raise ValueError("decode_plan_build: context_lens shape mismatch")
+    need = decode_plan_bytes(num_q_heads, num_kv_heads, B, max_blocks, pad_items)
+    if image is None:
+        image = torch.empty((max(need, 16),), dtype=torch.uint8, pin_memory=pin)
+    if image.device.type != "cpu" or image.dtype != torch.uint8:
+        raise ValueError("decode_plan_build: image must be a uint8 host tensor")
+    dm = dims(1, num_q_heads, num_kv_heads, torch.float16)
+    plan = kvp_decode_plan() if plan is None else plan
+    _check(_lib.decode_plan_build(ctypes.byref(dm), _host_i32(block_table, "block_table"), int(max_blocks),
+                                  _host_i32(context_lens, "context_lens"), int(B), int(num_blocks),
+                                  PLAN_SHARE_PREFIX if share_prefix else 0, int(pad_items),
+                                  ctypes.c_void_p(image.data_ptr()), image.numel(), ctypes.byref(plan)))
+    return plan, image
+
+
+def decode_plan_workspace_bytes(plan):
+    return int(_lib.decode_plan_workspace_bytes(ctypes.byref(plan)))
+
+
+def upload_plan(plan, image, device="cuda"):
+    """Device copy of a plan image (16-byte aligned torch allocation)."""
+    return image[: max(int(plan.bytes), 16)].to(device)
+
+
+def make_plan_workspace(plan, device="cuda"):
+    """Zero-filled workspace for paged_decode_attention_planned with this plan."""
+    return torch.zeros((max(decode_plan_workspace_bytes(plan), 256),), dtype=torch.uint8, device=device)
+
+
+def paged_decode_attention_planned(cache: PagedKVCache, layer, q, plan, d_plan, k_new=None, v_new=None,
+                                   out=None, scale=0.0, workspace=None, stream=None):
+    """Decode following a plan (decode_plan_build + upload_plan).  With k_new / v_new
+    ([B, H_kv, 64]) the step's token is appended in the same kernel."""
+    B, hq, d = q.shape
+    if hq != cache.num_q_heads or d != HEAD_DIM or B != plan.B:
+        raise ValueError("paged_decode_attention_planned: q shape does not match the cache / plan")
+    if (k_new is None) != (v_new is None):
+        raise ValueError("paged_decode_attention_planned: give both k_new and v_new or neither")
+    if k_new is not None and (k_new.shape != (B, cache.num_kv_heads, HEAD_DIM) or v_new.shape != k_new.shape):
+        raise ValueError("paged_decode_attention_planned: k_new / v_new shape mismatch")
+    if out is None:
+        out = torch.empty_like(q)
+    if workspace is None:
+        workspace = make_plan_workspace(plan, q.device)
+    kn = _dev(k_new, "k_new", cache.dtype) if k_new is not None else None
+    vn = _dev(v_new, "v_new", cache.dtype) if v_new is not None else None
+    _check(_lib.paged_decode_attention_planned(ctypes.byref(cache.desc), int(layer), _dev(out, "out", cache.dtype),
+                                               _dev(q, "q", cache.dtype), kn, vn, ctypes.byref(plan),
+                                               _dev(d_plan, "plan"), float(scale), _dev(workspace, "workspace"),
+                                               workspace.numel(), _stream(stream)))
     return out
 
 

@@ -6,7 +6,6 @@
 #include <algorithm>
 #include <cmath>
 #include <cstdlib>
-#include <mutex>
 
 #include "kvp_decode_common.h"
 
@@ -31,56 +30,27 @@ static kvp_status check_dims(const kvp_dims *d, const char *who)
     return KVP_OK;
 }
 
-// compute units of the current device (cached per device)
-static int device_cus()
-{
-    static std::mutex mu;
-    static int cache[64] = {0};
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
-        return 256;
-    std::lock_guard<std::mutex> lk(mu);
-    if (!cache[dev]) {
-        int n = 0;
-        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
-            n = 256;
-        cache[dev] = n;
-    }
-    return cache[dev];
-}
-
-// fp16 worker waves: 4 per CU (the LDS ring of one wave takes ~38 KB), and at least enough
-// that a chunk never exceeds 64 tiles; KVP_DECODE_WORKERS overrides the per-device default
-int decode_f16_workers(int B, int hkv, int max_context)
-{
-    const long long tiles_per_req = (std::max(max_context, 1) + TILE - 1) / TILE;
-    const long long tmax = (long long)B * hkv * tiles_per_req;
-    long long w = 4LL * device_cus();
-    if (const char *e = getenv("KVP_DECODE_WORKERS")) {
-        const long long v = atoll(e);
-        if (v > 0)
-            w = v;
-    }
-    w = std::max(w, (tmax + 63) / 64);
-    return (int)std::min<long long>(w, 0x7fffffff);
-}
-
 static size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
 static size_t part_bytes(const kvp_dims *d, int B, int max_context)
 {
-    if (d->dtype == KVP_F16)
-        return decode_f16_part_bytes(decode_f16_workers(B, d->num_kv_heads, max_context));
+    if (d->dtype == KVP_F16) {
+        const int ipp = decode_f16_items_per_pair(max_context);
+        return ipp > 1 ? decode_f16_part_bytes((long long)B * d->num_kv_heads * ipp) : 0;
+    }
     const int ms = decode_f32_max_splits(max_context);
     return ms > 1 ? decode_f32_part_bytes(B, d->num_q_heads, ms) : 0;
 }
+
+// workspace: [tickets: one int per (request, KV head), 256-byte aligned][partials]
+static size_t ticket_bytes(int B, int hkv) { return align256((size_t)B * hkv * sizeof(int)); }
 
 static size_t workspace_bytes(const kvp_dims *d, int B, int max_context)
 {
     const size_t pb = part_bytes(d, B, max_context);
     if (pb == 0)
         return 0;
-    return align256(pb) + align256((size_t)B * d->num_kv_heads * sizeof(int));
+    return ticket_bytes(B, d->num_kv_heads) + pb;
 }
 
 template <typename Addr>
@@ -124,7 +94,7 @@ static kvp_status decode_common(const kvp_dims *dims, void *out, const void *q, 
     P.scale_log2 = scale * LOG2E;
     P.part = nullptr;
     P.tickets = nullptr;
-    P.workers = dims->dtype == KVP_F16 ? decode_f16_workers(B, P.hkv, max_ctx) : decode_f32_max_splits(max_ctx);
+    P.workers = dims->dtype == KVP_F16 ? 0 : decode_f32_max_splits(max_ctx);
     const size_t pb = part_bytes(dims, B, max_ctx);
     if (pb > 0) {
         const size_t need = workspace_bytes(dims, B, max_ctx);
@@ -132,12 +102,13 @@ static kvp_status decode_common(const kvp_dims *dims, void *out, const void *q, 
             return fail(KVP_ERR_INVALID, "%s: workspace %zu bytes < %zu needed", who, ws_bytes, need);
         if ((uintptr_t)ws & 255)
             return fail(KVP_ERR_INVALID, "%s: workspace must be 256-byte aligned", who);
-        P.part = (float *)ws;
-        P.tickets = (int *)((char *)ws + align256(pb));
+        P.tickets = (int *)ws;
+        P.part = (float *)((char *)ws + ticket_bytes(B, dims->num_kv_heads));
     }
     const int group = P.hq / P.hkv;
     hipStream_t st_ = (hipStream_t)stream;
-    return dims->dtype == KVP_F16 ? launch_decode_f16(P, A, group, st_) : launch_decode_f32(P, A, group, st_);
+    return dims->dtype == KVP_F16 ? launch_decode_f16(P, A, group, max_ctx, st_)
+                                  : launch_decode_f32(P, A, group, st_);
 }
 
 static kvp_status paged_common(const kvp_cache_desc *cache, int32_t layer, void *out,
@@ -169,6 +140,13 @@ static kvp_status paged_common(const kvp_cache_desc *cache, int32_t layer, void 
     PagedAddr A{d_block_table, max_blocks, cache->dims.num_kv_heads, cache->num_blocks};
     return decode_common(&cache->dims, out, q, kc, vc, k_new, v_new, A, max_blocks * BS,
                          d_context_lens, B, scale, workspace, ws_bytes, stream, who);
+}
+
+static size_t plan_workspace_bytes(const kvp_decode_plan *plan)
+{
+    if (plan->n_slots <= 0)
+        return 0;
+    return ticket_bytes(plan->B, plan->num_kv_heads) + decode_f16_part_bytes(plan->n_slots);
 }
 
 } // namespace kvp
@@ -206,6 +184,74 @@ kvp_status paged_decode_append_attention(const kvp_cache_desc *cache, int32_t la
     return paged_common(cache, layer, out, q, k_new, v_new, d_block_table, max_blocks,
                         d_context_lens, B, scale, workspace, ws_bytes, stream,
                         "paged_decode_append_attention");
+}
+
+size_t decode_plan_workspace_bytes(const kvp_decode_plan *plan)
+{
+    return plan ? plan_workspace_bytes(plan) : 0;
+}
+
+kvp_status paged_decode_attention_planned(const kvp_cache_desc *cache, int32_t layer, void *out,
+                                          const void *q, const void *k_new, const void *v_new,
+                                          const kvp_decode_plan *plan, const void *d_plan, float scale,
+                                          void *workspace, size_t ws_bytes, kvp_stream stream)
+{
+    const char *who = "paged_decode_attention_planned";
+    if (!cache || !plan)
+        return fail(KVP_ERR_INVALID, "%s: cache / plan is NULL", who);
+    kvp_status st = check_dims(&cache->dims, who);
+    if (st != KVP_OK)
+        return st;
+    if (cache->dims.dtype != KVP_F16)
+        return fail(KVP_ERR_UNSUPPORTED, "%s: planned decode is implemented for fp16", who);
+    if (cache->block_size != BS)
+        return fail(KVP_ERR_UNSUPPORTED, "%s: block_size=%d (only 16)", who, cache->block_size);
+    if (layer < 0 || layer >= cache->dims.num_layers)
+        return fail(KVP_ERR_INVALID, "%s: layer %d out of range", who, layer);
+    const int hkv = cache->dims.num_kv_heads, group = cache->dims.num_q_heads / hkv;
+    if (plan->num_kv_heads != hkv || plan->group != group || plan->B < 0 || plan->n_items < 0 ||
+        plan->num_blocks <= 0 || plan->num_blocks > cache->num_blocks)
+        return fail(KVP_ERR_INVALID, "%s: plan (Hkv=%d group=%d num_blocks=%d) does not fit the cache "
+                    "(Hkv=%d group=%d num_blocks=%d)", who, plan->num_kv_heads, plan->group,
+                    plan->num_blocks, hkv, group, cache->num_blocks);
+    if (plan->B == 0 || plan->n_items == 0)
+        return KVP_OK;
+    if (!out || !q || !d_plan || !cache->k_pool || !cache->v_pool)
+        return fail(KVP_ERR_INVALID, "%s: NULL pointer argument", who);
+    if ((k_new == nullptr) != (v_new == nullptr))
+        return fail(KVP_ERR_INVALID, "%s: k_new and v_new must both be given or both be NULL", who);
+    if (((uintptr_t)out | (uintptr_t)q | (uintptr_t)k_new | (uintptr_t)v_new | (uintptr_t)d_plan) & 15)
+        return fail(KVP_ERR_INVALID, "%s: q/out/new-row/plan pointers must be 16-byte aligned", who);
+    const size_t need = plan_workspace_bytes(plan);
+    if (need > 0) {
+        if (!workspace || ws_bytes < need)
+            return fail(KVP_ERR_INVALID, "%s: workspace %zu bytes < %zu needed", who, ws_bytes, need);
+        if ((uintptr_t)workspace & 255)
+            return fail(KVP_ERR_INVALID, "%s: workspace must be 256-byte aligned", who);
+    }
+    const size_t layer_elems = (size_t)cache->num_blocks * hkv * BS * D;
+    DecodeParams P;
+    P.q = q;
+    P.out = out;
+    P.kc = (const f16 *)cache->k_pool + (size_t)layer * layer_elems;
+    P.vc = (const f16 *)cache->v_pool + (size_t)layer * layer_elems;
+    P.kc_w = const_cast<void *>(P.kc);
+    P.vc_w = const_cast<void *>(P.vc);
+    P.k_new = k_new;
+    P.v_new = v_new;
+    P.ctx_lens = nullptr;
+    P.B = plan->B;
+    P.hq = cache->dims.num_q_heads;
+    P.hkv = hkv;
+    if (scale == 0.f)
+        scale = 1.0f / sqrtf((float)D);
+    P.scale_log2 = scale * LOG2E;
+    P.workers = 0;
+    // tickets first: the layout does not depend on the plan's slot count
+    P.tickets = need > 0 ? (int *)workspace : nullptr;
+    P.part = need > 0 ? (float *)((char *)workspace + ticket_bytes(plan->B, hkv)) : nullptr;
+    PagedAddr A{nullptr, 0, hkv, plan->num_blocks};
+    return launch_decode_f16_planned(P, A, group, d_plan, *plan, (hipStream_t)stream);
 }
 
 kvp_status contiguous_decode_attention(const kvp_dims *dims, void *out, const void *q,

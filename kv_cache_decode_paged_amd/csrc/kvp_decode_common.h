@@ -46,6 +46,9 @@ struct PagedAddr {
     __device__ int max_ctx() const { return max_blocks * dec::BS; }
     // row to read for in-block row r (blocks always hold 16 rows)
     __device__ int row(int, int r) const { return r; }
+    // a block that is always readable (block 0 of KV head g), for rows that are masked
+    __device__ size_t safe_off(int, int g) const { return (size_t)g * (dec::BS * dec::D); }
+    __device__ int safe_row(int r) const { return r; }
 };
 
 struct ContigAddr {
@@ -61,6 +64,8 @@ struct ContigAddr {
     __device__ int max_ctx() const { return lmax; }
     // the last 16-row group of a slice may run past Lmax: clamp (such rows are masked)
     __device__ int row(int idx, int r) const { return min(idx * dec::BS + r, lmax - 1) - idx * dec::BS; }
+    __device__ size_t safe_off(int b, int g) const { return ((size_t)b * hkv + g) * lmax * dec::D; }
+    __device__ int safe_row(int r) const { return min(r, lmax - 1); }
 };
 
 // ---------------------------------------------------------------------------------------
@@ -152,21 +157,25 @@ struct DecodeParams {
     int hq;
     int hkv;
     float scale_log2;
-    int workers;       // fp16: number of worker waves (stream-K); fp32: max splits
+    int workers;       // fp32: max splits per pair
     float *part;       // partial results
     int *tickets;      // [B][Hkv], zero between calls
 };
 
 // launchers (one translation unit per kernel family)
-kvp_status launch_decode_f16(const DecodeParams &P, const PagedAddr &A, int group, hipStream_t st);
-kvp_status launch_decode_f16(const DecodeParams &P, const ContigAddr &A, int group, hipStream_t st);
+kvp_status launch_decode_f16(const DecodeParams &P, const PagedAddr &A, int group, int max_context,
+                             hipStream_t st);
+kvp_status launch_decode_f16(const DecodeParams &P, const ContigAddr &A, int group, int max_context,
+                             hipStream_t st);
+kvp_status launch_decode_f16_planned(const DecodeParams &P, const PagedAddr &A, int group,
+                                     const void *d_image, const kvp_decode_plan &plan, hipStream_t st);
 kvp_status launch_decode_f32(const DecodeParams &P, const PagedAddr &A, int group, hipStream_t st);
 kvp_status launch_decode_f32(const DecodeParams &P, const ContigAddr &A, int group, hipStream_t st);
 
-// workspace layout helpers (bytes), shared by the launchers and the size query
-size_t decode_f16_part_bytes(int workers);
+// workspace layout helpers (bytes), shared by the launchers and the size queries
+size_t decode_f16_part_bytes(long long slots);
+int decode_f16_items_per_pair(int max_context);
 size_t decode_f32_part_bytes(int B, int hq, int max_splits);
-int decode_f16_workers(int B, int hkv, int max_context);
 int decode_f32_max_splits(int max_context);
 
 } // namespace kvp

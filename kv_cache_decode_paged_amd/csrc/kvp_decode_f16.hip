@@ -1,12 +1,13 @@
-// kvp_decode_f16.hip -- fp16 grouped-query decode attention for gfx950: one fused kernel
-// per layer (optional append of the new token, attention over the whole cache, merge of
-// split partitions).
+// kvp_decode_f16.hip -- fp16 grouped-query decode attention for gfx950: one kernel per
+// layer that (optionally) appends the step's new token, attends over the cache and merges
+// split partitions.
 //
 // What is computed (pages cited by title and section):
 //   neuralialabs "Tornar a inferencia barata: KV cache, batching e quantizacao": decode
 //   feeds one token whose query attends over every cached key (a 1 x n score row);
 //   grouped-query attention shares each key-value head among a group of query heads;
-//   PagedAttention reaches the cache through a per-sequence table of fixed-size blocks.
+//   PagedAttention reaches the cache through a per-sequence table of fixed-size blocks,
+//   and forked sequences share their prefix blocks (copy-on-write).
 //   gustavoai "La cache de claves y valores", four-step token recipe: k_t, v_t are put at
 //   the end of each head's cache (step 2) before the attention row over the whole cache
 //   (step 3), so the new position sees itself.
@@ -16,546 +17,556 @@
 //   softmaxes keep their maximum and exponential sum and are merged by rescaling with
 //   e^(block max - global max) -- used across tiles and across split partitions.
 //
-// Work decomposition (stream-K): every (request, KV head) pair is cut into 64-token tiles
-// (4 blocks of 16); the tiles of all pairs, in pair order, form one sequence that is cut
-// into equal contiguous chunks, one per worker wave (4 per CU).  Load balance is within
-// one tile whatever the mix of context lengths.  A pair lying inside one chunk is finished
-// by that wave; a pair spread over several chunks leaves one partial (m, l, o) per chunk
-// and the last wave to finish (device-scope ticket) merges them in chunk order, so the
-// result is deterministic.  Partials travel through relaxed device-scope atomics (sc1
-// stores / loads) ordered by a store-completion wait: no L2 write-back is needed.
+// Work decomposition: one wave per work item.  An item is up to 32 consecutive 16-token
+// blocks (8 tiles of 64 tokens) of one KV head, either of one request ("private") or of a
+// few requests that share those physical blocks ("shared": the query rows of every member,
+// up to 16 rows, are scored against the same K/V tile).  The planner puts all shared items
+// of one prefix on one XCD close together in dispatch order, so the prefix is fetched
+// from HBM about once per step and served from that XCD's L2 to its other readers.  Items come from a host-built plan
+// (paged_decode_attention_planned) or, without a plan, from the wave index: request pair
+// (b, g), split k of ceil(blocks / 32).  A pair split over several items leaves one partial
+// (m, l, o) per item; the last item to finish (device-scope ticket) merges them in slot
+// order, so results are deterministic.  Partials travel through relaxed device-scope
+// atomics (coherent stores / loads) ordered by a store-completion wait.
 //
-// Per wave: K, V and q tiles stream HBM -> LDS through global_load_lds_dwordx4 into a ring
-// of NBUF slots (16 KB per tile); waits are explicit vmcnt counts (17 loads per tile).
-// Scores S^T = K Q^T run on the matrix cores (v_mfma_f32_16x16x32_f16, exact fp16 products,
-// fp32 sums); softmax in fp32 with the hardware exp2; p*v on the vector ALUs in fp32 with
-// v_fma_mix_f32 reading fp16 values straight from LDS.
+// Per wave: K and V tiles stream HBM -> LDS through global_load_lds_dwordx4 into a ring of
+// NBUF slots (16 KB per tile, 16 loads); waits are explicit vmcnt counts.
+//   scores  S^T = K Q^T       v_mfma_f32_16x16x32_f16, K rows from LDS (chunk-swizzled),
+//                             query rows as one 16-column block
+//   softmax fp32, hardware exp2, running max / sum per query row, p rounded once to fp16
+//   values  O^T = V^T P^T     v_mfma_f32_16x16x32_f16; P^T is the score MFMA's own output
+//                             layout (no data movement), V^T is built per lane from
+//                             8-byte LDS reads (4 dims x 8 tokens) and byte permutes.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
 #include <cmath>
 
 #include "kvp_decode_common.h"
+#include "kvp_plan_format.h"
 
 namespace kvp {
 
 using namespace dec;
+using namespace plan;
 
-constexpr int QB = MAXG * D * 2; // bytes of one q slot
-constexpr int TB = TILE * D * 2; // bytes of one K (or V) tile
+constexpr int TB = TILE * D * 2;   // bytes of one K (or V) tile in LDS
 constexpr int PART_FLOATS = D + 2; // o[64], m, l
-constexpr int DMA_PER_TILE = 18;   // 8 K + 8 V + 1 q + 1 new-token row
-
-__device__ inline int wave_sum_i(int x)
-{
-    x += __builtin_amdgcn_update_dpp(x, x, 0xB1, 0xf, 0xf, false);
-    x += __builtin_amdgcn_update_dpp(x, x, 0x4E, 0xf, 0xf, false);
-    x += __builtin_amdgcn_update_dpp(x, x, 0x141, 0xf, 0xf, false);
-    x += __builtin_amdgcn_update_dpp(x, x, 0x140, 0xf, 0xf, false);
-    x += __builtin_amdgcn_update_dpp(x, x, 0x142, 0xa, 0xf, false);
-    x += __builtin_amdgcn_update_dpp(x, x, 0x143, 0xc, 0xf, false);
-    return __builtin_amdgcn_readlane(x, 63);
-}
-
-// inclusive prefix sum over the 64 lanes (row_shr steps inside rows, then row broadcasts)
-__device__ inline int wave_incl_scan_i(int x)
-{
-    x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false); // row_shr:1
-    x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, false); // row_shr:2
-    x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, false); // row_shr:4
-    x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, false); // row_shr:8
-    x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false); // row_bcast:15
-    x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false); // row_bcast:31
-    return x;
-}
+constexpr int DMA_PER_TILE = 16;   // 8 K + 8 V loads of 1 KB
 
 // s_waitcnt with only the vector-memory count set (gfx9 encoding: vmcnt in bits 3:0 and
-// 15:14, expcnt 6:4 and lgkmcnt 11:8 left at their maxima); issued through the builtin so
-// that the compiler's own wait insertion knows about it
+// 15:14, expcnt 6:4 and lgkmcnt 11:8 left at their maxima)
 template <int N> __device__ inline void wait_vm()
 {
     static_assert(N >= 0 && N < 64, "vmcnt range");
     constexpr int imm = (N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8);
     __builtin_amdgcn_s_waitcnt(imm);
 }
+// s_waitcnt lgkmcnt(0): every LDS access of the wave has completed
+__device__ inline void wait_lds() { __builtin_amdgcn_s_waitcnt(0xF | (3 << 14) | (7 << 4)); }
 
-// number of tiles of a request (context clamped to [1, max_ctx])
-__device__ inline int tiles_of(int ctx, int maxc)
+__device__ inline int lane_int(int v, int l) { return __builtin_amdgcn_readlane(v, l); }
+
+// LDS reads of the DMA-filled ring, issued as inline assembly.  The compiler's wait
+// insertion cannot tell these reads from reads of the slot a DMA is still filling, so for a
+// plain LDS read it waits for every outstanding vector-memory operation -- the prefetched
+// tiles included.  The ring is ordered by the explicit vmcnt waits instead; the results
+// are tied to an explicit lgkmcnt(0) before use (lds_ready).
+__device__ inline unsigned lds_addr(const char *p)
 {
-    ctx = ctx < 1 ? 1 : (ctx > maxc ? maxc : ctx);
-    return (ctx + TILE - 1) / TILE;
+    return (unsigned)(uintptr_t)(const __attribute__((address_space(3))) char *)p;
+}
+__device__ inline f16x8 lds_b128(const char *p)
+{
+    f16x8 r;
+    asm volatile("ds_read_b128 %0, %1" : "=v"(r) : "v"(lds_addr(p)));
+    return r;
+}
+__device__ inline uint2 lds_b64(const char *p)
+{
+    uint2 r;
+    asm volatile("ds_read_b64 %0, %1" : "=v"(r) : "v"(lds_addr(p)));
+    return r;
 }
 
-// worker owning flattened tile x: chunks are [floor(w T / W), floor((w+1) T / W))
-__device__ inline int owner_of(long long x, long long T, int W)
+// V^T operand of one k-step for dim 4 col + db: lane (col, grp) read dims 4col..4col+3 of
+// the 8 tokens of its k-group as 64-bit words (lo: dims 0-1, hi: dims 2-3); dword w of the
+// operand packs tokens 2w, 2w+1
+__device__ inline f16x8 vt_operand(const unsigned (&lo)[8], const unsigned (&hi)[8], int db)
 {
-    return (int)(((x + 1) * W + T - 1) / T) - 1;
+    const unsigned sel = (db & 1) ? 0x07060302u : 0x05040100u;
+    const unsigned *src = (db >> 1) ? hi : lo;
+    unsigned w[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+        w[k] = __builtin_amdgcn_perm(src[2 * k + 1], src[2 * k], sel);
+    return __builtin_bit_cast(f16x8, (i32x4){(int)w[0], (int)w[1], (int)w[2], (int)w[3]});
 }
-__device__ inline long long chunk_begin(int w, long long T, int W) { return (long long)w * T / W; }
 
-template <int G, int NBUF, typename Addr>
-__global__ __launch_bounds__(64) void decode_f16_kernel(DecodeParams P, Addr A)
+struct PlanView {
+    const int *items;       // planned: [n_items][REC]
+    const int *pair_base;   // planned: [B*Hkv]
+    const int *pair_nparts; // planned: [B*Hkv]
+    const int *req_shared;  // planned: [B]
+    int ipp;                // unplanned: items per pair
+};
+
+struct Item {
+    int b, g, nmem, blk0, nblk, end, slot, nparts, pbase;
+};
+
+// Merge the nparts partials of pair (b, g) (slots pbase ..) in slot order; lane = dim.
+template <int G>
+__device__ void merge_pair(const DecodeParams &P, int b, int g, int pbase, int nparts)
 {
-    static_assert(G >= 1 && G <= MAXG, "group size");
-    static_assert(NBUF == 2 || NBUF == 3, "ring depth");
-    __shared__ __attribute__((aligned(16))) char kring[NBUF][TB];
-    __shared__ __attribute__((aligned(16))) char vring[NBUF][TB];
-    __shared__ __attribute__((aligned(16))) char qring[NBUF][QB];
-    __shared__ __attribute__((aligned(16))) char nring[NBUF][1024]; // new-token K (lanes 0-7), V (8-15)
-    __shared__ __attribute__((aligned(16))) float pbuf[TILE * MAXG];
-
     const int lane = threadIdx.x;
-    const int w = blockIdx.x;
-    const int hkv = P.hkv;
-    const int maxc = A.max_ctx();
-
-    // ---- 1. total number of tiles ----
-    long long T = 0;
-    for (int b0 = 0; b0 < P.B; b0 += 64) {
-        const int b = b0 + lane;
-        const int nt = b < P.B ? tiles_of(P.ctx_lens[b], maxc) : 0;
-        T += wave_sum_i(nt);
+    float M[G], L[G], O[G];
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+        M[h] = -INFINITY;
+        L[h] = 0.f;
+        O[h] = 0.f;
     }
-    T *= hkv;
-    // with fewer tiles than workers only the first T workers take part, so every chunk is
-    // non-empty and the workers sharing a pair are exactly its tiles' owners
-    const int W = (int)std::min<long long>(gridDim.x, T);
-    if (w >= W)
-        return;
-    const long long c0 = chunk_begin(w, T, W), c1 = chunk_begin(w + 1, T, W);
-
-    // ---- 2. request holding tile c0: the last b with hkv * prefix(b) <= c0 ----
-    int rb = 0;
-    long long rbase = 0; // tiles before request rb (all heads)
-    {
-        long long run = 0;
-        for (int b0 = 0; b0 < P.B; b0 += 64) {
-            const int b = b0 + lane;
-            const int nt = b < P.B ? tiles_of(P.ctx_lens[b], maxc) : 0;
-            const int incl = wave_incl_scan_i(nt);
-            const long long excl = run + (incl - nt);
-            const bool le = b < P.B && (long long)hkv * excl <= c0;
-            const unsigned long long bal = __ballot(le);
-            if (bal) {
-                const int hi = 63 - __builtin_clzll(bal);
-                rb = b0 + hi;
-                const int ex_lo = __builtin_amdgcn_readlane((int)(excl & 0xffffffff), hi);
-                const int ex_hi = __builtin_amdgcn_readlane((int)(excl >> 32), hi);
-                rbase = (long long)hkv * (((long long)ex_hi << 32) | (unsigned)ex_lo);
+    for (int j0 = 0; j0 < nparts; j0 += 4) {
+        float mv[4][G], lv[4][G], ov[4][G];
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+            const int j = min(j0 + jj, nparts - 1);
+#pragma unroll
+            for (int h = 0; h < G; ++h) {
+                const float *src = P.part + ((size_t)(pbase + j) * MAXG + h) * PART_FLOATS;
+                mv[jj][h] = coherent_load(src + D);
+                lv[jj][h] = coherent_load(src + D + 1);
+                ov[jj][h] = coherent_load(src + lane);
             }
-            run += __builtin_amdgcn_readlane(incl, 63);
+        }
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+            if (j0 + jj < nparts) {
+#pragma unroll
+                for (int h = 0; h < G; ++h) {
+                    const float mn = fmaxf(M[h], mv[jj][h]);
+                    if (mn != -INFINITY) {
+                        const float a = fast_exp2(M[h] - mn), c = fast_exp2(mv[jj][h] - mn);
+                        L[h] = L[h] * a + lv[jj][h] * c;
+                        O[h] = O[h] * a + ov[jj][h] * c;
+                        M[h] = mn;
+                    }
+                }
+            }
         }
     }
+    f16 *outp = (f16 *)P.out + ((size_t)b * P.hq + (size_t)g * G) * D;
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+        outp[h * D + lane] = (f16)(L[h] > 0.f ? O[h] / L[h] : 0.f);
+}
 
+// One work item.  rv: lane R_ENT + j holds the physical id of the item's block j.
+template <int G, int NQB, bool SHARED, int NBUF, typename Addr>
+__device__ __forceinline__ void run_item(const DecodeParams &P, const Addr &A, const PlanView &PV,
+                                         const Item &it, int rv, char (*kring)[TB], char (*vring)[TB])
+{
+    const int lane = threadIdx.x;
+    const int col = lane & 15, grp = lane >> 4;
+    const int hkv = P.hkv;
     const f16 *kc = (const f16 *)P.kc;
     const f16 *vc = (const f16 *)P.vc;
-    const int hl = lane & 15, grp = lane >> 4; // MFMA layout: head / token column, lane group
-    const int tg = lane >> 3, cv = lane & 7;   // value layout: token group, 16-byte chunk
 
-    // a cursor over the chunk: pair (b, g) with nt tiles starting at flattened index
-    // pstart; current tile t of the pair; the chunk's part of this pair ends at tile te
-    struct Cur {
-        int b, g, nt, ctx, t, te;
-        long long pstart;
-    };
-    auto cur_at = [&](int b, long long bbase, long long pos) -> Cur {
-        Cur c;
-        c.b = b;
-        const int ctx = P.ctx_lens[b];
-        c.ctx = ctx < 0 ? 0 : (ctx > maxc ? maxc : ctx);
-        c.nt = tiles_of(ctx, maxc);
-        const long long off = pos - bbase;
-        c.g = (int)(off / c.nt);
-        c.t = (int)(off - (long long)c.g * c.nt);
-        c.pstart = bbase + (long long)c.g * c.nt;
-        c.te = (int)std::min<long long>(c.nt, c.t + (c1 - pos));
-        return c;
-    };
-    // first tile of the next pair after the part of c that lies in the chunk
-    auto cur_next_pair = [&](const Cur &c) -> Cur {
-        const long long pos = c.pstart + c.nt;
-        if (c.g + 1 < hkv) {
-            Cur n = c;
-            n.g = c.g + 1;
-            n.pstart = pos;
-            n.t = 0;
-            n.te = (int)std::min<long long>(n.nt, c1 - pos);
-            return n;
-        }
-        return cur_at(c.b + 1, pos, pos);
-    };
-    const Cur first = cur_at(rb, rbase, c0);
-
-    // ---- 3. table entries of the whole chunk, flat: entry f = 4 * (tile - c0) + block ----
-    const int nflat = (int)std::min<long long>(4 * (c1 - c0), 256);
-    int ent[4] = {-1, -1, -1, -1};
-    if (A.paged) {
-        Cur c = first;
-        for (;;) {
-            const long long xs = c.pstart + c.t, xe = c.pstart + c.te; // chunk tiles of c
+    // ---- per query-row column: q operand, token limit, output slot ----
+    // column block nb, column col is query row r = 16 nb + col: member r / G, head r % G
+    f16x8 qop[NQB][2];
+    int lim[NQB], pb[NQB], np[NQB];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int f = lane + 64 * j;
-                const long long x = c0 + f / 4;
-                if (f < nflat && x >= xs && x < xe)
-                    ent[j] = A.entry(c.b, (int)(4 * (x - c.pstart)) + (f & 3));
-            }
-            if (xe >= c1)
-                break;
-            c = cur_next_pair(c);
+    for (int nb = 0; nb < NQB; ++nb) {
+        const int r = nb * 16 + col;
+        const int mem = r / G, hd = r - mem * G;
+        const bool cv = mem < it.nmem;
+        const int bm = it.b + (cv ? mem : 0);
+        const f16 *qp = (const f16 *)P.q + ((size_t)bm * P.hq + (size_t)it.g * G + hd) * D + grp * 8;
+        const f16x8 q0 = *(const f16x8 *)qp;
+        const f16x8 q1 = *(const f16x8 *)(qp + 32);
+        const f16x8 z = {0, 0, 0, 0, 0, 0, 0, 0};
+        qop[nb][0] = cv ? q0 : z;
+        qop[nb][1] = cv ? q1 : z;
+        if constexpr (SHARED) {
+            // a member takes part if its shared extent reaches into this item; its part
+            // index inside the pair's slot range is the item's R_SLOT
+            const int pair = bm * hkv + it.g;
+            const int l0 = PV.req_shared[bm], b0 = PV.pair_base[pair], n0 = PV.pair_nparts[pair];
+            const bool in = cv && l0 > BS * it.blk0;
+            lim[nb] = in ? l0 : 0;
+            pb[nb] = b0 + it.slot;
+            np[nb] = in ? n0 : 0;
+        } else {
+            lim[nb] = cv ? it.end : 0;
+            pb[nb] = it.slot;
+            np[nb] = it.nparts;
         }
-        wait_vm<0>(); // entries in registers before the stream starts
     }
-    auto ent_flat = [&](int f) -> int { // f uniform
-        if (f >= nflat)
-            return -1;
-        const int j = f >> 6, l = f & 63;
-        const int v = j == 0 ? ent[0] : (j == 1 ? ent[1] : (j == 2 ? ent[2] : ent[3]));
-        return __builtin_amdgcn_readlane(v, l);
-    };
+    // the step's new K / V row (lanes 0-7: K chunks, 8-15: V chunks)
+    const bool app = !SHARED && P.k_new != nullptr;
+    i32x4 nrow = {0, 0, 0, 0};
+    if (app && lane < 16) {
+        const f16 *src = (const f16 *)(lane < 8 ? P.k_new : P.v_new) + ((size_t)it.b * hkv + it.g) * D +
+                         (lane & 7) * 8;
+        nrow = *(const i32x4 *)src;
+    }
 
-    // ---- DMA of one tile (17 instructions, no lane masked off) ----
-    auto issue_tile = [&](const Cur &c, long long x, int slot) {
-        const int t = c.t;
-        const int fb = (int)(4 * (x - c0));
-        const int t0 = t * TILE; // first token of the tile in the pair
-        // an unusable block is read from a known-good one (its rows are masked later)
-        const int e0 = ent_flat(fb);
-        char *kdst = kring[slot];
-        char *vdst = vring[slot];
+    const int nt = (it.nblk + 3) >> 2;
+    auto ent = [&](int j) -> int { return lane_int(rv, R_ENT + min(j, BPI - 1)); };
+    auto block_ok = [&](int j) -> bool { return j < it.nblk && A.valid(ent(j)); };
+
+    // ---- DMA of tile t into ring slot t % NBUF (16 loads, no lane masked off) ----
+    auto issue = [&](int t) {
+        char *kd = kring[t % NBUF];
+        char *vd = vring[t % NBUF];
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            const int kb = i >> 1; // block of rows 8i .. 8i+7
-            const int e = ent_flat(fb + kb);
-            const int bi = 4 * t + kb;
-            const bool ok = t0 + kb * BS < c.ctx && A.valid(e);
-            const bool ok0 = A.valid(e0);
-            const size_t base = ok ? A.block_off(c.b, c.g, bi, e)
-                                   : (ok0 ? A.block_off(c.b, c.g, 4 * t, e0) : A.block_off(c.b, c.g, 0, 0));
-            const int bir = ok ? bi : (ok0 ? 4 * t : 0);
-            const int r = i * 8 + (lane >> 3);   // tile row of this lane
-            const int rr = A.row(bir, r & 15);
-            const int cg = (lane & 7) ^ (r & 7); // K chunk kept at this LDS slot
-            __builtin_amdgcn_global_load_lds((const void *)(kc + base + (size_t)rr * D + cg * 8),
-                                             (__attribute__((address_space(3))) void *)(kdst + i * 1024),
+            const int j = 4 * t + (i >> 1); // item block of tile rows 8i .. 8i+7
+            const int e = ent(j);
+            const bool ok = j < it.nblk && A.valid(e);
+            const int lb = it.blk0 + j;
+            const size_t base = ok ? A.block_off(it.b, it.g, lb, e) : A.safe_off(it.b, it.g);
+            // K: LDS row r, chunk slot (lane & 7) holds chunk (lane & 7) ^ (r & 7)
+            const int r = 8 * i + (lane >> 3);
+            const int rk = ok ? A.row(lb, r & 15) : A.safe_row(r & 15);
+            const int cg = (lane & 7) ^ (r & 7);
+            __builtin_amdgcn_global_load_lds((const void *)(kc + base + (size_t)rk * D + cg * 8),
+                                             (__attribute__((address_space(3))) void *)(kd + i * 1024),
                                              16, 0, 0);
-            __builtin_amdgcn_global_load_lds((const void *)(vc + base + (size_t)rr * D + (lane & 7) * 8),
-                                             (__attribute__((address_space(3))) void *)(vdst + i * 1024),
+            // V: LDS row slot r holds tile row r ^ ((r >> 2) & 1) (rows 4 apart land in
+            // different bank halves for the transposed 8-byte reads)
+            const int rvv = r ^ ((r >> 2) & 1);
+            const int rw = ok ? A.row(lb, rvv & 15) : A.safe_row(rvv & 15);
+            __builtin_amdgcn_global_load_lds((const void *)(vc + base + (size_t)rw * D + (lane & 7) * 8),
+                                             (__attribute__((address_space(3))) void *)(vd + i * 1024),
                                              16, 0, 0);
         }
-        // q rows of the group: lane 8h + c carries head h, chunk c (rows past G repeat row 0)
-        const int qh = (lane >> 3) < G ? (lane >> 3) : 0;
-        const f16 *qs = (const f16 *)P.q + ((size_t)c.b * P.hq + (size_t)c.g * G + qh) * D + (lane & 7) * 8;
-        __builtin_amdgcn_global_load_lds((const void *)qs, (__attribute__((address_space(3))) void *)qring[slot],
-                                         16, 0, 0);
-        // the step's new K / V row of this pair (read for every tile so that every tile
-        // costs the same number of loads; used only on the pair's last tile)
-        const void *ns = qs;
-        if (P.k_new) {
-            const size_t src = ((size_t)c.b * hkv + c.g) * D + (lane & 7) * 8;
-            ns = ((lane >> 3) & 1) ? (const void *)((const f16 *)P.v_new + src)
-                                   : (const void *)((const f16 *)P.k_new + src);
-        }
-        __builtin_amdgcn_global_load_lds(ns, (__attribute__((address_space(3))) void *)nring[slot], 16, 0, 0);
     };
 
-    float m = -INFINITY, lsum = 0.f;
-    float o[G][8];
-    auto reset_acc = [&]() {
-        m = -INFINITY;
-        lsum = 0.f;
+    float m[NQB], lsum[NQB];
+    f32x4 acc[NQB][4];
 #pragma unroll
-        for (int h = 0; h < G; ++h)
+    for (int nb = 0; nb < NQB; ++nb) {
+        m[nb] = -INFINITY;
+        lsum[nb] = 0.f;
 #pragma unroll
-            for (int e = 0; e < 8; ++e)
-                o[h][e] = 0.f;
-    };
-    reset_acc();
+        for (int db = 0; db < 4; ++db)
+            acc[nb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    // tokens >= rend hold no data for any column of this item
+    const int rend = SHARED ? BS * (it.blk0 + it.nblk) : it.end;
 
-    // ---- one tile: fix-ups, scores, softmax, p*v ----
-    auto compute_tile = [&](const Cur &c, long long x, int slot) {
-        const int t = c.t;
-        const int fb = (int)(4 * (x - c0));
-        const int t0 = t * TILE;
-        char *kt = kring[slot];
-        char *vt = vring[slot];
-        // rows that must not contribute: past the context, or in an unusable block
-        const int valid_rows = min(TILE, c.ctx - t0);
-        bool bad_block = false;
+    auto compute = [&](int t) {
+        char *kt = kring[t % NBUF];
+        char *vt = vring[t % NBUF];
+        const int tb = BS * (it.blk0 + 4 * t); // position of tile row 0
+        bool bok[4];
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb)
-            if (t0 + kb * BS < c.ctx && !A.valid(ent_flat(fb + kb)))
-                bad_block = true;
-        if (valid_rows < TILE || bad_block) {
-            // zero the value rows that get p = 0 (the cache may hold NaN there)
+            bok[kb] = block_ok(4 * t + kb);
+        // value rows that no column may use: zero them (the cache can hold NaN there)
+        if (tb + TILE > rend || !(bok[0] && bok[1] && bok[2] && bok[3])) {
 #pragma unroll
             for (int k = 0; k < 8; ++k) {
-                const int ch = lane + 64 * k, r = ch >> 3;
-                if (r >= valid_rows || !A.valid(ent_flat(fb + (k >> 1))))
+                const int ch = lane + 64 * k, rs = ch >> 3;
+                const int r = rs ^ ((rs >> 2) & 1);
+                const int kb = r >> 4;
+                const bool okb = kb == 0 ? bok[0] : (kb == 1 ? bok[1] : (kb == 2 ? bok[2] : bok[3]));
+                if (!(okb && tb + r < rend))
                     *(i32x4 *)(vt + ch * 16) = i32x4{0, 0, 0, 0};
             }
         }
         // the new token of this step: into LDS (this tile) and into the cache
-        if (P.k_new && c.ctx >= 1 && t == c.nt - 1) {
-            const int pos = c.ctx - 1, r = pos - t0;
-            const int e = ent_flat(fb + (r >> 4));
-            if (lane < 8 && A.valid(e)) {
-                const i32x4 kn = *(const i32x4 *)(nring[slot] + lane * 16);
-                const i32x4 vn = *(const i32x4 *)(nring[slot] + 128 + lane * 16);
-                *(i32x4 *)(kt + r * 128 + ((lane ^ (r & 7)) * 16)) = kn;
-                *(i32x4 *)(vt + r * 128 + lane * 16) = vn;
-                const int bi = pos / BS;
-                const size_t dst = A.block_off(c.b, c.g, bi, e) + (size_t)A.row(bi, pos % BS) * D + lane * 8;
-                *(i32x4 *)((f16 *)P.kc_w + dst) = kn;
-                *(i32x4 *)((f16 *)P.vc_w + dst) = vn;
+        if (app) {
+            const int pos = it.end - 1, r = pos - tb;
+            if (r >= 0 && r < TILE) {
+                const int j = 4 * t + (r >> 4);
+                const int e = ent(j);
+                if (lane < 16 && j < it.nblk && A.valid(e)) {
+                    const int c = lane & 7;
+                    const int lb = it.blk0 + j;
+                    const size_t dst = A.block_off(it.b, it.g, lb, e) + (size_t)A.row(lb, r & 15) * D + c * 8;
+                    if (lane < 8) {
+                        *(i32x4 *)(kt + r * 128 + ((c ^ (r & 7)) * 16)) = nrow;
+                        *(i32x4 *)((f16 *)P.kc_w + dst) = nrow;
+                    } else {
+                        const int rs = r ^ ((r >> 2) & 1);
+                        *(i32x4 *)(vt + rs * 128 + c * 16) = nrow;
+                        *(i32x4 *)((f16 *)P.vc_w + dst) = nrow;
+                    }
+                }
             }
         }
         wave_lds_sync();
-        // scores on the matrix cores: lane holds S[16kb + 4grp + i][head hl]
-        const char *qt = qring[slot];
-        f16x8 qop[2];
-#pragma unroll
-        for (int st = 0; st < 2; ++st) {
-            const f16x8 qv = *(const f16x8 *)(qt + (hl < G ? hl : 0) * 128 + (st * 4 + grp) * 16);
-            qop[st] = hl < G ? qv : f16x8{0, 0, 0, 0, 0, 0, 0, 0};
-        }
-        f32x4 sacc[4];
+
+        // operands of the whole tile: K rows (A of the score MFMA) and V^T (A of the value
+        // MFMA: lane (col, grp), k-step ks, slot s is token 16 (2 ks + s / 4) + 4 grp + s % 4)
+        f16x8 kop[4][2];
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) {
-            const int r = kb * 16 + hl;
-            sacc[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int st = 0; st < 2; ++st) {
-                const int ch = st * 4 + grp;
-                const f16x8 kop = *(const f16x8 *)(kt + r * 128 + ((ch ^ (r & 7)) * 16));
-                sacc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop, qop[st], sacc[kb], 0, 0, 0);
-            }
+            const int r = kb * 16 + col;
+            kop[kb][0] = lds_b128(kt + r * 128 + ((grp ^ (r & 7)) * 16));
+            kop[kb][1] = lds_b128(kt + r * 128 + (((4 + grp) ^ (r & 7)) * 16));
         }
-        float mt = -INFINITY;
+        uint2 vraw[2][8];
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
-            const bool okb = A.valid(ent_flat(fb + kb));
+        for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int r = kb * BS + grp * 4 + i;
-                const float xs = (okb && r < valid_rows) ? sacc[kb][i] * P.scale_log2 : -INFINITY;
-                sacc[kb][i] = xs;
-                mt = fmaxf(mt, xs);
+            for (int s = 0; s < 8; ++s) {
+                const int tok = 16 * (2 * ks + (s >> 2)) + 4 * grp + (s & 3);
+                const int rs = tok ^ ((tok >> 2) & 1);
+                vraw[ks][s] = lds_b64(vt + rs * 128 + col * 8);
             }
+        // all 24 reads have returned before any result is used
+        asm volatile("s_waitcnt lgkmcnt(0)"
+                     : "+v"(kop[0][0]), "+v"(kop[0][1]), "+v"(kop[1][0]), "+v"(kop[1][1]), "+v"(kop[2][0]),
+                       "+v"(kop[2][1]), "+v"(kop[3][0]), "+v"(kop[3][1]));
+        asm volatile(""
+                     : "+v"(vraw[0][0]), "+v"(vraw[0][1]), "+v"(vraw[0][2]), "+v"(vraw[0][3]), "+v"(vraw[0][4]),
+                       "+v"(vraw[0][5]), "+v"(vraw[0][6]), "+v"(vraw[0][7]), "+v"(vraw[1][0]), "+v"(vraw[1][1]),
+                       "+v"(vraw[1][2]), "+v"(vraw[1][3]), "+v"(vraw[1][4]), "+v"(vraw[1][5]), "+v"(vraw[1][6]),
+                       "+v"(vraw[1][7]));
+        f16x8 vop[2][4];
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            unsigned lo[8], hi[8];
+#pragma unroll
+            for (int s = 0; s < 8; ++s) {
+                lo[s] = vraw[ks][s].x;
+                hi[s] = vraw[ks][s].y;
+            }
+#pragma unroll
+            for (int db = 0; db < 4; ++db)
+                vop[ks][db] = vt_operand(lo, hi, db);
         }
-        mt = fmaxf(mt, lane_xor(mt, 16));
-        mt = fmaxf(mt, lane_xor(mt, 32));
-        const float mn = fmaxf(m, mt);
-        const float alpha = mn == -INFINITY ? 1.f : fast_exp2(m - mn);
-        m = mn;
-        float ps = 0.f;
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb)
+        for (int nb = 0; nb < NQB; ++nb) {
+            // scores: sacc[kb][i] = S[token 16 kb + 4 grp + i][query row 16 nb + col]
+            f32x4 sacc[4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float p = mn == -INFINITY ? 0.f : fast_exp2(sacc[kb][i] - mn);
-                sacc[kb][i] = p;
-                ps += p;
+            for (int kb = 0; kb < 4; ++kb) {
+                const f32x4 s0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop[kb][0], qop[nb][0],
+                                                                        f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+                sacc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop[kb][1], qop[nb][1], s0, 0, 0, 0);
             }
-        lsum = lsum * alpha + ps;
-        if (hl < MAXG) {
+            // softmax; the P^T operand of k-step ks, slot s is sacc[2 ks + s / 4][s % 4] --
+            // already in this lane
+            float mt = -INFINITY;
 #pragma unroll
             for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    pbuf[(kb * BS + grp * 4 + i) * MAXG + hl] = sacc[kb][i];
-        }
-        float al[G];
-        bool any = false;
+                for (int i = 0; i < 4; ++i) {
+                    const int tok = tb + kb * 16 + grp * 4 + i;
+                    const float x = (bok[kb] && tok < lim[nb]) ? sacc[kb][i] * P.scale_log2 : -INFINITY;
+                    sacc[kb][i] = x;
+                    mt = fmaxf(mt, x);
+                }
+            mt = fmaxf(mt, lane_xor(mt, 16));
+            mt = fmaxf(mt, lane_xor(mt, 32));
+            const float mn = fmaxf(m[nb], mt);
+            const float alpha = mn == -INFINITY ? 1.f : fast_exp2(m[nb] - mn);
+            m[nb] = mn;
+            float ps = 0.f;
+            f16x8 pop[2];
 #pragma unroll
-        for (int h = 0; h < G; ++h) {
-            al[h] = uniform_lane(alpha, h);
-            any |= al[h] != 1.f;
-        }
-        if (any) {
+            for (int ks = 0; ks < 2; ++ks) {
 #pragma unroll
-            for (int h = 0; h < G; ++h)
+                for (int s = 0; s < 8; ++s) {
+                    const float p = mn == -INFINITY ? 0.f : fast_exp2(sacc[2 * ks + (s >> 2)][s & 3] - mn);
+                    pop[ks][s] = (f16)p;
+                    ps += (float)pop[ks][s];
+                }
+            }
+            lsum[nb] = lsum[nb] * alpha + ps;
+            // values: acc[nb][db][i] = O[query row 16 nb + col][dim 16 grp + 4 i + db]
 #pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    o[h][e] *= al[h];
+            for (int db = 0; db < 4; ++db) {
+                acc[nb][db] *= alpha;
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks)
+                    acc[nb][db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vop[ks][db], pop[ks], acc[nb][db], 0, 0, 0);
+            }
         }
+        wait_lds(); // this slot is refilled by a later DMA
         wave_lds_sync();
-        // p * v: rows 8i + tg, dims 8cv .. 8cv+7
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int r = i * 8 + tg;
-            const f32x4 p0 = *(const f32x4 *)&pbuf[r * MAXG];
-            const f32x4 p1 = *(const f32x4 *)&pbuf[r * MAXG + 4];
-            const float pr[8] = {p0[0], p0[1], p0[2], p0[3], p1[0], p1[1], p1[2], p1[3]};
-            const f16x8 vh = *(const f16x8 *)(vt + r * 128 + cv * 16);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const float ve = (float)vh[e];
-#pragma unroll
-                for (int h = 0; h < G; ++h)
-                    o[h][e] = fmaf(pr[h], ve, o[h][e]);
-            }
-        }
-        wave_lds_sync(); // pbuf and this slot are rewritten later
     };
 
-    Cur pend = first; // a pair whose partial was stored and whose ticket is not yet taken
-    bool has_pend = false;
-    // ---- end of the chunk's part of a pair: a complete pair is written, otherwise a
-    // partial is stored (its ticket is taken after the next wait, see settle) ----
-    auto finish_pair = [&](const Cur &c, bool first_of_chunk) {
-#pragma unroll
-        for (int h = 0; h < G; ++h)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                float xv = o[h][e];
-                xv += dpp<0x128>(xv); // row_ror:8: lane ^ 8 inside 16-lane rows
-                xv += lane_xor(xv, 16);
-                xv += lane_xor(xv, 32);
-                o[h][e] = xv;
-            }
-        float lt = lsum;
-        lt += lane_xor(lt, 16);
-        lt += lane_xor(lt, 32);
-        // head h: max and sum sit in lane h; lanes with tg == h write head h
-        float mh = -INFINITY, lh = 0.f;
-        float oh[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-            oh[e] = 0.f;
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-            const float mu = uniform_lane(m, h), lu = uniform_lane(lt, h);
-            if (tg == h) {
-                mh = mu;
-                lh = lu;
-#pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    oh[e] = o[h][e];
-            }
-        }
-        const int pair = c.b * hkv + c.g;
-        f16 *outp = (f16 *)P.out + ((size_t)c.b * P.hq + (size_t)c.g * G) * D;
-        const bool whole = c.pstart >= c0 && c.pstart + c.nt <= c1;
-        if (whole) {
-            if (tg < G) {
-                const float inv = lh > 0.f ? 1.f / lh : 0.f;
-                f16x8 r;
-#pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    r[e] = (f16)(oh[e] * inv);
-                *(f16x8 *)(outp + tg * D + cv * 8) = r;
-            }
-            return;
-        }
-        const int slotp = first_of_chunk ? 0 : 1;
-        float *mine = P.part + ((size_t)w * 2 + slotp) * MAXG * PART_FLOATS;
-        if (tg < G) {
-            float *dst = mine + tg * PART_FLOATS;
-#pragma unroll
-            for (int e = 0; e < 8; ++e)
-                coherent_store(dst + cv * 8 + e, oh[e]);
-            if (cv == 0) {
-                coherent_store(dst + D, mh);
-                coherent_store(dst + D + 1, lh);
-            }
-        }
-        pend = c;
-        has_pend = true;
-    };
-    // Ticket of a pair whose partial is known to be complete (every store issued before the
-    // last wait has finished: vector memory operations complete in order); the pair's last
-    // worker merges the partials in chunk order, lane = dim.
-    auto settle = [&](const Cur &c) {
-        const int pair = c.b * hkv + c.g;
-        f16 *outp = (f16 *)P.out + ((size_t)c.b * P.hq + (size_t)c.g * G) * D;
-        const int wf = owner_of(c.pstart, T, W), wl = owner_of(c.pstart + c.nt - 1, T, W);
-        int tk = 0;
-        if (lane == 0)
-            tk = take_ticket(&P.tickets[pair]);
-        tk = __builtin_amdgcn_readfirstlane(tk);
-        if (tk != wl - wf)
-            return;
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-            float M = -INFINITY;
-            for (int ww = wf; ww <= wl; ++ww) {
-                const int sl = chunk_begin(ww, T, W) >= c.pstart ? 0 : 1;
-                M = fmaxf(M, coherent_load(P.part + (((size_t)ww * 2 + sl) * MAXG + h) * PART_FLOATS + D));
-            }
-            float L = 0.f, O = 0.f;
-            for (int ww = wf; ww <= wl; ++ww) {
-                const int sl = chunk_begin(ww, T, W) >= c.pstart ? 0 : 1;
-                const float *src = P.part + (((size_t)ww * 2 + sl) * MAXG + h) * PART_FLOATS;
-                const float f = M == -INFINITY ? 0.f : fast_exp2(coherent_load(src + D) - M);
-                L = fmaf(coherent_load(src + D + 1), f, L);
-                O = fmaf(coherent_load(src + lane), f, O);
-            }
-            outp[h * D + lane] = (f16)(L > 0.f ? O / L : 0.f);
-        }
-        if (lane == 0)
-            reset_ticket(&P.tickets[pair]);
-    };
-
-    // ---- 4. stream the chunk: the issue cursor runs NBUF-1 tiles ahead ----
-    const long long ntot = c1 - c0;
-    Cur ic = first; // issue cursor (tile ic.t of its pair, flattened c0 + issued)
-    long long issued = 0;
-    auto issue_next = [&]() {
-        issue_tile(ic, c0 + issued, (int)(issued % NBUF));
-        ++issued;
-        if (issued < ntot) {
-            ++ic.t;
-            if (ic.t >= ic.te)
-                ic = cur_next_pair(ic);
-        }
-    };
+    // ---- stream the item's tiles, NBUF-1 ahead ----
 #pragma unroll
     for (int k = 0; k < NBUF - 1; ++k)
-        if (issued < ntot)
-            issue_next();
-    Cur cc = first; // compute cursor
-    bool first_pair = true;
-    for (long long done = 0; done < ntot; ++done) {
-        if (issued < ntot)
-            issue_next();
-        const long long ahead = issued - done - 1; // tiles issued after this one
+        if (k < nt)
+            issue(k);
+    for (int t = 0; t < nt; ++t) {
+        if (t + NBUF - 1 < nt)
+            issue(t + NBUF - 1);
+        const int ahead = min(nt - 1 - t, NBUF - 1); // tiles issued after this one
         if (ahead >= 2)
             wait_vm<2 * DMA_PER_TILE>();
         else if (ahead == 1)
             wait_vm<DMA_PER_TILE>();
         else
             wait_vm<0>();
-        if (has_pend) { // its partial stores were issued before this tile's successor
-            settle(pend);
-            has_pend = false;
-        }
-        compute_tile(cc, c0 + done, (int)(done % NBUF));
-        ++cc.t;
-        if (cc.t >= cc.te) {
-            finish_pair(cc, first_pair);
-            first_pair = false;
-            if (done + 1 < ntot) {
-                cc = cur_next_pair(cc);
-                reset_acc();
+        compute(t);
+    }
+
+    // ---- results: direct output, or a partial and the pair's ticket ----
+#pragma unroll
+    for (int nb = 0; nb < NQB; ++nb) {
+        lsum[nb] += lane_xor(lsum[nb], 16);
+        lsum[nb] += lane_xor(lsum[nb], 32);
+    }
+    bool any_part = false;
+#pragma unroll
+    for (int nb = 0; nb < NQB; ++nb) {
+        const int r = nb * 16 + col;
+        const int mem = r / G, hd = r - mem * G;
+        if (mem >= it.nmem || np[nb] == 0)
+            continue;
+        const int bm = it.b + mem;
+        if (np[nb] == 1) {
+            const float inv = lsum[nb] > 0.f ? 1.f / lsum[nb] : 0.f;
+            f16x8 o0, o1;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int db = 0; db < 4; ++db) {
+                    const int e = 4 * i + db;
+                    const f16 v = (f16)(acc[nb][db][i] * inv);
+                    if (e < 8)
+                        o0[e] = v;
+                    else
+                        o1[e - 8] = v;
+                }
+            f16 *op = (f16 *)P.out + ((size_t)bm * P.hq + (size_t)it.g * G + hd) * D + grp * 16;
+            *(f16x8 *)op = o0;
+            *(f16x8 *)(op + 8) = o1;
+        } else {
+            float *dst = P.part + ((size_t)pb[nb] * MAXG + hd) * PART_FLOATS;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int db = 0; db < 4; ++db)
+                    coherent_store(dst + grp * 16 + 4 * i + db, acc[nb][db][i]);
+            if (grp == 0) {
+                coherent_store(dst + D, m[nb]);
+                coherent_store(dst + D + 1, lsum[nb]);
             }
+            any_part = true;
         }
     }
-    if (has_pend) {
-        wait_vm<0>();
-        settle(pend);
+    if (__ballot(any_part) == 0)
+        return;
+    wait_stores(); // every partial store has completed before a ticket publishes it
+    if constexpr (SHARED) {
+        // member m's ticket is taken by lane m; members whose last part this was are merged
+        int tk = -2, nparts = 1, pbase = 0;
+        if (lane < it.nmem) {
+            const int pair = (it.b + lane) * hkv + it.g;
+            nparts = PV.pair_nparts[pair];
+            pbase = PV.pair_base[pair];
+            if (nparts > 1 && PV.req_shared[it.b + lane] > BS * it.blk0)
+                tk = take_ticket(&P.tickets[pair]);
+        }
+        unsigned long long last = __ballot(tk >= 0 && tk == nparts - 1);
+        while (last) {
+            const int mm = __builtin_ctzll(last);
+            last &= last - 1;
+            const int pair = (it.b + mm) * hkv + it.g;
+            merge_pair<G>(P, it.b + mm, it.g, lane_int(pbase, mm), lane_int(nparts, mm));
+            if (lane == 0)
+                reset_ticket(&P.tickets[pair]);
+        }
+    } else {
+        const int pair = it.b * hkv + it.g;
+        int tk = 0;
+        if (lane == 0)
+            tk = take_ticket(&P.tickets[pair]);
+        tk = __builtin_amdgcn_readfirstlane(tk);
+        if (tk != it.nparts - 1)
+            return;
+        merge_pair<G>(P, it.b, it.g, it.pbase, it.nparts);
+        if (lane == 0)
+            reset_ticket(&P.tickets[pair]);
+    }
+}
+
+template <int G, int NBUF, bool PLANNED, typename Addr>
+__global__ __launch_bounds__(64) void decode_f16_kernel(DecodeParams P, Addr A, PlanView PV)
+{
+    static_assert(G >= 1 && G <= MAXG, "group size");
+    __shared__ __attribute__((aligned(16))) char kring[NBUF][TB];
+    __shared__ __attribute__((aligned(16))) char vring[NBUF][TB];
+    const int lane = threadIdx.x;
+    Item it;
+    int rv;
+    if constexpr (PLANNED) {
+        const int *rec = PV.items + (size_t)blockIdx.x * REC;
+        rv = lane < REC ? rec[lane] : -1;
+        const int flags = lane_int(rv, R_FLAGS);
+        it.b = lane_int(rv, R_B);
+        it.g = lane_int(rv, R_G);
+        it.nmem = lane_int(rv, R_NMEM);
+        it.blk0 = lane_int(rv, R_BLK0);
+        it.nblk = lane_int(rv, R_NBLK);
+        it.end = lane_int(rv, R_END);
+        it.slot = lane_int(rv, R_SLOT);
+        it.nparts = lane_int(rv, R_NPARTS);
+        it.pbase = lane_int(rv, R_PBASE);
+        // a record that does not fit this call is skipped rather than trusted
+        if (it.b < 0 || it.g < 0 || it.g >= P.hkv || it.nmem < 1 || it.b + it.nmem > P.B ||
+            it.nblk < 0 || it.nblk > BPI || it.blk0 < 0)
+            return;
+        if (flags & F_EMPTY)
+            return;
+        if (flags & F_SHARED) {
+            if (it.nmem * G > 16 || it.slot < 0)
+                return;
+            run_item<G, 1, true, NBUF>(P, A, PV, it, rv, kring, vring);
+            return;
+        }
+        if (it.nmem != 1)
+            return;
+        run_item<G, 1, false, NBUF>(P, A, PV, it, rv, kring, vring);
+    } else {
+        const int pair = blockIdx.x / PV.ipp;
+        const int k = blockIdx.x - pair * PV.ipp;
+        it.b = pair / P.hkv;
+        it.g = pair - it.b * P.hkv;
+        const int maxc = A.max_ctx();
+        int ctx = P.ctx_lens[it.b];
+        ctx = ctx < 0 ? 0 : (ctx > maxc ? maxc : ctx);
+        const int nbt = (ctx + BS - 1) / BS;
+        it.blk0 = k * BPI;
+        if (k > 0 && it.blk0 >= nbt)
+            return;
+        it.nmem = 1;
+        it.nblk = max(0, min(BPI, nbt - it.blk0));
+        it.end = ctx;
+        it.nparts = max(1, (nbt + BPI - 1) / BPI);
+        it.pbase = pair * PV.ipp;
+        it.slot = it.pbase + k;
+        const int j = lane - R_ENT;
+        rv = (j >= 0 && j < it.nblk) ? A.entry(it.b, it.blk0 + j) : -1;
+        run_item<G, 1, false, NBUF>(P, A, PV, it, rv, kring, vring);
     }
 }
 
 // ---------------------------------------------------------------------------------------
-template <typename Addr>
-static kvp_status launch_f16(const DecodeParams &P, const Addr &A, int group, hipStream_t st)
+template <bool PLANNED, typename Addr>
+static kvp_status launch_f16(const DecodeParams &P, const Addr &A, const PlanView &PV, int group,
+                             long long grid, hipStream_t st)
 {
-    dim3 grid(P.workers), block(64);
+    if (grid <= 0)
+        return KVP_OK;
+    if (grid > 0x7fffffffLL)
+        return fail(KVP_ERR_UNSUPPORTED, "decode: %lld work items", grid);
+    dim3 g((unsigned)grid), block(64);
     switch (group) {
-#define KVP_G(GG)                                                                              \
-    case GG:                                                                                   \
-        hipLaunchKernelGGL((decode_f16_kernel<GG, 2, Addr>), grid, block, 0, st, P, A);       \
+#define KVP_G(GG)                                                                                  \
+    case GG:                                                                                       \
+        hipLaunchKernelGGL((decode_f16_kernel<GG, 2, PLANNED, Addr>), g, block, 0, st, P, A, PV); \
         break;
         KVP_G(1) KVP_G(2) KVP_G(3) KVP_G(4) KVP_G(5) KVP_G(6) KVP_G(7) KVP_G(8)
 #undef KVP_G
@@ -568,18 +579,36 @@ static kvp_status launch_f16(const DecodeParams &P, const Addr &A, int group, hi
     return KVP_OK;
 }
 
-kvp_status launch_decode_f16(const DecodeParams &P, const PagedAddr &A, int group, hipStream_t st)
+int decode_f16_items_per_pair(int max_context)
 {
-    return launch_f16(P, A, group, st);
-}
-kvp_status launch_decode_f16(const DecodeParams &P, const ContigAddr &A, int group, hipStream_t st)
-{
-    return launch_f16(P, A, group, st);
+    const int nb = (std::max(max_context, 1) + BS - 1) / BS;
+    return (nb + BPI - 1) / BPI;
 }
 
-size_t decode_f16_part_bytes(int workers)
+size_t decode_f16_part_bytes(long long slots)
 {
-    return (size_t)workers * 2 * MAXG * PART_FLOATS * sizeof(float);
+    return (size_t)slots * MAXG * PART_FLOATS * sizeof(float);
+}
+
+kvp_status launch_decode_f16(const DecodeParams &P, const PagedAddr &A, int group, int max_context,
+                             hipStream_t st)
+{
+    PlanView PV{nullptr, nullptr, nullptr, nullptr, decode_f16_items_per_pair(max_context)};
+    return launch_f16<false>(P, A, PV, group, (long long)P.B * P.hkv * PV.ipp, st);
+}
+kvp_status launch_decode_f16(const DecodeParams &P, const ContigAddr &A, int group, int max_context,
+                             hipStream_t st)
+{
+    PlanView PV{nullptr, nullptr, nullptr, nullptr, decode_f16_items_per_pair(max_context)};
+    return launch_f16<false>(P, A, PV, group, (long long)P.B * P.hkv * PV.ipp, st);
+}
+kvp_status launch_decode_f16_planned(const DecodeParams &P, const PagedAddr &A, int group,
+                                     const void *d_image, const kvp_decode_plan &plan, hipStream_t st)
+{
+    const char *img = (const char *)d_image;
+    PlanView PV{(const int *)img, (const int *)(img + plan.off_pair_base),
+                (const int *)(img + plan.off_pair_nparts), (const int *)(img + plan.off_req_shared), 0};
+    return launch_f16<true>(P, A, PV, group, plan.n_items, st);
 }
 
 } // namespace kvp

@@ -1,0 +1,324 @@
+// kvp_plan.cpp -- host planner for the fp16 decode kernel: work items (one wave each), the
+// partial-slot layout of split pairs, and shared-prefix items for requests whose block
+// tables start with the same physical blocks.
+//
+// Pages: [PAGED] (paged-attention article, SECTION 3): forked requests share the physical
+// blocks of a common prefix until copy-on-write makes a block private; [CHAP] (PagedAttention
+// passage): sharing prefix blocks among requests.  Reading a shared block once for all of
+// its readers is this library's choice; the attention each request receives is unchanged
+// (same keys and values, only the order of the fp32 sums differs).
+#include <algorithm>
+#include <cstdlib>
+#include <cstring>
+#include <vector>
+
+#include "kvp_internal.h"
+#include "kvp_plan_format.h"
+
+using namespace kvp;
+using namespace kvp::plan;
+
+namespace {
+
+constexpr int BS = 16;
+
+size_t align16(size_t x) { return (x + 15) / 16 * 16; }
+
+kvp_status check_plan_dims(const kvp_dims *d, const char *who)
+{
+    if (!d)
+        return fail(KVP_ERR_INVALID, "%s: dims is NULL", who);
+    if (d->num_q_heads <= 0 || d->num_kv_heads <= 0 || d->num_q_heads % d->num_kv_heads != 0)
+        return fail(KVP_ERR_INVALID, "%s: num_q_heads=%d must be a positive multiple of num_kv_heads=%d",
+                    who, d->num_q_heads, d->num_kv_heads);
+    if (d->head_dim != 64)
+        return fail(KVP_ERR_UNSUPPORTED, "%s: head_dim=%d (only 64 is implemented)", who, d->head_dim);
+    if (d->dtype != KVP_F16)
+        return fail(d->dtype == KVP_F32 ? KVP_ERR_UNSUPPORTED : KVP_ERR_INVALID,
+                    "%s: planned decode is implemented for fp16 (dtype=%d)", who, d->dtype);
+    if (d->num_q_heads / d->num_kv_heads > 8)
+        return fail(KVP_ERR_UNSUPPORTED, "%s: %d query heads per KV head (1..8 supported)", who,
+                    d->num_q_heads / d->num_kv_heads);
+    return KVP_OK;
+}
+
+constexpr int MAX_BUNDLE = 8; // shared items kept together on one XCD
+
+int plan_bpi()
+{
+    int bpi = BPI; // blocks per item
+    if (const char *e = getenv("KVP_PLAN_BPI"))
+        bpi = std::max(1, std::min(BPI, atoi(e)));
+    return bpi;
+}
+
+long long max_items(long long B, long long hkv, long long max_blocks)
+{
+    const long long ipp = std::max<long long>(1, (max_blocks + plan_bpi() - 1) / plan_bpi());
+    // private items: at most ipp per pair; shared items: at most one set per two requests;
+    // plus the padding that evens out the XCD queues
+    const long long work = B * hkv * ipp + (B / 2) * hkv * ipp;
+    return XCDS * ((work + XCDS - 1) / XCDS + MAX_BUNDLE);
+}
+
+size_t image_bytes_for(long long items, long long B, long long hkv)
+{
+    return align16((size_t)items * REC * 4) + 2 * align16((size_t)B * hkv * 4) + align16((size_t)B * 4);
+}
+
+struct SubRun {
+    int a, n, shared_tokens, run;
+};
+
+} // namespace
+
+extern "C" {
+
+size_t decode_plan_bytes(const kvp_dims *dims, int32_t B, int32_t max_blocks, int32_t pad_items)
+{
+    if (check_plan_dims(dims, "decode_plan_bytes") != KVP_OK || B < 0 || max_blocks <= 0 || pad_items < 0)
+        return 0;
+    const long long pad = ((long long)pad_items + XCDS - 1) / XCDS * XCDS;
+    return image_bytes_for(std::max(pad, max_items(B, dims->num_kv_heads, max_blocks)), B, dims->num_kv_heads);
+}
+
+kvp_status decode_plan_build(const kvp_dims *dims, const int32_t *table, int32_t max_blocks,
+                             const int32_t *ctx_lens, int32_t B, int32_t num_blocks, uint32_t flags,
+                             int32_t pad_items, void *h_image, size_t image_bytes, kvp_decode_plan *plan)
+{
+    const char *who = "decode_plan_build";
+    kvp_status st = check_plan_dims(dims, who);
+    if (st != KVP_OK)
+        return st;
+    if (B < 0 || max_blocks <= 0 || num_blocks <= 0)
+        return fail(KVP_ERR_INVALID, "%s: B=%d max_blocks=%d num_blocks=%d", who, B, max_blocks, num_blocks);
+    if (!plan || !h_image || (B > 0 && (!table || !ctx_lens)))
+        return fail(KVP_ERR_INVALID, "%s: NULL pointer argument", who);
+    if (flags & ~KVP_PLAN_SHARE_PREFIX)
+        return fail(KVP_ERR_INVALID, "%s: unknown flags 0x%x", who, flags);
+    if (pad_items < 0)
+        return fail(KVP_ERR_INVALID, "%s: pad_items=%d", who, pad_items);
+    if ((long long)max_blocks * BS > 0x7fffffffLL)
+        return fail(KVP_ERR_UNSUPPORTED, "%s: max_blocks too large", who);
+    const int hkv = dims->num_kv_heads;
+    const int G = dims->num_q_heads / hkv;
+    const int bpi = plan_bpi();
+    const int maxm = std::max(1, std::min(MAXM, 16 / G)); // members of a shared item (<= 16 rows)
+    const long long npairs = (long long)B * hkv;
+
+    std::vector<int> c(B), nbt(B), E(B, 0);
+    auto ent = [&](int b, int j) -> int {
+        const int e = table[(size_t)b * max_blocks + j];
+        return (e >= 0 && e < num_blocks) ? e : -1;
+    };
+    for (int b = 0; b < B; ++b) {
+        c[b] = std::min(std::max(ctx_lens[b], 0), max_blocks * BS);
+        nbt[b] = (c[b] + BS - 1) / BS;
+    }
+
+    // ---- shared prefixes: runs of consecutive requests with the same first block, cut
+    // into sub-runs of at most maxm members; member m shares E[m] tokens (whole blocks
+    // equal to the sub-run leader's, never the block holding its last token) ----
+    std::vector<SubRun> subs;
+    if (flags & KVP_PLAN_SHARE_PREFIX) {
+        int b = 0, run = 0;
+        while (b < B) {
+            if (nbt[b] == 0 || ent(b, 0) < 0) {
+                ++b;
+                continue;
+            }
+            int r = b + 1;
+            while (r < B && nbt[r] > 0 && ent(r, 0) == ent(b, 0))
+                ++r;
+            for (int a = b; a < r; a += maxm) {
+                const int n = std::min(maxm, r - a);
+                if (n < 2)
+                    continue;
+                int S = 0;
+                for (int m = a + 1; m < a + n; ++m) {
+                    const int lim = std::min(nbt[a], nbt[m]);
+                    int k = 0;
+                    while (k < lim && ent(m, k) >= 0 && ent(m, k) == ent(a, k))
+                        ++k;
+                    E[m] = std::min(BS * k, BS * ((c[m] - 1) / BS));
+                    S = std::max(S, E[m]);
+                }
+                E[a] = std::min(S, BS * ((c[a] - 1) / BS));
+                if (S > 0)
+                    subs.push_back({a, n, S, run});
+                else
+                    for (int m = a; m < a + n; ++m)
+                        E[m] = 0;
+            }
+            b = r;
+            ++run;
+        }
+    }
+
+    // ---- parts per pair and slot ranges ----
+    // shared items a member takes part in: those starting below its shared extent
+    std::vector<int> shared_parts(B, 0);
+    for (int b = 0; b < B; ++b)
+        shared_parts[b] = (E[b] / BS + bpi - 1) / bpi;
+    auto private_items = [&](int b) -> int {
+        const int nb = nbt[b] - E[b] / BS;
+        return nb <= 0 ? 1 : (nb + bpi - 1) / bpi;
+    };
+    std::vector<int> pair_base(npairs, -1), pair_nparts(npairs, 1);
+    long long slots = 0, n_items = 0;
+    for (int b = 0; b < B; ++b)
+        for (int g = 0; g < hkv; ++g) {
+            const long long p = (long long)b * hkv + g;
+            pair_nparts[p] = shared_parts[b] + private_items(b);
+            if (pair_nparts[p] > 1) {
+                pair_base[p] = (int)slots;
+                slots += pair_nparts[p];
+            }
+            n_items += private_items(b);
+        }
+    long long n_shared = 0;
+    for (const SubRun &s : subs)
+        n_shared += (long long)hkv * ((s.shared_tokens / BS + bpi - 1) / bpi);
+    n_items += n_shared;
+    if (slots > 0x7fffffffLL || n_items > 0x7fffffffLL)
+        return fail(KVP_ERR_UNSUPPORTED, "%s: plan too large", who);
+
+    // ---- records (built in plan order, placed into XCD queues below) ----
+    std::vector<int32_t> recs((size_t)n_items * REC, -1);
+    std::vector<long long> cost(n_items);
+    long long idx = 0, blocks_read = 0;
+    auto record = [&](int fl, int b, int g, int nmem, int blk0, int nblk, int end, int slot, int nparts,
+                      int pbase, int src_req) {
+        int32_t *r = recs.data() + (size_t)idx * REC;
+        r[R_FLAGS] = fl;
+        r[R_B] = b;
+        r[R_G] = g;
+        r[R_NMEM] = nmem;
+        r[R_BLK0] = blk0;
+        r[R_NBLK] = nblk;
+        r[R_END] = end;
+        r[R_SLOT] = slot;
+        r[R_NPARTS] = nparts;
+        r[R_PBASE] = pbase;
+        for (int j = R_PBASE + 1; j < R_ENT; ++j)
+            r[j] = 0;
+        for (int j = 0; j < BPI; ++j)
+            r[R_ENT + j] = j < nblk ? ent(src_req, blk0 + j) : -1;
+        blocks_read += nblk;
+        cost[idx] = nblk + 2; // a tile stream plus the fixed start / finish of a wave
+        ++idx;
+    };
+    // bundles: the shared items of one run and KV head (at most MAX_BUNDLE per bundle)
+    std::vector<std::vector<long long>> bundles;
+    {
+        std::vector<std::pair<long long, long long>> keyed; // (run * hkv + g, item)
+        for (const SubRun &sr : subs) {
+            const int nsb = sr.shared_tokens / BS;
+            for (int g = 0; g < hkv; ++g)
+                for (int k = 0; k * bpi < nsb; ++k) {
+                    keyed.push_back({(long long)sr.run * hkv + g, idx});
+                    record(F_SHARED, sr.a, g, sr.n, k * bpi, std::min(bpi, nsb - k * bpi), 0, k, 0, -1, sr.a);
+                }
+        }
+        std::stable_sort(keyed.begin(), keyed.end(),
+                         [](const std::pair<long long, long long> &x, const std::pair<long long, long long> &y) {
+                             return x.first < y.first;
+                         });
+        for (size_t i = 0; i < keyed.size(); ++i) {
+            if (i == 0 || keyed[i].first != keyed[i - 1].first || bundles.back().size() >= (size_t)MAX_BUNDLE)
+                bundles.push_back({});
+            bundles.back().push_back(keyed[i].second);
+        }
+    }
+    const long long first_private = idx;
+    for (int b = 0; b < B; ++b) {
+        const int first = E[b] / BS;
+        const int npriv = private_items(b);
+        for (int g = 0; g < hkv; ++g) {
+            const long long p = (long long)b * hkv + g;
+            for (int k = 0; k < npriv; ++k) {
+                const int blk0 = first + k * bpi;
+                const int nblk = std::max(0, std::min(bpi, nbt[b] - blk0));
+                const int slot = pair_nparts[p] > 1 ? pair_base[p] + shared_parts[b] + k : -1;
+                record(0, b, g, 1, blk0, nblk, c[b], slot, pair_nparts[p], pair_base[p], b);
+            }
+        }
+    }
+
+    // ---- XCD queues: item p of the image runs on XCD p % XCDS.  Bundles first, then private
+    // items longest first, each to the least-loaded queue that stays within the length cap;
+    // shorter queues are padded with empty items ----
+    const long long cap = (n_items + XCDS - 1) / XCDS + MAX_BUNDLE;
+    std::vector<std::vector<long long>> q(XCDS);
+    std::vector<long long> load(XCDS, 0);
+    auto place = [&](const std::vector<long long> &its) {
+        long long c = 0;
+        for (long long i : its)
+            c += cost[i];
+        int best = -1;
+        for (int x = 0; x < XCDS; ++x)
+            if ((long long)(q[x].size() + its.size()) <= cap && (best < 0 || load[x] < load[best]))
+                best = x;
+        for (long long i : its)
+            q[best].push_back(i);
+        load[best] += c;
+    };
+    for (const auto &bd : bundles)
+        place(bd);
+    std::vector<long long> priv(n_items - first_private);
+    for (size_t i = 0; i < priv.size(); ++i)
+        priv[i] = first_private + (long long)i;
+    std::stable_sort(priv.begin(), priv.end(), [&](long long x, long long y) { return cost[x] > cost[y]; });
+    for (long long i : priv)
+        place({i});
+    size_t qlen = 0;
+    for (const auto &qq : q)
+        qlen = std::max(qlen, qq.size());
+    if (pad_items > 0) {
+        const size_t padq = ((size_t)pad_items + XCDS - 1) / XCDS;
+        if (qlen > padq)
+            return fail(KVP_ERR_INVALID, "%s: the plan needs %zu items, more than pad_items=%d", who,
+                        qlen * XCDS, pad_items);
+        qlen = padq;
+    }
+    const long long n_image = (long long)qlen * XCDS;
+
+    const size_t off_pb = align16((size_t)n_image * REC * 4);
+    const size_t off_np = off_pb + align16((size_t)npairs * 4);
+    const size_t off_rs = off_np + align16((size_t)npairs * 4);
+    const size_t bytes = off_rs + align16((size_t)B * 4);
+    if (image_bytes < bytes)
+        return fail(KVP_ERR_INVALID, "%s: image buffer %zu bytes < %zu needed", who, image_bytes, bytes);
+    int32_t *img = (int32_t *)h_image;
+    std::memset(h_image, 0, bytes);
+    for (size_t qi = 0; qi < qlen; ++qi)
+        for (int x = 0; x < XCDS; ++x) {
+            int32_t *dst = img + ((size_t)qi * XCDS + x) * REC;
+            if (qi < q[x].size()) {
+                std::memcpy(dst, recs.data() + (size_t)q[x][qi] * REC, REC * 4);
+            } else {
+                for (int j = 0; j < REC; ++j)
+                    dst[j] = -1;
+                dst[R_FLAGS] = F_EMPTY;
+            }
+        }
+    std::memcpy((char *)h_image + off_pb, pair_base.data(), (size_t)npairs * 4);
+    std::memcpy((char *)h_image + off_np, pair_nparts.data(), (size_t)npairs * 4);
+    std::memcpy((char *)h_image + off_rs, E.data(), (size_t)B * 4);
+
+    plan->B = B;
+    plan->num_kv_heads = hkv;
+    plan->group = G;
+    plan->num_blocks = num_blocks;
+    plan->n_items = (int32_t)n_image;
+    plan->n_shared = (int32_t)n_shared;
+    plan->n_slots = slots;
+    plan->bytes = (int64_t)bytes;
+    plan->off_pair_base = (int64_t)off_pb;
+    plan->off_pair_nparts = (int64_t)off_np;
+    plan->off_req_shared = (int64_t)off_rs;
+    plan->kv_blocks_read = blocks_read;
+    return KVP_OK;
+}
+
+} // extern "C"

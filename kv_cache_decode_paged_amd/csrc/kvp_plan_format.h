@@ -1,0 +1,44 @@
+// kvp_plan_format.h -- layout of a decode work plan (internal to the library; the host
+// planner writes it, the fp16 decode kernel reads it).
+//
+// A plan is one int32 image:
+//   items       [n_items][REC]   one record per work item (= one wave of the kernel)
+//   pair_base   [B * Hkv]        first partial slot of pair (b, g), -1 if the pair has one part
+//   pair_nparts [B * Hkv]        parts the pair's attention row is split into (>= 1)
+//   req_shared  [B]              tokens [0, req_shared[b]) of request b are read by a shared item
+//
+// A work item covers up to BPI consecutive 16-token blocks of one KV head: either of one
+// request (private item) or of the leading request of a run of requests whose tables point
+// at the same physical blocks there (shared item: the blocks are read once and attended by
+// every member's queries, each member up to its own req_shared limit).
+#pragma once
+
+namespace kvp {
+namespace plan {
+
+constexpr int BPI = 32;  // blocks per work item (8 tiles of 64 tokens)
+constexpr int REC = 48;  // int32 per record
+constexpr int MAXM = 16; // members of one shared item (and at most 16 query rows)
+constexpr int XCDS = 8;  // MI355X: workgroup i runs on XCD i % 8 (round-robin dispatch)
+
+enum : int {
+    R_FLAGS = 0,  // F_SHARED: shared item; F_EMPTY: padding, no work
+    R_B = 1,      // request (private) or first member (shared)
+    R_G = 2,      // KV head
+    R_NMEM = 3,   // members (1 for a private item)
+    R_BLK0 = 4,   // first logical block
+    R_NBLK = 5,   // blocks in the item (0 only for an empty context)
+    R_END = 6,    // private: context length of the request (tokens >= END are masked)
+    R_SLOT = 7,   // private: partial slot written by this item (when NPARTS > 1);
+                  // shared: part index inside each member's slot range
+    R_NPARTS = 8, // private: parts of the pair
+    R_PBASE = 9,  // private: first slot of the pair
+    R_ENT = 16,   // BPI physical block ids (-1: unusable, rows masked)
+};
+static_assert(R_ENT + BPI <= REC, "record too small");
+
+constexpr int F_SHARED = 1;
+constexpr int F_EMPTY = 2;
+
+} // namespace plan
+} // namespace kvp

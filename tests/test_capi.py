@@ -31,7 +31,8 @@ def test_header_declares_the_boundary():
     for must in ["kv_append", "paged_decode_attention", "varlen_causal_prefill", "block_table_alloc",
                  "block_table_fork", "block_table_cow", "block_table_free", "block_table_append_slot",
                  "kv_copy_blocks", "contiguous_decode_attention", "kv_gather", "decode_workspace_bytes",
-                 "kv_bytes_per_token", "kvp_last_error"]:
+                 "kv_bytes_per_token", "kvp_last_error", "decode_plan_build", "decode_plan_bytes",
+                 "decode_plan_workspace_bytes", "paged_decode_attention_planned"]:
         assert must in names
 
 
@@ -80,10 +81,14 @@ def test_device_calls_reject_bad_arguments_before_launch():
 
 def test_workspace_size():
     import kv_cache_decode_paged_amd as kvp
-    # fp16: partials of every worker wave (2 slots x 8 heads x 66 floats) + tickets
+    # fp16: one partial per 512-token split of every pair (8 head slots x 66 floats) +
+    # one ticket per pair
     ws = kvp.decode_workspace_bytes(14, 2, torch.float16, 32, 32768)
-    assert ws > 0 and ws % 256 == 0
+    assert ws == 32 * 2 * 64 * 8 * 66 * 4 + 256
+    # contexts of at most 512 tokens are never split: no workspace
+    assert kvp.decode_workspace_bytes(14, 2, torch.float16, 200, 512) == 0
+    assert kvp.decode_workspace_bytes(14, 2, torch.float16, 200, 513) == 1792 + 200 * 2 * 2 * 8 * 66 * 4
     # fp32 single head, short context: one split, no workspace needed
     assert kvp.decode_workspace_bytes(1, 1, torch.float32, 1, 88) == 0
     # 5000 tokens: at most 16 splits (256-token splits up to 4096 tokens, 512 beyond)
-    assert kvp.decode_workspace_bytes(1, 1, torch.float32, 4, 5000) == 4 * 1 * 16 * 66 * 4 + 256
+    assert kvp.decode_workspace_bytes(1, 1, torch.float32, 4, 5000) == 256 + 4 * 1 * 16 * 66 * 4

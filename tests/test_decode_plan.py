@@ -1,0 +1,265 @@
+"""Host planner of the fp16 decode (decode_plan_build), checked on the CPU against what a
+plan must guarantee, read independently from the image:
+
+* every (request, KV head) pair attends over every token j < context length exactly once,
+  each token through the block its own table names (a shared item reads the leading
+  member's block, which must be the same physical block);
+* a pair split into several parts has slots pbase .. pbase+nparts-1, each written once,
+  in token order (the merge order), and single-part pairs are written directly;
+* shared items hold at most 16 query rows and a prefix's items run on one XCD;
+* without prefix sharing the plan is exactly the per-pair split of 32 blocks that
+  paged_decode_attention uses (so the two are bit-identical on the GPU).
+
+Prefix sharing follows the pages: requests forked from one prefix share its physical
+blocks until copy-on-write ([PAGED] paged-attention article, SECTION 3).
+"""
+import math
+import random
+
+import numpy as np
+import pytest
+import torch
+
+import kv_cache_decode_paged_amd as kvp
+import workloads as W
+
+REC, BPI, R_ENT, XCDS = 48, 32, 16, 8
+F_SHARED, F_EMPTY = 1, 2
+BS = 16
+
+
+def parse(plan, image, B, hkv):
+    raw = image[: plan.bytes].numpy().view(np.int32)
+    items = raw[: plan.n_items * REC].reshape(plan.n_items, REC)
+    pb = raw[plan.off_pair_base // 4: plan.off_pair_base // 4 + B * hkv]
+    npt = raw[plan.off_pair_nparts // 4: plan.off_pair_nparts // 4 + B * hkv]
+    rs = raw[plan.off_req_shared // 4: plan.off_req_shared // 4 + B]
+    return items, pb, npt, rs
+
+
+def check_plan(plan, image, table, ctx, num_blocks, hq, hkv, shared_expected=None):
+    B, mb = table.shape
+    G = hq // hkv
+    items, pbase, nparts, req_shared = parse(plan, image, B, hkv)
+    assert plan.n_items % XCDS == 0
+    ctx = np.clip(ctx, 0, mb * BS)
+
+    def ent(b, j):
+        e = int(table[b, j])
+        return e if 0 <= e < num_blocks else -1
+
+    # sharing runs: maximal runs of consecutive requests with the same usable first block
+    run_of, run = [], -1
+    for b in range(B):
+        cont = b > 0 and ctx[b] > 0 and ctx[b - 1] > 0 and ent(b, 0) >= 0 and ent(b, 0) == ent(b - 1, 0)
+        run += 0 if cont else 1
+        run_of.append(run)
+
+    cover = {}   # (b, g) -> token coverage count array
+    writes = {}  # (b, g) -> list of (slot or 'direct', first token)
+    bundles = {}
+    for p, r in enumerate(items):
+        fl = int(r[0])
+        if fl == F_EMPTY:
+            continue
+        b, g, nmem, blk0, nblk, end, slot, np_, pb_ = (int(x) for x in r[1:10])
+        assert 0 <= g < hkv and nmem >= 1 and b + nmem <= B and 0 <= nblk <= BPI and blk0 >= 0
+        for j in range(BPI):
+            want = ent(b, blk0 + j) if j < nblk else -1
+            assert int(r[R_ENT + j]) == want, (p, j)
+        if fl == F_SHARED:
+            assert nmem * G <= 16 and slot >= 0
+            key = (run_of[b], g)  # one sharing run and KV head
+            xs, n = bundles.get(key, (set(), 0))
+            bundles[key] = (xs | {p % XCDS}, n + 1)
+            for m in range(b, b + nmem):
+                E = int(req_shared[m])
+                if E <= BS * blk0:  # the member's shared extent ends before this item
+                    continue
+                assert E % BS == 0 and E < ctx[m]
+                lo, hi = BS * blk0, min(BS * (blk0 + nblk), E)
+                for j in range(lo // BS, (hi + BS - 1) // BS):
+                    assert ent(m, j) == ent(b, j) and ent(m, j) >= 0, "shared block differs"
+                c = cover.setdefault((m, g), np.zeros(mb * BS + 1, np.int32))
+                c[lo:hi] += 1
+                pair = m * hkv + g
+                writes.setdefault((m, g), []).append((int(pbase[pair]) + slot, lo))
+        else:
+            assert fl == 0 and nmem == 1 and end == ctx[b]
+            pair = b * hkv + g
+            assert np_ == nparts[pair] and pb_ == pbase[pair]
+            lo, hi = BS * blk0, min(BS * (blk0 + nblk), end)
+            c = cover.setdefault((b, g), np.zeros(mb * BS + 1, np.int32))
+            c[lo:max(lo, hi)] += 1
+            writes.setdefault((b, g), []).append(("direct" if np_ == 1 else slot, lo))
+    for b in range(B):
+        for g in range(hkv):
+            c = cover.get((b, g))
+            assert c is not None, f"pair {(b, g)} has no item"
+            assert (c[: ctx[b]] == 1).all() and (c[ctx[b]:] == 0).all(), f"coverage of {(b, g)}"
+            w = writes[(b, g)]
+            pair = b * hkv + g
+            if nparts[pair] == 1:
+                assert w == [("direct", 0)] or (ctx[b] == 0 and w[0][0] == "direct")
+            else:
+                slots = [s for s, _ in sorted(w, key=lambda x: x[1])]
+                assert slots == list(range(int(pbase[pair]), int(pbase[pair]) + int(nparts[pair])))
+    for key, (xs, n) in bundles.items():
+        if n <= 8:  # a run's shared items of one head (at most one bundle) share an XCD
+            assert len(xs) == 1, f"shared items of run {key} spread over XCDs {xs}"
+    if shared_expected is not None:
+        assert (plan.n_shared > 0) == shared_expected
+    return items, pbase, nparts, req_shared
+
+
+def build(table, ctx, num_blocks, hq=14, hkv=2, share=True):
+    t = torch.from_numpy(np.ascontiguousarray(table, dtype=np.int32))
+    c = torch.from_numpy(np.ascontiguousarray(ctx, dtype=np.int32))
+    return kvp.decode_plan_build(hq, hkv, t, c, num_blocks, share_prefix=share)
+
+
+def c4_tables(B, steps_done=1, seed=42):
+    """Host block tables of the batch-B shared-prefix workload after one reserved step."""
+    pb = W.paged_batch(B)
+    need = sum(math.ceil((c + 8) / BS) for c in pb.ctx_before) + 64 * B
+    pool = kvp.BlockPool(need)
+    pool.set_free_order(W.free_list_permutation(need, seed + 1).tolist())
+    seqs = [None] * B
+    for gi in sorted(set(pb.group)):
+        pre = pool.alloc(pb.prefix)
+        for i in [i for i in range(B) if pb.group[i] == gi]:
+            s = pool.fork(pre)
+            L = pb.ctx_before[i]
+            if L < pb.prefix:
+                pool.truncate(s, L)
+            elif L > pb.prefix:
+                pool.reserve(s, L - pb.prefix)
+            seqs[i] = s
+        pool.free(pre)
+    for _ in range(steps_done):
+        pool.append_slots(seqs)
+    max_blocks = max(math.ceil(pool.tokens(s) / BS) for s in seqs)
+    table, ctx = pool.export(seqs, max_blocks)
+    return table.numpy(), ctx.numpy(), need, pool, seqs
+
+
+@pytest.mark.parametrize("B", [10, 50, 200])
+def test_plan_shared_prefix_workload(B):
+    table, ctx, nb, _, _ = c4_tables(B)
+    plan, image = build(table, ctx, nb)
+    check_plan(plan, image, table, ctx, nb, 14, 2, shared_expected=True)
+    # reading each shared prefix through fewer items than requests
+    plain, image0 = build(table, ctx, nb, share=False)
+    check_plan(plain, image0, table, ctx, nb, 14, 2, shared_expected=False)
+    assert plan.kv_blocks_read < plain.kv_blocks_read
+
+
+def test_plan_without_sharing_is_the_plain_split():
+    table, ctx, nb, _, _ = c4_tables(50)
+    plan, image = build(table, ctx, nb, share=False)
+    items, pbase, nparts, _ = check_plan(plan, image, table, ctx, nb, 14, 2)
+    got = sorted((int(r[1]), int(r[2]), int(r[4]), int(r[5])) for r in items if r[0] != F_EMPTY)
+    want = []
+    for b in range(len(ctx)):
+        nbt = math.ceil(ctx[b] / BS)
+        for g in range(2):
+            for k in range(max(1, math.ceil(nbt / BPI))):
+                want.append((b, g, BPI * k, max(0, min(BPI, nbt - BPI * k))))
+    assert got == sorted(want)
+
+
+def test_plan_members_without_shared_blocks():
+    # consecutive requests with the same first block but a short leader whose later blocks
+    # were made private; a member whose context ends inside the first block
+    table = np.array([[5, 6, 7, 8], [5, 6, 9, 10], [5, 11, -1, -1], [5, 6, 7, 12]], np.int32)
+    ctx = np.array([64, 60, 20, 10], np.int32)
+    plan, image = build(table, ctx, 16, hq=4, hkv=1)  # group 4: four members per shared item
+    items, pbase, nparts, rs = check_plan(plan, image, table, ctx, 16, 4, 1)
+    assert list(rs) == [32, 32, 16, 0]  # last member: its only block holds its last token
+    assert list(nparts) == [2, 2, 2, 1]  # one shared part (if any) + one private part
+    plan, image = build(table, ctx, 16, hq=8, hkv=1)  # group 8: pairs of members
+    items, pbase, nparts, rs = check_plan(plan, image, table, ctx, 16, 8, 1)
+    assert list(rs) == [32, 32, 0, 0]  # requests 2 and 3 share no whole block
+
+
+def test_plan_empty_and_unusable_entries():
+    table = np.array([[3, -1, 99, 4], [3, -1, 99, 4], [0, 1, 2, 3]], np.int32)
+    ctx = np.array([64, 0, 50], np.int32)
+    plan, image = build(table, ctx, 10, hq=4, hkv=2)
+    check_plan(plan, image, table, ctx, 10, 4, 2)
+
+
+@pytest.mark.parametrize("G", [1, 2, 7, 8])
+def test_plan_random_forks(G):
+    rng = random.Random(1000 + G)
+    for trial in range(20):
+        hkv = rng.choice([1, 2])
+        hq = G * hkv
+        B = rng.randint(1, 40)
+        mb = rng.randint(1, 80)
+        nb = B * mb + 8
+        free = list(range(nb))
+        rng.shuffle(free)
+        table = np.full((B, mb), -1, np.int32)
+        ctx = np.zeros(B, np.int32)
+        b = 0
+        while b < B:
+            run = min(B - b, rng.randint(1, 20))
+            pre = rng.randint(0, mb)
+            pre_blocks = [free.pop() for _ in range(pre)]
+            for m in range(b, b + run):
+                c = rng.randint(0, mb * BS)
+                nbt = math.ceil(c / BS)
+                keep = min(rng.randint(0, pre), nbt)
+                row = pre_blocks[:keep] + [free.pop() for _ in range(nbt - keep)]
+                table[m, :nbt] = row
+                ctx[m] = c
+            b += run
+        if rng.random() < 0.3:  # unusable entries
+            i, j = rng.randrange(B), rng.randrange(mb)
+            table[i, j] = rng.choice([-7, nb + 3])
+        plan, image = build(table, ctx, nb, hq=hq, hkv=hkv)
+        check_plan(plan, image, table, ctx, nb, hq, hkv)
+        need = kvp.decode_plan_bytes(hq, hkv, B, mb)
+        assert plan.bytes <= need
+
+
+def test_plan_validation():
+    table = torch.zeros((2, 4), dtype=torch.int32)
+    ctx = torch.tensor([5, 6], dtype=torch.int32)
+    with pytest.raises(kvp.KvpError) as e:
+        kvp.decode_plan_build(14, 2, table, ctx, 0)
+    assert e.value.status == kvp.KVP_ERR_INVALID
+    with pytest.raises(kvp.KvpError) as e:
+        kvp.decode_plan_build(18, 2, table, ctx, 8)  # group 9
+    assert e.value.status == kvp.KVP_ERR_UNSUPPORTED
+    small = torch.empty((64,), dtype=torch.uint8)
+    with pytest.raises(kvp.KvpError) as e:
+        kvp.decode_plan_build(14, 2, table, ctx, 8, image=small)
+    assert e.value.status == kvp.KVP_ERR_INVALID
+    plan, _ = kvp.decode_plan_build(14, 2, table, ctx, 8)
+    assert plan.B == 2 and plan.group == 7 and plan.n_items % XCDS == 0
+
+
+def test_plan_padding_fixes_the_launch():
+    # successive steps of the same batch, padded to one item count: same item count and
+    # offsets, so a graph captured with the first plan replays the later ones
+    table, ctx, nb, pool, seqs = c4_tables(50)
+    plan, _ = build(table, ctx, nb)
+    pad = plan.n_items + 40
+    got = []
+    for step in range(3):
+        t = torch.from_numpy(np.ascontiguousarray(table))
+        c = torch.from_numpy(np.ascontiguousarray(ctx))
+        p, image = kvp.decode_plan_build(14, 2, t, c, nb, pad_items=pad)
+        check_plan(p, image, table, ctx, nb, 14, 2)
+        got.append((p.n_items, p.bytes, p.off_pair_base, p.off_pair_nparts, p.off_req_shared))
+        pool.append_slots(seqs)
+        table, ctx = (x.numpy() for x in pool.export(seqs, table.shape[1] + 1))
+    assert got[0][0] == ((pad + 7) // 8) * 8
+    assert len(set(got)) == 1
+    t = torch.from_numpy(np.ascontiguousarray(table))
+    c = torch.from_numpy(np.ascontiguousarray(ctx))
+    with pytest.raises(kvp.KvpError) as e:
+        kvp.decode_plan_build(14, 2, t, c, nb, pad_items=8)
+    assert e.value.status == kvp.KVP_ERR_INVALID

@@ -245,19 +245,6 @@ def test_deterministic_repeat():
     assert torch.equal(_bits(a.cpu()), _bits(b.cpu()))
 
 
-@pytest.mark.parametrize("workers", ["1", "7", "64", "333"])
-def test_worker_counts_agree(monkeypatch, workers):
-    # different worker counts cut the pairs at different tiles (and 1 worker splits none)
-    need_gpu()
-    pb = W.paged_batch(12, lo=1, hi=3000, prefix=0, group_size=1, seed=55)
-    step = PagedStep(kvp, pb, layers=1, hq=14, hkv=2, dtype=torch.float16, seed=7000)
-    q = step.q(0).cuda()
-    monkeypatch.setenv("KVP_DECODE_WORKERS", workers)
-    say("workers", workers)
-    out = to64(kvp.paged_decode_attention(step.cache, 0, q, step.table, step.ctx))
-    assert max_abs(out, step.oracle(0)) <= 2e-3
-
-
 def test_fused_append_matches_separate_append():
     need_gpu()
     pb = W.paged_batch(40, seed=91)
