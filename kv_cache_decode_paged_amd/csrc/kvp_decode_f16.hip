@@ -117,7 +117,7 @@ struct Item {
 
 // Merge the nparts partials of pair (b, g) (slots pbase ..) in slot order; lane = dim.
 template <int G>
-__device__ void merge_pair(const DecodeParams &P, int b, int g, int pbase, int nparts)
+__device__ __forceinline__ void merge_pair(const DecodeParams &P, int b, int g, int pbase, int nparts)
 {
     const int lane = threadIdx.x;
     float M[G], L[G], O[G];
@@ -208,9 +208,12 @@ __device__ __forceinline__ void run_item(const DecodeParams &P, const Addr &A, c
     const bool app = !SHARED && P.k_new != nullptr;
     i32x4 nrow = {0, 0, 0, 0};
     if (app && lane < 16) {
-        const f16 *src = (const f16 *)(lane < 8 ? P.k_new : P.v_new) + ((size_t)it.b * hkv + it.g) * D +
-                         (lane & 7) * 8;
-        nrow = *(const i32x4 *)src;
+        // K or V row by lane, as masked arithmetic (a select of the two pointers is turned
+        // into a table in scratch memory)
+        const uintptr_t kb = (uintptr_t)P.k_new, vb = (uintptr_t)P.v_new;
+        const uintptr_t base = kb + ((vb - kb) & (uintptr_t)(-(intptr_t)(lane >= 8)));
+        const size_t off = (((size_t)it.b * hkv + it.g) * D + (lane & 7) * 8) * sizeof(f16);
+        nrow = *(const __attribute__((address_space(1))) i32x4 *)(base + off);
     }
 
     const int nt = (it.nblk + 3) >> 2;
@@ -288,14 +291,12 @@ __device__ __forceinline__ void run_item(const DecodeParams &P, const Addr &A, c
                     const int c = lane & 7;
                     const int lb = it.blk0 + j;
                     const size_t dst = A.block_off(it.b, it.g, lb, e) + (size_t)A.row(lb, r & 15) * D + c * 8;
-                    if (lane < 8) {
-                        *(i32x4 *)(kt + r * 128 + ((c ^ (r & 7)) * 16)) = nrow;
-                        *(i32x4 *)((f16 *)P.kc_w + dst) = nrow;
-                    } else {
-                        const int rs = r ^ ((r >> 2) & 1);
-                        *(i32x4 *)(vt + rs * 128 + c * 16) = nrow;
-                        *(i32x4 *)((f16 *)P.vc_w + dst) = nrow;
-                    }
+                    const int rs = r ^ ((r >> 2) & 1);
+                    const int lds_off = lane < 8 ? r * 128 + ((c ^ (r & 7)) * 16) : rs * 128 + c * 16;
+                    *(i32x4 *)((lane < 8 ? kt : vt) + lds_off) = nrow;
+                    const uintptr_t kb = (uintptr_t)P.kc_w, vb = (uintptr_t)P.vc_w;
+                    const uintptr_t base = kb + ((vb - kb) & (uintptr_t)(-(intptr_t)(lane >= 8)));
+                    *(__attribute__((address_space(1))) i32x4 *)(base + dst * sizeof(f16)) = nrow;
                 }
             }
         }

@@ -8,7 +8,6 @@
 // its readers is this library's choice; the attention each request receives is unchanged
 // (same keys and values, only the order of the fp32 sums differs).
 #include <algorithm>
-#include <cstdlib>
 #include <cstring>
 #include <vector>
 
@@ -44,17 +43,10 @@ kvp_status check_plan_dims(const kvp_dims *d, const char *who)
 
 constexpr int MAX_BUNDLE = 8; // shared items kept together on one XCD
 
-int plan_bpi()
-{
-    int bpi = BPI; // blocks per item
-    if (const char *e = getenv("KVP_PLAN_BPI"))
-        bpi = std::max(1, std::min(BPI, atoi(e)));
-    return bpi;
-}
 
 long long max_items(long long B, long long hkv, long long max_blocks)
 {
-    const long long ipp = std::max<long long>(1, (max_blocks + plan_bpi() - 1) / plan_bpi());
+    const long long ipp = std::max<long long>(1, (max_blocks + BPI - 1) / BPI);
     // private items: at most ipp per pair; shared items: at most one set per two requests;
     // plus the padding that evens out the XCD queues
     const long long work = B * hkv * ipp + (B / 2) * hkv * ipp;
@@ -102,7 +94,7 @@ kvp_status decode_plan_build(const kvp_dims *dims, const int32_t *table, int32_t
         return fail(KVP_ERR_UNSUPPORTED, "%s: max_blocks too large", who);
     const int hkv = dims->num_kv_heads;
     const int G = dims->num_q_heads / hkv;
-    const int bpi = plan_bpi();
+    const int bpi = BPI; // blocks per item
     const int maxm = std::max(1, std::min(MAXM, 16 / G)); // members of a shared item (<= 16 rows)
     const long long npairs = (long long)B * hkv;
 
