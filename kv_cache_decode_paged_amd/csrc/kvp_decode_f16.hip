@@ -50,9 +50,16 @@ namespace kvp {
 using namespace dec;
 using namespace plan;
 
-constexpr int TB = TILE * D * 2;   // bytes of one K (or V) tile in LDS
 constexpr int PART_FLOATS = D + 2; // o[64], m, l
-constexpr int DMA_PER_TILE = 16;   // 8 K + 8 V loads of 1 KB
+// tile length (tokens) and ring depth of the decode kernel: 64-token tiles in a 2-slot ring
+// (32 KB of LDS, five waves per CU); 32-token tiles in a 4-slot ring hold more loads in
+// flight in the same LDS but measure about 3 % slower on the batch-200 step
+#ifndef DEC_TT
+#define DEC_TT 64
+#endif
+#ifndef DEC_NBUF
+#define DEC_NBUF 2
+#endif
 
 // s_waitcnt with only the vector-memory count set (gfx9 encoding: vmcnt in bits 3:0 and
 // 15:14, expcnt 6:4 and lgkmcnt 11:8 left at their maxima)
@@ -163,10 +170,15 @@ __device__ __forceinline__ void merge_pair(const DecodeParams &P, int b, int g, 
 }
 
 // One work item.  rv: lane R_ENT + j holds the physical id of the item's block j.
-template <int G, int NQB, bool SHARED, int NBUF, typename Addr>
+template <int G, int NQB, bool SHARED, int NBUF, int TT, typename Addr>
 __device__ __forceinline__ void run_item(const DecodeParams &P, const Addr &A, const PlanView &PV,
-                                         const Item &it, int rv, char (*kring)[TB], char (*vring)[TB])
+                                         const Item &it, int rv, char *kring, char *vring)
 {
+    static_assert(TT == 32 || TT == 64, "tile of 32 or 64 tokens");
+    constexpr int KB = TT / 16;   // blocks per tile
+    constexpr int KS = TT / 32;   // k-steps of 32 tokens per tile (value product)
+    constexpr int NDMA = TT / 4;  // 1 KB loads per tile: TT/8 for K, TT/8 for V
+    constexpr int SLOT = TT * 128; // bytes of one K (or V) tile
     const int lane = threadIdx.x;
     const int col = lane & 15, grp = lane >> 4;
     const int hkv = P.hkv;
@@ -216,17 +228,17 @@ __device__ __forceinline__ void run_item(const DecodeParams &P, const Addr &A, c
         nrow = *(const __attribute__((address_space(1))) i32x4 *)(base + off);
     }
 
-    const int nt = (it.nblk + 3) >> 2;
+    const int nt = (it.nblk + KB - 1) / KB;
     auto ent = [&](int j) -> int { return lane_int(rv, R_ENT + min(j, BPI - 1)); };
     auto block_ok = [&](int j) -> bool { return j < it.nblk && A.valid(ent(j)); };
 
     // ---- DMA of tile t into ring slot t % NBUF (16 loads, no lane masked off) ----
     auto issue = [&](int t) {
-        char *kd = kring[t % NBUF];
-        char *vd = vring[t % NBUF];
+        char *kd = kring + (t % NBUF) * SLOT;
+        char *vd = vring + (t % NBUF) * SLOT;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int j = 4 * t + (i >> 1); // item block of tile rows 8i .. 8i+7
+        for (int i = 0; i < TT / 8; ++i) {
+            const int j = KB * t + (i >> 1); // item block of tile rows 8i .. 8i+7
             const int e = ent(j);
             const bool ok = j < it.nblk && A.valid(e);
             const int lb = it.blk0 + j;
@@ -262,21 +274,27 @@ __device__ __forceinline__ void run_item(const DecodeParams &P, const Addr &A, c
     const int rend = SHARED ? BS * (it.blk0 + it.nblk) : it.end;
 
     auto compute = [&](int t) {
-        char *kt = kring[t % NBUF];
-        char *vt = vring[t % NBUF];
-        const int tb = BS * (it.blk0 + 4 * t); // position of tile row 0
-        bool bok[4];
+        char *kt = kring + (t % NBUF) * SLOT;
+        char *vt = vring + (t % NBUF) * SLOT;
+        const int tb = BS * (it.blk0 + KB * t); // position of tile row 0
+        bool bok[KB];
+        bool all_ok = true;
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb)
-            bok[kb] = block_ok(4 * t + kb);
+        for (int kb = 0; kb < KB; ++kb) {
+            bok[kb] = block_ok(KB * t + kb);
+            all_ok = all_ok && bok[kb];
+        }
         // value rows that no column may use: zero them (the cache can hold NaN there)
-        if (tb + TILE > rend || !(bok[0] && bok[1] && bok[2] && bok[3])) {
+        if (tb + TT > rend || !all_ok) {
 #pragma unroll
-            for (int k = 0; k < 8; ++k) {
+            for (int k = 0; k < TT / 8; ++k) {
                 const int ch = lane + 64 * k, rs = ch >> 3;
                 const int r = rs ^ ((rs >> 2) & 1);
                 const int kb = r >> 4;
-                const bool okb = kb == 0 ? bok[0] : (kb == 1 ? bok[1] : (kb == 2 ? bok[2] : bok[3]));
+                bool okb = bok[0];
+#pragma unroll
+                for (int q = 1; q < KB; ++q)
+                    okb = kb == q ? bok[q] : okb;
                 if (!(okb && tb + r < rend))
                     *(i32x4 *)(vt + ch * 16) = i32x4{0, 0, 0, 0};
             }
@@ -284,8 +302,8 @@ __device__ __forceinline__ void run_item(const DecodeParams &P, const Addr &A, c
         // the new token of this step: into LDS (this tile) and into the cache
         if (app) {
             const int pos = it.end - 1, r = pos - tb;
-            if (r >= 0 && r < TILE) {
-                const int j = 4 * t + (r >> 4);
+            if (r >= 0 && r < TT) {
+                const int j = KB * t + (r >> 4);
                 const int e = ent(j);
                 if (lane < 16 && j < it.nblk && A.valid(e)) {
                     const int c = lane & 7;
@@ -304,34 +322,36 @@ __device__ __forceinline__ void run_item(const DecodeParams &P, const Addr &A, c
 
         // operands of the whole tile: K rows (A of the score MFMA) and V^T (A of the value
         // MFMA: lane (col, grp), k-step ks, slot s is token 16 (2 ks + s / 4) + 4 grp + s % 4)
-        f16x8 kop[4][2];
+        f16x8 kop[KB][2];
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
+        for (int kb = 0; kb < KB; ++kb) {
             const int r = kb * 16 + col;
             kop[kb][0] = lds_b128(kt + r * 128 + ((grp ^ (r & 7)) * 16));
             kop[kb][1] = lds_b128(kt + r * 128 + (((4 + grp) ^ (r & 7)) * 16));
         }
-        uint2 vraw[2][8];
+        uint2 vraw[KS][8];
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
+        for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
             for (int s = 0; s < 8; ++s) {
                 const int tok = 16 * (2 * ks + (s >> 2)) + 4 * grp + (s & 3);
                 const int rs = tok ^ ((tok >> 2) & 1);
                 vraw[ks][s] = lds_b64(vt + rs * 128 + col * 8);
             }
-        // all 24 reads have returned before any result is used
-        asm volatile("s_waitcnt lgkmcnt(0)"
-                     : "+v"(kop[0][0]), "+v"(kop[0][1]), "+v"(kop[1][0]), "+v"(kop[1][1]), "+v"(kop[2][0]),
-                       "+v"(kop[2][1]), "+v"(kop[3][0]), "+v"(kop[3][1]));
-        asm volatile(""
-                     : "+v"(vraw[0][0]), "+v"(vraw[0][1]), "+v"(vraw[0][2]), "+v"(vraw[0][3]), "+v"(vraw[0][4]),
-                       "+v"(vraw[0][5]), "+v"(vraw[0][6]), "+v"(vraw[0][7]), "+v"(vraw[1][0]), "+v"(vraw[1][1]),
-                       "+v"(vraw[1][2]), "+v"(vraw[1][3]), "+v"(vraw[1][4]), "+v"(vraw[1][5]), "+v"(vraw[1][6]),
-                       "+v"(vraw[1][7]));
-        f16x8 vop[2][4];
+        // every read has returned before any result is used (the empty statements tie each
+        // result to the wait)
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
+        for (int kb = 0; kb < KB; ++kb)
+            asm volatile("" : "+v"(kop[kb][0]), "+v"(kop[kb][1]));
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+            for (int s = 0; s < 8; ++s)
+                asm volatile("" : "+v"(vraw[ks][s]));
+        f16x8 vop[KS][4];
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
             unsigned lo[8], hi[8];
 #pragma unroll
             for (int s = 0; s < 8; ++s) {
@@ -345,9 +365,9 @@ __device__ __forceinline__ void run_item(const DecodeParams &P, const Addr &A, c
 #pragma unroll
         for (int nb = 0; nb < NQB; ++nb) {
             // scores: sacc[kb][i] = S[token 16 kb + 4 grp + i][query row 16 nb + col]
-            f32x4 sacc[4];
+            f32x4 sacc[KB];
 #pragma unroll
-            for (int kb = 0; kb < 4; ++kb) {
+            for (int kb = 0; kb < KB; ++kb) {
                 const f32x4 s0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop[kb][0], qop[nb][0],
                                                                         f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
                 sacc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop[kb][1], qop[nb][1], s0, 0, 0, 0);
@@ -356,7 +376,7 @@ __device__ __forceinline__ void run_item(const DecodeParams &P, const Addr &A, c
             // already in this lane
             float mt = -INFINITY;
 #pragma unroll
-            for (int kb = 0; kb < 4; ++kb)
+            for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int tok = tb + kb * 16 + grp * 4 + i;
@@ -370,9 +390,9 @@ __device__ __forceinline__ void run_item(const DecodeParams &P, const Addr &A, c
             const float alpha = mn == -INFINITY ? 1.f : fast_exp2(m[nb] - mn);
             m[nb] = mn;
             float ps = 0.f;
-            f16x8 pop[2];
+            f16x8 pop[KS];
 #pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
+            for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
                 for (int s = 0; s < 8; ++s) {
                     const float p = mn == -INFINITY ? 0.f : fast_exp2(sacc[2 * ks + (s >> 2)][s & 3] - mn);
@@ -386,7 +406,7 @@ __device__ __forceinline__ void run_item(const DecodeParams &P, const Addr &A, c
             for (int db = 0; db < 4; ++db) {
                 acc[nb][db] *= alpha;
 #pragma unroll
-                for (int ks = 0; ks < 2; ++ks)
+                for (int ks = 0; ks < KS; ++ks)
                     acc[nb][db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vop[ks][db], pop[ks], acc[nb][db], 0, 0, 0);
             }
         }
@@ -403,10 +423,12 @@ __device__ __forceinline__ void run_item(const DecodeParams &P, const Addr &A, c
         if (t + NBUF - 1 < nt)
             issue(t + NBUF - 1);
         const int ahead = min(nt - 1 - t, NBUF - 1); // tiles issued after this one
-        if (ahead >= 2)
-            wait_vm<2 * DMA_PER_TILE>();
+        if (ahead >= 3)
+            wait_vm<3 * NDMA>();
+        else if (ahead == 2)
+            wait_vm<2 * NDMA>();
         else if (ahead == 1)
-            wait_vm<DMA_PER_TILE>();
+            wait_vm<NDMA>();
         else
             wait_vm<0>();
         compute(t);
@@ -493,12 +515,13 @@ __device__ __forceinline__ void run_item(const DecodeParams &P, const Addr &A, c
     }
 }
 
-template <int G, int NBUF, bool PLANNED, typename Addr>
+template <int G, int NBUF, int TT, bool PLANNED, typename Addr>
 __global__ __launch_bounds__(64) void decode_f16_kernel(DecodeParams P, Addr A, PlanView PV)
 {
     static_assert(G >= 1 && G <= MAXG, "group size");
-    __shared__ __attribute__((aligned(16))) char kring[NBUF][TB];
-    __shared__ __attribute__((aligned(16))) char vring[NBUF][TB];
+    static_assert(NBUF >= 2 && NBUF <= 4, "ring depth");
+    __shared__ __attribute__((aligned(16))) char kring[NBUF * TT * 128];
+    __shared__ __attribute__((aligned(16))) char vring[NBUF * TT * 128];
     const int lane = threadIdx.x;
     Item it;
     int rv;
@@ -524,12 +547,12 @@ __global__ __launch_bounds__(64) void decode_f16_kernel(DecodeParams P, Addr A, 
         if (flags & F_SHARED) {
             if (it.nmem * G > 16 || it.slot < 0)
                 return;
-            run_item<G, 1, true, NBUF>(P, A, PV, it, rv, kring, vring);
+            run_item<G, 1, true, NBUF, TT>(P, A, PV, it, rv, kring, vring);
             return;
         }
         if (it.nmem != 1)
             return;
-        run_item<G, 1, false, NBUF>(P, A, PV, it, rv, kring, vring);
+        run_item<G, 1, false, NBUF, TT>(P, A, PV, it, rv, kring, vring);
     } else {
         const int pair = blockIdx.x / PV.ipp;
         const int k = blockIdx.x - pair * PV.ipp;
@@ -539,18 +562,22 @@ __global__ __launch_bounds__(64) void decode_f16_kernel(DecodeParams P, Addr A, 
         int ctx = P.ctx_lens[it.b];
         ctx = ctx < 0 ? 0 : (ctx > maxc ? maxc : ctx);
         const int nbt = (ctx + BS - 1) / BS;
-        it.blk0 = k * BPI;
-        if (k > 0 && it.blk0 >= nbt)
+        // one item up to BPI blocks, else ceil(blocks / SPLIT_BLOCKS) parts of equal tile
+        // counts: part k holds tiles [k T / n, (k+1) T / n) of the pair's T tiles
+        const int n = nbt <= BPI ? 1 : (nbt + SPLIT_BLOCKS - 1) / SPLIT_BLOCKS;
+        if (k >= n)
             return;
+        const int T = (nbt + 3) >> 2;
+        it.blk0 = 4 * (int)((long long)k * T / n);
         it.nmem = 1;
-        it.nblk = max(0, min(BPI, nbt - it.blk0));
+        it.nblk = max(0, min(4 * (int)((long long)(k + 1) * T / n), nbt) - it.blk0);
         it.end = ctx;
-        it.nparts = max(1, (nbt + BPI - 1) / BPI);
+        it.nparts = n;
         it.pbase = pair * PV.ipp;
         it.slot = it.pbase + k;
         const int j = lane - R_ENT;
         rv = (j >= 0 && j < it.nblk) ? A.entry(it.b, it.blk0 + j) : -1;
-        run_item<G, 1, false, NBUF>(P, A, PV, it, rv, kring, vring);
+        run_item<G, 1, false, NBUF, TT>(P, A, PV, it, rv, kring, vring);
     }
 }
 
@@ -567,7 +594,7 @@ static kvp_status launch_f16(const DecodeParams &P, const Addr &A, const PlanVie
     switch (group) {
 #define KVP_G(GG)                                                                                  \
     case GG:                                                                                       \
-        hipLaunchKernelGGL((decode_f16_kernel<GG, 2, PLANNED, Addr>), g, block, 0, st, P, A, PV); \
+        hipLaunchKernelGGL((decode_f16_kernel<GG, DEC_NBUF, DEC_TT, PLANNED, Addr>), g, block, 0, st, P, A, PV); \
         break;
         KVP_G(1) KVP_G(2) KVP_G(3) KVP_G(4) KVP_G(5) KVP_G(6) KVP_G(7) KVP_G(8)
 #undef KVP_G
@@ -583,7 +610,7 @@ static kvp_status launch_f16(const DecodeParams &P, const Addr &A, const PlanVie
 int decode_f16_items_per_pair(int max_context)
 {
     const int nb = (std::max(max_context, 1) + BS - 1) / BS;
-    return (nb + BPI - 1) / BPI;
+    return nb <= BPI ? 1 : (nb + SPLIT_BLOCKS - 1) / SPLIT_BLOCKS;
 }
 
 size_t decode_f16_part_bytes(long long slots)

@@ -58,6 +58,21 @@ size_t image_bytes_for(long long items, long long B, long long hkv)
     return align16((size_t)items * REC * 4) + 2 * align16((size_t)B * hkv * 4) + align16((size_t)B * 4);
 }
 
+// parts of a range of nb blocks: one item up to BPI blocks unless `forced` (the pair has
+// other parts anyway), else ceil(nb / SPLIT_BLOCKS) parts of equal tile counts
+int split_parts(int nb, bool forced)
+{
+    if (nb <= 0 || (!forced && nb <= BPI))
+        return 1;
+    return (nb + SPLIT_BLOCKS - 1) / SPLIT_BLOCKS;
+}
+// first block of part k of n over nb blocks (part k holds tiles [k T / n, (k+1) T / n))
+int split_start(int nb, int n, int k)
+{
+    const int T = (nb + 3) / 4;
+    return std::min(nb, 4 * (int)((long long)k * T / n));
+}
+
 struct SubRun {
     int a, n, shared_tokens, run;
 };
@@ -94,7 +109,6 @@ kvp_status decode_plan_build(const kvp_dims *dims, const int32_t *table, int32_t
         return fail(KVP_ERR_UNSUPPORTED, "%s: max_blocks too large", who);
     const int hkv = dims->num_kv_heads;
     const int G = dims->num_q_heads / hkv;
-    const int bpi = BPI; // blocks per item
     const int maxm = std::max(1, std::min(MAXM, 16 / G)); // members of a shared item (<= 16 rows)
     const long long npairs = (long long)B * hkv;
 
@@ -150,11 +164,16 @@ kvp_status decode_plan_build(const kvp_dims *dims, const int32_t *table, int32_t
     // ---- parts per pair and slot ranges ----
     // shared items a member takes part in: those starting below its shared extent
     std::vector<int> shared_parts(B, 0);
-    for (int b = 0; b < B; ++b)
-        shared_parts[b] = (E[b] / BS + bpi - 1) / bpi;
+    for (const SubRun &sr : subs) {
+        const int nsb = sr.shared_tokens / BS;
+        const int ns = split_parts(nsb, true);
+        for (int m = sr.a; m < sr.a + sr.n; ++m)
+            for (int k = 0; k < ns; ++k)
+                if (BS * split_start(nsb, ns, k) < E[m])
+                    ++shared_parts[m];
+    }
     auto private_items = [&](int b) -> int {
-        const int nb = nbt[b] - E[b] / BS;
-        return nb <= 0 ? 1 : (nb + bpi - 1) / bpi;
+        return split_parts(nbt[b] - E[b] / BS, E[b] > 0);
     };
     std::vector<int> pair_base(npairs, -1), pair_nparts(npairs, 1);
     long long slots = 0, n_items = 0;
@@ -170,7 +189,7 @@ kvp_status decode_plan_build(const kvp_dims *dims, const int32_t *table, int32_t
         }
     long long n_shared = 0;
     for (const SubRun &s : subs)
-        n_shared += (long long)hkv * ((s.shared_tokens / BS + bpi - 1) / bpi);
+        n_shared += (long long)hkv * split_parts(s.shared_tokens / BS, true);
     n_items += n_shared;
     if (slots > 0x7fffffffLL || n_items > 0x7fffffffLL)
         return fail(KVP_ERR_UNSUPPORTED, "%s: plan too large", who);
@@ -206,10 +225,12 @@ kvp_status decode_plan_build(const kvp_dims *dims, const int32_t *table, int32_t
         std::vector<std::pair<long long, long long>> keyed; // (run * hkv + g, item)
         for (const SubRun &sr : subs) {
             const int nsb = sr.shared_tokens / BS;
+            const int ns = split_parts(nsb, true);
             for (int g = 0; g < hkv; ++g)
-                for (int k = 0; k * bpi < nsb; ++k) {
+                for (int k = 0; k < ns; ++k) {
+                    const int b0 = split_start(nsb, ns, k), b1 = split_start(nsb, ns, k + 1);
                     keyed.push_back({(long long)sr.run * hkv + g, idx});
-                    record(F_SHARED, sr.a, g, sr.n, k * bpi, std::min(bpi, nsb - k * bpi), 0, k, 0, -1, sr.a);
+                    record(F_SHARED, sr.a, g, sr.n, b0, b1 - b0, 0, k, 0, -1, sr.a);
                 }
         }
         std::stable_sort(keyed.begin(), keyed.end(),
@@ -229,8 +250,9 @@ kvp_status decode_plan_build(const kvp_dims *dims, const int32_t *table, int32_t
         for (int g = 0; g < hkv; ++g) {
             const long long p = (long long)b * hkv + g;
             for (int k = 0; k < npriv; ++k) {
-                const int blk0 = first + k * bpi;
-                const int nblk = std::max(0, std::min(bpi, nbt[b] - blk0));
+                const int nb = nbt[b] - first;
+                const int blk0 = first + split_start(nb, npriv, k);
+                const int nblk = nb <= 0 ? 0 : first + split_start(nb, npriv, k + 1) - blk0;
                 const int slot = pair_nparts[p] > 1 ? pair_base[p] + shared_parts[b] + k : -1;
                 record(0, b, g, 1, blk0, nblk, c[b], slot, pair_nparts[p], pair_base[p], b);
             }

@@ -16,7 +16,12 @@
 namespace kvp {
 namespace plan {
 
-constexpr int BPI = 32;  // blocks per work item (8 tiles of 64 tokens)
+constexpr int BPI = 32;  // blocks per work item (512 tokens)
+// A pair (or shared unit) of at most BPI blocks is one item when nothing else splits it;
+// otherwise it is cut into ceil(blocks / SPLIT_BLOCKS) parts of equal tile counts (at most
+// BPI blocks each).  Shorter parts mean more waves, and the decode time grows with the wave
+// count faster than the shorter tail saves, so the parts are as long as an item may be.
+constexpr int SPLIT_BLOCKS = 32;
 constexpr int REC = 48;  // int32 per record
 constexpr int MAXM = 16; // members of one shared item (and at most 16 query rows)
 constexpr int XCDS = 8;  // MI355X: workgroup i runs on XCD i % 8 (round-robin dispatch)

@@ -81,8 +81,8 @@ def test_device_calls_reject_bad_arguments_before_launch():
 
 def test_workspace_size():
     import kv_cache_decode_paged_amd as kvp
-    # fp16: one partial per 512-token split of every pair (8 head slots x 66 floats) +
-    # one ticket per pair
+    # fp16: a pair longer than 32 blocks is cut into ceil(blocks / 32) parts, one partial per
+    # part (8 head slots x 66 floats) + one ticket per pair; 32768 tokens = 2048 blocks -> 64
     ws = kvp.decode_workspace_bytes(14, 2, torch.float16, 32, 32768)
     assert ws == 32 * 2 * 64 * 8 * 66 * 4 + 256
     # contexts of at most 512 tokens are never split: no workspace

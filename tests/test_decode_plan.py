@@ -7,8 +7,8 @@ plan must guarantee, read independently from the image:
 * a pair split into several parts has slots pbase .. pbase+nparts-1, each written once,
   in token order (the merge order), and single-part pairs are written directly;
 * shared items hold at most 16 query rows and a prefix's items run on one XCD;
-* without prefix sharing the plan is exactly the per-pair split of 32 blocks that
-  paged_decode_attention uses (so the two are bit-identical on the GPU).
+* without prefix sharing the plan is exactly the per-pair split (one item up to 32 blocks,
+  else ceil(blocks/32) parts of equal tile counts) that paged_decode_attention uses (so the two are bit-identical on the GPU).
 
 Prefix sharing follows the pages: requests forked from one prefix share its physical
 blocks until copy-on-write ([PAGED] paged-attention article, SECTION 3).
@@ -162,9 +162,11 @@ def test_plan_without_sharing_is_the_plain_split():
     want = []
     for b in range(len(ctx)):
         nbt = math.ceil(ctx[b] / BS)
+        n, T = (1 if nbt <= BPI else math.ceil(nbt / BPI)), math.ceil(nbt / 4)
         for g in range(2):
-            for k in range(max(1, math.ceil(nbt / BPI))):
-                want.append((b, g, BPI * k, max(0, min(BPI, nbt - BPI * k))))
+            for k in range(n):  # equal tile counts per part
+                b0, b1 = min(nbt, 4 * (k * T // n)), min(nbt, 4 * ((k + 1) * T // n))
+                want.append((b, g, b0, b1 - b0))
     assert got == sorted(want)
 
 
