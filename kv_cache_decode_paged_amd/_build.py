@@ -20,6 +20,9 @@ ARCH = "gfx950"
 def hip_flags():
     return ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall",
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            # MFMA accumulators in ordinary VGPRs: no copies between accumulation registers
+            # and VGPRs around the VALU work on scores and outputs
+            "-mllvm", "-amdgpu-mfma-vgpr-form",
             "-I", os.path.join(ROOT, "include"), "-I", CSRC]
 
 

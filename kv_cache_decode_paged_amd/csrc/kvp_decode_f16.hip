@@ -51,12 +51,7 @@ using namespace dec;
 using namespace plan;
 
 constexpr int PART_FLOATS = D + 2; // o[64], m, l
-// tile length (tokens) and ring depth of the decode kernel: 64-token tiles in a 2-slot ring
-// (32 KB of LDS, five waves per CU); 32-token tiles in a 4-slot ring hold more loads in
-// flight in the same LDS but measure about 3 % slower on the batch-200 step
-#ifndef DEC_TT
-#define DEC_TT 64
-#endif
+// ring depth of the decode kernel: two 64-token slots (32 KB of LDS, five waves per CU)
 #ifndef DEC_NBUF
 #define DEC_NBUF 2
 #endif
@@ -96,19 +91,31 @@ __device__ inline uint2 lds_b64(const char *p)
     return r;
 }
 
-// V^T operand of one k-step for dim 4 col + db: lane (col, grp) read dims 4col..4col+3 of
-// the 8 tokens of its k-group as 64-bit words (lo: dims 0-1, hi: dims 2-3); dword w of the
-// operand packs tokens 2w, 2w+1
-__device__ inline f16x8 vt_operand(const unsigned (&lo)[8], const unsigned (&hi)[8], int db)
+__device__ inline f16x4 lds_tr16_b64(const char *p)
 {
-    const unsigned sel = (db & 1) ? 0x07060302u : 0x05040100u;
-    const unsigned *src = (db >> 1) ? hi : lo;
-    unsigned w[4];
-#pragma unroll
-    for (int k = 0; k < 4; ++k)
-        w[k] = __builtin_amdgcn_perm(src[2 * k + 1], src[2 * k], sel);
-    return __builtin_bit_cast(f16x8, (i32x4){(int)w[0], (int)w[1], (int)w[2], (int)w[3]});
+    f16x4 r;
+    asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(r) : "v"(lds_addr(p)));
+    return r;
 }
+__device__ inline void lds_store_b128(char *p, i32x4 v)
+{
+    asm volatile("ds_write_b128 %0, %1" ::"v"(lds_addr(p)), "v"(v) : "memory");
+}
+
+// max over lanes col, col + 16, col + 32, col + 48 (the k-groups of one MFMA column): swap
+// odd and even 16-lane rows, then the two 32-lane halves, without an LDS round trip
+__device__ inline float group_max(float x)
+{
+    const unsigned u = __builtin_bit_cast(unsigned, x);
+    const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    x = fmaxf(__builtin_bit_cast(float, (unsigned)a[0]), __builtin_bit_cast(float, (unsigned)a[1]));
+    const unsigned w = __builtin_bit_cast(unsigned, x);
+    const auto b = __builtin_amdgcn_permlane32_swap(w, w, false, false);
+    return fmaxf(__builtin_bit_cast(float, (unsigned)b[0]), __builtin_bit_cast(float, (unsigned)b[1]));
+}
+
+// growth of a column's maximum (log2 units) that moves its softmax reference
+constexpr float RESCALE_LOG2 = 8.f;
 
 struct PlanView {
     const int *items;       // planned: [n_items][REC]
@@ -170,52 +177,67 @@ __device__ __forceinline__ void merge_pair(const DecodeParams &P, int b, int g, 
 }
 
 // One work item.  rv: lane R_ENT + j holds the physical id of the item's block j.
-template <int G, int NQB, bool SHARED, int NBUF, int TT, typename Addr>
+//
+// Tile t = 64 tokens = blocks 4t .. 4t+3 of the item.  Lane (col, grp) = (lane % 16,
+// lane / 16).  MFMA column col is query row col of the item (member col / G, head col % G).
+// K and V tiles sit in LDS as 64 rows of 128 bytes; 16-byte chunk c of row r is stored at
+// chunk slot c ^ (r & 7).
+template <int G, bool SHARED, int NBUF, typename Addr>
 __device__ __forceinline__ void run_item(const DecodeParams &P, const Addr &A, const PlanView &PV,
                                          const Item &it, int rv, char *kring, char *vring)
 {
-    static_assert(TT == 32 || TT == 64, "tile of 32 or 64 tokens");
-    constexpr int KB = TT / 16;   // blocks per tile
-    constexpr int KS = TT / 32;   // k-steps of 32 tokens per tile (value product)
-    constexpr int NDMA = TT / 4;  // 1 KB loads per tile: TT/8 for K, TT/8 for V
+    constexpr int TT = TILE;       // tokens per tile
+    constexpr int KB = TT / BS;    // blocks per tile
+    constexpr int KS = TT / 32;    // k-steps of 32 tokens per tile (value product)
+    constexpr int NDMA = 2 * KB * 2; // 1 KB loads per tile: two per block for K and for V
     constexpr int SLOT = TT * 128; // bytes of one K (or V) tile
     const int lane = threadIdx.x;
     const int col = lane & 15, grp = lane >> 4;
     const int hkv = P.hkv;
     const f16 *kc = (const f16 *)P.kc;
     const f16 *vc = (const f16 *)P.vc;
+    const float c = P.scale_log2;
 
-    // ---- per query-row column: q operand, token limit, output slot ----
-    // column block nb, column col is query row r = 16 nb + col: member r / G, head r % G
-    f16x8 qop[NQB][2];
-    int lim[NQB], pb[NQB], np[NQB];
-#pragma unroll
-    for (int nb = 0; nb < NQB; ++nb) {
-        const int r = nb * 16 + col;
-        const int mem = r / G, hd = r - mem * G;
-        const bool cv = mem < it.nmem;
-        const int bm = it.b + (cv ? mem : 0);
+    // ---- this lane's query row: q operand, token limit, output slot ----
+    const int mem = col / G, hd = col - mem * G;
+    const bool cv = mem < it.nmem;
+    const int bm = it.b + (cv ? mem : 0);
+    f16x8 qop[2];
+    {
         const f16 *qp = (const f16 *)P.q + ((size_t)bm * P.hq + (size_t)it.g * G + hd) * D + grp * 8;
         const f16x8 q0 = *(const f16x8 *)qp;
         const f16x8 q1 = *(const f16x8 *)(qp + 32);
         const f16x8 z = {0, 0, 0, 0, 0, 0, 0, 0};
-        qop[nb][0] = cv ? q0 : z;
-        qop[nb][1] = cv ? q1 : z;
-        if constexpr (SHARED) {
-            // a member takes part if its shared extent reaches into this item; its part
-            // index inside the pair's slot range is the item's R_SLOT
-            const int pair = bm * hkv + it.g;
-            const int l0 = PV.req_shared[bm], b0 = PV.pair_base[pair], n0 = PV.pair_nparts[pair];
-            const bool in = cv && l0 > BS * it.blk0;
-            lim[nb] = in ? l0 : 0;
-            pb[nb] = b0 + it.slot;
-            np[nb] = in ? n0 : 0;
-        } else {
-            lim[nb] = cv ? it.end : 0;
-            pb[nb] = it.slot;
-            np[nb] = it.nparts;
-        }
+        qop[0] = cv ? q0 : z;
+        qop[1] = cv ? q1 : z;
     }
+    // lim: tokens >= lim are masked for this row; rows whose results are not kept (padding
+    // columns, members that do not take part) have no limit -- their columns of the MFMA
+    // tiles are independent of the others and are never stored
+    int lim, pb, np;
+    if constexpr (SHARED) {
+        // a member takes part if its shared extent reaches into this item; its part index
+        // inside the pair's slot range is the item's R_SLOT
+        const int pair = bm * hkv + it.g;
+        const int l0 = PV.req_shared[bm], b0 = PV.pair_base[pair], n0 = PV.pair_nparts[pair];
+        const bool in = cv && l0 > BS * it.blk0;
+        lim = in ? l0 : 0x7fffffff;
+        pb = b0 + it.slot;
+        np = in ? n0 : 0;
+    } else {
+        lim = cv ? it.end : 0x7fffffff;
+        pb = it.slot;
+        np = it.nparts;
+    }
+    // tokens >= rend hold no data for any column of this item
+    const int rend = SHARED ? BS * (it.blk0 + it.nblk) : it.end;
+    // a tile ending at or before full_end needs no masking (when all its blocks are valid)
+    int full_end = rend;
+    if constexpr (SHARED) {
+        for (int m = 0; m < it.nmem; ++m)
+            full_end = min(full_end, lane_int(lim, m * G));
+    }
+
     // the step's new K / V row (lanes 0-7: K chunks, 8-15: V chunks)
     const bool app = !SHARED && P.k_new != nullptr;
     i32x4 nrow = {0, 0, 0, 0};
@@ -230,48 +252,44 @@ __device__ __forceinline__ void run_item(const DecodeParams &P, const Addr &A, c
 
     const int nt = (it.nblk + KB - 1) / KB;
     auto ent = [&](int j) -> int { return lane_int(rv, R_ENT + min(j, BPI - 1)); };
-    auto block_ok = [&](int j) -> bool { return j < it.nblk && A.valid(ent(j)); };
+    auto block_ok = [&](int j) -> bool { return (j < it.nblk) & A.valid(ent(j)); };
 
-    // ---- DMA of tile t into ring slot t % NBUF (16 loads, no lane masked off) ----
+    // ---- DMA of tile t into ring slot t % NBUF: per block, rows 0-7 then 8-15 of K and V
+    // (lane: row 8 h + lane / 8, chunk lane % 8 of the LDS row) ----
     auto issue = [&](int t) {
         char *kd = kring + (t % NBUF) * SLOT;
         char *vd = vring + (t % NBUF) * SLOT;
 #pragma unroll
-        for (int i = 0; i < TT / 8; ++i) {
-            const int j = KB * t + (i >> 1); // item block of tile rows 8i .. 8i+7
+        for (int kb = 0; kb < KB; ++kb) {
+            const int j = KB * t + kb;
             const int e = ent(j);
-            const bool ok = j < it.nblk && A.valid(e);
+            const bool ok = (j < it.nblk) & A.valid(e);
             const int lb = it.blk0 + j;
             const size_t base = ok ? A.block_off(it.b, it.g, lb, e) : A.safe_off(it.b, it.g);
-            // K: LDS row r, chunk slot (lane & 7) holds chunk (lane & 7) ^ (r & 7)
-            const int r = 8 * i + (lane >> 3);
-            const int rk = ok ? A.row(lb, r & 15) : A.safe_row(r & 15);
-            const int cg = (lane & 7) ^ (r & 7);
-            __builtin_amdgcn_global_load_lds((const void *)(kc + base + (size_t)rk * D + cg * 8),
-                                             (__attribute__((address_space(3))) void *)(kd + i * 1024),
-                                             16, 0, 0);
-            // V: LDS row slot r holds tile row r ^ ((r >> 2) & 1) (rows 4 apart land in
-            // different bank halves for the transposed 8-byte reads)
-            const int rvv = r ^ ((r >> 2) & 1);
-            const int rw = ok ? A.row(lb, rvv & 15) : A.safe_row(rvv & 15);
-            __builtin_amdgcn_global_load_lds((const void *)(vc + base + (size_t)rw * D + (lane & 7) * 8),
-                                             (__attribute__((address_space(3))) void *)(vd + i * 1024),
-                                             16, 0, 0);
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int r = 8 * h + (lane >> 3);
+                const int sr = ok ? A.row(lb, r) : A.safe_row(r);
+                const size_t off = base + (size_t)sr * D + (((lane & 7) ^ (r & 7)) * 8);
+                const int i = 2 * kb + h;
+                __builtin_amdgcn_global_load_lds((const void *)(kc + off),
+                                                 (__attribute__((address_space(3))) void *)(kd + i * 1024),
+                                                 16, 0, 0);
+                __builtin_amdgcn_global_load_lds((const void *)(vc + off),
+                                                 (__attribute__((address_space(3))) void *)(vd + i * 1024),
+                                                 16, 0, 0);
+            }
         }
     };
 
-    float m[NQB], lsum[NQB];
-    f32x4 acc[NQB][4];
+    // running state of this lane's column: reference max (scaled, log2 units), output
+    // O^T rows 16 db + 4 grp + i, and the row sum (every entry of accl holds it)
+    float mref = -INFINITY;
+    f32x4 acc[4], accl = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int nb = 0; nb < NQB; ++nb) {
-        m[nb] = -INFINITY;
-        lsum[nb] = 0.f;
-#pragma unroll
-        for (int db = 0; db < 4; ++db)
-            acc[nb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
-    // tokens >= rend hold no data for any column of this item
-    const int rend = SHARED ? BS * (it.blk0 + it.nblk) : it.end;
+    for (int db = 0; db < 4; ++db)
+        acc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const f16x8 ones = {1, 1, 1, 1, 1, 1, 1, 1};
 
     auto compute = [&](int t) {
         char *kt = kring + (t % NBUF) * SLOT;
@@ -284,19 +302,19 @@ __device__ __forceinline__ void run_item(const DecodeParams &P, const Addr &A, c
             bok[kb] = block_ok(KB * t + kb);
             all_ok = all_ok && bok[kb];
         }
+        const bool full = all_ok && tb + TT <= full_end;
         // value rows that no column may use: zero them (the cache can hold NaN there)
-        if (tb + TT > rend || !all_ok) {
+        if (!full) {
 #pragma unroll
             for (int k = 0; k < TT / 8; ++k) {
-                const int ch = lane + 64 * k, rs = ch >> 3;
-                const int r = rs ^ ((rs >> 2) & 1);
+                const int ch = lane + 64 * k, r = ch >> 3;
                 const int kb = r >> 4;
                 bool okb = bok[0];
 #pragma unroll
                 for (int q = 1; q < KB; ++q)
                     okb = kb == q ? bok[q] : okb;
                 if (!(okb && tb + r < rend))
-                    *(i32x4 *)(vt + ch * 16) = i32x4{0, 0, 0, 0};
+                    lds_store_b128(vt + ch * 16, i32x4{0, 0, 0, 0});
             }
         }
         // the new token of this step: into LDS (this tile) and into the cache
@@ -306,12 +324,10 @@ __device__ __forceinline__ void run_item(const DecodeParams &P, const Addr &A, c
                 const int j = KB * t + (r >> 4);
                 const int e = ent(j);
                 if (lane < 16 && j < it.nblk && A.valid(e)) {
-                    const int c = lane & 7;
+                    const int ch = lane & 7;
                     const int lb = it.blk0 + j;
-                    const size_t dst = A.block_off(it.b, it.g, lb, e) + (size_t)A.row(lb, r & 15) * D + c * 8;
-                    const int rs = r ^ ((r >> 2) & 1);
-                    const int lds_off = lane < 8 ? r * 128 + ((c ^ (r & 7)) * 16) : rs * 128 + c * 16;
-                    *(i32x4 *)((lane < 8 ? kt : vt) + lds_off) = nrow;
+                    const size_t dst = A.block_off(it.b, it.g, lb, e) + (size_t)A.row(lb, r & 15) * D + ch * 8;
+                    lds_store_b128((lane < 8 ? kt : vt) + r * 128 + ((ch ^ (r & 7)) * 16), nrow);
                     const uintptr_t kb = (uintptr_t)P.kc_w, vb = (uintptr_t)P.vc_w;
                     const uintptr_t base = kb + ((vb - kb) & (uintptr_t)(-(intptr_t)(lane >= 8)));
                     *(__attribute__((address_space(1))) i32x4 *)(base + dst * sizeof(f16)) = nrow;
@@ -320,8 +336,7 @@ __device__ __forceinline__ void run_item(const DecodeParams &P, const Addr &A, c
         }
         wave_lds_sync();
 
-        // operands of the whole tile: K rows (A of the score MFMA) and V^T (A of the value
-        // MFMA: lane (col, grp), k-step ks, slot s is token 16 (2 ks + s / 4) + 4 grp + s % 4)
+        // K rows (A of the score MFMA): row 16 kb + col, dims 8 grp .. and 32 + 8 grp ..
         f16x8 kop[KB][2];
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
@@ -329,15 +344,23 @@ __device__ __forceinline__ void run_item(const DecodeParams &P, const Addr &A, c
             kop[kb][0] = lds_b128(kt + r * 128 + ((grp ^ (r & 7)) * 16));
             kop[kb][1] = lds_b128(kt + r * 128 + (((4 + grp) ^ (r & 7)) * 16));
         }
-        uint2 vraw[KS][8];
+        // V^T (A of the value MFMA) of k-step ks and dims 16 db ..: lane (col, grp) needs
+        // V[token][16 db + col] for its k-slots s, token 16 (2 ks + s / 4) + 4 grp + s % 4.
+        // A transposing read hands lane i of a 16-lane group half i % 4 of the 8 bytes
+        // addressed by lane 4 j + i / 4 as its element j; so lane L of the group addresses
+        // token row 16 (2 ks + h) + 4 grp + L / 4, dims 16 db + 4 (L % 4) .. + 3, and the two
+        // reads h = 0, 1 give slots 0-3 and 4-7.
+        f16x4 vraw[KS][4][2];
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-            for (int s = 0; s < 8; ++s) {
-                const int tok = 16 * (2 * ks + (s >> 2)) + 4 * grp + (s & 3);
-                const int rs = tok ^ ((tok >> 2) & 1);
-                vraw[ks][s] = lds_b64(vt + rs * 128 + col * 8);
-            }
+            for (int db = 0; db < 4; ++db)
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const int row = 16 * (2 * ks + h) + 4 * grp + (col >> 2);
+                    const int ch = 2 * db + ((col & 3) >> 1);
+                    vraw[ks][db][h] = lds_tr16_b64(vt + row * 128 + ((ch ^ (row & 7)) * 16) + (col & 1) * 8);
+                }
         // every read has returned before any result is used (the empty statements tie each
         // result to the wait)
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
@@ -347,68 +370,65 @@ __device__ __forceinline__ void run_item(const DecodeParams &P, const Addr &A, c
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-            for (int s = 0; s < 8; ++s)
-                asm volatile("" : "+v"(vraw[ks][s]));
-        f16x8 vop[KS][4];
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            unsigned lo[8], hi[8];
-#pragma unroll
-            for (int s = 0; s < 8; ++s) {
-                lo[s] = vraw[ks][s].x;
-                hi[s] = vraw[ks][s].y;
-            }
-#pragma unroll
             for (int db = 0; db < 4; ++db)
-                vop[ks][db] = vt_operand(lo, hi, db);
+                asm volatile("" : "+v"(vraw[ks][db][0]), "+v"(vraw[ks][db][1]));
+
+        // scores: sacc[kb][i] = S[token 16 kb + 4 grp + i][column col] (unscaled)
+        f32x4 sacc[KB];
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+            const f32x4 s0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop[kb][0], qop[0],
+                                                                    f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+            sacc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop[kb][1], qop[1], s0, 0, 0, 0);
         }
-#pragma unroll
-        for (int nb = 0; nb < NQB; ++nb) {
-            // scores: sacc[kb][i] = S[token 16 kb + 4 grp + i][query row 16 nb + col]
-            f32x4 sacc[KB];
-#pragma unroll
-            for (int kb = 0; kb < KB; ++kb) {
-                const f32x4 s0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop[kb][0], qop[nb][0],
-                                                                        f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-                sacc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop[kb][1], qop[nb][1], s0, 0, 0, 0);
-            }
-            // softmax; the P^T operand of k-step ks, slot s is sacc[2 ks + s / 4][s % 4] --
-            // already in this lane
-            float mt = -INFINITY;
+        if (!full) {
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int tok = tb + kb * 16 + grp * 4 + i;
-                    const float x = (bok[kb] && tok < lim[nb]) ? sacc[kb][i] * P.scale_log2 : -INFINITY;
-                    sacc[kb][i] = x;
-                    mt = fmaxf(mt, x);
+                    sacc[kb][i] = (bok[kb] && tok < lim) ? sacc[kb][i] : -INFINITY;
                 }
-            mt = fmaxf(mt, lane_xor(mt, 16));
-            mt = fmaxf(mt, lane_xor(mt, 32));
-            const float mn = fmaxf(m[nb], mt);
-            const float alpha = mn == -INFINITY ? 1.f : fast_exp2(m[nb] - mn);
-            m[nb] = mn;
-            float ps = 0.f;
-            f16x8 pop[KS];
+        }
+        float mt = fmaxf(fmaxf(sacc[0][0], sacc[0][1]), fmaxf(sacc[0][2], sacc[0][3]));
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
+        for (int kb = 1; kb < KB; ++kb)
+            mt = fmaxf(mt, fmaxf(fmaxf(sacc[kb][0], sacc[kb][1]), fmaxf(sacc[kb][2], sacc[kb][3])));
+        mt = group_max(mt) * c;
+        // the reference max moves only when a column's maximum passes it by more than 2^8:
+        // between moves p = 2^(s c - mref) stays below 256, exact in fp16 range, and the
+        // output and row sum need no rescaling
+        if (__ballot(mt > mref + RESCALE_LOG2) != 0) {
+            const float mn = fmaxf(mref, mt);
+            const float alpha = mref == -INFINITY ? 0.f : fast_exp2(mref - mn);
 #pragma unroll
-                for (int s = 0; s < 8; ++s) {
-                    const float p = mn == -INFINITY ? 0.f : fast_exp2(sacc[2 * ks + (s >> 2)][s & 3] - mn);
-                    pop[ks][s] = (f16)p;
-                    ps += (float)pop[ks][s];
-                }
+            for (int db = 0; db < 4; ++db)
+                acc[db] *= alpha;
+            accl *= alpha;
+            mref = mn;
+        }
+        const float mc = mref == -INFINITY ? 0.f : mref;
+        // P^T operand of k-step ks, slot s = p of token 16 (2 ks + s / 4) + 4 grp + s % 4:
+        // sacc[2 ks + s / 4][s % 4] -- already in this lane; rounded once to fp16
+        f16x8 pop[KS];
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+            for (int s = 0; s < 8; s += 2) {
+                const float p0 = fast_exp2(fmaf(sacc[2 * ks + (s >> 2)][s & 3], c, -mc));
+                const float p1 = fast_exp2(fmaf(sacc[2 * ks + (s >> 2)][(s & 3) + 1], c, -mc));
+                pop[ks][s] = (f16)p0;
+                pop[ks][s + 1] = (f16)p1;
             }
-            lsum[nb] = lsum[nb] * alpha + ps;
-            // values: acc[nb][db][i] = O[query row 16 nb + col][dim 16 grp + 4 i + db]
+        // values: acc[db][i] = O[column col][dim 16 db + 4 grp + i]; row sums from a ones operand
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
             for (int db = 0; db < 4; ++db) {
-                acc[nb][db] *= alpha;
-#pragma unroll
-                for (int ks = 0; ks < KS; ++ks)
-                    acc[nb][db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vop[ks][db], pop[ks], acc[nb][db], 0, 0, 0);
+                const f16x8 vop = __builtin_shufflevector(vraw[ks][db][0], vraw[ks][db][1], 0, 1, 2, 3, 4, 5, 6, 7);
+                acc[db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vop, pop[ks], acc[db], 0, 0, 0);
             }
+            accl = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, pop[ks], accl, 0, 0, 0);
         }
         wait_lds(); // this slot is refilled by a later DMA
         wave_lds_sync();
@@ -423,9 +443,7 @@ __device__ __forceinline__ void run_item(const DecodeParams &P, const Addr &A, c
         if (t + NBUF - 1 < nt)
             issue(t + NBUF - 1);
         const int ahead = min(nt - 1 - t, NBUF - 1); // tiles issued after this one
-        if (ahead >= 3)
-            wait_vm<3 * NDMA>();
-        else if (ahead == 2)
+        if (ahead >= 2)
             wait_vm<2 * NDMA>();
         else if (ahead == 1)
             wait_vm<NDMA>();
@@ -435,46 +453,28 @@ __device__ __forceinline__ void run_item(const DecodeParams &P, const Addr &A, c
     }
 
     // ---- results: direct output, or a partial and the pair's ticket ----
-#pragma unroll
-    for (int nb = 0; nb < NQB; ++nb) {
-        lsum[nb] += lane_xor(lsum[nb], 16);
-        lsum[nb] += lane_xor(lsum[nb], 32);
-    }
+    const float lsum = accl[0];
     bool any_part = false;
+    if (cv && np != 0) {
+        if (np == 1) {
+            const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+            f16 *op = (f16 *)P.out + ((size_t)bm * P.hq + (size_t)it.g * G + hd) * D + grp * 4;
 #pragma unroll
-    for (int nb = 0; nb < NQB; ++nb) {
-        const int r = nb * 16 + col;
-        const int mem = r / G, hd = r - mem * G;
-        if (mem >= it.nmem || np[nb] == 0)
-            continue;
-        const int bm = it.b + mem;
-        if (np[nb] == 1) {
-            const float inv = lsum[nb] > 0.f ? 1.f / lsum[nb] : 0.f;
-            f16x8 o0, o1;
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int db = 0; db < 4; ++db) {
-                    const int e = 4 * i + db;
-                    const f16 v = (f16)(acc[nb][db][i] * inv);
-                    if (e < 8)
-                        o0[e] = v;
-                    else
-                        o1[e - 8] = v;
-                }
-            f16 *op = (f16 *)P.out + ((size_t)bm * P.hq + (size_t)it.g * G + hd) * D + grp * 16;
-            *(f16x8 *)op = o0;
-            *(f16x8 *)(op + 8) = o1;
+            for (int db = 0; db < 4; ++db) {
+                const f16x4 o = {(f16)(acc[db][0] * inv), (f16)(acc[db][1] * inv), (f16)(acc[db][2] * inv),
+                                 (f16)(acc[db][3] * inv)};
+                *(f16x4 *)(op + 16 * db) = o;
+            }
         } else {
-            float *dst = P.part + ((size_t)pb[nb] * MAXG + hd) * PART_FLOATS;
+            float *dst = P.part + ((size_t)pb * MAXG + hd) * PART_FLOATS;
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
+            for (int db = 0; db < 4; ++db)
 #pragma unroll
-                for (int db = 0; db < 4; ++db)
-                    coherent_store(dst + grp * 16 + 4 * i + db, acc[nb][db][i]);
+                for (int i = 0; i < 4; ++i)
+                    coherent_store(dst + 16 * db + 4 * grp + i, acc[db][i]);
             if (grp == 0) {
-                coherent_store(dst + D, m[nb]);
-                coherent_store(dst + D + 1, lsum[nb]);
+                coherent_store(dst + D, mref);
+                coherent_store(dst + D + 1, lsum);
             }
             any_part = true;
         }
@@ -515,13 +515,13 @@ __device__ __forceinline__ void run_item(const DecodeParams &P, const Addr &A, c
     }
 }
 
-template <int G, int NBUF, int TT, bool PLANNED, typename Addr>
+template <int G, int NBUF, bool PLANNED, typename Addr>
 __global__ __launch_bounds__(64) void decode_f16_kernel(DecodeParams P, Addr A, PlanView PV)
 {
     static_assert(G >= 1 && G <= MAXG, "group size");
-    static_assert(NBUF >= 2 && NBUF <= 4, "ring depth");
-    __shared__ __attribute__((aligned(16))) char kring[NBUF * TT * 128];
-    __shared__ __attribute__((aligned(16))) char vring[NBUF * TT * 128];
+    static_assert(NBUF >= 2 && NBUF <= 3, "ring depth");
+    __shared__ __attribute__((aligned(16))) char kring[NBUF * TILE * 128];
+    __shared__ __attribute__((aligned(16))) char vring[NBUF * TILE * 128];
     const int lane = threadIdx.x;
     Item it;
     int rv;
@@ -547,12 +547,12 @@ __global__ __launch_bounds__(64) void decode_f16_kernel(DecodeParams P, Addr A, 
         if (flags & F_SHARED) {
             if (it.nmem * G > 16 || it.slot < 0)
                 return;
-            run_item<G, 1, true, NBUF, TT>(P, A, PV, it, rv, kring, vring);
+            run_item<G, true, NBUF>(P, A, PV, it, rv, kring, vring);
             return;
         }
         if (it.nmem != 1)
             return;
-        run_item<G, 1, false, NBUF, TT>(P, A, PV, it, rv, kring, vring);
+        run_item<G, false, NBUF>(P, A, PV, it, rv, kring, vring);
     } else {
         const int pair = blockIdx.x / PV.ipp;
         const int k = blockIdx.x - pair * PV.ipp;
@@ -577,7 +577,7 @@ __global__ __launch_bounds__(64) void decode_f16_kernel(DecodeParams P, Addr A, 
         it.slot = it.pbase + k;
         const int j = lane - R_ENT;
         rv = (j >= 0 && j < it.nblk) ? A.entry(it.b, it.blk0 + j) : -1;
-        run_item<G, 1, false, NBUF, TT>(P, A, PV, it, rv, kring, vring);
+        run_item<G, false, NBUF>(P, A, PV, it, rv, kring, vring);
     }
 }
 
@@ -594,7 +594,7 @@ static kvp_status launch_f16(const DecodeParams &P, const Addr &A, const PlanVie
     switch (group) {
 #define KVP_G(GG)                                                                                  \
     case GG:                                                                                       \
-        hipLaunchKernelGGL((decode_f16_kernel<GG, DEC_NBUF, DEC_TT, PLANNED, Addr>), g, block, 0, st, P, A, PV); \
+        hipLaunchKernelGGL((decode_f16_kernel<GG, DEC_NBUF, PLANNED, Addr>), g, block, 0, st, P, A, PV); \
         break;
         KVP_G(1) KVP_G(2) KVP_G(3) KVP_G(4) KVP_G(5) KVP_G(6) KVP_G(7) KVP_G(8)
 #undef KVP_G
