@@ -319,6 +319,16 @@ kvp_status paged_decode_attention_planned(const kvp_cache_desc *cache, int32_t l
                                           const void *d_plan, float scale, void *workspace,
                                           size_t ws_bytes, kvp_stream stream);
 
+/* Wait bound of the fp16 split merge.  A context split over several work items is merged
+ * by the item that holds its final blocks: it polls the pair's counter until the others
+ * have stored their partials, with a short sleep after each poll, and after `polls` polls
+ * it falls back to the counted merge, in which the last of the pair's items to finish
+ * merges every partial from memory.  Both merges combine the partials in the same order
+ * with the same arithmetic, so results are bit-identical either way; 0 always takes the
+ * counted merge.  Default 0.  Process-wide, for launches made after the call; returns
+ * the previous bound (a negative argument only queries it). */
+int32_t kvp_decode_merge_polls(int32_t polls);
+
 /* Packed variable-length prefill ([XF] section 4, [XF] 5 for the head map).  Segment s
  * covers packed rows d_cu_seqlens[s] .. d_cu_seqlens[s+1]-1.  Row i of a segment attends
  * to rows j <= i of the same segment (causal = 1) or to every row of its segment

@@ -129,6 +129,7 @@ _sig("contiguous_decode_attention", _i32, [ctypes.POINTER(kvp_dims), _p, _p, _p,
                                            _f32, _p, _sz, _p])
 _sig("varlen_causal_prefill", _i32, [ctypes.POINTER(kvp_dims), _p, _p, _p, _p, _p, _i32, _i32, _i32,
                                      _f32, _p])
+_sig("kvp_decode_merge_polls", _i32, [_i32])
 _sig("kv_gather", _i32, [ctypes.POINTER(kvp_cache_desc), _i32, _p, _i32, _p, _i32, _i32, _p, _p, _p])
 
 
@@ -497,6 +498,13 @@ def paged_decode_attention_planned(cache: PagedKVCache, layer, q, plan, d_plan, 
                                                _dev(d_plan, "plan"), float(scale), _dev(workspace, "workspace"),
                                                workspace.numel(), _stream(stream)))
     return out
+
+
+def decode_merge_polls(polls=-1):
+    """Wait bound of the fp16 split merge (kvp_decode_merge_polls): polls of a pair's
+    counter by its merging item before the counted merge takes over; 0 always takes the
+    counted merge.  Returns the previous bound; a negative value only queries it."""
+    return int(_lib.kvp_decode_merge_polls(int(polls)))
 
 
 def contiguous_decode_attention(q, k_cache, v_cache, context_lens, out=None, scale=0.0,

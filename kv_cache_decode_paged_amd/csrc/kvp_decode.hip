@@ -3,6 +3,8 @@
 // (fp16, the hot path) and kvp_decode_f32.hip (fp32).
 #include <hip/hip_runtime.h>
 
+#include <atomic>
+
 #include <algorithm>
 #include <cmath>
 #include <cstdlib>
@@ -10,6 +12,10 @@
 #include "kvp_decode_common.h"
 
 namespace kvp {
+
+// wait bound of the fp16 split merge (polls of a pair's ticket)
+static std::atomic<int> g_merge_polls{0};
+
 
 using namespace dec;
 
@@ -95,6 +101,7 @@ static kvp_status decode_common(const kvp_dims *dims, void *out, const void *q, 
     P.part = nullptr;
     P.tickets = nullptr;
     P.workers = dims->dtype == KVP_F16 ? 0 : decode_f32_max_splits(max_ctx);
+    P.merge_polls = g_merge_polls.load(std::memory_order_relaxed);
     const size_t pb = part_bytes(dims, B, max_ctx);
     if (pb > 0) {
         const size_t need = workspace_bytes(dims, B, max_ctx);
@@ -154,6 +161,14 @@ static size_t plan_workspace_bytes(const kvp_decode_plan *plan)
 using namespace kvp;
 
 extern "C" {
+
+int32_t kvp_decode_merge_polls(int32_t polls)
+{
+    const int old = g_merge_polls.load(std::memory_order_relaxed);
+    if (polls >= 0)
+        g_merge_polls.store(polls, std::memory_order_relaxed);
+    return old;
+}
 
 size_t decode_workspace_bytes(const kvp_dims *dims, int32_t B, int32_t max_context)
 {
@@ -247,6 +262,7 @@ kvp_status paged_decode_attention_planned(const kvp_cache_desc *cache, int32_t l
         scale = 1.0f / sqrtf((float)D);
     P.scale_log2 = scale * LOG2E;
     P.workers = 0;
+    P.merge_polls = g_merge_polls.load(std::memory_order_relaxed);
     // tickets first: the layout does not depend on the plan's slot count
     P.tickets = need > 0 ? (int *)workspace : nullptr;
     P.part = need > 0 ? (float *)((char *)workspace + ticket_bytes(plan->B, hkv)) : nullptr;

@@ -130,6 +130,10 @@ __device__ inline float coherent_load(const float *p)
 {
     return __hip_atomic_load(const_cast<float *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+__device__ inline int coherent_load_int(const int *p)
+{
+    return __hip_atomic_load(const_cast<int *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 __device__ inline void wait_stores() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 __device__ inline int take_ticket(int *t)
 {
@@ -160,6 +164,8 @@ struct DecodeParams {
     int workers;       // fp32: max splits per pair
     float *part;       // partial results
     int *tickets;      // [B][Hkv], zero between calls
+    int merge_polls;   // fp16: polls of a pair's ticket by its merging item before it falls
+                       // back to the counted merge
 };
 
 // launchers (one translation unit per kernel family)

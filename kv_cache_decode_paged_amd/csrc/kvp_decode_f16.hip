@@ -50,7 +50,7 @@ namespace kvp {
 using namespace dec;
 using namespace plan;
 
-constexpr int PART_FLOATS = D + 2; // o[64], m, l
+constexpr int PART_FLOATS = D + 4; // o[64], m, l, 2 floats of padding (16-byte records)
 // ring depth of the decode kernel: two 64-token slots (32 KB of LDS, five waves per CU)
 #ifndef DEC_NBUF
 #define DEC_NBUF 2
@@ -129,51 +129,102 @@ struct Item {
     int b, g, nmem, blk0, nblk, end, slot, nparts, pbase;
 };
 
-// Merge the nparts partials of pair (b, g) (slots pbase ..) in slot order; lane = dim.
-template <int G>
-__device__ __forceinline__ void merge_pair(const DecodeParams &P, int b, int g, int pbase, int nparts)
+// One step of the slot-order merge of partials (m, l, o): M, L, O absorb partial (m, l, o)
+// over n output elements.  Both merge paths below go through it, in the same order, so a
+// pair's result does not depend on which item merges it.
+__device__ __forceinline__ void merge_step(float &M, float &L, float *O, int n, float m, float l, const float *o)
 {
-    const int lane = threadIdx.x;
-    float M[G], L[G], O[G];
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-        M[h] = -INFINITY;
-        L[h] = 0.f;
-        O[h] = 0.f;
+    const float mn = fmaxf(M, m);
+    if (mn != -INFINITY) {
+        const float a = fast_exp2(M - mn), c = fast_exp2(m - mn);
+        L = fmaf(L, a, l * c);
+        for (int k = 0; k < n; ++k)
+            O[k] = fmaf(O[k], a, o[k] * c);
+        M = mn;
     }
-    for (int j0 = 0; j0 < nparts; j0 += 4) {
-        float mv[4][G], lv[4][G], ov[4][G];
+}
+
+// 16- and 8-byte device-coherent accesses (agent scope, like coherent_store / _load: the
+// write goes through to memory, the read misses the XCD's L2).  The loads are inline
+// assembly: the caller waits for them (wait_stores) before it uses the results.
+__device__ inline void coherent_store4(float *p, f32x4 v)
+{
+    asm volatile("global_store_dwordx4 %0, %1, off sc1" ::"v"(p), "v"(v) : "memory");
+}
+__device__ inline void coherent_store2(float *p, float a, float b)
+{
+    const float2 v = {a, b};
+    asm volatile("global_store_dwordx2 %0, %1, off sc1" ::"v"(p), "v"(v) : "memory");
+}
+__device__ inline f32x4 coherent_load4_async(const float *p)
+{
+    f32x4 r;
+    asm volatile("global_load_dwordx4 %0, %1, off sc1" : "=v"(r) : "v"(p) : "memory");
+    return r;
+}
+__device__ inline float2 coherent_load2_async(const float *p)
+{
+    float2 r;
+    asm volatile("global_load_dwordx2 %0, %1, off sc1" : "=v"(r) : "v"(p) : "memory");
+    return r;
+}
+
+// Merge, for this lane's column, the np partials of its pair (slots pbase .. pbase+np-1) in
+// slot order; the partial of slot own is this lane's registers (om, ol, oacc), the others are
+// read from memory.  Lane (col, grp) holds output dims 16 db + 4 grp + i as O[4 db + i].
+// Writes the normalised row to outp (this column's 64 outputs).
+__device__ __forceinline__ void merge_column(const float *part, int pbase, int np, int own, int hd, int grp,
+                                             float om, float ol, const f32x4 (&oacc)[4], f16 *outp)
+{
+    float M = -INFINITY, L = 0.f, O[16];
+#pragma unroll
+    for (int k = 0; k < 16; ++k)
+        O[k] = 0.f;
+    for (int j0 = 0; j0 < np; j0 += 4) {
+        f32x4 ov[4][4];
+        float2 ml[4];
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) {
-            const int j = min(j0 + jj, nparts - 1);
+            const int j = j0 + jj;
+            if (j < np && j != own) {
+                const float *src = part + ((size_t)(pbase + j) * MAXG + hd) * PART_FLOATS;
 #pragma unroll
-            for (int h = 0; h < G; ++h) {
-                const float *src = P.part + ((size_t)(pbase + j) * MAXG + h) * PART_FLOATS;
-                mv[jj][h] = coherent_load(src + D);
-                lv[jj][h] = coherent_load(src + D + 1);
-                ov[jj][h] = coherent_load(src + lane);
+                for (int db = 0; db < 4; ++db)
+                    ov[jj][db] = coherent_load4_async(src + 16 * db + 4 * grp);
+                ml[jj] = coherent_load2_async(src + D);
+            } else {
+#pragma unroll
+                for (int db = 0; db < 4; ++db)
+                    ov[jj][db] = oacc[db];
+                ml[jj] = float2{om, ol};
             }
         }
+        wait_stores(); // the loads above have returned
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) {
-            if (j0 + jj < nparts) {
 #pragma unroll
-                for (int h = 0; h < G; ++h) {
-                    const float mn = fmaxf(M[h], mv[jj][h]);
-                    if (mn != -INFINITY) {
-                        const float a = fast_exp2(M[h] - mn), c = fast_exp2(mv[jj][h] - mn);
-                        L[h] = L[h] * a + lv[jj][h] * c;
-                        O[h] = O[h] * a + ov[jj][h] * c;
-                        M[h] = mn;
-                    }
-                }
+            for (int db = 0; db < 4; ++db)
+                asm volatile("" : "+v"(ov[jj][db]));
+            asm volatile("" : "+v"(ml[jj]));
+            if (j0 + jj < np) {
+                float o[16];
+#pragma unroll
+                for (int db = 0; db < 4; ++db)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        o[4 * db + i] = ov[jj][db][i];
+                merge_step(M, L, O, 16, ml[jj].x, ml[jj].y, o);
             }
         }
     }
-    f16 *outp = (f16 *)P.out + ((size_t)b * P.hq + (size_t)g * G) * D;
 #pragma unroll
-    for (int h = 0; h < G; ++h)
-        outp[h * D + lane] = (f16)(L[h] > 0.f ? O[h] / L[h] : 0.f);
+    for (int db = 0; db < 4; ++db) {
+        f16x4 o;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            o[i] = (f16)(L > 0.f ? O[4 * db + i] / L : 0.f);
+        *(f16x4 *)(outp + 16 * db + 4 * grp) = o;
+    }
 }
 
 // One work item.  rv: lane R_ENT + j holds the physical id of the item's block j.
@@ -452,66 +503,80 @@ __device__ __forceinline__ void run_item(const DecodeParams &P, const Addr &A, c
         compute(t);
     }
 
-    // ---- results: direct output, or a partial and the pair's ticket ----
+    // ---- results ----
+    // Rows of an unsplit pair are normalised and written.  A pair split over several items
+    // (np > 1) leaves one partial (m, l, o) per item in its slot range and is merged in slot
+    // order by one of them: normally the item that counts last on the pair's ticket after
+    // storing its partial; with merge polls enabled, the private item of the pair's last
+    // slot instead waits (bounded) for the others' count and merges without storing its
+    // own.  Every merge goes through merge_column, so the result does not depend on which
+    // item merges.
     const float lsum = accl[0];
-    bool any_part = false;
-    if (cv && np != 0) {
-        if (np == 1) {
-            const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
-            f16 *op = (f16 *)P.out + ((size_t)bm * P.hq + (size_t)it.g * G + hd) * D + grp * 4;
+    f16 *outp = (f16 *)P.out + ((size_t)bm * P.hq + (size_t)it.g * G + hd) * D;
+    if (cv && np == 1) {
+        const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
 #pragma unroll
-            for (int db = 0; db < 4; ++db) {
-                const f16x4 o = {(f16)(acc[db][0] * inv), (f16)(acc[db][1] * inv), (f16)(acc[db][2] * inv),
-                                 (f16)(acc[db][3] * inv)};
-                *(f16x4 *)(op + 16 * db) = o;
-            }
-        } else {
-            float *dst = P.part + ((size_t)pb * MAXG + hd) * PART_FLOATS;
-#pragma unroll
-            for (int db = 0; db < 4; ++db)
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    coherent_store(dst + 16 * db + 4 * grp + i, acc[db][i]);
-            if (grp == 0) {
-                coherent_store(dst + D, mref);
-                coherent_store(dst + D + 1, lsum);
-            }
-            any_part = true;
+        for (int db = 0; db < 4; ++db) {
+            const f16x4 o = {(f16)(acc[db][0] * inv), (f16)(acc[db][1] * inv), (f16)(acc[db][2] * inv),
+                             (f16)(acc[db][3] * inv)};
+            *(f16x4 *)(outp + 16 * db + 4 * grp) = o;
         }
     }
-    if (__ballot(any_part) == 0)
+    const bool split_col = cv && np > 1;
+    if (__ballot(split_col) == 0)
         return;
-    wait_stores(); // every partial store has completed before a ticket publishes it
+    // this column's pair: first slot and this item's part index in it
+    int pbase, own;
     if constexpr (SHARED) {
-        // member m's ticket is taken by lane m; members whose last part this was are merged
-        int tk = -2, nparts = 1, pbase = 0;
-        if (lane < it.nmem) {
-            const int pair = (it.b + lane) * hkv + it.g;
-            nparts = PV.pair_nparts[pair];
-            pbase = PV.pair_base[pair];
-            if (nparts > 1 && PV.req_shared[it.b + lane] > BS * it.blk0)
-                tk = take_ticket(&P.tickets[pair]);
-        }
-        unsigned long long last = __ballot(tk >= 0 && tk == nparts - 1);
-        while (last) {
-            const int mm = __builtin_ctzll(last);
-            last &= last - 1;
-            const int pair = (it.b + mm) * hkv + it.g;
-            merge_pair<G>(P, it.b + mm, it.g, lane_int(pbase, mm), lane_int(nparts, mm));
-            if (lane == 0)
-                reset_ticket(&P.tickets[pair]);
-        }
+        pbase = PV.pair_base[bm * hkv + it.g];
+        own = it.slot;
     } else {
-        const int pair = it.b * hkv + it.g;
-        int tk = 0;
-        if (lane == 0)
-            tk = take_ticket(&P.tickets[pair]);
-        tk = __builtin_amdgcn_readfirstlane(tk);
-        if (tk != it.nparts - 1)
-            return;
-        merge_pair<G>(P, it.b, it.g, it.pbase, it.nparts);
-        if (lane == 0)
-            reset_ticket(&P.tickets[pair]);
+        pbase = it.pbase;
+        own = it.slot - it.pbase;
+    }
+    if constexpr (!SHARED) {
+        if (P.merge_polls > 0 && own == np - 1) {
+            const int pair = it.b * hkv + it.g;
+            int ready = 0;
+            if (lane == 0) {
+                for (int k = 0; k < P.merge_polls; ++k) {
+                    if (coherent_load_int(&P.tickets[pair]) >= np - 1) {
+                        ready = 1;
+                        break;
+                    }
+                    __builtin_amdgcn_s_sleep(2);
+                }
+            }
+            if (__builtin_amdgcn_readfirstlane(ready)) {
+                if (cv)
+                    merge_column(P.part, pbase, np, own, hd, grp, mref, lsum, acc, outp);
+                if (lane == 0)
+                    reset_ticket(&P.tickets[pair]);
+                return;
+            }
+        }
+    }
+    if (split_col) {
+        float *dst = P.part + ((size_t)pb * MAXG + hd) * PART_FLOATS;
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+            coherent_store4(dst + 16 * db + 4 * grp, acc[db]);
+        if (grp == 0)
+            coherent_store2(dst + D, mref, lsum);
+    }
+    wait_stores(); // every partial store has completed before a ticket publishes it
+    // one ticket per member pair, taken by the lane of the member's first column
+    int tk = -1;
+    if (split_col && hd == 0 && grp == 0)
+        tk = take_ticket(&P.tickets[bm * hkv + it.g]);
+    tk = __shfl(tk, mem * G, 64);
+    const bool last = split_col && tk == np - 1;
+    if (__ballot(last) == 0)
+        return;
+    if (last) {
+        merge_column(P.part, pbase, np, own, hd, grp, mref, lsum, acc, outp);
+        if (hd == 0 && grp == 0)
+            reset_ticket(&P.tickets[bm * hkv + it.g]);
     }
 }
 

@@ -82,12 +82,12 @@ def test_device_calls_reject_bad_arguments_before_launch():
 def test_workspace_size():
     import kv_cache_decode_paged_amd as kvp
     # fp16: a pair longer than 32 blocks is cut into ceil(blocks / 32) parts, one partial per
-    # part (8 head slots x 66 floats) + one ticket per pair; 32768 tokens = 2048 blocks -> 64
+    # part (8 head slots x 68 floats) + one ticket per pair; 32768 tokens = 2048 blocks -> 64
     ws = kvp.decode_workspace_bytes(14, 2, torch.float16, 32, 32768)
-    assert ws == 32 * 2 * 64 * 8 * 66 * 4 + 256
+    assert ws == 32 * 2 * 64 * 8 * 68 * 4 + 256
     # contexts of at most 512 tokens are never split: no workspace
     assert kvp.decode_workspace_bytes(14, 2, torch.float16, 200, 512) == 0
-    assert kvp.decode_workspace_bytes(14, 2, torch.float16, 200, 513) == 1792 + 200 * 2 * 2 * 8 * 66 * 4
+    assert kvp.decode_workspace_bytes(14, 2, torch.float16, 200, 513) == 1792 + 200 * 2 * 2 * 8 * 68 * 4
     # fp32 single head, short context: one split, no workspace needed
     assert kvp.decode_workspace_bytes(1, 1, torch.float32, 1, 88) == 0
     # 5000 tokens: at most 16 splits (256-token splits up to 4096 tokens, 512 beyond)

@@ -245,6 +245,31 @@ def test_deterministic_repeat():
     assert torch.equal(_bits(a.cpu()), _bits(b.cpu()))
 
 
+def test_counted_merge_matches_polled_merge():
+    """A split context is merged by the item holding its final blocks, which polls for the
+    others' partials; with zero polls every pair takes the counted merge (the last item to
+    finish merges from memory).  Both combine in slot order with the same arithmetic, so the
+    outputs must be bit-identical."""
+    need_gpu()
+    pb = W.paged_batch(50, seed=78)
+    say("polled vs counted merge, B", pb.batch)
+    step = PagedStep(kvp, pb, layers=1, hq=14, hkv=2, dtype=torch.float16, seed=6100)
+    q = step.q(0).cuda()
+    old = kvp.decode_merge_polls(1 << 14)
+    try:
+        a = kvp.paged_decode_attention(step.cache, 0, q, step.table, step.ctx)
+        kvp.decode_merge_polls(0)
+        b = kvp.paged_decode_attention(step.cache, 0, q, step.table, step.ctx)
+        c = kvp.paged_decode_attention(step.cache, 0, q, step.table, step.ctx)
+    finally:
+        kvp.decode_merge_polls(old)
+    torch.cuda.synchronize()
+    assert torch.equal(_bits(a.cpu()), _bits(b.cpu()))
+    assert torch.equal(_bits(b.cpu()), _bits(c.cpu()))
+    err = max_abs(to64(a), step.oracle(0))
+    assert err <= TOL[torch.float16]
+
+
 def test_fused_append_matches_separate_append():
     need_gpu()
     pb = W.paged_batch(40, seed=91)
@@ -294,8 +319,14 @@ def test_long_context_split_k_sampled():
     table, ctx = pool.export(seqs, nb_per)
     out = kvp.paged_decode_attention(cache, 0, q, table.to(dev), ctx.to(dev))
     oc = kvp.contiguous_decode_attention(q, K, V, ctx.to(dev))
+    old = kvp.decode_merge_polls(1 << 14)  # 65 parts per pair through the polled merge
+    try:
+        ocount = kvp.paged_decode_attention(cache, 0, q, table.to(dev), ctx.to(dev))
+    finally:
+        kvp.decode_merge_polls(old)
     torch.cuda.synchronize()
     assert torch.equal(_bits(out.cpu()), _bits(oc.cpu()))
+    assert torch.equal(_bits(out.cpu()), _bits(ocount.cpu()))
     rows = [0, 13, 31]
     want = oracle.decode_gqa(to64(q[rows]), to64(K[rows]), to64(V[rows]), np.full(len(rows), L))
     err = max_abs(to64(out[rows]), want)

@@ -73,6 +73,13 @@ def test_planned_full_size_b200():
         o2 = kvp.paged_decode_attention_planned(step.cache, l, q, plan, dp, workspace=ws)
         torch.cuda.synchronize()
         assert torch.equal(_bits(o.cpu()), _bits(o2.cpu())), "repeat with the same workspace differs"
+        old = kvp.decode_merge_polls(1 << 14)  # split pairs merged by their last item, polling
+        try:
+            o3 = kvp.paged_decode_attention_planned(step.cache, l, q, plan, dp, workspace=ws)
+        finally:
+            kvp.decode_merge_polls(old)
+        torch.cuda.synchronize()
+        assert torch.equal(_bits(o.cpu()), _bits(o3.cpu())), "polled merge differs from the counted merge"
         err = max_abs(to64(o), step.oracle(l))
         say("planned b200 layer", l, "max err", err)
         assert err <= TOL[torch.float16]
