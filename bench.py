@@ -180,7 +180,7 @@ def main():
     pool.export_raw(ids.data_ptr(), B, max_blocks, t0h.data_ptr(), c0h.data_ptr())
     c0h += total_steps + 1  # the longest contexts of this run (plan sizing only)
     plan0, _ = kvp.decode_plan_build(HQ, HKV, t0h, c0h, cache.num_blocks, share_prefix=share)
-    pad_items = plan0.n_items + 64
+    pad_items = plan0.n_items + 8 * 32  # room for one more round of CU slots per XCD queue
     img_bytes = kvp.decode_plan_bytes(HQ, HKV, B, max_blocks, pad_items)
     hb = [dict(table=torch.empty((B, max_blocks), dtype=torch.int32).pin_memory(),
                ctx=torch.empty((B,), dtype=torch.int32).pin_memory(),

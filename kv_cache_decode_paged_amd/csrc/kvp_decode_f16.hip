@@ -51,7 +51,11 @@ using namespace dec;
 using namespace plan;
 
 constexpr int PART_FLOATS = D + 4; // o[64], m, l, 2 floats of padding (16-byte records)
-// ring depth of the decode kernel: two 64-token slots (32 KB of LDS, five waves per CU)
+// tile length (tokens) and ring depth of the decode kernel: 64-token tiles in a 2-slot ring
+// take 32 KB of LDS per wave, which leaves room for four waves per CU
+#ifndef DEC_TT
+#define DEC_TT 64
+#endif
 #ifndef DEC_NBUF
 #define DEC_NBUF 2
 #endif
@@ -233,11 +237,11 @@ __device__ __forceinline__ void merge_column(const float *part, int pbase, int n
 // lane / 16).  MFMA column col is query row col of the item (member col / G, head col % G).
 // K and V tiles sit in LDS as 64 rows of 128 bytes; 16-byte chunk c of row r is stored at
 // chunk slot c ^ (r & 7).
-template <int G, bool SHARED, int NBUF, typename Addr>
+template <int G, bool SHARED, int NBUF, int TT, typename Addr>
 __device__ __forceinline__ void run_item(const DecodeParams &P, const Addr &A, const PlanView &PV,
                                          const Item &it, int rv, char *kring, char *vring)
 {
-    constexpr int TT = TILE;       // tokens per tile
+    static_assert(TT == 32 || TT == 64, "tiles of 32 or 64 tokens");
     constexpr int KB = TT / BS;    // blocks per tile
     constexpr int KS = TT / 32;    // k-steps of 32 tokens per tile (value product)
     constexpr int NDMA = 2 * KB * 2; // 1 KB loads per tile: two per block for K and for V
@@ -580,13 +584,13 @@ __device__ __forceinline__ void run_item(const DecodeParams &P, const Addr &A, c
     }
 }
 
-template <int G, int NBUF, bool PLANNED, typename Addr>
+template <int G, int NBUF, int TT, bool PLANNED, typename Addr>
 __global__ __launch_bounds__(64) void decode_f16_kernel(DecodeParams P, Addr A, PlanView PV)
 {
     static_assert(G >= 1 && G <= MAXG, "group size");
     static_assert(NBUF >= 2 && NBUF <= 3, "ring depth");
-    __shared__ __attribute__((aligned(16))) char kring[NBUF * TILE * 128];
-    __shared__ __attribute__((aligned(16))) char vring[NBUF * TILE * 128];
+    __shared__ __attribute__((aligned(16))) char kring[NBUF * TT * 128];
+    __shared__ __attribute__((aligned(16))) char vring[NBUF * TT * 128];
     const int lane = threadIdx.x;
     Item it;
     int rv;
@@ -612,12 +616,12 @@ __global__ __launch_bounds__(64) void decode_f16_kernel(DecodeParams P, Addr A, 
         if (flags & F_SHARED) {
             if (it.nmem * G > 16 || it.slot < 0)
                 return;
-            run_item<G, true, NBUF>(P, A, PV, it, rv, kring, vring);
+            run_item<G, true, NBUF, TT>(P, A, PV, it, rv, kring, vring);
             return;
         }
         if (it.nmem != 1)
             return;
-        run_item<G, false, NBUF>(P, A, PV, it, rv, kring, vring);
+        run_item<G, false, NBUF, TT>(P, A, PV, it, rv, kring, vring);
     } else {
         const int pair = blockIdx.x / PV.ipp;
         const int k = blockIdx.x - pair * PV.ipp;
@@ -627,9 +631,9 @@ __global__ __launch_bounds__(64) void decode_f16_kernel(DecodeParams P, Addr A, 
         int ctx = P.ctx_lens[it.b];
         ctx = ctx < 0 ? 0 : (ctx > maxc ? maxc : ctx);
         const int nbt = (ctx + BS - 1) / BS;
-        // one item up to BPI blocks, else ceil(blocks / SPLIT_BLOCKS) parts of equal tile
+        // one item up to UNSPLIT_BLOCKS blocks, else ceil(blocks / SPLIT_BLOCKS) parts of equal tile
         // counts: part k holds tiles [k T / n, (k+1) T / n) of the pair's T tiles
-        const int n = nbt <= BPI ? 1 : (nbt + SPLIT_BLOCKS - 1) / SPLIT_BLOCKS;
+        const int n = nbt <= UNSPLIT_BLOCKS ? 1 : (nbt + SPLIT_BLOCKS - 1) / SPLIT_BLOCKS;
         if (k >= n)
             return;
         const int T = (nbt + 3) >> 2;
@@ -642,7 +646,7 @@ __global__ __launch_bounds__(64) void decode_f16_kernel(DecodeParams P, Addr A, 
         it.slot = it.pbase + k;
         const int j = lane - R_ENT;
         rv = (j >= 0 && j < it.nblk) ? A.entry(it.b, it.blk0 + j) : -1;
-        run_item<G, false, NBUF>(P, A, PV, it, rv, kring, vring);
+        run_item<G, false, NBUF, TT>(P, A, PV, it, rv, kring, vring);
     }
 }
 
@@ -659,7 +663,7 @@ static kvp_status launch_f16(const DecodeParams &P, const Addr &A, const PlanVie
     switch (group) {
 #define KVP_G(GG)                                                                                  \
     case GG:                                                                                       \
-        hipLaunchKernelGGL((decode_f16_kernel<GG, DEC_NBUF, PLANNED, Addr>), g, block, 0, st, P, A, PV); \
+        hipLaunchKernelGGL((decode_f16_kernel<GG, DEC_NBUF, DEC_TT, PLANNED, Addr>), g, block, 0, st, P, A, PV); \
         break;
         KVP_G(1) KVP_G(2) KVP_G(3) KVP_G(4) KVP_G(5) KVP_G(6) KVP_G(7) KVP_G(8)
 #undef KVP_G
@@ -675,7 +679,7 @@ static kvp_status launch_f16(const DecodeParams &P, const Addr &A, const PlanVie
 int decode_f16_items_per_pair(int max_context)
 {
     const int nb = (std::max(max_context, 1) + BS - 1) / BS;
-    return nb <= BPI ? 1 : (nb + SPLIT_BLOCKS - 1) / SPLIT_BLOCKS;
+    return nb <= UNSPLIT_BLOCKS ? 1 : (nb + SPLIT_BLOCKS - 1) / SPLIT_BLOCKS;
 }
 
 size_t decode_f16_part_bytes(long long slots)

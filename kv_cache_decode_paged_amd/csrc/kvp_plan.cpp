@@ -48,9 +48,9 @@ long long max_items(long long B, long long hkv, long long max_blocks)
 {
     const long long ipp = std::max<long long>(1, (max_blocks + BPI - 1) / BPI);
     // private items: at most ipp per pair; shared items: at most one set per two requests;
-    // plus the padding that evens out the XCD queues
+    // plus the padding that evens out the XCD queues and rounds them to whole CU rounds
     const long long work = B * hkv * ipp + (B / 2) * hkv * ipp;
-    return XCDS * ((work + XCDS - 1) / XCDS + MAX_BUNDLE);
+    return XCDS * ((work + XCDS - 1) / XCDS + MAX_BUNDLE + CU_SLOTS - 1);
 }
 
 size_t image_bytes_for(long long items, long long B, long long hkv)
@@ -62,7 +62,7 @@ size_t image_bytes_for(long long items, long long B, long long hkv)
 // other parts anyway), else ceil(nb / SPLIT_BLOCKS) parts of equal tile counts
 int split_parts(int nb, bool forced)
 {
-    if (nb <= 0 || (!forced && nb <= BPI))
+    if (nb <= 0 || (!forced && nb <= UNSPLIT_BLOCKS))
         return 1;
     return (nb + SPLIT_BLOCKS - 1) / SPLIT_BLOCKS;
 }
@@ -285,9 +285,31 @@ kvp_status decode_plan_build(const kvp_dims *dims, const int32_t *table, int32_t
     std::stable_sort(priv.begin(), priv.end(), [&](long long x, long long y) { return cost[x] > cost[y]; });
     for (long long i : priv)
         place({i});
+    // within each XCD: items to CU slots, longest first to the least-loaded slot that has
+    // fewer than K items (K = the XCD's items over its slots, rounded up); the k-th item of
+    // slot s takes queue position CU_SLOTS k + s
+    std::vector<std::vector<long long>> qpos(XCDS);
     size_t qlen = 0;
-    for (const auto &qq : q)
-        qlen = std::max(qlen, qq.size());
+    for (int x = 0; x < XCDS; ++x) {
+        std::vector<long long> its = q[x];
+        std::stable_sort(its.begin(), its.end(), [&](long long a, long long b) { return cost[a] > cost[b]; });
+        const size_t K = (its.size() + CU_SLOTS - 1) / CU_SLOTS;
+        std::vector<std::vector<long long>> slot(CU_SLOTS);
+        std::vector<long long> sload(CU_SLOTS, 0);
+        for (long long i : its) {
+            int best = -1;
+            for (int c = 0; c < CU_SLOTS; ++c)
+                if (slot[c].size() < K && (best < 0 || sload[c] < sload[best]))
+                    best = c;
+            slot[best].push_back(i);
+            sload[best] += cost[i];
+        }
+        qpos[x].assign(K * CU_SLOTS, -1);
+        for (int c = 0; c < CU_SLOTS; ++c)
+            for (size_t k = 0; k < slot[c].size(); ++k)
+                qpos[x][k * CU_SLOTS + c] = slot[c][k];
+        qlen = std::max(qlen, qpos[x].size());
+    }
     if (pad_items > 0) {
         const size_t padq = ((size_t)pad_items + XCDS - 1) / XCDS;
         if (qlen > padq)
@@ -308,8 +330,8 @@ kvp_status decode_plan_build(const kvp_dims *dims, const int32_t *table, int32_t
     for (size_t qi = 0; qi < qlen; ++qi)
         for (int x = 0; x < XCDS; ++x) {
             int32_t *dst = img + ((size_t)qi * XCDS + x) * REC;
-            if (qi < q[x].size()) {
-                std::memcpy(dst, recs.data() + (size_t)q[x][qi] * REC, REC * 4);
+            if (qi < qpos[x].size() && qpos[x][qi] >= 0) {
+                std::memcpy(dst, recs.data() + (size_t)qpos[x][qi] * REC, REC * 4);
             } else {
                 for (int j = 0; j < REC; ++j)
                     dst[j] = -1;

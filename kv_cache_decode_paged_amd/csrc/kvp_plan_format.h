@@ -22,9 +22,13 @@ constexpr int BPI = 32;  // blocks per work item (512 tokens)
 // BPI blocks each).  Shorter parts mean more waves, and the decode time grows with the wave
 // count faster than the shorter tail saves, so the parts are as long as an item may be.
 constexpr int SPLIT_BLOCKS = 32;
+constexpr int UNSPLIT_BLOCKS = 32; // longest pair kept in one item (at most BPI)
 constexpr int REC = 48;  // int32 per record
 constexpr int MAXM = 16; // members of one shared item (and at most 16 query rows)
 constexpr int XCDS = 8;  // MI355X: workgroup i runs on XCD i % 8 (round-robin dispatch)
+// CUs per XCD: within an XCD, the dispatcher deals the queue positions of one launch
+// round-robin over its CUs, so positions p and p + CU_SLOTS of an XCD queue share a CU
+constexpr int CU_SLOTS = 32;
 
 enum : int {
     R_FLAGS = 0,  // F_SHARED: shared item; F_EMPTY: padding, no work

@@ -7,6 +7,8 @@ plan must guarantee, read independently from the image:
 * a pair split into several parts has slots pbase .. pbase+nparts-1, each written once,
   in token order (the merge order), and single-part pairs are written directly;
 * shared items hold at most 16 query rows and a prefix's items run on one XCD;
+* each XCD's items are spread over its 32 CUs (queue indices 32 apart share a CU) so that
+  no CU carries more than its share of the work plus one item;
 * without prefix sharing the plan is exactly the per-pair split (one item up to 32 blocks,
   else ceil(blocks/32) parts of equal tile counts) that paged_decode_attention uses (so the two are bit-identical on the GPU).
 
@@ -104,6 +106,19 @@ def check_plan(plan, image, table, ctx, num_blocks, hq, hkv, shared_expected=Non
             else:
                 slots = [s for s, _ in sorted(w, key=lambda x: x[1])]
                 assert slots == list(range(int(pbase[pair]), int(pbase[pair]) + int(nparts[pair])))
+    # per CU: position p runs on XCD p % 8 at queue index p // 8, and queue indices 32 apart
+    # share a CU; the planner spreads each XCD's work over its 32 CUs longest first, so no
+    # CU carries more than its share plus one item
+    for x in range(XCDS):
+        loads, costs = np.zeros(32), []
+        for qi in range(plan.n_items // XCDS):
+            r = items[qi * XCDS + x]
+            if int(r[0]) != F_EMPTY:
+                cst = int(r[5]) + 2
+                loads[qi % 32] += cst
+                costs.append(cst)
+        if costs:
+            assert loads.max() <= loads.sum() / 32 + max(costs), (x, loads.max(), loads.sum() / 32)
     for key, (xs, n) in bundles.items():
         if n <= 8:  # a run's shared items of one head (at most one bundle) share an XCD
             assert len(xs) == 1, f"shared items of run {key} spread over XCDs {xs}"
