@@ -33,6 +33,38 @@ HQ, HKV, D, BLOCK = 14, 2, 64, 16
 KV_TOKEN_LAYER_BYTES = 2 * HKV * D * 2  # K and V, fp16: 512 B per token per layer
 
 
+# HBM traffic of the decode launch, counted by rocprofv3 (FETCH_SIZE / WRITE_SIZE passes,
+# scaled by the same counters on copies of known size) and recorded in the profile summary
+# together with a digest of the sources it was measured on; reported only while they match.
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "decode_f16_planned_b200.md")
+TRAFFIC_SOURCES = ["kv_cache_decode_paged_amd/csrc/" + f for f in
+                   ("kvp_decode_f16.hip", "kvp_decode_common.h", "kvp_decode.hip", "kvp_plan.cpp",
+                    "kvp_plan_format.h")]
+
+
+def decode_sources_digest():
+    import hashlib
+    h = hashlib.sha256()
+    for f in TRAFFIC_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """Bytes per decode launch from the recorded counter passes, or None when the summary is
+    missing or was measured on other sources."""
+    import re
+    try:
+        text = open(TRAFFIC_PROFILE).read()
+    except OSError:
+        return None
+    m = re.search(r"traffic_bytes_per_launch:\s*(\d+)\s+sources:\s*([0-9a-f]+)", text)
+    if not m or m.group(2) != decode_sources_digest():
+        return None
+    return int(m.group(1))
+
+
 def unique_and_logical_tokens(table, ctx):
     """Distinct cache slots read by one decode call (a block's readers each read a prefix
     of it, so a block contributes the longest prefix read) and the per-request sum."""
@@ -322,7 +354,8 @@ def main():
         "unique_GB_per_step": round(uniq_bytes_step / 1e9, 4),
         "logical_GB_per_step": round(logical_bytes_step / 1e9, 4),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": measured_traffic(),
+                     "traffic_unit": "bytes per launch (HBM read + write, counters)",
                      "kernel": "paged_decode_attention_planned (decode_f16_kernel: append + attention + "
                                "split merge)",
                      "bytes_per_launch": int(call_bytes), "avg_launch_us": round(avg_ms * 1e3, 3)},
@@ -330,6 +363,7 @@ def main():
                  "kv_block_reads": int(blocks_read_last), "share_prefix": share},
         "cpu_baseline": cpu,
     }
+    print(f"[bench] decode sources digest {decode_sources_digest()}", file=sys.stderr, flush=True)
     print(json.dumps(line), flush=True)
 
 
