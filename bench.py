@@ -43,11 +43,15 @@ TRAFFIC_SOURCES = ["kv_cache_decode_paged_amd/csrc/" + f for f in
 
 
 def decode_sources_digest():
+    """Digest of the decode sources' code (comments and whitespace removed)."""
     import hashlib
+    import re
     h = hashlib.sha256()
     for f in TRAFFIC_SOURCES:
-        with open(os.path.join(ROOT, f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, f)) as fh:
+            code = re.sub(r"/\*.*?\*/", " ", fh.read(), flags=re.S)
+        code = re.sub(r"//[^\n]*", " ", code)
+        h.update(" ".join(code.split()).encode())
     return h.hexdigest()[:16]
 
 

@@ -21,22 +21,23 @@
 // blocks (8 tiles of 64 tokens) of one KV head, either of one request ("private") or of a
 // few requests that share those physical blocks ("shared": the query rows of every member,
 // up to 16 rows, are scored against the same K/V tile).  The planner puts all shared items
-// of one prefix on one XCD close together in dispatch order, so the prefix is fetched
-// from HBM about once per step and served from that XCD's L2 to its other readers.  Items come from a host-built plan
-// (paged_decode_attention_planned) or, without a plan, from the wave index: request pair
-// (b, g), split k of ceil(blocks / 32).  A pair split over several items leaves one partial
-// (m, l, o) per item; the last item to finish (device-scope ticket) merges them in slot
-// order, so results are deterministic.  Partials travel through relaxed device-scope
-// atomics (coherent stores / loads) ordered by a store-completion wait.
+// of one prefix on one XCD, so the prefix is fetched from HBM about once per step and
+// served from that XCD's L2 to its other readers, and spreads each XCD's items over its
+// CUs.  Items come from a host-built plan (paged_decode_attention_planned) or, without a
+// plan, from the wave index: request pair (b, g), split k of ceil(blocks / 32).  A pair
+// split over several items leaves one partial (m, l, o) per item; one of them merges the
+// partials in slot order (merge_column), so results are deterministic.  Partials travel
+// through 16-byte device-coherent stores and loads, ordered by a store-completion wait.
 //
 // Per wave: K and V tiles stream HBM -> LDS through global_load_lds_dwordx4 into a ring of
 // NBUF slots (16 KB per tile, 16 loads); waits are explicit vmcnt counts.
 //   scores  S^T = K Q^T       v_mfma_f32_16x16x32_f16, K rows from LDS (chunk-swizzled),
 //                             query rows as one 16-column block
-//   softmax fp32, hardware exp2, running max / sum per query row, p rounded once to fp16
+//   softmax fp32, hardware exp2 of one FMA (scale folded in), reference max moved only
+//           when a row's maximum passes it by 2^8, p rounded once to fp16
 //   values  O^T = V^T P^T     v_mfma_f32_16x16x32_f16; P^T is the score MFMA's own output
-//                             layout (no data movement), V^T is built per lane from
-//                             8-byte LDS reads (4 dims x 8 tokens) and byte permutes.
+//                             layout (no data movement), V^T comes from transposing LDS
+//                             reads (ds_read_b64_tr_b16); row sums from an all-ones operand
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
