@@ -162,6 +162,76 @@ def cpu_baseline(W, B_sample_layers=2, seed=42):
                       f"(logical KV bytes / wall time, fp64 scalar C, {threads} threads)"}
 
 
+MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 matrix peak
+
+
+def prefill_flops(seqlens, hq, d, causal):
+    """Algorithmic flops of packed prefill: 2 d for q.k and 2 d for p.v per attended
+    (query, key) pair -- the unmasked pairs only when causal."""
+    pairs = sum(n * (n + 1) // 2 for n in seqlens) if causal else sum(n * n for n in seqlens)
+    return 4 * d * hq * pairs
+
+
+def prefill_cpu_baseline(W, hq, hkv, causal, n=4096, seed=7):
+    """The fp64 oracle on a bounded sample: one of the sequences (n rows, all hq heads)."""
+    import oracle
+    q, k, v, cu = W.varlen_inputs([n], hq, hkv, seed=seed)
+    args = (q.double().numpy(), k.double().numpy(), v.double().numpy(), cu.numpy())
+    t0 = time.perf_counter()
+    oracle.varlen_prefill(*args, causal=causal)
+    dt = time.perf_counter() - t0
+    return {"value": round(prefill_flops([n], hq, D, causal) / dt / 1e12, 6), "unit": "TFLOP/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"one segment of {n} rows x {hq} query heads ({hkv} KV heads), "
+                      f"{'causal' if causal else 'non-causal'}, fp64 scalar C, 1 thread"}
+
+
+def bench_prefill(args):
+    """Packed varlen prefill: 16 sequences of 4096 tokens, 8 query / 2 KV heads, fp16,
+    causal (the long-prompt prefill shape; MFMA-bound)."""
+    import torch
+
+    import kv_cache_decode_paged_amd as kvp
+    import workloads as W
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    seqlens, hq, hkv, causal = [4096] * 16, 8, 2, True
+    q, k, v, cu = W.varlen_inputs(seqlens, hq, hkv)
+    q, k, v, cu = q.cuda(), k.cuda(), v.cuda(), cu.cuda()
+    out = torch.empty_like(q)
+    for _ in range(args.warmup):
+        kvp.varlen_causal_prefill(q, k, v, cu, max(seqlens), causal=causal, out=out)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(args.steps):
+        kvp.varlen_causal_prefill(q, k, v, cu, max(seqlens), causal=causal, out=out)
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / args.steps
+    flops = prefill_flops(seqlens, hq, D, causal)
+    tflops = flops / (ms * 1e-3) / 1e12
+    cpu = None if args.no_cpu_baseline else prefill_cpu_baseline(W, hq, hkv, causal)
+    print(f"[bench] prefill {len(seqlens)} x {seqlens[0]} tokens, {hq}q/{hkv}kv heads: {ms * 1e3:.1f} us per call, "
+          f"{tflops:.1f} TFLOP/s ({tflops / MFMA_F16_PEAK_TFLOPS * 100:.1f}% of the fp16 MFMA peak)",
+          file=sys.stderr, flush=True)
+    line = {
+        "metric": "packed causal prefill attention TFLOP/s (% of MFMA fp16 peak)",
+        "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f16", "data": "synthetic",
+        "config": {"workload": f"packed varlen causal prefill, {len(seqlens)} sequences x {seqlens[0]} tokens, "
+                               f"{hq}q/{hkv}kv heads d64 fp16", "sequences": len(seqlens),
+                   "seq_len": seqlens[0]},
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 1), "peak": MFMA_F16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tflops / MFMA_F16_PEAK_TFLOPS, 4), "traffic": None,
+                     "kernel": "varlen_causal_prefill (prefill_mfma_f16_kernel)", "flops_per_launch": flops,
+                     "avg_launch_us": round(ms * 1e3, 3)},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -174,12 +244,18 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-share", action="store_true", help="plans without shared-prefix items")
     ap.add_argument("--seed", type=int, default=42)
+    ap.add_argument("--workload", choices=["decode", "prefill"], default="decode",
+                    help="decode: the batch-200 paged decode step (default); prefill: packed causal "
+                         "prefill of 16 x 4096 tokens")
     args = ap.parse_args()
 
     if args.gpus != 1:
         print(f"bench.py runs on one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}). "
-              "Requests would be sharded across GPUs by whole sharing groups; see DESIGN.md.", flush=True)
+              "Requests would be sharded across GPUs by whole sharing groups.", flush=True)
         sys.exit(2)
+    if args.workload == "prefill":
+        bench_prefill(args)
+        return
 
     import numpy as np
     import torch
