@@ -38,8 +38,8 @@ KV_TOKEN_LAYER_BYTES = 2 * HKV * D * 2  # K and V, fp16: 512 B per token per lay
 # together with a digest of the sources it was measured on; reported only while they match.
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "decode_f16_planned_b200.md")
 TRAFFIC_SOURCES = ["kv_cache_decode_paged_amd/csrc/" + f for f in
-                   ("kvp_decode_f16.hip", "kvp_decode_common.h", "kvp_decode.hip", "kvp_plan.cpp",
-                    "kvp_plan_format.h")]
+                   ("kvp_decode_f16.hip", "kvp_decode_common.h", "kvp_gfx950.h", "kvp_decode.hip",
+                    "kvp_plan.cpp", "kvp_plan_format.h")]
 
 
 def decode_sources_digest():

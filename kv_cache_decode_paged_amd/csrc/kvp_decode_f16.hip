@@ -44,6 +44,7 @@
 #include <cmath>
 
 #include "kvp_decode_common.h"
+#include "kvp_gfx950.h"
 #include "kvp_plan_format.h"
 
 namespace kvp {
@@ -60,67 +61,6 @@ constexpr int PART_FLOATS = D + 4; // o[64], m, l, 2 floats of padding (16-byte 
 #ifndef DEC_NBUF
 #define DEC_NBUF 2
 #endif
-
-// s_waitcnt with only the vector-memory count set (gfx9 encoding: vmcnt in bits 3:0 and
-// 15:14, expcnt 6:4 and lgkmcnt 11:8 left at their maxima)
-template <int N> __device__ inline void wait_vm()
-{
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    constexpr int imm = (N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8);
-    __builtin_amdgcn_s_waitcnt(imm);
-}
-// s_waitcnt lgkmcnt(0): every LDS access of the wave has completed
-__device__ inline void wait_lds() { __builtin_amdgcn_s_waitcnt(0xF | (3 << 14) | (7 << 4)); }
-
-__device__ inline int lane_int(int v, int l) { return __builtin_amdgcn_readlane(v, l); }
-
-// LDS reads of the DMA-filled ring, issued as inline assembly.  The compiler's wait
-// insertion cannot tell these reads from reads of the slot a DMA is still filling, so for a
-// plain LDS read it waits for every outstanding vector-memory operation -- the prefetched
-// tiles included.  The ring is ordered by the explicit vmcnt waits instead; the results
-// are tied to an explicit lgkmcnt(0) before use (lds_ready).
-__device__ inline unsigned lds_addr(const char *p)
-{
-    return (unsigned)(uintptr_t)(const __attribute__((address_space(3))) char *)p;
-}
-__device__ inline f16x8 lds_b128(const char *p)
-{
-    f16x8 r;
-    asm volatile("ds_read_b128 %0, %1" : "=v"(r) : "v"(lds_addr(p)));
-    return r;
-}
-__device__ inline uint2 lds_b64(const char *p)
-{
-    uint2 r;
-    asm volatile("ds_read_b64 %0, %1" : "=v"(r) : "v"(lds_addr(p)));
-    return r;
-}
-
-__device__ inline f16x4 lds_tr16_b64(const char *p)
-{
-    f16x4 r;
-    asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(r) : "v"(lds_addr(p)));
-    return r;
-}
-__device__ inline void lds_store_b128(char *p, i32x4 v)
-{
-    asm volatile("ds_write_b128 %0, %1" ::"v"(lds_addr(p)), "v"(v) : "memory");
-}
-
-// max over lanes col, col + 16, col + 32, col + 48 (the k-groups of one MFMA column): swap
-// odd and even 16-lane rows, then the two 32-lane halves, without an LDS round trip
-__device__ inline float group_max(float x)
-{
-    const unsigned u = __builtin_bit_cast(unsigned, x);
-    const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
-    x = fmaxf(__builtin_bit_cast(float, (unsigned)a[0]), __builtin_bit_cast(float, (unsigned)a[1]));
-    const unsigned w = __builtin_bit_cast(unsigned, x);
-    const auto b = __builtin_amdgcn_permlane32_swap(w, w, false, false);
-    return fmaxf(__builtin_bit_cast(float, (unsigned)b[0]), __builtin_bit_cast(float, (unsigned)b[1]));
-}
-
-// growth of a column's maximum (log2 units) that moves its softmax reference
-constexpr float RESCALE_LOG2 = 8.f;
 
 struct PlanView {
     const int *items;       // planned: [n_items][REC]
@@ -451,12 +391,14 @@ __device__ __forceinline__ void run_item(const DecodeParams &P, const Addr &A, c
         for (int kb = 1; kb < KB; ++kb)
             mt = fmaxf(mt, fmaxf(fmaxf(sacc[kb][0], sacc[kb][1]), fmaxf(sacc[kb][2], sacc[kb][3])));
         mt = group_max(mt) * c;
-        // the reference max moves only when a column's maximum passes it by more than 2^8:
-        // between moves p = 2^(s c - mref) stays below 256, exact in fp16 range, and the
-        // output and row sum need no rescaling
-        if (__ballot(mt > mref + RESCALE_LOG2) != 0) {
-            const float mn = fmaxf(mref, mt);
-            const float alpha = mref == -INFINITY ? 0.f : fast_exp2(mref - mn);
+        // a column's reference max moves only when the column's own maximum passes it by more
+        // than 2^8: between moves p = 2^(s c - mref) stays below 256, exact in fp16 range, and
+        // the output and row sum need no rescaling.  Columns that do not move scale by exactly
+        // 1, so no query row depends on another's keys.
+        const bool need = mt > mref + RESCALE_LOG2;
+        if (__ballot(need) != 0) {
+            const float mn = need ? mt : mref;
+            const float alpha = need ? (mref == -INFINITY ? 0.f : fast_exp2(mref - mn)) : 1.f;
 #pragma unroll
             for (int db = 0; db < 4; ++db)
                 acc[db] *= alpha;

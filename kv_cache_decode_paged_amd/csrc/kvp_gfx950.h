@@ -1,0 +1,76 @@
+// kvp_gfx950.h -- gfx950 device helpers shared by the attention kernels (internal to the
+// library): explicit memory-counter waits, LDS reads and writes of DMA-filled tiles as
+// inline assembly, the transposing LDS read, and a cross-row maximum by lane swaps.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+namespace kvp {
+
+typedef _Float16 f16;
+typedef f16 f16x4 __attribute__((ext_vector_type(4)));
+typedef f16 f16x8 __attribute__((ext_vector_type(8)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// s_waitcnt with only the vector-memory count set (gfx9 encoding: vmcnt in bits 3:0 and
+// 15:14, expcnt 6:4 and lgkmcnt 11:8 left at their maxima)
+template <int N> __device__ inline void wait_vm()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    constexpr int imm = (N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8);
+    __builtin_amdgcn_s_waitcnt(imm);
+}
+// s_waitcnt lgkmcnt(0): every LDS access of the wave has completed
+__device__ inline void wait_lds() { __builtin_amdgcn_s_waitcnt(0xF | (3 << 14) | (7 << 4)); }
+
+__device__ inline int lane_int(int v, int l) { return __builtin_amdgcn_readlane(v, l); }
+
+// LDS reads of the DMA-filled ring, issued as inline assembly.  The compiler's wait
+// insertion cannot tell these reads from reads of the slot a DMA is still filling, so for a
+// plain LDS read it waits for every outstanding vector-memory operation -- the prefetched
+// tiles included.  The ring is ordered by the explicit vmcnt waits instead; the results
+// are tied to an explicit lgkmcnt(0) before use.
+__device__ inline unsigned lds_addr(const char *p)
+{
+    return (unsigned)(uintptr_t)(const __attribute__((address_space(3))) char *)p;
+}
+__device__ inline f16x8 lds_b128(const char *p)
+{
+    f16x8 r;
+    asm volatile("ds_read_b128 %0, %1" : "=v"(r) : "v"(lds_addr(p)));
+    return r;
+}
+__device__ inline f16x4 lds_tr16_b64(const char *p)
+{
+    f16x4 r;
+    asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(r) : "v"(lds_addr(p)));
+    return r;
+}
+__device__ inline void lds_store_b128(char *p, i32x4 v)
+{
+    asm volatile("ds_write_b128 %0, %1" ::"v"(lds_addr(p)), "v"(v) : "memory");
+}
+
+// max over lanes col, col + 16, col + 32, col + 48 (the k-groups of one MFMA column): swap
+// odd and even 16-lane rows, then the two 32-lane halves, without an LDS round trip
+__device__ inline float group_max(float x)
+{
+    const unsigned u = __builtin_bit_cast(unsigned, x);
+    const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    x = fmaxf(__builtin_bit_cast(float, (unsigned)a[0]), __builtin_bit_cast(float, (unsigned)a[1]));
+    const unsigned w = __builtin_bit_cast(unsigned, x);
+    const auto b = __builtin_amdgcn_permlane32_swap(w, w, false, false);
+    return fmaxf(__builtin_bit_cast(float, (unsigned)b[0]), __builtin_bit_cast(float, (unsigned)b[1]));
+}
+
+// growth of a column's maximum (log2 units) that moves its softmax reference
+constexpr float RESCALE_LOG2 = 8.f;
+
+// workgroup execution barrier without a memory fence: the callers order their LDS and
+// LDS-DMA traffic with explicit counter waits, so the barrier must not also drain the
+// prefetch still in flight (as the fenced __syncthreads would)
+__device__ inline void block_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+} // namespace kvp

@@ -11,19 +11,24 @@
 //   neuralialabs chapter: prefill is one pass over the whole prompt, a matrix-matrix
 //   product, so this is where the matrix cores pay off.
 //
-// fp16: MFMA v_mfma_f32_16x16x32_f16 tiles with fp32 accumulation.  One workgroup = 4
-// wave64 = 64 query rows of one (segment, query head); each wave owns 16 rows.  Per
-// 64-key tile it computes S^T = K Q^T (keys as MFMA rows, so the result lands with one
-// query per lane column), runs the online softmax on S^T in registers, and accumulates
-// O^T = V^T P^T where P^T is the fp16-rounded probability tile taken straight from the
-// S^T accumulator registers.  K goes HBM -> LDS with global_load_lds (chunk-swizzled);
-// V is stored transposed in LDS for the A operand of the second product.  Tiles entirely
-// above the causal diagonal are skipped.
+// fp16: one workgroup = 4 wave64 = 256 query rows of one (segment, query head).  Wave w
+// owns four blocks of 16 rows, rows q0 + 64 nb + 16 w, so the four waves reach the causal
+// diagonal together and share every K/V tile.  K and V tiles of 64 keys stream HBM -> LDS
+// through global_load_lds into a 3-slot ring (one barrier per tile); each wave reads a
+// tile's K rows and its transposed V once and uses them for all four of its blocks:
+//   scores  S^T = K Q^T       v_mfma_f32_16x16x32_f16, one query row per MFMA column
+//   softmax fp32, exp2 of one FMA (scale folded in), reference max moved only when a row's
+//           maximum passes it by 2^8, masks only on the diagonal and ragged tiles
+//   values  O^T = V^T P^T     P^T is the score MFMA's own output layout; V^T comes from
+//                             transposing LDS reads; row sums from an all-ones operand
+// Tiles entirely above a block's causal diagonal are skipped; the longest (last) query
+// tiles are launched first.
 // fp32: a plain VALU kernel (wave = one query row), exact fp32 throughout.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
 
+#include "kvp_gfx950.h"
 #include "kvp_internal.h"
 
 namespace kvp {
@@ -37,173 +42,223 @@ typedef int i32x2 __attribute__((ext_vector_type(2)));
 
 namespace pf {
 constexpr int D = 64;
-constexpr int QT = 64;  // query rows per workgroup
-constexpr int KT = 64;  // keys per iteration
-constexpr int NW = 4;
-constexpr int VTS = KT + 4; // padded row (in halfs) of the transposed V tile
+constexpr int QB = 256;      // query rows per workgroup (fp16)
+constexpr int NQB = 4;       // 16-row query blocks per wave
+constexpr int KT = 64;       // keys per tile
+constexpr int NBUF = 3;      // ring slots for K and for V
+constexpr int SLOT = KT * 128; // bytes of one K (or V) tile
+constexpr int NDMA = 4;      // 1 KB loads per wave per tile (two of K, two of V)
 constexpr float LOG2E = 1.4426950408889634f;
 } // namespace pf
 
 __device__ inline float pf_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-__device__ inline float xor_shfl(float x, int m)
-{
-    return __shfl_xor(x, m, 64);
-}
-
-// grid = (ceil(max_seqlen/64), Hq, nseg), block = 256
+// grid = (ceil(max_seqlen / 256), Hq, nseg), block = 256
 __global__ __launch_bounds__(256) void prefill_mfma_f16_kernel(
     const f16 *__restrict__ q, const f16 *__restrict__ k, const f16 *__restrict__ v,
     f16 *__restrict__ out, const int *__restrict__ cu, int hq, int hkv, float scale_log2,
     int causal)
 {
     using namespace pf;
-    __shared__ __attribute__((aligned(16))) char klds[KT * D * 2];      // [key][64] swizzled
-    __shared__ __attribute__((aligned(16))) f16 vt[D * VTS];            // [d][key] padded
+    __shared__ __attribute__((aligned(16))) char kring[NBUF * SLOT];
+    __shared__ __attribute__((aligned(16))) char vring[NBUF * SLOT];
 
-    const int qtile = blockIdx.x, h = blockIdx.y, seg = blockIdx.z;
+    // causal: the last query tiles have the most keys, so they are launched first
+    const int qtile = causal ? (int)gridDim.x - 1 - (int)blockIdx.x : (int)blockIdx.x;
+    const int h = blockIdx.y, seg = blockIdx.z;
     const int a = cu[seg];
     const int n = cu[seg + 1] - a;
-    const int q0 = qtile * QT;
+    const int q0 = qtile * QB;
     if (q0 >= n || n <= 0)
         return;
     const int g_kv = h / (hq / hkv);
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int col = lane & 15; // query row within the wave's 16 (MFMA column)
+    const int col = lane & 15; // query row within a 16-row block (MFMA column)
     const int grp = lane >> 4; // lane group 0..3
-    const int qi = q0 + wave * 16 + col; // query index within the segment
+    const float c = scale_log2;
 
-    // Q^T operand: lane holds Q[qi][8*grp .. +8] (step 0) and [32 + 8*grp ..] (step 1)
-    f16x8 qop[2];
+    // ---- this wave's query blocks: Q^T operands and each row's key limit ----
+    f16x8 qop[NQB][2];
+    int r0[NQB], lim[NQB];
 #pragma unroll
-    for (int st = 0; st < 2; ++st) {
-        if (qi < n)
-            qop[st] = *(const f16x8 *)(q + ((size_t)(a + qi) * hq + h) * D + st * 32 + grp * 8);
-        else
-            qop[st] = f16x8{0, 0, 0, 0, 0, 0, 0, 0};
+    for (int nb = 0; nb < NQB; ++nb) {
+        r0[nb] = q0 + 64 * nb + 16 * wave;
+        const int row = r0[nb] + col;
+        const f16 *qp = q + ((size_t)(a + min(row, n - 1)) * hq + h) * D + grp * 8;
+        const f16x8 z = {0, 0, 0, 0, 0, 0, 0, 0};
+        const f16x8 qa = *(const f16x8 *)qp, qb = *(const f16x8 *)(qp + 32);
+        qop[nb][0] = row < n ? qa : z;
+        qop[nb][1] = row < n ? qb : z;
+        lim[nb] = causal ? min(row + 1, n) : n; // keys >= lim are masked for this row
     }
+    const int kend = causal ? min(n, q0 + QB) : n; // keys any row of the workgroup sees
+    const int nt = (kend + KT - 1) / KT;
 
-    f32x4 acc[4]; // O^T tiles: d = 16*dt + 4*grp + i, query col
+    // ---- DMA of tile t into ring slot t % NBUF: wave w loads rows 16 w .. 16 w + 15 of K and
+    // of V (LDS row r, chunk slot s holds chunk s ^ (r & 7)); rows past the segment re-read
+    // its last row (they are masked) ----
+    auto issue = [&](int t) {
+        char *kd = kring + (t % NBUF) * SLOT;
+        char *vd = vring + (t % NBUF) * SLOT;
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt)
-        acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float m_run = -INFINITY, l_run = 0.f;
+        for (int ii = 0; ii < 2; ++ii) {
+            const int i = 2 * wave + ii;
+            const int r = 8 * i + (lane >> 3);
+            const int kk = min(t * KT + r, n - 1);
+            const size_t off = ((size_t)(a + kk) * hkv + g_kv) * D + (((lane & 7) ^ (r & 7)) * 8);
+            __builtin_amdgcn_global_load_lds((const void *)(k + off),
+                                             (__attribute__((address_space(3))) void *)(kd + i * 1024), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds((const void *)(v + off),
+                                             (__attribute__((address_space(3))) void *)(vd + i * 1024), 16, 0, 0);
+        }
+    };
 
-    const int kend = causal ? min(n, q0 + QT) : n; // keys needed by this workgroup
-    const int ntiles = (kend + KT - 1) / KT;
-    const int wq_hi = q0 + wave * 16 + 15; // last query row of this wave
+    // running state per block: reference max (scaled, log2 units), O^T rows 16 db + 4 grp + i
+    // of column col, and the row sum (every entry of accl holds it)
+    float mref[NQB];
+    f32x4 acc[NQB][4], accl[NQB];
+#pragma unroll
+    for (int nb = 0; nb < NQB; ++nb) {
+        mref[nb] = -INFINITY;
+        accl[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+            acc[nb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    const f16x8 ones = {1, 1, 1, 1, 1, 1, 1, 1};
 
-    for (int t = 0; t < ntiles; ++t) {
+    issue(0);
+    if (nt > 1)
+        issue(1);
+    for (int t = 0; t < nt; ++t) {
+        // this wave's loads of tile t have landed; after the barrier every wave's have, and
+        // every wave has finished reading tile t - 1, whose slot the next DMA refills
+        if (t + 1 < nt)
+            wait_vm<NDMA>();
+        else
+            wait_vm<0>();
+        block_barrier();
+        if (t + 2 < nt)
+            issue(t + 2);
         const int k0 = t * KT;
-        // ---- K tile -> LDS (2 instructions of 1 KB per wave), chunk swizzled ----
+        bool any = false;
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int inst = wave * 2 + i;           // 0..7, rows 8*inst .. 8*inst+7
-            const int r = inst * 8 + (lane >> 3);
-            const int cg = (lane & 7) ^ (r & 7);
-            const int kk = k0 + r;
-            if (kk < kend) {
-                const f16 *src = k + ((size_t)(a + kk) * hkv + g_kv) * D + cg * 8;
-                __builtin_amdgcn_global_load_lds((const void *)src,
-                                                 (__attribute__((address_space(3))) void *)(klds + inst * 1024),
-                                                 16, 0, 0);
-            }
+        for (int nb = 0; nb < NQB; ++nb)
+            any = any || (r0[nb] < n && (!causal || k0 <= r0[nb] + 15));
+        if (!any)
+            continue;
+        const char *kt = kring + (t % NBUF) * SLOT;
+        const char *vt = vring + (t % NBUF) * SLOT;
+        // K rows (A of the score MFMA): key 16 kb + col, dims 8 grp .. and 32 + 8 grp ..
+        f16x8 kop[4][2];
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+            const int r = kb * 16 + col;
+            kop[kb][0] = lds_b128(kt + r * 128 + ((grp ^ (r & 7)) * 16));
+            kop[kb][1] = lds_b128(kt + r * 128 + (((4 + grp) ^ (r & 7)) * 16));
         }
-        // ---- V tile -> LDS transposed: thread loads 16 B of one key row ----
+        // V^T (A of the value MFMA), k-step ks, dims 16 db ..: lane L of group grp addresses
+        // key row 16 (2 ks + h) + 4 grp + L / 4, dims 16 db + 4 (L % 4); the transposing
+        // read hands lane i element j = half i % 4 of lane 4 j + i / 4's 8 bytes
+        f16x4 vraw[2][4][2];
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int idx = threadIdx.x + i * 256; // 0..511 = 64 rows x 8 chunks
-            const int r = idx >> 3, c = idx & 7;
-            const int kk = k0 + r;
-            f16x8 vv = f16x8{0, 0, 0, 0, 0, 0, 0, 0};
-            if (kk < kend)
-                vv = *(const f16x8 *)(v + ((size_t)(a + kk) * hkv + g_kv) * D + c * 8);
+        for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-            for (int e = 0; e < 8; ++e)
-                vt[(c * 8 + e) * VTS + r] = vv[e];
-        }
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();
+            for (int db = 0; db < 4; ++db)
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh) {
+                    const int row = 16 * (2 * ks + hh) + 4 * grp + (col >> 2);
+                    const int ch = 2 * db + ((col & 3) >> 1);
+                    vraw[ks][db][hh] = lds_tr16_b64(vt + row * 128 + ((ch ^ (row & 7)) * 16) + (col & 1) * 8);
+                }
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+            asm volatile("" : "+v"(kop[kb][0]), "+v"(kop[kb][1]));
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+            for (int db = 0; db < 4; ++db)
+                asm volatile("" : "+v"(vraw[ks][db][0]), "+v"(vraw[ks][db][1]));
+        f16x8 vop[2][4];
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+            for (int db = 0; db < 4; ++db)
+                vop[ks][db] = __builtin_shufflevector(vraw[ks][db][0], vraw[ks][db][1], 0, 1, 2, 3, 4, 5, 6, 7);
 
-        if (!(causal && k0 > wq_hi)) { // wave-uniform: tile has keys this wave can see
-            // ---- S^T = K Q^T : 4 key tiles of 16 ----
+#pragma unroll
+        for (int nb = 0; nb < NQB; ++nb) {
+            if (!(r0[nb] < n && (!causal || k0 <= r0[nb] + 15)))
+                continue; // wave-uniform: no key of this tile is visible to the block
+            // scores: sacc[kb][i] = S[key k0 + 16 kb + 4 grp + i][row r0 + col] (unscaled)
             f32x4 sacc[4];
 #pragma unroll
-            for (int kt = 0; kt < 4; ++kt) {
-                sacc[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
-                const int r = kt * 16 + col; // key row used as MFMA row
-#pragma unroll
-                for (int st = 0; st < 2; ++st) {
-                    const int c = st * 4 + grp;
-                    const f16x8 kop = *(const f16x8 *)(klds + r * 128 + ((c ^ (r & 7)) * 16));
-                    sacc[kt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop, qop[st], sacc[kt], 0, 0, 0);
-                }
+            for (int kb = 0; kb < 4; ++kb) {
+                const f32x4 s0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop[kb][0], qop[nb][0],
+                                                                        f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+                sacc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop[kb][1], qop[nb][1], s0, 0, 0, 0);
             }
-            // lane holds S^T[key = 16*kt + 4*grp + i][query col]
-            float tmax = -INFINITY;
+            const bool full = (!causal || k0 + KT - 1 <= r0[nb]) && k0 + KT <= n;
+            if (!full) {
 #pragma unroll
-            for (int kt = 0; kt < 4; ++kt)
+                for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int kk = k0 + kt * 16 + grp * 4 + i;
-                    const bool ok = kk < kend && (!causal || kk <= qi);
-                    const float x = ok ? sacc[kt][i] * scale_log2 : -INFINITY;
-                    sacc[kt][i] = x;
-                    tmax = fmaxf(tmax, x);
-                }
-            tmax = fmaxf(tmax, xor_shfl(tmax, 16));
-            tmax = fmaxf(tmax, xor_shfl(tmax, 32));
-            const float mn = fmaxf(m_run, tmax);
-            const float alpha = mn == -INFINITY ? 1.f : pf_exp2(m_run - mn);
-            m_run = mn;
-            float psum = 0.f;
+                    for (int i = 0; i < 4; ++i)
+                        sacc[kb][i] = k0 + 16 * kb + 4 * grp + i < lim[nb] ? sacc[kb][i] : -INFINITY;
+            }
+            float mt = fmaxf(fmaxf(sacc[0][0], sacc[0][1]), fmaxf(sacc[0][2], sacc[0][3]));
+#pragma unroll
+            for (int kb = 1; kb < 4; ++kb)
+                mt = fmaxf(mt, fmaxf(fmaxf(sacc[kb][0], sacc[kb][1]), fmaxf(sacc[kb][2], sacc[kb][3])));
+            mt = group_max(mt) * c;
+            // a row's reference max moves only when the row's own maximum passes it by more
+            // than 2^8; between moves p = 2^(s c - mref) < 256 and nothing needs rescaling.
+            // Rows that do not move scale by exactly 1, so no row depends on another's keys.
+            const bool need = mt > mref[nb] + RESCALE_LOG2;
+            if (__ballot(need) != 0) {
+                const float mn = need ? mt : mref[nb];
+                const float alpha = need ? (mref[nb] == -INFINITY ? 0.f : pf_exp2(mref[nb] - mn)) : 1.f;
+#pragma unroll
+                for (int db = 0; db < 4; ++db)
+                    acc[nb][db] *= alpha;
+                accl[nb] *= alpha;
+                mref[nb] = mn;
+            }
+            const float mc = mref[nb] == -INFINITY ? 0.f : mref[nb];
+            // P^T operand of k-step ks, slot s: key 16 (2 ks + s / 4) + 4 grp + s % 4 =
+            // sacc[2 ks + s / 4][s % 4], rounded once to fp16
             f16x8 pop[2];
 #pragma unroll
-            for (int kt = 0; kt < 4; ++kt)
+            for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const float p = mn == -INFINITY ? 0.f : pf_exp2(sacc[kt][i] - mn);
-                    const f16 ph = (f16)p;
-                    psum += (float)ph; // normaliser from the same rounded weights
-                    pop[kt >> 1][(kt & 1) * 4 + i] = ph;
-                }
-            l_run = l_run * alpha + psum;
-#pragma unroll
-            for (int dt = 0; dt < 4; ++dt)
-                acc[dt] *= alpha;
-            // ---- O^T += V^T P^T : per 32-key step, k slot (grp, e) -> key
-            //      32*ks + (e < 4 ? 4*grp + e : 16 + 4*grp + e - 4) ----
+                for (int s = 0; s < 8; ++s)
+                    pop[ks][s] = (f16)pf_exp2(fmaf(sacc[2 * ks + (s >> 2)][s & 3], c, -mc));
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) {
 #pragma unroll
-                for (int dt = 0; dt < 4; ++dt) {
-                    const int dr = dt * 16 + col;
-                    const f16 *row = vt + dr * VTS + ks * 32 + grp * 4;
-                    const f16x4 lo = *(const f16x4 *)(row);
-                    const f16x4 hi = *(const f16x4 *)(row + 16);
-                    const f16x8 vop = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-                    acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vop, pop[ks], acc[dt], 0, 0, 0);
-                }
+                for (int db = 0; db < 4; ++db)
+                    acc[nb][db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vop[ks][db], pop[ks], acc[nb][db], 0, 0, 0);
+                accl[nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, pop[ks], accl[nb], 0, 0, 0);
             }
         }
-        __syncthreads(); // before the next tile overwrites klds / vt
     }
 
-    // ---- normalise and store: lane holds O^T[d = 16*dt + 4*grp + i][query col] ----
-    float lt = l_run;
-    lt += xor_shfl(lt, 16);
-    lt += xor_shfl(lt, 32);
-    if (qi < n) {
-        const float inv = lt > 0.f ? 1.f / lt : 0.f;
-        f16 *dst = out + ((size_t)(a + qi) * hq + h) * D;
+    // ---- normalise and store: lane holds O^T[d = 16 db + 4 grp + i][row r0 + col] ----
 #pragma unroll
-        for (int dt = 0; dt < 4; ++dt) {
-            f16x4 o4;
+    for (int nb = 0; nb < NQB; ++nb) {
+        const int row = r0[nb] + col;
+        if (row >= n)
+            continue;
+        const float l = accl[nb][0];
+        const float inv = l > 0.f ? 1.f / l : 0.f;
+        f16 *dst = out + ((size_t)(a + row) * hq + h) * D + grp * 4;
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                o4[i] = (f16)(acc[dt][i] * inv);
-            *(f16x4 *)(dst + dt * 16 + grp * 4) = o4;
+        for (int db = 0; db < 4; ++db) {
+            const f16x4 o4 = {(f16)(acc[nb][db][0] * inv), (f16)(acc[nb][db][1] * inv), (f16)(acc[nb][db][2] * inv),
+                              (f16)(acc[nb][db][3] * inv)};
+            *(f16x4 *)(dst + 16 * db) = o4;
         }
     }
 }
@@ -296,7 +351,7 @@ extern "C" kvp_status varlen_causal_prefill(const kvp_dims *dims, void *out, con
     const float sl2 = scale * pf::LOG2E;
     hipStream_t st = (hipStream_t)stream;
     if (dims->dtype == KVP_F16) {
-        dim3 grid((max_seqlen + pf::QT - 1) / pf::QT, dims->num_q_heads, nseg);
+        dim3 grid((max_seqlen + pf::QB - 1) / pf::QB, dims->num_q_heads, nseg);
         hipLaunchKernelGGL(prefill_mfma_f16_kernel, grid, dim3(256), 0, st, (const f16 *)q,
                            (const f16 *)k, (const f16 *)v, (f16 *)out, d_cu_seqlens,
                            dims->num_q_heads, dims->num_kv_heads, sl2, causal);
