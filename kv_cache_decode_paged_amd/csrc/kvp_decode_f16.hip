@@ -386,10 +386,17 @@ __device__ __forceinline__ void run_item(const DecodeParams &P, const Addr &A, c
                     sacc[kb][i] = (bok[kb] && tok < lim) ? sacc[kb][i] : -INFINITY;
                 }
         }
-        float mt = fmaxf(fmaxf(sacc[0][0], sacc[0][1]), fmaxf(sacc[0][2], sacc[0][3]));
+        float mt;
+        if constexpr (KB == 4) {
+            mt = max16(sacc);
+        } else {
+            mt = max3(sacc[0][0], sacc[0][1], sacc[0][2]);
 #pragma unroll
-        for (int kb = 1; kb < KB; ++kb)
-            mt = fmaxf(mt, fmaxf(fmaxf(sacc[kb][0], sacc[kb][1]), fmaxf(sacc[kb][2], sacc[kb][3])));
+            for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                for (int i = kb == 0 ? 3 : 0; i < 4; ++i)
+                    mt = max3(mt, sacc[kb][i], sacc[kb][i]);
+        }
         mt = group_max(mt) * c;
         // a column's reference max moves only when the column's own maximum passes it by more
         // than 2^8: between moves p = 2^(s c - mref) stays below 256, exact in fp16 range, and

@@ -53,16 +53,36 @@ __device__ inline void lds_store_b128(char *p, i32x4 v)
     asm volatile("ds_write_b128 %0, %1" ::"v"(lds_addr(p)), "v"(v) : "memory");
 }
 
+// maximum of three as one v_max3_f32 (fmaxf would first quiet each operand, a
+// canonicalising v_max per input; the scores here are never signalling NaNs)
+__device__ inline float max3(float a, float b, float c)
+{
+    float r;
+    asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+    return r;
+}
+// maximum of the 16 scores a lane holds for one MFMA column (four 4-row accumulators)
+typedef float f32x4_ __attribute__((ext_vector_type(4)));
+__device__ inline float max16(const f32x4_ (&s)[4])
+{
+    const float a = max3(s[0][0], s[0][1], s[0][2]), b = max3(s[0][3], s[1][0], s[1][1]);
+    const float c = max3(s[1][2], s[1][3], s[2][0]), d = max3(s[2][1], s[2][2], s[2][3]);
+    const float e = max3(s[3][0], s[3][1], s[3][2]);
+    return max3(max3(a, b, c), max3(d, e, s[3][3]), a);
+}
+
 // max over lanes col, col + 16, col + 32, col + 48 (the k-groups of one MFMA column): swap
 // odd and even 16-lane rows, then the two 32-lane halves, without an LDS round trip
 __device__ inline float group_max(float x)
 {
     const unsigned u = __builtin_bit_cast(unsigned, x);
     const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
-    x = fmaxf(__builtin_bit_cast(float, (unsigned)a[0]), __builtin_bit_cast(float, (unsigned)a[1]));
+    const float x1 = __builtin_bit_cast(float, (unsigned)a[0]), x2 = __builtin_bit_cast(float, (unsigned)a[1]);
+    x = max3(x1, x2, x2);
     const unsigned w = __builtin_bit_cast(unsigned, x);
     const auto b = __builtin_amdgcn_permlane32_swap(w, w, false, false);
-    return fmaxf(__builtin_bit_cast(float, (unsigned)b[0]), __builtin_bit_cast(float, (unsigned)b[1]));
+    const float y1 = __builtin_bit_cast(float, (unsigned)b[0]), y2 = __builtin_bit_cast(float, (unsigned)b[1]);
+    return max3(y1, y2, y2);
 }
 
 // growth of a column's maximum (log2 units) that moves its softmax reference

@@ -53,19 +53,23 @@ constexpr float LOG2E = 1.4426950408889634f;
 
 __device__ inline float pf_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// grid = (ceil(max_seqlen / 256), Hq, nseg), block = 256
+// grid = (Hq, nseg, ceil(max_seqlen / 256)), block = 256
 __global__ __launch_bounds__(256) void prefill_mfma_f16_kernel(
     const f16 *__restrict__ q, const f16 *__restrict__ k, const f16 *__restrict__ v,
     f16 *__restrict__ out, const int *__restrict__ cu, int hq, int hkv, float scale_log2,
     int causal)
 {
     using namespace pf;
+    // one barrier per tile: the DMA of tile t + 2 refills the slot of tile t - 1, so three
+    // slots are the minimum
+    static_assert(NBUF >= 3, "ring of at least three slots");
     __shared__ __attribute__((aligned(16))) char kring[NBUF * SLOT];
     __shared__ __attribute__((aligned(16))) char vring[NBUF * SLOT];
 
-    // causal: the last query tiles have the most keys, so they are launched first
-    const int qtile = causal ? (int)gridDim.x - 1 - (int)blockIdx.x : (int)blockIdx.x;
-    const int h = blockIdx.y, seg = blockIdx.z;
+    // the query tile is the slowest grid dimension: workgroups are dispatched x fastest, so
+    // with causal masking every head's and segment's last (longest) tiles go first
+    const int qtile = causal ? (int)gridDim.z - 1 - (int)blockIdx.z : (int)blockIdx.z;
+    const int h = blockIdx.x, seg = blockIdx.y;
     const int a = cu[seg];
     const int n = cu[seg + 1] - a;
     const int q0 = qtile * QB;
@@ -208,11 +212,7 @@ __global__ __launch_bounds__(256) void prefill_mfma_f16_kernel(
                     for (int i = 0; i < 4; ++i)
                         sacc[kb][i] = k0 + 16 * kb + 4 * grp + i < lim[nb] ? sacc[kb][i] : -INFINITY;
             }
-            float mt = fmaxf(fmaxf(sacc[0][0], sacc[0][1]), fmaxf(sacc[0][2], sacc[0][3]));
-#pragma unroll
-            for (int kb = 1; kb < 4; ++kb)
-                mt = fmaxf(mt, fmaxf(fmaxf(sacc[kb][0], sacc[kb][1]), fmaxf(sacc[kb][2], sacc[kb][3])));
-            mt = group_max(mt) * c;
+            const float mt = group_max(max16(sacc)) * c;
             // a row's reference max moves only when the row's own maximum passes it by more
             // than 2^8; between moves p = 2^(s c - mref) < 256 and nothing needs rescaling.
             // Rows that do not move scale by exactly 1, so no row depends on another's keys.
@@ -344,14 +344,14 @@ extern "C" kvp_status varlen_causal_prefill(const kvp_dims *dims, void *out, con
     if (!out || !q || !k || !v || !d_cu_seqlens ||
         (((uintptr_t)out | (uintptr_t)q | (uintptr_t)k | (uintptr_t)v) & 15))
         return fail(KVP_ERR_INVALID, "varlen_causal_prefill: NULL or misaligned pointer");
-    if (nseg > 65535 || dims->num_q_heads > 65535)
-        return fail(KVP_ERR_UNSUPPORTED, "varlen_causal_prefill: nseg or H_q too large");
+    if (nseg > 65535 || dims->num_q_heads > 65535 || (max_seqlen + pf::QB - 1) / pf::QB > 65535)
+        return fail(KVP_ERR_UNSUPPORTED, "varlen_causal_prefill: nseg, H_q or max_seqlen too large");
     if (scale == 0.f)
         scale = 1.0f / sqrtf((float)pf::D);
     const float sl2 = scale * pf::LOG2E;
     hipStream_t st = (hipStream_t)stream;
     if (dims->dtype == KVP_F16) {
-        dim3 grid((max_seqlen + pf::QB - 1) / pf::QB, dims->num_q_heads, nseg);
+        dim3 grid(dims->num_q_heads, nseg, (max_seqlen + pf::QB - 1) / pf::QB);
         hipLaunchKernelGGL(prefill_mfma_f16_kernel, grid, dim3(256), 0, st, (const f16 *)q,
                            (const f16 *)k, (const f16 *)v, (f16 *)out, d_cu_seqlens,
                            dims->num_q_heads, dims->num_kv_heads, sl2, causal);
