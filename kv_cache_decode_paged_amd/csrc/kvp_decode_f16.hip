@@ -581,15 +581,15 @@ __global__ __launch_bounds__(64) void decode_f16_kernel(DecodeParams P, Addr A, 
         int ctx = P.ctx_lens[it.b];
         ctx = ctx < 0 ? 0 : (ctx > maxc ? maxc : ctx);
         const int nbt = (ctx + BS - 1) / BS;
-        // one item up to UNSPLIT_BLOCKS blocks, else ceil(blocks / SPLIT_BLOCKS) parts of equal tile
-        // counts: part k holds tiles [k T / n, (k+1) T / n) of the pair's T tiles
+        // one item up to UNSPLIT_BLOCKS blocks, else ceil(blocks / SPLIT_BLOCKS) parts; the last
+        // (the pair's merging item) up to SPLIT_SLACK tiles longer than the others
         const int n = nbt <= UNSPLIT_BLOCKS ? 1 : (nbt + SPLIT_BLOCKS - 1) / SPLIT_BLOCKS;
         if (k >= n)
             return;
         const int T = (nbt + 3) >> 2;
-        it.blk0 = 4 * (int)((long long)k * T / n);
+        it.blk0 = min(nbt, 4 * part_tile_begin(T, n, k, SPLIT_SLACK));
         it.nmem = 1;
-        it.nblk = max(0, min(4 * (int)((long long)(k + 1) * T / n), nbt) - it.blk0);
+        it.nblk = max(0, min(4 * part_tile_begin(T, n, k + 1, SPLIT_SLACK), nbt) - it.blk0);
         it.end = ctx;
         it.nparts = n;
         it.pbase = pair * PV.ipp;

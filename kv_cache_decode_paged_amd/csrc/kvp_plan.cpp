@@ -67,10 +67,9 @@ int split_parts(int nb, bool forced)
     return (nb + SPLIT_BLOCKS - 1) / SPLIT_BLOCKS;
 }
 // first block of part k of n over nb blocks (part k holds tiles [k T / n, (k+1) T / n))
-int split_start(int nb, int n, int k)
+int split_start(int nb, int n, int k, int slack = 0)
 {
-    const int T = (nb + 3) / 4;
-    return std::min(nb, 4 * (int)((long long)k * T / n));
+    return std::min(nb, 4 * part_tile_begin((nb + 3) / 4, n, k, slack));
 }
 
 struct SubRun {
@@ -251,8 +250,8 @@ kvp_status decode_plan_build(const kvp_dims *dims, const int32_t *table, int32_t
             const long long p = (long long)b * hkv + g;
             for (int k = 0; k < npriv; ++k) {
                 const int nb = nbt[b] - first;
-                const int blk0 = first + split_start(nb, npriv, k);
-                const int nblk = nb <= 0 ? 0 : first + split_start(nb, npriv, k + 1) - blk0;
+                const int blk0 = first + split_start(nb, npriv, k, SPLIT_SLACK);
+                const int nblk = nb <= 0 ? 0 : first + split_start(nb, npriv, k + 1, SPLIT_SLACK) - blk0;
                 const int slot = pair_nparts[p] > 1 ? pair_base[p] + shared_parts[b] + k : -1;
                 record(0, b, g, 1, blk0, nblk, c[b], slot, pair_nparts[p], pair_base[p], b);
             }

@@ -23,6 +23,28 @@ constexpr int BPI = 32;  // blocks per work item (512 tokens)
 // count faster than the shorter tail saves, so the parts are as long as an item may be.
 constexpr int SPLIT_BLOCKS = 32;
 constexpr int UNSPLIT_BLOCKS = 32; // longest pair kept in one item (at most BPI)
+// Tiles (4 blocks) of the parts of a range of T tiles split n ways: part k covers tiles
+// [part_tile_begin(T, n, k, slack), part_tile_begin(T, n, k + 1, slack)).  The last part
+// -- the one that holds the range's final blocks, which merges a split pair -- gets up to
+// `slack` tiles more than the others (at most 8), the others share the rest evenly.
+constexpr int part_tile_begin(int T, int n, int k, int slack)
+{
+    if (k <= 0)
+        return 0;
+    if (k >= n)
+        return T;
+    const int even = (T + n - 1) / n;
+    int m = even + slack < 8 ? even + slack : 8;
+    if (m > T - (n - 1))
+        m = T - (n - 1); // every other part keeps a tile
+    if (m < even)
+        m = even;
+    const int rest = T - m;
+    return k == n - 1 ? rest : (int)((long long)k * rest / (n - 1));
+}
+// tiles of extra length for the last part of a pair's private range (measured: giving the
+// polled merge two tiles of lead over the other parts gained nothing, so none)
+constexpr int SPLIT_SLACK = 0;
 constexpr int REC = 48;  // int32 per record
 constexpr int MAXM = 16; // members of one shared item (and at most 16 query rows)
 constexpr int XCDS = 8;  // MI355X: workgroup i runs on XCD i % 8 (round-robin dispatch)

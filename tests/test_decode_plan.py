@@ -10,7 +10,8 @@ plan must guarantee, read independently from the image:
 * each XCD's items are spread over its 32 CUs (queue indices 32 apart share a CU) so that
   no CU carries more than its share of the work plus one item;
 * without prefix sharing the plan is exactly the per-pair split (one item up to 32 blocks,
-  else ceil(blocks/32) parts of equal tile counts) that paged_decode_attention uses (so the two are bit-identical on the GPU).
+  else ceil(blocks/32) parts, the last ceil(tiles/parts) long, the others sharing the rest) that
+  paged_decode_attention uses (so the two are bit-identical on the GPU).
 
 Prefix sharing follows the pages: requests forked from one prefix share its physical
 blocks until copy-on-write ([PAGED] paged-attention article, SECTION 3).
@@ -178,9 +179,14 @@ def test_plan_without_sharing_is_the_plain_split():
     for b in range(len(ctx)):
         nbt = math.ceil(ctx[b] / BS)
         n, T = (1 if nbt <= BPI else math.ceil(nbt / BPI)), math.ceil(nbt / 4)
+        # the last part (it holds the final blocks) takes ceil(T / n) tiles, the others share
+        # the rest evenly
+        last = -(-T // n)
+        rest = T - last
+        starts = [0] + [k * rest // (n - 1) for k in range(1, n - 1)] + ([rest] if n > 1 else []) + [T]
         for g in range(2):
-            for k in range(n):  # equal tile counts per part
-                b0, b1 = min(nbt, 4 * (k * T // n)), min(nbt, 4 * ((k + 1) * T // n))
+            for k in range(n):
+                b0, b1 = min(nbt, 4 * starts[k]), min(nbt, 4 * starts[k + 1])
                 want.append((b, g, b0, b1 - b0))
     assert got == sorted(want)
 
