@@ -5,6 +5,7 @@ package.  The product library never does, and the oracle imports nothing from it
 
 Contents
   * libkvp_oracle.so (kvp_oracle.c): plain scalar fp64 loops -- attention row, GQA decode,
+    several new rows per request against a cache (chunked prefill / draft verification),
     full causal recompute, packed varlen prefill, block partial + merge, KV bytes/token.
   * brute.py   : an independent pure-Python brute force (math.fsum) for tiny shapes.
   * pagepool.py: the block pool / block table / copy-on-write model.
@@ -46,6 +47,8 @@ def _load():
     lib.orc_varlen_prefill.argtypes = [ctypes.c_int] * 4 + [_dp, _dp, _dp, _ip, ctypes.c_int,
                                                             ctypes.c_int, ctypes.c_double, _dp]
     lib.orc_varlen_prefill.restype = None
+    lib.orc_chunk_attention.argtypes = [ctypes.c_int] * 5 + [_ip, _ip, _dp, _dp, _dp, ctypes.c_double, _dp]
+    lib.orc_chunk_attention.restype = None
     lib.orc_partial.argtypes = [ctypes.c_int] * 3 + [_dp, _dp, ctypes.c_long, _dp, ctypes.c_long,
                                                      ctypes.c_double, _dp, _dp, _dp]
     lib.orc_partial.restype = None
@@ -118,6 +121,27 @@ def full_causal(q, k, v, scale=None):
     scale = default_scale(d) if scale is None else scale
     out, op = _d(np.zeros((n, Hq, d)))
     lib.orc_full_causal(n, Hq, Hkv, d, qp, kp, vp, scale, op)
+    return out
+
+
+def chunk_attention(q, K, V, ctx, cu_q, scale=None):
+    """Several new rows per request against its cache: q [T, Hq, d] packed by cu_q [B+1];
+    K, V [B, Hkv, Lmax, d]; the rows of request b are positions ctx[b] - m_b .. ctx[b] - 1
+    and row i attends to positions 0 .. ctx[b] - m_b + i.  -> out [T, Hq, d]."""
+    lib = _load()
+    q, qp = _d(q)
+    K, Kp = _d(K)
+    V, Vp = _d(V)
+    ctx, cp = _i(ctx)
+    cu, cup = _i(cu_q)
+    T, Hq, d = q.shape
+    B, Hkv, Lmax, _ = K.shape
+    m = np.diff(cu)
+    assert len(cu) == B + 1 and cu[0] == 0 and cu[-1] == T and (m >= 0).all()
+    assert (ctx >= m).all() and (ctx <= Lmax).all()
+    scale = default_scale(d) if scale is None else scale
+    out, op = _d(np.zeros((T, Hq, d)))
+    lib.orc_chunk_attention(B, Hq, Hkv, d, Lmax, cp, cup, qp, Kp, Vp, scale, op)
     return out
 
 

@@ -11,7 +11,10 @@ Definitions followed:
     (gustavoai "La cache de claves y valores", four-step token recipe);
   * GQA head map h -> h // (Hq // Hkv) (xformers demo, section 5, BMGHK layout);
   * packed varlen prefill, block-diagonal (optionally causal) mask (xformers demo,
-    section 4).
+    section 4);
+  * several new rows per request against its cache, each row over the positions up to its
+    own (draft verification as one pass over gamma positions, "Tornar a inferencia
+    barata" chapter, speculative-decoding section).
 """
 import math
 
@@ -63,4 +66,26 @@ def varlen_prefill(q, k, v, cu, causal, scale):
                 o, _ = attention_row(q[i][h], Ks, Vs, scale)
                 rows.append(o)
             out[i] = rows
+    return out
+
+
+def chunk_attention(q, K, V, ctx, cu, scale):
+    """Several new rows per request against its cache: q[T][Hq][d] with request b's rows
+    cu[b] .. cu[b+1]-1, K/V[B][Hkv][Lmax][d], ctx[B].  The m rows of request b are its
+    last m positions; row i attends to positions 0 .. ctx[b] - m + i (the draft-verification
+    pass of the "Tornar a inferencia barata" chapter, one forward pass over gamma positions)."""
+    B, Hq = len(ctx), len(q[0])
+    Hkv = len(K[0])
+    grp = Hq // Hkv
+    out = [None] * len(q)
+    for b in range(B):
+        m = cu[b + 1] - cu[b]
+        for i in range(m):
+            pos = ctx[b] - m + i  # this row's own position
+            rows = []
+            for h in range(Hq):
+                g = h // grp
+                o, _ = attention_row(q[cu[b] + i][h], K[b][g][:pos + 1], V[b][g][:pos + 1], scale)
+                rows.append(o)
+            out[cu[b] + i] = rows
     return out

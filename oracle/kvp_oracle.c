@@ -21,6 +21,8 @@
  *           (softmax(Q K^T / sqrt(d_k)) V).
  *   [FLASH] same feed, FlashAttention post: "Was ist der mathematische Aspekt von Softmax?"
  *           (partial softmax blocks merged by rescaling with e^(m_local - m_global)).
+ *   [PAGED] same feed, paged-attention article: SECTION 3 "Copy-on-Write: Shared System
+ *           Prompts".
  */
 #include <math.h>
 #include <stddef.h>
@@ -149,6 +151,37 @@ void orc_full_causal(int n, int Hq, int Hkv, int d, const double *q, const doubl
         }
     }
     free(S);
+}
+
+/* ---------------------------------------------------------------------------------------
+ * Several new query rows per request against its cache (chunked prefill into an existing
+ * prefix; verification of gamma drafted tokens).  [CHAP] speculative-decoding section:
+ * checking a proposed run of gamma tokens is one forward pass over gamma positions, a
+ * matrix-matrix product; [KVES] prompt paragraph: the rows of a stretch of known tokens
+ * are computed in one pass, each by the same causal mask, and leave one cached row per
+ * token; [PAGED] copy-on-write section: requests continue from shared prefix blocks with
+ * their own tokens.  Reading: the m new rows of request b are the last m positions of its
+ * context, ctx[b] - m .. ctx[b] - 1, already in the cache, and each attends to every
+ * position up to and including its own -- row i over positions 0 .. ctx[b] - m + i.
+ *   q   [T][Hq][d] packed, request b's rows cu[b] .. cu[b+1]-1
+ *   K, V  [B][Hkv][Lmax][d]        out [T][Hq][d]
+ * ------------------------------------------------------------------------------------- */
+void orc_chunk_attention(int B, int Hq, int Hkv, int d, int Lmax, const int *ctx,
+                         const int *cu, const double *q, const double *K, const double *V,
+                         double scale, double *out)
+{
+    for (int b = 0; b < B; ++b) {
+        int m = cu[b + 1] - cu[b];
+        int first = ctx[b] - m; /* position of the first new row */
+        for (int i = 0; i < m; ++i)
+            for (int h = 0; h < Hq; ++h) {
+                int g = orc_kv_head(h, Hq, Hkv);
+                long base = (((long)b * Hkv + g) * Lmax) * d;
+                long row = (long)cu[b] + i;
+                orc_attention_row(d, first + i + 1, q + (row * Hq + h) * d, K + base, d, V + base, d,
+                                  scale, out + (row * Hq + h) * d, NULL);
+            }
+    }
 }
 
 /* ---------------------------------------------------------------------------------------

@@ -33,11 +33,14 @@ MUTANTS = [
      "acc += row[j] * v[((long)j * Hkv + 0) * d + c];", None),
     ("kv_bytes_missing_two", "return 2LL * L * Hkv * d * elem_bytes;", "return 1LL * L * Hkv * d * elem_bytes;", None),
     ("decode_ctx_minus_one", "orc_attention_row(d, ctx[b],", "orc_attention_row(d, ctx[b] > 1 ? ctx[b] - 1 : 1,", None),
+    ("chunk_mask_from_cache_start", "orc_attention_row(d, first + i + 1,", "orc_attention_row(d, i + 1,", None),
+    ("chunk_drops_own_position", "orc_attention_row(d, first + i + 1,", "orc_attention_row(d, first + i > 0 ? first + i : 1,", None),
+    ("chunk_rows_of_first_request", "long row = (long)cu[b] + i;", "long row = (long)i;", None),
     ("score_transposed_index", "acc += q[c] * K[(long)j * kstride + c];\n        s[j] = scale * acc;\n        if (s[j] > m)\n            m = s[j];\n    }\n    double Z",
      "acc += q[c] * K[(long)c * kstride + (j % d)];\n        s[j] = scale * acc;\n        if (s[j] > m)\n            m = s[j];\n    }\n    double Z", None),
 ]
 
-SUITES = ["tests/test_oracle_pins.py", "tests/test_oracle_brute.py"]
+SUITES = ["tests/test_oracle_pins.py", "tests/test_oracle_brute.py", "tests/test_oracle_chunk.py"]
 
 
 @pytest.mark.parametrize("name,old,new,occ", MUTANTS, ids=[m[0] for m in MUTANTS])
