@@ -319,6 +319,26 @@ kvp_status paged_decode_attention_planned(const kvp_cache_desc *cache, int32_t l
                                           const void *d_plan, float scale, void *workspace,
                                           size_t ws_bytes, kvp_stream stream);
 
+/* Several new query rows per request against the paged cache: chunked prefill of a
+ * suffix into an existing (possibly shared) prefix, or the verification pass over gamma
+ * drafted tokens ([CHAP] speculative-decoding section: verifying gamma proposed tokens is
+ * one forward pass over gamma positions; [PAGED] SECTION 3: requests continue from shared
+ * prefix blocks with their own tokens).  Request b has m_b = d_cu_q[b+1] - d_cu_q[b] new
+ * rows, packed rows d_cu_q[b] .. of q and out; they are the last m_b of its
+ * d_context_lens[b] positions, whose K and V -- prefix and new rows -- are already in the
+ * cache (kv_append into block_table_reserve slots), and row i attends to positions
+ * 0 .. ctx_b - m_b + i (causal, aligned to the end of the context).
+ *   q, out        device fp16 [T][H_q][64], T = d_cu_q[B]
+ *   d_block_table device int32 [B][max_blocks]; entries outside [0, num_blocks) mask their
+ *                 keys; max_blocks <= 4096
+ *   d_cu_q        device int32 [B+1], non-decreasing from 0;  max_q >= every m_b
+ * Requires m_b <= ctx_b (rows with no position of their own get zeros).  fp16 caches only
+ * (UNSUPPORTED otherwise).  MFMA tiles with fp32 accumulation, as varlen_causal_prefill. */
+kvp_status paged_prefill_attention(const kvp_cache_desc *cache, int32_t layer, void *out,
+                                   const void *q, const int32_t *d_block_table, int32_t max_blocks,
+                                   const int32_t *d_context_lens, const int32_t *d_cu_q, int32_t B,
+                                   int32_t max_q, float scale, kvp_stream stream);
+
 /* Wait bound of the fp16 split merge.  A context split over several work items is merged
  * by the item that holds its final blocks: it polls the pair's counter until the others
  * have stored their partials, with a short sleep after each poll, and after `polls` polls

@@ -130,6 +130,8 @@ _sig("contiguous_decode_attention", _i32, [ctypes.POINTER(kvp_dims), _p, _p, _p,
 _sig("varlen_causal_prefill", _i32, [ctypes.POINTER(kvp_dims), _p, _p, _p, _p, _p, _i32, _i32, _i32,
                                      _f32, _p])
 _sig("kvp_decode_merge_polls", _i32, [_i32])
+_sig("paged_prefill_attention", _i32, [ctypes.POINTER(kvp_cache_desc), _i32, _p, _p, _p, _i32, _p, _p, _i32,
+                                       _i32, _f32, _p])
 _sig("kv_gather", _i32, [ctypes.POINTER(kvp_cache_desc), _i32, _p, _i32, _p, _i32, _i32, _p, _p, _p])
 
 
@@ -497,6 +499,29 @@ def paged_decode_attention_planned(cache: PagedKVCache, layer, q, plan, d_plan, 
                                                _dev(q, "q", cache.dtype), kn, vn, ctypes.byref(plan),
                                                _dev(d_plan, "plan"), float(scale), _dev(workspace, "workspace"),
                                                workspace.numel(), _stream(stream)))
+    return out
+
+
+def paged_prefill_attention(cache: PagedKVCache, layer, q, block_table, context_lens, cu_q, max_q, out=None,
+                            scale=0.0, stream=None):
+    """Several new rows per request against the paged cache (chunked prefill, draft
+    verification).  q: [T, H_q, 64] fp16 packed by cu_q (device int32 [B+1]); the rows of
+    request b are the last cu_q[b+1]-cu_q[b] of its context_lens[b] positions, already
+    appended to the cache; row i attends to positions 0 .. ctx - m + i."""
+    T, hq, d = q.shape
+    if hq != cache.num_q_heads or d != HEAD_DIM:
+        raise ValueError("paged_prefill_attention: q shape does not match the cache")
+    B = cu_q.numel() - 1
+    if block_table.shape[0] != B or context_lens.shape != (B,):
+        raise ValueError("paged_prefill_attention: table / context_lens / cu_q shape mismatch")
+    if out is None:
+        out = torch.empty_like(q)
+    _check(_lib.paged_prefill_attention(ctypes.byref(cache.desc), int(layer), _dev(out, "out", cache.dtype),
+                                        _dev(q, "q", cache.dtype),
+                                        _dev(block_table, "block_table", torch.int32), int(block_table.shape[1]),
+                                        _dev(context_lens, "context_lens", torch.int32),
+                                        _dev(cu_q, "cu_q", torch.int32), B, int(max_q), float(scale),
+                                        _stream(stream)))
     return out
 
 

@@ -42,6 +42,12 @@ __device__ inline f16x8 lds_b128(const char *p)
     asm volatile("ds_read_b128 %0, %1" : "=v"(r) : "v"(lds_addr(p)));
     return r;
 }
+__device__ inline int lds_b32(const void *p)
+{
+    int r;
+    asm volatile("ds_read_b32 %0, %1" : "=v"(r) : "v"(lds_addr((const char *)p)));
+    return r;
+}
 __device__ inline f16x4 lds_tr16_b64(const char *p)
 {
     f16x4 r;

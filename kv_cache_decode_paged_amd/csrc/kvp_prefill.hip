@@ -42,6 +42,7 @@ typedef int i32x2 __attribute__((ext_vector_type(2)));
 
 namespace pf {
 constexpr int D = 64;
+constexpr int BS = 16;       // tokens per cache block
 constexpr int QB = 256;      // query rows per workgroup (fp16)
 constexpr int NQB = 4;       // 16-row query blocks per wave
 constexpr int KT = 64;       // keys per tile
@@ -53,11 +54,32 @@ constexpr float LOG2E = 1.4426950408889634f;
 
 __device__ inline float pf_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// grid = (Hq, nseg, ceil(max_seqlen / 256)), block = 256
-__global__ __launch_bounds__(256) void prefill_mfma_f16_kernel(
-    const f16 *__restrict__ q, const f16 *__restrict__ k, const f16 *__restrict__ v,
-    f16 *__restrict__ out, const int *__restrict__ cu, int hq, int hkv, float scale_log2,
-    int causal)
+// Query rows and keys of one workgroup's sequence.  Packed (varlen prefill): segment s is
+// rows cu[s] .. cu[s+1]-1 of q and of k / v, every row a query and a key.  Paged (several
+// new rows against the cache): request s has rows cu[s] .. cu[s+1]-1 of q, the last of
+// its ctx[s] cached positions, whose keys are reached through the block table.
+struct PrefillArgs {
+    const f16 *q;
+    const f16 *k;      // packed k [T][Hkv][D], or the layer's K pool [blocks][Hkv][16][D]
+    const f16 *v;
+    f16 *out;
+    const int *cu;     // [nseg + 1] query-row offsets (packed: also key rows)
+    const int *ctx;    // paged: context length per request
+    const int *table;  // paged: block table [nseg][max_blocks]
+    int max_blocks;
+    int num_blocks;
+    int hq;
+    int hkv;
+    float scale_log2;
+    int causal;
+};
+
+// block ids of one request staged in LDS (paged): contexts of up to MAX_IDS blocks
+constexpr int MAX_IDS = 4096;
+
+// grid = (Hq, nseg, ceil(max query rows / 256)), block = 256
+template <bool PAGED>
+__global__ __launch_bounds__(256) void prefill_mfma_f16_kernel(PrefillArgs P)
 {
     using namespace pf;
     // one barrier per tile: the DMA of tile t + 2 refills the slot of tile t - 1, so three
@@ -65,13 +87,22 @@ __global__ __launch_bounds__(256) void prefill_mfma_f16_kernel(
     static_assert(NBUF >= 3, "ring of at least three slots");
     __shared__ __attribute__((aligned(16))) char kring[NBUF * SLOT];
     __shared__ __attribute__((aligned(16))) char vring[NBUF * SLOT];
+    __shared__ int ids[PAGED ? MAX_IDS : 1];
+    __shared__ int ids_bad;
 
     // the query tile is the slowest grid dimension: workgroups are dispatched x fastest, so
     // with causal masking every head's and segment's last (longest) tiles go first
-    const int qtile = causal ? (int)gridDim.z - 1 - (int)blockIdx.z : (int)blockIdx.z;
+    const int qtile = P.causal ? (int)gridDim.z - 1 - (int)blockIdx.z : (int)blockIdx.z;
     const int h = blockIdx.x, seg = blockIdx.y;
-    const int a = cu[seg];
-    const int n = cu[seg + 1] - a;
+    const int hq = P.hq, hkv = P.hkv, causal = P.causal;
+    const int a = P.cu[seg];             // first query row
+    const int n = P.cu[seg + 1] - a;     // query rows
+    int nk = n;                          // keys
+    if constexpr (PAGED) {
+        const int c = P.ctx[seg];
+        nk = c < 0 ? 0 : (c > P.max_blocks * BS ? P.max_blocks * BS : c);
+    }
+    const int off = nk - n; // row i attends to keys 0 .. off + i (the rows end the context)
     const int q0 = qtile * QB;
     if (q0 >= n || n <= 0)
         return;
@@ -80,7 +111,7 @@ __global__ __launch_bounds__(256) void prefill_mfma_f16_kernel(
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int col = lane & 15; // query row within a 16-row block (MFMA column)
     const int grp = lane >> 4; // lane group 0..3
-    const float c = scale_log2;
+    const float c = P.scale_log2;
 
     // ---- this wave's query blocks: Q^T operands and each row's key limit ----
     f16x8 qop[NQB][2];
@@ -89,31 +120,67 @@ __global__ __launch_bounds__(256) void prefill_mfma_f16_kernel(
     for (int nb = 0; nb < NQB; ++nb) {
         r0[nb] = q0 + 64 * nb + 16 * wave;
         const int row = r0[nb] + col;
-        const f16 *qp = q + ((size_t)(a + min(row, n - 1)) * hq + h) * D + grp * 8;
+        const f16 *qp = P.q + ((size_t)(a + min(row, n - 1)) * hq + h) * D + grp * 8;
         const f16x8 z = {0, 0, 0, 0, 0, 0, 0, 0};
         const f16x8 qa = *(const f16x8 *)qp, qb = *(const f16x8 *)(qp + 32);
         qop[nb][0] = row < n ? qa : z;
         qop[nb][1] = row < n ? qb : z;
-        lim[nb] = causal ? min(row + 1, n) : n; // keys >= lim are masked for this row
+        lim[nb] = causal ? max(0, min(off + row + 1, nk)) : nk; // keys >= lim are masked for this row
     }
-    const int kend = causal ? min(n, q0 + QB) : n; // keys any row of the workgroup sees
+    const int kend = causal ? max(0, min(nk, off + q0 + QB)) : nk; // keys any row of the workgroup sees
     const int nt = (kend + KT - 1) / KT;
+    // paged: the request's block ids for keys < kend, an unusable entry (-1) masks its keys
+    bool all_ok = true;
+    if constexpr (PAGED) {
+        if (threadIdx.x == 0)
+            ids_bad = 0;
+        __syncthreads();
+        const int nids = (kend + BS - 1) / BS;
+        int bad = 0;
+        for (int j = threadIdx.x; j < nids; j += 256) {
+            const int e = P.table[(size_t)seg * P.max_blocks + j];
+            const bool ok = e >= 0 && e < P.num_blocks;
+            ids[j] = ok ? e : -1;
+            bad |= !ok;
+        }
+        if (bad)
+            ids_bad = 1;
+        __syncthreads();
+        all_ok = ids_bad == 0;
+    }
 
     // ---- DMA of tile t into ring slot t % NBUF: wave w loads rows 16 w .. 16 w + 15 of K and
-    // of V (LDS row r, chunk slot s holds chunk s ^ (r & 7)); rows past the segment re-read
-    // its last row (they are masked) ----
+    // of V (LDS row r, chunk slot s holds chunk s ^ (r & 7)); rows past the workgroup's last
+    // visible key re-read that key's row (they are masked; its block id is staged), an
+    // unusable block reads block 0 (masked too) ----
     auto issue = [&](int t) {
         char *kd = kring + (t % NBUF) * SLOT;
         char *vd = vring + (t % NBUF) * SLOT;
+        int kk[2], e[2] = {0, 0};
+#pragma unroll
+        for (int ii = 0; ii < 2; ++ii) {
+            const int r = 8 * (2 * wave + ii) + (lane >> 3);
+            kk[ii] = min(t * KT + r, kend - 1); // beyond kend every row of the workgroup masks the key
+            if constexpr (PAGED)
+                e[ii] = lds_b32(&ids[kk[ii] >> 4]);
+        }
+        if constexpr (PAGED) {
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            asm volatile("" : "+v"(e[0]), "+v"(e[1]));
+        }
 #pragma unroll
         for (int ii = 0; ii < 2; ++ii) {
             const int i = 2 * wave + ii;
             const int r = 8 * i + (lane >> 3);
-            const int kk = min(t * KT + r, n - 1);
-            const size_t off = ((size_t)(a + kk) * hkv + g_kv) * D + (((lane & 7) ^ (r & 7)) * 8);
-            __builtin_amdgcn_global_load_lds((const void *)(k + off),
+            size_t off_e;
+            if constexpr (PAGED)
+                off_e = (((size_t)max(e[ii], 0) * hkv + g_kv) * BS + (kk[ii] & (BS - 1))) * D;
+            else
+                off_e = ((size_t)(a + kk[ii]) * hkv + g_kv) * D;
+            const size_t o = off_e + (((lane & 7) ^ (r & 7)) * 8);
+            __builtin_amdgcn_global_load_lds((const void *)(P.k + o),
                                              (__attribute__((address_space(3))) void *)(kd + i * 1024), 16, 0, 0);
-            __builtin_amdgcn_global_load_lds((const void *)(v + off),
+            __builtin_amdgcn_global_load_lds((const void *)(P.v + o),
                                              (__attribute__((address_space(3))) void *)(vd + i * 1024), 16, 0, 0);
         }
     };
@@ -149,7 +216,7 @@ __global__ __launch_bounds__(256) void prefill_mfma_f16_kernel(
         bool any = false;
 #pragma unroll
         for (int nb = 0; nb < NQB; ++nb)
-            any = any || (r0[nb] < n && (!causal || k0 <= r0[nb] + 15));
+            any = any || (r0[nb] < n && (!causal || k0 <= off + r0[nb] + 15));
         if (!any)
             continue;
         const char *kt = kring + (t % NBUF) * SLOT;
@@ -194,7 +261,7 @@ __global__ __launch_bounds__(256) void prefill_mfma_f16_kernel(
 
 #pragma unroll
         for (int nb = 0; nb < NQB; ++nb) {
-            if (!(r0[nb] < n && (!causal || k0 <= r0[nb] + 15)))
+            if (!(r0[nb] < n && (!causal || k0 <= off + r0[nb] + 15)))
                 continue; // wave-uniform: no key of this tile is visible to the block
             // scores: sacc[kb][i] = S[key k0 + 16 kb + 4 grp + i][row r0 + col] (unscaled)
             f32x4 sacc[4];
@@ -204,13 +271,28 @@ __global__ __launch_bounds__(256) void prefill_mfma_f16_kernel(
                                                                         f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
                 sacc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop[kb][1], qop[nb][1], s0, 0, 0, 0);
             }
-            const bool full = (!causal || k0 + KT - 1 <= r0[nb]) && k0 + KT <= n;
+            const bool full = all_ok && (!causal || k0 + KT - 1 <= off + r0[nb]) && k0 + KT <= nk;
             if (!full) {
+                bool bok[4] = {true, true, true, true};
+                if constexpr (PAGED) {
+                    if (!all_ok) { // keys of unusable blocks are masked
+                        int e4[4];
+#pragma unroll
+                        for (int kb = 0; kb < 4; ++kb)
+                            e4[kb] = lds_b32(&ids[min((k0 >> 4) + kb, MAX_IDS - 1)]);
+                        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+                        for (int kb = 0; kb < 4; ++kb) {
+                            asm volatile("" : "+v"(e4[kb]));
+                            bok[kb] = e4[kb] >= 0;
+                        }
+                    }
+                }
 #pragma unroll
                 for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
                     for (int i = 0; i < 4; ++i)
-                        sacc[kb][i] = k0 + 16 * kb + 4 * grp + i < lim[nb] ? sacc[kb][i] : -INFINITY;
+                        sacc[kb][i] = (bok[kb] && k0 + 16 * kb + 4 * grp + i < lim[nb]) ? sacc[kb][i] : -INFINITY;
             }
             const float mt = group_max(max16(sacc)) * c;
             // a row's reference max moves only when the row's own maximum passes it by more
@@ -253,7 +335,7 @@ __global__ __launch_bounds__(256) void prefill_mfma_f16_kernel(
             continue;
         const float l = accl[nb][0];
         const float inv = l > 0.f ? 1.f / l : 0.f;
-        f16 *dst = out + ((size_t)(a + row) * hq + h) * D + grp * 4;
+        f16 *dst = P.out + ((size_t)(a + row) * hq + h) * D + grp * 4;
 #pragma unroll
         for (int db = 0; db < 4; ++db) {
             const f16x4 o4 = {(f16)(acc[nb][db][0] * inv), (f16)(acc[nb][db][1] * inv), (f16)(acc[nb][db][2] * inv),
@@ -352,9 +434,9 @@ extern "C" kvp_status varlen_causal_prefill(const kvp_dims *dims, void *out, con
     hipStream_t st = (hipStream_t)stream;
     if (dims->dtype == KVP_F16) {
         dim3 grid(dims->num_q_heads, nseg, (max_seqlen + pf::QB - 1) / pf::QB);
-        hipLaunchKernelGGL(prefill_mfma_f16_kernel, grid, dim3(256), 0, st, (const f16 *)q,
-                           (const f16 *)k, (const f16 *)v, (f16 *)out, d_cu_seqlens,
-                           dims->num_q_heads, dims->num_kv_heads, sl2, causal);
+        PrefillArgs A{(const f16 *)q, (const f16 *)k, (const f16 *)v, (f16 *)out, d_cu_seqlens, nullptr, nullptr,
+                      0, 0, dims->num_q_heads, dims->num_kv_heads, sl2, causal};
+        hipLaunchKernelGGL(prefill_mfma_f16_kernel<false>, grid, dim3(256), 0, st, A);
     } else {
         dim3 grid(max_seqlen, dims->num_q_heads, nseg);
         hipLaunchKernelGGL(prefill_valu_f32_kernel, grid, dim3(64), 0, st, (const float *)q,
@@ -364,5 +446,53 @@ extern "C" kvp_status varlen_causal_prefill(const kvp_dims *dims, void *out, con
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return fail(KVP_ERR_HIP, "varlen_causal_prefill: launch failed: %s", hipGetErrorString(e));
+    return KVP_OK;
+}
+
+extern "C" kvp_status paged_prefill_attention(const kvp_cache_desc *cache, int32_t layer, void *out,
+                                              const void *q, const int32_t *d_block_table,
+                                              int32_t max_blocks, const int32_t *d_context_lens,
+                                              const int32_t *d_cu_q, int32_t B, int32_t max_q,
+                                              float scale, kvp_stream stream)
+{
+    const char *who = "paged_prefill_attention";
+    if (!cache)
+        return fail(KVP_ERR_INVALID, "%s: cache is NULL", who);
+    const kvp_dims &d = cache->dims;
+    if (d.num_layers <= 0 || d.num_q_heads <= 0 || d.num_kv_heads <= 0 || d.num_q_heads % d.num_kv_heads != 0)
+        return fail(KVP_ERR_INVALID, "%s: num_q_heads=%d, num_kv_heads=%d", who, d.num_q_heads, d.num_kv_heads);
+    if (d.head_dim != pf::D)
+        return fail(KVP_ERR_UNSUPPORTED, "%s: head_dim=%d (only 64)", who, d.head_dim);
+    if (d.dtype != KVP_F16)
+        return fail(KVP_ERR_UNSUPPORTED, "%s: dtype=%d (fp16 only)", who, d.dtype);
+    if (cache->block_size != pf::BS)
+        return fail(KVP_ERR_UNSUPPORTED, "%s: block_size=%d (only 16)", who, cache->block_size);
+    if (cache->num_blocks <= 0 || !cache->k_pool || !cache->v_pool ||
+        (((uintptr_t)cache->k_pool | (uintptr_t)cache->v_pool) & 15))
+        return fail(KVP_ERR_INVALID, "%s: empty or misaligned pool", who);
+    if (layer < 0 || layer >= d.num_layers)
+        return fail(KVP_ERR_INVALID, "%s: layer %d of %d", who, layer, d.num_layers);
+    if (B < 0 || max_q < 0 || max_blocks < 0)
+        return fail(KVP_ERR_INVALID, "%s: B=%d max_q=%d max_blocks=%d", who, B, max_q, max_blocks);
+    if (B == 0 || max_q == 0)
+        return KVP_OK;
+    if (!out || !q || !d_block_table || !d_context_lens || !d_cu_q || (((uintptr_t)out | (uintptr_t)q) & 15))
+        return fail(KVP_ERR_INVALID, "%s: NULL or misaligned pointer", who);
+    if (max_blocks > MAX_IDS)
+        return fail(KVP_ERR_UNSUPPORTED, "%s: max_blocks=%d (at most %d)", who, max_blocks, MAX_IDS);
+    if (B > 65535 || d.num_q_heads > 65535 || (max_q + pf::QB - 1) / pf::QB > 65535)
+        return fail(KVP_ERR_UNSUPPORTED, "%s: B, H_q or max_q too large", who);
+    if (scale == 0.f)
+        scale = 1.0f / sqrtf((float)pf::D);
+    const size_t layer_elems = (size_t)cache->num_blocks * d.num_kv_heads * pf::BS * pf::D;
+    PrefillArgs A{(const f16 *)q, (const f16 *)cache->k_pool + (size_t)layer * layer_elems,
+                  (const f16 *)cache->v_pool + (size_t)layer * layer_elems, (f16 *)out, d_cu_q, d_context_lens,
+                  d_block_table, max_blocks, cache->num_blocks, d.num_q_heads, d.num_kv_heads,
+                  scale * pf::LOG2E, 1};
+    dim3 grid(d.num_q_heads, B, (max_q + pf::QB - 1) / pf::QB);
+    hipLaunchKernelGGL(prefill_mfma_f16_kernel<true>, grid, dim3(256), 0, (hipStream_t)stream, A);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess)
+        return fail(KVP_ERR_HIP, "%s: launch failed: %s", who, hipGetErrorString(e));
     return KVP_OK;
 }
