@@ -232,6 +232,93 @@ def bench_prefill(args):
     print(json.dumps(line), flush=True)
 
 
+def chunk_flops(prefixes, chunks, hq, d):
+    """Algorithmic flops of new rows against a cache: row i of a chunk of m after a prefix
+    of C attends to C + i + 1 positions, 4 d flops per (row, position) per query head."""
+    pairs = sum(m * c + m * (m + 1) // 2 for c, m in zip(prefixes, chunks))
+    return 4 * d * hq * pairs
+
+
+def bench_chunked_prefill(args):
+    """Chunked prefill into a shared prefix: 16 requests forked from one 2048-token prompt
+    (copy-on-write blocks), each prefilling its own 512-token chunk against the paged cache;
+    the model's 14 query / 2 KV heads, fp16."""
+    import numpy as np
+    import torch
+
+    import kv_cache_decode_paged_amd as kvp
+    import workloads as W
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    B, prefix, chunk = 16, 2048, 512
+    nblocks = prefix // BLOCK + B * (chunk // BLOCK) + 64
+    pool = kvp.BlockPool(nblocks)
+    pool.set_free_order(W.free_list_permutation(nblocks, args.seed + 1).tolist())
+    cache = kvp.PagedKVCache(1, nblocks, HQ, HKV, torch.float16, "cuda")
+    cache.k_pool.copy_(W.randn_device(cache.k_pool.shape, args.seed + 10, torch.float16, "cuda"))
+    cache.v_pool.copy_(W.randn_device(cache.v_pool.shape, args.seed + 11, torch.float16, "cuda"))
+    base = pool.alloc(prefix)
+    seqs = []
+    for _ in range(B):
+        s = pool.fork(base)
+        pool.reserve(s, chunk)  # the chunk's K/V rows are the pool's seeded contents
+        seqs.append(s)
+    pool.free(base)
+    max_blocks = (prefix + chunk) // BLOCK
+    table, ctx = pool.export(seqs, max_blocks)
+    table, ctx = table.cuda(), ctx.cuda()
+    cu = torch.tensor([0] + [chunk * (b + 1) for b in range(B)], dtype=torch.int32).cuda()
+    q = W.randn_device((B * chunk, HQ, D), args.seed + 12, torch.float16, "cuda")
+    out = torch.empty_like(q)
+    call = lambda: kvp.paged_prefill_attention(cache, 0, q, table, ctx, cu, chunk, out=out)
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(args.steps):
+        call()
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / args.steps
+    flops = chunk_flops([prefix] * B, [chunk] * B, HQ, D)
+    tflops = flops / (ms * 1e-3) / 1e12
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        # the oracle on one of the 16 requests (all heads, the whole chunk)
+        K = torch.stack([cache.k_pool[0][table[0, j].item()] for j in range(max_blocks)]).permute(1, 0, 2, 3)
+        V = torch.stack([cache.v_pool[0][table[0, j].item()] for j in range(max_blocks)]).permute(1, 0, 2, 3)
+        K = K.reshape(HKV, -1, D)[None].double().cpu().numpy()
+        V = V.reshape(HKV, -1, D)[None].double().cpu().numpy()
+        t0 = time.perf_counter()
+        oracle.chunk_attention(q[:chunk].double().cpu().numpy(), K, V, np.array([prefix + chunk], np.int32),
+                               np.array([0, chunk], np.int32))
+        dt = time.perf_counter() - t0
+        cpu = {"value": round(chunk_flops([prefix], [chunk], HQ, D) / dt / 1e12, 6), "unit": "TFLOP/s",
+               "cores": 1, "kind": "oracle",
+               "sample": f"one of the {B} requests (its {chunk} rows x {HQ} heads after the {prefix}-token prefix), "
+                         "fp64 scalar C, 1 thread"}
+    print(f"[bench] chunked prefill {B} x {chunk} rows after a shared {prefix}-token prefix: {ms * 1e3:.1f} us per "
+          f"call, {tflops:.1f} TFLOP/s ({tflops / MFMA_F16_PEAK_TFLOPS * 100:.1f}% of the fp16 MFMA peak)",
+          file=sys.stderr, flush=True)
+    line = {
+        "metric": "chunked prefill against the paged cache TFLOP/s (% of MFMA fp16 peak)",
+        "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f16", "data": "synthetic",
+        "config": {"workload": f"{B} requests forked from one {prefix}-token prompt, {chunk}-token chunk each, "
+                               f"{HQ}q/{HKV}kv heads d64 fp16, 16-token blocks", "requests": B,
+                   "prefix": prefix, "chunk": chunk},
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 1), "peak": MFMA_F16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tflops / MFMA_F16_PEAK_TFLOPS, 4), "traffic": None,
+                     "kernel": "paged_prefill_attention (prefill_mfma_f16_kernel, paged keys)",
+                     "flops_per_launch": flops, "avg_launch_us": round(ms * 1e3, 3)},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -244,9 +331,10 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-share", action="store_true", help="plans without shared-prefix items")
     ap.add_argument("--seed", type=int, default=42)
-    ap.add_argument("--workload", choices=["decode", "prefill"], default="decode",
+    ap.add_argument("--workload", choices=["decode", "prefill", "chunked_prefill"], default="decode",
                     help="decode: the batch-200 paged decode step (default); prefill: packed causal "
-                         "prefill of 16 x 4096 tokens")
+                         "prefill of 16 x 4096 tokens; chunked_prefill: 16 x 512-token chunks after a "
+                         "shared 2048-token prefix in the paged cache")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -255,6 +343,9 @@ def main():
         sys.exit(2)
     if args.workload == "prefill":
         bench_prefill(args)
+        return
+    if args.workload == "chunked_prefill":
+        bench_chunked_prefill(args)
         return
 
     import numpy as np
