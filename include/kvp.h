@@ -274,6 +274,8 @@ typedef struct {
     int32_t num_blocks;   /* block ids in the plan are < num_blocks                  */
     int32_t n_items;      /* work items (one wave each)                              */
     int32_t n_shared;     /* of which read a shared prefix for several requests      */
+    int32_t head_dim;     /* head dim of the cache the plan is for (64 or 128)       */
+    int32_t reserved;     /* 0                                                       */
     int64_t n_slots;      /* partial slots the workspace must hold                   */
     int64_t bytes;        /* bytes of the plan image (device copy)                   */
     int64_t off_pair_base, off_pair_nparts, off_req_shared; /* offsets in the image  */

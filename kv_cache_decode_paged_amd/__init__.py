@@ -69,7 +69,7 @@ class kvp_pool_stats(ctypes.Structure):
 class kvp_decode_plan(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32), ("group", ctypes.c_int32),
                 ("num_blocks", ctypes.c_int32), ("n_items", ctypes.c_int32), ("n_shared", ctypes.c_int32),
-                ("n_slots", ctypes.c_int64), ("bytes", ctypes.c_int64), ("off_pair_base", ctypes.c_int64),
+                ("head_dim", ctypes.c_int32), ("reserved", ctypes.c_int32), ("n_slots", ctypes.c_int64), ("bytes", ctypes.c_int64), ("off_pair_base", ctypes.c_int64),
                 ("off_pair_nparts", ctypes.c_int64), ("off_req_shared", ctypes.c_int64),
                 ("kv_blocks_read", ctypes.c_int64)]
 
@@ -191,12 +191,12 @@ def dims(num_layers, num_q_heads, num_kv_heads, dtype, head_dim=HEAD_DIM):
 
 
 class PagedKVCache:
-    """K and V pools of shape [num_layers][num_blocks][H_kv][16][64] in device memory
-    (owned by the torch tensors held here)."""
+    """K and V pools of shape [num_layers][num_blocks][H_kv][16][head_dim] in device memory
+    (owned by the torch tensors held here); head_dim 64 or 128."""
 
     def __init__(self, num_layers, num_blocks, num_q_heads, num_kv_heads, dtype=torch.float16,
-                 device="cuda", k_pool=None, v_pool=None):
-        shape = (num_layers, num_blocks, num_kv_heads, BLOCK, HEAD_DIM)
+                 device="cuda", k_pool=None, v_pool=None, head_dim=HEAD_DIM):
+        shape = (num_layers, num_blocks, num_kv_heads, BLOCK, head_dim)
         self.k_pool = torch.empty(shape, dtype=dtype, device=device) if k_pool is None else k_pool
         self.v_pool = torch.empty(shape, dtype=dtype, device=device) if v_pool is None else v_pool
         for t, n in ((self.k_pool, "k_pool"), (self.v_pool, "v_pool")):
@@ -205,7 +205,8 @@ class PagedKVCache:
             _dev(t, n, dtype)
         self.num_layers, self.num_blocks = num_layers, num_blocks
         self.num_q_heads, self.num_kv_heads, self.dtype = num_q_heads, num_kv_heads, dtype
-        self.desc = kvp_cache_desc(dims(num_layers, num_q_heads, num_kv_heads, dtype), BLOCK,
+        self.head_dim = head_dim
+        self.desc = kvp_cache_desc(dims(num_layers, num_q_heads, num_kv_heads, dtype, head_dim), BLOCK,
                                    num_blocks, self.k_pool.data_ptr(), self.v_pool.data_ptr())
 
     @property
@@ -351,9 +352,9 @@ def kv_copy_blocks(cache: PagedKVCache, pairs, stream=None):
 
 
 def kv_append(cache: PagedKVCache, layer, k, v, slots, stream=None):
-    """k, v: device [n, H_kv, 64] in the cache dtype; slots: device int64 [n]."""
+    """k, v: device [n, H_kv, head_dim] in the cache dtype; slots: device int64 [n]."""
     n = k.shape[0]
-    if v.shape != k.shape or k.shape[1:] != (cache.num_kv_heads, HEAD_DIM) or slots.shape != (n,):
+    if v.shape != k.shape or k.shape[1:] != (cache.num_kv_heads, cache.head_dim) or slots.shape != (n,):
         raise ValueError("kv_append: shape mismatch")
     _check(_lib.kv_append(ctypes.byref(cache.desc), int(layer), _dev(k, "k", cache.dtype),
                           _dev(v, "v", cache.dtype), _dev(slots, "slots", torch.int64), n,
@@ -361,7 +362,7 @@ def kv_append(cache: PagedKVCache, layer, k, v, slots, stream=None):
 
 
 def contiguous_kv_append(k_cache, v_cache, k, v, pos, num_q_heads=None, stream=None):
-    """k_cache, v_cache: [B, H_kv, Lmax, 64]; k, v: [B, H_kv, 64]; pos: device int32 [B]."""
+    """k_cache, v_cache: [B, H_kv, Lmax, d]; k, v: [B, H_kv, d]; pos: device int32 [B]."""
     B, hkv, lmax, d = k_cache.shape
     if v_cache.shape != k_cache.shape or k.shape != (B, hkv, d) or v.shape != k.shape or pos.shape != (B,):
         raise ValueError("contiguous_kv_append: shape mismatch")
@@ -371,24 +372,24 @@ def contiguous_kv_append(k_cache, v_cache, k, v, pos, num_q_heads=None, stream=N
                                      _dev(pos, "pos", torch.int32), B, _stream(stream)))
 
 
-def decode_workspace_bytes(num_q_heads, num_kv_heads, dtype, B, max_context):
-    dm = dims(1, num_q_heads, num_kv_heads, dtype)
+def decode_workspace_bytes(num_q_heads, num_kv_heads, dtype, B, max_context, head_dim=HEAD_DIM):
+    dm = dims(1, num_q_heads, num_kv_heads, dtype, head_dim)
     return int(_lib.decode_workspace_bytes(ctypes.byref(dm), int(B), int(max_context)))
 
 
-def make_workspace(num_q_heads, num_kv_heads, dtype, B, max_context, device="cuda"):
+def make_workspace(num_q_heads, num_kv_heads, dtype, B, max_context, device="cuda", head_dim=HEAD_DIM):
     """Decode workspace, zero-filled as the C ABI requires before first use (torch's
     allocator returns 256-byte aligned blocks)."""
-    n = decode_workspace_bytes(num_q_heads, num_kv_heads, dtype, B, max_context)
+    n = decode_workspace_bytes(num_q_heads, num_kv_heads, dtype, B, max_context, head_dim)
     return torch.zeros((max(n, 256),), dtype=torch.uint8, device=device)
 
 
 def paged_decode_attention(cache: PagedKVCache, layer, q, block_table, context_lens, out=None,
                            scale=0.0, workspace=None, stream=None):
-    """q: device [B, H_q, 64]; block_table: device int32 [B, max_blocks]; context_lens:
-    device int32 [B].  Returns out [B, H_q, 64]."""
+    """q: device [B, H_q, d] (d = cache.head_dim); block_table: device int32 [B, max_blocks];
+    context_lens: device int32 [B].  Returns out [B, H_q, d]."""
     B, hq, d = q.shape
-    if hq != cache.num_q_heads or d != HEAD_DIM:
+    if hq != cache.num_q_heads or d != cache.head_dim:
         raise ValueError("paged_decode_attention: q shape does not match the cache")
     max_blocks = block_table.shape[1]
     if block_table.shape[0] != B or context_lens.shape != (B,):
@@ -396,7 +397,7 @@ def paged_decode_attention(cache: PagedKVCache, layer, q, block_table, context_l
     if out is None:
         out = torch.empty_like(q)
     if workspace is None:
-        workspace = make_workspace(hq, cache.num_kv_heads, cache.dtype, B, max_blocks * BLOCK, q.device)
+        workspace = make_workspace(hq, cache.num_kv_heads, cache.dtype, B, max_blocks * BLOCK, q.device, d)
     _check(_lib.paged_decode_attention(ctypes.byref(cache.desc), int(layer), _dev(out, "out", cache.dtype),
                                        _dev(q, "q", cache.dtype), _dev(block_table, "block_table", torch.int32),
                                        max_blocks, _dev(context_lens, "context_lens", torch.int32), B,
@@ -407,12 +408,12 @@ def paged_decode_attention(cache: PagedKVCache, layer, q, block_table, context_l
 
 def paged_decode_append_attention(cache: PagedKVCache, layer, q, k_new, v_new, block_table, context_lens,
                                   out=None, scale=0.0, workspace=None, stream=None):
-    """Fused step: k_new / v_new [B, H_kv, 64] go to position context_lens[b] - 1 of each
+    """Fused step: k_new / v_new [B, H_kv, d] go to position context_lens[b] - 1 of each
     request (through block_table) and the decode of q attends over them in the same call."""
     B, hq, d = q.shape
-    if hq != cache.num_q_heads or d != HEAD_DIM:
+    if hq != cache.num_q_heads or d != cache.head_dim:
         raise ValueError("paged_decode_append_attention: q shape does not match the cache")
-    if k_new.shape != (B, cache.num_kv_heads, HEAD_DIM) or v_new.shape != k_new.shape:
+    if k_new.shape != (B, cache.num_kv_heads, d) or v_new.shape != k_new.shape:
         raise ValueError("paged_decode_append_attention: k_new / v_new shape mismatch")
     max_blocks = block_table.shape[1]
     if block_table.shape[0] != B or context_lens.shape != (B,):
@@ -420,7 +421,7 @@ def paged_decode_append_attention(cache: PagedKVCache, layer, q, k_new, v_new, b
     if out is None:
         out = torch.empty_like(q)
     if workspace is None:
-        workspace = make_workspace(hq, cache.num_kv_heads, cache.dtype, B, max_blocks * BLOCK, q.device)
+        workspace = make_workspace(hq, cache.num_kv_heads, cache.dtype, B, max_blocks * BLOCK, q.device, d)
     _check(_lib.paged_decode_append_attention(ctypes.byref(cache.desc), int(layer), _dev(out, "out", cache.dtype),
                                               _dev(q, "q", cache.dtype), _dev(k_new, "k_new", cache.dtype),
                                               _dev(v_new, "v_new", cache.dtype),
@@ -430,8 +431,8 @@ def paged_decode_append_attention(cache: PagedKVCache, layer, q, k_new, v_new, b
     return out
 
 
-def decode_plan_bytes(num_q_heads, num_kv_heads, B, max_blocks, pad_items=0):
-    dm = dims(1, num_q_heads, num_kv_heads, torch.float16)
+def decode_plan_bytes(num_q_heads, num_kv_heads, B, max_blocks, pad_items=0, head_dim=HEAD_DIM):
+    dm = dims(1, num_q_heads, num_kv_heads, torch.float16, head_dim)
     return int(_lib.decode_plan_bytes(ctypes.byref(dm), int(B), int(max_blocks), int(pad_items)))
 
 
@@ -442,7 +443,7 @@ def _host_i32(t, name):
 
 
 def decode_plan_build(num_q_heads, num_kv_heads, block_table, context_lens, num_blocks, share_prefix=True,
-                      image=None, pin=False, pad_items=0, plan=None):
+                      image=None, pin=False, pad_items=0, plan=None, head_dim=HEAD_DIM):
     """Build a decode plan on the host from the HOST block table [B, max_blocks] and context
     lengths [B] (int32 CPU tensors).  Returns (plan, image): plan is a kvp_decode_plan, image
     a uint8 CPU tensor whose first plan.bytes bytes are to be copied to the device.
@@ -450,12 +451,12 @@ def decode_plan_build(num_q_heads, num_kv_heads, block_table, context_lens, num_
     B, max_blocks = block_table.shape
     if context_lens.shape != (B,):
         raise ValueError("decode_plan_build: context_lens shape mismatch")
-    need = decode_plan_bytes(num_q_heads, num_kv_heads, B, max_blocks, pad_items)
+    need = decode_plan_bytes(num_q_heads, num_kv_heads, B, max_blocks, pad_items, head_dim)
     if image is None:
         image = torch.empty((max(need, 16),), dtype=torch.uint8, pin_memory=pin)
     if image.device.type != "cpu" or image.dtype != torch.uint8:
         raise ValueError("decode_plan_build: image must be a uint8 host tensor")
-    dm = dims(1, num_q_heads, num_kv_heads, torch.float16)
+    dm = dims(1, num_q_heads, num_kv_heads, torch.float16, head_dim)
     plan = kvp_decode_plan() if plan is None else plan
     _check(_lib.decode_plan_build(ctypes.byref(dm), _host_i32(block_table, "block_table"), int(max_blocks),
                                   _host_i32(context_lens, "context_lens"), int(B), int(num_blocks),
@@ -481,13 +482,13 @@ def make_plan_workspace(plan, device="cuda"):
 def paged_decode_attention_planned(cache: PagedKVCache, layer, q, plan, d_plan, k_new=None, v_new=None,
                                    out=None, scale=0.0, workspace=None, stream=None):
     """Decode following a plan (decode_plan_build + upload_plan).  With k_new / v_new
-    ([B, H_kv, 64]) the step's token is appended in the same kernel."""
+    ([B, H_kv, d]) the step's token is appended in the same kernel."""
     B, hq, d = q.shape
-    if hq != cache.num_q_heads or d != HEAD_DIM or B != plan.B:
+    if hq != cache.num_q_heads or d != cache.head_dim or B != plan.B:
         raise ValueError("paged_decode_attention_planned: q shape does not match the cache / plan")
     if (k_new is None) != (v_new is None):
         raise ValueError("paged_decode_attention_planned: give both k_new and v_new or neither")
-    if k_new is not None and (k_new.shape != (B, cache.num_kv_heads, HEAD_DIM) or v_new.shape != k_new.shape):
+    if k_new is not None and (k_new.shape != (B, cache.num_kv_heads, d) or v_new.shape != k_new.shape):
         raise ValueError("paged_decode_attention_planned: k_new / v_new shape mismatch")
     if out is None:
         out = torch.empty_like(q)
@@ -505,11 +506,11 @@ def paged_decode_attention_planned(cache: PagedKVCache, layer, q, plan, d_plan, 
 def paged_prefill_attention(cache: PagedKVCache, layer, q, block_table, context_lens, cu_q, max_q, out=None,
                             scale=0.0, stream=None):
     """Several new rows per request against the paged cache (chunked prefill, draft
-    verification).  q: [T, H_q, 64] fp16 packed by cu_q (device int32 [B+1]); the rows of
+    verification).  q: [T, H_q, d] fp16 packed by cu_q (device int32 [B+1]); the rows of
     request b are the last cu_q[b+1]-cu_q[b] of its context_lens[b] positions, already
     appended to the cache; row i attends to positions 0 .. ctx - m + i."""
     T, hq, d = q.shape
-    if hq != cache.num_q_heads or d != HEAD_DIM:
+    if hq != cache.num_q_heads or d != cache.head_dim:
         raise ValueError("paged_prefill_attention: q shape does not match the cache")
     B = cu_q.numel() - 1
     if block_table.shape[0] != B or context_lens.shape != (B,):
@@ -534,7 +535,7 @@ def decode_merge_polls(polls=-1):
 
 def contiguous_decode_attention(q, k_cache, v_cache, context_lens, out=None, scale=0.0,
                                 workspace=None, stream=None):
-    """q: [B, H_q, 64]; k_cache, v_cache: [B, H_kv, Lmax, 64]; context_lens: int32 [B]."""
+    """q: [B, H_q, d]; k_cache, v_cache: [B, H_kv, Lmax, d]; context_lens: int32 [B]."""
     B, hq, d = q.shape
     Bk, hkv, lmax, dk = k_cache.shape
     if Bk != B or dk != d or v_cache.shape != k_cache.shape or context_lens.shape != (B,):
@@ -543,7 +544,7 @@ def contiguous_decode_attention(q, k_cache, v_cache, context_lens, out=None, sca
     if out is None:
         out = torch.empty_like(q)
     if workspace is None:
-        workspace = make_workspace(hq, hkv, q.dtype, B, lmax, q.device)
+        workspace = make_workspace(hq, hkv, q.dtype, B, lmax, q.device, d)
     _check(_lib.contiguous_decode_attention(ctypes.byref(dm), _dev(out, "out", q.dtype), _dev(q, "q"),
                                             _dev(k_cache, "k_cache", q.dtype), _dev(v_cache, "v_cache", q.dtype),
                                             lmax, _dev(context_lens, "context_lens", torch.int32), B,
@@ -554,7 +555,7 @@ def contiguous_decode_attention(q, k_cache, v_cache, context_lens, out=None, sca
 
 def varlen_causal_prefill(q, k, v, cu_seqlens, max_seqlen, causal=True, out=None, scale=0.0,
                           stream=None):
-    """q: [T, H_q, 64]; k, v: [T, H_kv, 64]; cu_seqlens: device int32 [nseg+1];
+    """q: [T, H_q, d]; k, v: [T, H_kv, d]; cu_seqlens: device int32 [nseg+1];
     max_seqlen: host int >= every segment length."""
     T, hq, d = q.shape
     hkv = k.shape[1]
@@ -574,7 +575,7 @@ def varlen_causal_prefill(q, k, v, cu_seqlens, max_seqlen, causal=True, out=None
 def kv_gather(cache: PagedKVCache, layer, block_table, context_lens, lmax, k_out=None, v_out=None,
               stream=None):
     B, max_blocks = block_table.shape
-    shape = (B, cache.num_kv_heads, lmax, HEAD_DIM)
+    shape = (B, cache.num_kv_heads, lmax, cache.head_dim)
     if k_out is None:
         k_out = torch.zeros(shape, dtype=cache.dtype, device=block_table.device)
     if v_out is None:

@@ -18,8 +18,9 @@ namespace kvp {
 
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int D = 64;
 constexpr int BS = 16;
+
+static bool head_dim_ok(int d) { return d == 64 || d == 128; }
 
 static kvp_status check_cache(const kvp_cache_desc *c, const char *who)
 {
@@ -30,8 +31,8 @@ static kvp_status check_cache(const kvp_cache_desc *c, const char *who)
         d.num_q_heads % d.num_kv_heads != 0)
         return fail(KVP_ERR_INVALID, "%s: bad dims (L=%d Hq=%d Hkv=%d)", who, d.num_layers,
                     d.num_q_heads, d.num_kv_heads);
-    if (d.head_dim != D)
-        return fail(KVP_ERR_UNSUPPORTED, "%s: head_dim=%d (only 64)", who, d.head_dim);
+    if (!head_dim_ok(d.head_dim))
+        return fail(KVP_ERR_UNSUPPORTED, "%s: head_dim=%d (64 or 128)", who, d.head_dim);
     if (d.dtype != KVP_F16 && d.dtype != KVP_F32)
         return fail(KVP_ERR_INVALID, "%s: dtype=%d", who, d.dtype);
     if (c->block_size != BS)
@@ -43,7 +44,8 @@ static kvp_status check_cache(const kvp_cache_desc *c, const char *who)
     return KVP_OK;
 }
 
-static inline int chunks_per_row(int dtype) { return D * (dtype == KVP_F16 ? 2 : 4) / 16; }
+// 16-byte chunks of one (token, head) row
+static inline int chunks_per_row(const kvp_dims &d) { return d.head_dim * (d.dtype == KVP_F16 ? 2 : 4) / 16; }
 
 static kvp_status launched(const char *who)
 {
@@ -168,7 +170,7 @@ kvp_status kv_append(const kvp_cache_desc *cache, int32_t layer, const void *k, 
         return KVP_OK;
     if (!k || !v || !d_slots || (((uintptr_t)k | (uintptr_t)v) & 15))
         return fail(KVP_ERR_INVALID, "kv_append: k/v/slots must be non-NULL, k/v 16-byte aligned");
-    const int nch = chunks_per_row(cache->dims.dtype);
+    const int nch = chunks_per_row(cache->dims);
     const int hkv = cache->dims.num_kv_heads;
     const int64_t layer_chunks = (int64_t)cache->num_blocks * hkv * BS * nch;
     i32x4 *kp = (i32x4 *)cache->k_pool + layer * layer_chunks;
@@ -197,7 +199,7 @@ kvp_status kv_copy_blocks(const kvp_cache_desc *cache, const int32_t *d_pairs, i
         return fail(KVP_ERR_INVALID, "kv_copy_blocks: pairs is NULL");
     if (n > 0x7fffffff / 1 || cache->dims.num_layers > 65535)
         return fail(KVP_ERR_UNSUPPORTED, "kv_copy_blocks: too many pairs or layers");
-    const int nch = chunks_per_row(cache->dims.dtype);
+    const int nch = chunks_per_row(cache->dims);
     const int64_t block_chunks = (int64_t)cache->dims.num_kv_heads * BS * nch;
     const int64_t layer_chunks = block_chunks * cache->num_blocks;
     hipLaunchKernelGGL(copy_blocks_kernel, dim3(n, cache->dims.num_layers, 2), dim3(256), 0,
@@ -224,7 +226,7 @@ kvp_status kv_gather(const kvp_cache_desc *cache, int32_t layer, const int32_t *
         return fail(KVP_ERR_INVALID, "kv_gather: NULL or misaligned pointer");
     if (B > 65535 || cache->dims.num_kv_heads > 65535)
         return fail(KVP_ERR_UNSUPPORTED, "kv_gather: B or H_kv too large");
-    const int nch = chunks_per_row(cache->dims.dtype);
+    const int nch = chunks_per_row(cache->dims);
     const int hkv = cache->dims.num_kv_heads;
     const int64_t layer_chunks = (int64_t)cache->num_blocks * hkv * BS * nch;
     dim3 grid((Lmax + BS - 1) / BS, hkv, B);
@@ -242,8 +244,8 @@ kvp_status contiguous_kv_append(const kvp_dims *dims, void *k_cache, void *v_cac
 {
     if (!dims)
         return fail(KVP_ERR_INVALID, "contiguous_kv_append: dims is NULL");
-    if (dims->head_dim != D)
-        return fail(KVP_ERR_UNSUPPORTED, "contiguous_kv_append: head_dim=%d", dims->head_dim);
+    if (!head_dim_ok(dims->head_dim))
+        return fail(KVP_ERR_UNSUPPORTED, "contiguous_kv_append: head_dim=%d (64 or 128)", dims->head_dim);
     if ((dims->dtype != KVP_F16 && dims->dtype != KVP_F32) || dims->num_kv_heads <= 0 || B < 0 ||
         Lmax <= 0)
         return fail(KVP_ERR_INVALID, "contiguous_kv_append: bad arguments");
@@ -252,7 +254,7 @@ kvp_status contiguous_kv_append(const kvp_dims *dims, void *k_cache, void *v_cac
     if (!k_cache || !v_cache || !k || !v || !d_pos ||
         (((uintptr_t)k_cache | (uintptr_t)v_cache | (uintptr_t)k | (uintptr_t)v) & 15))
         return fail(KVP_ERR_INVALID, "contiguous_kv_append: NULL or misaligned pointer");
-    const int nch = chunks_per_row(dims->dtype);
+    const int nch = chunks_per_row(*dims);
     const int total = B * dims->num_kv_heads * nch;
     hipLaunchKernelGGL(contig_append_kernel, dim3((total + 255) / 256), dim3(256), 0,
                        (hipStream_t)stream, (i32x4 *)k_cache, (i32x4 *)v_cache, (const i32x4 *)k,

@@ -26,10 +26,10 @@ static kvp_status check_dims(const kvp_dims *d, const char *who)
     if (d->num_q_heads <= 0 || d->num_kv_heads <= 0 || d->num_q_heads % d->num_kv_heads != 0)
         return fail(KVP_ERR_INVALID, "%s: num_q_heads=%d must be a positive multiple of num_kv_heads=%d",
                     who, d->num_q_heads, d->num_kv_heads);
-    if (d->head_dim != D)
-        return fail(KVP_ERR_UNSUPPORTED, "%s: head_dim=%d (only 64 is implemented)", who, d->head_dim);
     if (d->dtype != KVP_F16 && d->dtype != KVP_F32)
         return fail(KVP_ERR_INVALID, "%s: dtype=%d", who, d->dtype);
+    if (d->head_dim != D && !(d->dtype == KVP_F16 && d->head_dim == 128))
+        return fail(KVP_ERR_UNSUPPORTED, "%s: head_dim=%d (64, or 128 for fp16)", who, d->head_dim);
     const int group = d->num_q_heads / d->num_kv_heads;
     if (group > MAXG)
         return fail(KVP_ERR_UNSUPPORTED, "%s: %d query heads per KV head (1..%d supported)", who, group, MAXG);
@@ -42,7 +42,7 @@ static size_t part_bytes(const kvp_dims *d, int B, int max_context)
 {
     if (d->dtype == KVP_F16) {
         const int ipp = decode_f16_items_per_pair(max_context);
-        return ipp > 1 ? decode_f16_part_bytes((long long)B * d->num_kv_heads * ipp) : 0;
+        return ipp > 1 ? decode_f16_part_bytes((long long)B * d->num_kv_heads * ipp, d->head_dim) : 0;
     }
     const int ms = decode_f32_max_splits(max_context);
     return ms > 1 ? decode_f32_part_bytes(B, d->num_q_heads, ms) : 0;
@@ -95,8 +95,9 @@ static kvp_status decode_common(const kvp_dims *dims, void *out, const void *q, 
     P.B = B;
     P.hq = dims->num_q_heads;
     P.hkv = dims->num_kv_heads;
+    P.dim = dims->head_dim;
     if (scale == 0.f)
-        scale = 1.0f / sqrtf((float)D);
+        scale = 1.0f / sqrtf((float)P.dim);
     P.scale_log2 = scale * LOG2E;
     P.part = nullptr;
     P.tickets = nullptr;
@@ -141,10 +142,10 @@ static kvp_status paged_common(const kvp_cache_desc *cache, int32_t layer, void 
     if ((long long)max_blocks * BS > 0x7fffffffLL)
         return fail(KVP_ERR_UNSUPPORTED, "%s: max_blocks too large", who);
     const size_t esz = cache->dims.dtype == KVP_F16 ? 2 : 4;
-    const size_t layer_elems = (size_t)cache->num_blocks * cache->dims.num_kv_heads * BS * D;
+    const size_t layer_elems = (size_t)cache->num_blocks * cache->dims.num_kv_heads * BS * cache->dims.head_dim;
     const char *kc = (const char *)cache->k_pool + (size_t)layer * layer_elems * esz;
     const char *vc = (const char *)cache->v_pool + (size_t)layer * layer_elems * esz;
-    PagedAddr A{d_block_table, max_blocks, cache->dims.num_kv_heads, cache->num_blocks};
+    PagedAddr A{d_block_table, max_blocks, cache->dims.num_kv_heads, cache->num_blocks, cache->dims.head_dim};
     return decode_common(&cache->dims, out, q, kc, vc, k_new, v_new, A, max_blocks * BS,
                          d_context_lens, B, scale, workspace, ws_bytes, stream, who);
 }
@@ -153,7 +154,7 @@ static size_t plan_workspace_bytes(const kvp_decode_plan *plan)
 {
     if (plan->n_slots <= 0)
         return 0;
-    return ticket_bytes(plan->B, plan->num_kv_heads) + decode_f16_part_bytes(plan->n_slots);
+    return ticket_bytes(plan->B, plan->num_kv_heads) + decode_f16_part_bytes(plan->n_slots, plan->head_dim);
 }
 
 } // namespace kvp
@@ -224,11 +225,12 @@ kvp_status paged_decode_attention_planned(const kvp_cache_desc *cache, int32_t l
     if (layer < 0 || layer >= cache->dims.num_layers)
         return fail(KVP_ERR_INVALID, "%s: layer %d out of range", who, layer);
     const int hkv = cache->dims.num_kv_heads, group = cache->dims.num_q_heads / hkv;
-    if (plan->num_kv_heads != hkv || plan->group != group || plan->B < 0 || plan->n_items < 0 ||
-        plan->num_blocks <= 0 || plan->num_blocks > cache->num_blocks)
-        return fail(KVP_ERR_INVALID, "%s: plan (Hkv=%d group=%d num_blocks=%d) does not fit the cache "
-                    "(Hkv=%d group=%d num_blocks=%d)", who, plan->num_kv_heads, plan->group,
-                    plan->num_blocks, hkv, group, cache->num_blocks);
+    const int dim = cache->dims.head_dim;
+    if (plan->num_kv_heads != hkv || plan->group != group || plan->head_dim != dim || plan->B < 0 ||
+        plan->n_items < 0 || plan->num_blocks <= 0 || plan->num_blocks > cache->num_blocks)
+        return fail(KVP_ERR_INVALID, "%s: plan (Hkv=%d group=%d d=%d num_blocks=%d) does not fit the cache "
+                    "(Hkv=%d group=%d d=%d num_blocks=%d)", who, plan->num_kv_heads, plan->group,
+                    plan->head_dim, plan->num_blocks, hkv, group, dim, cache->num_blocks);
     if (plan->B == 0 || plan->n_items == 0)
         return KVP_OK;
     if (!out || !q || !d_plan || !cache->k_pool || !cache->v_pool)
@@ -244,7 +246,7 @@ kvp_status paged_decode_attention_planned(const kvp_cache_desc *cache, int32_t l
         if ((uintptr_t)workspace & 255)
             return fail(KVP_ERR_INVALID, "%s: workspace must be 256-byte aligned", who);
     }
-    const size_t layer_elems = (size_t)cache->num_blocks * hkv * BS * D;
+    const size_t layer_elems = (size_t)cache->num_blocks * hkv * BS * dim;
     DecodeParams P;
     P.q = q;
     P.out = out;
@@ -258,15 +260,16 @@ kvp_status paged_decode_attention_planned(const kvp_cache_desc *cache, int32_t l
     P.B = plan->B;
     P.hq = cache->dims.num_q_heads;
     P.hkv = hkv;
+    P.dim = dim;
     if (scale == 0.f)
-        scale = 1.0f / sqrtf((float)D);
+        scale = 1.0f / sqrtf((float)dim);
     P.scale_log2 = scale * LOG2E;
     P.workers = 0;
     P.merge_polls = g_merge_polls.load(std::memory_order_relaxed);
     // tickets first: the layout does not depend on the plan's slot count
     P.tickets = need > 0 ? (int *)workspace : nullptr;
     P.part = need > 0 ? (float *)((char *)workspace + ticket_bytes(plan->B, hkv)) : nullptr;
-    PagedAddr A{nullptr, 0, hkv, plan->num_blocks};
+    PagedAddr A{nullptr, 0, hkv, plan->num_blocks, dim};
     return launch_decode_f16_planned(P, A, group, d_plan, *plan, (hipStream_t)stream);
 }
 
@@ -280,7 +283,7 @@ kvp_status contiguous_decode_attention(const kvp_dims *dims, void *out, const vo
         return st0;
     if (Lmax <= 0)
         return fail(KVP_ERR_INVALID, "contiguous_decode_attention: Lmax=%d", Lmax);
-    ContigAddr A{dims->num_kv_heads, Lmax};
+    ContigAddr A{dims->num_kv_heads, Lmax, dims->head_dim};
     return decode_common(dims, out, q, k_cache, v_cache, nullptr, nullptr, A, Lmax, d_context_lens,
                          B, scale, workspace, ws_bytes, stream, "contiguous_decode_attention");
 }

@@ -16,7 +16,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 
 namespace dec {
-constexpr int D = 64;    // head dim
+constexpr int D = 64;    // head dim of the fp32 kernel (fp16: 64 or 128, a template argument)
 constexpr int BS = 16;   // tokens per block
 constexpr int TILE = 64; // tokens per tile (4 blocks)
 constexpr int MAXG = 8;  // query heads per group handled by one wave
@@ -31,6 +31,7 @@ struct PagedAddr {
     int max_blocks;
     int hkv;
     int num_blocks;
+    int dim;          // head dim
     static constexpr bool paged = true;
     __device__ int entry(int b, int idx) const
     {
@@ -41,30 +42,31 @@ struct PagedAddr {
     // table entry e)
     __device__ size_t block_off(int, int g, int, int e) const
     {
-        return ((size_t)e * hkv + g) * (dec::BS * dec::D);
+        return ((size_t)e * hkv + g) * (dec::BS * dim);
     }
     __device__ int max_ctx() const { return max_blocks * dec::BS; }
     // row to read for in-block row r (blocks always hold 16 rows)
     __device__ int row(int, int r) const { return r; }
     // a block that is always readable (block 0 of KV head g), for rows that are masked
-    __device__ size_t safe_off(int, int g) const { return (size_t)g * (dec::BS * dec::D); }
+    __device__ size_t safe_off(int, int g) const { return (size_t)g * (dec::BS * dim); }
     __device__ int safe_row(int r) const { return r; }
 };
 
 struct ContigAddr {
     int hkv;
     int lmax;
+    int dim;          // head dim
     static constexpr bool paged = false;
     __device__ int entry(int, int) const { return 0; }
     __device__ bool valid(int) const { return true; }
     __device__ size_t block_off(int b, int g, int idx, int) const
     {
-        return (((size_t)b * hkv + g) * lmax + (size_t)idx * dec::BS) * dec::D;
+        return (((size_t)b * hkv + g) * lmax + (size_t)idx * dec::BS) * dim;
     }
     __device__ int max_ctx() const { return lmax; }
     // the last 16-row group of a slice may run past Lmax: clamp (such rows are masked)
     __device__ int row(int idx, int r) const { return min(idx * dec::BS + r, lmax - 1) - idx * dec::BS; }
-    __device__ size_t safe_off(int b, int g) const { return ((size_t)b * hkv + g) * lmax * dec::D; }
+    __device__ size_t safe_off(int b, int g) const { return ((size_t)b * hkv + g) * lmax * dim; }
     __device__ int safe_row(int r) const { return min(r, lmax - 1); }
 };
 
@@ -148,18 +150,19 @@ __device__ inline void reset_ticket(int *t)
 // parameters
 // ---------------------------------------------------------------------------------------
 struct DecodeParams {
-    const void *q;     // [B][Hq][D]
-    void *out;         // [B][Hq][D]
+    const void *q;     // [B][Hq][dim]
+    void *out;         // [B][Hq][dim]
     const void *kc;    // layer base of the K pool / cache
     const void *vc;
     void *kc_w;        // same as kc, writable (fused append)
     void *vc_w;
-    const void *k_new; // [B][Hkv][D] or NULL: new token written at position ctx-1
+    const void *k_new; // [B][Hkv][dim] or NULL: new token written at position ctx-1
     const void *v_new;
     const int *ctx_lens;
     int B;
     int hq;
     int hkv;
+    int dim;           // head dim: 64 (fp32, fp16) or 128 (fp16)
     float scale_log2;
     int workers;       // fp32: max splits per pair
     float *part;       // partial results
@@ -179,7 +182,7 @@ kvp_status launch_decode_f32(const DecodeParams &P, const PagedAddr &A, int grou
 kvp_status launch_decode_f32(const DecodeParams &P, const ContigAddr &A, int group, hipStream_t st);
 
 // workspace layout helpers (bytes), shared by the launchers and the size queries
-size_t decode_f16_part_bytes(long long slots);
+size_t decode_f16_part_bytes(long long slots, int dim);
 int decode_f16_items_per_pair(int max_context);
 size_t decode_f32_part_bytes(int B, int hq, int max_splits);
 int decode_f32_max_splits(int max_context);

@@ -18,7 +18,7 @@
 //   e^(block max - global max) -- used across tiles and across split partitions.
 //
 // Work decomposition: one wave per work item.  An item is up to 32 consecutive 16-token
-// blocks (8 tiles of 64 tokens) of one KV head, either of one request ("private") or of a
+// blocks (8 tiles of 64 tokens at head dim 64, 16 tiles of 32 tokens at 128) of one KV head, either of one request ("private") or of a
 // few requests that share those physical blocks ("shared": the query rows of every member,
 // up to 16 rows, are scored against the same K/V tile).  The planner puts all shared items
 // of one prefix on one XCD, so the prefix is fetched from HBM about once per step and
@@ -30,7 +30,7 @@
 // through 16-byte device-coherent stores and loads, ordered by a store-completion wait.
 //
 // Per wave: K and V tiles stream HBM -> LDS through global_load_lds_dwordx4 into a ring of
-// NBUF slots (16 KB per tile, 16 loads); waits are explicit vmcnt counts.
+// NBUF slots (16 KB of K and V per tile, 16 loads); waits are explicit vmcnt counts.
 //   scores  S^T = K Q^T       v_mfma_f32_16x16x32_f16, K rows from LDS (chunk-swizzled),
 //                             query rows as one 16-column block
 //   softmax fp32, hardware exp2 of one FMA (scale folded in), reference max moved only
@@ -52,9 +52,12 @@ namespace kvp {
 using namespace dec;
 using namespace plan;
 
-constexpr int PART_FLOATS = D + 4; // o[64], m, l, 2 floats of padding (16-byte records)
-// tile length (tokens) and ring depth of the decode kernel: 64-token tiles in a 2-slot ring
-// take 32 KB of LDS per wave, which leaves room for four waves per CU
+// floats of one partial record of a head of dimension HD: o[HD], m, l and 2 of padding
+// (16-byte records)
+constexpr int part_floats(int HD) { return HD + 4; }
+// tile length (tokens) and ring depth of the decode kernel at head dim 64: 64-token tiles in
+// a 2-slot ring take 32 KB of LDS per wave, which leaves room for four waves per CU (head
+// dim 128 takes 32-token tiles, the same 32 KB)
 #ifndef DEC_TT
 #define DEC_TT 64
 #endif
@@ -117,29 +120,31 @@ __device__ inline float2 coherent_load2_async(const float *p)
 // Merge, for this lane's column, the np partials of its pair (slots pbase .. pbase+np-1) in
 // slot order; the partial of slot own is this lane's registers (om, ol, oacc), the others are
 // read from memory.  Lane (col, grp) holds output dims 16 db + 4 grp + i as O[4 db + i].
-// Writes the normalised row to outp (this column's 64 outputs).
+// Writes the normalised row to outp (this column's HD outputs).
+template <int HD>
 __device__ __forceinline__ void merge_column(const float *part, int pbase, int np, int own, int hd, int grp,
-                                             float om, float ol, const f32x4 (&oacc)[4], f16 *outp)
+                                             float om, float ol, const f32x4 (&oacc)[HD / 16], f16 *outp)
 {
-    float M = -INFINITY, L = 0.f, O[16];
+    constexpr int NDB = HD / 16;
+    float M = -INFINITY, L = 0.f, O[4 * NDB];
 #pragma unroll
-    for (int k = 0; k < 16; ++k)
+    for (int k = 0; k < 4 * NDB; ++k)
         O[k] = 0.f;
     for (int j0 = 0; j0 < np; j0 += 4) {
-        f32x4 ov[4][4];
+        f32x4 ov[4][NDB];
         float2 ml[4];
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) {
             const int j = j0 + jj;
             if (j < np && j != own) {
-                const float *src = part + ((size_t)(pbase + j) * MAXG + hd) * PART_FLOATS;
+                const float *src = part + ((size_t)(pbase + j) * MAXG + hd) * part_floats(HD);
 #pragma unroll
-                for (int db = 0; db < 4; ++db)
+                for (int db = 0; db < NDB; ++db)
                     ov[jj][db] = coherent_load4_async(src + 16 * db + 4 * grp);
-                ml[jj] = coherent_load2_async(src + D);
+                ml[jj] = coherent_load2_async(src + HD);
             } else {
 #pragma unroll
-                for (int db = 0; db < 4; ++db)
+                for (int db = 0; db < NDB; ++db)
                     ov[jj][db] = oacc[db];
                 ml[jj] = float2{om, ol};
             }
@@ -148,22 +153,22 @@ __device__ __forceinline__ void merge_column(const float *part, int pbase, int n
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) {
 #pragma unroll
-            for (int db = 0; db < 4; ++db)
+            for (int db = 0; db < NDB; ++db)
                 asm volatile("" : "+v"(ov[jj][db]));
             asm volatile("" : "+v"(ml[jj]));
             if (j0 + jj < np) {
-                float o[16];
+                float o[4 * NDB];
 #pragma unroll
-                for (int db = 0; db < 4; ++db)
+                for (int db = 0; db < NDB; ++db)
 #pragma unroll
                     for (int i = 0; i < 4; ++i)
                         o[4 * db + i] = ov[jj][db][i];
-                merge_step(M, L, O, 16, ml[jj].x, ml[jj].y, o);
+                merge_step(M, L, O, 4 * NDB, ml[jj].x, ml[jj].y, o);
             }
         }
     }
 #pragma unroll
-    for (int db = 0; db < 4; ++db) {
+    for (int db = 0; db < NDB; ++db) {
         f16x4 o;
 #pragma unroll
         for (int i = 0; i < 4; ++i)
@@ -174,19 +179,26 @@ __device__ __forceinline__ void merge_column(const float *part, int pbase, int n
 
 // One work item.  rv: lane R_ENT + j holds the physical id of the item's block j.
 //
-// Tile t = 64 tokens = blocks 4t .. 4t+3 of the item.  Lane (col, grp) = (lane % 16,
+// Tile t = TT tokens = blocks (TT / 16) t .. of the item.  Lane (col, grp) = (lane % 16,
 // lane / 16).  MFMA column col is query row col of the item (member col / G, head col % G).
-// K and V tiles sit in LDS as 64 rows of 128 bytes; 16-byte chunk c of row r is stored at
-// chunk slot c ^ (r & 7).
-template <int G, bool SHARED, int NBUF, int TT, typename Addr>
+// K and V tiles sit in LDS as TT rows of 2 HD bytes; 16-byte chunk c of row r is stored at
+// chunk slot swz<HD>(c, r).
+template <int G, bool SHARED, int NBUF, int TT, int HD, typename Addr>
 __device__ __forceinline__ void run_item(const DecodeParams &P, const Addr &A, const PlanView &PV,
                                          const Item &it, int rv, char *kring, char *vring)
 {
     static_assert(TT == 32 || TT == 64, "tiles of 32 or 64 tokens");
-    constexpr int KB = TT / BS;    // blocks per tile
-    constexpr int KS = TT / 32;    // k-steps of 32 tokens per tile (value product)
-    constexpr int NDMA = 2 * KB * 2; // 1 KB loads per tile: two per block for K and for V
-    constexpr int SLOT = TT * 128; // bytes of one K (or V) tile
+    static_assert(HD == 64 || HD == 128, "head dimension 64 or 128");
+    constexpr int KB = TT / BS;      // blocks per tile
+    constexpr int KS = TT / 32;      // k-steps of 32 tokens per tile (value product)
+    constexpr int RB = 2 * HD;       // bytes of one K (or V) row
+    constexpr int CPR = HD / 8;      // 16-byte chunks per row
+    constexpr int RPI = 1024 / RB;   // rows per 1 KB DMA load
+    constexpr int IPB = BS / RPI;    // 1 KB loads per block and tensor
+    constexpr int KD = HD / 32;      // k-steps of 32 dims (score product)
+    constexpr int NDB = HD / 16;     // 16-dim blocks (value product)
+    constexpr int NDMA = 2 * KB * IPB; // 1 KB loads per tile, K and V
+    constexpr int SLOT = TT * RB;    // bytes of one K (or V) tile
     const int lane = threadIdx.x;
     const int col = lane & 15, grp = lane >> 4;
     const int hkv = P.hkv;
@@ -198,14 +210,15 @@ __device__ __forceinline__ void run_item(const DecodeParams &P, const Addr &A, c
     const int mem = col / G, hd = col - mem * G;
     const bool cv = mem < it.nmem;
     const int bm = it.b + (cv ? mem : 0);
-    f16x8 qop[2];
+    f16x8 qop[KD];
     {
-        const f16 *qp = (const f16 *)P.q + ((size_t)bm * P.hq + (size_t)it.g * G + hd) * D + grp * 8;
-        const f16x8 q0 = *(const f16x8 *)qp;
-        const f16x8 q1 = *(const f16x8 *)(qp + 32);
+        const f16 *qp = (const f16 *)P.q + ((size_t)bm * P.hq + (size_t)it.g * G + hd) * HD + grp * 8;
         const f16x8 z = {0, 0, 0, 0, 0, 0, 0, 0};
-        qop[0] = cv ? q0 : z;
-        qop[1] = cv ? q1 : z;
+#pragma unroll
+        for (int ks = 0; ks < KD; ++ks) {
+            const f16x8 qv = *(const f16x8 *)(qp + 32 * ks);
+            qop[ks] = cv ? qv : z;
+        }
     }
     // lim: tokens >= lim are masked for this row; rows whose results are not kept (padding
     // columns, members that do not take part) have no limit -- their columns of the MFMA
@@ -234,15 +247,15 @@ __device__ __forceinline__ void run_item(const DecodeParams &P, const Addr &A, c
             full_end = min(full_end, lane_int(lim, m * G));
     }
 
-    // the step's new K / V row (lanes 0-7: K chunks, 8-15: V chunks)
+    // the step's new K / V row (lanes 0 .. CPR-1: K chunks, CPR .. 2 CPR-1: V chunks)
     const bool app = !SHARED && P.k_new != nullptr;
     i32x4 nrow = {0, 0, 0, 0};
-    if (app && lane < 16) {
+    if (app && lane < 2 * CPR) {
         // K or V row by lane, as masked arithmetic (a select of the two pointers is turned
         // into a table in scratch memory)
         const uintptr_t kb = (uintptr_t)P.k_new, vb = (uintptr_t)P.v_new;
-        const uintptr_t base = kb + ((vb - kb) & (uintptr_t)(-(intptr_t)(lane >= 8)));
-        const size_t off = (((size_t)it.b * hkv + it.g) * D + (lane & 7) * 8) * sizeof(f16);
+        const uintptr_t base = kb + ((vb - kb) & (uintptr_t)(-(intptr_t)(lane >= CPR)));
+        const size_t off = (((size_t)it.b * hkv + it.g) * HD + (lane & (CPR - 1)) * 8) * sizeof(f16);
         nrow = *(const __attribute__((address_space(1))) i32x4 *)(base + off);
     }
 
@@ -250,8 +263,8 @@ __device__ __forceinline__ void run_item(const DecodeParams &P, const Addr &A, c
     auto ent = [&](int j) -> int { return lane_int(rv, R_ENT + min(j, BPI - 1)); };
     auto block_ok = [&](int j) -> bool { return (j < it.nblk) & A.valid(ent(j)); };
 
-    // ---- DMA of tile t into ring slot t % NBUF: per block, rows 0-7 then 8-15 of K and V
-    // (lane: row 8 h + lane / 8, chunk lane % 8 of the LDS row) ----
+    // ---- DMA of tile t into ring slot t % NBUF: per block, IPB loads of RPI rows of K and V
+    // (lane: row RPI h + lane / CPR, chunk lane % CPR of the LDS row) ----
     auto issue = [&](int t) {
         char *kd = kring + (t % NBUF) * SLOT;
         char *vd = vring + (t % NBUF) * SLOT;
@@ -263,11 +276,11 @@ __device__ __forceinline__ void run_item(const DecodeParams &P, const Addr &A, c
             const int lb = it.blk0 + j;
             const size_t base = ok ? A.block_off(it.b, it.g, lb, e) : A.safe_off(it.b, it.g);
 #pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                const int r = 8 * h + (lane >> 3);
+            for (int h = 0; h < IPB; ++h) {
+                const int r = RPI * h + lane / CPR;
                 const int sr = ok ? A.row(lb, r) : A.safe_row(r);
-                const size_t off = base + (size_t)sr * D + (((lane & 7) ^ (r & 7)) * 8);
-                const int i = 2 * kb + h;
+                const size_t off = base + (size_t)sr * HD + swz<HD>(lane & (CPR - 1), r) * 8;
+                const int i = IPB * kb + h;
                 __builtin_amdgcn_global_load_lds((const void *)(kc + off),
                                                  (__attribute__((address_space(3))) void *)(kd + i * 1024),
                                                  16, 0, 0);
@@ -281,9 +294,9 @@ __device__ __forceinline__ void run_item(const DecodeParams &P, const Addr &A, c
     // running state of this lane's column: reference max (scaled, log2 units), output
     // O^T rows 16 db + 4 grp + i, and the row sum (every entry of accl holds it)
     float mref = -INFINITY;
-    f32x4 acc[4], accl = {0.f, 0.f, 0.f, 0.f};
+    f32x4 acc[NDB], accl = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int db = 0; db < 4; ++db)
+    for (int db = 0; db < NDB; ++db)
         acc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
     const f16x8 ones = {1, 1, 1, 1, 1, 1, 1, 1};
 
@@ -302,8 +315,8 @@ __device__ __forceinline__ void run_item(const DecodeParams &P, const Addr &A, c
         // value rows that no column may use: zero them (the cache can hold NaN there)
         if (!full) {
 #pragma unroll
-            for (int k = 0; k < TT / 8; ++k) {
-                const int ch = lane + 64 * k, r = ch >> 3;
+            for (int k = 0; k < TT * CPR / 64; ++k) {
+                const int ch = lane + 64 * k, r = ch / CPR;
                 const int kb = r >> 4;
                 bool okb = bok[0];
 #pragma unroll
@@ -319,26 +332,27 @@ __device__ __forceinline__ void run_item(const DecodeParams &P, const Addr &A, c
             if (r >= 0 && r < TT) {
                 const int j = KB * t + (r >> 4);
                 const int e = ent(j);
-                if (lane < 16 && j < it.nblk && A.valid(e)) {
-                    const int ch = lane & 7;
+                if (lane < 2 * CPR && j < it.nblk && A.valid(e)) {
+                    const int ch = lane & (CPR - 1);
                     const int lb = it.blk0 + j;
-                    const size_t dst = A.block_off(it.b, it.g, lb, e) + (size_t)A.row(lb, r & 15) * D + ch * 8;
-                    lds_store_b128((lane < 8 ? kt : vt) + r * 128 + ((ch ^ (r & 7)) * 16), nrow);
+                    const size_t dst = A.block_off(it.b, it.g, lb, e) + (size_t)A.row(lb, r & 15) * HD + ch * 8;
+                    lds_store_b128((lane < CPR ? kt : vt) + r * RB + swz<HD>(ch, r) * 16, nrow);
                     const uintptr_t kb = (uintptr_t)P.kc_w, vb = (uintptr_t)P.vc_w;
-                    const uintptr_t base = kb + ((vb - kb) & (uintptr_t)(-(intptr_t)(lane >= 8)));
+                    const uintptr_t base = kb + ((vb - kb) & (uintptr_t)(-(intptr_t)(lane >= CPR)));
                     *(__attribute__((address_space(1))) i32x4 *)(base + dst * sizeof(f16)) = nrow;
                 }
             }
         }
         wave_lds_sync();
 
-        // K rows (A of the score MFMA): row 16 kb + col, dims 8 grp .. and 32 + 8 grp ..
-        f16x8 kop[KB][2];
+        // K rows (A of the score MFMA): row 16 kb + col, dims 32 ks + 8 grp .. (chunk 4 ks + grp)
+        f16x8 kop[KB][KD];
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
             const int r = kb * 16 + col;
-            kop[kb][0] = lds_b128(kt + r * 128 + ((grp ^ (r & 7)) * 16));
-            kop[kb][1] = lds_b128(kt + r * 128 + (((4 + grp) ^ (r & 7)) * 16));
+#pragma unroll
+            for (int ks = 0; ks < KD; ++ks)
+                kop[kb][ks] = lds_b128(kt + r * RB + swz<HD>(4 * ks + grp, r) * 16);
         }
         // V^T (A of the value MFMA) of k-step ks and dims 16 db ..: lane (col, grp) needs
         // V[token][16 db + col] for its k-slots s, token 16 (2 ks + s / 4) + 4 grp + s % 4.
@@ -346,36 +360,40 @@ __device__ __forceinline__ void run_item(const DecodeParams &P, const Addr &A, c
         // addressed by lane 4 j + i / 4 as its element j; so lane L of the group addresses
         // token row 16 (2 ks + h) + 4 grp + L / 4, dims 16 db + 4 (L % 4) .. + 3, and the two
         // reads h = 0, 1 give slots 0-3 and 4-7.
-        f16x4 vraw[KS][4][2];
+        f16x4 vraw[KS][NDB][2];
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-            for (int db = 0; db < 4; ++db)
+            for (int db = 0; db < NDB; ++db)
 #pragma unroll
                 for (int h = 0; h < 2; ++h) {
                     const int row = 16 * (2 * ks + h) + 4 * grp + (col >> 2);
                     const int ch = 2 * db + ((col & 3) >> 1);
-                    vraw[ks][db][h] = lds_tr16_b64(vt + row * 128 + ((ch ^ (row & 7)) * 16) + (col & 1) * 8);
+                    vraw[ks][db][h] = lds_tr16_b64(vt + row * RB + swz<HD>(ch, row) * 16 + (col & 1) * 8);
                 }
         // every read has returned before any result is used (the empty statements tie each
         // result to the wait)
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb)
-            asm volatile("" : "+v"(kop[kb][0]), "+v"(kop[kb][1]));
+#pragma unroll
+            for (int ks = 0; ks < KD; ++ks)
+                asm volatile("" : "+v"(kop[kb][ks]));
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-            for (int db = 0; db < 4; ++db)
+            for (int db = 0; db < NDB; ++db)
                 asm volatile("" : "+v"(vraw[ks][db][0]), "+v"(vraw[ks][db][1]));
 
         // scores: sacc[kb][i] = S[token 16 kb + 4 grp + i][column col] (unscaled)
         f32x4 sacc[KB];
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
-            const f32x4 s0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop[kb][0], qop[0],
-                                                                    f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-            sacc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop[kb][1], qop[1], s0, 0, 0, 0);
+            f32x4 s = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop[kb][0], qop[0], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+#pragma unroll
+            for (int ks = 1; ks < KD; ++ks)
+                s = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop[kb][ks], qop[ks], s, 0, 0, 0);
+            sacc[kb] = s;
         }
         if (!full) {
 #pragma unroll
@@ -407,7 +425,7 @@ __device__ __forceinline__ void run_item(const DecodeParams &P, const Addr &A, c
             const float mn = need ? mt : mref;
             const float alpha = need ? (mref == -INFINITY ? 0.f : fast_exp2(mref - mn)) : 1.f;
 #pragma unroll
-            for (int db = 0; db < 4; ++db)
+            for (int db = 0; db < NDB; ++db)
                 acc[db] *= alpha;
             accl *= alpha;
             mref = mn;
@@ -429,7 +447,7 @@ __device__ __forceinline__ void run_item(const DecodeParams &P, const Addr &A, c
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
-            for (int db = 0; db < 4; ++db) {
+            for (int db = 0; db < NDB; ++db) {
                 const f16x8 vop = __builtin_shufflevector(vraw[ks][db][0], vraw[ks][db][1], 0, 1, 2, 3, 4, 5, 6, 7);
                 acc[db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vop, pop[ks], acc[db], 0, 0, 0);
             }
@@ -466,11 +484,11 @@ __device__ __forceinline__ void run_item(const DecodeParams &P, const Addr &A, c
     // own.  Every merge goes through merge_column, so the result does not depend on which
     // item merges.
     const float lsum = accl[0];
-    f16 *outp = (f16 *)P.out + ((size_t)bm * P.hq + (size_t)it.g * G + hd) * D;
+    f16 *outp = (f16 *)P.out + ((size_t)bm * P.hq + (size_t)it.g * G + hd) * HD;
     if (cv && np == 1) {
         const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
 #pragma unroll
-        for (int db = 0; db < 4; ++db) {
+        for (int db = 0; db < NDB; ++db) {
             const f16x4 o = {(f16)(acc[db][0] * inv), (f16)(acc[db][1] * inv), (f16)(acc[db][2] * inv),
                              (f16)(acc[db][3] * inv)};
             *(f16x4 *)(outp + 16 * db + 4 * grp) = o;
@@ -503,7 +521,7 @@ __device__ __forceinline__ void run_item(const DecodeParams &P, const Addr &A, c
             }
             if (__builtin_amdgcn_readfirstlane(ready)) {
                 if (cv)
-                    merge_column(P.part, pbase, np, own, hd, grp, mref, lsum, acc, outp);
+                    merge_column<HD>(P.part, pbase, np, own, hd, grp, mref, lsum, acc, outp);
                 if (lane == 0)
                     reset_ticket(&P.tickets[pair]);
                 return;
@@ -511,12 +529,12 @@ __device__ __forceinline__ void run_item(const DecodeParams &P, const Addr &A, c
         }
     }
     if (split_col) {
-        float *dst = P.part + ((size_t)pb * MAXG + hd) * PART_FLOATS;
+        float *dst = P.part + ((size_t)pb * MAXG + hd) * part_floats(HD);
 #pragma unroll
-        for (int db = 0; db < 4; ++db)
+        for (int db = 0; db < NDB; ++db)
             coherent_store4(dst + 16 * db + 4 * grp, acc[db]);
         if (grp == 0)
-            coherent_store2(dst + D, mref, lsum);
+            coherent_store2(dst + HD, mref, lsum);
     }
     wait_stores(); // every partial store has completed before a ticket publishes it
     // one ticket per member pair, taken by the lane of the member's first column
@@ -528,19 +546,19 @@ __device__ __forceinline__ void run_item(const DecodeParams &P, const Addr &A, c
     if (__ballot(last) == 0)
         return;
     if (last) {
-        merge_column(P.part, pbase, np, own, hd, grp, mref, lsum, acc, outp);
+        merge_column<HD>(P.part, pbase, np, own, hd, grp, mref, lsum, acc, outp);
         if (hd == 0 && grp == 0)
             reset_ticket(&P.tickets[bm * hkv + it.g]);
     }
 }
 
-template <int G, int NBUF, int TT, bool PLANNED, typename Addr>
+template <int G, int NBUF, int TT, int HD, bool PLANNED, typename Addr>
 __global__ __launch_bounds__(64) void decode_f16_kernel(DecodeParams P, Addr A, PlanView PV)
 {
     static_assert(G >= 1 && G <= MAXG, "group size");
     static_assert(NBUF >= 2 && NBUF <= 3, "ring depth");
-    __shared__ __attribute__((aligned(16))) char kring[NBUF * TT * 128];
-    __shared__ __attribute__((aligned(16))) char vring[NBUF * TT * 128];
+    __shared__ __attribute__((aligned(16))) char kring[NBUF * TT * 2 * HD];
+    __shared__ __attribute__((aligned(16))) char vring[NBUF * TT * 2 * HD];
     const int lane = threadIdx.x;
     Item it;
     int rv;
@@ -566,12 +584,12 @@ __global__ __launch_bounds__(64) void decode_f16_kernel(DecodeParams P, Addr A, 
         if (flags & F_SHARED) {
             if (it.nmem * G > 16 || it.slot < 0)
                 return;
-            run_item<G, true, NBUF, TT>(P, A, PV, it, rv, kring, vring);
+            run_item<G, true, NBUF, TT, HD>(P, A, PV, it, rv, kring, vring);
             return;
         }
         if (it.nmem != 1)
             return;
-        run_item<G, false, NBUF, TT>(P, A, PV, it, rv, kring, vring);
+        run_item<G, false, NBUF, TT, HD>(P, A, PV, it, rv, kring, vring);
     } else {
         const int pair = blockIdx.x / PV.ipp;
         const int k = blockIdx.x - pair * PV.ipp;
@@ -596,7 +614,7 @@ __global__ __launch_bounds__(64) void decode_f16_kernel(DecodeParams P, Addr A, 
         it.slot = it.pbase + k;
         const int j = lane - R_ENT;
         rv = (j >= 0 && j < it.nblk) ? A.entry(it.b, it.blk0 + j) : -1;
-        run_item<G, false, NBUF, TT>(P, A, PV, it, rv, kring, vring);
+        run_item<G, false, NBUF, TT, HD>(P, A, PV, it, rv, kring, vring);
     }
 }
 
@@ -610,15 +628,21 @@ static kvp_status launch_f16(const DecodeParams &P, const Addr &A, const PlanVie
     if (grid > 0x7fffffffLL)
         return fail(KVP_ERR_UNSUPPORTED, "decode: %lld work items", grid);
     dim3 g((unsigned)grid), block(64);
-    switch (group) {
+    if (group < 1 || group > MAXG)
+        return fail(KVP_ERR_UNSUPPORTED, "decode: %d query heads per KV head (1..8 supported)", group);
+    if (P.dim != 64 && P.dim != 128)
+        return fail(KVP_ERR_UNSUPPORTED, "decode: head_dim=%d (64 or 128)", P.dim);
+    // head_dim 64: 64-token tiles; 128: 32-token tiles (the same 32 KB of LDS for the rings)
+    switch (group * 1000 + P.dim) {
 #define KVP_G(GG)                                                                                  \
-    case GG:                                                                                       \
-        hipLaunchKernelGGL((decode_f16_kernel<GG, DEC_NBUF, DEC_TT, PLANNED, Addr>), g, block, 0, st, P, A, PV); \
+    case GG * 1000 + 64:                                                                           \
+        hipLaunchKernelGGL((decode_f16_kernel<GG, DEC_NBUF, DEC_TT, 64, PLANNED, Addr>), g, block, 0, st, P, A, PV); \
+        break;                                                                                     \
+    case GG * 1000 + 128:                                                                          \
+        hipLaunchKernelGGL((decode_f16_kernel<GG, 2, 32, 128, PLANNED, Addr>), g, block, 0, st, P, A, PV); \
         break;
         KVP_G(1) KVP_G(2) KVP_G(3) KVP_G(4) KVP_G(5) KVP_G(6) KVP_G(7) KVP_G(8)
 #undef KVP_G
-    default:
-        return fail(KVP_ERR_UNSUPPORTED, "decode: %d query heads per KV head (1..8 supported)", group);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
@@ -632,9 +656,9 @@ int decode_f16_items_per_pair(int max_context)
     return nb <= UNSPLIT_BLOCKS ? 1 : (nb + SPLIT_BLOCKS - 1) / SPLIT_BLOCKS;
 }
 
-size_t decode_f16_part_bytes(long long slots)
+size_t decode_f16_part_bytes(long long slots, int dim)
 {
-    return (size_t)slots * MAXG * PART_FLOATS * sizeof(float);
+    return (size_t)slots * MAXG * part_floats(dim) * sizeof(float);
 }
 
 kvp_status launch_decode_f16(const DecodeParams &P, const PagedAddr &A, int group, int max_context,

@@ -76,6 +76,33 @@ __device__ inline float max16(const f32x4_ (&s)[4])
     const float e = max3(s[3][0], s[3][1], s[3][2]);
     return max3(max3(a, b, c), max3(d, e, s[3][3]), a);
 }
+// the same for 8 scores (two 4-row accumulators)
+__device__ inline float max8(const f32x4_ (&s)[2])
+{
+    const float a = max3(s[0][0], s[0][1], s[0][2]), b = max3(s[0][3], s[1][0], s[1][1]);
+    return max3(a, b, max3(s[1][2], s[1][3], s[1][3]));
+}
+// maximum of the scores of KB 16-key blocks (KB = 2 or 4)
+template <int KB> __device__ inline float max_scores(const f32x4_ (&s)[KB])
+{
+    static_assert(KB == 2 || KB == 4, "2 or 4 key blocks");
+    if constexpr (KB == 4)
+        return max16(s);
+    else
+        return max8(s);
+}
+
+// LDS slot of 16-byte chunk c of tile row r, for rows of HD fp16 values (128 or 256 bytes):
+// an XOR swizzle under which 8 consecutive rows read at one chunk, and 4 consecutive rows
+// read at two neighbouring chunks (the transposing reads of V), fall on distinct banks.
+// 128-byte rows alternate between the two bank halves, so XOR with r mod 8 suffices;
+// 256-byte rows all start at bank 0, so the XOR keeps the chunk's low bit and moves the
+// other bits with r mod 8.
+template <int HD> __device__ inline int swz(int c, int r)
+{
+    static_assert(HD == 64 || HD == 128, "rows of 64 or 128 values");
+    return HD == 64 ? c ^ (r & 7) : c ^ ((r & 7) << 1);
+}
 
 // max over lanes col, col + 16, col + 32, col + 48 (the k-groups of one MFMA column): swap
 // odd and even 16-lane rows, then the two 32-lane halves, without an LDS round trip

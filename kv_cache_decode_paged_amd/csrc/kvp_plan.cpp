@@ -30,8 +30,8 @@ kvp_status check_plan_dims(const kvp_dims *d, const char *who)
     if (d->num_q_heads <= 0 || d->num_kv_heads <= 0 || d->num_q_heads % d->num_kv_heads != 0)
         return fail(KVP_ERR_INVALID, "%s: num_q_heads=%d must be a positive multiple of num_kv_heads=%d",
                     who, d->num_q_heads, d->num_kv_heads);
-    if (d->head_dim != 64)
-        return fail(KVP_ERR_UNSUPPORTED, "%s: head_dim=%d (only 64 is implemented)", who, d->head_dim);
+    if (d->head_dim != 64 && d->head_dim != 128)
+        return fail(KVP_ERR_UNSUPPORTED, "%s: head_dim=%d (64 or 128)", who, d->head_dim);
     if (d->dtype != KVP_F16)
         return fail(d->dtype == KVP_F32 ? KVP_ERR_UNSUPPORTED : KVP_ERR_INVALID,
                     "%s: planned decode is implemented for fp16 (dtype=%d)", who, d->dtype);
@@ -347,6 +347,8 @@ kvp_status decode_plan_build(const kvp_dims *dims, const int32_t *table, int32_t
     plan->num_blocks = num_blocks;
     plan->n_items = (int32_t)n_image;
     plan->n_shared = (int32_t)n_shared;
+    plan->head_dim = dims->head_dim;
+    plan->reserved = 0;
     plan->n_slots = slots;
     plan->bytes = (int64_t)bytes;
     plan->off_pair_base = (int64_t)off_pb;

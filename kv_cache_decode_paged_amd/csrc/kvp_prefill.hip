@@ -11,11 +11,13 @@
 //   neuralialabs chapter: prefill is one pass over the whole prompt, a matrix-matrix
 //   product, so this is where the matrix cores pay off.
 //
-// fp16: one workgroup = 4 wave64 = 256 query rows of one (segment, query head).  Wave w
-// owns four blocks of 16 rows, rows q0 + 64 nb + 16 w, so the four waves reach the causal
-// diagonal together and share every K/V tile.  K and V tiles of 64 keys stream HBM -> LDS
+// fp16: one workgroup = 4 wave64 = 64 NQB query rows of one (segment, query head).  Wave w
+// owns NQB blocks of 16 rows, rows q0 + 64 nb + 16 w, so the four waves reach the causal
+// diagonal together and share every K/V tile.  K and V tiles of KT keys stream HBM -> LDS
 // through global_load_lds into a 3-slot ring (one barrier per tile); each wave reads a
-// tile's K rows and its transposed V once and uses them for all four of its blocks:
+// tile's K rows and its transposed V once and uses them for all of its blocks.  Head dim
+// 64: NQB = 4, KT = 64; head dim 128: NQB = 2, KT = 32 (the operands of twice the width in
+// the same register budget, and the same 8 KB K or V tile):
 //   scores  S^T = K Q^T       v_mfma_f32_16x16x32_f16, one query row per MFMA column
 //   softmax fp32, exp2 of one FMA (scale folded in), reference max moved only when a row's
 //           maximum passes it by 2^8, masks only on the diagonal and ragged tiles
@@ -41,15 +43,24 @@ typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x2 __attribute__((ext_vector_type(2)));
 
 namespace pf {
-constexpr int D = 64;
+constexpr int D = 64;        // head dim of the fp32 kernel
 constexpr int BS = 16;       // tokens per cache block
-constexpr int QB = 256;      // query rows per workgroup (fp16)
-constexpr int NQB = 4;       // 16-row query blocks per wave
-constexpr int KT = 64;       // keys per tile
 constexpr int NBUF = 3;      // ring slots for K and for V
-constexpr int SLOT = KT * 128; // bytes of one K (or V) tile
-constexpr int NDMA = 4;      // 1 KB loads per wave per tile (two of K, two of V)
 constexpr float LOG2E = 1.4426950408889634f;
+
+// tiling of the fp16 kernel by head dim HD
+template <int HD> struct Tiles {
+    static_assert(HD == 64 || HD == 128, "head dim 64 or 128");
+    static constexpr int NQB = HD == 64 ? 4 : 2; // 16-row query blocks per wave
+    static constexpr int QB = 64 * NQB;         // query rows per workgroup
+    static constexpr int KT = HD == 64 ? 64 : 32; // keys per tile
+    static constexpr int RB = 2 * HD;           // bytes of one K (or V) row
+    static constexpr int SLOT = KT * RB;        // bytes of one K (or V) tile
+    static constexpr int LPW = SLOT / 1024 / 4; // 1 KB loads per wave per tile, each of K and V
+    static constexpr int NDMA = 2 * LPW;
+};
+// query rows per workgroup of the fp16 kernel
+inline int query_rows_per_workgroup(int hd) { return hd == 64 ? Tiles<64>::QB : Tiles<128>::QB; }
 } // namespace pf
 
 __device__ inline float pf_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -60,7 +71,7 @@ __device__ inline float pf_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 // its ctx[s] cached positions, whose keys are reached through the block table.
 struct PrefillArgs {
     const f16 *q;
-    const f16 *k;      // packed k [T][Hkv][D], or the layer's K pool [blocks][Hkv][16][D]
+    const f16 *k;      // packed k [T][Hkv][d], or the layer's K pool [blocks][Hkv][16][d]
     const f16 *v;
     f16 *out;
     const int *cu;     // [nseg + 1] query-row offsets (packed: also key rows)
@@ -77,11 +88,20 @@ struct PrefillArgs {
 // block ids of one request staged in LDS (paged): contexts of up to MAX_IDS blocks
 constexpr int MAX_IDS = 4096;
 
-// grid = (Hq, nseg, ceil(max query rows / 256)), block = 256
-template <bool PAGED>
+// grid = (Hq, nseg, ceil(max query rows / QB)), block = 256
+template <bool PAGED, int D>
 __global__ __launch_bounds__(256) void prefill_mfma_f16_kernel(PrefillArgs P)
 {
     using namespace pf;
+    using T_ = Tiles<D>;
+    constexpr int NQB = T_::NQB, QB = T_::QB, KT = T_::KT, RB = T_::RB, SLOT = T_::SLOT;
+    constexpr int LPW = T_::LPW, NDMA = T_::NDMA;
+    constexpr int CPR = D / 8;    // 16-byte chunks per row
+    constexpr int RPI = 1024 / RB; // rows per 1 KB load
+    constexpr int KB = KT / 16;   // 16-key blocks per tile
+    constexpr int KS = KT / 32;   // 32-key steps per tile (value product)
+    constexpr int KD = D / 32;    // 32-dim steps (score product)
+    constexpr int NDB = D / 16;   // 16-dim blocks of the output
     // one barrier per tile: the DMA of tile t + 2 refills the slot of tile t - 1, so three
     // slots are the minimum
     static_assert(NBUF >= 3, "ring of at least three slots");
@@ -114,7 +134,7 @@ __global__ __launch_bounds__(256) void prefill_mfma_f16_kernel(PrefillArgs P)
     const float c = P.scale_log2;
 
     // ---- this wave's query blocks: Q^T operands and each row's key limit ----
-    f16x8 qop[NQB][2];
+    f16x8 qop[NQB][KD];
     int r0[NQB], lim[NQB];
 #pragma unroll
     for (int nb = 0; nb < NQB; ++nb) {
@@ -122,9 +142,11 @@ __global__ __launch_bounds__(256) void prefill_mfma_f16_kernel(PrefillArgs P)
         const int row = r0[nb] + col;
         const f16 *qp = P.q + ((size_t)(a + min(row, n - 1)) * hq + h) * D + grp * 8;
         const f16x8 z = {0, 0, 0, 0, 0, 0, 0, 0};
-        const f16x8 qa = *(const f16x8 *)qp, qb = *(const f16x8 *)(qp + 32);
-        qop[nb][0] = row < n ? qa : z;
-        qop[nb][1] = row < n ? qb : z;
+#pragma unroll
+        for (int ks = 0; ks < KD; ++ks) {
+            const f16x8 qv = *(const f16x8 *)(qp + 32 * ks);
+            qop[nb][ks] = row < n ? qv : z;
+        }
         lim[nb] = causal ? max(0, min(off + row + 1, nk)) : nk; // keys >= lim are masked for this row
     }
     const int kend = causal ? max(0, min(nk, off + q0 + QB)) : nk; // keys any row of the workgroup sees
@@ -149,35 +171,39 @@ __global__ __launch_bounds__(256) void prefill_mfma_f16_kernel(PrefillArgs P)
         all_ok = ids_bad == 0;
     }
 
-    // ---- DMA of tile t into ring slot t % NBUF: wave w loads rows 16 w .. 16 w + 15 of K and
-    // of V (LDS row r, chunk slot s holds chunk s ^ (r & 7)); rows past the workgroup's last
-    // visible key re-read that key's row (they are masked; its block id is staged), an
-    // unusable block reads block 0 (masked too) ----
+    // ---- DMA of tile t into ring slot t % NBUF: wave w loads the tile's 1 KB pieces
+    // LPW w .. LPW w + LPW - 1 of K and of V (RPI rows each; LDS row r, chunk slot
+    // swz(c, r) holds chunk c); rows past the workgroup's last visible key re-read that
+    // key's row (they are masked; its block id is staged), an unusable block reads block 0
+    // (masked too) ----
     auto issue = [&](int t) {
         char *kd = kring + (t % NBUF) * SLOT;
         char *vd = vring + (t % NBUF) * SLOT;
-        int kk[2], e[2] = {0, 0};
+        int kk[LPW], e[LPW];
 #pragma unroll
-        for (int ii = 0; ii < 2; ++ii) {
-            const int r = 8 * (2 * wave + ii) + (lane >> 3);
+        for (int ii = 0; ii < LPW; ++ii) {
+            const int r = RPI * (LPW * wave + ii) + lane / CPR;
             kk[ii] = min(t * KT + r, kend - 1); // beyond kend every row of the workgroup masks the key
+            e[ii] = 0;
             if constexpr (PAGED)
                 e[ii] = lds_b32(&ids[kk[ii] >> 4]);
         }
         if constexpr (PAGED) {
             asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-            asm volatile("" : "+v"(e[0]), "+v"(e[1]));
+#pragma unroll
+            for (int ii = 0; ii < LPW; ++ii)
+                asm volatile("" : "+v"(e[ii]));
         }
 #pragma unroll
-        for (int ii = 0; ii < 2; ++ii) {
-            const int i = 2 * wave + ii;
-            const int r = 8 * i + (lane >> 3);
+        for (int ii = 0; ii < LPW; ++ii) {
+            const int i = LPW * wave + ii;
+            const int r = RPI * i + lane / CPR;
             size_t off_e;
             if constexpr (PAGED)
                 off_e = (((size_t)max(e[ii], 0) * hkv + g_kv) * BS + (kk[ii] & (BS - 1))) * D;
             else
                 off_e = ((size_t)(a + kk[ii]) * hkv + g_kv) * D;
-            const size_t o = off_e + (((lane & 7) ^ (r & 7)) * 8);
+            const size_t o = off_e + swz<D>(lane & (CPR - 1), r) * 8;
             __builtin_amdgcn_global_load_lds((const void *)(P.k + o),
                                              (__attribute__((address_space(3))) void *)(kd + i * 1024), 16, 0, 0);
             __builtin_amdgcn_global_load_lds((const void *)(P.v + o),
@@ -188,13 +214,13 @@ __global__ __launch_bounds__(256) void prefill_mfma_f16_kernel(PrefillArgs P)
     // running state per block: reference max (scaled, log2 units), O^T rows 16 db + 4 grp + i
     // of column col, and the row sum (every entry of accl holds it)
     float mref[NQB];
-    f32x4 acc[NQB][4], accl[NQB];
+    f32x4 acc[NQB][NDB], accl[NQB];
 #pragma unroll
     for (int nb = 0; nb < NQB; ++nb) {
         mref[nb] = -INFINITY;
         accl[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int db = 0; db < 4; ++db)
+        for (int db = 0; db < NDB; ++db)
             acc[nb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
     const f16x8 ones = {1, 1, 1, 1, 1, 1, 1, 1};
@@ -221,42 +247,45 @@ __global__ __launch_bounds__(256) void prefill_mfma_f16_kernel(PrefillArgs P)
             continue;
         const char *kt = kring + (t % NBUF) * SLOT;
         const char *vt = vring + (t % NBUF) * SLOT;
-        // K rows (A of the score MFMA): key 16 kb + col, dims 8 grp .. and 32 + 8 grp ..
-        f16x8 kop[4][2];
+        // K rows (A of the score MFMA): key 16 kb + col, dims 32 ks + 8 grp .. (chunk 4 ks + grp)
+        f16x8 kop[KB][KD];
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
+        for (int kb = 0; kb < KB; ++kb) {
             const int r = kb * 16 + col;
-            kop[kb][0] = lds_b128(kt + r * 128 + ((grp ^ (r & 7)) * 16));
-            kop[kb][1] = lds_b128(kt + r * 128 + (((4 + grp) ^ (r & 7)) * 16));
+#pragma unroll
+            for (int ks = 0; ks < KD; ++ks)
+                kop[kb][ks] = lds_b128(kt + r * RB + swz<D>(4 * ks + grp, r) * 16);
         }
         // V^T (A of the value MFMA), k-step ks, dims 16 db ..: lane L of group grp addresses
         // key row 16 (2 ks + h) + 4 grp + L / 4, dims 16 db + 4 (L % 4); the transposing
         // read hands lane i element j = half i % 4 of lane 4 j + i / 4's 8 bytes
-        f16x4 vraw[2][4][2];
+        f16x4 vraw[KS][NDB][2];
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
+        for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-            for (int db = 0; db < 4; ++db)
+            for (int db = 0; db < NDB; ++db)
 #pragma unroll
                 for (int hh = 0; hh < 2; ++hh) {
                     const int row = 16 * (2 * ks + hh) + 4 * grp + (col >> 2);
                     const int ch = 2 * db + ((col & 3) >> 1);
-                    vraw[ks][db][hh] = lds_tr16_b64(vt + row * 128 + ((ch ^ (row & 7)) * 16) + (col & 1) * 8);
+                    vraw[ks][db][hh] = lds_tr16_b64(vt + row * RB + swz<D>(ch, row) * 16 + (col & 1) * 8);
                 }
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb)
-            asm volatile("" : "+v"(kop[kb][0]), "+v"(kop[kb][1]));
+        for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
+            for (int ks = 0; ks < KD; ++ks)
+                asm volatile("" : "+v"(kop[kb][ks]));
 #pragma unroll
-            for (int db = 0; db < 4; ++db)
+        for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
                 asm volatile("" : "+v"(vraw[ks][db][0]), "+v"(vraw[ks][db][1]));
-        f16x8 vop[2][4];
+        f16x8 vop[KS][NDB];
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
+        for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-            for (int db = 0; db < 4; ++db)
+            for (int db = 0; db < NDB; ++db)
                 vop[ks][db] = __builtin_shufflevector(vraw[ks][db][0], vraw[ks][db][1], 0, 1, 2, 3, 4, 5, 6, 7);
 
 #pragma unroll
@@ -264,37 +293,43 @@ __global__ __launch_bounds__(256) void prefill_mfma_f16_kernel(PrefillArgs P)
             if (!(r0[nb] < n && (!causal || k0 <= off + r0[nb] + 15)))
                 continue; // wave-uniform: no key of this tile is visible to the block
             // scores: sacc[kb][i] = S[key k0 + 16 kb + 4 grp + i][row r0 + col] (unscaled)
-            f32x4 sacc[4];
+            f32x4 sacc[KB];
 #pragma unroll
-            for (int kb = 0; kb < 4; ++kb) {
-                const f32x4 s0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop[kb][0], qop[nb][0],
-                                                                        f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-                sacc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop[kb][1], qop[nb][1], s0, 0, 0, 0);
+            for (int kb = 0; kb < KB; ++kb) {
+                f32x4 s = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop[kb][0], qop[nb][0], f32x4{0.f, 0.f, 0.f, 0.f},
+                                                                 0, 0, 0);
+#pragma unroll
+                for (int ks = 1; ks < KD; ++ks)
+                    s = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop[kb][ks], qop[nb][ks], s, 0, 0, 0);
+                sacc[kb] = s;
             }
             const bool full = all_ok && (!causal || k0 + KT - 1 <= off + r0[nb]) && k0 + KT <= nk;
             if (!full) {
-                bool bok[4] = {true, true, true, true};
+                bool bok[KB];
+#pragma unroll
+                for (int kb = 0; kb < KB; ++kb)
+                    bok[kb] = true;
                 if constexpr (PAGED) {
                     if (!all_ok) { // keys of unusable blocks are masked
-                        int e4[4];
+                        int e4[KB];
 #pragma unroll
-                        for (int kb = 0; kb < 4; ++kb)
+                        for (int kb = 0; kb < KB; ++kb)
                             e4[kb] = lds_b32(&ids[min((k0 >> 4) + kb, MAX_IDS - 1)]);
                         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 #pragma unroll
-                        for (int kb = 0; kb < 4; ++kb) {
+                        for (int kb = 0; kb < KB; ++kb) {
                             asm volatile("" : "+v"(e4[kb]));
                             bok[kb] = e4[kb] >= 0;
                         }
                     }
                 }
 #pragma unroll
-                for (int kb = 0; kb < 4; ++kb)
+                for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
                     for (int i = 0; i < 4; ++i)
                         sacc[kb][i] = (bok[kb] && k0 + 16 * kb + 4 * grp + i < lim[nb]) ? sacc[kb][i] : -INFINITY;
             }
-            const float mt = group_max(max16(sacc)) * c;
+            const float mt = group_max(max_scores<KB>(sacc)) * c;
             // a row's reference max moves only when the row's own maximum passes it by more
             // than 2^8; between moves p = 2^(s c - mref) < 256 and nothing needs rescaling.
             // Rows that do not move scale by exactly 1, so no row depends on another's keys.
@@ -303,7 +338,7 @@ __global__ __launch_bounds__(256) void prefill_mfma_f16_kernel(PrefillArgs P)
                 const float mn = need ? mt : mref[nb];
                 const float alpha = need ? (mref[nb] == -INFINITY ? 0.f : pf_exp2(mref[nb] - mn)) : 1.f;
 #pragma unroll
-                for (int db = 0; db < 4; ++db)
+                for (int db = 0; db < NDB; ++db)
                     acc[nb][db] *= alpha;
                 accl[nb] *= alpha;
                 mref[nb] = mn;
@@ -311,16 +346,16 @@ __global__ __launch_bounds__(256) void prefill_mfma_f16_kernel(PrefillArgs P)
             const float mc = mref[nb] == -INFINITY ? 0.f : mref[nb];
             // P^T operand of k-step ks, slot s: key 16 (2 ks + s / 4) + 4 grp + s % 4 =
             // sacc[2 ks + s / 4][s % 4], rounded once to fp16
-            f16x8 pop[2];
+            f16x8 pop[KS];
 #pragma unroll
-            for (int ks = 0; ks < 2; ++ks)
+            for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
                 for (int s = 0; s < 8; ++s)
                     pop[ks][s] = (f16)pf_exp2(fmaf(sacc[2 * ks + (s >> 2)][s & 3], c, -mc));
 #pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
+            for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
-                for (int db = 0; db < 4; ++db)
+                for (int db = 0; db < NDB; ++db)
                     acc[nb][db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vop[ks][db], pop[ks], acc[nb][db], 0, 0, 0);
                 accl[nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, pop[ks], accl[nb], 0, 0, 0);
             }
@@ -337,7 +372,7 @@ __global__ __launch_bounds__(256) void prefill_mfma_f16_kernel(PrefillArgs P)
         const float inv = l > 0.f ? 1.f / l : 0.f;
         f16 *dst = P.out + ((size_t)(a + row) * hq + h) * D + grp * 4;
 #pragma unroll
-        for (int db = 0; db < 4; ++db) {
+        for (int db = 0; db < NDB; ++db) {
             const f16x4 o4 = {(f16)(acc[nb][db][0] * inv), (f16)(acc[nb][db][1] * inv), (f16)(acc[nb][db][2] * inv),
                               (f16)(acc[nb][db][3] * inv)};
             *(f16x4 *)(dst + 16 * db) = o4;
@@ -414,10 +449,12 @@ extern "C" kvp_status varlen_causal_prefill(const kvp_dims *dims, void *out, con
         dims->num_q_heads % dims->num_kv_heads != 0)
         return fail(KVP_ERR_INVALID, "varlen_causal_prefill: num_q_heads=%d, num_kv_heads=%d",
                     dims->num_q_heads, dims->num_kv_heads);
-    if (dims->head_dim != pf::D)
-        return fail(KVP_ERR_UNSUPPORTED, "varlen_causal_prefill: head_dim=%d (only 64)", dims->head_dim);
     if (dims->dtype != KVP_F16 && dims->dtype != KVP_F32)
         return fail(KVP_ERR_INVALID, "varlen_causal_prefill: dtype=%d", dims->dtype);
+    const int hd = dims->head_dim;
+    if (hd != pf::D && !(dims->dtype == KVP_F16 && hd == 128))
+        return fail(KVP_ERR_UNSUPPORTED, "varlen_causal_prefill: head_dim=%d (64, or 128 for fp16)", hd);
+    const int QB = pf::query_rows_per_workgroup(hd);
     if (nseg < 0 || max_seqlen < 0 || (causal != 0 && causal != 1))
         return fail(KVP_ERR_INVALID, "varlen_causal_prefill: nseg=%d max_seqlen=%d causal=%d", nseg,
                     max_seqlen, causal);
@@ -426,17 +463,20 @@ extern "C" kvp_status varlen_causal_prefill(const kvp_dims *dims, void *out, con
     if (!out || !q || !k || !v || !d_cu_seqlens ||
         (((uintptr_t)out | (uintptr_t)q | (uintptr_t)k | (uintptr_t)v) & 15))
         return fail(KVP_ERR_INVALID, "varlen_causal_prefill: NULL or misaligned pointer");
-    if (nseg > 65535 || dims->num_q_heads > 65535 || (max_seqlen + pf::QB - 1) / pf::QB > 65535)
+    if (nseg > 65535 || dims->num_q_heads > 65535 || (max_seqlen + QB - 1) / QB > 65535)
         return fail(KVP_ERR_UNSUPPORTED, "varlen_causal_prefill: nseg, H_q or max_seqlen too large");
     if (scale == 0.f)
-        scale = 1.0f / sqrtf((float)pf::D);
+        scale = 1.0f / sqrtf((float)hd);
     const float sl2 = scale * pf::LOG2E;
     hipStream_t st = (hipStream_t)stream;
     if (dims->dtype == KVP_F16) {
-        dim3 grid(dims->num_q_heads, nseg, (max_seqlen + pf::QB - 1) / pf::QB);
+        dim3 grid(dims->num_q_heads, nseg, (max_seqlen + QB - 1) / QB);
         PrefillArgs A{(const f16 *)q, (const f16 *)k, (const f16 *)v, (f16 *)out, d_cu_seqlens, nullptr, nullptr,
                       0, 0, dims->num_q_heads, dims->num_kv_heads, sl2, causal};
-        hipLaunchKernelGGL(prefill_mfma_f16_kernel<false>, grid, dim3(256), 0, st, A);
+        if (hd == 64)
+            hipLaunchKernelGGL((prefill_mfma_f16_kernel<false, 64>), grid, dim3(256), 0, st, A);
+        else
+            hipLaunchKernelGGL((prefill_mfma_f16_kernel<false, 128>), grid, dim3(256), 0, st, A);
     } else {
         dim3 grid(max_seqlen, dims->num_q_heads, nseg);
         hipLaunchKernelGGL(prefill_valu_f32_kernel, grid, dim3(64), 0, st, (const float *)q,
@@ -461,8 +501,10 @@ extern "C" kvp_status paged_prefill_attention(const kvp_cache_desc *cache, int32
     const kvp_dims &d = cache->dims;
     if (d.num_layers <= 0 || d.num_q_heads <= 0 || d.num_kv_heads <= 0 || d.num_q_heads % d.num_kv_heads != 0)
         return fail(KVP_ERR_INVALID, "%s: num_q_heads=%d, num_kv_heads=%d", who, d.num_q_heads, d.num_kv_heads);
-    if (d.head_dim != pf::D)
-        return fail(KVP_ERR_UNSUPPORTED, "%s: head_dim=%d (only 64)", who, d.head_dim);
+    const int hd = d.head_dim;
+    if (hd != 64 && hd != 128)
+        return fail(KVP_ERR_UNSUPPORTED, "%s: head_dim=%d (64 or 128)", who, hd);
+    const int QB = pf::query_rows_per_workgroup(hd);
     if (d.dtype != KVP_F16)
         return fail(KVP_ERR_UNSUPPORTED, "%s: dtype=%d (fp16 only)", who, d.dtype);
     if (cache->block_size != pf::BS)
@@ -480,17 +522,20 @@ extern "C" kvp_status paged_prefill_attention(const kvp_cache_desc *cache, int32
         return fail(KVP_ERR_INVALID, "%s: NULL or misaligned pointer", who);
     if (max_blocks > MAX_IDS)
         return fail(KVP_ERR_UNSUPPORTED, "%s: max_blocks=%d (at most %d)", who, max_blocks, MAX_IDS);
-    if (B > 65535 || d.num_q_heads > 65535 || (max_q + pf::QB - 1) / pf::QB > 65535)
+    if (B > 65535 || d.num_q_heads > 65535 || (max_q + QB - 1) / QB > 65535)
         return fail(KVP_ERR_UNSUPPORTED, "%s: B, H_q or max_q too large", who);
     if (scale == 0.f)
-        scale = 1.0f / sqrtf((float)pf::D);
-    const size_t layer_elems = (size_t)cache->num_blocks * d.num_kv_heads * pf::BS * pf::D;
+        scale = 1.0f / sqrtf((float)hd);
+    const size_t layer_elems = (size_t)cache->num_blocks * d.num_kv_heads * pf::BS * hd;
     PrefillArgs A{(const f16 *)q, (const f16 *)cache->k_pool + (size_t)layer * layer_elems,
                   (const f16 *)cache->v_pool + (size_t)layer * layer_elems, (f16 *)out, d_cu_q, d_context_lens,
                   d_block_table, max_blocks, cache->num_blocks, d.num_q_heads, d.num_kv_heads,
                   scale * pf::LOG2E, 1};
-    dim3 grid(d.num_q_heads, B, (max_q + pf::QB - 1) / pf::QB);
-    hipLaunchKernelGGL(prefill_mfma_f16_kernel<true>, grid, dim3(256), 0, (hipStream_t)stream, A);
+    dim3 grid(d.num_q_heads, B, (max_q + QB - 1) / QB);
+    if (hd == 64)
+        hipLaunchKernelGGL((prefill_mfma_f16_kernel<true, 64>), grid, dim3(256), 0, (hipStream_t)stream, A);
+    else
+        hipLaunchKernelGGL((prefill_mfma_f16_kernel<true, 128>), grid, dim3(256), 0, (hipStream_t)stream, A);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return fail(KVP_ERR_HIP, "%s: launch failed: %s", who, hipGetErrorString(e));

@@ -44,9 +44,10 @@ class PagedStep:
     write where the target block is shared) and writes its K/V in every layer."""
 
     def __init__(self, kvp, pb: W.PagedBatch, layers, hq, hkv, dtype, seed, device="cuda",
-                 extra_blocks=64, poison=True, layers_with_data=None):
+                 extra_blocks=64, poison=True, layers_with_data=None, head_dim=W.HEAD_DIM):
         self.kvp, self.pb, self.layers = kvp, pb, layers
         self.hq, self.hkv, self.dtype, self.seed = hq, hkv, dtype, seed
+        self.head_dim = head_dim
         B = pb.batch
         ctx_after = [c + 1 for c in pb.ctx_before]
         self.lmax = max(ctx_after)
@@ -56,13 +57,15 @@ class PagedStep:
         self.num_blocks = need + extra_blocks
         self.pool = kvp.BlockPool(self.num_blocks)
         self.pool.set_free_order(W.free_list_permutation(self.num_blocks, seed + 17).tolist())
-        self.cache = kvp.PagedKVCache(layers, self.num_blocks, hq, hkv, dtype, device)
+        self.cache = kvp.PagedKVCache(layers, self.num_blocks, hq, hkv, dtype, device, head_dim=head_dim)
         if poison:  # never-written rows hold NaN: any read of them shows up in the output
             self.cache.k_pool.fill_(float("nan"))
             self.cache.v_pool.fill_(float("nan"))
         self.layers_with_data = list(range(layers)) if layers_with_data is None else layers_with_data
-        self.logical = {l: W.logical_kv(pb, hkv, self.lmax, seed, dtype, layer=l) for l in self.layers_with_data}
-        prefix = {l: W.group_prefix_kv(pb, hkv, seed, dtype, layer=l) for l in self.layers_with_data}
+        self.logical = {l: W.logical_kv(pb, hkv, self.lmax, seed, dtype, layer=l, head_dim=head_dim)
+                        for l in self.layers_with_data}
+        prefix = {l: W.group_prefix_kv(pb, hkv, seed, dtype, layer=l, head_dim=head_dim)
+                  for l in self.layers_with_data}
 
         seqs = [None] * B
         for gi in sorted(set(pb.group)):
@@ -123,7 +126,7 @@ class PagedStep:
                                V[i, :, start:end].transpose(0, 1).contiguous().to(device), sl)
 
     def q(self, layer):
-        return W.decode_q(self.pb.batch, self.hq, self.seed, self.dtype, layer)
+        return W.decode_q(self.pb.batch, self.hq, self.seed, self.dtype, layer, self.head_dim)
 
     def oracle(self, layer, rows=None):
         """Oracle decode output [B, Hq, d] (float64) for the given requests (all if None)."""
@@ -134,3 +137,80 @@ class PagedStep:
         out = oracle.decode_gqa(to64(q[rows]), to64(K[rows]), to64(V[rows]),
                                 np.array([self.ctx_host[r] for r in rows]))
         return out
+
+
+class ChunkStep:
+    """Requests with cached prefixes and a chunk of new rows, written through the block
+    manager (scattered block ids) into layer 0 of a paged cache; optionally requests fork a
+    shared prefix first.  Never-written cache rows hold NaN, so a read of one shows."""
+
+    def __init__(self, kvp, prefixes, chunks, seed, hq=14, hkv=2, share_groups=None, layers=1,
+                 head_dim=W.HEAD_DIM):
+        self.kvp = kvp
+        self.B = len(prefixes)
+        D = self.head_dim = head_dim
+        ctx = [p + m for p, m in zip(prefixes, chunks)]
+        self.ctx, self.m, self.hq, self.hkv = ctx, list(chunks), hq, hkv
+        self.lmax = max(ctx)
+        self.max_blocks = math.ceil(self.lmax / W.BLOCK)
+        nblocks = sum(math.ceil(c / W.BLOCK) for c in ctx) + 64
+        self.pool = kvp.BlockPool(nblocks)
+        self.pool.set_free_order(W.free_list_permutation(nblocks, seed).tolist())
+        self.cache = kvp.PagedKVCache(layers, nblocks, hq, hkv, torch.float16, "cuda", head_dim=D)
+        self.cache.k_pool.fill_(float("nan"))  # never-written rows show up as NaN
+        self.cache.v_pool.fill_(float("nan"))
+        # logical K / V of every request, seeded
+        self.K = W.randn((self.B, hkv, self.lmax, D), seed + 1)
+        self.V = W.randn((self.B, hkv, self.lmax, D), seed + 2)
+        if share_groups:
+            # requests in one group share the first prefix's tokens (same K/V rows, one set
+            # of physical blocks): fork the leader after it is written
+            for grp in share_groups:
+                lead = grp[0]
+                p = prefixes[lead]
+                for b in grp[1:]:
+                    assert prefixes[b] == p
+                    self.K[b, :, :p] = self.K[lead, :, :p]
+                    self.V[b, :, :p] = self.V[lead, :, :p]
+        self.seqs = [None] * self.B
+        grouped = {b for g in (share_groups or []) for b in g}
+        for b in range(self.B):
+            if b in grouped:
+                continue
+            s = self.pool.alloc(0)
+            self._write(s, b, 0, ctx[b])
+            self.seqs[b] = s
+        for grp in share_groups or []:
+            lead = grp[0]
+            p = prefixes[lead]
+            base = self.pool.alloc(0)
+            self._write(base, lead, 0, p)
+            for b in grp:
+                s = self.pool.fork(base)
+                self._write(s, b, p, ctx[b])
+                self.seqs[b] = s
+            self.pool.free(base)
+        table, ctxt = self.pool.export(self.seqs, self.max_blocks)
+        assert ctxt.tolist() == ctx
+        self.table, self.ctxd = table.cuda(), ctxt.cuda()
+        self.cu = torch.tensor([0] + list(np.cumsum(self.m)), dtype=torch.int32)
+        self.q = W.randn((int(self.cu[-1]), hq, D), seed + 3)
+
+    def _write(self, seq, b, lo, hi):
+        if hi <= lo:
+            return
+        slots, cow = self.pool.reserve(seq, hi - lo)
+        if cow is not None:  # the chunk starts inside a shared, partly filled prefix block
+            self.kvp.kv_copy_blocks(self.cache, torch.tensor([cow], dtype=torch.int32).cuda())
+        k = self.K[b, :, lo:hi].transpose(0, 1).contiguous().cuda()
+        v = self.V[b, :, lo:hi].transpose(0, 1).contiguous().cuda()
+        self.kvp.kv_append(self.cache, 0, k, v, slots.cuda())
+
+    def run(self):
+        return self.kvp.paged_prefill_attention(self.cache, 0, self.q.cuda(), self.table, self.ctxd, self.cu.cuda(),
+                                           max(self.m))
+
+    def oracle(self):
+        import oracle
+        return oracle.chunk_attention(to64(self.q), to64(self.K), to64(self.V), np.array(self.ctx, np.int32),
+                                      self.cu.numpy())

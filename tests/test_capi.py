@@ -66,9 +66,16 @@ def test_device_calls_reject_bad_arguments_before_launch():
     st = lib.contiguous_decode_attention(ctypes.byref(d), None, None, None, None, 16, None, 1, 0.0,
                                          None, 0, None)
     assert st == kvp.KVP_ERR_INVALID
-    d = kvp.kvp_dims(1, 14, 2, 128, kvp.KVP_F16)  # head_dim 128 not built
-    st = lib.varlen_causal_prefill(ctypes.byref(d), None, None, None, None, None, 1, 8, 1, 0.0, None)
-    assert st == kvp.KVP_ERR_UNSUPPORTED
+    for hd, dt in ((96, kvp.KVP_F16), (128, kvp.KVP_F32), (256, kvp.KVP_F16)):  # not built
+        d = kvp.kvp_dims(1, 14, 2, hd, dt)
+        st = lib.varlen_causal_prefill(ctypes.byref(d), None, None, None, None, None, 1, 8, 1, 0.0, None)
+        assert st == kvp.KVP_ERR_UNSUPPORTED
+        assert lib.decode_workspace_bytes(ctypes.byref(d), 1, 100) == 0
+        st = lib.contiguous_decode_attention(ctypes.byref(d), None, None, None, None, 16, None, 1, 0.0,
+                                             None, 0, None)
+        assert st == kvp.KVP_ERR_UNSUPPORTED
+    desc = kvp.kvp_cache_desc(kvp.kvp_dims(2, 14, 2, 96, kvp.KVP_F16), 16, 8, 16, 16)
+    assert lib.kv_copy_blocks(ctypes.byref(desc), None, 1, None) == kvp.KVP_ERR_UNSUPPORTED
     desc = kvp.kvp_cache_desc(kvp.kvp_dims(2, 14, 2, 64, kvp.KVP_F16), 16, 8, None, None)
     st = lib.kv_append(ctypes.byref(desc), 0, None, None, None, 1, None)
     assert st == kvp.KVP_ERR_INVALID  # NULL pools
@@ -88,6 +95,8 @@ def test_workspace_size():
     # contexts of at most 512 tokens are never split: no workspace
     assert kvp.decode_workspace_bytes(14, 2, torch.float16, 200, 512) == 0
     assert kvp.decode_workspace_bytes(14, 2, torch.float16, 200, 513) == 1792 + 200 * 2 * 2 * 8 * 68 * 4
+    # head_dim 128: 132-float partial records
+    assert kvp.decode_workspace_bytes(32, 8, torch.float16, 4, 4096, head_dim=128) == 256 + 4 * 8 * 8 * 8 * 132 * 4
     # fp32 single head, short context: one split, no workspace needed
     assert kvp.decode_workspace_bytes(1, 1, torch.float32, 1, 88) == 0
     # 5000 tokens: at most 16 splits (256-token splits up to 4096 tokens, 512 beyond)

@@ -84,10 +84,11 @@ def cu_seqlens(seqlens):
     return torch.tensor(cu, dtype=torch.int32)
 
 
-def varlen_inputs(seqlens, hq, hkv, seed=SEED + 100, dtype=torch.float16):
+def varlen_inputs(seqlens, hq, hkv, seed=SEED + 100, dtype=torch.float16, head_dim=HEAD_DIM):
     T = int(sum(seqlens))
-    return (randn((T, hq, HEAD_DIM), seed, dtype), randn((T, hkv, HEAD_DIM), seed + 1, dtype),
-            randn((T, hkv, HEAD_DIM), seed + 2, dtype), cu_seqlens(seqlens))
+    d = head_dim
+    return (randn((T, hq, d), seed, dtype), randn((T, hkv, d), seed + 1, dtype),
+            randn((T, hkv, d), seed + 2, dtype), cu_seqlens(seqlens))
 
 
 # ---------------------------------------------------------------------------------------
@@ -133,27 +134,27 @@ def free_list_permutation(num_blocks, seed=SEED + 400):
     return torch.randperm(num_blocks, generator=gen(seed)).to(torch.int32)
 
 
-def group_prefix_kv(pb: PagedBatch, hkv, seed, dtype=torch.float16, layer=0):
+def group_prefix_kv(pb: PagedBatch, hkv, seed, dtype=torch.float16, layer=0, head_dim=HEAD_DIM):
     """{group: (K, V)} of shape [hkv, prefix, d]: the rows every member of a sharing group
     holds in common."""
     base = seed + 1000 * layer
     pref = {}
     if pb.prefix > 0:
         for gi in sorted(set(pb.group)):
-            pref[gi] = (randn((hkv, pb.prefix, HEAD_DIM), base + 2 * gi, dtype),
-                        randn((hkv, pb.prefix, HEAD_DIM), base + 2 * gi + 1, dtype))
+            pref[gi] = (randn((hkv, pb.prefix, head_dim), base + 2 * gi, dtype),
+                        randn((hkv, pb.prefix, head_dim), base + 2 * gi + 1, dtype))
     return pref
 
 
-def logical_kv(pb: PagedBatch, hkv, lmax, seed, dtype=torch.float16, layer=0):
+def logical_kv(pb: PagedBatch, hkv, lmax, seed, dtype=torch.float16, layer=0, head_dim=HEAD_DIM):
     """Logical (contiguous) K and V [B, hkv, lmax, d] for one layer: positions below the
     prefix are the group's shared rows, the rest are private to each request; positions
     at or beyond ctx_before+1 are zero padding (never read)."""
     B = pb.batch
-    K = torch.zeros((B, hkv, lmax, HEAD_DIM), dtype=dtype)
+    K = torch.zeros((B, hkv, lmax, head_dim), dtype=dtype)
     V = torch.zeros_like(K)
     base = seed + 1000 * layer
-    pref = group_prefix_kv(pb, hkv, seed, dtype, layer)
+    pref = group_prefix_kv(pb, hkv, seed, dtype, layer, head_dim)
     for i in range(B):
         n = pb.ctx_before[i] + 1
         shared = min(pb.ctx_before[i], pb.prefix)
@@ -163,10 +164,10 @@ def logical_kv(pb: PagedBatch, hkv, lmax, seed, dtype=torch.float16, layer=0):
             V[i, :, :shared] = pv[:, :shared]
         if n > shared:
             s = base + 100000 + 2 * i
-            K[i, :, shared:n] = randn((hkv, n - shared, HEAD_DIM), s, dtype)
-            V[i, :, shared:n] = randn((hkv, n - shared, HEAD_DIM), s + 1, dtype)
+            K[i, :, shared:n] = randn((hkv, n - shared, head_dim), s, dtype)
+            V[i, :, shared:n] = randn((hkv, n - shared, head_dim), s + 1, dtype)
     return K, V
 
 
-def decode_q(batch, hq, seed, dtype=torch.float16, layer=0):
-    return randn((batch, hq, HEAD_DIM), seed + 7919 * (layer + 1), dtype)
+def decode_q(batch, hq, seed, dtype=torch.float16, layer=0, head_dim=HEAD_DIM):
+    return randn((batch, hq, head_dim), seed + 7919 * (layer + 1), dtype)
