@@ -13,6 +13,10 @@ copies run, then for each of the 24 layers one kernel appends the new token's K/
 the paged decode attention over the whole cache (paged_decode_attention_planned, replayed
 as one captured graph).  Contexts grow by one token per step.
 
+--shape 32q8kv_d128 / 32q32kv_d128 runs the same step at the 7B-class head shapes (32
+layers, head dim 128, 8 or 32 KV heads).  --workload prefill / chunked_prefill time the
+prefill kernels instead.
+
 Printed: one JSON line with the decode-attention KV throughput (unique bytes), steps/s,
 the roofline of the dominant kernel (the paged decode call: split-K partial + merge),
 and the fp64 CPU oracle timed on a bounded sample of the same workload.
@@ -31,6 +35,22 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBPS = 8000.0
 HQ, HKV, D, BLOCK = 14, 2, 64, 16
 KV_TOKEN_LAYER_BYTES = 2 * HKV * D * 2  # K and V, fp16: 512 B per token per layer
+
+# head shapes of the decode step: (layers, query heads, KV heads, head dim, description)
+SHAPES = {
+    "14q2kv_d64": (24, 14, 2, 64, "24 layers, 14q/2kv heads d64"),
+    # the 7B-class GQA shape (32 layers, 8 KV heads of d = 128) with 32 query heads
+    "32q8kv_d128": (32, 32, 8, 128, "32 layers, 32q/8kv heads d128 (7B-class GQA)"),
+    # the same model as plain multi-head attention (32 KV heads)
+    "32q32kv_d128": (32, 32, 32, 128, "32 layers, 32q/32kv heads d128 (MHA)"),
+}
+DEFAULT_SHAPE = "14q2kv_d64"
+
+
+def set_shape(name):
+    global HQ, HKV, D, KV_TOKEN_LAYER_BYTES
+    _, HQ, HKV, D, _ = SHAPES[name]
+    KV_TOKEN_LAYER_BYTES = 2 * HKV * D * 2
 
 
 # HBM traffic of the decode launch, counted by rocprofv3 (FETCH_SIZE / WRITE_SIZE passes,
@@ -99,6 +119,9 @@ def decode_call_bytes(table, ctx, B):
 
 
 def build_state(kvp, torch, W, B, layers, total_steps, seed):
+    """Block pool, cache (every slot seeded N(0,1)) and the batch's sequences: groups fork
+    their prefix, then each member truncates to a shorter context or reserves its private
+    tokens."""
     pb = W.paged_batch(B)
     dev = "cuda"
     ngroups = len(set(pb.group))
@@ -108,7 +131,7 @@ def build_state(kvp, torch, W, B, layers, total_steps, seed):
     max_blocks = math.ceil((max(pb.ctx_before) + total_steps + 1) / BLOCK)
     pool = kvp.BlockPool(num_blocks)
     pool.set_free_order(W.free_list_permutation(num_blocks, seed + 1).tolist())
-    cache = kvp.PagedKVCache(layers, num_blocks, HQ, HKV, torch.float16, dev)
+    cache = kvp.PagedKVCache(layers, num_blocks, HQ, HKV, torch.float16, dev, head_dim=D)
     for l in range(layers):  # cache contents: seeded N(0,1) in every slot
         cache.k_pool[l].copy_(W.randn_device(cache.k_pool[l].shape, seed + 10 + 2 * l, torch.float16, dev))
         cache.v_pool[l].copy_(W.randn_device(cache.v_pool[l].shape, seed + 11 + 2 * l, torch.float16, dev))
@@ -127,23 +150,28 @@ def build_state(kvp, torch, W, B, layers, total_steps, seed):
     return pb, pool, cache, seqs, max_blocks
 
 
-def cpu_baseline(W, B_sample_layers=2, seed=42):
-    """The fp64 oracle, as it is, on a bounded sample of the same workload: all 200
-    requests of `B_sample_layers` layers, one thread per request in flight."""
+def cpu_baseline(W, layers, seed=42):
+    """The fp64 oracle, as it is, on a bounded sample of the same workload, one thread per
+    request in flight: every request of 2 layers at the 14q/2kv d64 shape; for the larger
+    head shapes one layer of the first requests, sized to about the same oracle work."""
     import concurrent.futures as cf
 
     import numpy as np
 
     import oracle
     pb = W.paged_batch(200)
+    budget = 2 * 200 * 512 // KV_TOKEN_LAYER_BYTES  # request-layers
+    n_layers = 2 if budget >= 400 else 1
+    n_req = max(8, min(200, budget // n_layers))
+    pb = W.PagedBatch(ctx_before=pb.ctx_before[:n_req], group=pb.group[:n_req], prefix=pb.prefix)
     lmax = max(pb.ctx_before) + 1
     threads = min(16, len(os.sched_getaffinity(0)))
     ctx = np.array([c + 1 for c in pb.ctx_before], dtype=np.int32)
     total_bytes = 0
     elapsed = 0.0
-    for layer in range(B_sample_layers):
-        K, V = W.logical_kv(pb, HKV, lmax, seed, layer=layer)
-        q = W.decode_q(pb.batch, HQ, seed, layer=layer)
+    for layer in range(n_layers):
+        K, V = W.logical_kv(pb, HKV, lmax, seed, layer=layer, head_dim=D)
+        q = W.decode_q(pb.batch, HQ, seed, layer=layer, head_dim=D)
         K64, V64, q64 = K.double().numpy(), V.double().numpy(), q.double().numpy()
 
         def one(i):
@@ -158,7 +186,7 @@ def cpu_baseline(W, B_sample_layers=2, seed=42):
         total_bytes += int(ctx.sum()) * KV_TOKEN_LAYER_BYTES
     return {"value": round(total_bytes / elapsed / 1e9, 4), "unit": "GB/s", "cores": threads,
             "kind": "oracle",
-            "sample": f"{B_sample_layers} of 24 layers x all 200 requests of the batch-200 step "
+            "sample": f"{n_layers} of {layers} layers x {n_req} of the 200 requests of the batch-200 step "
                       f"(logical KV bytes / wall time, fp64 scalar C, {threads} threads)"}
 
 
@@ -175,7 +203,7 @@ def prefill_flops(seqlens, hq, d, causal):
 def prefill_cpu_baseline(W, hq, hkv, causal, n=4096, seed=7):
     """The fp64 oracle on a bounded sample: one of the sequences (n rows, all hq heads)."""
     import oracle
-    q, k, v, cu = W.varlen_inputs([n], hq, hkv, seed=seed)
+    q, k, v, cu = W.varlen_inputs([n], hq, hkv, seed=seed, head_dim=D)
     args = (q.double().numpy(), k.double().numpy(), v.double().numpy(), cu.numpy())
     t0 = time.perf_counter()
     oracle.varlen_prefill(*args, causal=causal)
@@ -187,16 +215,17 @@ def prefill_cpu_baseline(W, hq, hkv, causal, n=4096, seed=7):
 
 
 def bench_prefill(args):
-    """Packed varlen prefill: 16 sequences of 4096 tokens, 8 query / 2 KV heads, fp16,
-    causal (the long-prompt prefill shape; MFMA-bound)."""
+    """Packed varlen prefill: 16 sequences of 4096 tokens, 8 query / 2 KV heads of d 64 (or
+    the --shape's heads), fp16, causal (the long-prompt prefill shape; MFMA-bound)."""
     import torch
 
     import kv_cache_decode_paged_amd as kvp
     import workloads as W
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
-    seqlens, hq, hkv, causal = [4096] * 16, 8, 2, True
-    q, k, v, cu = W.varlen_inputs(seqlens, hq, hkv)
+    seqlens, causal = [4096] * 16, True
+    hq, hkv = (8, 2) if args.shape == DEFAULT_SHAPE else (HQ, HKV)
+    q, k, v, cu = W.varlen_inputs(seqlens, hq, hkv, head_dim=D)
     q, k, v, cu = q.cuda(), k.cuda(), v.cuda(), cu.cuda()
     out = torch.empty_like(q)
     for _ in range(args.warmup):
@@ -211,7 +240,9 @@ def bench_prefill(args):
     ms = a.elapsed_time(b) / args.steps
     flops = prefill_flops(seqlens, hq, D, causal)
     tflops = flops / (ms * 1e-3) / 1e12
-    cpu = None if args.no_cpu_baseline else prefill_cpu_baseline(W, hq, hkv, causal)
+    # the oracle's sample: one 4096-row segment, or 1536 rows at the wider head shapes
+    cpu = None if args.no_cpu_baseline else prefill_cpu_baseline(W, hq, hkv, causal,
+                                                                 n=4096 if hq * D <= 512 else 1536)
     print(f"[bench] prefill {len(seqlens)} x {seqlens[0]} tokens, {hq}q/{hkv}kv heads: {ms * 1e3:.1f} us per call, "
           f"{tflops:.1f} TFLOP/s ({tflops / MFMA_F16_PEAK_TFLOPS * 100:.1f}% of the fp16 MFMA peak)",
           file=sys.stderr, flush=True)
@@ -221,7 +252,7 @@ def bench_prefill(args):
         "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "f16", "data": "synthetic",
         "config": {"workload": f"packed varlen causal prefill, {len(seqlens)} sequences x {seqlens[0]} tokens, "
-                               f"{hq}q/{hkv}kv heads d64 fp16", "sequences": len(seqlens),
+                               f"{hq}q/{hkv}kv heads d{D} fp16", "sequences": len(seqlens),
                    "seq_len": seqlens[0]},
         "roofline": {"bound": "mfma", "achieved": round(tflops, 1), "peak": MFMA_F16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tflops / MFMA_F16_PEAK_TFLOPS, 4), "traffic": None,
@@ -242,7 +273,7 @@ def chunk_flops(prefixes, chunks, hq, d):
 def bench_chunked_prefill(args):
     """Chunked prefill into a shared prefix: 16 requests forked from one 2048-token prompt
     (copy-on-write blocks), each prefilling its own 512-token chunk against the paged cache;
-    the model's 14 query / 2 KV heads, fp16."""
+    the model's 14 query / 2 KV heads of d 64 (or the --shape's heads), fp16."""
     import numpy as np
     import torch
 
@@ -254,7 +285,7 @@ def bench_chunked_prefill(args):
     nblocks = prefix // BLOCK + B * (chunk // BLOCK) + 64
     pool = kvp.BlockPool(nblocks)
     pool.set_free_order(W.free_list_permutation(nblocks, args.seed + 1).tolist())
-    cache = kvp.PagedKVCache(1, nblocks, HQ, HKV, torch.float16, "cuda")
+    cache = kvp.PagedKVCache(1, nblocks, HQ, HKV, torch.float16, "cuda", head_dim=D)
     cache.k_pool.copy_(W.randn_device(cache.k_pool.shape, args.seed + 10, torch.float16, "cuda"))
     cache.v_pool.copy_(W.randn_device(cache.v_pool.shape, args.seed + 11, torch.float16, "cuda"))
     base = pool.alloc(prefix)
@@ -308,7 +339,7 @@ def bench_chunked_prefill(args):
         "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "f16", "data": "synthetic",
         "config": {"workload": f"{B} requests forked from one {prefix}-token prompt, {chunk}-token chunk each, "
-                               f"{HQ}q/{HKV}kv heads d64 fp16, 16-token blocks", "requests": B,
+                               f"{HQ}q/{HKV}kv heads d{D} fp16, 16-token blocks", "requests": B,
                    "prefix": prefix, "chunk": chunk},
         "roofline": {"bound": "mfma", "achieved": round(tflops, 1), "peak": MFMA_F16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tflops / MFMA_F16_PEAK_TFLOPS, 4), "traffic": None,
@@ -325,9 +356,11 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--batch", type=int, default=200)
-    ap.add_argument("--layers", type=int, default=24)
+    ap.add_argument("--layers", type=int, default=None, help="default: the shape's layer count")
+    ap.add_argument("--shape", choices=sorted(SHAPES), default=DEFAULT_SHAPE,
+                    help="decode head shape (default 14q2kv_d64)")
     ap.add_argument("--kernel-reps", type=int, default=4, help="rounds of per-layer decode timing")
-    ap.add_argument("--no-graph", action="store_true", help="launch the 24 layers eagerly")
+    ap.add_argument("--no-graph", action="store_true", help="launch the layers eagerly")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-share", action="store_true", help="plans without shared-prefix items")
     ap.add_argument("--seed", type=int, default=42)
@@ -341,6 +374,7 @@ def main():
         print(f"bench.py runs on one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}). "
               "Requests would be sharded across GPUs by whole sharing groups.", flush=True)
         sys.exit(2)
+    set_shape(args.shape)
     if args.workload == "prefill":
         bench_prefill(args)
         return
@@ -357,7 +391,8 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
     dev = "cuda"
-    B, L = args.batch, args.layers
+    set_shape(args.shape)
+    B, L = args.batch, (args.layers if args.layers is not None else SHAPES[args.shape][0])
     total_steps = args.warmup + args.steps + 1
     t_setup = time.perf_counter()
     pb, pool, cache, seqs, max_blocks = build_state(kvp, torch, W, B, L, total_steps, args.seed)
@@ -382,9 +417,9 @@ def main():
     cows = (kvp.kvp_copy * B)()
     pool.export_raw(ids.data_ptr(), B, max_blocks, t0h.data_ptr(), c0h.data_ptr())
     c0h += total_steps + 1  # the longest contexts of this run (plan sizing only)
-    plan0, _ = kvp.decode_plan_build(HQ, HKV, t0h, c0h, cache.num_blocks, share_prefix=share)
+    plan0, _ = kvp.decode_plan_build(HQ, HKV, t0h, c0h, cache.num_blocks, share_prefix=share, head_dim=D)
     pad_items = plan0.n_items + 8 * 32  # room for one more round of CU slots per XCD queue
-    img_bytes = kvp.decode_plan_bytes(HQ, HKV, B, max_blocks, pad_items)
+    img_bytes = kvp.decode_plan_bytes(HQ, HKV, B, max_blocks, pad_items, head_dim=D)
     hb = [dict(table=torch.empty((B, max_blocks), dtype=torch.int32).pin_memory(),
                ctx=torch.empty((B,), dtype=torch.int32).pin_memory(),
                slots=torch.empty((B,), dtype=torch.int64).pin_memory(),
@@ -394,7 +429,7 @@ def main():
     plan_d = torch.empty((img_bytes,), dtype=torch.uint8, device=dev)
     slot_cap = 2 * plan0.n_slots + B * HKV
     ws_plan = kvp.kvp_decode_plan()
-    ws_plan.B, ws_plan.num_kv_heads, ws_plan.n_slots = B, HKV, slot_cap
+    ws_plan.B, ws_plan.num_kv_heads, ws_plan.n_slots, ws_plan.head_dim = B, HKV, slot_cap, D
     ws = torch.zeros((max(kvp.decode_plan_workspace_bytes(ws_plan), 256),), dtype=torch.uint8, device=dev)
     done = [torch.cuda.Event(), torch.cuda.Event()]
     stream = torch.cuda.current_stream()
@@ -422,7 +457,7 @@ def main():
                 npairs += 1
         pool.export_raw(ids.data_ptr(), B, max_blocks, h["table"].data_ptr(), h["ctx"].data_ptr())
         plan, _ = kvp.decode_plan_build(HQ, HKV, h["table"], h["ctx"], cache.num_blocks, share_prefix=share,
-                                        image=h["image"], pad_items=pad_items, plan=h["plan"])
+                                        image=h["image"], pad_items=pad_items, plan=h["plan"], head_dim=D)
         if launch_plan[0] is None:  # the launch arguments: this layout, slots up to slot_cap
             launch_plan[0] = kvp.kvp_decode_plan.from_buffer_copy(plan)
             launch_plan[0].n_slots = slot_cap
@@ -499,7 +534,7 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(W)
+        cpu = cpu_baseline(W, L)
         print(f"[bench] cpu oracle {cpu}", file=sys.stderr, flush=True)
 
     line = {
@@ -515,17 +550,18 @@ def main():
         "vs_baseline": None,
         "dtype": "f16",
         "data": "synthetic",
-        "config": {"workload": f"paged GQA decode step, batch {B}, 24 layers x fused (append + paged decode), "
-                               "14q/2kv heads d64 fp16, 16-token blocks, contexts U{128..2048}, "
+        "config": {"workload": f"paged GQA decode step, batch {B}, {L} layers x fused (append + paged decode), "
+                               f"{HQ}q/{HKV}kv heads d{D} fp16, 16-token blocks, contexts U{{128..2048}}, "
                                "groups of 8 sharing a 512-token prefix (copy-on-write)",
-                   "batch": B, "layers": L, "graph": graph is not None},
+                   "batch": B, "layers": L, "shape": args.shape, "graph": graph is not None},
         "steps_per_sec": round(1e3 / ms_per_step, 2),
         "hbm_pct": round(value / HBM_PEAK_GBPS * 100, 2),
         "logical_GBps": round(logical_gbps, 2),
         "unique_GB_per_step": round(uniq_bytes_step / 1e9, 4),
         "logical_GB_per_step": round(logical_bytes_step / 1e9, 4),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": measured_traffic(),
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "traffic": measured_traffic() if args.shape == DEFAULT_SHAPE and B == 200 else None,
                      "traffic_unit": "bytes per launch (HBM read + write, counters)",
                      "kernel": "paged_decode_attention_planned (decode_f16_kernel: append + attention + "
                                "split merge)",
