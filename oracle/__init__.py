@@ -10,6 +10,8 @@ Contents
   * brute.py   : an independent pure-Python brute force (math.fsum) for tiny shapes.
   * pagepool.py: the block pool / block table / copy-on-write model.
   * opcount.py : the multiply-accumulate cost model of cached vs uncached generation.
+  * kvquant.py : symmetric absmax quantization of cache rows (int8 codes, fp16 scale per
+                 row) and its exact reconstruction.
 
 Parity status: every function here is pinned by a CPU test (see tests/test_oracle_*.py);
 none is "parity unpinned".
