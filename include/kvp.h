@@ -30,8 +30,11 @@
  *     before anything is enqueued.
  *   - Host objects (kvp_pool) are owned by the library and freed by block_pool_destroy.
  *     A pool is not thread-safe: one owner thread at a time.
- *   - Layouts: head_dim d = 64.  dtype is fp16 (KVP_F16) or fp32 (KVP_F32).
+ *   - Layouts: head_dim d = 64, or 128 with fp16 or int8.  dtype is fp16 (KVP_F16), fp32
+ *     (KVP_F32) or int8 codes with one fp16 scale per row (KVP_I8, paged caches only; q,
+ *     out and appended rows are then fp16).
  *       paged K/V pool, one per K and V:  [num_layers][num_blocks][H_kv][block_size][d]
+ *       int8 scale pool, one per K and V:   fp16 [num_layers][num_blocks][H_kv][block_size]
  *       contiguous cache (one layer):       [B][H_kv][Lmax][d]
  *       decode q / out:                     [B][H_q][d]
  *       packed prefill q / out:             [T][H_q][d];  k, v: [T][H_kv][d]
@@ -61,22 +64,30 @@ typedef int32_t kvp_status;
 #define KVP_ERR_HIP (-4)         /* the HIP runtime reported an error on launch     */
 #define KVP_ERR_UNSUPPORTED (-5) /* valid request this build does not implement     */
 
-enum { KVP_F16 = 0, KVP_F32 = 1 };
+enum { KVP_F16 = 0, KVP_F32 = 1, KVP_I8 = 2 };
 
 typedef struct {
     int32_t num_layers;
     int32_t num_q_heads;
     int32_t num_kv_heads; /* num_q_heads % num_kv_heads == 0            */
-    int32_t head_dim;     /* 64                                         */
-    int32_t dtype;        /* KVP_F16 or KVP_F32                          */
+    int32_t head_dim;     /* 64, or 128 (fp16 / int8)                   */
+    int32_t dtype;        /* KVP_F16, KVP_F32 or KVP_I8                  */
 } kvp_dims;
 
+/* Quantized cache rows (KVP_I8; [CHAP] quantization section, symmetric absmax, applied to
+ * the cache): each (token, KV head) row x of d values of K, and separately of V, is stored
+ * as int8 codes and one fp16 scale: scale = fp16(max|x| / 127) (fp32 quotient rounded to
+ * nearest even), code = clamp(rint(x / scale), -128, 127) in fp32 with the stored scale
+ * (round half to even), all codes 0 when the scale is 0.  Reconstruction: code * scale. */
 typedef struct {
     kvp_dims dims;
     int32_t block_size; /* tokens per block: 16                          */
     int32_t num_blocks;
     void *k_pool; /* device [num_layers][num_blocks][H_kv][block_size][d] */
     void *v_pool; /* device, same shape                                   */
+    void *k_scale; /* KVP_I8: device fp16 [num_layers][num_blocks][H_kv][block_size];
+                      NULL otherwise                                      */
+    void *v_scale; /* KVP_I8: same, for V                                 */
 } kvp_cache_desc;
 
 /* Thread-local description of the last error on this thread ("" if none). */
@@ -143,7 +154,7 @@ kvp_status block_table_reserve(kvp_pool *pool, int32_t seq, int32_t n, int64_t *
 kvp_status block_table_fork(kvp_pool *pool, int32_t parent, int32_t *child);
 
 /* Copy-on-write of one logical block: if its block is shared, take a new block, release
- * the old one and point the table at the new one; *src/*dst report the pair to copy on the
+ * the old one and point the table at the new one; *src and *dst report the pair to copy on the
  * device.  If the block is private, *src = *dst = that block (nothing to do). */
 kvp_status block_table_cow(kvp_pool *pool, int32_t seq, int32_t logical_block, int32_t *src,
                            int32_t *dst);
@@ -185,15 +196,17 @@ int64_t kv_bytes_per_token(int32_t num_layers, int32_t num_kv_heads, int32_t hea
  * ==================================================================================== */
 
 /* Copy whole blocks for copy-on-write: for each pair p < n, block d_pairs[2p] is copied to
- * block d_pairs[2p+1] in every layer, in both K and V pools, bit for bit ([PAGED] 3).
+ * block d_pairs[2p+1] in every layer, in both K and V pools (and, for an int8 cache, in
+ * both scale pools), bit for bit ([PAGED] 3).
  * d_pairs: device int32 [n][2].  n == 0 is a no-op. */
 kvp_status kv_copy_blocks(const kvp_cache_desc *cache, const int32_t *d_pairs, int32_t n,
                           kvp_stream stream);
 
 /* Write n new tokens' keys and values of one layer into their slots ([KVES] step 2:
  * k_t, v_t go to the end of each head's cache).  k, v: device [n][H_kv][d] in the cache
- * dtype; d_slots: device int64 [n] (slot = block * block_size + offset, every slot
- * < num_blocks * block_size, distinct).  Bit-exact copy. */
+ * dtype (fp16 for an int8 cache); d_slots: device int64 [n] (slot = block * block_size +
+ * offset, every slot < num_blocks * block_size, distinct).  Bit-exact copy; an int8 cache
+ * stores each row's codes and scale (quantized as described at kvp_cache_desc). */
 kvp_status kv_append(const kvp_cache_desc *cache, int32_t layer, const void *k, const void *v,
                      const int64_t *d_slots, int32_t n, kvp_stream stream);
 
@@ -213,7 +226,8 @@ size_t decode_workspace_bytes(const kvp_dims *dims, int32_t B, int32_t max_conte
  *   out[b][h] = sum_j softmax_j(scale * q[b][h] . k_j) v_j over j < d_context_lens[b],
  * k_j / v_j read from block d_block_table[b][j / block_size], offset j % block_size, KV
  * head h / (H_q / H_kv).  The token of this step must already be appended.
- *   q, out: device [B][H_q][d] in the cache dtype.  d_block_table: device int32
+ *   q, out: device [B][H_q][d] in the cache dtype (fp16 for an int8 cache, whose rows are
+ *   reconstructed as code * scale inside the kernel).  d_block_table: device int32
  *   [B][max_blocks].  d_context_lens: device int32 [B], each in 1..max_blocks*block_size.
  *   scale: 0 means 1/sqrt(d).  workspace: device, at least
  *   decode_workspace_bytes(dims, B, max_blocks * block_size) bytes (may be NULL if that is
@@ -237,7 +251,8 @@ kvp_status paged_decode_attention(const kvp_cache_desc *cache, int32_t layer, vo
  * are written into the cache at position d_context_lens[b] - 1 (through the block table; that
  * block must be private to the request, i.e. copy-on-write already done) and the attention
  * of the same call already sees them.  Equivalent to kv_append at those slots followed by
- * paged_decode_attention, in one kernel.  fp16 only (UNSUPPORTED otherwise). */
+ * paged_decode_attention, in one kernel.  fp16 or int8 caches (the kernel quantizes the
+ * new rows exactly as kv_append does); UNSUPPORTED for fp32. */
 kvp_status paged_decode_append_attention(const kvp_cache_desc *cache, int32_t layer, void *out,
                                          const void *q, const void *k_new, const void *v_new,
                                          const int32_t *d_block_table, int32_t max_blocks,
@@ -247,7 +262,7 @@ kvp_status paged_decode_append_attention(const kvp_cache_desc *cache, int32_t la
 /* The same decode over a contiguous cache k_cache / v_cache [B][H_kv][Lmax][d] (one layer;
  * the layout of the cache tensors in [CHAP]'s allocator check).  Same kernels, same split
  * policy and the same arithmetic order as the paged call, so the outputs of the two are
- * bit-identical for the same logical data. */
+ * bit-identical for the same logical data.  fp16 and fp32 (UNSUPPORTED for int8). */
 kvp_status contiguous_decode_attention(const kvp_dims *dims, void *out, const void *q,
                                        const void *k_cache, const void *v_cache, int32_t Lmax,
                                        const int32_t *d_context_lens, int32_t B, float scale,
@@ -296,8 +311,8 @@ size_t decode_plan_bytes(const kvp_dims *dims, int32_t B, int32_t max_blocks, in
  * graph can be replayed with a new image in the same device buffer); INVALID if the step
  * needs more items.  h_image: host buffer of image_bytes >= decode_plan_bytes(...)
  * receiving the image; the caller copies plan->bytes of it to device memory (16-byte
- * aligned) before the decode.  UNSUPPORTED for fp32 (the planned kernel is fp16) or a
- * group size above 8. */
+ * aligned) before the decode.  UNSUPPORTED for fp32 (the planned kernel serves fp16 and
+ * int8 caches) or a group size above 8. */
 kvp_status decode_plan_build(const kvp_dims *dims, const int32_t *h_block_table,
                              int32_t max_blocks, const int32_t *h_context_lens, int32_t B,
                              int32_t num_blocks, uint32_t flags, int32_t pad_items,
@@ -364,7 +379,8 @@ kvp_status varlen_causal_prefill(const kvp_dims *dims, void *out, const void *q,
 
 /* Gather one layer of the paged cache back to the contiguous layout: positions
  * j < d_context_lens[b] of k_out / v_out [B][H_kv][Lmax][d] receive the paged rows, bit for
- * bit; other positions are left untouched. */
+ * bit; other positions are left untouched.  For an int8 cache the rows are the codes (the
+ * scales stay in the scale pools). */
 kvp_status kv_gather(const kvp_cache_desc *cache, int32_t layer, const int32_t *d_block_table,
                      int32_t max_blocks, const int32_t *d_context_lens, int32_t B, int32_t Lmax,
                      void *k_out, void *v_out, kvp_stream stream);

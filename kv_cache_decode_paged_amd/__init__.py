@@ -31,6 +31,7 @@ _STATUS = {KVP_ERR_INVALID: "INVALID", KVP_ERR_OOM: "OOM", KVP_ERR_NOT_FOUND: "N
            KVP_ERR_HIP: "HIP", KVP_ERR_UNSUPPORTED: "UNSUPPORTED"}
 KVP_F16 = 0
 KVP_F32 = 1
+KVP_I8 = 2
 BLOCK = 16
 HEAD_DIM = 64
 
@@ -53,7 +54,8 @@ class kvp_dims(ctypes.Structure):
 
 class kvp_cache_desc(ctypes.Structure):
     _fields_ = [("dims", kvp_dims), ("block_size", ctypes.c_int32), ("num_blocks", ctypes.c_int32),
-                ("k_pool", ctypes.c_void_p), ("v_pool", ctypes.c_void_p)]
+                ("k_pool", ctypes.c_void_p), ("v_pool", ctypes.c_void_p),
+                ("k_scale", ctypes.c_void_p), ("v_scale", ctypes.c_void_p)]
 
 
 class kvp_copy(ctypes.Structure):
@@ -157,12 +159,12 @@ def lib():
 # ---------------------------------------------------------------------------------------
 # tensors and streams
 # ---------------------------------------------------------------------------------------
-_DT = {torch.float16: KVP_F16, torch.float32: KVP_F32}
+_DT = {torch.float16: KVP_F16, torch.float32: KVP_F32, torch.int8: KVP_I8}
 
 
 def _dtype_code(dt):
     if dt not in _DT:
-        raise TypeError(f"unsupported dtype {dt} (float16 or float32)")
+        raise TypeError(f"unsupported dtype {dt} (float16, float32 or int8)")
     return _DT[dt]
 
 
@@ -192,7 +194,10 @@ def dims(num_layers, num_q_heads, num_kv_heads, dtype, head_dim=HEAD_DIM):
 
 class PagedKVCache:
     """K and V pools of shape [num_layers][num_blocks][H_kv][16][head_dim] in device memory
-    (owned by the torch tensors held here); head_dim 64 or 128."""
+    (owned by the torch tensors held here); head_dim 64 or 128.  dtype torch.int8 holds
+    quantized rows: int8 code pools plus fp16 scale pools k_scale / v_scale of shape
+    [num_layers][num_blocks][H_kv][16]; q, out and appended rows are then fp16
+    (`io_dtype`)."""
 
     def __init__(self, num_layers, num_blocks, num_q_heads, num_kv_heads, dtype=torch.float16,
                  device="cuda", k_pool=None, v_pool=None, head_dim=HEAD_DIM):
@@ -203,11 +208,18 @@ class PagedKVCache:
             if tuple(t.shape) != shape:
                 raise ValueError(f"{n} must have shape {shape}")
             _dev(t, n, dtype)
+        self.k_scale = self.v_scale = None
+        if dtype == torch.int8:
+            self.k_scale = torch.empty(shape[:-1], dtype=torch.float16, device=device)
+            self.v_scale = torch.empty(shape[:-1], dtype=torch.float16, device=device)
         self.num_layers, self.num_blocks = num_layers, num_blocks
         self.num_q_heads, self.num_kv_heads, self.dtype = num_q_heads, num_kv_heads, dtype
+        self.io_dtype = torch.float16 if dtype == torch.int8 else dtype
         self.head_dim = head_dim
         self.desc = kvp_cache_desc(dims(num_layers, num_q_heads, num_kv_heads, dtype, head_dim), BLOCK,
-                                   num_blocks, self.k_pool.data_ptr(), self.v_pool.data_ptr())
+                                   num_blocks, self.k_pool.data_ptr(), self.v_pool.data_ptr(),
+                                   self.k_scale.data_ptr() if self.k_scale is not None else None,
+                                   self.v_scale.data_ptr() if self.v_scale is not None else None)
 
     @property
     def dims(self):
@@ -352,12 +364,13 @@ def kv_copy_blocks(cache: PagedKVCache, pairs, stream=None):
 
 
 def kv_append(cache: PagedKVCache, layer, k, v, slots, stream=None):
-    """k, v: device [n, H_kv, head_dim] in the cache dtype; slots: device int64 [n]."""
+    """k, v: device [n, H_kv, head_dim] in the cache dtype (fp16 for an int8 cache, which
+    stores each row's codes and scale); slots: device int64 [n]."""
     n = k.shape[0]
     if v.shape != k.shape or k.shape[1:] != (cache.num_kv_heads, cache.head_dim) or slots.shape != (n,):
         raise ValueError("kv_append: shape mismatch")
-    _check(_lib.kv_append(ctypes.byref(cache.desc), int(layer), _dev(k, "k", cache.dtype),
-                          _dev(v, "v", cache.dtype), _dev(slots, "slots", torch.int64), n,
+    _check(_lib.kv_append(ctypes.byref(cache.desc), int(layer), _dev(k, "k", cache.io_dtype),
+                          _dev(v, "v", cache.io_dtype), _dev(slots, "slots", torch.int64), n,
                           _stream(stream)))
 
 
@@ -398,8 +411,8 @@ def paged_decode_attention(cache: PagedKVCache, layer, q, block_table, context_l
         out = torch.empty_like(q)
     if workspace is None:
         workspace = make_workspace(hq, cache.num_kv_heads, cache.dtype, B, max_blocks * BLOCK, q.device, d)
-    _check(_lib.paged_decode_attention(ctypes.byref(cache.desc), int(layer), _dev(out, "out", cache.dtype),
-                                       _dev(q, "q", cache.dtype), _dev(block_table, "block_table", torch.int32),
+    _check(_lib.paged_decode_attention(ctypes.byref(cache.desc), int(layer), _dev(out, "out", cache.io_dtype),
+                                       _dev(q, "q", cache.io_dtype), _dev(block_table, "block_table", torch.int32),
                                        max_blocks, _dev(context_lens, "context_lens", torch.int32), B,
                                        float(scale), _dev(workspace, "workspace"), workspace.numel(),
                                        _stream(stream)))
@@ -422,9 +435,9 @@ def paged_decode_append_attention(cache: PagedKVCache, layer, q, k_new, v_new, b
         out = torch.empty_like(q)
     if workspace is None:
         workspace = make_workspace(hq, cache.num_kv_heads, cache.dtype, B, max_blocks * BLOCK, q.device, d)
-    _check(_lib.paged_decode_append_attention(ctypes.byref(cache.desc), int(layer), _dev(out, "out", cache.dtype),
-                                              _dev(q, "q", cache.dtype), _dev(k_new, "k_new", cache.dtype),
-                                              _dev(v_new, "v_new", cache.dtype),
+    _check(_lib.paged_decode_append_attention(ctypes.byref(cache.desc), int(layer), _dev(out, "out", cache.io_dtype),
+                                              _dev(q, "q", cache.io_dtype), _dev(k_new, "k_new", cache.io_dtype),
+                                              _dev(v_new, "v_new", cache.io_dtype),
                                               _dev(block_table, "block_table", torch.int32), max_blocks,
                                               _dev(context_lens, "context_lens", torch.int32), B, float(scale),
                                               _dev(workspace, "workspace"), workspace.numel(), _stream(stream)))
@@ -494,10 +507,10 @@ def paged_decode_attention_planned(cache: PagedKVCache, layer, q, plan, d_plan, 
         out = torch.empty_like(q)
     if workspace is None:
         workspace = make_plan_workspace(plan, q.device)
-    kn = _dev(k_new, "k_new", cache.dtype) if k_new is not None else None
-    vn = _dev(v_new, "v_new", cache.dtype) if v_new is not None else None
-    _check(_lib.paged_decode_attention_planned(ctypes.byref(cache.desc), int(layer), _dev(out, "out", cache.dtype),
-                                               _dev(q, "q", cache.dtype), kn, vn, ctypes.byref(plan),
+    kn = _dev(k_new, "k_new", cache.io_dtype) if k_new is not None else None
+    vn = _dev(v_new, "v_new", cache.io_dtype) if v_new is not None else None
+    _check(_lib.paged_decode_attention_planned(ctypes.byref(cache.desc), int(layer), _dev(out, "out", cache.io_dtype),
+                                               _dev(q, "q", cache.io_dtype), kn, vn, ctypes.byref(plan),
                                                _dev(d_plan, "plan"), float(scale), _dev(workspace, "workspace"),
                                                workspace.numel(), _stream(stream)))
     return out
@@ -517,8 +530,8 @@ def paged_prefill_attention(cache: PagedKVCache, layer, q, block_table, context_
         raise ValueError("paged_prefill_attention: table / context_lens / cu_q shape mismatch")
     if out is None:
         out = torch.empty_like(q)
-    _check(_lib.paged_prefill_attention(ctypes.byref(cache.desc), int(layer), _dev(out, "out", cache.dtype),
-                                        _dev(q, "q", cache.dtype),
+    _check(_lib.paged_prefill_attention(ctypes.byref(cache.desc), int(layer), _dev(out, "out", cache.io_dtype),
+                                        _dev(q, "q", cache.io_dtype),
                                         _dev(block_table, "block_table", torch.int32), int(block_table.shape[1]),
                                         _dev(context_lens, "context_lens", torch.int32),
                                         _dev(cu_q, "cu_q", torch.int32), B, int(max_q), float(scale),

@@ -23,6 +23,9 @@ def hip_flags():
             # MFMA accumulators in ordinary VGPRs: no copies between accumulation registers
             # and VGPRs around the VALU work on scores and outputs
             "-mllvm", "-amdgpu-mfma-vgpr-form",
+            # fp32 division and square root correctly rounded (the int8 codes are decided by
+            # an fp32 division and must match the definition bit for bit)
+            "-fhip-fp32-correctly-rounded-divide-sqrt",
             "-I", os.path.join(ROOT, "include"), "-I", CSRC]
 
 

@@ -1,6 +1,7 @@
 // kvp_cache_ops.hip -- data movement of the paged KV cache on gfx950: append of new
 // tokens into their slots, whole-block copies for copy-on-write, the paged -> contiguous
-// gather, and the contiguous-layout append.  All are bit-exact 16-byte copies.
+// gather, and the contiguous-layout append.  All are bit-exact 16-byte copies, except the
+// append into an int8 cache, which quantizes each row (kvp_quant.h).
 //
 //   gustavoai "La cache de claves y valores", four-step token recipe, step 2: the new
 //   token's k_t and v_t go to the end of each head's cache.
@@ -13,6 +14,7 @@
 #include <hip/hip_runtime.h>
 
 #include "kvp_internal.h"
+#include "kvp_quant.h"
 
 namespace kvp {
 
@@ -33,8 +35,10 @@ static kvp_status check_cache(const kvp_cache_desc *c, const char *who)
                     d.num_q_heads, d.num_kv_heads);
     if (!head_dim_ok(d.head_dim))
         return fail(KVP_ERR_UNSUPPORTED, "%s: head_dim=%d (64 or 128)", who, d.head_dim);
-    if (d.dtype != KVP_F16 && d.dtype != KVP_F32)
+    if (d.dtype != KVP_F16 && d.dtype != KVP_F32 && d.dtype != KVP_I8)
         return fail(KVP_ERR_INVALID, "%s: dtype=%d", who, d.dtype);
+    if (d.dtype == KVP_I8 && (!c->k_scale || !c->v_scale || (((uintptr_t)c->k_scale | (uintptr_t)c->v_scale) & 15)))
+        return fail(KVP_ERR_INVALID, "%s: an int8 cache needs 16-byte aligned scale pools", who);
     if (c->block_size != BS)
         return fail(KVP_ERR_UNSUPPORTED, "%s: block_size=%d (only 16)", who, c->block_size);
     if (c->num_blocks <= 0 || !c->k_pool || !c->v_pool)
@@ -45,7 +49,8 @@ static kvp_status check_cache(const kvp_cache_desc *c, const char *who)
 }
 
 // 16-byte chunks of one (token, head) row
-static inline int chunks_per_row(const kvp_dims &d) { return d.head_dim * (d.dtype == KVP_F16 ? 2 : 4) / 16; }
+static inline int elem_bytes(int dtype) { return dtype == KVP_F32 ? 4 : dtype == KVP_F16 ? 2 : 1; }
+static inline int chunks_per_row(const kvp_dims &d) { return d.head_dim * elem_bytes(d.dtype) / 16; }
 
 static kvp_status launched(const char *who)
 {
@@ -79,15 +84,55 @@ __global__ __launch_bounds__(256) void append_kernel(i32x4 *__restrict__ kpool,
     vpool[dst] = v[idx];
 }
 
-// grid = (pairs, layers, 2 pools); each workgroup copies one block of one layer
-__global__ __launch_bounds__(256) void copy_blocks_kernel(i32x4 *__restrict__ kpool,
-                                                          i32x4 *__restrict__ vpool,
-                                                          const int *__restrict__ pairs,
-                                                          int num_blocks, int64_t block_chunks,
-                                                          int64_t layer_chunks)
+// int8 cache: thread = 8 values of one (token, head) row, for K and V; the CPR threads of a
+// row are an aligned lane group that exchanges the row maximum
+template <int CPR>
+__global__ __launch_bounds__(256) void append_i8_kernel(char *__restrict__ kpool, char *__restrict__ vpool,
+                                                        qf16 *__restrict__ kscale, qf16 *__restrict__ vscale,
+                                                        const qf16 *__restrict__ k, const qf16 *__restrict__ v,
+                                                        const int64_t *__restrict__ slots, int n, int hkv,
+                                                        int64_t num_slots)
+{
+    constexpr int D = CPR * 8;
+    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t row = idx / CPR; // (token, head)
+    const int piece = (int)(idx % CPR);
+    const bool valid = row < (int64_t)n * hkv;
+    const int tok = valid ? (int)(row / hkv) : 0, h = valid ? (int)(row % hkv) : 0;
+    const int64_t slot = valid ? slots[tok] : -1;
+    const bool ok = slot >= 0 && slot < num_slots;
+    const qf16x8 z = {0, 0, 0, 0, 0, 0, 0, 0};
+    const size_t src = ((size_t)tok * hkv + h) * D + piece * 8;
+    const qf16x8 xk = valid ? *(const qf16x8 *)(k + src) : z;
+    const qf16x8 xv = valid ? *(const qf16x8 *)(v + src) : z;
+    u32x2 ck, cvv;
+    const qf16 sk = quantize_row_piece<CPR>(xk, ck); // every lane takes part in the exchange
+    const qf16 sv = quantize_row_piece<CPR>(xv, cvv);
+    if (!ok)
+        return;
+    const int64_t blk = slot / BS, off = slot % BS;
+    const int64_t dst = (blk * hkv + h) * BS + off; // row index in the pool
+    *(u32x2 *)(kpool + dst * D + piece * 8) = ck;
+    *(u32x2 *)(vpool + dst * D + piece * 8) = cvv;
+    if (piece == 0) {
+        kscale[dst] = sk;
+        vscale[dst] = sv;
+    }
+}
+
+// grid = (pairs, layers, pools): pools 0 / 1 are K / V (block_chunks[0] chunks per block),
+// 2 / 3 the int8 scale pools (block_chunks[1]); each workgroup copies one block of one layer
+struct CopyPools {
+    i32x4 *pool[4];
+    int64_t block_chunks[2];
+};
+__global__ __launch_bounds__(256) void copy_blocks_kernel(CopyPools C, const int *__restrict__ pairs,
+                                                          int num_blocks)
 {
     const int p = blockIdx.x, layer = blockIdx.y;
-    i32x4 *pool = blockIdx.z == 0 ? kpool : vpool;
+    i32x4 *pool = C.pool[blockIdx.z];
+    const int64_t block_chunks = C.block_chunks[blockIdx.z >> 1];
+    const int64_t layer_chunks = block_chunks * num_blocks;
     const int src = pairs[2 * p], dst = pairs[2 * p + 1];
     if (src < 0 || src >= num_blocks || dst < 0 || dst >= num_blocks || src == dst)
         return;
@@ -173,6 +218,26 @@ kvp_status kv_append(const kvp_cache_desc *cache, int32_t layer, const void *k, 
     const int nch = chunks_per_row(cache->dims);
     const int hkv = cache->dims.num_kv_heads;
     const int64_t layer_chunks = (int64_t)cache->num_blocks * hkv * BS * nch;
+    if (cache->dims.dtype == KVP_I8) {
+        const int d = cache->dims.head_dim;
+        const int64_t rows = (int64_t)cache->num_blocks * hkv * BS; // rows per layer
+        const int64_t total = (int64_t)n * hkv * (d / 8);
+        const int64_t blocks = (total + 255) / 256;
+        if (blocks > 0x7fffffff)
+            return fail(KVP_ERR_UNSUPPORTED, "kv_append: n too large");
+        char *kp = (char *)cache->k_pool + layer * rows * d;
+        char *vp = (char *)cache->v_pool + layer * rows * d;
+        qf16 *ks = (qf16 *)cache->k_scale + layer * rows;
+        qf16 *vs = (qf16 *)cache->v_scale + layer * rows;
+        const int64_t num_slots = (int64_t)cache->num_blocks * BS;
+        if (d == 64)
+            hipLaunchKernelGGL(append_i8_kernel<8>, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream, kp,
+                               vp, ks, vs, (const qf16 *)k, (const qf16 *)v, d_slots, n, hkv, num_slots);
+        else
+            hipLaunchKernelGGL(append_i8_kernel<16>, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream, kp,
+                               vp, ks, vs, (const qf16 *)k, (const qf16 *)v, d_slots, n, hkv, num_slots);
+        return launched("kv_append");
+    }
     i32x4 *kp = (i32x4 *)cache->k_pool + layer * layer_chunks;
     i32x4 *vp = (i32x4 *)cache->v_pool + layer * layer_chunks;
     const int64_t total = (int64_t)n * hkv * nch;
@@ -200,11 +265,16 @@ kvp_status kv_copy_blocks(const kvp_cache_desc *cache, const int32_t *d_pairs, i
     if (n > 0x7fffffff / 1 || cache->dims.num_layers > 65535)
         return fail(KVP_ERR_UNSUPPORTED, "kv_copy_blocks: too many pairs or layers");
     const int nch = chunks_per_row(cache->dims);
-    const int64_t block_chunks = (int64_t)cache->dims.num_kv_heads * BS * nch;
-    const int64_t layer_chunks = block_chunks * cache->num_blocks;
-    hipLaunchKernelGGL(copy_blocks_kernel, dim3(n, cache->dims.num_layers, 2), dim3(256), 0,
-                       (hipStream_t)stream, (i32x4 *)cache->k_pool, (i32x4 *)cache->v_pool,
-                       d_pairs, cache->num_blocks, block_chunks, layer_chunks);
+    const bool i8 = cache->dims.dtype == KVP_I8;
+    CopyPools C;
+    C.pool[0] = (i32x4 *)cache->k_pool;
+    C.pool[1] = (i32x4 *)cache->v_pool;
+    C.pool[2] = i8 ? (i32x4 *)cache->k_scale : nullptr;
+    C.pool[3] = i8 ? (i32x4 *)cache->v_scale : nullptr;
+    C.block_chunks[0] = (int64_t)cache->dims.num_kv_heads * BS * nch;
+    C.block_chunks[1] = (int64_t)cache->dims.num_kv_heads * BS * 2 / 16; // fp16 scales
+    hipLaunchKernelGGL(copy_blocks_kernel, dim3(n, cache->dims.num_layers, i8 ? 4 : 2), dim3(256), 0,
+                       (hipStream_t)stream, C, d_pairs, cache->num_blocks);
     return launched("kv_copy_blocks");
 }
 
@@ -246,6 +316,8 @@ kvp_status contiguous_kv_append(const kvp_dims *dims, void *k_cache, void *v_cac
         return fail(KVP_ERR_INVALID, "contiguous_kv_append: dims is NULL");
     if (!head_dim_ok(dims->head_dim))
         return fail(KVP_ERR_UNSUPPORTED, "contiguous_kv_append: head_dim=%d (64 or 128)", dims->head_dim);
+    if (dims->dtype == KVP_I8)
+        return fail(KVP_ERR_UNSUPPORTED, "contiguous_kv_append: int8 caches are paged only");
     if ((dims->dtype != KVP_F16 && dims->dtype != KVP_F32) || dims->num_kv_heads <= 0 || B < 0 ||
         Lmax <= 0)
         return fail(KVP_ERR_INVALID, "contiguous_kv_append: bad arguments");

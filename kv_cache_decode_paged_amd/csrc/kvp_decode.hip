@@ -26,10 +26,10 @@ static kvp_status check_dims(const kvp_dims *d, const char *who)
     if (d->num_q_heads <= 0 || d->num_kv_heads <= 0 || d->num_q_heads % d->num_kv_heads != 0)
         return fail(KVP_ERR_INVALID, "%s: num_q_heads=%d must be a positive multiple of num_kv_heads=%d",
                     who, d->num_q_heads, d->num_kv_heads);
-    if (d->dtype != KVP_F16 && d->dtype != KVP_F32)
+    if (d->dtype != KVP_F16 && d->dtype != KVP_F32 && d->dtype != KVP_I8)
         return fail(KVP_ERR_INVALID, "%s: dtype=%d", who, d->dtype);
-    if (d->head_dim != D && !(d->dtype == KVP_F16 && d->head_dim == 128))
-        return fail(KVP_ERR_UNSUPPORTED, "%s: head_dim=%d (64, or 128 for fp16)", who, d->head_dim);
+    if (d->head_dim != D && !(d->dtype != KVP_F32 && d->head_dim == 128))
+        return fail(KVP_ERR_UNSUPPORTED, "%s: head_dim=%d (64, or 128 for fp16 / int8)", who, d->head_dim);
     const int group = d->num_q_heads / d->num_kv_heads;
     if (group > MAXG)
         return fail(KVP_ERR_UNSUPPORTED, "%s: %d query heads per KV head (1..%d supported)", who, group, MAXG);
@@ -40,7 +40,7 @@ static size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
 static size_t part_bytes(const kvp_dims *d, int B, int max_context)
 {
-    if (d->dtype == KVP_F16) {
+    if (d->dtype != KVP_F32) { // the fp16 kernel (fp16 or int8 caches)
         const int ipp = decode_f16_items_per_pair(max_context);
         return ipp > 1 ? decode_f16_part_bytes((long long)B * d->num_kv_heads * ipp, d->head_dim) : 0;
     }
@@ -61,9 +61,9 @@ static size_t workspace_bytes(const kvp_dims *d, int B, int max_context)
 
 template <typename Addr>
 static kvp_status decode_common(const kvp_dims *dims, void *out, const void *q, const void *kc,
-                                const void *vc, const void *k_new, const void *v_new,
-                                const Addr &A, int max_ctx, const int32_t *d_ctx, int32_t B,
-                                float scale, void *ws, size_t ws_bytes, kvp_stream stream,
+                                const void *vc, const void *ksc, const void *vsc, const void *k_new,
+                                const void *v_new, const Addr &A, int max_ctx, const int32_t *d_ctx,
+                                int32_t B, float scale, void *ws, size_t ws_bytes, kvp_stream stream,
                                 const char *who)
 {
     kvp_status st = check_dims(dims, who);
@@ -80,9 +80,11 @@ static kvp_status decode_common(const kvp_dims *dims, void *out, const void *q, 
         return fail(KVP_ERR_INVALID, "%s: q/out/cache/new-row pointers must be 16-byte aligned", who);
     if ((k_new == nullptr) != (v_new == nullptr))
         return fail(KVP_ERR_INVALID, "%s: k_new and v_new must both be given or both be NULL", who);
-    if (k_new && dims->dtype != KVP_F16)
-        return fail(KVP_ERR_UNSUPPORTED, "%s: the fused append is implemented for fp16", who);
-    DecodeParams P;
+    if (k_new && dims->dtype == KVP_F32)
+        return fail(KVP_ERR_UNSUPPORTED, "%s: the fused append is implemented for fp16 and int8", who);
+    if (dims->dtype == KVP_I8 && (!ksc || !vsc))
+        return fail(KVP_ERR_INVALID, "%s: an int8 cache needs its scale pools", who);
+    DecodeParams P{};
     P.q = q;
     P.out = out;
     P.kc = kc;
@@ -91,6 +93,11 @@ static kvp_status decode_common(const kvp_dims *dims, void *out, const void *q, 
     P.vc_w = const_cast<void *>(vc);
     P.k_new = k_new;
     P.v_new = v_new;
+    P.ksc = ksc;
+    P.vsc = vsc;
+    P.ksc_w = const_cast<void *>(ksc);
+    P.vsc_w = const_cast<void *>(vsc);
+    P.kv_i8 = dims->dtype == KVP_I8;
     P.ctx_lens = d_ctx;
     P.B = B;
     P.hq = dims->num_q_heads;
@@ -101,7 +108,7 @@ static kvp_status decode_common(const kvp_dims *dims, void *out, const void *q, 
     P.scale_log2 = scale * LOG2E;
     P.part = nullptr;
     P.tickets = nullptr;
-    P.workers = dims->dtype == KVP_F16 ? 0 : decode_f32_max_splits(max_ctx);
+    P.workers = dims->dtype != KVP_F32 ? 0 : decode_f32_max_splits(max_ctx);
     P.merge_polls = g_merge_polls.load(std::memory_order_relaxed);
     const size_t pb = part_bytes(dims, B, max_ctx);
     if (pb > 0) {
@@ -115,7 +122,7 @@ static kvp_status decode_common(const kvp_dims *dims, void *out, const void *q, 
     }
     const int group = P.hq / P.hkv;
     hipStream_t st_ = (hipStream_t)stream;
-    return dims->dtype == KVP_F16 ? launch_decode_f16(P, A, group, max_ctx, st_)
+    return dims->dtype != KVP_F32 ? launch_decode_f16(P, A, group, max_ctx, st_)
                                   : launch_decode_f32(P, A, group, st_);
 }
 
@@ -141,12 +148,19 @@ static kvp_status paged_common(const kvp_cache_desc *cache, int32_t layer, void 
         return fail(KVP_ERR_INVALID, "%s: pool pointer is NULL", who);
     if ((long long)max_blocks * BS > 0x7fffffffLL)
         return fail(KVP_ERR_UNSUPPORTED, "%s: max_blocks too large", who);
-    const size_t esz = cache->dims.dtype == KVP_F16 ? 2 : 4;
-    const size_t layer_elems = (size_t)cache->num_blocks * cache->dims.num_kv_heads * BS * cache->dims.head_dim;
+    const int dt = cache->dims.dtype;
+    const size_t esz = dt == KVP_F16 ? 2 : dt == KVP_F32 ? 4 : 1;
+    const size_t layer_rows = (size_t)cache->num_blocks * cache->dims.num_kv_heads * BS;
+    const size_t layer_elems = layer_rows * cache->dims.head_dim;
     const char *kc = (const char *)cache->k_pool + (size_t)layer * layer_elems * esz;
     const char *vc = (const char *)cache->v_pool + (size_t)layer * layer_elems * esz;
+    const bool i8 = dt == KVP_I8;
+    if (i8 && (!cache->k_scale || !cache->v_scale || (((uintptr_t)cache->k_scale | (uintptr_t)cache->v_scale) & 15)))
+        return fail(KVP_ERR_INVALID, "%s: an int8 cache needs 16-byte aligned scale pools", who);
+    const char *ksc = i8 ? (const char *)cache->k_scale + (size_t)layer * layer_rows * 2 : nullptr;
+    const char *vsc = i8 ? (const char *)cache->v_scale + (size_t)layer * layer_rows * 2 : nullptr;
     PagedAddr A{d_block_table, max_blocks, cache->dims.num_kv_heads, cache->num_blocks, cache->dims.head_dim};
-    return decode_common(&cache->dims, out, q, kc, vc, k_new, v_new, A, max_blocks * BS,
+    return decode_common(&cache->dims, out, q, kc, vc, ksc, vsc, k_new, v_new, A, max_blocks * BS,
                          d_context_lens, B, scale, workspace, ws_bytes, stream, who);
 }
 
@@ -218,8 +232,11 @@ kvp_status paged_decode_attention_planned(const kvp_cache_desc *cache, int32_t l
     kvp_status st = check_dims(&cache->dims, who);
     if (st != KVP_OK)
         return st;
-    if (cache->dims.dtype != KVP_F16)
-        return fail(KVP_ERR_UNSUPPORTED, "%s: planned decode is implemented for fp16", who);
+    if (cache->dims.dtype == KVP_F32)
+        return fail(KVP_ERR_UNSUPPORTED, "%s: planned decode is implemented for fp16 and int8", who);
+    const bool i8 = cache->dims.dtype == KVP_I8;
+    if (i8 && (!cache->k_scale || !cache->v_scale || (((uintptr_t)cache->k_scale | (uintptr_t)cache->v_scale) & 15)))
+        return fail(KVP_ERR_INVALID, "%s: an int8 cache needs 16-byte aligned scale pools", who);
     if (cache->block_size != BS)
         return fail(KVP_ERR_UNSUPPORTED, "%s: block_size=%d (only 16)", who, cache->block_size);
     if (layer < 0 || layer >= cache->dims.num_layers)
@@ -246,16 +263,22 @@ kvp_status paged_decode_attention_planned(const kvp_cache_desc *cache, int32_t l
         if ((uintptr_t)workspace & 255)
             return fail(KVP_ERR_INVALID, "%s: workspace must be 256-byte aligned", who);
     }
-    const size_t layer_elems = (size_t)cache->num_blocks * hkv * BS * dim;
-    DecodeParams P;
+    const size_t layer_rows = (size_t)cache->num_blocks * hkv * BS;
+    const size_t layer_bytes = layer_rows * dim * (i8 ? 1 : 2);
+    DecodeParams P{};
     P.q = q;
     P.out = out;
-    P.kc = (const f16 *)cache->k_pool + (size_t)layer * layer_elems;
-    P.vc = (const f16 *)cache->v_pool + (size_t)layer * layer_elems;
+    P.kc = (const char *)cache->k_pool + (size_t)layer * layer_bytes;
+    P.vc = (const char *)cache->v_pool + (size_t)layer * layer_bytes;
     P.kc_w = const_cast<void *>(P.kc);
     P.vc_w = const_cast<void *>(P.vc);
     P.k_new = k_new;
     P.v_new = v_new;
+    P.kv_i8 = i8;
+    P.ksc = i8 ? (const char *)cache->k_scale + (size_t)layer * layer_rows * 2 : nullptr;
+    P.vsc = i8 ? (const char *)cache->v_scale + (size_t)layer * layer_rows * 2 : nullptr;
+    P.ksc_w = const_cast<void *>(P.ksc);
+    P.vsc_w = const_cast<void *>(P.vsc);
     P.ctx_lens = nullptr;
     P.B = plan->B;
     P.hq = cache->dims.num_q_heads;
@@ -283,8 +306,10 @@ kvp_status contiguous_decode_attention(const kvp_dims *dims, void *out, const vo
         return st0;
     if (Lmax <= 0)
         return fail(KVP_ERR_INVALID, "contiguous_decode_attention: Lmax=%d", Lmax);
+    if (dims->dtype == KVP_I8)
+        return fail(KVP_ERR_UNSUPPORTED, "contiguous_decode_attention: int8 caches are paged only");
     ContigAddr A{dims->num_kv_heads, Lmax, dims->head_dim};
-    return decode_common(dims, out, q, k_cache, v_cache, nullptr, nullptr, A, Lmax, d_context_lens,
+    return decode_common(dims, out, q, k_cache, v_cache, nullptr, nullptr, nullptr, nullptr, A, Lmax, d_context_lens,
                          B, scale, workspace, ws_bytes, stream, "contiguous_decode_attention");
 }
 

@@ -38,17 +38,16 @@ struct PagedAddr {
         return (idx >= 0 && idx < max_blocks) ? table[(size_t)b * max_blocks + idx] : -1;
     }
     __device__ bool valid(int e) const { return e >= 0 && e < num_blocks; }
-    // element offset of row 0 of the block (request b, kv head g, logical block idx,
-    // table entry e)
-    __device__ size_t block_off(int, int g, int, int e) const
-    {
-        return ((size_t)e * hkv + g) * (dec::BS * dim);
-    }
+    // row index (rows of dim elements) of row 0 of the block (request b, kv head g,
+    // logical block idx, table entry e), and its element offset
+    __device__ size_t block_row(int, int g, int, int e) const { return ((size_t)e * hkv + g) * dec::BS; }
+    __device__ size_t block_off(int b, int g, int idx, int e) const { return block_row(b, g, idx, e) * dim; }
     __device__ int max_ctx() const { return max_blocks * dec::BS; }
     // row to read for in-block row r (blocks always hold 16 rows)
     __device__ int row(int, int r) const { return r; }
     // a block that is always readable (block 0 of KV head g), for rows that are masked
-    __device__ size_t safe_off(int, int g) const { return (size_t)g * (dec::BS * dim); }
+    __device__ size_t safe_row0(int, int g) const { return (size_t)g * dec::BS; }
+    __device__ size_t safe_off(int b, int g) const { return safe_row0(b, g) * dim; }
     __device__ int safe_row(int r) const { return r; }
 };
 
@@ -59,14 +58,16 @@ struct ContigAddr {
     static constexpr bool paged = false;
     __device__ int entry(int, int) const { return 0; }
     __device__ bool valid(int) const { return true; }
-    __device__ size_t block_off(int b, int g, int idx, int) const
+    __device__ size_t block_row(int b, int g, int idx, int) const
     {
-        return (((size_t)b * hkv + g) * lmax + (size_t)idx * dec::BS) * dim;
+        return ((size_t)b * hkv + g) * lmax + (size_t)idx * dec::BS;
     }
+    __device__ size_t block_off(int b, int g, int idx, int e) const { return block_row(b, g, idx, e) * dim; }
     __device__ int max_ctx() const { return lmax; }
     // the last 16-row group of a slice may run past Lmax: clamp (such rows are masked)
     __device__ int row(int idx, int r) const { return min(idx * dec::BS + r, lmax - 1) - idx * dec::BS; }
-    __device__ size_t safe_off(int b, int g) const { return ((size_t)b * hkv + g) * lmax * dim; }
+    __device__ size_t safe_row0(int b, int g) const { return ((size_t)b * hkv + g) * lmax; }
+    __device__ size_t safe_off(int b, int g) const { return safe_row0(b, g) * dim; }
     __device__ int safe_row(int r) const { return min(r, lmax - 1); }
 };
 
@@ -158,11 +159,16 @@ struct DecodeParams {
     void *vc_w;
     const void *k_new; // [B][Hkv][dim] or NULL: new token written at position ctx-1
     const void *v_new;
+    const void *ksc;   // int8 cache: layer base of the K / V scale pools (fp16 per row)
+    const void *vsc;
+    void *ksc_w;       // same, writable (fused append)
+    void *vsc_w;
     const int *ctx_lens;
     int B;
     int hq;
     int hkv;
-    int dim;           // head dim: 64 (fp32, fp16) or 128 (fp16)
+    int dim;           // head dim: 64 (fp32, fp16) or 128 (fp16, int8)
+    int kv_i8;         // the cache holds int8 codes and fp16 row scales
     float scale_log2;
     int workers;       // fp32: max splits per pair
     float *part;       // partial results

@@ -46,6 +46,7 @@
 #include "kvp_decode_common.h"
 #include "kvp_gfx950.h"
 #include "kvp_plan_format.h"
+#include "kvp_quant.h"
 
 namespace kvp {
 
@@ -181,11 +182,16 @@ __device__ __forceinline__ void merge_column(const float *part, int pbase, int n
 //
 // Tile t = TT tokens = blocks (TT / 16) t .. of the item.  Lane (col, grp) = (lane % 16,
 // lane / 16).  MFMA column col is query row col of the item (member col / G, head col % G).
-// K and V tiles sit in LDS as TT rows of 2 HD bytes; 16-byte chunk c of row r is stored at
-// chunk slot swz<HD>(c, r).
-template <int G, bool SHARED, int NBUF, int TT, int HD, typename Addr>
+// K and V tiles are read by the products as TT rows of 2 HD bytes of fp16; 16-byte chunk c
+// of row r is stored at chunk slot swz<HD>(c, r).  An fp16 cache is DMA'd straight into
+// that layout (the ring slot is the tile).  An int8 cache (I8) is DMA'd as rows of HD codes
+// into the ring, with the tile's row scales (K scales of tile row tt at byte 2 tt of the
+// scale slot, V scales at 32 KB + 2 tt), and each tile is reconstructed (code * scale,
+// rounded once to fp16) into the staging tiles kst / vst before the products.
+template <int G, bool SHARED, int NBUF, int TT, int HD, bool I8, typename Addr>
 __device__ __forceinline__ void run_item(const DecodeParams &P, const Addr &A, const PlanView &PV,
-                                         const Item &it, int rv, char *kring, char *vring)
+                                         const Item &it, int rv, char *kring, char *vring, char *sring,
+                                         char *kst, char *vst)
 {
     static_assert(TT == 32 || TT == 64, "tiles of 32 or 64 tokens");
     static_assert(HD == 64 || HD == 128, "head dimension 64 or 128");
@@ -197,13 +203,21 @@ __device__ __forceinline__ void run_item(const DecodeParams &P, const Addr &A, c
     constexpr int IPB = BS / RPI;    // 1 KB loads per block and tensor
     constexpr int KD = HD / 32;      // k-steps of 32 dims (score product)
     constexpr int NDB = HD / 16;     // 16-dim blocks (value product)
-    constexpr int NDMA = 2 * KB * IPB; // 1 KB loads per tile, K and V
-    constexpr int SLOT = TT * RB;    // bytes of one K (or V) tile
+    constexpr int SLOT = TT * RB;    // bytes of one K (or V) fp16 tile
+    // the cached rows as the ring holds them (int8: one byte per value)
+    constexpr int RQ = I8 ? HD : RB;   // bytes of one cached row
+    constexpr int CPQ = RQ / 16;       // 16-byte chunks per cached row
+    constexpr int RPIQ = 1024 / RQ;    // cached rows per 1 KB DMA load
+    constexpr int IPBQ = BS / RPIQ;    // 1 KB loads per block and tensor
+    constexpr int SLOTQ = TT * RQ;     // bytes of one ring slot per tensor
+    constexpr int NDMA = 2 * KB * IPBQ + (I8 ? 1 : 0); // loads per tile (+ the row scales)
+    static_assert(!I8 || Addr::paged, "int8 caches are paged");
+    static_assert(I8 || (RQ == RB && IPBQ == IPB), "fp16 ring = tile");
     const int lane = threadIdx.x;
     const int col = lane & 15, grp = lane >> 4;
     const int hkv = P.hkv;
-    const f16 *kc = (const f16 *)P.kc;
-    const f16 *vc = (const f16 *)P.vc;
+    const char *kc = (const char *)P.kc;
+    const char *vc = (const char *)P.vc;
     const float c = P.scale_log2;
 
     // ---- this lane's query row: q operand, token limit, output slot ----
@@ -258,6 +272,15 @@ __device__ __forceinline__ void run_item(const DecodeParams &P, const Addr &A, c
         const size_t off = (((size_t)it.b * hkv + it.g) * HD + (lane & (CPR - 1)) * 8) * sizeof(f16);
         nrow = *(const __attribute__((address_space(1))) i32x4 *)(base + off);
     }
+    // int8: the new rows' codes and scales (lanes of one row exchange its maximum)
+    u32x2 ncodes = {0u, 0u};
+    unsigned nscale = 0;
+    if constexpr (I8) {
+        if (app) {
+            const f16 s16 = quantize_row_piece<CPR>(__builtin_bit_cast(f16x8, nrow), ncodes);
+            nscale = __builtin_bit_cast(unsigned short, s16);
+        }
+    }
 
     const int nt = (it.nblk + KB - 1) / KB;
     auto ent = [&](int j) -> int { return lane_int(rv, R_ENT + min(j, BPI - 1)); };
@@ -266,21 +289,26 @@ __device__ __forceinline__ void run_item(const DecodeParams &P, const Addr &A, c
     // ---- DMA of tile t into ring slot t % NBUF: per block, IPB loads of RPI rows of K and V
     // (lane: row RPI h + lane / CPR, chunk lane % CPR of the LDS row) ----
     auto issue = [&](int t) {
-        char *kd = kring + (t % NBUF) * SLOT;
-        char *vd = vring + (t % NBUF) * SLOT;
+        char *kd = kring + (t % NBUF) * SLOTQ;
+        char *vd = vring + (t % NBUF) * SLOTQ;
+        size_t brow[KB]; // row index of row 0 of each block (a readable block if unusable)
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
             const int j = KB * t + kb;
             const int e = ent(j);
             const bool ok = (j < it.nblk) & A.valid(e);
             const int lb = it.blk0 + j;
-            const size_t base = ok ? A.block_off(it.b, it.g, lb, e) : A.safe_off(it.b, it.g);
+            brow[kb] = ok ? A.block_row(it.b, it.g, lb, e) : A.safe_row0(it.b, it.g);
 #pragma unroll
-            for (int h = 0; h < IPB; ++h) {
-                const int r = RPI * h + lane / CPR;
+            for (int h = 0; h < IPBQ; ++h) {
+                const int r = RPIQ * h + lane / CPQ;
                 const int sr = ok ? A.row(lb, r) : A.safe_row(r);
-                const size_t off = base + (size_t)sr * HD + swz<HD>(lane & (CPR - 1), r) * 8;
-                const int i = IPB * kb + h;
+                size_t off; // bytes
+                if constexpr (I8)
+                    off = (brow[kb] + sr) * HD + (lane % CPQ) * 16;
+                else
+                    off = ((brow[kb] + sr) * HD + swz<HD>(lane & (CPR - 1), r) * 8) * sizeof(f16);
+                const int i = IPBQ * kb + h;
                 __builtin_amdgcn_global_load_lds((const void *)(kc + off),
                                                  (__attribute__((address_space(3))) void *)(kd + i * 1024),
                                                  16, 0, 0);
@@ -288,6 +316,21 @@ __device__ __forceinline__ void run_item(const DecodeParams &P, const Addr &A, c
                                                  (__attribute__((address_space(3))) void *)(vd + i * 1024),
                                                  16, 0, 0);
             }
+        }
+        if constexpr (I8) {
+            // row scales: lane i < 2 KB takes half i % 2 of block i / 2's 16 K scales, the next
+            // 2 KB lanes the V scales; the other lanes repeat them (their copies are unused)
+            const int idx = lane % (4 * KB);
+            const int sb = (idx >> 1) % KB, half = idx & 1;
+            size_t rs = brow[0];
+#pragma unroll
+            for (int q = 1; q < KB; ++q)
+                rs = sb == q ? brow[q] : rs;
+            const uintptr_t kb_ = (uintptr_t)P.ksc, vb_ = (uintptr_t)P.vsc;
+            const uintptr_t base = kb_ + ((vb_ - kb_) & (uintptr_t)(-(intptr_t)(idx >= 2 * KB)));
+            __builtin_amdgcn_global_load_lds((const void *)(base + (rs + 8 * half) * sizeof(f16)),
+                                             (__attribute__((address_space(3))) void *)(sring + (t % NBUF) * 1024),
+                                             16, 0, 0);
         }
     };
 
@@ -301,8 +344,8 @@ __device__ __forceinline__ void run_item(const DecodeParams &P, const Addr &A, c
     const f16x8 ones = {1, 1, 1, 1, 1, 1, 1, 1};
 
     auto compute = [&](int t) {
-        char *kt = kring + (t % NBUF) * SLOT;
-        char *vt = vring + (t % NBUF) * SLOT;
+        char *kt = I8 ? kst : kring + (t % NBUF) * SLOT; // fp16 tiles read by the products
+        char *vt = I8 ? vst : vring + (t % NBUF) * SLOT;
         const int tb = BS * (it.blk0 + KB * t); // position of tile row 0
         bool bok[KB];
         bool all_ok = true;
@@ -312,35 +355,118 @@ __device__ __forceinline__ void run_item(const DecodeParams &P, const Addr &A, c
             all_ok = all_ok && bok[kb];
         }
         const bool full = all_ok && tb + TT <= full_end;
-        // value rows that no column may use: zero them (the cache can hold NaN there)
-        if (!full) {
+        // value row r of the tile holds data some column may use
+        auto row_used = [&](int r) -> bool {
+            const int kb = r >> 4;
+            bool okb = bok[0];
 #pragma unroll
-            for (int k = 0; k < TT * CPR / 64; ++k) {
-                const int ch = lane + 64 * k, r = ch / CPR;
-                const int kb = r >> 4;
-                bool okb = bok[0];
+            for (int q = 1; q < KB; ++q)
+                okb = kb == q ? bok[q] : okb;
+            return okb && tb + r < rend;
+        };
+        if constexpr (!I8) {
+            // value rows that no column may use: zero them (the cache can hold NaN there)
+            if (!full) {
 #pragma unroll
-                for (int q = 1; q < KB; ++q)
-                    okb = kb == q ? bok[q] : okb;
-                if (!(okb && tb + r < rend))
-                    lds_store_b128(vt + ch * 16, i32x4{0, 0, 0, 0});
-            }
-        }
-        // the new token of this step: into LDS (this tile) and into the cache
-        if (app) {
-            const int pos = it.end - 1, r = pos - tb;
-            if (r >= 0 && r < TT) {
-                const int j = KB * t + (r >> 4);
-                const int e = ent(j);
-                if (lane < 2 * CPR && j < it.nblk && A.valid(e)) {
-                    const int ch = lane & (CPR - 1);
-                    const int lb = it.blk0 + j;
-                    const size_t dst = A.block_off(it.b, it.g, lb, e) + (size_t)A.row(lb, r & 15) * HD + ch * 8;
-                    lds_store_b128((lane < CPR ? kt : vt) + r * RB + swz<HD>(ch, r) * 16, nrow);
-                    const uintptr_t kb = (uintptr_t)P.kc_w, vb = (uintptr_t)P.vc_w;
-                    const uintptr_t base = kb + ((vb - kb) & (uintptr_t)(-(intptr_t)(lane >= CPR)));
-                    *(__attribute__((address_space(1))) i32x4 *)(base + dst * sizeof(f16)) = nrow;
+                for (int k = 0; k < TT * CPR / 64; ++k) {
+                    const int ch = lane + 64 * k, r = ch / CPR;
+                    if (!row_used(r))
+                        lds_store_b128(vt + ch * 16, i32x4{0, 0, 0, 0});
                 }
+            }
+            // the new token of this step: into LDS (this tile) and into the cache
+            if (app) {
+                const int pos = it.end - 1, r = pos - tb;
+                if (r >= 0 && r < TT) {
+                    const int j = KB * t + (r >> 4);
+                    const int e = ent(j);
+                    if (lane < 2 * CPR && j < it.nblk && A.valid(e)) {
+                        const int ch = lane & (CPR - 1);
+                        const int lb = it.blk0 + j;
+                        const size_t dst = A.block_off(it.b, it.g, lb, e) + (size_t)A.row(lb, r & 15) * HD + ch * 8;
+                        lds_store_b128((lane < CPR ? kt : vt) + r * RB + swz<HD>(ch, r) * 16, nrow);
+                        const uintptr_t kb = (uintptr_t)P.kc_w, vb = (uintptr_t)P.vc_w;
+                        const uintptr_t base = kb + ((vb - kb) & (uintptr_t)(-(intptr_t)(lane >= CPR)));
+                        *(__attribute__((address_space(1))) i32x4 *)(base + dst * sizeof(f16)) = nrow;
+                    }
+                }
+            }
+        } else {
+            char *kq = kring + (t % NBUF) * SLOTQ;
+            char *vq = vring + (t % NBUF) * SLOTQ;
+            char *sq = sring + (t % NBUF) * 1024;
+            // the new token of this step: codes and scale into the ring slot and the cache
+            if (app) {
+                const int pos = it.end - 1, r = pos - tb;
+                if (r >= 0 && r < TT) {
+                    const int j = KB * t + (r >> 4);
+                    const int e = ent(j);
+                    if (lane < 2 * CPR && j < it.nblk && A.valid(e)) {
+                        const int ch = lane & (CPR - 1); // 8 values per lane
+                        const int lb = it.blk0 + j;
+                        const size_t rowi = A.block_row(it.b, it.g, lb, e) + A.row(lb, r & 15);
+                        lds_store_b64((lane < CPR ? kq : vq) + r * RQ + ch * 8, ncodes);
+                        const uintptr_t kb = (uintptr_t)P.kc_w, vb = (uintptr_t)P.vc_w;
+                        const uintptr_t base = kb + ((vb - kb) & (uintptr_t)(-(intptr_t)(lane >= CPR)));
+                        *(__attribute__((address_space(1))) u32x2 *)(base + rowi * HD + ch * 8) = ncodes;
+                        if (ch == 0) {
+                            lds_store_b16(sq + (lane < CPR ? 0 : 32 * KB) + 2 * r, nscale);
+                            const uintptr_t ks = (uintptr_t)P.ksc_w, vs = (uintptr_t)P.vsc_w;
+                            const uintptr_t sb = ks + ((vs - ks) & (uintptr_t)(-(intptr_t)(lane >= CPR)));
+                            *(__attribute__((address_space(1))) unsigned short *)(sb + rowi * sizeof(f16)) =
+                                (unsigned short)nscale;
+                        }
+                    }
+                }
+            }
+            wave_lds_sync();
+            // reconstruction: 16 codes of one row per lane and step, K chunks then V chunks;
+            // code * scale rounded once to fp16 into the tile layout.  Value rows no column
+            // may use become zeros (their scales can be anything).
+            constexpr int NCH = 2 * TT * CPQ / 64; // chunks per lane
+            static_assert(NCH % 2 == 0, "K and V chunks split evenly");
+            i32x4 raw[NCH];
+            unsigned sc[NCH];
+#pragma unroll
+            for (int k = 0; k < NCH; ++k) {
+                const bool isv = k >= NCH / 2;
+                const int ci = lane + 64 * (isv ? k - NCH / 2 : k), r = ci / CPQ, cq = ci % CPQ;
+                raw[k] = lds_i128((isv ? vq : kq) + r * RQ + cq * 16);
+                sc[k] = lds_u16(sq + (isv ? 32 * KB : 0) + 2 * r);
+            }
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+            for (int k = 0; k < NCH; ++k)
+                asm volatile("" : "+v"(raw[k]), "+v"(sc[k]));
+            typedef f16 f16x2_ __attribute__((ext_vector_type(2)));
+            const f16x2_ bias = {(f16)1152.f, (f16)1152.f};
+#pragma unroll
+            for (int k = 0; k < NCH; ++k) {
+                const bool isv = k >= NCH / 2;
+                const int ci = lane + 64 * (isv ? k - NCH / 2 : k), r = ci / CPQ, cq = ci % CPQ;
+                const unsigned s2u = sc[k] | (sc[k] << 16);
+                const f16x2_ s2 = __builtin_bit_cast(f16x2_, s2u);
+                unsigned h[8];
+#pragma unroll
+                for (int w = 0; w < 4; ++w) {
+                    // code + 128 as the low byte of the fp16 number 1024 + byte, minus 1152
+                    const unsigned x = (unsigned)raw[k][w] ^ 0x80808080u;
+                    const unsigned lo = __builtin_amdgcn_perm(0x64646464u, x, 0x04010400u);
+                    const unsigned hi = __builtin_amdgcn_perm(0x64646464u, x, 0x04030402u);
+                    const f16x2_ vlo = (__builtin_bit_cast(f16x2_, lo) - bias) * s2;
+                    const f16x2_ vhi = (__builtin_bit_cast(f16x2_, hi) - bias) * s2;
+                    h[2 * w] = __builtin_bit_cast(unsigned, vlo);
+                    h[2 * w + 1] = __builtin_bit_cast(unsigned, vhi);
+                }
+                i32x4 o0 = {(int)h[0], (int)h[1], (int)h[2], (int)h[3]};
+                i32x4 o1 = {(int)h[4], (int)h[5], (int)h[6], (int)h[7]};
+                if (isv && !full && !row_used(r)) {
+                    o0 = i32x4{0, 0, 0, 0};
+                    o1 = i32x4{0, 0, 0, 0};
+                }
+                char *dt = isv ? vt : kt;
+                lds_store_b128(dt + r * RB + swz<HD>(2 * cq, r) * 16, o0);
+                lds_store_b128(dt + r * RB + swz<HD>(2 * cq + 1, r) * 16, o1);
             }
         }
         wave_lds_sync();
@@ -552,13 +678,18 @@ __device__ __forceinline__ void run_item(const DecodeParams &P, const Addr &A, c
     }
 }
 
-template <int G, int NBUF, int TT, int HD, bool PLANNED, typename Addr>
+template <int G, int NBUF, int TT, int HD, bool I8, bool PLANNED, typename Addr>
 __global__ __launch_bounds__(64) void decode_f16_kernel(DecodeParams P, Addr A, PlanView PV)
 {
     static_assert(G >= 1 && G <= MAXG, "group size");
     static_assert(NBUF >= 2 && NBUF <= 3, "ring depth");
-    __shared__ __attribute__((aligned(16))) char kring[NBUF * TT * 2 * HD];
-    __shared__ __attribute__((aligned(16))) char vring[NBUF * TT * 2 * HD];
+    constexpr int EB = I8 ? 1 : 2; // bytes per cached value
+    __shared__ __attribute__((aligned(16))) char kring[NBUF * TT * EB * HD];
+    __shared__ __attribute__((aligned(16))) char vring[NBUF * TT * EB * HD];
+    // int8 only: row scales per ring slot, and the reconstructed fp16 tiles
+    __shared__ __attribute__((aligned(16))) char sring[I8 ? NBUF * 1024 : 16];
+    __shared__ __attribute__((aligned(16))) char kst[I8 ? TT * 2 * HD : 16];
+    __shared__ __attribute__((aligned(16))) char vst[I8 ? TT * 2 * HD : 16];
     const int lane = threadIdx.x;
     Item it;
     int rv;
@@ -584,12 +715,12 @@ __global__ __launch_bounds__(64) void decode_f16_kernel(DecodeParams P, Addr A, 
         if (flags & F_SHARED) {
             if (it.nmem * G > 16 || it.slot < 0)
                 return;
-            run_item<G, true, NBUF, TT, HD>(P, A, PV, it, rv, kring, vring);
+            run_item<G, true, NBUF, TT, HD, I8>(P, A, PV, it, rv, kring, vring, sring, kst, vst);
             return;
         }
         if (it.nmem != 1)
             return;
-        run_item<G, false, NBUF, TT, HD>(P, A, PV, it, rv, kring, vring);
+        run_item<G, false, NBUF, TT, HD, I8>(P, A, PV, it, rv, kring, vring, sring, kst, vst);
     } else {
         const int pair = blockIdx.x / PV.ipp;
         const int k = blockIdx.x - pair * PV.ipp;
@@ -614,7 +745,7 @@ __global__ __launch_bounds__(64) void decode_f16_kernel(DecodeParams P, Addr A, 
         it.slot = it.pbase + k;
         const int j = lane - R_ENT;
         rv = (j >= 0 && j < it.nblk) ? A.entry(it.b, it.blk0 + j) : -1;
-        run_item<G, false, NBUF, TT, HD>(P, A, PV, it, rv, kring, vring);
+        run_item<G, false, NBUF, TT, HD, I8>(P, A, PV, it, rv, kring, vring, sring, kst, vst);
     }
 }
 
@@ -633,16 +764,34 @@ static kvp_status launch_f16(const DecodeParams &P, const Addr &A, const PlanVie
     if (P.dim != 64 && P.dim != 128)
         return fail(KVP_ERR_UNSUPPORTED, "decode: head_dim=%d (64 or 128)", P.dim);
     // head_dim 64: 64-token tiles; 128: 32-token tiles (the same 32 KB of LDS for the rings)
-    switch (group * 1000 + P.dim) {
+    if (P.kv_i8) {
+        if constexpr (Addr::paged) {
+            switch (group * 1000 + P.dim) {
 #define KVP_G(GG)                                                                                  \
     case GG * 1000 + 64:                                                                           \
-        hipLaunchKernelGGL((decode_f16_kernel<GG, DEC_NBUF, DEC_TT, 64, PLANNED, Addr>), g, block, 0, st, P, A, PV); \
+        hipLaunchKernelGGL((decode_f16_kernel<GG, DEC_NBUF, DEC_TT, 64, true, PLANNED, Addr>), g, block, 0, st, P, A, PV); \
         break;                                                                                     \
     case GG * 1000 + 128:                                                                          \
-        hipLaunchKernelGGL((decode_f16_kernel<GG, 2, 32, 128, PLANNED, Addr>), g, block, 0, st, P, A, PV); \
+        hipLaunchKernelGGL((decode_f16_kernel<GG, 2, 32, 128, true, PLANNED, Addr>), g, block, 0, st, P, A, PV); \
         break;
-        KVP_G(1) KVP_G(2) KVP_G(3) KVP_G(4) KVP_G(5) KVP_G(6) KVP_G(7) KVP_G(8)
+                KVP_G(1) KVP_G(2) KVP_G(3) KVP_G(4) KVP_G(5) KVP_G(6) KVP_G(7) KVP_G(8)
 #undef KVP_G
+            }
+        } else {
+            return fail(KVP_ERR_UNSUPPORTED, "decode: int8 caches are paged only");
+        }
+    } else {
+        switch (group * 1000 + P.dim) {
+#define KVP_G(GG)                                                                                  \
+    case GG * 1000 + 64:                                                                           \
+        hipLaunchKernelGGL((decode_f16_kernel<GG, DEC_NBUF, DEC_TT, 64, false, PLANNED, Addr>), g, block, 0, st, P, A, PV); \
+        break;                                                                                     \
+    case GG * 1000 + 128:                                                                          \
+        hipLaunchKernelGGL((decode_f16_kernel<GG, 2, 32, 128, false, PLANNED, Addr>), g, block, 0, st, P, A, PV); \
+        break;
+            KVP_G(1) KVP_G(2) KVP_G(3) KVP_G(4) KVP_G(5) KVP_G(6) KVP_G(7) KVP_G(8)
+#undef KVP_G
+        }
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)

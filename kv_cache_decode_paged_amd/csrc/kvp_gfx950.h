@@ -13,6 +13,7 @@ typedef _Float16 f16;
 typedef f16 f16x4 __attribute__((ext_vector_type(4)));
 typedef f16 f16x8 __attribute__((ext_vector_type(8)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 
 // s_waitcnt with only the vector-memory count set (gfx9 encoding: vmcnt in bits 3:0 and
 // 15:14, expcnt 6:4 and lgkmcnt 11:8 left at their maxima)
@@ -57,6 +58,26 @@ __device__ inline f16x4 lds_tr16_b64(const char *p)
 __device__ inline void lds_store_b128(char *p, i32x4 v)
 {
     asm volatile("ds_write_b128 %0, %1" ::"v"(lds_addr(p)), "v"(v) : "memory");
+}
+__device__ inline void lds_store_b64(char *p, u32x2 v)
+{
+    asm volatile("ds_write_b64 %0, %1" ::"v"(lds_addr(p)), "v"(v) : "memory");
+}
+__device__ inline void lds_store_b16(char *p, unsigned v)
+{
+    asm volatile("ds_write_b16 %0, %1" ::"v"(lds_addr(p)), "v"(v) : "memory");
+}
+__device__ inline i32x4 lds_i128(const char *p)
+{
+    i32x4 r;
+    asm volatile("ds_read_b128 %0, %1" : "=v"(r) : "v"(lds_addr(p)));
+    return r;
+}
+__device__ inline unsigned lds_u16(const char *p)
+{
+    unsigned r;
+    asm volatile("ds_read_u16 %0, %1" : "=v"(r) : "v"(lds_addr(p)));
+    return r;
 }
 
 // maximum of three as one v_max3_f32 (fmaxf would first quiet each operand, a

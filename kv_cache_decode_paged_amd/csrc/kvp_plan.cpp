@@ -32,9 +32,9 @@ kvp_status check_plan_dims(const kvp_dims *d, const char *who)
                     who, d->num_q_heads, d->num_kv_heads);
     if (d->head_dim != 64 && d->head_dim != 128)
         return fail(KVP_ERR_UNSUPPORTED, "%s: head_dim=%d (64 or 128)", who, d->head_dim);
-    if (d->dtype != KVP_F16)
+    if (d->dtype != KVP_F16 && d->dtype != KVP_I8)
         return fail(d->dtype == KVP_F32 ? KVP_ERR_UNSUPPORTED : KVP_ERR_INVALID,
-                    "%s: planned decode is implemented for fp16 (dtype=%d)", who, d->dtype);
+                    "%s: planned decode is implemented for fp16 and int8 (dtype=%d)", who, d->dtype);
     if (d->num_q_heads / d->num_kv_heads > 8)
         return fail(KVP_ERR_UNSUPPORTED, "%s: %d query heads per KV head (1..8 supported)", who,
                     d->num_q_heads / d->num_kv_heads);

@@ -48,6 +48,8 @@ class PagedStep:
         self.kvp, self.pb, self.layers = kvp, pb, layers
         self.hq, self.hkv, self.dtype, self.seed = hq, hkv, dtype, seed
         self.head_dim = head_dim
+        # an int8 cache quantizes fp16 rows on append; q, out and the logical rows are fp16
+        io = self.io_dtype = torch.float16 if dtype == torch.int8 else dtype
         B = pb.batch
         ctx_after = [c + 1 for c in pb.ctx_before]
         self.lmax = max(ctx_after)
@@ -59,12 +61,18 @@ class PagedStep:
         self.pool.set_free_order(W.free_list_permutation(self.num_blocks, seed + 17).tolist())
         self.cache = kvp.PagedKVCache(layers, self.num_blocks, hq, hkv, dtype, device, head_dim=head_dim)
         if poison:  # never-written rows hold NaN: any read of them shows up in the output
-            self.cache.k_pool.fill_(float("nan"))
-            self.cache.v_pool.fill_(float("nan"))
+            if dtype == torch.int8:  # codes cannot be NaN: the scales are
+                self.cache.k_pool.fill_(127)
+                self.cache.v_pool.fill_(-128)
+                self.cache.k_scale.fill_(float("nan"))
+                self.cache.v_scale.fill_(float("nan"))
+            else:
+                self.cache.k_pool.fill_(float("nan"))
+                self.cache.v_pool.fill_(float("nan"))
         self.layers_with_data = list(range(layers)) if layers_with_data is None else layers_with_data
-        self.logical = {l: W.logical_kv(pb, hkv, self.lmax, seed, dtype, layer=l, head_dim=head_dim)
+        self.logical = {l: W.logical_kv(pb, hkv, self.lmax, seed, io, layer=l, head_dim=head_dim)
                         for l in self.layers_with_data}
-        prefix = {l: W.group_prefix_kv(pb, hkv, seed, dtype, layer=l, head_dim=head_dim)
+        prefix = {l: W.group_prefix_kv(pb, hkv, seed, io, layer=l, head_dim=head_dim)
                   for l in self.layers_with_data}
 
         seqs = [None] * B
@@ -126,7 +134,7 @@ class PagedStep:
                                V[i, :, start:end].transpose(0, 1).contiguous().to(device), sl)
 
     def q(self, layer):
-        return W.decode_q(self.pb.batch, self.hq, self.seed, self.dtype, layer, self.head_dim)
+        return W.decode_q(self.pb.batch, self.hq, self.seed, self.io_dtype, layer, self.head_dim)
 
     def oracle(self, layer, rows=None):
         """Oracle decode output [B, Hq, d] (float64) for the given requests (all if None)."""
@@ -134,9 +142,18 @@ class PagedStep:
         K, V = self.logical[layer]
         q = self.q(layer)
         rows = list(range(self.pb.batch)) if rows is None else rows
-        out = oracle.decode_gqa(to64(q[rows]), to64(K[rows]), to64(V[rows]),
-                                np.array([self.ctx_host[r] for r in rows]))
+        K64, V64 = to64(K[rows]), to64(V[rows])
+        if self.dtype == torch.int8:  # the cache holds the oracle's quantization of the rows
+            K64, V64 = self.dequantized(K[rows]), self.dequantized(V[rows])
+        out = oracle.decode_gqa(to64(q[rows]), K64, V64, np.array([self.ctx_host[r] for r in rows]))
         return out
+
+    @staticmethod
+    def dequantized(x):
+        """fp64 reconstruction of the oracle's int8 row quantization of fp16 rows x [..., d]."""
+        from oracle import kvquant as KQ
+        codes, scales = KQ.absmax_quantize_rows(x.numpy())
+        return KQ.dequantize_rows(codes, scales)
 
 
 class ChunkStep:
