@@ -47,10 +47,15 @@ SHAPES = {
 DEFAULT_SHAPE = "14q2kv_d64"
 
 
-def set_shape(name):
-    global HQ, HKV, D, KV_TOKEN_LAYER_BYTES
+KV_INT8 = False  # the cache holds int8 codes and one fp16 scale per row
+
+
+def set_shape(name, kv_int8=False):
+    global HQ, HKV, D, KV_TOKEN_LAYER_BYTES, KV_INT8
     _, HQ, HKV, D, _ = SHAPES[name]
-    KV_TOKEN_LAYER_BYTES = 2 * HKV * D * 2
+    KV_INT8 = kv_int8
+    # K and V bytes per token and layer: fp16 values, or int8 codes plus a 2-byte scale per row
+    KV_TOKEN_LAYER_BYTES = 2 * HKV * (D + 2) if kv_int8 else 2 * HKV * D * 2
 
 
 # HBM traffic of the decode launch, counted by rocprofv3 (FETCH_SIZE / WRITE_SIZE passes,
@@ -131,8 +136,16 @@ def build_state(kvp, torch, W, B, layers, total_steps, seed):
     max_blocks = math.ceil((max(pb.ctx_before) + total_steps + 1) / BLOCK)
     pool = kvp.BlockPool(num_blocks)
     pool.set_free_order(W.free_list_permutation(num_blocks, seed + 1).tolist())
-    cache = kvp.PagedKVCache(layers, num_blocks, HQ, HKV, torch.float16, dev, head_dim=D)
+    cache = kvp.PagedKVCache(layers, num_blocks, HQ, HKV, torch.int8 if KV_INT8 else torch.float16, dev, head_dim=D)
     for l in range(layers):  # cache contents: seeded N(0,1) in every slot
+        if KV_INT8:  # codes uniform on -127..127, row scales of N(0,1) rows (about 3 / 127)
+            g = torch.Generator(device=dev)
+            g.manual_seed(seed + 10 + 2 * l)
+            for codes in (cache.k_pool[l], cache.v_pool[l]):
+                codes.copy_(torch.randint(-127, 128, codes.shape, generator=g, device=dev, dtype=torch.int8))
+            for sc in (cache.k_scale[l], cache.v_scale[l]):
+                sc.copy_((torch.rand(sc.shape, generator=g, device=dev) * 0.01 + 0.02).to(torch.float16))
+            continue
         cache.k_pool[l].copy_(W.randn_device(cache.k_pool[l].shape, seed + 10 + 2 * l, torch.float16, dev))
         cache.v_pool[l].copy_(W.randn_device(cache.v_pool[l].shape, seed + 11 + 2 * l, torch.float16, dev))
     seqs = [None] * B
@@ -173,6 +186,13 @@ def cpu_baseline(W, layers, seed=42):
         K, V = W.logical_kv(pb, HKV, lmax, seed, layer=layer, head_dim=D)
         q = W.decode_q(pb.batch, HQ, seed, layer=layer, head_dim=D)
         K64, V64, q64 = K.double().numpy(), V.double().numpy(), q.double().numpy()
+        t_q = 0.0
+        if KV_INT8:  # the oracle's quantization and reconstruction of the rows, timed too
+            from oracle import kvquant as KQ
+            t0 = time.perf_counter()
+            K64 = KQ.dequantize_rows(*KQ.absmax_quantize_rows(K.numpy()))
+            V64 = KQ.dequantize_rows(*KQ.absmax_quantize_rows(V.numpy()))
+            t_q = time.perf_counter() - t0
 
         def one(i):
             n = int(ctx[i])
@@ -182,12 +202,13 @@ def cpu_baseline(W, layers, seed=42):
         t0 = time.perf_counter()
         with cf.ThreadPoolExecutor(threads) as ex:
             list(ex.map(one, range(pb.batch)))
-        elapsed += time.perf_counter() - t0
+        elapsed += time.perf_counter() - t0 + t_q
         total_bytes += int(ctx.sum()) * KV_TOKEN_LAYER_BYTES
     return {"value": round(total_bytes / elapsed / 1e9, 4), "unit": "GB/s", "cores": threads,
             "kind": "oracle",
             "sample": f"{n_layers} of {layers} layers x {n_req} of the 200 requests of the batch-200 step "
-                      f"(logical KV bytes / wall time, fp64 scalar C, {threads} threads)"}
+                      f"(logical KV bytes / wall time, fp64 scalar C, {threads} threads"
+                      + (", with the numpy quantization and reconstruction of the rows)" if KV_INT8 else ")")}
 
 
 MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 matrix peak
@@ -359,6 +380,8 @@ def main():
     ap.add_argument("--layers", type=int, default=None, help="default: the shape's layer count")
     ap.add_argument("--shape", choices=sorted(SHAPES), default=DEFAULT_SHAPE,
                     help="decode head shape (default 14q2kv_d64)")
+    ap.add_argument("--kv-dtype", choices=["fp16", "int8"], default="fp16",
+                    help="decode cache: fp16, or int8 codes with an fp16 scale per row")
     ap.add_argument("--kernel-reps", type=int, default=4, help="rounds of per-layer decode timing")
     ap.add_argument("--no-graph", action="store_true", help="launch the layers eagerly")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -374,7 +397,10 @@ def main():
         print(f"bench.py runs on one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}). "
               "Requests would be sharded across GPUs by whole sharing groups.", flush=True)
         sys.exit(2)
-    set_shape(args.shape)
+    set_shape(args.shape, args.kv_dtype == "int8")
+    if args.kv_dtype == "int8" and args.workload != "decode":
+        print("--kv-dtype int8 applies to the decode workload", flush=True)
+        sys.exit(2)
     if args.workload == "prefill":
         bench_prefill(args)
         return
@@ -391,7 +417,6 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
     dev = "cuda"
-    set_shape(args.shape)
     B, L = args.batch, (args.layers if args.layers is not None else SHAPES[args.shape][0])
     total_steps = args.warmup + args.steps + 1
     t_setup = time.perf_counter()
@@ -548,12 +573,15 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f16",
+        "dtype": "f16" if not KV_INT8 else "i8 cache (fp16 scales), f16 arithmetic",
         "data": "synthetic",
         "config": {"workload": f"paged GQA decode step, batch {B}, {L} layers x fused (append + paged decode), "
-                               f"{HQ}q/{HKV}kv heads d{D} fp16, 16-token blocks, contexts U{{128..2048}}, "
+                               f"{HQ}q/{HKV}kv heads d{D} "
+                               + ("int8 cache (absmax codes, fp16 scale per row)" if KV_INT8 else "fp16")
+                               + ", 16-token blocks, contexts U{128..2048}, "
                                "groups of 8 sharing a 512-token prefix (copy-on-write)",
-                   "batch": B, "layers": L, "shape": args.shape, "graph": graph is not None},
+                   "batch": B, "layers": L, "shape": args.shape, "kv_dtype": args.kv_dtype,
+                   "graph": graph is not None},
         "steps_per_sec": round(1e3 / ms_per_step, 2),
         "hbm_pct": round(value / HBM_PEAK_GBPS * 100, 2),
         "logical_GBps": round(logical_gbps, 2),
@@ -561,7 +589,8 @@ def main():
         "logical_GB_per_step": round(logical_bytes_step / 1e9, 4),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                     "traffic": measured_traffic() if args.shape == DEFAULT_SHAPE and B == 200 else None,
+                     "traffic": measured_traffic() if (args.shape == DEFAULT_SHAPE and B == 200
+                                                       and not KV_INT8) else None,
                      "traffic_unit": "bytes per launch (HBM read + write, counters)",
                      "kernel": "paged_decode_attention_planned (decode_f16_kernel: append + attention + "
                                "split merge)",

@@ -34,6 +34,7 @@
  *     (KVP_F32) or int8 codes with one fp16 scale per row (KVP_I8, paged caches only; q,
  *     out and appended rows are then fp16).
  *       paged K/V pool, one per K and V:  [num_layers][num_blocks][H_kv][block_size][d]
+ *         (int8 V pool: dim-major blocks [num_layers][num_blocks][H_kv][d][block_size])
  *       int8 scale pool, one per K and V:   fp16 [num_layers][num_blocks][H_kv][block_size]
  *       contiguous cache (one layer):       [B][H_kv][Lmax][d]
  *       decode q / out:                     [B][H_q][d]
@@ -78,13 +79,16 @@ typedef struct {
  * the cache): each (token, KV head) row x of d values of K, and separately of V, is stored
  * as int8 codes and one fp16 scale: scale = fp16(max|x| / 127) (fp32 quotient rounded to
  * nearest even), code = clamp(rint(x / scale), -128, 127) in fp32 with the stored scale
- * (round half to even), all codes 0 when the scale is 0.  Reconstruction: code * scale. */
+ * (round half to even), all codes 0 when the scale is 0.  Reconstruction: code * scale.
+ * K codes are stored like fp16 rows; V codes dim-major within a block (byte j * 16 + r of
+ * a (block, head) is dimension j of the block's row r), so that the decode kernel reads
+ * the values of one dimension for consecutive tokens as consecutive bytes. */
 typedef struct {
     kvp_dims dims;
     int32_t block_size; /* tokens per block: 16                          */
     int32_t num_blocks;
     void *k_pool; /* device [num_layers][num_blocks][H_kv][block_size][d] */
-    void *v_pool; /* device, same shape                                   */
+    void *v_pool; /* device, same shape (int8: [..][H_kv][d][block_size])  */
     void *k_scale; /* KVP_I8: device fp16 [num_layers][num_blocks][H_kv][block_size];
                       NULL otherwise                                      */
     void *v_scale; /* KVP_I8: same, for V                                 */

@@ -195,18 +195,20 @@ def dims(num_layers, num_q_heads, num_kv_heads, dtype, head_dim=HEAD_DIM):
 class PagedKVCache:
     """K and V pools of shape [num_layers][num_blocks][H_kv][16][head_dim] in device memory
     (owned by the torch tensors held here); head_dim 64 or 128.  dtype torch.int8 holds
-    quantized rows: int8 code pools plus fp16 scale pools k_scale / v_scale of shape
-    [num_layers][num_blocks][H_kv][16]; q, out and appended rows are then fp16
-    (`io_dtype`)."""
+    quantized rows: int8 code pools (V dim-major within a block: [..][H_kv][head_dim][16])
+    plus fp16 scale pools k_scale / v_scale of shape [num_layers][num_blocks][H_kv][16]; q,
+    out and appended rows are then fp16 (`io_dtype`)."""
 
     def __init__(self, num_layers, num_blocks, num_q_heads, num_kv_heads, dtype=torch.float16,
                  device="cuda", k_pool=None, v_pool=None, head_dim=HEAD_DIM):
         shape = (num_layers, num_blocks, num_kv_heads, BLOCK, head_dim)
+        # int8: V codes dim-major within a block
+        vshape = shape[:3] + (head_dim, BLOCK) if dtype == torch.int8 else shape
         self.k_pool = torch.empty(shape, dtype=dtype, device=device) if k_pool is None else k_pool
-        self.v_pool = torch.empty(shape, dtype=dtype, device=device) if v_pool is None else v_pool
-        for t, n in ((self.k_pool, "k_pool"), (self.v_pool, "v_pool")):
-            if tuple(t.shape) != shape:
-                raise ValueError(f"{n} must have shape {shape}")
+        self.v_pool = torch.empty(vshape, dtype=dtype, device=device) if v_pool is None else v_pool
+        for t, n, shp in ((self.k_pool, "k_pool", shape), (self.v_pool, "v_pool", vshape)):
+            if tuple(t.shape) != shp:
+                raise ValueError(f"{n} must have shape {shp}")
             _dev(t, n, dtype)
         self.k_scale = self.v_scale = None
         if dtype == torch.int8:

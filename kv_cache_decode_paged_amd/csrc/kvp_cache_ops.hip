@@ -85,7 +85,8 @@ __global__ __launch_bounds__(256) void append_kernel(i32x4 *__restrict__ kpool,
 }
 
 // int8 cache: thread = 8 values of one (token, head) row, for K and V; the CPR threads of a
-// row are an aligned lane group that exchanges the row maximum
+// row are an aligned lane group that exchanges the row maximum.  K codes are stored
+// row-major ([block][head][16][d]), V codes dim-major ([block][head][d][16]).
 template <int CPR>
 __global__ __launch_bounds__(256) void append_i8_kernel(char *__restrict__ kpool, char *__restrict__ vpool,
                                                         qf16 *__restrict__ kscale, qf16 *__restrict__ vscale,
@@ -113,7 +114,10 @@ __global__ __launch_bounds__(256) void append_i8_kernel(char *__restrict__ kpool
     const int64_t blk = slot / BS, off = slot % BS;
     const int64_t dst = (blk * hkv + h) * BS + off; // row index in the pool
     *(u32x2 *)(kpool + dst * D + piece * 8) = ck;
-    *(u32x2 *)(vpool + dst * D + piece * 8) = cvv;
+    char *vb = vpool + (blk * hkv + h) * BS * D + off; // dim-major block of this head
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+        vb[(piece * 8 + i) * BS] = (char)((cvv[i >> 2] >> (8 * (i & 3))) & 0xff);
     if (piece == 0) {
         kscale[dst] = sk;
         vscale[dst] = sv;
@@ -140,6 +144,33 @@ __global__ __launch_bounds__(256) void copy_blocks_kernel(CopyPools C, const int
     i32x4 *d = pool + layer * layer_chunks + dst * block_chunks;
     for (int64_t i = threadIdx.x; i < block_chunks; i += blockDim.x)
         d[i] = s[i];
+}
+
+// int8 cache, V codes: grid = (ceil(Lmax/16), Hkv, B), thread = one (token, dim) code of a
+// dim-major block, written token-major
+__global__ __launch_bounds__(256) void gather_v_i8_kernel(const char *__restrict__ vl,
+                                                          const int *__restrict__ table, int max_blocks,
+                                                          const int *__restrict__ ctx_lens, int hkv, int lmax,
+                                                          int d, int num_blocks, char *__restrict__ vo)
+{
+    const int lb = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    int ctx = ctx_lens[b];
+    if (ctx > max_blocks * BS)
+        ctx = max_blocks * BS;
+    if (ctx > lmax)
+        ctx = lmax;
+    if (lb * BS >= ctx)
+        return;
+    const int e = table[(size_t)b * max_blocks + lb];
+    if (e < 0 || e >= num_blocks)
+        return;
+    for (int i = threadIdx.x; i < BS * d; i += blockDim.x) {
+        const int r = i / d, c = i % d;
+        const int t = lb * BS + r;
+        if (t >= ctx)
+            continue;
+        vo[(((size_t)b * hkv + h) * lmax + t) * d + c] = vl[(((size_t)e * hkv + h) * d + c) * BS + r];
+    }
 }
 
 // grid = (ceil(Lmax/16), Hkv, B): one 16-token block of one (request, head) per workgroup
@@ -305,6 +336,10 @@ kvp_status kv_gather(const kvp_cache_desc *cache, int32_t layer, const int32_t *
                        (const i32x4 *)cache->v_pool + layer * layer_chunks, d_block_table,
                        max_blocks, d_context_lens, hkv, Lmax, nch, cache->num_blocks,
                        (i32x4 *)k_out, (i32x4 *)v_out);
+    if (cache->dims.dtype == KVP_I8) // V codes are stored dim-major: rewrite them token-major
+        hipLaunchKernelGGL(gather_v_i8_kernel, grid, dim3(256), 0, (hipStream_t)stream,
+                           (const char *)cache->v_pool + layer * layer_chunks * 16, d_block_table, max_blocks,
+                           d_context_lens, hkv, Lmax, cache->dims.head_dim, cache->num_blocks, (char *)v_out);
     return launched("kv_gather");
 }
 

@@ -182,16 +182,19 @@ __device__ __forceinline__ void merge_column(const float *part, int pbase, int n
 //
 // Tile t = TT tokens = blocks (TT / 16) t .. of the item.  Lane (col, grp) = (lane % 16,
 // lane / 16).  MFMA column col is query row col of the item (member col / G, head col % G).
-// K and V tiles are read by the products as TT rows of 2 HD bytes of fp16; 16-byte chunk c
-// of row r is stored at chunk slot swz<HD>(c, r).  An fp16 cache is DMA'd straight into
-// that layout (the ring slot is the tile).  An int8 cache (I8) is DMA'd as rows of HD codes
-// into the ring, with the tile's row scales (K scales of tile row tt at byte 2 tt of the
-// scale slot, V scales at 32 KB + 2 tt), and each tile is reconstructed (code * scale,
-// rounded once to fp16) into the staging tiles kst / vst before the products.
+// fp16 cache: K and V tiles sit in LDS as TT rows of 2 HD bytes; 16-byte chunk c of row r
+// is stored at chunk slot swz<HD>(c, r); the score MFMA's row m of 16-key block kb is tile
+// row 16 kb + m, and V^T comes from transposing reads.
+// int8 cache (I8): K rows of HD codes (16-byte chunk c of row r at slot swz8<HD>(c, r)), V
+// blocks dim-major (HD rows of 16 codes per block, as the cache stores them), and the
+// tile's row scales (K scales of tile row tt at byte 2 tt of the scale slot, V scales at
+// 32 KB + 2 tt).  The score MFMA's row m of block kb is tile row 32 (kb / 2) + 8 (m / 4) +
+// 4 (kb % 2) + m % 4, so that lane group grp's probabilities of k-step ks are the eight
+// consecutive tokens 32 ks + 8 grp + s, whose V codes of one dimension are eight
+// consecutive bytes.  Codes become fp16 operands in registers: code * scale, rounded once.
 template <int G, bool SHARED, int NBUF, int TT, int HD, bool I8, typename Addr>
 __device__ __forceinline__ void run_item(const DecodeParams &P, const Addr &A, const PlanView &PV,
-                                         const Item &it, int rv, char *kring, char *vring, char *sring,
-                                         char *kst, char *vst)
+                                         const Item &it, int rv, char *kring, char *vring, char *sring)
 {
     static_assert(TT == 32 || TT == 64, "tiles of 32 or 64 tokens");
     static_assert(HD == 64 || HD == 128, "head dimension 64 or 128");
@@ -211,6 +214,7 @@ __device__ __forceinline__ void run_item(const DecodeParams &P, const Addr &A, c
     constexpr int IPBQ = BS / RPIQ;    // 1 KB loads per block and tensor
     constexpr int SLOTQ = TT * RQ;     // bytes of one ring slot per tensor
     constexpr int NDMA = 2 * KB * IPBQ + (I8 ? 1 : 0); // loads per tile (+ the row scales)
+    constexpr int VBLK = BS * HD;      // int8: bytes of one dim-major V block (per KV head)
     static_assert(!I8 || Addr::paged, "int8 caches are paged");
     static_assert(I8 || (RQ == RB && IPBQ == IPB), "fp16 ring = tile");
     const int lane = threadIdx.x;
@@ -303,16 +307,19 @@ __device__ __forceinline__ void run_item(const DecodeParams &P, const Addr &A, c
             for (int h = 0; h < IPBQ; ++h) {
                 const int r = RPIQ * h + lane / CPQ;
                 const int sr = ok ? A.row(lb, r) : A.safe_row(r);
-                size_t off; // bytes
-                if constexpr (I8)
-                    off = (brow[kb] + sr) * HD + (lane % CPQ) * 16;
-                else
+                size_t off, voff; // bytes
+                if constexpr (I8) {
+                    off = (brow[kb] + sr) * HD + swz8<HD>(lane % CPQ, 16 * kb + r) * 16;
+                    voff = brow[kb] * HD + h * 1024 + lane * 16; // dim-major block, linear
+                } else {
                     off = ((brow[kb] + sr) * HD + swz<HD>(lane & (CPR - 1), r) * 8) * sizeof(f16);
+                    voff = off;
+                }
                 const int i = IPBQ * kb + h;
                 __builtin_amdgcn_global_load_lds((const void *)(kc + off),
                                                  (__attribute__((address_space(3))) void *)(kd + i * 1024),
                                                  16, 0, 0);
-                __builtin_amdgcn_global_load_lds((const void *)(vc + off),
+                __builtin_amdgcn_global_load_lds((const void *)(vc + voff),
                                                  (__attribute__((address_space(3))) void *)(vd + i * 1024),
                                                  16, 0, 0);
             }
@@ -344,8 +351,8 @@ __device__ __forceinline__ void run_item(const DecodeParams &P, const Addr &A, c
     const f16x8 ones = {1, 1, 1, 1, 1, 1, 1, 1};
 
     auto compute = [&](int t) {
-        char *kt = I8 ? kst : kring + (t % NBUF) * SLOT; // fp16 tiles read by the products
-        char *vt = I8 ? vst : vring + (t % NBUF) * SLOT;
+        char *kt = kring + (t % NBUF) * SLOT; // fp16 cache: the tiles read by the products
+        char *vt = vring + (t % NBUF) * SLOT;
         const int tb = BS * (it.blk0 + KB * t); // position of tile row 0
         bool bok[KB];
         bool all_ok = true;
@@ -396,83 +403,143 @@ __device__ __forceinline__ void run_item(const DecodeParams &P, const Addr &A, c
             char *vq = vring + (t % NBUF) * SLOTQ;
             char *sq = sring + (t % NBUF) * 1024;
             // the new token of this step: codes and scale into the ring slot and the cache
+            // (K row-major, V dim-major: one byte per dimension)
             if (app) {
                 const int pos = it.end - 1, r = pos - tb;
                 if (r >= 0 && r < TT) {
                     const int j = KB * t + (r >> 4);
                     const int e = ent(j);
                     if (lane < 2 * CPR && j < it.nblk && A.valid(e)) {
-                        const int ch = lane & (CPR - 1); // 8 values per lane
+                        const int ch = lane & (CPR - 1); // dims 8 ch .. 8 ch + 7
                         const int lb = it.blk0 + j;
-                        const size_t rowi = A.block_row(it.b, it.g, lb, e) + A.row(lb, r & 15);
-                        lds_store_b64((lane < CPR ? kq : vq) + r * RQ + ch * 8, ncodes);
-                        const uintptr_t kb = (uintptr_t)P.kc_w, vb = (uintptr_t)P.vc_w;
-                        const uintptr_t base = kb + ((vb - kb) & (uintptr_t)(-(intptr_t)(lane >= CPR)));
-                        *(__attribute__((address_space(1))) u32x2 *)(base + rowi * HD + ch * 8) = ncodes;
+                        const size_t brow = A.block_row(it.b, it.g, lb, e);
+                        if (lane < CPR) {
+                            lds_store_b64(kq + r * RQ + swz8<HD>(ch >> 1, r) * 16 + (ch & 1) * 8, ncodes);
+                            *(__attribute__((address_space(1))) u32x2 *)((uintptr_t)P.kc_w + (brow + (r & 15)) * HD +
+                                                                          ch * 8) = ncodes;
+                        } else {
+                            char *vg = (char *)P.vc_w + brow * HD + (r & 15);
+#pragma unroll
+                            for (int i = 0; i < 8; ++i) {
+                                const unsigned b = (ncodes[i >> 2] >> (8 * (i & 3))) & 0xff;
+                                lds_store_b8(vq + (r >> 4) * VBLK + (8 * ch + i) * BS + (r & 15), b);
+                                *(__attribute__((address_space(1))) unsigned char *)(vg + (8 * ch + i) * BS) =
+                                    (unsigned char)b;
+                            }
+                        }
                         if (ch == 0) {
                             lds_store_b16(sq + (lane < CPR ? 0 : 32 * KB) + 2 * r, nscale);
                             const uintptr_t ks = (uintptr_t)P.ksc_w, vs = (uintptr_t)P.vsc_w;
                             const uintptr_t sb = ks + ((vs - ks) & (uintptr_t)(-(intptr_t)(lane >= CPR)));
-                            *(__attribute__((address_space(1))) unsigned short *)(sb + rowi * sizeof(f16)) =
+                            *(__attribute__((address_space(1))) unsigned short *)(sb + (brow + (r & 15)) * sizeof(f16)) =
                                 (unsigned short)nscale;
                         }
                     }
                 }
             }
-            wave_lds_sync();
-            // reconstruction: 16 codes of one row per lane and step, K chunks then V chunks;
-            // code * scale rounded once to fp16 into the tile layout.  Value rows no column
-            // may use become zeros (their scales can be anything).
-            constexpr int NCH = 2 * TT * CPQ / 64; // chunks per lane
-            static_assert(NCH % 2 == 0, "K and V chunks split evenly");
-            i32x4 raw[NCH];
-            unsigned sc[NCH];
-#pragma unroll
-            for (int k = 0; k < NCH; ++k) {
-                const bool isv = k >= NCH / 2;
-                const int ci = lane + 64 * (isv ? k - NCH / 2 : k), r = ci / CPQ, cq = ci % CPQ;
-                raw[k] = lds_i128((isv ? vq : kq) + r * RQ + cq * 16);
-                sc[k] = lds_u16(sq + (isv ? 32 * KB : 0) + 2 * r);
-            }
-            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-#pragma unroll
-            for (int k = 0; k < NCH; ++k)
-                asm volatile("" : "+v"(raw[k]), "+v"(sc[k]));
-            typedef f16 f16x2_ __attribute__((ext_vector_type(2)));
-            const f16x2_ bias = {(f16)1152.f, (f16)1152.f};
-#pragma unroll
-            for (int k = 0; k < NCH; ++k) {
-                const bool isv = k >= NCH / 2;
-                const int ci = lane + 64 * (isv ? k - NCH / 2 : k), r = ci / CPQ, cq = ci % CPQ;
-                const unsigned s2u = sc[k] | (sc[k] << 16);
-                const f16x2_ s2 = __builtin_bit_cast(f16x2_, s2u);
-                unsigned h[8];
-#pragma unroll
-                for (int w = 0; w < 4; ++w) {
-                    // code + 128 as the low byte of the fp16 number 1024 + byte, minus 1152
-                    const unsigned x = (unsigned)raw[k][w] ^ 0x80808080u;
-                    const unsigned lo = __builtin_amdgcn_perm(0x64646464u, x, 0x04010400u);
-                    const unsigned hi = __builtin_amdgcn_perm(0x64646464u, x, 0x04030402u);
-                    const f16x2_ vlo = (__builtin_bit_cast(f16x2_, lo) - bias) * s2;
-                    const f16x2_ vhi = (__builtin_bit_cast(f16x2_, hi) - bias) * s2;
-                    h[2 * w] = __builtin_bit_cast(unsigned, vlo);
-                    h[2 * w + 1] = __builtin_bit_cast(unsigned, vhi);
-                }
-                i32x4 o0 = {(int)h[0], (int)h[1], (int)h[2], (int)h[3]};
-                i32x4 o1 = {(int)h[4], (int)h[5], (int)h[6], (int)h[7]};
-                if (isv && !full && !row_used(r)) {
-                    o0 = i32x4{0, 0, 0, 0};
-                    o1 = i32x4{0, 0, 0, 0};
-                }
-                char *dt = isv ? vt : kt;
-                lds_store_b128(dt + r * RB + swz<HD>(2 * cq, r) * 16, o0);
-                lds_store_b128(dt + r * RB + swz<HD>(2 * cq + 1, r) * 16, o1);
-            }
         }
         wave_lds_sync();
 
+        f16x8 kop[KB][KD]; // A of the score MFMA
+        f16x8 vop[KS][NDB]; // A of the value MFMA (V^T)
+        if constexpr (I8) {
+            char *kq = kring + (t % NBUF) * SLOTQ;
+            char *vq = vring + (t % NBUF) * SLOTQ;
+            char *sq = sring + (t % NBUF) * 1024;
+            // K: lane (col, grp) of block kb reads tile row 32 (kb/2) + 8 (col/4) + 4 (kb%2) +
+            // col%4, dims 32 ks + 8 grp .. (8 bytes), and that row's scale
+            u32x2 kraw[KB][KD];
+            unsigned ksc[KB];
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) {
+                const int rt = 32 * (kb >> 1) + 8 * (col >> 2) + 4 * (kb & 1) + (col & 3);
+#pragma unroll
+                for (int ks = 0; ks < KD; ++ks)
+                    kraw[kb][ks] = lds_b64(kq + rt * RQ + swz8<HD>(2 * ks + (grp >> 1), rt) * 16 + (grp & 1) * 8);
+                ksc[kb] = lds_u16(sq + 2 * rt);
+            }
+            // V^T: lane (col, grp) of k-step ks reads dimension 16 db + col of tokens 32 ks +
+            // 8 grp .. + 7 (8 consecutive bytes of the dim-major block), and their 8 scales
+            u32x2 vraw8[KS][NDB];
+            i32x4 vsc[KS];
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                vsc[ks] = lds_i128(sq + 32 * KB + 2 * (32 * ks + 8 * grp));
+#pragma unroll
+                for (int db = 0; db < NDB; ++db)
+                    vraw8[ks][db] = lds_b64(vq + (2 * ks + (grp >> 1)) * VBLK + (16 * db + col) * BS + 8 * (grp & 1));
+            }
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) {
+#pragma unroll
+                for (int ks = 0; ks < KD; ++ks)
+                    asm volatile("" : "+v"(kraw[kb][ks]));
+                asm volatile("" : "+v"(ksc[kb]));
+            }
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                asm volatile("" : "+v"(vsc[ks]));
+#pragma unroll
+                for (int db = 0; db < NDB; ++db)
+                    asm volatile("" : "+v"(vraw8[ks][db]));
+            }
+            // value rows no column may use: their scales (which can be anything) become 0
+            if (!full) {
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) {
+                    const int tb0 = 32 * ks + 8 * grp; // tile row of slot 0
+                    bool okb = bok[0];
+#pragma unroll
+                    for (int q = 1; q < KB; ++q)
+                        okb = (tb0 >> 4) == q ? bok[q] : okb;
+#pragma unroll
+                    for (int w = 0; w < 4; ++w) {
+                        unsigned m = 0;
+                        if (okb && tb + tb0 + 2 * w < rend)
+                            m |= 0xffffu;
+                        if (okb && tb + tb0 + 2 * w + 1 < rend)
+                            m |= 0xffff0000u;
+                        vsc[ks][w] = (int)((unsigned)vsc[ks][w] & m);
+                    }
+                }
+            }
+            // codes -> fp16: code + 128 as the low byte of the fp16 number 1024 + byte, minus
+            // 1152 (exact), times the scale (one rounding)
+            typedef f16 f16x2_ __attribute__((ext_vector_type(2)));
+            const f16x2_ bias = {(f16)1152.f, (f16)1152.f};
+            auto dequant8 = [&](u32x2 code, const unsigned (&sc)[4]) -> f16x8 {
+                unsigned h[4];
+#pragma unroll
+                for (int w = 0; w < 2; ++w) {
+                    const unsigned x = code[w] ^ 0x80808080u;
+                    const unsigned lo = __builtin_amdgcn_perm(0x64646464u, x, 0x04010400u);
+                    const unsigned hi = __builtin_amdgcn_perm(0x64646464u, x, 0x04030402u);
+                    h[2 * w] = __builtin_bit_cast(
+                        unsigned, (__builtin_bit_cast(f16x2_, lo) - bias) * __builtin_bit_cast(f16x2_, sc[2 * w]));
+                    h[2 * w + 1] = __builtin_bit_cast(
+                        unsigned, (__builtin_bit_cast(f16x2_, hi) - bias) * __builtin_bit_cast(f16x2_, sc[2 * w + 1]));
+                }
+                return __builtin_bit_cast(f16x8, i32x4{(int)h[0], (int)h[1], (int)h[2], (int)h[3]});
+            };
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) {
+                const unsigned s2 = ksc[kb] | (ksc[kb] << 16);
+                const unsigned sc[4] = {s2, s2, s2, s2};
+#pragma unroll
+                for (int ks = 0; ks < KD; ++ks)
+                    kop[kb][ks] = dequant8(kraw[kb][ks], sc);
+            }
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                const unsigned sc[4] = {(unsigned)vsc[ks][0], (unsigned)vsc[ks][1], (unsigned)vsc[ks][2],
+                                        (unsigned)vsc[ks][3]};
+#pragma unroll
+                for (int db = 0; db < NDB; ++db)
+                    vop[ks][db] = dequant8(vraw8[ks][db], sc);
+            }
+        } else {
         // K rows (A of the score MFMA): row 16 kb + col, dims 32 ks + 8 grp .. (chunk 4 ks + grp)
-        f16x8 kop[KB][KD];
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
             const int r = kb * 16 + col;
@@ -508,10 +575,13 @@ __device__ __forceinline__ void run_item(const DecodeParams &P, const Addr &A, c
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-            for (int db = 0; db < NDB; ++db)
+            for (int db = 0; db < NDB; ++db) {
                 asm volatile("" : "+v"(vraw[ks][db][0]), "+v"(vraw[ks][db][1]));
+                vop[ks][db] = __builtin_shufflevector(vraw[ks][db][0], vraw[ks][db][1], 0, 1, 2, 3, 4, 5, 6, 7);
+            }
+        }
 
-        // scores: sacc[kb][i] = S[token 16 kb + 4 grp + i][column col] (unscaled)
+        // scores: sacc[kb][i] = S[token of MFMA row 4 grp + i of block kb][column col] (unscaled)
         f32x4 sacc[KB];
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
@@ -523,12 +593,17 @@ __device__ __forceinline__ void run_item(const DecodeParams &P, const Addr &A, c
         }
         if (!full) {
 #pragma unroll
-            for (int kb = 0; kb < KB; ++kb)
+            for (int kb = 0; kb < KB; ++kb) {
+                // tile row of sacc[kb][0] and its block
+                const int r0 = I8 ? 32 * (kb >> 1) + 8 * grp + 4 * (kb & 1) : 16 * kb + 4 * grp;
+                bool okb = bok[0];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int tok = tb + kb * 16 + grp * 4 + i;
-                    sacc[kb][i] = (bok[kb] && tok < lim) ? sacc[kb][i] : -INFINITY;
-                }
+                for (int q = 1; q < KB; ++q)
+                    okb = (r0 >> 4) == q ? bok[q] : okb;
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    sacc[kb][i] = (okb && tb + r0 + i < lim) ? sacc[kb][i] : -INFINITY;
+            }
         }
         float mt;
         if constexpr (KB == 4) {
@@ -557,8 +632,9 @@ __device__ __forceinline__ void run_item(const DecodeParams &P, const Addr &A, c
             mref = mn;
         }
         const float mc = mref == -INFINITY ? 0.f : mref;
-        // P^T operand of k-step ks, slot s = p of token 16 (2 ks + s / 4) + 4 grp + s % 4:
-        // sacc[2 ks + s / 4][s % 4] -- already in this lane; rounded once to fp16
+        // P^T operand of k-step ks, slot s = sacc[2 ks + s / 4][s % 4] -- already in this lane
+        // (tile row 16 (2 ks + s / 4) + 4 grp + s % 4 for an fp16 cache, 32 ks + 8 grp + s for
+        // int8); rounded once to fp16
         f16x8 pop[KS];
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
@@ -573,10 +649,8 @@ __device__ __forceinline__ void run_item(const DecodeParams &P, const Addr &A, c
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
-            for (int db = 0; db < NDB; ++db) {
-                const f16x8 vop = __builtin_shufflevector(vraw[ks][db][0], vraw[ks][db][1], 0, 1, 2, 3, 4, 5, 6, 7);
-                acc[db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vop, pop[ks], acc[db], 0, 0, 0);
-            }
+            for (int db = 0; db < NDB; ++db)
+                acc[db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vop[ks][db], pop[ks], acc[db], 0, 0, 0);
             accl = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, pop[ks], accl, 0, 0, 0);
         }
         wait_lds(); // this slot is refilled by a later DMA
@@ -686,10 +760,8 @@ __global__ __launch_bounds__(64) void decode_f16_kernel(DecodeParams P, Addr A, 
     constexpr int EB = I8 ? 1 : 2; // bytes per cached value
     __shared__ __attribute__((aligned(16))) char kring[NBUF * TT * EB * HD];
     __shared__ __attribute__((aligned(16))) char vring[NBUF * TT * EB * HD];
-    // int8 only: row scales per ring slot, and the reconstructed fp16 tiles
+    // int8 only: the tile's row scales per ring slot
     __shared__ __attribute__((aligned(16))) char sring[I8 ? NBUF * 1024 : 16];
-    __shared__ __attribute__((aligned(16))) char kst[I8 ? TT * 2 * HD : 16];
-    __shared__ __attribute__((aligned(16))) char vst[I8 ? TT * 2 * HD : 16];
     const int lane = threadIdx.x;
     Item it;
     int rv;
@@ -715,12 +787,12 @@ __global__ __launch_bounds__(64) void decode_f16_kernel(DecodeParams P, Addr A, 
         if (flags & F_SHARED) {
             if (it.nmem * G > 16 || it.slot < 0)
                 return;
-            run_item<G, true, NBUF, TT, HD, I8>(P, A, PV, it, rv, kring, vring, sring, kst, vst);
+            run_item<G, true, NBUF, TT, HD, I8>(P, A, PV, it, rv, kring, vring, sring);
             return;
         }
         if (it.nmem != 1)
             return;
-        run_item<G, false, NBUF, TT, HD, I8>(P, A, PV, it, rv, kring, vring, sring, kst, vst);
+        run_item<G, false, NBUF, TT, HD, I8>(P, A, PV, it, rv, kring, vring, sring);
     } else {
         const int pair = blockIdx.x / PV.ipp;
         const int k = blockIdx.x - pair * PV.ipp;
@@ -745,7 +817,7 @@ __global__ __launch_bounds__(64) void decode_f16_kernel(DecodeParams P, Addr A, 
         it.slot = it.pbase + k;
         const int j = lane - R_ENT;
         rv = (j >= 0 && j < it.nblk) ? A.entry(it.b, it.blk0 + j) : -1;
-        run_item<G, false, NBUF, TT, HD, I8>(P, A, PV, it, rv, kring, vring, sring, kst, vst);
+        run_item<G, false, NBUF, TT, HD, I8>(P, A, PV, it, rv, kring, vring, sring);
     }
 }
 

@@ -67,6 +67,16 @@ __device__ inline void lds_store_b16(char *p, unsigned v)
 {
     asm volatile("ds_write_b16 %0, %1" ::"v"(lds_addr(p)), "v"(v) : "memory");
 }
+__device__ inline void lds_store_b8(char *p, unsigned v)
+{
+    asm volatile("ds_write_b8 %0, %1" ::"v"(lds_addr(p)), "v"(v) : "memory");
+}
+__device__ inline u32x2 lds_b64(const char *p)
+{
+    u32x2 r;
+    asm volatile("ds_read_b64 %0, %1" : "=v"(r) : "v"(lds_addr(p)));
+    return r;
+}
 __device__ inline i32x4 lds_i128(const char *p)
 {
     i32x4 r;
@@ -123,6 +133,17 @@ template <int HD> __device__ inline int swz(int c, int r)
 {
     static_assert(HD == 64 || HD == 128, "rows of 64 or 128 values");
     return HD == 64 ? c ^ (r & 7) : c ^ ((r & 7) << 1);
+}
+
+// The same for int8 rows of HD bytes (64 or 128), read 8 bytes per lane by 16 lanes at one
+// 8-byte piece of rows 8 (c / 4) + 4 h + c % 4 (c = 0..15; the score operand's row order):
+// 64-byte rows fall on four bank quarters by r mod 4, and XOR with (r / 8) mod 4 spreads
+// the four row groups; 128-byte rows fall on two bank halves by r mod 2, and the XOR with
+// a 3-bit value of r / 2 and r / 8 spreads the eight rows of each half.
+template <int HD> __device__ inline int swz8(int c, int r)
+{
+    static_assert(HD == 64 || HD == 128, "rows of 64 or 128 bytes");
+    return HD == 64 ? c ^ ((r >> 3) & 3) : c ^ (((r >> 1) & 1) | ((r >> 2) & 6));
 }
 
 // max over lanes col, col + 16, col + 32, col + 48 (the k-groups of one MFMA column): swap
