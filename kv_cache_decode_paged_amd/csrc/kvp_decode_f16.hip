@@ -666,8 +666,10 @@ __device__ __forceinline__ void run_item(const DecodeParams &P, const Addr &A, c
         if (t + NBUF - 1 < nt)
             issue(t + NBUF - 1);
         const int ahead = min(nt - 1 - t, NBUF - 1); // tiles issued after this one
-        if (ahead >= 2)
-            wait_vm<2 * NDMA>();
+        if (ahead >= 3)
+            wait_vm<(NBUF > 3 ? 3 : 0) * NDMA>();
+        else if (ahead == 2)
+            wait_vm<(NBUF > 2 ? 2 : 0) * NDMA>();
         else if (ahead == 1)
             wait_vm<NDMA>();
         else
@@ -756,7 +758,7 @@ template <int G, int NBUF, int TT, int HD, bool I8, bool PLANNED, typename Addr>
 __global__ __launch_bounds__(64) void decode_f16_kernel(DecodeParams P, Addr A, PlanView PV)
 {
     static_assert(G >= 1 && G <= MAXG, "group size");
-    static_assert(NBUF >= 2 && NBUF <= 3, "ring depth");
+    static_assert(NBUF >= 2 && NBUF <= 4, "ring depth");
     constexpr int EB = I8 ? 1 : 2; // bytes per cached value
     __shared__ __attribute__((aligned(16))) char kring[NBUF * TT * EB * HD];
     __shared__ __attribute__((aligned(16))) char vring[NBUF * TT * EB * HD];
