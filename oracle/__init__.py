@@ -12,6 +12,8 @@ Contents
   * opcount.py : the multiply-accumulate cost model of cached vs uncached generation.
   * kvquant.py : symmetric absmax quantization of cache rows (int8 codes, fp16 scale per
                  row) and its exact reconstruction.
+  * batching.py: static vs continuous batching over a page pool (step-by-step schedule,
+                 latencies, pages, utilisation) and the naive vs paged utilisation formulas.
 
 Parity status: every function here is pinned by a CPU test (see tests/test_oracle_*.py);
 none is "parity unpinned".
