@@ -371,6 +371,64 @@ def bench_chunked_prefill(args):
     print(json.dumps(line), flush=True)
 
 
+def bench_batching(args):
+    """Continuous vs static batching over the block pool (host scheduler, no GPU): 2000
+    requests with SECTION 4's response lengths (normal(500, 200) clipped to 200..2048, seeded)
+    and 0..255-token prompts on a pool of 8192 blocks of 16 tokens (the naive reservation of
+    64 requests of 2048 tokens).  Times the library's scheduler against the oracle's loop."""
+    import numpy as np
+
+    import kv_cache_decode_paged_amd as kvp
+    from oracle import batching as Bt
+    rng = np.random.default_rng(args.seed)
+    n, blocks = 2000, 8192
+    outs = [int(x) for x in Bt.response_lengths(n, seed=args.seed)]
+    prompts = [int(x) for x in rng.integers(0, 256, size=n)]
+    runs = {}
+    for name, slots, pol, alloc in (("paged continuous 160 places", 160, kvp.SCHED_CONTINUOUS, kvp.ALLOC_PAGED),
+                                    ("paged static 160 places", 160, kvp.SCHED_STATIC, kvp.ALLOC_PAGED),
+                                    ("naive continuous 64 places", 64, kvp.SCHED_CONTINUOUS, kvp.ALLOC_NAIVE),
+                                    ("naive static 64 places", 64, kvp.SCHED_STATIC, kvp.ALLOC_NAIVE)):
+        t0 = time.perf_counter()
+        res, lat, svc = kvp.sched_simulate(prompts, outs, slots, pol, alloc, 2048 + 256, 16, blocks)
+        dt = time.perf_counter() - t0
+        runs[name] = (res, dt)
+        print(f"[bench] {name}: {res.steps} steps, {res.tokens / res.steps:.1f} tokens/step, mean service "
+              f"{res.mean_service:.1f} steps, utilisation {res.mean_utilisation * 100:.1f} %, peak blocks "
+              f"{res.peak_blocks}, deferrals {res.deferrals}, stalls {res.stalls}; {dt * 1e3:.1f} ms host",
+              file=sys.stderr, flush=True)
+    main_res, main_dt = runs["paged continuous 160 places"]
+    value = main_res.steps / main_dt
+    cpu = None
+    if not args.no_cpu_baseline:  # the oracle on the first 500 requests of the same run
+        m = 500
+        t0 = time.perf_counter()
+        w = Bt.simulate(prompts[:m], outs[:m], 160, Bt.CONTINUOUS, Bt.PAGED, 2048 + 256, 16, blocks)
+        dt = time.perf_counter() - t0
+        cpu = {"value": round(w["steps"] / dt, 2), "unit": "simulated steps/s", "cores": 1, "kind": "oracle",
+               "sample": f"the first {m} of the {n} requests, paged continuous, 160 places (pure-Python loop)"}
+    st = runs["paged static 160 places"][0]
+    nv = runs["naive continuous 64 places"][0]
+    line = {
+        "metric": "continuous batching over the block pool: simulated decode steps per second (host scheduler)",
+        "value": round(value, 2), "unit": "steps/s", "n_gpus": 1, "steps": 1, "warmup": 0,
+        "ms_per_step": round(main_dt * 1e3 / max(main_res.steps, 1), 6), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "int64", "data": "synthetic",
+        "config": {"workload": f"{n} requests, outputs normal(500, 200) clipped to 200..2048, prompts 0..255, "
+                               f"pool of {blocks} blocks x 16 tokens",
+                   "requests": n, "blocks": blocks},
+        "continuous_vs_static_throughput": round(st.steps / main_res.steps, 3),
+        "continuous_vs_static_service": round(st.mean_service / main_res.mean_service, 3),
+        "paged_vs_naive_throughput": round(nv.steps / main_res.steps, 3),
+        "utilisation_paged_pct": round(main_res.mean_utilisation * 100, 2),
+        "utilisation_naive_pct": round(nv.mean_utilisation * 100, 2),
+        "roofline": None,
+        "roofline_note": "host-only scheduler: no GPU kernel runs in this workload",
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -387,10 +445,11 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-share", action="store_true", help="plans without shared-prefix items")
     ap.add_argument("--seed", type=int, default=42)
-    ap.add_argument("--workload", choices=["decode", "prefill", "chunked_prefill"], default="decode",
+    ap.add_argument("--workload", choices=["decode", "prefill", "chunked_prefill", "batching"], default="decode",
                     help="decode: the batch-200 paged decode step (default); prefill: packed causal "
                          "prefill of 16 x 4096 tokens; chunked_prefill: 16 x 512-token chunks after a "
-                         "shared 2048-token prefix in the paged cache")
+                         "shared 2048-token prefix in the paged cache; batching: continuous vs static "
+                         "batching over the block pool (host scheduler)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -401,6 +460,9 @@ def main():
     if args.kv_dtype == "int8" and args.workload != "decode":
         print("--kv-dtype int8 applies to the decode workload", flush=True)
         sys.exit(2)
+    if args.workload == "batching":
+        bench_batching(args)
+        return
     if args.workload == "prefill":
         bench_prefill(args)
         return

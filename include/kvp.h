@@ -196,6 +196,63 @@ int64_t kv_bytes_per_token(int32_t num_layers, int32_t num_kv_heads, int32_t hea
                            int32_t elem_bytes);
 
 /* ======================================================================================
+ * Batching over the block pool  ([CHAP] batching passage; [PAGED] SECTION 1, 2 and 4)
+ * A step-by-step schedule of n requests on `slots` places, driving a private kvp_pool of
+ * num_blocks blocks of block_size tokens:
+ *   - all requests are queued at step 0, in index order;
+ *   - at the start of a step, free places admit queued requests in order -- with
+ *     KVP_SCHED_STATIC only when no place is occupied (the previous batch was returned),
+ *     with KVP_SCHED_CONTINUOUS whenever a place is free; admission allocates the prompt
+ *     (KVP_ALLOC_PAGED: ceil(prompt / block_size) blocks) or max_seq_len tokens
+ *     (KVP_ALLOC_NAIVE, the contiguous worst-case reservation) and stops at the first
+ *     request the pool cannot hold (a deferral);
+ *   - in a step every admitted, unfinished request produces one token (paged: through
+ *     block_table_append_slot; a request whose token needs a block the pool cannot give
+ *     stalls for the step);
+ *   - a request finishes in the step that produces its last token; continuous: it is
+ *     returned at once and its place and blocks are free for the next step; static: the
+ *     batch is returned, and its blocks freed, when its last member finishes (the others
+ *     hold their places as padding until then);
+ *   - latency[i] = number of the step that returns request i (from 1); service[i] = steps
+ *     from its admission to its return; utilisation after a step = resident tokens /
+ *     (blocks held * block_size), averaged over steps.
+ * OOM when every admitted request waits for a block and nothing can be admitted (no
+ * preemption); INVALID for bad arguments (output_lens >= 1, prompts >= 0, and with naive
+ * allocation prompt + output <= max_seq_len).  latency / service: host int32 [n] or NULL.
+ * ==================================================================================== */
+#define KVP_SCHED_STATIC 0
+#define KVP_SCHED_CONTINUOUS 1
+#define KVP_ALLOC_PAGED 0
+#define KVP_ALLOC_NAIVE 1
+
+typedef struct {
+    int32_t slots;       /* places in the batch                              */
+    int32_t policy;      /* KVP_SCHED_STATIC or KVP_SCHED_CONTINUOUS          */
+    int32_t alloc;       /* KVP_ALLOC_PAGED or KVP_ALLOC_NAIVE                */
+    int32_t max_seq_len; /* naive reservation per request (tokens)            */
+    int32_t block_size;  /* tokens per block                                  */
+    int32_t num_blocks;  /* blocks in the pool                                */
+} kvp_sched_config;
+
+typedef struct {
+    int64_t steps;              /* steps until every request was returned            */
+    int64_t tokens;             /* tokens produced (sum of output_lens)              */
+    int64_t busy_slot_steps;    /* tokens produced, i.e. places that did work        */
+    int64_t padding_slot_steps; /* places held by finished members of a static batch */
+    int64_t peak_blocks;        /* most blocks held at the end of a step             */
+    int64_t deferrals;          /* admissions stopped by a full pool                 */
+    int64_t stalls;             /* tokens delayed by a full pool                     */
+    int64_t max_latency;
+    double mean_latency;        /* steps, from arrival                               */
+    double mean_service;        /* steps, from admission                             */
+    double mean_utilisation;    /* mean over steps of resident / held tokens         */
+} kvp_sched_result;
+
+kvp_status sched_simulate(const kvp_sched_config *cfg, const int32_t *prompt_lens,
+                          const int32_t *output_lens, int32_t n, int32_t *latency,
+                          int32_t *service, kvp_sched_result *res);
+
+/* ======================================================================================
  * Device operations (HIP kernels for gfx950)
  * ==================================================================================== */
 

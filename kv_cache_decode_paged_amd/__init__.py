@@ -78,6 +78,20 @@ class kvp_decode_plan(ctypes.Structure):
 
 PLAN_SHARE_PREFIX = 1
 
+SCHED_STATIC, SCHED_CONTINUOUS = 0, 1
+ALLOC_PAGED, ALLOC_NAIVE = 0, 1
+
+
+class kvp_sched_config(ctypes.Structure):
+    _fields_ = [("slots", ctypes.c_int32), ("policy", ctypes.c_int32), ("alloc", ctypes.c_int32),
+                ("max_seq_len", ctypes.c_int32), ("block_size", ctypes.c_int32), ("num_blocks", ctypes.c_int32)]
+
+
+class kvp_sched_result(ctypes.Structure):
+    _fields_ = [(f, ctypes.c_int64) for f in ("steps", "tokens", "busy_slot_steps", "padding_slot_steps",
+                                              "peak_blocks", "deferrals", "stalls", "max_latency")] + \
+               [(f, ctypes.c_double) for f in ("mean_latency", "mean_service", "mean_utilisation")]
+
 _i32 = ctypes.c_int32
 _i64 = ctypes.c_int64
 _p = ctypes.c_void_p
@@ -124,6 +138,7 @@ _sig("paged_decode_append_attention", _i32, [ctypes.POINTER(kvp_cache_desc), _i3
 _sig("decode_plan_bytes", _sz, [ctypes.POINTER(kvp_dims), _i32, _i32, _i32])
 _sig("decode_plan_build", _i32, [ctypes.POINTER(kvp_dims), _p, _i32, _p, _i32, _i32, ctypes.c_uint32, _i32, _p, _sz,
                                  ctypes.POINTER(kvp_decode_plan)])
+_sig("sched_simulate", _i32, [ctypes.POINTER(kvp_sched_config), _p, _p, _i32, _p, _p, ctypes.POINTER(kvp_sched_result)])
 _sig("decode_plan_workspace_bytes", _sz, [ctypes.POINTER(kvp_decode_plan)])
 _sig("paged_decode_attention_planned", _i32, [ctypes.POINTER(kvp_cache_desc), _i32, _p, _p, _p, _p,
                                               ctypes.POINTER(kvp_decode_plan), _p, _f32, _p, _sz, _p])
@@ -539,6 +554,24 @@ def paged_prefill_attention(cache: PagedKVCache, layer, q, block_table, context_
                                         _dev(cu_q, "cu_q", torch.int32), B, int(max_q), float(scale),
                                         _stream(stream)))
     return out
+
+
+def sched_simulate(prompt_lens, output_lens, slots, policy=SCHED_CONTINUOUS, alloc=ALLOC_PAGED, max_seq_len=2048,
+                   block_size=BLOCK, num_blocks=1 << 20):
+    """Static or continuous batching of the requests over a block pool (sched_simulate in
+    kvp.h).  Returns (kvp_sched_result, latency int32 [n], service int32 [n]) on the host."""
+    p = torch.as_tensor(prompt_lens, dtype=torch.int32).contiguous()
+    o = torch.as_tensor(output_lens, dtype=torch.int32).contiguous()
+    n = int(o.numel())
+    if p.numel() != n:
+        raise ValueError("sched_simulate: prompt_lens and output_lens differ in length")
+    lat = torch.zeros(max(n, 1), dtype=torch.int32)
+    svc = torch.zeros(max(n, 1), dtype=torch.int32)
+    cfg = kvp_sched_config(int(slots), int(policy), int(alloc), int(max_seq_len), int(block_size), int(num_blocks))
+    res = kvp_sched_result()
+    _check(_lib.sched_simulate(ctypes.byref(cfg), ctypes.c_void_p(p.data_ptr()), ctypes.c_void_p(o.data_ptr()), n,
+                               ctypes.c_void_p(lat.data_ptr()), ctypes.c_void_p(svc.data_ptr()), ctypes.byref(res)))
+    return res, lat[:n], svc[:n]
 
 
 def decode_merge_polls(polls=-1):
