@@ -46,7 +46,7 @@ constexpr int MAX_BUNDLE = 8; // shared items kept together on one XCD
 
 long long max_items(long long B, long long hkv, long long max_blocks)
 {
-    const long long ipp = std::max<long long>(1, (max_blocks + BPI - 1) / BPI);
+    const long long ipp = std::max<long long>(1, (max_blocks + SPLIT_BLOCKS - 1) / SPLIT_BLOCKS);
     // private items: at most ipp per pair; shared items: at most one set per two requests;
     // plus the padding that evens out the XCD queues and rounds them to whole CU rounds
     const long long work = B * hkv * ipp + (B / 2) * hkv * ipp;
