@@ -208,3 +208,26 @@ def test_zero_and_extreme_rows():
     torch.cuda.synchronize()
     assert not kc.cpu()[0, :, 3].any() and not vc.cpu()[0, :, 5].any()
     assert kc.cpu()[1, 0, 7, 9].item() == 127
+
+
+def test_planned_full_size_b200():
+    # the batch-200 step of the benchmark over an int8 cache: 24-layer pool (data in layers 0
+    # and 23), shared prefixes, the graph-style padded plan; all rows against the oracle
+    need_gpu()
+    pb = W.paged_batch(200)
+    say("int8 planned batch 200 (24-layer pool, data in layers 0 and 23)")
+    step = PagedStep(kvp, pb, layers=24, hq=14, hkv=2, dtype=I8, seed=31700, layers_with_data=[0, 23])
+    plan0, _ = kvp.decode_plan_build(14, 2, step.table.cpu(), step.ctx.cpu(), step.num_blocks, share_prefix=True)
+    plan, image = kvp.decode_plan_build(14, 2, step.table.cpu(), step.ctx.cpu(), step.num_blocks, share_prefix=True,
+                                        pad_items=plan0.n_items + 256)
+    dp = kvp.upload_plan(plan, image)
+    ws = kvp.make_plan_workspace(plan)
+    for l in (0, 23):
+        q = step.q(l).cuda()
+        o = kvp.paged_decode_attention_planned(step.cache, l, q, plan, dp, workspace=ws)
+        o2 = kvp.paged_decode_attention(step.cache, l, q, step.table, step.ctx)
+        torch.cuda.synchronize()
+        err = max_abs(to64(o), step.oracle(l))
+        say("int8 planned b200 layer", l, "max err", err)
+        assert err <= TOL[torch.float16]
+        assert max_abs(to64(o), to64(o2)) <= TOL[torch.float16]
