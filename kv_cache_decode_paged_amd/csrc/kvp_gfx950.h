@@ -6,6 +6,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <type_traits>
 
 namespace kvp {
 
@@ -54,6 +55,30 @@ __device__ inline f16x4 lds_tr16_b64(const char *p)
     f16x4 r;
     asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(r) : "v"(lds_addr(p)));
     return r;
+}
+// the same reads at an LDS byte address plus an immediate offset (the instruction's own
+// 16-bit offset field): one base register serves every read that differs by a constant
+template <int OFF> __device__ inline f16x8 lds_b128_at(unsigned addr)
+{
+    static_assert(OFF >= 0 && OFF < 65536, "ds offset field");
+    f16x8 r;
+    asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF));
+    return r;
+}
+template <int OFF> __device__ inline f16x4 lds_tr16_b64_at(unsigned addr)
+{
+    static_assert(OFF >= 0 && OFF < 65536, "ds offset field");
+    f16x4 r;
+    asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF));
+    return r;
+}
+// compile-time loop: f(integral_constant<int, I>) for I = B .. E - 1
+template <int B, int E, typename F> __device__ __forceinline__ void static_for(F &&f)
+{
+    if constexpr (B < E) {
+        f(std::integral_constant<int, B>{});
+        static_for<B + 1, E>(f);
+    }
 }
 __device__ inline void lds_store_b128(char *p, i32x4 v)
 {

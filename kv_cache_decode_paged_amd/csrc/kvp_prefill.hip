@@ -225,6 +225,24 @@ __global__ __launch_bounds__(256) void prefill_mfma_f16_kernel(PrefillArgs P)
     }
     const f16x8 ones = {1, 1, 1, 1, 1, 1, 1, 1};
 
+    // LDS byte addresses of this lane's operand reads in ring slot 0.  The swizzle depends
+    // on a row only through row % 8, which the 16-row steps leave alone, so K reads of one
+    // 32-dim step and V reads of one 16-dim block differ only by constants (the offset
+    // field): KD + NDB base registers per lane, moved to the tile's slot once per tile.
+    //   K: key 16 kb + col, chunk 4 ks + grp        -> kbase[ks] + 16 kb RB
+    //   V: key row 16 (2 ks + hh) + 4 grp + col / 4, chunk 2 db + (col % 4) / 2, half col % 2
+    //                                               -> vbase[db] + 16 (2 ks + hh) RB
+    unsigned kbase[KD], vbase[NDB];
+#pragma unroll
+    for (int ks = 0; ks < KD; ++ks)
+        kbase[ks] = lds_addr(kring) + col * RB + swz<D>(4 * ks + grp, col) * 16;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+        const int row = 4 * grp + (col >> 2);
+        const int ch = 2 * db + ((col & 3) >> 1);
+        vbase[db] = lds_addr(vring) + row * RB + swz<D>(ch, row) * 16 + (col & 1) * 8;
+    }
+
     issue(0);
     if (nt > 1)
         issue(1);
@@ -245,31 +263,32 @@ __global__ __launch_bounds__(256) void prefill_mfma_f16_kernel(PrefillArgs P)
             any = any || (r0[nb] < n && (!causal || k0 <= off + r0[nb] + 15));
         if (!any)
             continue;
-        const char *kt = kring + (t % NBUF) * SLOT;
-        const char *vt = vring + (t % NBUF) * SLOT;
+        const unsigned soff = (unsigned)((t % NBUF) * SLOT);
         // K rows (A of the score MFMA): key 16 kb + col, dims 32 ks + 8 grp .. (chunk 4 ks + grp)
         f16x8 kop[KB][KD];
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
-            const int r = kb * 16 + col;
-#pragma unroll
-            for (int ks = 0; ks < KD; ++ks)
-                kop[kb][ks] = lds_b128(kt + r * RB + swz<D>(4 * ks + grp, r) * 16);
-        }
+        static_for<0, KD>([&](auto ks_) {
+            constexpr int ks = decltype(ks_)::value;
+            const unsigned base = kbase[ks] + soff;
+            static_for<0, KB>([&](auto kb_) {
+                constexpr int kb = decltype(kb_)::value;
+                kop[kb][ks] = lds_b128_at<16 * kb * RB>(base);
+            });
+        });
         // V^T (A of the value MFMA), k-step ks, dims 16 db ..: lane L of group grp addresses
         // key row 16 (2 ks + h) + 4 grp + L / 4, dims 16 db + 4 (L % 4); the transposing
         // read hands lane i element j = half i % 4 of lane 4 j + i / 4's 8 bytes
         f16x4 vraw[KS][NDB][2];
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-            for (int db = 0; db < NDB; ++db)
-#pragma unroll
-                for (int hh = 0; hh < 2; ++hh) {
-                    const int row = 16 * (2 * ks + hh) + 4 * grp + (col >> 2);
-                    const int ch = 2 * db + ((col & 3) >> 1);
-                    vraw[ks][db][hh] = lds_tr16_b64(vt + row * RB + swz<D>(ch, row) * 16 + (col & 1) * 8);
-                }
+        static_for<0, NDB>([&](auto db_) {
+            constexpr int db = decltype(db_)::value;
+            const unsigned base = vbase[db] + soff;
+            static_for<0, KS>([&](auto ks_) {
+                constexpr int ks = decltype(ks_)::value;
+                static_for<0, 2>([&](auto hh_) {
+                    constexpr int hh = decltype(hh_)::value;
+                    vraw[ks][db][hh] = lds_tr16_b64_at<16 * (2 * ks + hh) * RB>(base);
+                });
+            });
+        });
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb)
