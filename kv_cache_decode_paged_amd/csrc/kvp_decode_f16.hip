@@ -350,6 +350,24 @@ __device__ __forceinline__ void run_item(const DecodeParams &P, const Addr &A, c
         acc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
     const f16x8 ones = {1, 1, 1, 1, 1, 1, 1, 1};
 
+    // fp16 cache: LDS byte addresses of this lane's operand reads in ring slot 0.  The
+    // swizzle sees a row only through row % 8, which 16-row steps leave alone, so the K reads
+    // of one 32-dim step and the V reads of one 16-dim block differ only by constants (the
+    // instruction's offset field); the bases move to the tile's slot once per tile.
+    //   K: row 16 kb + col, chunk 4 ks + grp              -> kbase[ks] + 16 kb RB
+    //   V: row 16 (2 ks + h) + 4 grp + col / 4, chunk 2 db + (col % 4) / 2, half col % 2
+    //                                                     -> vbase[db] + 16 (2 ks + h) RB
+    unsigned kbase[KD], vbase[NDB];
+#pragma unroll
+    for (int ks = 0; ks < KD; ++ks)
+        kbase[ks] = lds_addr(kring) + col * RB + swz<HD>(4 * ks + grp, col) * 16;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+        const int row = 4 * grp + (col >> 2);
+        const int ch = 2 * db + ((col & 3) >> 1);
+        vbase[db] = lds_addr(vring) + row * RB + swz<HD>(ch, row) * 16 + (col & 1) * 8;
+    }
+
     auto compute = [&](int t) {
         char *kt = kring + (t % NBUF) * SLOT; // fp16 cache: the tiles read by the products
         char *vt = vring + (t % NBUF) * SLOT;
@@ -540,13 +558,15 @@ __device__ __forceinline__ void run_item(const DecodeParams &P, const Addr &A, c
             }
         } else {
         // K rows (A of the score MFMA): row 16 kb + col, dims 32 ks + 8 grp .. (chunk 4 ks + grp)
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
-            const int r = kb * 16 + col;
-#pragma unroll
-            for (int ks = 0; ks < KD; ++ks)
-                kop[kb][ks] = lds_b128(kt + r * RB + swz<HD>(4 * ks + grp, r) * 16);
-        }
+        const unsigned soff = (unsigned)((t % NBUF) * SLOT);
+        static_for<0, KD>([&](auto ks_) {
+            constexpr int ks = decltype(ks_)::value;
+            const unsigned base = kbase[ks] + soff;
+            static_for<0, KB>([&](auto kb_) {
+                constexpr int kb = decltype(kb_)::value;
+                kop[kb][ks] = lds_b128_at<16 * kb * RB>(base);
+            });
+        });
         // V^T (A of the value MFMA) of k-step ks and dims 16 db ..: lane (col, grp) needs
         // V[token][16 db + col] for its k-slots s, token 16 (2 ks + s / 4) + 4 grp + s % 4.
         // A transposing read hands lane i of a 16-lane group half i % 4 of the 8 bytes
@@ -554,16 +574,17 @@ __device__ __forceinline__ void run_item(const DecodeParams &P, const Addr &A, c
         // token row 16 (2 ks + h) + 4 grp + L / 4, dims 16 db + 4 (L % 4) .. + 3, and the two
         // reads h = 0, 1 give slots 0-3 and 4-7.
         f16x4 vraw[KS][NDB][2];
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-            for (int db = 0; db < NDB; ++db)
-#pragma unroll
-                for (int h = 0; h < 2; ++h) {
-                    const int row = 16 * (2 * ks + h) + 4 * grp + (col >> 2);
-                    const int ch = 2 * db + ((col & 3) >> 1);
-                    vraw[ks][db][h] = lds_tr16_b64(vt + row * RB + swz<HD>(ch, row) * 16 + (col & 1) * 8);
-                }
+        static_for<0, NDB>([&](auto db_) {
+            constexpr int db = decltype(db_)::value;
+            const unsigned base = vbase[db] + soff;
+            static_for<0, KS>([&](auto ks_) {
+                constexpr int ks = decltype(ks_)::value;
+                static_for<0, 2>([&](auto h_) {
+                    constexpr int h = decltype(h_)::value;
+                    vraw[ks][db][h] = lds_tr16_b64_at<16 * (2 * ks + h) * RB>(base);
+                });
+            });
+        });
         // every read has returned before any result is used (the empty statements tie each
         // result to the wait)
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
