@@ -33,6 +33,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
+# the long-context decode configuration: 32 requests of 32768 cached tokens
+LONG_BATCH, LONG_CONTEXT = 32, 32768
 HQ, HKV, D, BLOCK = 14, 2, 64, 16
 KV_TOKEN_LAYER_BYTES = 2 * HKV * D * 2  # K and V, fp16: 512 B per token per layer
 
@@ -111,29 +113,31 @@ def unique_and_logical_tokens(table, ctx):
     b_sorted, c_sorted = blocks[order], counts[order]
     last = np.r_[b_sorted[1:] != b_sorted[:-1], True]
     unique = int(c_sorted[last].sum())
-    return unique, int(sum(ctx))
+    return unique, sum(int(c) for c in ctx)
 
 
 def decode_call_bytes(table, ctx, B):
     """Algorithmic bytes of one paged_decode_attention call (one layer): unique K/V bytes,
     q in, out, the block-table entries and the context lengths."""
     uniq, logical = unique_and_logical_tokens(table, ctx)
-    blocks_read = sum((c + BLOCK - 1) // BLOCK for c in ctx)
+    # Python integers throughout: a layer of a long batch holds more than 2^31 bytes
+    blocks_read = sum((int(c) + BLOCK - 1) // BLOCK for c in ctx)
     qo = 2 * B * HQ * D * 2
     return uniq * KV_TOKEN_LAYER_BYTES + qo + 4 * blocks_read + 4 * B, uniq, logical
 
 
-def build_state(kvp, torch, W, B, layers, total_steps, seed):
+def build_state(kvp, torch, W, B, layers, total_steps, seed, long_ctx=None):
     """Block pool, cache (every slot seeded N(0,1)) and the batch's sequences: groups fork
     their prefix, then each member truncates to a shorter context or reserves its private
-    tokens."""
-    pb = W.paged_batch(B)
+    tokens.  With long_ctx, B private sequences of long_ctx tokens each (no sharing)."""
+    pb = W.paged_batch(B) if long_ctx is None else None
     dev = "cuda"
-    ngroups = len(set(pb.group))
-    need = sum(math.ceil((c + total_steps + 1) / BLOCK) for c in pb.ctx_before)
-    need += ngroups * math.ceil(pb.prefix / BLOCK) + B + 64
+    ctx_before = pb.ctx_before if pb is not None else [long_ctx] * B
+    need = sum(math.ceil((c + total_steps + 1) / BLOCK) for c in ctx_before) + B + 64
+    if pb is not None:
+        need += len(set(pb.group)) * math.ceil(pb.prefix / BLOCK)
     num_blocks = need
-    max_blocks = math.ceil((max(pb.ctx_before) + total_steps + 1) / BLOCK)
+    max_blocks = math.ceil((max(ctx_before) + total_steps + 1) / BLOCK)
     pool = kvp.BlockPool(num_blocks)
     pool.set_free_order(W.free_list_permutation(num_blocks, seed + 1).tolist())
     cache = kvp.PagedKVCache(layers, num_blocks, HQ, HKV, torch.int8 if KV_INT8 else torch.float16, dev, head_dim=D)
@@ -148,6 +152,8 @@ def build_state(kvp, torch, W, B, layers, total_steps, seed):
             continue
         cache.k_pool[l].copy_(W.randn_device(cache.k_pool[l].shape, seed + 10 + 2 * l, torch.float16, dev))
         cache.v_pool[l].copy_(W.randn_device(cache.v_pool[l].shape, seed + 11 + 2 * l, torch.float16, dev))
+    if pb is None:
+        return pb, pool, cache, [pool.alloc(long_ctx) for _ in range(B)], max_blocks
     seqs = [None] * B
     for gi in sorted(set(pb.group)):
         pre = pool.alloc(pb.prefix)
@@ -445,11 +451,13 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-share", action="store_true", help="plans without shared-prefix items")
     ap.add_argument("--seed", type=int, default=42)
-    ap.add_argument("--workload", choices=["decode", "prefill", "chunked_prefill", "batching"], default="decode",
-                    help="decode: the batch-200 paged decode step (default); prefill: packed causal "
-                         "prefill of 16 x 4096 tokens; chunked_prefill: 16 x 512-token chunks after a "
-                         "shared 2048-token prefix in the paged cache; batching: continuous vs static "
-                         "batching over the block pool (host scheduler)")
+    ap.add_argument("--workload", choices=["decode", "long_context", "prefill", "chunked_prefill", "batching"],
+                    default="decode",
+                    help="decode: the batch-200 paged decode step (default); long_context: the same step "
+                         "for 32 requests of 32768 cached tokens each (split-K across CUs, 537 MB per "
+                         "layer); prefill: packed causal prefill of 16 x 4096 tokens; chunked_prefill: "
+                         "16 x 512-token chunks after a shared 2048-token prefix in the paged cache; "
+                         "batching: continuous vs static batching over the block pool (host scheduler)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -479,10 +487,12 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
     dev = "cuda"
-    B, L = args.batch, (args.layers if args.layers is not None else SHAPES[args.shape][0])
+    long_ctx = LONG_CONTEXT if args.workload == "long_context" else None
+    B = LONG_BATCH if long_ctx is not None else args.batch
+    L = args.layers if args.layers is not None else SHAPES[args.shape][0]
     total_steps = args.warmup + args.steps + 1
     t_setup = time.perf_counter()
-    pb, pool, cache, seqs, max_blocks = build_state(kvp, torch, W, B, L, total_steps, args.seed)
+    pb, pool, cache, seqs, max_blocks = build_state(kvp, torch, W, B, L, total_steps, args.seed, long_ctx)
     print(f"[bench] setup: B={B} layers={L} blocks={cache.num_blocks} max_blocks={max_blocks} "
           f"({time.perf_counter() - t_setup:.1f}s)", file=sys.stderr, flush=True)
 
@@ -620,12 +630,13 @@ def main():
           f"-> {achieved:.1f} GB/s ({achieved / HBM_PEAK_GBPS * 100:.1f}% of peak)", file=sys.stderr, flush=True)
 
     cpu = None
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and long_ctx is None:
         cpu = cpu_baseline(W, L)
         print(f"[bench] cpu oracle {cpu}", file=sys.stderr, flush=True)
 
     line = {
-        "metric": "decode attention KV GB/s (% of HBM peak) + decode steps/sec at batch 200",
+        "metric": ("decode attention KV GB/s (% of HBM peak) + decode steps/sec at batch 200" if long_ctx is None
+                   else "long-context split-K decode attention KV GB/s (% of HBM peak) + decode steps/sec"),
         "value": round(value, 2),
         "unit": "GB/s",
         "n_gpus": 1,
@@ -640,8 +651,9 @@ def main():
         "config": {"workload": f"paged GQA decode step, batch {B}, {L} layers x fused (append + paged decode), "
                                f"{HQ}q/{HKV}kv heads d{D} "
                                + ("int8 cache (absmax codes, fp16 scale per row)" if KV_INT8 else "fp16")
-                               + ", 16-token blocks, contexts U{128..2048}, "
-                               "groups of 8 sharing a 512-token prefix (copy-on-write)",
+                               + (", 16-token blocks, contexts U{128..2048}, "
+                                  "groups of 8 sharing a 512-token prefix (copy-on-write)" if long_ctx is None else
+                                  f", 16-token blocks, every context {long_ctx} tokens (+1 per step), no sharing"),
                    "batch": B, "layers": L, "shape": args.shape, "kv_dtype": args.kv_dtype,
                    "graph": graph is not None},
         "steps_per_sec": round(1e3 / ms_per_step, 2),
@@ -652,7 +664,7 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": measured_traffic() if (args.shape == DEFAULT_SHAPE and B == 200
-                                                       and not KV_INT8) else None,
+                                                       and long_ctx is None and not KV_INT8) else None,
                      "traffic_unit": "bytes per launch (HBM read + write, counters)",
                      "kernel": "paged_decode_attention_planned (decode_f16_kernel: append + attention + "
                                "split merge)",
