@@ -103,10 +103,14 @@ def unique_and_logical_tokens(table, ctx):
     blocks, counts = [], []
     for i, c in enumerate(ctx):
         nb = (c + BLOCK - 1) // BLOCK
+        if nb <= 0:  # an empty context reads nothing
+            continue
         cnt = np.full(nb, BLOCK, dtype=np.int64)
         cnt[-1] = c - BLOCK * (nb - 1)
         blocks.append(table[i, :nb])
         counts.append(cnt)
+    if not blocks:
+        return 0, 0
     blocks = np.concatenate(blocks)
     counts = np.concatenate(counts)
     order = np.lexsort((counts, blocks))
