@@ -518,7 +518,9 @@ def main():
     cows = (kvp.kvp_copy * B)()
     pool.export_raw(ids.data_ptr(), B, max_blocks, t0h.data_ptr(), c0h.data_ptr())
     c0h += total_steps + 1  # the longest contexts of this run (plan sizing only)
-    plan0, _ = kvp.decode_plan_build(HQ, HKV, t0h, c0h, cache.num_blocks, share_prefix=share, head_dim=D)
+    long_items = long_ctx is not None  # fewer, longer parts: the batch far exceeds the resident waves
+    plan0, _ = kvp.decode_plan_build(HQ, HKV, t0h, c0h, cache.num_blocks, share_prefix=share, head_dim=D,
+                                     long_items=long_items)
     pad_items = plan0.n_items + 8 * 32  # room for one more round of CU slots per XCD queue
     img_bytes = kvp.decode_plan_bytes(HQ, HKV, B, max_blocks, pad_items, head_dim=D)
     hb = [dict(table=torch.empty((B, max_blocks), dtype=torch.int32).pin_memory(),
@@ -558,14 +560,17 @@ def main():
                 npairs += 1
         pool.export_raw(ids.data_ptr(), B, max_blocks, h["table"].data_ptr(), h["ctx"].data_ptr())
         plan, _ = kvp.decode_plan_build(HQ, HKV, h["table"], h["ctx"], cache.num_blocks, share_prefix=share,
-                                        image=h["image"], pad_items=pad_items, plan=h["plan"], head_dim=D)
-        if launch_plan[0] is None:  # the launch arguments: this layout, slots up to slot_cap
-            launch_plan[0] = kvp.kvp_decode_plan.from_buffer_copy(plan)
+                                        image=h["image"], pad_items=pad_items, plan=h["plan"], head_dim=D,
+                                        long_items=long_items)
+        if launch_plan[0] is None:  # the launch arguments: this layout, slots up to slot_cap, ids
+            launch_plan[0] = kvp.kvp_decode_plan.from_buffer_copy(plan)  # up to the buffer's end
             launch_plan[0].n_slots = slot_cap
+            launch_plan[0].n_ids = (img_bytes - plan.off_ids) // 4
         lp = launch_plan[0]
         assert plan.n_slots <= slot_cap, "workspace too small for this step's plan"
-        assert (plan.n_items, plan.off_pair_base, plan.off_req_shared) == (lp.n_items, lp.off_pair_base,
-                                                                           lp.off_req_shared)
+        assert (plan.n_items, plan.off_pair_base, plan.off_req_shared, plan.off_ids) == \
+            (lp.n_items, lp.off_pair_base, lp.off_req_shared, lp.off_ids)
+        assert plan.off_ids + 4 * plan.n_ids <= img_bytes
         if keep:
             record.append((h["table"].numpy().copy(), h["ctx"].numpy().copy(), npairs, plan.n_shared,
                            plan.kv_blocks_read))
@@ -674,7 +679,7 @@ def main():
                                "split merge)",
                      "bytes_per_launch": int(call_bytes), "avg_launch_us": round(avg_ms * 1e3, 3)},
         "plan": {"items": int(launch_plan[0].n_items), "shared_items": int(n_shared_last),
-                 "kv_block_reads": int(blocks_read_last), "share_prefix": share},
+                 "kv_block_reads": int(blocks_read_last), "share_prefix": share, "long_items": long_items},
         "cpu_baseline": cpu,
     }
     print(f"[bench] decode sources digest {decode_sources_digest()}", file=sys.stderr, flush=True)

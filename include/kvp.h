@@ -342,6 +342,12 @@ kvp_status contiguous_decode_attention(const kvp_dims *dims, void *out, const vo
  * (flags = 0) the plan reproduces paged_decode_attention's splits exactly, bit for bit.
  * ------------------------------------------------------------------------------------ */
 #define KVP_PLAN_SHARE_PREFIX 1u
+/* Batches of long contexts: when the private blocks number far more than the waves the GPU
+ * holds at once (about 1024), cut each pair's private range into fewer, longer parts (up to
+ * 128 blocks; their block ids go to an id area at the end of the image) so that the launch
+ * runs in about one generation of waves.  Changes the splits, so the result equals the
+ * unplanned call's up to the order of the fp32 sums only. */
+#define KVP_PLAN_LONG_ITEMS 2u
 
 typedef struct {
     int32_t B;            /* batch the plan was built for                            */
@@ -356,6 +362,9 @@ typedef struct {
     int64_t bytes;        /* bytes of the plan image (device copy)                   */
     int64_t off_pair_base, off_pair_nparts, off_req_shared; /* offsets in the image  */
     int64_t kv_blocks_read; /* (block, KV head) reads the plan performs               */
+    int64_t off_ids, n_ids; /* id area of long items (offset in the image, int32 count);
+                             * n_ids bounds the kernel's id reads, so a launch replayed
+                             * for later plans may carry the device buffer's capacity  */
 } kvp_decode_plan;
 
 /* Upper bound of the plan image bytes for B requests of at most max_blocks blocks, or for
@@ -365,7 +374,8 @@ size_t decode_plan_bytes(const kvp_dims *dims, int32_t B, int32_t max_blocks, in
 /* Build a plan on the host.  h_block_table: host int32 [B][max_blocks]; h_context_lens:
  * host int32 [B] (the lengths the decode will use, i.e. with this step's token); entries
  * outside 0..num_blocks-1 are recorded as unusable (their rows are masked).  flags:
- * KVP_PLAN_SHARE_PREFIX to read shared prefixes once (0: plain per-request splits).
+ * KVP_PLAN_SHARE_PREFIX to read shared prefixes once (0: plain per-request splits), plus
+ * KVP_PLAN_LONG_ITEMS for long-context batches.
  * pad_items: 0, or a fixed item count (rounded up to a multiple of 8): the image then has
  * exactly that many items (the rest are empty) and offsets that depend only on pad_items,
  * B and the head shape, so that successive steps' plans launch identically (a captured

@@ -73,10 +73,11 @@ class kvp_decode_plan(ctypes.Structure):
                 ("num_blocks", ctypes.c_int32), ("n_items", ctypes.c_int32), ("n_shared", ctypes.c_int32),
                 ("head_dim", ctypes.c_int32), ("reserved", ctypes.c_int32), ("n_slots", ctypes.c_int64), ("bytes", ctypes.c_int64), ("off_pair_base", ctypes.c_int64),
                 ("off_pair_nparts", ctypes.c_int64), ("off_req_shared", ctypes.c_int64),
-                ("kv_blocks_read", ctypes.c_int64)]
+                ("kv_blocks_read", ctypes.c_int64), ("off_ids", ctypes.c_int64), ("n_ids", ctypes.c_int64)]
 
 
 PLAN_SHARE_PREFIX = 1
+PLAN_LONG_ITEMS = 2
 
 SCHED_STATIC, SCHED_CONTINUOUS = 0, 1
 ALLOC_PAGED, ALLOC_NAIVE = 0, 1
@@ -473,11 +474,12 @@ def _host_i32(t, name):
 
 
 def decode_plan_build(num_q_heads, num_kv_heads, block_table, context_lens, num_blocks, share_prefix=True,
-                      image=None, pin=False, pad_items=0, plan=None, head_dim=HEAD_DIM):
+                      image=None, pin=False, pad_items=0, plan=None, head_dim=HEAD_DIM, long_items=False):
     """Build a decode plan on the host from the HOST block table [B, max_blocks] and context
     lengths [B] (int32 CPU tensors).  Returns (plan, image): plan is a kvp_decode_plan, image
     a uint8 CPU tensor whose first plan.bytes bytes are to be copied to the device.
-    pad_items > 0 fixes the item count (see decode_plan_build in kvp.h)."""
+    pad_items > 0 fixes the item count (see decode_plan_build in kvp.h); long_items asks for
+    KVP_PLAN_LONG_ITEMS (fewer, longer parts for batches of long contexts)."""
     B, max_blocks = block_table.shape
     if context_lens.shape != (B,):
         raise ValueError("decode_plan_build: context_lens shape mismatch")
@@ -490,7 +492,8 @@ def decode_plan_build(num_q_heads, num_kv_heads, block_table, context_lens, num_
     plan = kvp_decode_plan() if plan is None else plan
     _check(_lib.decode_plan_build(ctypes.byref(dm), _host_i32(block_table, "block_table"), int(max_blocks),
                                   _host_i32(context_lens, "context_lens"), int(B), int(num_blocks),
-                                  PLAN_SHARE_PREFIX if share_prefix else 0, int(pad_items),
+                                  (PLAN_SHARE_PREFIX if share_prefix else 0) |
+                                  (PLAN_LONG_ITEMS if long_items else 0), int(pad_items),
                                   ctypes.c_void_p(image.data_ptr()), image.numel(), ctypes.byref(plan)))
     return plan, image
 

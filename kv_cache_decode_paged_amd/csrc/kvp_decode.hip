@@ -248,6 +248,9 @@ kvp_status paged_decode_attention_planned(const kvp_cache_desc *cache, int32_t l
         return fail(KVP_ERR_INVALID, "%s: plan (Hkv=%d group=%d d=%d num_blocks=%d) does not fit the cache "
                     "(Hkv=%d group=%d d=%d num_blocks=%d)", who, plan->num_kv_heads, plan->group,
                     plan->head_dim, plan->num_blocks, hkv, group, dim, cache->num_blocks);
+    if (plan->n_ids < 0 || plan->off_ids < 0 || (plan->off_ids & 3) || plan->n_ids > 0x7fffffffLL)
+        return fail(KVP_ERR_INVALID, "%s: plan id area (offset %lld, %lld ids) is not valid", who,
+                    (long long)plan->off_ids, (long long)plan->n_ids);
     if (plan->B == 0 || plan->n_items == 0)
         return KVP_OK;
     if (!out || !q || !d_plan || !cache->k_pool || !cache->v_pool)

@@ -72,6 +72,8 @@ struct PlanView {
     const int *pair_nparts; // planned: [B*Hkv]
     const int *req_shared;  // planned: [B]
     int ipp;                // unplanned: items per pair
+    const int *ids;         // planned: id area of long items
+    long long n_ids;        // planned: ints in the id area
 };
 
 struct Item {
@@ -178,7 +180,8 @@ __device__ __forceinline__ void merge_column(const float *part, int pbase, int n
     }
 }
 
-// One work item.  rv: lane R_ENT + j holds the physical id of the item's block j.
+// One work item.  rv: lane R_ENT + j holds the physical id of the item's block j; a long
+// item (longi) has id j in lane j % 64 of rid[j / 64] instead.
 //
 // Tile t = TT tokens = blocks (TT / 16) t .. of the item.  Lane (col, grp) = (lane % 16,
 // lane / 16).  MFMA column col is query row col of the item (member col / G, head col % G).
@@ -192,9 +195,10 @@ __device__ __forceinline__ void merge_column(const float *part, int pbase, int n
 // 4 (kb % 2) + m % 4, so that lane group grp's probabilities of k-step ks are the eight
 // consecutive tokens 32 ks + 8 grp + s, whose V codes of one dimension are eight
 // consecutive bytes.  Codes become fp16 operands in registers: code * scale, rounded once.
-template <int G, bool SHARED, int NBUF, int TT, int HD, bool I8, typename Addr>
+template <int G, bool SHARED, int NBUF, int TT, int HD, bool I8, bool LONGI, typename Addr>
 __device__ __forceinline__ void run_item(const DecodeParams &P, const Addr &A, const PlanView &PV,
-                                         const Item &it, int rv, char *kring, char *vring, char *sring)
+                                         const Item &it, int rv, const int (&rid)[3], char *kring, char *vring,
+                                         char *sring)
 {
     static_assert(TT == 32 || TT == 64, "tiles of 32 or 64 tokens");
     static_assert(HD == 64 || HD == 128, "head dimension 64 or 128");
@@ -287,7 +291,14 @@ __device__ __forceinline__ void run_item(const DecodeParams &P, const Addr &A, c
     }
 
     const int nt = (it.nblk + KB - 1) / KB;
-    auto ent = [&](int j) -> int { return lane_int(rv, R_ENT + min(j, BPI - 1)); };
+    auto ent = [&](int j) -> int {
+        if constexpr (LONGI) {
+            const int jj = min(j, LONG_BPI - 1);
+            return jj < 64 ? lane_int(rid[0], jj) : (jj < 128 ? lane_int(rid[1], jj - 64) : lane_int(rid[2], jj - 128));
+        } else {
+            return lane_int(rv, R_ENT + min(j, BPI - 1));
+        }
+    };
     auto block_ok = [&](int j) -> bool { return (j < it.nblk) & A.valid(ent(j)); };
 
     // ---- DMA of tile t into ring slot t % NBUF: per block, IPB loads of RPI rows of K and V
@@ -801,21 +812,39 @@ __global__ __launch_bounds__(64) void decode_f16_kernel(DecodeParams P, Addr A, 
         it.slot = lane_int(rv, R_SLOT);
         it.nparts = lane_int(rv, R_NPARTS);
         it.pbase = lane_int(rv, R_PBASE);
+        const bool longi = (flags & F_LONG) != 0;
         // a record that does not fit this call is skipped rather than trusted
         if (it.b < 0 || it.g < 0 || it.g >= P.hkv || it.nmem < 1 || it.b + it.nmem > P.B ||
-            it.nblk < 0 || it.nblk > BPI || it.blk0 < 0)
+            it.nblk < 0 || it.nblk > (longi ? LONG_BPI : BPI) || it.blk0 < 0)
             return;
         if (flags & F_EMPTY)
             return;
         if (flags & F_SHARED) {
             if (it.nmem * G > 16 || it.slot < 0)
                 return;
-            run_item<G, true, NBUF, TT, HD, I8>(P, A, PV, it, rv, kring, vring, sring);
+            if (longi)
+                return;
+            run_item<G, true, NBUF, TT, HD, I8, false>(P, A, PV, it, rv, {-1, -1, -1}, kring, vring, sring);
             return;
         }
         if (it.nmem != 1)
             return;
-        run_item<G, false, NBUF, TT, HD, I8>(P, A, PV, it, rv, kring, vring, sring);
+        // a long item's block ids: from the id area into three registers, lane j holding ids
+        // j, 64 + j and 128 + j
+        int rid[3] = {-1, -1, -1};
+        if (longi) {
+            const int off = lane_int(rv, R_IDS);
+            if (off < 0 || (long long)off + it.nblk > PV.n_ids)
+                return;
+#pragma unroll
+            for (int k = 0; k < 3; ++k)
+                if (64 * k + lane < it.nblk)
+                    rid[k] = PV.ids[off + 64 * k + lane];
+        }
+        if (longi)
+            run_item<G, false, NBUF, TT, HD, I8, true>(P, A, PV, it, rv, rid, kring, vring, sring);
+        else
+            run_item<G, false, NBUF, TT, HD, I8, false>(P, A, PV, it, rv, rid, kring, vring, sring);
     } else {
         const int pair = blockIdx.x / PV.ipp;
         const int k = blockIdx.x - pair * PV.ipp;
@@ -840,7 +869,7 @@ __global__ __launch_bounds__(64) void decode_f16_kernel(DecodeParams P, Addr A, 
         it.slot = it.pbase + k;
         const int j = lane - R_ENT;
         rv = (j >= 0 && j < it.nblk) ? A.entry(it.b, it.blk0 + j) : -1;
-        run_item<G, false, NBUF, TT, HD, I8>(P, A, PV, it, rv, kring, vring, sring);
+        run_item<G, false, NBUF, TT, HD, I8, false>(P, A, PV, it, rv, {-1, -1, -1}, kring, vring, sring);
     }
 }
 
@@ -908,13 +937,13 @@ size_t decode_f16_part_bytes(long long slots, int dim)
 kvp_status launch_decode_f16(const DecodeParams &P, const PagedAddr &A, int group, int max_context,
                              hipStream_t st)
 {
-    PlanView PV{nullptr, nullptr, nullptr, nullptr, decode_f16_items_per_pair(max_context)};
+    PlanView PV{nullptr, nullptr, nullptr, nullptr, decode_f16_items_per_pair(max_context), nullptr, 0};
     return launch_f16<false>(P, A, PV, group, (long long)P.B * P.hkv * PV.ipp, st);
 }
 kvp_status launch_decode_f16(const DecodeParams &P, const ContigAddr &A, int group, int max_context,
                              hipStream_t st)
 {
-    PlanView PV{nullptr, nullptr, nullptr, nullptr, decode_f16_items_per_pair(max_context)};
+    PlanView PV{nullptr, nullptr, nullptr, nullptr, decode_f16_items_per_pair(max_context), nullptr, 0};
     return launch_f16<false>(P, A, PV, group, (long long)P.B * P.hkv * PV.ipp, st);
 }
 kvp_status launch_decode_f16_planned(const DecodeParams &P, const PagedAddr &A, int group,
@@ -922,7 +951,8 @@ kvp_status launch_decode_f16_planned(const DecodeParams &P, const PagedAddr &A, 
 {
     const char *img = (const char *)d_image;
     PlanView PV{(const int *)img, (const int *)(img + plan.off_pair_base),
-                (const int *)(img + plan.off_pair_nparts), (const int *)(img + plan.off_req_shared), 0};
+                (const int *)(img + plan.off_pair_nparts), (const int *)(img + plan.off_req_shared), 0,
+                (const int *)(img + plan.off_ids), plan.n_ids};
     return launch_f16<true>(P, A, PV, group, plan.n_items, st);
 }
 

@@ -53,9 +53,12 @@ long long max_items(long long B, long long hkv, long long max_blocks)
     return XCDS * ((work + XCDS - 1) / XCDS + MAX_BUNDLE + CU_SLOTS - 1);
 }
 
-size_t image_bytes_for(long long items, long long B, long long hkv)
+// records, the pair and request arrays, and the id area of long items (at most every block
+// of every pair)
+size_t image_bytes_for(long long items, long long B, long long hkv, long long max_blocks)
 {
-    return align16((size_t)items * REC * 4) + 2 * align16((size_t)B * hkv * 4) + align16((size_t)B * 4);
+    return align16((size_t)items * REC * 4) + 2 * align16((size_t)B * hkv * 4) + align16((size_t)B * 4) +
+           align16((size_t)B * hkv * max_blocks * 4);
 }
 
 // parts of a range of nb blocks: one item up to BPI blocks unless `forced` (the pair has
@@ -85,7 +88,8 @@ size_t decode_plan_bytes(const kvp_dims *dims, int32_t B, int32_t max_blocks, in
     if (check_plan_dims(dims, "decode_plan_bytes") != KVP_OK || B < 0 || max_blocks <= 0 || pad_items < 0)
         return 0;
     const long long pad = ((long long)pad_items + XCDS - 1) / XCDS * XCDS;
-    return image_bytes_for(std::max(pad, max_items(B, dims->num_kv_heads, max_blocks)), B, dims->num_kv_heads);
+    return image_bytes_for(std::max(pad, max_items(B, dims->num_kv_heads, max_blocks)), B, dims->num_kv_heads,
+                           max_blocks);
 }
 
 kvp_status decode_plan_build(const kvp_dims *dims, const int32_t *table, int32_t max_blocks,
@@ -100,7 +104,7 @@ kvp_status decode_plan_build(const kvp_dims *dims, const int32_t *table, int32_t
         return fail(KVP_ERR_INVALID, "%s: B=%d max_blocks=%d num_blocks=%d", who, B, max_blocks, num_blocks);
     if (!plan || !h_image || (B > 0 && (!table || !ctx_lens)))
         return fail(KVP_ERR_INVALID, "%s: NULL pointer argument", who);
-    if (flags & ~KVP_PLAN_SHARE_PREFIX)
+    if (flags & ~(KVP_PLAN_SHARE_PREFIX | KVP_PLAN_LONG_ITEMS))
         return fail(KVP_ERR_INVALID, "%s: unknown flags 0x%x", who, flags);
     if (pad_items < 0)
         return fail(KVP_ERR_INVALID, "%s: pad_items=%d", who, pad_items);
@@ -171,8 +175,23 @@ kvp_status decode_plan_build(const kvp_dims *dims, const int32_t *table, int32_t
                 if (BS * split_start(nsb, ns, k) < E[m])
                     ++shared_parts[m];
     }
+    // long items: parts of up to S blocks, S sized so the private blocks fill about one
+    // generation of waves (whole tiles, between SPLIT_BLOCKS and LONG_BPI); S = SPLIT_BLOCKS
+    // leaves the plan as without the flag
+    int S = SPLIT_BLOCKS;
+    if (flags & KVP_PLAN_LONG_ITEMS) {
+        long long priv_blocks = 0;
+        for (int b = 0; b < B; ++b)
+            priv_blocks += (long long)hkv * std::max(0, nbt[b] - E[b] / BS);
+        const long long waves = dims->dtype == KVP_I8 ? LONG_TARGET_WAVES_I8 : LONG_TARGET_WAVES_F16;
+        const long long per_wave = (priv_blocks + waves - 1) / waves;
+        S = (int)std::min<long long>(LONG_BPI, std::max<long long>(SPLIT_BLOCKS, (per_wave + 3) / 4 * 4));
+    }
     auto private_items = [&](int b) -> int {
-        return split_parts(nbt[b] - E[b] / BS, E[b] > 0);
+        const int nb = nbt[b] - E[b] / BS;
+        if (S == SPLIT_BLOCKS || nb <= UNSPLIT_BLOCKS)
+            return split_parts(nb, E[b] > 0);
+        return (nb + S - 1) / S;
     };
     std::vector<int> pair_base(npairs, -1), pair_nparts(npairs, 1);
     long long slots = 0, n_items = 0;
@@ -195,6 +214,7 @@ kvp_status decode_plan_build(const kvp_dims *dims, const int32_t *table, int32_t
 
     // ---- records (built in plan order, placed into XCD queues below) ----
     std::vector<int32_t> recs((size_t)n_items * REC, -1);
+    std::vector<int32_t> long_ids; // id area
     std::vector<long long> cost(n_items);
     long long idx = 0, blocks_read = 0;
     auto record = [&](int fl, int b, int g, int nmem, int blk0, int nblk, int end, int slot, int nparts,
@@ -212,8 +232,17 @@ kvp_status decode_plan_build(const kvp_dims *dims, const int32_t *table, int32_t
         r[R_PBASE] = pbase;
         for (int j = R_PBASE + 1; j < R_ENT; ++j)
             r[j] = 0;
-        for (int j = 0; j < BPI; ++j)
-            r[R_ENT + j] = j < nblk ? ent(src_req, blk0 + j) : -1;
+        if (nblk > BPI) { // long item (private only): ids in the id area
+            r[R_FLAGS] |= F_LONG;
+            for (int j = 0; j < BPI; ++j)
+                r[R_ENT + j] = -1;
+            r[R_IDS] = (int32_t)long_ids.size();
+            for (int j = 0; j < nblk; ++j)
+                long_ids.push_back(ent(src_req, blk0 + j));
+        } else {
+            for (int j = 0; j < BPI; ++j)
+                r[R_ENT + j] = j < nblk ? ent(src_req, blk0 + j) : -1;
+        }
         blocks_read += nblk;
         cost[idx] = nblk + 2; // a tile stream plus the fixed start / finish of a wave
         ++idx;
@@ -321,7 +350,8 @@ kvp_status decode_plan_build(const kvp_dims *dims, const int32_t *table, int32_t
     const size_t off_pb = align16((size_t)n_image * REC * 4);
     const size_t off_np = off_pb + align16((size_t)npairs * 4);
     const size_t off_rs = off_np + align16((size_t)npairs * 4);
-    const size_t bytes = off_rs + align16((size_t)B * 4);
+    const size_t off_ids = off_rs + align16((size_t)B * 4);
+    const size_t bytes = off_ids + align16(long_ids.size() * 4);
     if (image_bytes < bytes)
         return fail(KVP_ERR_INVALID, "%s: image buffer %zu bytes < %zu needed", who, image_bytes, bytes);
     int32_t *img = (int32_t *)h_image;
@@ -340,6 +370,8 @@ kvp_status decode_plan_build(const kvp_dims *dims, const int32_t *table, int32_t
     std::memcpy((char *)h_image + off_pb, pair_base.data(), (size_t)npairs * 4);
     std::memcpy((char *)h_image + off_np, pair_nparts.data(), (size_t)npairs * 4);
     std::memcpy((char *)h_image + off_rs, E.data(), (size_t)B * 4);
+    if (!long_ids.empty())
+        std::memcpy((char *)h_image + off_ids, long_ids.data(), long_ids.size() * 4);
 
     plan->B = B;
     plan->num_kv_heads = hkv;
@@ -355,6 +387,8 @@ kvp_status decode_plan_build(const kvp_dims *dims, const int32_t *table, int32_t
     plan->off_pair_nparts = (int64_t)off_np;
     plan->off_req_shared = (int64_t)off_rs;
     plan->kv_blocks_read = blocks_read;
+    plan->off_ids = (int64_t)off_ids;
+    plan->n_ids = (int64_t)long_ids.size();
     return KVP_OK;
 }
 

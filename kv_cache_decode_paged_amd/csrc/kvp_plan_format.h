@@ -6,6 +6,7 @@
 //   pair_base   [B * Hkv]        first partial slot of pair (b, g), -1 if the pair has one part
 //   pair_nparts [B * Hkv]        parts the pair's attention row is split into (>= 1)
 //   req_shared  [B]              tokens [0, req_shared[b]) of request b are read by a shared item
+//   ids         [n_ids]          block ids of long items (built with KVP_PLAN_LONG_ITEMS only)
 //
 // A work item covers up to BPI consecutive 16-token blocks of one KV head: either of one
 // request (private item) or of the leading request of a run of requests whose tables point
@@ -46,6 +47,15 @@ constexpr int part_tile_begin(int T, int n, int k, int slack)
 // polled merge two tiles of lead over the other parts gained nothing, so none)
 constexpr int SPLIT_SLACK = 0;
 constexpr int REC = 48;  // int32 per record
+// Long items (plans built with KVP_PLAN_LONG_ITEMS): a private range of a batch with many
+// more blocks than resident waves is cut into parts of up to LONG_BPI blocks, whose ids sit
+// in the image's id area (the record's first id entry holds the offset there).  Fewer,
+// longer items pay the fixed start and finish of a wave fewer times.
+constexpr int LONG_BPI = 192; // blocks of a long item (three ids per lane)
+// waves resident at once, which a long-item plan fills about once: four 32 KB fp16
+// workgroups per CU, eight of the int8 kernel's 18 KB, on 256 CUs
+constexpr int LONG_TARGET_WAVES_F16 = 1024;
+constexpr int LONG_TARGET_WAVES_I8 = 2048;
 constexpr int MAXM = 16; // members of one shared item (and at most 16 query rows)
 constexpr int XCDS = 8;  // MI355X: workgroup i runs on XCD i % 8 (round-robin dispatch)
 // CUs per XCD: within an XCD, the dispatcher deals the queue positions of one launch
@@ -70,6 +80,8 @@ static_assert(R_ENT + BPI <= REC, "record too small");
 
 constexpr int F_SHARED = 1;
 constexpr int F_EMPTY = 2;
+constexpr int F_LONG = 4; // private item of up to LONG_BPI blocks, ids in the id area
+constexpr int R_IDS = R_ENT; // long item: offset of its ids in the id area
 
 } // namespace plan
 } // namespace kvp

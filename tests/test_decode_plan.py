@@ -27,7 +27,8 @@ import kv_cache_decode_paged_amd as kvp
 import workloads as W
 
 REC, BPI, R_ENT, XCDS = 48, 32, 16, 8
-F_SHARED, F_EMPTY = 1, 2
+F_SHARED, F_EMPTY, F_LONG = 1, 2, 4
+LONG_BPI = 192
 BS = 16
 
 
@@ -37,13 +38,15 @@ def parse(plan, image, B, hkv):
     pb = raw[plan.off_pair_base // 4: plan.off_pair_base // 4 + B * hkv]
     npt = raw[plan.off_pair_nparts // 4: plan.off_pair_nparts // 4 + B * hkv]
     rs = raw[plan.off_req_shared // 4: plan.off_req_shared // 4 + B]
-    return items, pb, npt, rs
+    ids = raw[plan.off_ids // 4: plan.off_ids // 4 + plan.n_ids]
+    assert plan.off_ids // 4 + plan.n_ids <= raw.size
+    return items, pb, npt, rs, ids
 
 
 def check_plan(plan, image, table, ctx, num_blocks, hq, hkv, shared_expected=None):
     B, mb = table.shape
     G = hq // hkv
-    items, pbase, nparts, req_shared = parse(plan, image, B, hkv)
+    items, pbase, nparts, req_shared, long_ids = parse(plan, image, B, hkv)
     assert plan.n_items % XCDS == 0
     ctx = np.clip(ctx, 0, mb * BS)
 
@@ -66,10 +69,20 @@ def check_plan(plan, image, table, ctx, num_blocks, hq, hkv, shared_expected=Non
         if fl == F_EMPTY:
             continue
         b, g, nmem, blk0, nblk, end, slot, np_, pb_ = (int(x) for x in r[1:10])
-        assert 0 <= g < hkv and nmem >= 1 and b + nmem <= B and 0 <= nblk <= BPI and blk0 >= 0
-        for j in range(BPI):
-            want = ent(b, blk0 + j) if j < nblk else -1
-            assert int(r[R_ENT + j]) == want, (p, j)
+        longi = bool(fl & F_LONG)
+        fl &= ~F_LONG
+        assert 0 <= g < hkv and nmem >= 1 and b + nmem <= B and blk0 >= 0
+        assert 0 <= nblk <= (LONG_BPI if longi else BPI)
+        if longi:  # a private item whose ids sit in the id area
+            assert fl == 0 and nblk > BPI
+            off = int(r[R_ENT])
+            assert 0 <= off and off + nblk <= long_ids.size
+            assert [int(e) for e in long_ids[off: off + nblk]] == [ent(b, blk0 + j) for j in range(nblk)], p
+            assert (r[R_ENT + 1: R_ENT + BPI] == -1).all()
+        else:
+            for j in range(BPI):
+                want = ent(b, blk0 + j) if j < nblk else -1
+                assert int(r[R_ENT + j]) == want, (p, j)
         if fl == F_SHARED:
             assert nmem * G <= 16 and slot >= 0
             key = (run_of[b], g)  # one sharing run and KV head
@@ -128,10 +141,10 @@ def check_plan(plan, image, table, ctx, num_blocks, hq, hkv, shared_expected=Non
     return items, pbase, nparts, req_shared
 
 
-def build(table, ctx, num_blocks, hq=14, hkv=2, share=True):
+def build(table, ctx, num_blocks, hq=14, hkv=2, share=True, long_items=False):
     t = torch.from_numpy(np.ascontiguousarray(table, dtype=np.int32))
     c = torch.from_numpy(np.ascontiguousarray(ctx, dtype=np.int32))
-    return kvp.decode_plan_build(hq, hkv, t, c, num_blocks, share_prefix=share)
+    return kvp.decode_plan_build(hq, hkv, t, c, num_blocks, share_prefix=share, long_items=long_items)
 
 
 def c4_tables(B, steps_done=1, seed=42):
@@ -286,3 +299,71 @@ def test_plan_padding_fixes_the_launch():
     with pytest.raises(kvp.KvpError) as e:
         kvp.decode_plan_build(14, 2, t, c, nb, pad_items=8)
     assert e.value.status == kvp.KVP_ERR_INVALID
+
+
+def long_tables(B, ctx_len, seed=3, num_blocks=None):
+    """B private contexts of ctx_len tokens on a shuffled pool (the long-context batch)."""
+    nbt = (ctx_len + BS - 1) // BS
+    nb = num_blocks or B * nbt + 16
+    ids = np.random.default_rng(seed).permutation(nb)[: B * nbt].astype(np.int32)
+    return ids.reshape(B, nbt), np.full(B, ctx_len, np.int32), nb
+
+
+def test_long_items_fill_one_generation():
+    # 32 requests x 32790 tokens, 2 KV heads: 131200 private blocks over 1024 waves -> parts
+    # of 132 blocks (whole tiles), 16 per pair, 1024 items, ids in the id area
+    table, ctx, nb = long_tables(32, 32790)
+    plan, image = build(table, ctx, nb, share=False, long_items=True)
+    items, pbase, nparts, _ = check_plan(plan, image, table, ctx, nb, 14, 2)
+    live = items[items[:, 0] != F_EMPTY]
+    assert len(live) == 1024 and (live[:, 0] == F_LONG).all()
+    assert live[:, 5].max() <= 132 and (nparts == 16).all()
+    assert plan.n_ids == live[:, 5].sum() == 32 * 2 * 2050
+    assert plan.bytes >= plan.off_ids + 4 * plan.n_ids
+    # without the flag: the 32-block splits, no id area
+    plain, image0 = build(table, ctx, nb, share=False)
+    items0, _, nparts0, _ = check_plan(plain, image0, table, ctx, nb, 14, 2)
+    assert plain.n_ids == 0 and ((items0[:, 0] & F_LONG) == 0).all() and (nparts0 == 65).all()
+
+
+@pytest.mark.parametrize("B,ctx_len", [(1, 40000), (4, 70000), (200, 3000)])
+def test_long_items_only_when_the_batch_is_long(B, ctx_len):
+    # long items appear only when the private blocks exceed 1024 waves x 32 blocks: a small
+    # total keeps the 32-block splits, a larger one (many short contexts too) gets parts of
+    # up to 192 blocks
+    table, ctx, nb = long_tables(B, ctx_len, seed=B)
+    plan, image = build(table, ctx, nb, share=False, long_items=True)
+    items, _, _, _ = check_plan(plan, image, table, ctx, nb, 14, 2)
+    live = items[items[:, 0] != F_EMPTY]
+    priv_blocks = 2 * B * ((ctx_len + BS - 1) // BS)
+    if priv_blocks <= 1024 * BPI:
+        assert plan.n_ids == 0 and live[:, 5].max() <= BPI
+    else:
+        assert live[:, 5].max() <= LONG_BPI and plan.n_ids > 0
+
+
+def test_long_items_with_shared_prefixes_and_padding():
+    # shared-prefix items keep their 32-block records; private ranges after the prefix become
+    # long items; a padded plan keeps its offsets when the id area grows
+    B, pre, tail = 16, 8192, 40000
+    nbp, nbt = pre // BS, (pre + tail) // BS
+    rng = np.random.default_rng(9)
+    nb = nbp + B * (nbt - nbp) + 8
+    ids = rng.permutation(nb).astype(np.int32)
+    table = np.empty((B, nbt), np.int32)
+    table[:, :nbp] = ids[:nbp]
+    table[:, nbp:] = ids[nbp: nbp + B * (nbt - nbp)].reshape(B, nbt - nbp)
+    ctx = np.full(B, pre + tail, np.int32)
+    plan, image = build(table, ctx, nb, share=True, long_items=True)
+    items, _, _, _ = check_plan(plan, image, table, ctx, nb, 14, 2, shared_expected=True)
+    sh = items[(items[:, 0] & F_SHARED) != 0]
+    assert len(sh) > 0 and sh[:, 5].max() <= BPI
+    assert ((items[:, 0] & F_LONG) != 0).any()
+    t = torch.from_numpy(table)
+    c = torch.from_numpy(ctx)
+    p1, im1 = kvp.decode_plan_build(14, 2, t, c, nb, long_items=True, pad_items=plan.n_items + 64)
+    check_plan(p1, im1, table, ctx, nb, 14, 2)
+    c2 = torch.from_numpy(ctx + 1)
+    p2, im2 = kvp.decode_plan_build(14, 2, t, c2, nb, long_items=True, pad_items=plan.n_items + 64)
+    assert (p1.n_items, p1.off_pair_base, p1.off_req_shared, p1.off_ids) == \
+        (p2.n_items, p2.off_pair_base, p2.off_req_shared, p2.off_ids)

@@ -332,3 +332,21 @@ def test_long_context_split_k_sampled():
     err = max_abs(to64(out[rows]), want)
     say("long context max err", err)
     assert err <= TOL[torch.float16]
+    # the planned decode with long items: 16 parts of up to 132 blocks per pair (one wave
+    # each, 1024 in all), ids from the plan's id area; counted and polled merges agree
+    plan, image = kvp.decode_plan_build(hq, hkv, table, ctx, B * nb_per, share_prefix=False, long_items=True)
+    assert plan.n_ids == B * hkv * nb_per
+    dp = kvp.upload_plan(plan, image)
+    ws = kvp.make_plan_workspace(plan)
+    olong = kvp.paged_decode_attention_planned(cache, 0, q, plan, dp, workspace=ws)
+    old = kvp.decode_merge_polls(1 << 14)
+    try:
+        olong_p = kvp.paged_decode_attention_planned(cache, 0, q, plan, dp, workspace=ws)
+    finally:
+        kvp.decode_merge_polls(old)
+    torch.cuda.synchronize()
+    assert torch.equal(_bits(olong.cpu()), _bits(olong_p.cpu()))
+    err = max_abs(to64(olong[rows]), want)
+    say("long context, long items: items", plan.n_items, "max err", err)
+    assert err <= TOL[torch.float16]
+    assert (olong.float() - out.float()).abs().max().item() <= 2 * TOL[torch.float16]

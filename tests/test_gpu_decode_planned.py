@@ -21,9 +21,9 @@ def _bits(t):
     return t.contiguous().view(torch.int16)
 
 
-def _plan(step, share=True):
+def _plan(step, share=True, long_items=False):
     plan, image = kvp.decode_plan_build(step.hq, step.hkv, step.table.cpu(), step.ctx.cpu(), step.num_blocks,
-                                        share_prefix=share)
+                                        share_prefix=share, head_dim=step.head_dim, long_items=long_items)
     return plan, kvp.upload_plan(plan, image)
 
 
@@ -134,3 +134,25 @@ def test_planned_rejects_mismatched_plan():
     small = kvp.PagedKVCache(1, plan.num_blocks - 1, 14, 2, torch.float16, "cuda")
     with pytest.raises(kvp.KvpError):
         kvp.paged_decode_attention_planned(small, 0, q, plan, dp)
+
+
+@pytest.mark.parametrize("dtype", [torch.float16, torch.int8])
+def test_planned_long_items_match_oracle(dtype):
+    # 200 requests of 2000-3000 tokens in sharing groups: about 60000 private blocks, more
+    # than 1024 waves x 32 blocks, so the private ranges become long items (ids in the id
+    # area); the shared prefixes stay 32-block items
+    need_gpu()
+    pb = W.paged_batch(200, lo=2000, hi=3000, seed=61)
+    say("planned long items", dtype, "B", pb.batch)
+    step = PagedStep(kvp, pb, layers=1, hq=14, hkv=2, dtype=dtype, seed=9700)
+    plan, dp = _plan(step, long_items=True)
+    assert plan.n_ids > 0 and plan.n_shared > 0
+    ws = kvp.make_plan_workspace(plan)
+    q = step.q(0).cuda()
+    o = kvp.paged_decode_attention_planned(step.cache, 0, q, plan, dp, workspace=ws)
+    o2 = kvp.paged_decode_attention_planned(step.cache, 0, q, plan, dp, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(_bits(o.cpu()), _bits(o2.cpu())), "repeat with the same workspace differs"
+    err = max_abs(to64(o), step.oracle(0))
+    say("planned long items", dtype, "items", plan.n_items, "ids", plan.n_ids, "max err", err)
+    assert err <= TOL[torch.float16]
