@@ -469,8 +469,8 @@ def main():
               "Requests would be sharded across GPUs by whole sharing groups.", flush=True)
         sys.exit(2)
     set_shape(args.shape, args.kv_dtype == "int8")
-    if args.kv_dtype == "int8" and args.workload != "decode":
-        print("--kv-dtype int8 applies to the decode workload", flush=True)
+    if args.kv_dtype == "int8" and args.workload not in ("decode", "long_context"):
+        print("--kv-dtype int8 applies to the decode workloads", flush=True)
         sys.exit(2)
     if args.workload == "batching":
         bench_batching(args)
@@ -519,8 +519,9 @@ def main():
     pool.export_raw(ids.data_ptr(), B, max_blocks, t0h.data_ptr(), c0h.data_ptr())
     c0h += total_steps + 1  # the longest contexts of this run (plan sizing only)
     long_items = long_ctx is not None  # fewer, longer parts: the batch far exceeds the resident waves
+    kv_dtype = torch.int8 if KV_INT8 else torch.float16
     plan0, _ = kvp.decode_plan_build(HQ, HKV, t0h, c0h, cache.num_blocks, share_prefix=share, head_dim=D,
-                                     long_items=long_items)
+                                     long_items=long_items, kv_dtype=kv_dtype)
     pad_items = plan0.n_items + 8 * 32  # room for one more round of CU slots per XCD queue
     img_bytes = kvp.decode_plan_bytes(HQ, HKV, B, max_blocks, pad_items, head_dim=D)
     hb = [dict(table=torch.empty((B, max_blocks), dtype=torch.int32).pin_memory(),
@@ -561,7 +562,7 @@ def main():
         pool.export_raw(ids.data_ptr(), B, max_blocks, h["table"].data_ptr(), h["ctx"].data_ptr())
         plan, _ = kvp.decode_plan_build(HQ, HKV, h["table"], h["ctx"], cache.num_blocks, share_prefix=share,
                                         image=h["image"], pad_items=pad_items, plan=h["plan"], head_dim=D,
-                                        long_items=long_items)
+                                        long_items=long_items, kv_dtype=kv_dtype)
         if launch_plan[0] is None:  # the launch arguments: this layout, slots up to slot_cap, ids
             launch_plan[0] = kvp.kvp_decode_plan.from_buffer_copy(plan)  # up to the buffer's end
             launch_plan[0].n_slots = slot_cap

@@ -474,12 +474,14 @@ def _host_i32(t, name):
 
 
 def decode_plan_build(num_q_heads, num_kv_heads, block_table, context_lens, num_blocks, share_prefix=True,
-                      image=None, pin=False, pad_items=0, plan=None, head_dim=HEAD_DIM, long_items=False):
+                      image=None, pin=False, pad_items=0, plan=None, head_dim=HEAD_DIM, long_items=False,
+                      kv_dtype=torch.float16):
     """Build a decode plan on the host from the HOST block table [B, max_blocks] and context
     lengths [B] (int32 CPU tensors).  Returns (plan, image): plan is a kvp_decode_plan, image
     a uint8 CPU tensor whose first plan.bytes bytes are to be copied to the device.
     pad_items > 0 fixes the item count (see decode_plan_build in kvp.h); long_items asks for
-    KVP_PLAN_LONG_ITEMS (fewer, longer parts for batches of long contexts)."""
+    KVP_PLAN_LONG_ITEMS (fewer, longer parts for batches of long contexts), sized for the
+    waves the kernel of kv_dtype's cache keeps resident (torch.float16 or torch.int8)."""
     B, max_blocks = block_table.shape
     if context_lens.shape != (B,):
         raise ValueError("decode_plan_build: context_lens shape mismatch")
@@ -488,7 +490,7 @@ def decode_plan_build(num_q_heads, num_kv_heads, block_table, context_lens, num_
         image = torch.empty((max(need, 16),), dtype=torch.uint8, pin_memory=pin)
     if image.device.type != "cpu" or image.dtype != torch.uint8:
         raise ValueError("decode_plan_build: image must be a uint8 host tensor")
-    dm = dims(1, num_q_heads, num_kv_heads, torch.float16, head_dim)
+    dm = dims(1, num_q_heads, num_kv_heads, kv_dtype, head_dim)
     plan = kvp_decode_plan() if plan is None else plan
     _check(_lib.decode_plan_build(ctypes.byref(dm), _host_i32(block_table, "block_table"), int(max_blocks),
                                   _host_i32(context_lens, "context_lens"), int(B), int(num_blocks),

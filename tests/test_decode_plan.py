@@ -367,3 +367,16 @@ def test_long_items_with_shared_prefixes_and_padding():
     p2, im2 = kvp.decode_plan_build(14, 2, t, c2, nb, long_items=True, pad_items=plan.n_items + 64)
     assert (p1.n_items, p1.off_pair_base, p1.off_req_shared, p1.off_ids) == \
         (p2.n_items, p2.off_pair_base, p2.off_req_shared, p2.off_ids)
+
+
+def test_long_items_sized_for_the_int8_kernel():
+    # the int8 kernel keeps 2048 waves resident (18 KB of LDS each): the same batch gets
+    # parts of about half the length (131200 / 2048 blocks, whole tiles: 68), 31 per pair,
+    # 1984 items in one generation
+    table, ctx, nb = long_tables(32, 32790)
+    t = torch.from_numpy(table)
+    c = torch.from_numpy(ctx)
+    plan, image = kvp.decode_plan_build(14, 2, t, c, nb, share_prefix=False, long_items=True, kv_dtype=torch.int8)
+    items, _, nparts, _ = check_plan(plan, image, table, ctx, nb, 14, 2)
+    live = items[items[:, 0] != F_EMPTY]
+    assert len(live) == 1984 and live[:, 5].max() <= 68 and (nparts == 31).all()

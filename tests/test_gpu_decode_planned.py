@@ -23,7 +23,8 @@ def _bits(t):
 
 def _plan(step, share=True, long_items=False):
     plan, image = kvp.decode_plan_build(step.hq, step.hkv, step.table.cpu(), step.ctx.cpu(), step.num_blocks,
-                                        share_prefix=share, head_dim=step.head_dim, long_items=long_items)
+                                        share_prefix=share, head_dim=step.head_dim, long_items=long_items,
+                                        kv_dtype=step.dtype)
     return plan, kvp.upload_plan(plan, image)
 
 
@@ -138,11 +139,11 @@ def test_planned_rejects_mismatched_plan():
 
 @pytest.mark.parametrize("dtype", [torch.float16, torch.int8])
 def test_planned_long_items_match_oracle(dtype):
-    # 200 requests of 2000-3000 tokens in sharing groups: about 60000 private blocks, more
-    # than 1024 waves x 32 blocks, so the private ranges become long items (ids in the id
-    # area); the shared prefixes stay 32-block items
+    # 200 requests of 3000-4000 tokens in sharing groups: about 75000 private blocks, more
+    # than the resident waves x 32 blocks (1024 fp16 waves, 2048 int8 waves), so the private
+    # ranges become long items (ids in the id area); the shared prefixes stay 32-block items
     need_gpu()
-    pb = W.paged_batch(200, lo=2000, hi=3000, seed=61)
+    pb = W.paged_batch(200, lo=3000, hi=4000, seed=61)
     say("planned long items", dtype, "B", pb.batch)
     step = PagedStep(kvp, pb, layers=1, hq=14, hkv=2, dtype=dtype, seed=9700)
     plan, dp = _plan(step, long_items=True)
