@@ -454,6 +454,10 @@ def main():
     ap.add_argument("--no-graph", action="store_true", help="launch the layers eagerly")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-share", action="store_true", help="plans without shared-prefix items")
+    ap.add_argument("--long-items", action="store_true",
+                    help="decode workload: plans with long items (KVP_PLAN_LONG_ITEMS, which sizes parts to "
+                         "one generation of waves when a batch's private blocks far exceed them and leaves "
+                         "smaller batches' plans as they are); always on for long_context")
     ap.add_argument("--seed", type=int, default=42)
     ap.add_argument("--workload", choices=["decode", "long_context", "prefill", "chunked_prefill", "batching"],
                     default="decode",
@@ -518,7 +522,7 @@ def main():
     cows = (kvp.kvp_copy * B)()
     pool.export_raw(ids.data_ptr(), B, max_blocks, t0h.data_ptr(), c0h.data_ptr())
     c0h += total_steps + 1  # the longest contexts of this run (plan sizing only)
-    long_items = long_ctx is not None  # fewer, longer parts: the batch far exceeds the resident waves
+    long_items = args.long_items or long_ctx is not None  # fewer, longer parts for very large batches
     kv_dtype = torch.int8 if KV_INT8 else torch.float16
     plan0, _ = kvp.decode_plan_build(HQ, HKV, t0h, c0h, cache.num_blocks, share_prefix=share, head_dim=D,
                                      long_items=long_items, kv_dtype=kv_dtype)
