@@ -11,7 +11,8 @@ included), the host planner turns the block table into the step's work plan (sha
 prefixes read once per group of members), the plan is uploaded and the copy-on-write block
 copies run, then for each of the 24 layers one kernel appends the new token's K/V and runs
 the paged decode attention over the whole cache (paged_decode_attention_planned, replayed
-as one captured graph).  Contexts grow by one token per step.
+as one captured graph).  Contexts grow by one token per step.  The plan upload runs on a
+copy stream into one of two device buffers, beside the previous step's layers.
 
 --shape 32q8kv_d128 / 32q32kv_d128 runs the same step at the 7B-class head shapes (32
 layers, head dim 128, 8 or 32 KV heads).  --workload prefill / chunked_prefill time the
@@ -534,7 +535,13 @@ def main():
                pairs=torch.empty((B, 2), dtype=torch.int32).pin_memory(),
                image=torch.empty((img_bytes,), dtype=torch.uint8).pin_memory(),
                plan=kvp.kvp_decode_plan()) for _ in range(2)]
-    plan_d = torch.empty((img_bytes,), dtype=torch.uint8, device=dev)
+    # two device plan buffers: step k's plan is uploaded on a copy stream into buffer k % 2
+    # while step k - 1's layers (reading the other buffer) run; one captured graph per buffer
+    plan_d = [torch.empty((img_bytes,), dtype=torch.uint8, device=dev) for _ in range(2)]
+    copy_stream = torch.cuda.Stream()  # default priority
+    uploaded = [torch.cuda.Event(), torch.cuda.Event()]
+    released = [torch.cuda.Event(), torch.cuda.Event()]  # the layers that read buffer i are done
+    in_use = [False, False]
     slot_cap = 2 * plan0.n_slots + B * HKV
     ws_plan = kvp.kvp_decode_plan()
     ws_plan.B, ws_plan.num_kv_heads, ws_plan.n_slots, ws_plan.head_dim = B, HKV, slot_cap, D
@@ -543,14 +550,14 @@ def main():
     stream = torch.cuda.current_stream()
     launch_plan = [None]
 
-    def layers_body():
+    def layers_body(pd):
         # per layer: the new token's K/V go into the cache and the decode attends over it,
         # in one kernel following the step's plan
         for l in range(L):
-            kvp.paged_decode_attention_planned(cache, l, q[l], launch_plan[0], plan_d, k_new=knew[l], v_new=vnew[l],
+            kvp.paged_decode_attention_planned(cache, l, q[l], launch_plan[0], pd, k_new=knew[l], v_new=vnew[l],
                                                out=out[l], workspace=ws)
 
-    graph = None
+    graphs = [None, None]
     record = []
 
     def step(k, keep=False):
@@ -579,23 +586,32 @@ def main():
         if keep:
             record.append((h["table"].numpy().copy(), h["ctx"].numpy().copy(), npairs, plan.n_shared,
                            plan.kv_blocks_read))
-        plan_d[: plan.bytes].copy_(h["image"][: plan.bytes], non_blocking=True)
+        i = k % 2
+        if in_use[i]:  # step k - 2 read this buffer
+            copy_stream.wait_event(released[i])
+        with torch.cuda.stream(copy_stream):
+            plan_d[i][: plan.bytes].copy_(h["image"][: plan.bytes], non_blocking=True)
+            uploaded[i].record(copy_stream)
         if npairs:
             pairs_d[:npairs].copy_(h["pairs"][:npairs], non_blocking=True)
             kvp.kv_copy_blocks(cache, pairs_d[:npairs])
-        if graph is not None:
-            graph.replay()
+        stream.wait_event(uploaded[i])
+        if graphs[i] is not None:
+            graphs[i].replay()
         else:
-            layers_body()
-        done[k % 2].record(stream)
+            layers_body(plan_d[i])
+        released[i].record(stream)
+        in_use[i] = True
+        done[i].record(stream)  # also covers the upload, which the layers waited for
 
     # first step eagerly (loads code objects), then capture the 24-layer body
     step(0)
     torch.cuda.synchronize()
     if not args.no_graph:
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph):
-            layers_body()
+        for i in range(2):
+            graphs[i] = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graphs[i]):
+                layers_body(plan_d[i])
         torch.cuda.synchronize()
     k = 1
     for _ in range(args.warmup):
@@ -632,7 +648,7 @@ def main():
     for r in range(args.kernel_reps):
         for l in range(L):
             evs[i][0].record(stream)
-            kvp.paged_decode_attention_planned(cache, l, q[l], launch_plan[0], plan_d, k_new=knew[l],
+            kvp.paged_decode_attention_planned(cache, l, q[l], launch_plan[0], plan_d[(k - 1) % 2], k_new=knew[l],
                                                v_new=vnew[l], out=out[l], workspace=ws)
             evs[i][1].record(stream)
             i += 1
@@ -669,7 +685,7 @@ def main():
                                   "groups of 8 sharing a 512-token prefix (copy-on-write)" if long_ctx is None else
                                   f", 16-token blocks, every context {long_ctx} tokens (+1 per step), no sharing"),
                    "batch": B, "layers": L, "shape": args.shape, "kv_dtype": args.kv_dtype,
-                   "graph": graph is not None},
+                   "graph": graphs[0] is not None},
         "steps_per_sec": round(1e3 / ms_per_step, 2),
         "hbm_pct": round(value / HBM_PEAK_GBPS * 100, 2),
         "logical_GBps": round(logical_gbps, 2),
