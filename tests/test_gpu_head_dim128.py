@@ -26,9 +26,10 @@ def _bits(t):
     return t.contiguous().view(torch.int16 if t.dtype == torch.float16 else torch.int32)
 
 
-def _plan(step, share=True):
+def _plan(step, share=True, long_items=False):
     plan, image = kvp.decode_plan_build(step.hq, step.hkv, step.table.cpu(), step.ctx.cpu(), step.num_blocks,
-                                        share_prefix=share, head_dim=D)
+                                        share_prefix=share, head_dim=D, long_items=long_items,
+                                        kv_dtype=step.dtype)
     assert plan.head_dim == D
     return plan, kvp.upload_plan(plan, image)
 
@@ -99,6 +100,27 @@ def test_planned_decode_bit_identical_without_sharing_and_oracle_with_sharing():
     want = step.oracle(0)
     err = max_abs(to64(o_plan1), want)
     say("d128 planned shared max err", err)
+    assert err <= TOL[torch.float16]
+
+
+@pytest.mark.parametrize("dtype", [torch.float16, torch.int8])
+def test_planned_long_items_match_oracle(dtype):
+    # 32q/8kv: batch 200 has about 57000 private blocks (fp16: more than 1024 waves x 32),
+    # batch 80 of 3000-4000 tokens about 120000 (int8: more than 2048 x 32), so the private
+    # ranges become long items of 32-token tiles (two blocks a tile); every 13th request is
+    # compared with the oracle
+    need_gpu()
+    pb = W.paged_batch(200) if dtype == torch.float16 else W.paged_batch(80, lo=3000, hi=4000, seed=62)
+    say("d128 planned long items", dtype)
+    step = PagedStep(kvp, pb, layers=1, hq=32, hkv=8, dtype=dtype, seed=22300, head_dim=D)
+    plan, dp = _plan(step, long_items=True)
+    assert plan.n_ids > 0
+    q = step.q(0).cuda()
+    o = kvp.paged_decode_attention_planned(step.cache, 0, q, plan, dp, workspace=kvp.make_plan_workspace(plan))
+    torch.cuda.synchronize()
+    rows = list(range(0, pb.batch, 13))
+    err = max_abs(to64(o[rows]), step.oracle(0, rows))
+    say("d128 long items", dtype, "items", plan.n_items, "ids", plan.n_ids, "max err", err)
     assert err <= TOL[torch.float16]
 
 
