@@ -41,7 +41,7 @@ static size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 static size_t part_bytes(const kvp_dims *d, int B, int max_context)
 {
     if (d->dtype != KVP_F32) { // the fp16 kernel (fp16 or int8 caches)
-        const int ipp = decode_f16_items_per_pair(max_context);
+        const int ipp = decode_f16_items_per_pair(max_context, d->dtype == KVP_I8, d->head_dim);
         return ipp > 1 ? decode_f16_part_bytes((long long)B * d->num_kv_heads * ipp, d->head_dim) : 0;
     }
     const int ms = decode_f32_max_splits(max_context);

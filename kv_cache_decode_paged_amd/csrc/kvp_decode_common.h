@@ -189,7 +189,7 @@ kvp_status launch_decode_f32(const DecodeParams &P, const ContigAddr &A, int gro
 
 // workspace layout helpers (bytes), shared by the launchers and the size queries
 size_t decode_f16_part_bytes(long long slots, int dim);
-int decode_f16_items_per_pair(int max_context);
+int decode_f16_items_per_pair(int max_context, bool i8, int dim);
 size_t decode_f32_part_bytes(int B, int hq, int max_splits);
 int decode_f32_max_splits(int max_context);
 

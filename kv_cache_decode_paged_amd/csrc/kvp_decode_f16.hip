@@ -854,9 +854,9 @@ __global__ __launch_bounds__(64) void decode_f16_kernel(DecodeParams P, Addr A, 
         int ctx = P.ctx_lens[it.b];
         ctx = ctx < 0 ? 0 : (ctx > maxc ? maxc : ctx);
         const int nbt = (ctx + BS - 1) / BS;
-        // one item up to UNSPLIT_BLOCKS blocks, else ceil(blocks / SPLIT_BLOCKS) parts; the last
+        // one item up to unsplit_blocks blocks, else ceil(blocks / split_blocks) parts; the last
         // (the pair's merging item) up to SPLIT_SLACK tiles longer than the others
-        const int n = nbt <= UNSPLIT_BLOCKS ? 1 : (nbt + SPLIT_BLOCKS - 1) / SPLIT_BLOCKS;
+        const int n = nbt <= unsplit_blocks(I8, HD) ? 1 : (nbt + split_blocks(I8, HD) - 1) / split_blocks(I8, HD);
         if (k >= n)
             return;
         const int T = (nbt + 3) >> 2;
@@ -923,10 +923,10 @@ static kvp_status launch_f16(const DecodeParams &P, const Addr &A, const PlanVie
     return KVP_OK;
 }
 
-int decode_f16_items_per_pair(int max_context)
+int decode_f16_items_per_pair(int max_context, bool i8, int dim)
 {
     const int nb = (std::max(max_context, 1) + BS - 1) / BS;
-    return nb <= UNSPLIT_BLOCKS ? 1 : (nb + SPLIT_BLOCKS - 1) / SPLIT_BLOCKS;
+    return nb <= unsplit_blocks(i8, dim) ? 1 : (nb + split_blocks(i8, dim) - 1) / split_blocks(i8, dim);
 }
 
 size_t decode_f16_part_bytes(long long slots, int dim)
@@ -937,13 +937,15 @@ size_t decode_f16_part_bytes(long long slots, int dim)
 kvp_status launch_decode_f16(const DecodeParams &P, const PagedAddr &A, int group, int max_context,
                              hipStream_t st)
 {
-    PlanView PV{nullptr, nullptr, nullptr, nullptr, decode_f16_items_per_pair(max_context), nullptr, 0};
+    PlanView PV{nullptr, nullptr, nullptr, nullptr, decode_f16_items_per_pair(max_context, P.kv_i8 != 0, P.dim), nullptr,
+                0};
     return launch_f16<false>(P, A, PV, group, (long long)P.B * P.hkv * PV.ipp, st);
 }
 kvp_status launch_decode_f16(const DecodeParams &P, const ContigAddr &A, int group, int max_context,
                              hipStream_t st)
 {
-    PlanView PV{nullptr, nullptr, nullptr, nullptr, decode_f16_items_per_pair(max_context), nullptr, 0};
+    PlanView PV{nullptr, nullptr, nullptr, nullptr, decode_f16_items_per_pair(max_context, P.kv_i8 != 0, P.dim), nullptr,
+                0};
     return launch_f16<false>(P, A, PV, group, (long long)P.B * P.hkv * PV.ipp, st);
 }
 kvp_status launch_decode_f16_planned(const DecodeParams &P, const PagedAddr &A, int group,

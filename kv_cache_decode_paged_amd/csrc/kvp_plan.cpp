@@ -44,9 +44,9 @@ kvp_status check_plan_dims(const kvp_dims *d, const char *who)
 constexpr int MAX_BUNDLE = 8; // shared items kept together on one XCD
 
 
-long long max_items(long long B, long long hkv, long long max_blocks)
+long long max_items(long long B, long long hkv, long long max_blocks, bool i8, int hd)
 {
-    const long long ipp = std::max<long long>(1, (max_blocks + SPLIT_BLOCKS - 1) / SPLIT_BLOCKS);
+    const long long ipp = std::max<long long>(1, (max_blocks + split_blocks(i8, hd) - 1) / split_blocks(i8, hd));
     // private items: at most ipp per pair; shared items: at most one set per two requests;
     // plus the padding that evens out the XCD queues and rounds them to whole CU rounds
     const long long work = B * hkv * ipp + (B / 2) * hkv * ipp;
@@ -61,13 +61,13 @@ size_t image_bytes_for(long long items, long long B, long long hkv, long long ma
            align16((size_t)B * hkv * max_blocks * 4);
 }
 
-// parts of a range of nb blocks: one item up to BPI blocks unless `forced` (the pair has
-// other parts anyway), else ceil(nb / SPLIT_BLOCKS) parts of equal tile counts
-int split_parts(int nb, bool forced)
+// parts of a range of nb blocks: one item up to unsplit_blocks blocks unless `forced` (the
+// pair has other parts anyway), else ceil(nb / split_blocks) parts of equal tile counts
+int split_parts(int nb, bool forced, bool i8, int hd)
 {
-    if (nb <= 0 || (!forced && nb <= UNSPLIT_BLOCKS))
+    if (nb <= 0 || (!forced && nb <= unsplit_blocks(i8, hd)))
         return 1;
-    return (nb + SPLIT_BLOCKS - 1) / SPLIT_BLOCKS;
+    return (nb + split_blocks(i8, hd) - 1) / split_blocks(i8, hd);
 }
 // first block of part k of n over nb blocks (part k holds tiles [k T / n, (k+1) T / n))
 int split_start(int nb, int n, int k, int slack = 0)
@@ -88,7 +88,9 @@ size_t decode_plan_bytes(const kvp_dims *dims, int32_t B, int32_t max_blocks, in
     if (check_plan_dims(dims, "decode_plan_bytes") != KVP_OK || B < 0 || max_blocks <= 0 || pad_items < 0)
         return 0;
     const long long pad = ((long long)pad_items + XCDS - 1) / XCDS * XCDS;
-    return image_bytes_for(std::max(pad, max_items(B, dims->num_kv_heads, max_blocks)), B, dims->num_kv_heads,
+    return image_bytes_for(std::max(pad, max_items(B, dims->num_kv_heads, max_blocks, dims->dtype == KVP_I8,
+                                                     dims->head_dim)), B,
+                           dims->num_kv_heads,
                            max_blocks);
 }
 
@@ -111,6 +113,8 @@ kvp_status decode_plan_build(const kvp_dims *dims, const int32_t *table, int32_t
     if ((long long)max_blocks * BS > 0x7fffffffLL)
         return fail(KVP_ERR_UNSUPPORTED, "%s: max_blocks too large", who);
     const int hkv = dims->num_kv_heads;
+    const bool i8 = dims->dtype == KVP_I8; // the int8 kernel's split sizes
+    const int hd = dims->head_dim;
     const int G = dims->num_q_heads / hkv;
     const int maxm = std::max(1, std::min(MAXM, 16 / G)); // members of a shared item (<= 16 rows)
     const long long npairs = (long long)B * hkv;
@@ -169,7 +173,7 @@ kvp_status decode_plan_build(const kvp_dims *dims, const int32_t *table, int32_t
     std::vector<int> shared_parts(B, 0);
     for (const SubRun &sr : subs) {
         const int nsb = sr.shared_tokens / BS;
-        const int ns = split_parts(nsb, true);
+        const int ns = split_parts(nsb, true, i8, hd);
         for (int m = sr.a; m < sr.a + sr.n; ++m)
             for (int k = 0; k < ns; ++k)
                 if (BS * split_start(nsb, ns, k) < E[m])
@@ -178,19 +182,19 @@ kvp_status decode_plan_build(const kvp_dims *dims, const int32_t *table, int32_t
     // long items: parts of up to S blocks, S sized so the private blocks fill about one
     // generation of waves (whole tiles, between SPLIT_BLOCKS and LONG_BPI); S = SPLIT_BLOCKS
     // leaves the plan as without the flag
-    int S = SPLIT_BLOCKS;
+    int S = split_blocks(i8, hd);
     if (flags & KVP_PLAN_LONG_ITEMS) {
         long long priv_blocks = 0;
         for (int b = 0; b < B; ++b)
             priv_blocks += (long long)hkv * std::max(0, nbt[b] - E[b] / BS);
         const long long waves = dims->dtype == KVP_I8 ? LONG_TARGET_WAVES_I8 : LONG_TARGET_WAVES_F16;
         const long long per_wave = (priv_blocks + waves - 1) / waves;
-        S = (int)std::min<long long>(LONG_BPI, std::max<long long>(SPLIT_BLOCKS, (per_wave + 3) / 4 * 4));
+        S = (int)std::min<long long>(LONG_BPI, std::max<long long>(split_blocks(i8, hd), (per_wave + 3) / 4 * 4));
     }
     auto private_items = [&](int b) -> int {
         const int nb = nbt[b] - E[b] / BS;
-        if (S == SPLIT_BLOCKS || nb <= UNSPLIT_BLOCKS)
-            return split_parts(nb, E[b] > 0);
+        if (S == split_blocks(i8, hd) || nb <= unsplit_blocks(i8, hd))
+            return split_parts(nb, E[b] > 0, i8, hd);
         return (nb + S - 1) / S;
     };
     std::vector<int> pair_base(npairs, -1), pair_nparts(npairs, 1);
@@ -207,7 +211,7 @@ kvp_status decode_plan_build(const kvp_dims *dims, const int32_t *table, int32_t
         }
     long long n_shared = 0;
     for (const SubRun &s : subs)
-        n_shared += (long long)hkv * split_parts(s.shared_tokens / BS, true);
+        n_shared += (long long)hkv * split_parts(s.shared_tokens / BS, true, i8, hd);
     n_items += n_shared;
     if (slots > 0x7fffffffLL || n_items > 0x7fffffffLL)
         return fail(KVP_ERR_UNSUPPORTED, "%s: plan too large", who);
@@ -253,7 +257,7 @@ kvp_status decode_plan_build(const kvp_dims *dims, const int32_t *table, int32_t
         std::vector<std::pair<long long, long long>> keyed; // (run * hkv + g, item)
         for (const SubRun &sr : subs) {
             const int nsb = sr.shared_tokens / BS;
-            const int ns = split_parts(nsb, true);
+            const int ns = split_parts(nsb, true, i8, hd);
             for (int g = 0; g < hkv; ++g)
                 for (int k = 0; k < ns; ++k) {
                     const int b0 = split_start(nsb, ns, k), b1 = split_start(nsb, ns, k + 1);

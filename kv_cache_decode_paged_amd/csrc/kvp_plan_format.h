@@ -24,6 +24,14 @@ constexpr int BPI = 32;  // blocks per work item (512 tokens)
 // count faster than the shorter tail saves, so the parts are as long as an item may be.
 constexpr int SPLIT_BLOCKS = 32;
 constexpr int UNSPLIT_BLOCKS = 32; // longest pair kept in one item (at most BPI)
+// The int8 kernel keeps twice the waves resident (18 KB of LDS each, eight per CU): at head
+// dim 64, parts of 16 blocks fill them (batch 200, 14q / 2kv: 18.6 us per launch by the trace
+// against 20.6 with 32-block parts).  At head dim 128 the many more pairs already fill them
+// and the extra merges cost more (32q / 8kv: 72.4 against 69.4 us), so 32 blocks stay.
+constexpr int SPLIT_BLOCKS_I8_D64 = 16;
+constexpr int UNSPLIT_BLOCKS_I8_D64 = 16;
+constexpr int split_blocks(bool i8, int hd) { return i8 && hd == 64 ? SPLIT_BLOCKS_I8_D64 : SPLIT_BLOCKS; }
+constexpr int unsplit_blocks(bool i8, int hd) { return i8 && hd == 64 ? UNSPLIT_BLOCKS_I8_D64 : UNSPLIT_BLOCKS; }
 // Tiles (4 blocks) of the parts of a range of T tiles split n ways: part k covers tiles
 // [part_tile_begin(T, n, k, slack), part_tile_begin(T, n, k + 1, slack)).  The last part
 // -- the one that holds the range's final blocks, which merges a split pair -- gets up to

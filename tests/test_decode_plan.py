@@ -380,3 +380,27 @@ def test_long_items_sized_for_the_int8_kernel():
     items, _, nparts, _ = check_plan(plan, image, table, ctx, nb, 14, 2)
     live = items[items[:, 0] != F_EMPTY]
     assert len(live) == 1984 and live[:, 5].max() <= 68 and (nparts == 31).all()
+
+
+def test_int8_plans_split_at_16_blocks():
+    # an int8 cache's plan (kv_dtype=int8): without sharing, one item up to 16 blocks, else
+    # ceil(blocks / 16) parts -- the unplanned int8 call's own splits
+    rng = np.random.default_rng(21)
+    B = 12
+    ctx = rng.integers(1, 900, size=B).astype(np.int32)
+    nbt = (ctx + BS - 1) // BS
+    nb = int(nbt.sum()) + 4
+    ids = rng.permutation(nb).astype(np.int32)
+    table = np.full((B, int(nbt.max())), -1, np.int32)
+    o = 0
+    for b in range(B):
+        table[b, : nbt[b]] = ids[o: o + nbt[b]]
+        o += nbt[b]
+    t, c = torch.from_numpy(table), torch.from_numpy(ctx)
+    plan, image = kvp.decode_plan_build(14, 2, t, c, nb, share_prefix=False, kv_dtype=torch.int8)
+    items, _, nparts, _ = check_plan(plan, image, table, ctx, nb, 14, 2)
+    for b in range(B):
+        want = 1 if nbt[b] <= 16 else -(-int(nbt[b]) // 16)
+        assert int(nparts[2 * b]) == want == int(nparts[2 * b + 1]), b
+    live = items[items[:, 0] != F_EMPTY]
+    assert live[:, 5].max() <= 16

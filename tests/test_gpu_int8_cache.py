@@ -111,7 +111,7 @@ def test_ragged_edges_and_tile_boundaries(d):
 
 def _plan(step, share=True):
     plan, image = kvp.decode_plan_build(step.hq, step.hkv, step.table.cpu(), step.ctx.cpu(), step.num_blocks,
-                                        share_prefix=share, head_dim=step.head_dim)
+                                        share_prefix=share, head_dim=step.head_dim, kv_dtype=I8)
     return plan, kvp.upload_plan(plan, image)
 
 
@@ -217,9 +217,10 @@ def test_planned_full_size_b200():
     pb = W.paged_batch(200)
     say("int8 planned batch 200 (24-layer pool, data in layers 0 and 23)")
     step = PagedStep(kvp, pb, layers=24, hq=14, hkv=2, dtype=I8, seed=31700, layers_with_data=[0, 23])
-    plan0, _ = kvp.decode_plan_build(14, 2, step.table.cpu(), step.ctx.cpu(), step.num_blocks, share_prefix=True)
+    plan0, _ = kvp.decode_plan_build(14, 2, step.table.cpu(), step.ctx.cpu(), step.num_blocks, share_prefix=True,
+                                     kv_dtype=I8)
     plan, image = kvp.decode_plan_build(14, 2, step.table.cpu(), step.ctx.cpu(), step.num_blocks, share_prefix=True,
-                                        pad_items=plan0.n_items + 256)
+                                        pad_items=plan0.n_items + 256, kv_dtype=I8)
     dp = kvp.upload_plan(plan, image)
     ws = kvp.make_plan_workspace(plan)
     for l in (0, 23):
