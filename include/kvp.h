@@ -343,10 +343,12 @@ kvp_status contiguous_decode_attention(const kvp_dims *dims, void *out, const vo
  * ------------------------------------------------------------------------------------ */
 #define KVP_PLAN_SHARE_PREFIX 1u
 /* Batches of long contexts: when the private blocks number far more than the waves the GPU
- * holds at once (about 1024), cut each pair's private range into fewer, longer parts (up to
- * 128 blocks; their block ids go to an id area at the end of the image) so that the launch
- * runs in about one generation of waves.  Changes the splits, so the result equals the
- * unplanned call's up to the order of the fp32 sums only. */
+ * holds at once (about 1024 for fp16, 2048 for int8 caches, from dims->dtype), cut each
+ * pair's private range into fewer, longer parts (up to 192 blocks; their block ids go to an
+ * id area at the end of the image) so that the launch runs in about one generation of
+ * waves.  Changes the splits, so the result equals the unplanned call's up to the order of
+ * the fp32 sums only.  The plan's split sizes also follow dims->dtype: int8 caches at head
+ * dim 64 are cut into 16-block parts (32 otherwise), as in the unplanned call. */
 #define KVP_PLAN_LONG_ITEMS 2u
 
 typedef struct {
