@@ -481,7 +481,9 @@ def decode_plan_build(num_q_heads, num_kv_heads, block_table, context_lens, num_
     a uint8 CPU tensor whose first plan.bytes bytes are to be copied to the device.
     pad_items > 0 fixes the item count (see decode_plan_build in kvp.h); long_items asks for
     KVP_PLAN_LONG_ITEMS (fewer, longer parts for batches of long contexts), sized for the
-    waves the kernel of kv_dtype's cache keeps resident (torch.float16 or torch.int8)."""
+    waves the kernel of kv_dtype's cache keeps resident.  kv_dtype (torch.float16 or
+    torch.int8, the cache's) also sets the split size: an int8 cache at head dim 64 is cut
+    into 16-block parts, as the unplanned call does, so pass it for int8 caches."""
     B, max_blocks = block_table.shape
     if context_lens.shape != (B,):
         raise ValueError("decode_plan_build: context_lens shape mismatch")
