@@ -130,7 +130,10 @@ void block_pool_destroy(kvp_pool *pool);
 kvp_status block_pool_set_free_order(kvp_pool *pool, const int32_t *perm, int32_t n);
 
 /* New sequence holding n_tokens tokens: ceil(n_tokens / block_size) fresh blocks, each
- * with reference count 1.  OOM (and no change) if too few blocks are free. */
+ * with reference count 1, taken from the front of the free list ([PAGED] SECTION 2: a new
+ * request is given the pages its tokens need; [CHAP] PagedAttention passage: the cache is
+ * allocated in fixed-size blocks on demand).  OOM (and no change) if too few blocks are
+ * free. */
 kvp_status block_table_alloc(kvp_pool *pool, int32_t n_tokens, int32_t *seq_id);
 
 /* Reserve the position of sequence `seq`'s next token and return its slot.  At a block
@@ -170,12 +173,18 @@ kvp_status block_table_cow(kvp_pool *pool, int32_t seq, int32_t logical_block, i
 kvp_status block_table_truncate(kvp_pool *pool, int32_t seq, int32_t n_tokens);
 
 /* Release every block of the sequence (a block returns to the free list when its
- * reference count reaches 0) and forget the sequence. */
+ * reference count reaches 0) and forget the sequence ([PAGED] SECTION 2: a finished
+ * request hands its pages back, a page is free again once no table refers to it; SECTION
+ * 3: a shared page survives while other requests hold it).  NOT_FOUND for an unknown id;
+ * releasing a block that is already free is INVALID (nothing changes). */
 kvp_status block_table_free(kvp_pool *pool, int32_t seq);
 
 /* Host export of n sequences' tables into host_table [n][max_blocks] (unused entries -1)
- * and their token counts into context_lens [n].  INVALID if a table is longer than
- * max_blocks.  The caller uploads both to the device for the attention calls. */
+ * and their token counts into context_lens [n] ([PAGED] SECTION 2: the per-request block
+ * table maps logical block j / block_size to a physical page; [CHAP] PagedAttention
+ * passage: the kernel reaches the cache through that table).  INVALID if a table is longer
+ * than max_blocks; NOT_FOUND for an unknown id.  The caller uploads both to the device for
+ * the attention calls. */
 kvp_status block_table_export(const kvp_pool *pool, const int32_t *seqs, int32_t n,
                               int32_t max_blocks, int32_t *host_table, int32_t *context_lens);
 
@@ -271,14 +280,20 @@ kvp_status kv_copy_blocks(const kvp_cache_desc *cache, const int32_t *d_pairs, i
 kvp_status kv_append(const kvp_cache_desc *cache, int32_t layer, const void *k, const void *v,
                      const int64_t *d_slots, int32_t n, kvp_stream stream);
 
-/* Contiguous-layout append: for each b < B, writes k[b], v[b] ([B][H_kv][d]) at position
- * d_pos[b] (< Lmax) of k_cache / v_cache ([B][H_kv][Lmax][d], one layer). */
+/* Contiguous-layout append ([KVES] step 2: k_t, v_t go to the end of each head's cache;
+ * [CHAP] allocator check: one contiguous (B, H_kv, L, d) tensor per layer): for each b < B,
+ * writes k[b], v[b] ([B][H_kv][d], device) at position d_pos[b] (device int32 [B], each in
+ * 0..Lmax-1, distinct per b) of k_cache / v_cache ([B][H_kv][Lmax][d], one layer, device),
+ * bit for bit.  fp16 or fp32 (UNSUPPORTED for int8); INVALID for Lmax <= 0 or NULL
+ * pointers. */
 kvp_status contiguous_kv_append(const kvp_dims *dims, void *k_cache, void *v_cache,
                                 int32_t Lmax, const void *k, const void *v,
                                 const int32_t *d_pos, int32_t B, kvp_stream stream);
 
-/* Workspace bytes for decode with B requests and contexts up to max_context tokens
- * (split-K partials).  0 if the arguments are invalid. */
+/* Workspace bytes for decode with B requests and contexts up to max_context tokens: one
+ * counter per (request, KV head) and the split partials (m, l, o) that the [FLASH] rescale
+ * merge combines (block softmaxes kept with their maximum and sum).  0 if the arguments are
+ * invalid or no split is needed. */
 size_t decode_workspace_bytes(const kvp_dims *dims, int32_t B, int32_t max_context);
 
 /* Paged grouped-query decode attention for one layer ([CHAP] decode loop; [KVES] the new
@@ -450,13 +465,27 @@ kvp_status varlen_causal_prefill(const kvp_dims *dims, void *out, const void *q,
                                  int32_t max_seqlen, int32_t causal, float scale,
                                  kvp_stream stream);
 
-/* Gather one layer of the paged cache back to the contiguous layout: positions
- * j < d_context_lens[b] of k_out / v_out [B][H_kv][Lmax][d] receive the paged rows, bit for
- * bit; other positions are left untouched.  For an int8 cache the rows are the codes (the
- * scales stay in the scale pools). */
+/* Gather one layer of the paged cache back to the contiguous layout ([PAGED] SECTION 2:
+ * logical token j of a request lives in page table[j / block_size] at offset
+ * j % block_size; [CHAP] allocator check: the contiguous (B, H_kv, L, d) layout): positions
+ * j < d_context_lens[b] of k_out / v_out [B][H_kv][Lmax][d] (device) receive the paged
+ * rows, bit for bit; other positions are left untouched.  For an int8 cache the rows are
+ * the codes (the scales stay in the scale pools).  A test aid: INVALID for bad sizes or
+ * NULL pointers. */
 kvp_status kv_gather(const kvp_cache_desc *cache, int32_t layer, const int32_t *d_block_table,
                      int32_t max_blocks, const int32_t *d_context_lens, int32_t B, int32_t Lmax,
                      void *k_out, void *v_out, kvp_stream stream);
+
+/* --------------------------------------------------------------------------------------
+ * Measurement aid: the achievable HBM read bandwidth, against which the decode kernels'
+ * rates are set ([CHAP] decode is bound by the bytes read from memory).  Reads `bytes`
+ * bytes of d_buf (device, 16-byte aligned, bytes a multiple of 16) once, with 16-byte
+ * loads (8 in flight per lane) from `waves` wavefronts of 64 lanes (0: 8 per compute
+ * unit) striding over the buffer, and stores nothing unless the data holds a bit pattern that decides it (into
+ * d_sink, device int32 [1]); time it with events on `stream`.  INVALID for bad sizes.
+ * ------------------------------------------------------------------------------------ */
+kvp_status kvp_read_bandwidth_probe(const void *d_buf, size_t bytes, int32_t waves, int32_t *d_sink,
+                                    kvp_stream stream);
 
 #ifdef __cplusplus
 }

@@ -150,6 +150,7 @@ _sig("varlen_causal_prefill", _i32, [ctypes.POINTER(kvp_dims), _p, _p, _p, _p, _
 _sig("kvp_decode_merge_polls", _i32, [_i32])
 _sig("paged_prefill_attention", _i32, [ctypes.POINTER(kvp_cache_desc), _i32, _p, _p, _p, _i32, _p, _p, _i32,
                                        _i32, _f32, _p])
+_sig("kvp_read_bandwidth_probe", _i32, [_p, _sz, _i32, _p, _p])
 _sig("kv_gather", _i32, [ctypes.POINTER(kvp_cache_desc), _i32, _p, _i32, _p, _i32, _i32, _p, _p, _p])
 
 
@@ -462,8 +463,12 @@ def paged_decode_append_attention(cache: PagedKVCache, layer, q, k_new, v_new, b
     return out
 
 
-def decode_plan_bytes(num_q_heads, num_kv_heads, B, max_blocks, pad_items=0, head_dim=HEAD_DIM):
-    dm = dims(1, num_q_heads, num_kv_heads, torch.float16, head_dim)
+def decode_plan_bytes(num_q_heads, num_kv_heads, B, max_blocks, pad_items=0, head_dim=HEAD_DIM,
+                      kv_dtype=torch.float16):
+    """Bytes of a plan image for B requests and tables of max_blocks entries.  kv_dtype is
+    the cache's (torch.float16 or torch.int8): the int8 cache at head dim 64 splits into
+    shorter parts, so its plans can hold more items."""
+    dm = dims(1, num_q_heads, num_kv_heads, kv_dtype, head_dim)
     return int(_lib.decode_plan_bytes(ctypes.byref(dm), int(B), int(max_blocks), int(pad_items)))
 
 
@@ -487,7 +492,7 @@ def decode_plan_build(num_q_heads, num_kv_heads, block_table, context_lens, num_
     B, max_blocks = block_table.shape
     if context_lens.shape != (B,):
         raise ValueError("decode_plan_build: context_lens shape mismatch")
-    need = decode_plan_bytes(num_q_heads, num_kv_heads, B, max_blocks, pad_items, head_dim)
+    need = decode_plan_bytes(num_q_heads, num_kv_heads, B, max_blocks, pad_items, head_dim, kv_dtype)
     if image is None:
         image = torch.empty((max(need, 16),), dtype=torch.uint8, pin_memory=pin)
     if image.device.type != "cpu" or image.dtype != torch.uint8:
@@ -640,3 +645,13 @@ def kv_gather(cache: PagedKVCache, layer, block_table, context_lens, lmax, k_out
                           _dev(k_out, "k_out", cache.dtype), _dev(v_out, "v_out", cache.dtype),
                           _stream(stream)))
     return k_out, v_out
+
+
+def read_bandwidth_probe(buf, waves=0, sink=None, stream=None):
+    """Stream-read every byte of the device tensor `buf` once (kvp_read_bandwidth_probe);
+    time it with events on the stream.  sink: device int32 [1] (allocated if None)."""
+    if sink is None:
+        sink = torch.zeros((1,), dtype=torch.int32, device=buf.device)
+    _check(_lib.kvp_read_bandwidth_probe(_dev(buf, "buf"), buf.numel() * buf.element_size(), int(waves),
+                                         _dev(sink, "sink", torch.int32), _stream(stream)))
+    return sink

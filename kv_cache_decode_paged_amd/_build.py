@@ -12,7 +12,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libkvp.so")
 SOURCES = ["kvp_manager.cpp", "kvp_plan.cpp", "kvp_sched.cpp", "kvp_cache_ops.hip", "kvp_decode.hip", "kvp_decode_f16.hip",
-           "kvp_decode_f32.hip", "kvp_prefill.hip"]
+           "kvp_decode_f32.hip", "kvp_prefill.hip", "kvp_probe.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 

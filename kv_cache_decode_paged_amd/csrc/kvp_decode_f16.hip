@@ -194,7 +194,9 @@ __device__ __forceinline__ void merge_column(const float *part, int pbase, int n
 // 32 KB + 2 tt).  The score MFMA's row m of block kb is tile row 32 (kb / 2) + 8 (m / 4) +
 // 4 (kb % 2) + m % 4, so that lane group grp's probabilities of k-step ks are the eight
 // consecutive tokens 32 ks + 8 grp + s, whose V codes of one dimension are eight
-// consecutive bytes.  Codes become fp16 operands in registers: code * scale, rounded once.
+// consecutive bytes.  K codes enter the score product as exact fp16 integers and each key's
+// score is multiplied by its row scale in fp32; V codes become fp16 operands code * scale,
+// rounded once.
 template <int G, bool SHARED, int NBUF, int TT, int HD, bool I8, bool LONGI, typename Addr>
 __device__ __forceinline__ void run_item(const DecodeParams &P, const Addr &A, const PlanView &PV,
                                          const Item &it, int rv, const int (&rid)[3], char *kring, char *vring,
@@ -471,21 +473,25 @@ __device__ __forceinline__ void run_item(const DecodeParams &P, const Addr &A, c
 
         f16x8 kop[KB][KD]; // A of the score MFMA
         f16x8 vop[KS][NDB]; // A of the value MFMA (V^T)
+        float kscale[KB][4]; // int8: the K row scales of this lane's score rows
         if constexpr (I8) {
             char *kq = kring + (t % NBUF) * SLOTQ;
             char *vq = vring + (t % NBUF) * SLOTQ;
             char *sq = sring + (t % NBUF) * 1024;
             // K: lane (col, grp) of block kb reads tile row 32 (kb/2) + 8 (col/4) + 4 (kb%2) +
-            // col%4, dims 32 ks + 8 grp .. (8 bytes), and that row's scale
+            // col%4, dims 32 ks + 8 grp .. (8 bytes); the codes enter the score product as
+            // exact fp16 integers and the row scales multiply the fp32 scores afterwards.
+            // The lane's score rows 4 grp + i of block kb are the consecutive tile rows
+            // 32 (kb/2) + 8 grp + 4 (kb%2) + i: their four scales are one 8-byte read.
             u32x2 kraw[KB][KD];
-            unsigned ksc[KB];
+            u32x2 ksc4[KB];
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb) {
                 const int rt = 32 * (kb >> 1) + 8 * (col >> 2) + 4 * (kb & 1) + (col & 3);
 #pragma unroll
                 for (int ks = 0; ks < KD; ++ks)
                     kraw[kb][ks] = lds_b64(kq + rt * RQ + swz8<HD>(2 * ks + (grp >> 1), rt) * 16 + (grp & 1) * 8);
-                ksc[kb] = lds_u16(sq + 2 * rt);
+                ksc4[kb] = lds_b64(sq + 2 * (32 * (kb >> 1) + 8 * grp + 4 * (kb & 1)));
             }
             // V^T: lane (col, grp) of k-step ks reads dimension 16 db + col of tokens 32 ks +
             // 8 grp .. + 7 (8 consecutive bytes of the dim-major block), and their 8 scales
@@ -504,8 +510,15 @@ __device__ __forceinline__ void run_item(const DecodeParams &P, const Addr &A, c
 #pragma unroll
                 for (int ks = 0; ks < KD; ++ks)
                     asm volatile("" : "+v"(kraw[kb][ks]));
-                asm volatile("" : "+v"(ksc[kb]));
+                asm volatile("" : "+v"(ksc4[kb]));
             }
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const unsigned w = ksc4[kb][i >> 1];
+                    kscale[kb][i] = (float)__builtin_bit_cast(f16, (unsigned short)(i & 1 ? w >> 16 : w & 0xffffu));
+                }
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
                 asm volatile("" : "+v"(vsc[ks]));
@@ -537,6 +550,19 @@ __device__ __forceinline__ void run_item(const DecodeParams &P, const Addr &A, c
             // 1152 (exact), times the scale (one rounding)
             typedef f16 f16x2_ __attribute__((ext_vector_type(2)));
             const f16x2_ bias = {(f16)1152.f, (f16)1152.f};
+            // the codes alone, as exact fp16 integers
+            auto codes8 = [&](u32x2 code) -> f16x8 {
+                unsigned h[4];
+#pragma unroll
+                for (int w = 0; w < 2; ++w) {
+                    const unsigned x = code[w] ^ 0x80808080u;
+                    const unsigned lo = __builtin_amdgcn_perm(0x64646464u, x, 0x04010400u);
+                    const unsigned hi = __builtin_amdgcn_perm(0x64646464u, x, 0x04030402u);
+                    h[2 * w] = __builtin_bit_cast(unsigned, __builtin_bit_cast(f16x2_, lo) - bias);
+                    h[2 * w + 1] = __builtin_bit_cast(unsigned, __builtin_bit_cast(f16x2_, hi) - bias);
+                }
+                return __builtin_bit_cast(f16x8, i32x4{(int)h[0], (int)h[1], (int)h[2], (int)h[3]});
+            };
             auto dequant8 = [&](u32x2 code, const unsigned (&sc)[4]) -> f16x8 {
                 unsigned h[4];
 #pragma unroll
@@ -552,13 +578,10 @@ __device__ __forceinline__ void run_item(const DecodeParams &P, const Addr &A, c
                 return __builtin_bit_cast(f16x8, i32x4{(int)h[0], (int)h[1], (int)h[2], (int)h[3]});
             };
 #pragma unroll
-            for (int kb = 0; kb < KB; ++kb) {
-                const unsigned s2 = ksc[kb] | (ksc[kb] << 16);
-                const unsigned sc[4] = {s2, s2, s2, s2};
+            for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
                 for (int ks = 0; ks < KD; ++ks)
-                    kop[kb][ks] = dequant8(kraw[kb][ks], sc);
-            }
+                    kop[kb][ks] = codes8(kraw[kb][ks]);
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
                 const unsigned sc[4] = {(unsigned)vsc[ks][0], (unsigned)vsc[ks][1], (unsigned)vsc[ks][2],
@@ -622,6 +645,13 @@ __device__ __forceinline__ void run_item(const DecodeParams &P, const Addr &A, c
             for (int ks = 1; ks < KD; ++ks)
                 s = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop[kb][ks], qop[ks], s, 0, 0, 0);
             sacc[kb] = s;
+        }
+        if constexpr (I8) {
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    sacc[kb][i] *= kscale[kb][i];
         }
         if (!full) {
 #pragma unroll

@@ -37,15 +37,72 @@ def max_abs(a, b):
 TOL = {torch.float16: 2e-3, torch.float32: 1e-5}
 
 
+class ScoreShaper:
+    """Inputs whose scores move the kernels' softmax reference during a row.
+
+    The decode and prefill kernels keep a per-row reference maximum and move it only when
+    a tile's maximum passes it by more than 2^8; the accumulators are then rescaled by
+    2^(old - new), and split partials are merged with the same rescale (chatgpz.de
+    "Aufmerksamkeit", FlashAttention post: block softmaxes merged through their maxima).
+    N(0,1) inputs never get there, so these shapes force it (values only: no attention
+    arithmetic here):
+      ramp_up    key dim 0 grows with the position, query dim 0 = 8: the score rises by
+                 about 40 log2 units over 2048 positions (moves once per 512 tokens, and
+                 split partials whose maxima differ by about 10 units)
+      steep      the same ramp four times steeper: a move every second 64-key tile
+      ramp_down  the mirrored ramp: the first tile holds the maximum, later partials lie
+                 tens of units below it
+      late_peak  one key 3 positions before the end of each request (outside any shared
+                 prefix) scores about 12 log2 units above the rest
+      big_q      queries times 40: scores spread over hundreds of log2 units
+    V is halved everywhere (exact in fp16), so outputs stay below 2 in magnitude and their
+    single fp16 rounding stays well inside the tolerance."""
+    KINDS = ("ramp_up", "steep", "ramp_down", "late_peak", "big_q")
+    SPAN = 2048
+
+    def __init__(self, kind):
+        assert kind in self.KINDS, kind
+        self.kind = kind
+
+    def keys(self, K, V, start=0, peak_at=None):
+        """K, V [..., n, d] (positions start .. start + n - 1 along dim -2); peak_at: the
+        position to raise (late_peak), or None.  Returns shaped copies in the same dtype."""
+        dt = K.dtype
+        K = K.to(torch.float32).clone()
+        V = (V.to(torch.float32) * 0.5)
+        n = K.shape[-2]
+        pos = torch.arange(start, start + n, dtype=torch.float32)
+        if self.kind in ("ramp_up", "steep"):
+            K[..., :, 0] += (28.0 if self.kind == "ramp_up" else 112.0) * pos / self.SPAN
+        elif self.kind == "ramp_down":
+            K[..., :, 0] += 28.0 * (self.SPAN - pos) / self.SPAN
+        elif self.kind == "late_peak" and peak_at is not None and start <= peak_at < start + n:
+            K[..., peak_at - start, 0] += 11.0
+        return K.to(dt), V.to(dt)
+
+    def query(self, q):
+        dt = q.dtype
+        q = q.to(torch.float32).clone()
+        if self.kind == "big_q":
+            q = q * 40.0
+        else:
+            q[..., 0] = 8.0 if self.kind != "late_peak" else 6.0
+        return q.to(dt)
+
+
 class PagedStep:
     """One decode step of a batch over a paged cache, built through the block manager:
     sharing groups fork a prefix sequence (and truncate to shorter contexts), private
     tokens are reserved after it, then the step appends one token per request (copy-on-
-    write where the target block is shared) and writes its K/V in every layer."""
+    write where the target block is shared) and writes its K/V in every layer.  With
+    take_step=False only the state before the step is built (pool, cache, seqs, logical
+    rows of positions below each context)."""
 
     def __init__(self, kvp, pb: W.PagedBatch, layers, hq, hkv, dtype, seed, device="cuda",
-                 extra_blocks=64, poison=True, layers_with_data=None, head_dim=W.HEAD_DIM):
+                 extra_blocks=64, poison=True, layers_with_data=None, head_dim=W.HEAD_DIM, take_step=True,
+                 shaper=None):
         self.kvp, self.pb, self.layers = kvp, pb, layers
+        self.shaper = shaper
         self.hq, self.hkv, self.dtype, self.seed = hq, hkv, dtype, seed
         self.head_dim = head_dim
         # an int8 cache quantizes fp16 rows on append; q, out and the logical rows are fp16
@@ -74,6 +131,20 @@ class PagedStep:
                         for l in self.layers_with_data}
         prefix = {l: W.group_prefix_kv(pb, hkv, seed, io, layer=l, head_dim=head_dim)
                   for l in self.layers_with_data}
+        if shaper is not None:
+            # the same position-dependent shaping of the logical rows and of the group prefixes
+            # (the late peak sits past each request's shared prefix)
+            for l in self.layers_with_data:
+                K, V = self.logical[l]
+                Ks, Vs = [], []
+                for b in range(B):
+                    pk_at = pb.ctx_before[b] - 3
+                    assert shaper.kind != "late_peak" or pk_at >= min(pb.ctx_before[b], pb.prefix)
+                    kb, vb = shaper.keys(K[b], V[b], 0, pk_at)
+                    Ks.append(kb)
+                    Vs.append(vb)
+                self.logical[l] = (torch.stack(Ks), torch.stack(Vs))
+                prefix[l] = {g: shaper.keys(pk, pv, 0, None) for g, (pk, pv) in prefix[l].items()}
 
         seqs = [None] * B
         for gi in sorted(set(pb.group)):
@@ -100,6 +171,8 @@ class PagedStep:
                     self._reserve_private(s, i, 0, pb.ctx_before[i], device)
                     seqs[i] = s
         self.seqs = seqs
+        if not take_step:  # the state before the step (a caller drives the steps)
+            return
         # the decode step: one new token per request
         pairs, slots = [], []
         for i in range(B):
@@ -134,7 +207,8 @@ class PagedStep:
                                V[i, :, start:end].transpose(0, 1).contiguous().to(device), sl)
 
     def q(self, layer):
-        return W.decode_q(self.pb.batch, self.hq, self.seed, self.io_dtype, layer, self.head_dim)
+        q = W.decode_q(self.pb.batch, self.hq, self.seed, self.io_dtype, layer, self.head_dim)
+        return q if self.shaper is None else self.shaper.query(q)
 
     def oracle(self, layer, rows=None):
         """Oracle decode output [B, Hq, d] (float64) for the given requests (all if None)."""
@@ -162,7 +236,7 @@ class ChunkStep:
     shared prefix first.  Never-written cache rows hold NaN, so a read of one shows."""
 
     def __init__(self, kvp, prefixes, chunks, seed, hq=14, hkv=2, share_groups=None, layers=1,
-                 head_dim=W.HEAD_DIM):
+                 head_dim=W.HEAD_DIM, shaper=None):
         self.kvp = kvp
         self.B = len(prefixes)
         D = self.head_dim = head_dim
@@ -179,6 +253,10 @@ class ChunkStep:
         # logical K / V of every request, seeded
         self.K = W.randn((self.B, hkv, self.lmax, D), seed + 1)
         self.V = W.randn((self.B, hkv, self.lmax, D), seed + 2)
+        if shaper is not None:  # position-dependent shaping; the peak past any shared prefix
+            for b in range(self.B):
+                assert shaper.kind != "late_peak" or ctx[b] - 3 >= prefixes[b]
+                self.K[b], self.V[b] = shaper.keys(self.K[b], self.V[b], 0, ctx[b] - 3)
         if share_groups:
             # requests in one group share the first prefix's tokens (same K/V rows, one set
             # of physical blocks): fork the leader after it is written
@@ -212,6 +290,8 @@ class ChunkStep:
         self.table, self.ctxd = table.cuda(), ctxt.cuda()
         self.cu = torch.tensor([0] + list(np.cumsum(self.m)), dtype=torch.int32)
         self.q = W.randn((int(self.cu[-1]), hq, D), seed + 3)
+        if shaper is not None:
+            self.q = shaper.query(self.q)
 
     def _write(self, seq, b, lo, hi):
         if hi <= lo:

@@ -100,7 +100,7 @@ def test_gqa_24_layers_batch1(C):
 # ---------------------------------------------------------------------------------------
 # paged batches with shared prefixes (copy-on-write on the step), all rows vs the oracle
 # ---------------------------------------------------------------------------------------
-@pytest.mark.parametrize("B", [10, 50])
+@pytest.mark.parametrize("B", [10, 50, 100])
 def test_paged_batch_matches_oracle(B):
     need_gpu()
     pb = W.paged_batch(B)
@@ -327,8 +327,14 @@ def test_long_context_split_k_sampled():
     torch.cuda.synchronize()
     assert torch.equal(_bits(out.cpu()), _bits(oc.cpu()))
     assert torch.equal(_bits(out.cpu()), _bits(ocount.cpu()))
-    rows = [0, 13, 31]
-    want = oracle.decode_gqa(to64(q[rows]), to64(K[rows]), to64(V[rows]), np.full(len(rows), L))
+    # every request against the oracle, one request per host thread
+    import concurrent.futures as cf
+    rows = list(range(B))
+
+    def one(b):
+        return oracle.decode_gqa(to64(q[b:b + 1]), to64(K[b:b + 1]), to64(V[b:b + 1]), np.array([L]))[0]
+    with cf.ThreadPoolExecutor(max(1, min(16, len(os.sched_getaffinity(0))))) as ex:
+        want = np.stack(list(ex.map(one, rows)))
     err = max_abs(to64(out[rows]), want)
     say("long context max err", err)
     assert err <= TOL[torch.float16]

@@ -42,7 +42,7 @@ def test_planned_without_sharing_is_bit_identical():
     assert torch.equal(_bits(o_plan.cpu()), _bits(o_plain.cpu()))
 
 
-@pytest.mark.parametrize("B", [10, 50])
+@pytest.mark.parametrize("B", [10, 50, 100])
 def test_planned_shared_prefix_matches_oracle(B):
     need_gpu()
     pb = W.paged_batch(B)
