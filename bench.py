@@ -416,7 +416,7 @@ def decode_line(args, metric, B, L, ctx_before, group, prefix, long_items, share
     snap = snapshot_state(torch, pool, cache, seqs, max_blocks, check_layers) if want_cpu else None
     runner = DecodeStepRunner(cache, pool, seqs, max_blocks, q, knew, vnew, out, share_prefix=share,
                               long_items=long_items, graph=not args.no_graph, grow_tokens=total_steps + 1,
-                              spare_items=8 * 32 if B >= 8 else 8)
+                              spare_items=8 * 32 if B >= 8 else 8, share_width=args.share_width)
     stream = runner.stream
     runner.step()  # first step: eager launches (code objects load), the first copy-on-write; graphs captured
     torch.cuda.synchronize()
@@ -525,7 +525,8 @@ def decode_line(args, metric, B, L, ctx_before, group, prefix, long_items, share
                      "avg_launch_from": f"graph replay of the {L} layers / {L}, median of {reps}"},
         "hbm_read_probe": probe,
         "plan": {"items": int(last.n_items), "shared_items": int(last.n_shared),
-                 "kv_block_reads": int(last.kv_blocks_read), "share_prefix": share, "long_items": long_items},
+                 "kv_block_reads": int(last.kv_blocks_read), "share_prefix": share, "long_items": long_items,
+                 "share_width": args.share_width},
         "check": check,
         "cpu_baseline": cpu,
     }
@@ -987,6 +988,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle (and the output check)")
     ap.add_argument("--no-probe", action="store_true", help="skip the read-bandwidth probe")
     ap.add_argument("--no-share", action="store_true", help="plans without shared-prefix items")
+    ap.add_argument("--share-width", type=int, choices=[1, 2, 4], default=1,
+                    help="shared items span this many blocks of 16 query columns (KVP_PLAN_SHARE_WIDE2 / 4)")
     ap.add_argument("--long-items", action="store_true",
                     help="decode workload: plans with long items (KVP_PLAN_LONG_ITEMS, which sizes parts to "
                          "one generation of waves when a batch's private blocks far exceed them and leaves "

@@ -365,6 +365,15 @@ kvp_status contiguous_decode_attention(const kvp_dims *dims, void *out, const vo
  * the fp32 sums only.  The plan's split sizes also follow dims->dtype: int8 caches at head
  * dim 64 are cut into 16-block parts (32 otherwise), as in the unplanned call. */
 #define KVP_PLAN_LONG_ITEMS 2u
+/* Width of shared items, in blocks of 16 query columns (a block holds 16 / G members of G
+ * heads, G = H_q / H_kv <= 16).  By default a shared item is one block wide -- two blocks
+ * when a block holds a single member (9 <= G <= 16) -- so a prefix is read once per run of
+ * up to 16 / G members; KVP_PLAN_SHARE_WIDE2 / KVP_PLAN_SHARE_WIDE4 let one item serve 2 or
+ * 4 blocks of members (at most 2 at head dim 128) and cut it to 16 or 8 blocks of the
+ * prefix, so the prefix is read fewer times by more, shorter items.  Groups above 16 have
+ * no shared items. */
+#define KVP_PLAN_SHARE_WIDE2 4u
+#define KVP_PLAN_SHARE_WIDE4 8u
 
 typedef struct {
     int32_t B;            /* batch the plan was built for                            */
@@ -400,7 +409,8 @@ size_t decode_plan_bytes(const kvp_dims *dims, int32_t B, int32_t max_blocks, in
  * needs more items.  h_image: host buffer of image_bytes >= decode_plan_bytes(...)
  * receiving the image; the caller copies plan->bytes of it to device memory (16-byte
  * aligned) before the decode.  UNSUPPORTED for fp32 (the planned kernel serves fp16 and
- * int8 caches) or a group size above 8. */
+ * int8 caches), or a group size above 16 that is not a multiple of 16 or needs more than 4
+ * column blocks (2 at head dim 128). */
 kvp_status decode_plan_build(const kvp_dims *dims, const int32_t *h_block_table,
                              int32_t max_blocks, const int32_t *h_context_lens, int32_t B,
                              int32_t num_blocks, uint32_t flags, int32_t pad_items,

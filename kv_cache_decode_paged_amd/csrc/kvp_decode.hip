@@ -10,6 +10,7 @@
 #include <cstdlib>
 
 #include "kvp_decode_common.h"
+#include "kvp_plan_format.h"
 
 namespace kvp {
 
@@ -31,8 +32,11 @@ static kvp_status check_dims(const kvp_dims *d, const char *who)
     if (d->head_dim != D && !(d->dtype != KVP_F32 && d->head_dim == 128))
         return fail(KVP_ERR_UNSUPPORTED, "%s: head_dim=%d (64, or 128 for fp16 / int8)", who, d->head_dim);
     const int group = d->num_q_heads / d->num_kv_heads;
-    if (group > MAXG)
-        return fail(KVP_ERR_UNSUPPORTED, "%s: %d query heads per KV head (1..%d supported)", who, group, MAXG);
+    if (d->dtype == KVP_F32 && group > MAXG)
+        return fail(KVP_ERR_UNSUPPORTED, "%s: %d query heads per KV head (fp32: 1..%d supported)", who, group, MAXG);
+    if (d->dtype != KVP_F32 && !plan::group_supported(group, d->head_dim))
+        return fail(KVP_ERR_UNSUPPORTED, "%s: %d query heads per KV head (1..16, or a multiple of 16 up to %d at head "
+                    "dim %d)", who, group, 16 * plan::max_col_blocks(d->head_dim), d->head_dim);
     return KVP_OK;
 }
 
@@ -42,7 +46,9 @@ static size_t part_bytes(const kvp_dims *d, int B, int max_context)
 {
     if (d->dtype != KVP_F32) { // the fp16 kernel (fp16 or int8 caches)
         const int ipp = decode_f16_items_per_pair(max_context, d->dtype == KVP_I8, d->head_dim);
-        return ipp > 1 ? decode_f16_part_bytes((long long)B * d->num_kv_heads * ipp, d->head_dim) : 0;
+        return ipp > 1 ? decode_f16_part_bytes((long long)B * d->num_kv_heads * ipp, d->num_q_heads / d->num_kv_heads,
+                                               d->head_dim)
+                       : 0;
     }
     const int ms = decode_f32_max_splits(max_context);
     return ms > 1 ? decode_f32_part_bytes(B, d->num_q_heads, ms) : 0;
@@ -103,6 +109,7 @@ static kvp_status decode_common(const kvp_dims *dims, void *out, const void *q, 
     P.hq = dims->num_q_heads;
     P.hkv = dims->num_kv_heads;
     P.dim = dims->head_dim;
+    P.group = dims->num_q_heads / dims->num_kv_heads;
     if (scale == 0.f)
         scale = 1.0f / sqrtf((float)P.dim);
     P.scale_log2 = scale * LOG2E;
@@ -168,7 +175,7 @@ static size_t plan_workspace_bytes(const kvp_decode_plan *plan)
 {
     if (plan->n_slots <= 0)
         return 0;
-    return ticket_bytes(plan->B, plan->num_kv_heads) + decode_f16_part_bytes(plan->n_slots, plan->head_dim);
+    return ticket_bytes(plan->B, plan->num_kv_heads) + decode_f16_part_bytes(plan->n_slots, plan->group, plan->head_dim);
 }
 
 } // namespace kvp
@@ -287,6 +294,7 @@ kvp_status paged_decode_attention_planned(const kvp_cache_desc *cache, int32_t l
     P.hq = cache->dims.num_q_heads;
     P.hkv = hkv;
     P.dim = dim;
+    P.group = group;
     if (scale == 0.f)
         scale = 1.0f / sqrtf((float)dim);
     P.scale_log2 = scale * LOG2E;

@@ -19,7 +19,7 @@ namespace dec {
 constexpr int D = 64;    // head dim of the fp32 kernel (fp16: 64 or 128, a template argument)
 constexpr int BS = 16;   // tokens per block
 constexpr int TILE = 64; // tokens per tile (4 blocks)
-constexpr int MAXG = 8;  // query heads per group handled by one wave
+constexpr int MAXG = 8;  // fp32 kernel: query heads per group handled by one wave
 constexpr float LOG2E = 1.4426950408889634f;
 } // namespace dec
 
@@ -168,6 +168,7 @@ struct DecodeParams {
     int hq;
     int hkv;
     int dim;           // head dim: 64 (fp32, fp16) or 128 (fp16, int8)
+    int group;         // query heads per KV head (hq / hkv)
     int kv_i8;         // the cache holds int8 codes and fp16 row scales
     float scale_log2;
     int workers;       // fp32: max splits per pair
@@ -188,7 +189,7 @@ kvp_status launch_decode_f32(const DecodeParams &P, const PagedAddr &A, int grou
 kvp_status launch_decode_f32(const DecodeParams &P, const ContigAddr &A, int group, hipStream_t st);
 
 // workspace layout helpers (bytes), shared by the launchers and the size queries
-size_t decode_f16_part_bytes(long long slots, int dim);
+size_t decode_f16_part_bytes(long long slots, int group, int dim);
 int decode_f16_items_per_pair(int max_context, bool i8, int dim);
 size_t decode_f32_part_bytes(int B, int hq, int max_splits);
 int decode_f32_max_splits(int max_context);

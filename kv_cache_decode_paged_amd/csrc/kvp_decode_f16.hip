@@ -125,7 +125,7 @@ __device__ inline float2 coherent_load2_async(const float *p)
 // read from memory.  Lane (col, grp) holds output dims 16 db + 4 grp + i as O[4 db + i].
 // Writes the normalised row to outp (this column's HD outputs).
 template <int HD>
-__device__ __forceinline__ void merge_column(const float *part, int pbase, int np, int own, int hd, int grp,
+__device__ __forceinline__ void merge_column(const float *part, int G, int pbase, int np, int own, int hd, int grp,
                                              float om, float ol, const f32x4 (&oacc)[HD / 16], f16 *outp)
 {
     constexpr int NDB = HD / 16;
@@ -140,7 +140,7 @@ __device__ __forceinline__ void merge_column(const float *part, int pbase, int n
         for (int jj = 0; jj < 4; ++jj) {
             const int j = j0 + jj;
             if (j < np && j != own) {
-                const float *src = part + ((size_t)(pbase + j) * MAXG + hd) * part_floats(HD);
+                const float *src = part + ((size_t)(pbase + j) * G + hd) * part_floats(HD);
 #pragma unroll
                 for (int db = 0; db < NDB; ++db)
                     ov[jj][db] = coherent_load4_async(src + 16 * db + 4 * grp);
@@ -197,7 +197,7 @@ __device__ __forceinline__ void merge_column(const float *part, int pbase, int n
 // consecutive bytes.  K codes enter the score product as exact fp16 integers and each key's
 // score is multiplied by its row scale in fp32; V codes become fp16 operands code * scale,
 // rounded once.
-template <int G, bool SHARED, int NBUF, int TT, int HD, bool I8, bool LONGI, typename Addr>
+template <int NCB, bool SHARED, int NBUF, int TT, int HD, bool I8, bool LONGI, typename Addr>
 __device__ __forceinline__ void run_item(const DecodeParams &P, const Addr &A, const PlanView &PV,
                                          const Item &it, int rv, const int (&rid)[3], char *kring, char *vring,
                                          char *sring)
@@ -230,45 +230,67 @@ __device__ __forceinline__ void run_item(const DecodeParams &P, const Addr &A, c
     const char *vc = (const char *)P.vc;
     const float c = P.scale_log2;
 
-    // ---- this lane's query row: q operand, token limit, output slot ----
-    const int mem = col / G, hd = col - mem * G;
-    const bool cv = mem < it.nmem;
-    const int bm = it.b + (cv ? mem : 0);
-    f16x8 qop[KD];
-    {
-        const f16 *qp = (const f16 *)P.q + ((size_t)bm * P.hq + (size_t)it.g * G + hd) * HD + grp * 8;
+    // ---- this lane's query rows, one per column block: q operand, token limit, slots ----
+    // Group size G = Hq / Hkv.  G <= 16: column block cb holds members cb mpb .. (mpb =
+    // 16 / G members of G columns each); column col is member cb mpb + col / G, head col % G,
+    // and columns >= mpb G are unused.  G > 16 (a multiple of 16, private items only): block
+    // cb holds heads 16 (cb % bpm) .. + 15 of member cb / bpm (bpm = G / 16).
+    const int G = P.group;
+    const int mpb = G <= 16 ? 16 / G : 1;
+    const int bpm = G <= 16 ? 1 : G >> 4;
+    const int jm = G <= 16 ? col / G : 0; // member of this column within its block
+    int hdc[NCB], bm[NCB];
+    bool cv[NCB];
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) {
+        const int mem = G <= 16 ? cb * mpb + jm : cb / bpm;
+        hdc[cb] = G <= 16 ? col - jm * G : 16 * (cb % bpm) + col;
+        cv[cb] = (G > 16 || jm < mpb) && mem < it.nmem;
+        bm[cb] = it.b + (cv[cb] ? mem : 0);
+    }
+    f16x8 qop[NCB][KD];
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) {
+        const f16 *qp = (const f16 *)P.q + ((size_t)bm[cb] * P.hq + (size_t)it.g * G + hdc[cb]) * HD + grp * 8;
         const f16x8 z = {0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
         for (int ks = 0; ks < KD; ++ks) {
             const f16x8 qv = *(const f16x8 *)(qp + 32 * ks);
-            qop[ks] = cv ? qv : z;
+            qop[cb][ks] = cv[cb] ? qv : z;
         }
     }
     // lim: tokens >= lim are masked for this row; rows whose results are not kept (padding
     // columns, members that do not take part) have no limit -- their columns of the MFMA
     // tiles are independent of the others and are never stored
-    int lim, pb, np;
-    if constexpr (SHARED) {
-        // a member takes part if its shared extent reaches into this item; its part index
-        // inside the pair's slot range is the item's R_SLOT
-        const int pair = bm * hkv + it.g;
-        const int l0 = PV.req_shared[bm], b0 = PV.pair_base[pair], n0 = PV.pair_nparts[pair];
-        const bool in = cv && l0 > BS * it.blk0;
-        lim = in ? l0 : 0x7fffffff;
-        pb = b0 + it.slot;
-        np = in ? n0 : 0;
-    } else {
-        lim = cv ? it.end : 0x7fffffff;
-        pb = it.slot;
-        np = it.nparts;
+    int lim[NCB], pb[NCB], np[NCB];
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) {
+        if constexpr (SHARED) {
+            // a member takes part if its shared extent reaches into this item; its part index
+            // inside the pair's slot range is the item's R_SLOT
+            const int pair = bm[cb] * hkv + it.g;
+            const int l0 = PV.req_shared[bm[cb]], b0 = PV.pair_base[pair], n0 = PV.pair_nparts[pair];
+            const bool in = cv[cb] && l0 > BS * it.blk0;
+            lim[cb] = in ? l0 : 0x7fffffff;
+            pb[cb] = b0 + it.slot;
+            np[cb] = in ? n0 : 0;
+        } else {
+            lim[cb] = cv[cb] ? it.end : 0x7fffffff;
+            pb[cb] = it.slot;
+            np[cb] = it.nparts;
+        }
     }
     // tokens >= rend hold no data for any column of this item
     const int rend = SHARED ? BS * (it.blk0 + it.nblk) : it.end;
     // a tile ending at or before full_end needs no masking (when all its blocks are valid)
     int full_end = rend;
     if constexpr (SHARED) {
-        for (int m = 0; m < it.nmem; ++m)
-            full_end = min(full_end, lane_int(lim, m * G));
+        // member cb mpb + j's limit sits in block cb, lane j G
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb)
+            for (int j = 0; j < mpb; ++j)
+                if (cb * mpb + j < it.nmem)
+                    full_end = min(full_end, lane_int(lim[cb], j * G));
     }
 
     // the step's new K / V row (lanes 0 .. CPR-1: K chunks, CPR .. 2 CPR-1: V chunks)
@@ -354,13 +376,18 @@ __device__ __forceinline__ void run_item(const DecodeParams &P, const Addr &A, c
         }
     };
 
-    // running state of this lane's column: reference max (scaled, log2 units), output
-    // O^T rows 16 db + 4 grp + i, and the row sum (every entry of accl holds it)
-    float mref = -INFINITY;
-    f32x4 acc[NDB], accl = {0.f, 0.f, 0.f, 0.f};
+    // running state of this lane's column in each block: reference max (scaled, log2 units),
+    // output O^T rows 16 db + 4 grp + i, and the row sum (every entry of accl holds it)
+    float mref[NCB];
+    f32x4 acc[NCB][NDB], accl[NCB];
 #pragma unroll
-    for (int db = 0; db < NDB; ++db)
-        acc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int cb = 0; cb < NCB; ++cb) {
+        mref[cb] = -INFINITY;
+        accl[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+            acc[cb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
     const f16x8 ones = {1, 1, 1, 1, 1, 1, 1, 1};
 
     // fp16 cache: LDS byte addresses of this lane's operand reads in ring slot 0.  The
@@ -636,14 +663,17 @@ __device__ __forceinline__ void run_item(const DecodeParams &P, const Addr &A, c
             }
         }
 
+        // per column block: scores, softmax, values (the K and V operands serve every block)
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) {
         // scores: sacc[kb][i] = S[token of MFMA row 4 grp + i of block kb][column col] (unscaled)
         f32x4 sacc[KB];
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
-            f32x4 s = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop[kb][0], qop[0], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+            f32x4 s = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop[kb][0], qop[cb][0], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
 #pragma unroll
             for (int ks = 1; ks < KD; ++ks)
-                s = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop[kb][ks], qop[ks], s, 0, 0, 0);
+                s = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop[kb][ks], qop[cb][ks], s, 0, 0, 0);
             sacc[kb] = s;
         }
         if constexpr (I8) {
@@ -664,7 +694,7 @@ __device__ __forceinline__ void run_item(const DecodeParams &P, const Addr &A, c
                     okb = (r0 >> 4) == q ? bok[q] : okb;
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
-                    sacc[kb][i] = (okb && tb + r0 + i < lim) ? sacc[kb][i] : -INFINITY;
+                    sacc[kb][i] = (okb && tb + r0 + i < lim[cb]) ? sacc[kb][i] : -INFINITY;
             }
         }
         float mt;
@@ -683,17 +713,17 @@ __device__ __forceinline__ void run_item(const DecodeParams &P, const Addr &A, c
         // than 2^8: between moves p = 2^(s c - mref) stays below 256, exact in fp16 range, and
         // the output and row sum need no rescaling.  Columns that do not move scale by exactly
         // 1, so no query row depends on another's keys.
-        const bool need = mt > mref + RESCALE_LOG2;
+        const bool need = mt > mref[cb] + RESCALE_LOG2;
         if (__ballot(need) != 0) {
-            const float mn = need ? mt : mref;
-            const float alpha = need ? (mref == -INFINITY ? 0.f : fast_exp2(mref - mn)) : 1.f;
+            const float mn = need ? mt : mref[cb];
+            const float alpha = need ? (mref[cb] == -INFINITY ? 0.f : fast_exp2(mref[cb] - mn)) : 1.f;
 #pragma unroll
             for (int db = 0; db < NDB; ++db)
-                acc[db] *= alpha;
-            accl *= alpha;
-            mref = mn;
+                acc[cb][db] *= alpha;
+            accl[cb] *= alpha;
+            mref[cb] = mn;
         }
-        const float mc = mref == -INFINITY ? 0.f : mref;
+        const float mc = mref[cb] == -INFINITY ? 0.f : mref[cb];
         // P^T operand of k-step ks, slot s = sacc[2 ks + s / 4][s % 4] -- already in this lane
         // (tile row 16 (2 ks + s / 4) + 4 grp + s % 4 for an fp16 cache, 32 ks + 8 grp + s for
         // int8); rounded once to fp16
@@ -712,9 +742,10 @@ __device__ __forceinline__ void run_item(const DecodeParams &P, const Addr &A, c
         for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
             for (int db = 0; db < NDB; ++db)
-                acc[db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vop[ks][db], pop[ks], acc[db], 0, 0, 0);
-            accl = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, pop[ks], accl, 0, 0, 0);
+                acc[cb][db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vop[ks][db], pop[ks], acc[cb][db], 0, 0, 0);
+            accl[cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, pop[ks], accl[cb], 0, 0, 0);
         }
+        } // column blocks
         wait_lds(); // this slot is refilled by a later DMA
         wave_lds_sync();
     };
@@ -747,36 +778,40 @@ __device__ __forceinline__ void run_item(const DecodeParams &P, const Addr &A, c
     // slot instead waits (bounded) for the others' count and merges without storing its
     // own.  Every merge goes through merge_column, so the result does not depend on which
     // item merges.
-    const float lsum = accl[0];
-    f16 *outp = (f16 *)P.out + ((size_t)bm * P.hq + (size_t)it.g * G + hd) * HD;
-    if (cv && np == 1) {
-        const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+    f16 *outp[NCB];
+    bool split_col[NCB];
+    bool any_split = false;
 #pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-            const f16x4 o = {(f16)(acc[db][0] * inv), (f16)(acc[db][1] * inv), (f16)(acc[db][2] * inv),
-                             (f16)(acc[db][3] * inv)};
-            *(f16x4 *)(outp + 16 * db + 4 * grp) = o;
+    for (int cb = 0; cb < NCB; ++cb) {
+        outp[cb] = (f16 *)P.out + ((size_t)bm[cb] * P.hq + (size_t)it.g * G + hdc[cb]) * HD;
+        if (cv[cb] && np[cb] == 1) {
+            const float lsum = accl[cb][0];
+            const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) {
+                const f16x4 o = {(f16)(acc[cb][db][0] * inv), (f16)(acc[cb][db][1] * inv),
+                                 (f16)(acc[cb][db][2] * inv), (f16)(acc[cb][db][3] * inv)};
+                *(f16x4 *)(outp[cb] + 16 * db + 4 * grp) = o;
+            }
         }
+        split_col[cb] = cv[cb] && np[cb] > 1;
+        any_split = any_split || split_col[cb];
     }
-    const bool split_col = cv && np > 1;
-    if (__ballot(split_col) == 0)
+    if (__ballot(any_split) == 0)
         return;
-    // this column's pair: first slot and this item's part index in it
-    int pbase, own;
-    if constexpr (SHARED) {
-        pbase = PV.pair_base[bm * hkv + it.g];
-        own = it.slot;
-    } else {
-        pbase = it.pbase;
-        own = it.slot - it.pbase;
-    }
+    // each column's pair: first slot and this item's part index in it
+    int pbase[NCB], own;
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb)
+        pbase[cb] = SHARED ? PV.pair_base[bm[cb] * hkv + it.g] : it.pbase;
+    own = SHARED ? it.slot : it.slot - it.pbase;
     if constexpr (!SHARED) {
-        if (P.merge_polls > 0 && own == np - 1) {
+        if (P.merge_polls > 0 && own == np[0] - 1) {
             const int pair = it.b * hkv + it.g;
             int ready = 0;
             if (lane == 0) {
                 for (int k = 0; k < P.merge_polls; ++k) {
-                    if (coherent_load_int(&P.tickets[pair]) >= np - 1) {
+                    if (coherent_load_int(&P.tickets[pair]) >= np[0] - 1) {
                         ready = 1;
                         break;
                     }
@@ -784,42 +819,92 @@ __device__ __forceinline__ void run_item(const DecodeParams &P, const Addr &A, c
                 }
             }
             if (__builtin_amdgcn_readfirstlane(ready)) {
-                if (cv)
-                    merge_column<HD>(P.part, pbase, np, own, hd, grp, mref, lsum, acc, outp);
+#pragma unroll
+                for (int cb = 0; cb < NCB; ++cb)
+                    if (cv[cb])
+                        merge_column<HD>(P.part, G, pbase[cb], np[cb], own, hdc[cb], grp, mref[cb], accl[cb][0],
+                                         acc[cb], outp[cb]);
                 if (lane == 0)
                     reset_ticket(&P.tickets[pair]);
                 return;
             }
         }
     }
-    if (split_col) {
-        float *dst = P.part + ((size_t)pb * MAXG + hd) * part_floats(HD);
 #pragma unroll
-        for (int db = 0; db < NDB; ++db)
-            coherent_store4(dst + 16 * db + 4 * grp, acc[db]);
-        if (grp == 0)
-            coherent_store2(dst + HD, mref, lsum);
+    for (int cb = 0; cb < NCB; ++cb) {
+        if (split_col[cb]) {
+            float *dst = P.part + ((size_t)pb[cb] * G + hdc[cb]) * part_floats(HD);
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+                coherent_store4(dst + 16 * db + 4 * grp, acc[cb][db]);
+            if (grp == 0)
+                coherent_store2(dst + HD, mref[cb], accl[cb][0]);
+        }
     }
     wait_stores(); // every partial store has completed before a ticket publishes it
-    // one ticket per member pair, taken by the lane of the member's first column
-    int tk = -1;
-    if (split_col && hd == 0 && grp == 0)
-        tk = take_ticket(&P.tickets[bm * hkv + it.g]);
-    tk = __shfl(tk, mem * G, 64);
-    const bool last = split_col && tk == np - 1;
-    if (__ballot(last) == 0)
+    // one ticket per member pair, taken by the lane of the member's first column (G <= 16:
+    // head 0 of the member in its block; G > 16: the item's single member, block 0, lane 0)
+    int tk[NCB];
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) {
+        int t = -1;
+        const bool first = G <= 16 ? hdc[cb] == 0 : (cb == 0 && col == 0);
+        if (split_col[cb] && first && grp == 0)
+            t = take_ticket(&P.tickets[bm[cb] * hkv + it.g]);
+        tk[cb] = t;
+    }
+    bool last[NCB];
+    bool any_last = false;
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) {
+        const int t = G <= 16 ? __shfl(tk[cb], jm * G, 64) : __builtin_amdgcn_readfirstlane(tk[0]);
+        last[cb] = split_col[cb] && t == np[cb] - 1;
+        any_last = any_last || last[cb];
+    }
+    if (__ballot(any_last) == 0)
         return;
-    if (last) {
-        merge_column<HD>(P.part, pbase, np, own, hd, grp, mref, lsum, acc, outp);
-        if (hd == 0 && grp == 0)
-            reset_ticket(&P.tickets[bm * hkv + it.g]);
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) {
+        if (last[cb]) {
+            merge_column<HD>(P.part, G, pbase[cb], np[cb], own, hdc[cb], grp, mref[cb], accl[cb][0], acc[cb],
+                             outp[cb]);
+            const bool first = G <= 16 ? hdc[cb] == 0 : (cb == 0 && col == 0);
+            if (first && grp == 0)
+                reset_ticket(&P.tickets[bm[cb] * hkv + it.g]);
+        }
     }
 }
 
-template <int G, int NBUF, int TT, int HD, bool I8, bool PLANNED, typename Addr>
+// Private items of a pair take G / 16 column blocks when G > 16 (else one); shared items
+// take ceil(members / (16 / G)) blocks, rounded up to 1, 2 or 4.  At most 4 blocks at head
+// dim 64 and 2 at 128 (the accumulators of 4 blocks of 128 dims would not fit the VGPRs).
+template <int NCB, int NBUF, int TT, int HD, bool I8, bool LONGI, typename Addr>
+__device__ __forceinline__ void run_private(const DecodeParams &P, const Addr &A, const PlanView &PV,
+                                            const Item &it, int rv, const int (&rid)[3], char *kring, char *vring,
+                                            char *sring)
+{
+    run_item<NCB, false, NBUF, TT, HD, I8, LONGI>(P, A, PV, it, rv, rid, kring, vring, sring);
+}
+
+template <int NBUF, int TT, int HD, bool I8, bool LONGI, typename Addr>
+__device__ __forceinline__ void dispatch_private(const DecodeParams &P, const Addr &A, const PlanView &PV,
+                                                 const Item &it, int rv, const int (&rid)[3], char *kring,
+                                                 char *vring, char *sring)
+{
+    const int bpm = P.group <= 16 ? 1 : P.group >> 4;
+    if (bpm == 1)
+        run_private<1, NBUF, TT, HD, I8, LONGI>(P, A, PV, it, rv, rid, kring, vring, sring);
+    else if (bpm == 2)
+        run_private<2, NBUF, TT, HD, I8, LONGI>(P, A, PV, it, rv, rid, kring, vring, sring);
+    else if constexpr (HD == 64) {
+        if (bpm == 4)
+            run_private<4, NBUF, TT, HD, I8, LONGI>(P, A, PV, it, rv, rid, kring, vring, sring);
+    }
+}
+
+template <int NBUF, int TT, int HD, bool I8, bool PLANNED, typename Addr>
 __global__ __launch_bounds__(64) void decode_f16_kernel(DecodeParams P, Addr A, PlanView PV)
 {
-    static_assert(G >= 1 && G <= MAXG, "group size");
     static_assert(NBUF >= 2 && NBUF <= 4, "ring depth");
     constexpr int EB = I8 ? 1 : 2; // bytes per cached value
     __shared__ __attribute__((aligned(16))) char kring[NBUF * TT * EB * HD];
@@ -850,11 +935,19 @@ __global__ __launch_bounds__(64) void decode_f16_kernel(DecodeParams P, Addr A, 
         if (flags & F_EMPTY)
             return;
         if (flags & F_SHARED) {
-            if (it.nmem * G > 16 || it.slot < 0)
+            const int G = P.group;
+            if (G > 16 || it.slot < 0 || longi)
                 return;
-            if (longi)
-                return;
-            run_item<G, true, NBUF, TT, HD, I8, false>(P, A, PV, it, rv, {-1, -1, -1}, kring, vring, sring);
+            const int mpb = 16 / G;
+            const int ncb = (it.nmem + mpb - 1) / mpb;
+            if (ncb <= 1)
+                run_item<1, true, NBUF, TT, HD, I8, false>(P, A, PV, it, rv, {-1, -1, -1}, kring, vring, sring);
+            else if (ncb <= 2)
+                run_item<2, true, NBUF, TT, HD, I8, false>(P, A, PV, it, rv, {-1, -1, -1}, kring, vring, sring);
+            else if constexpr (HD == 64) {
+                if (ncb <= 4)
+                    run_item<4, true, NBUF, TT, HD, I8, false>(P, A, PV, it, rv, {-1, -1, -1}, kring, vring, sring);
+            }
             return;
         }
         if (it.nmem != 1)
@@ -872,9 +965,9 @@ __global__ __launch_bounds__(64) void decode_f16_kernel(DecodeParams P, Addr A, 
                     rid[k] = PV.ids[off + 64 * k + lane];
         }
         if (longi)
-            run_item<G, false, NBUF, TT, HD, I8, true>(P, A, PV, it, rv, rid, kring, vring, sring);
+            dispatch_private<NBUF, TT, HD, I8, true>(P, A, PV, it, rv, rid, kring, vring, sring);
         else
-            run_item<G, false, NBUF, TT, HD, I8, false>(P, A, PV, it, rv, rid, kring, vring, sring);
+            dispatch_private<NBUF, TT, HD, I8, false>(P, A, PV, it, rv, rid, kring, vring, sring);
     } else {
         const int pair = blockIdx.x / PV.ipp;
         const int k = blockIdx.x - pair * PV.ipp;
@@ -899,53 +992,42 @@ __global__ __launch_bounds__(64) void decode_f16_kernel(DecodeParams P, Addr A, 
         it.slot = it.pbase + k;
         const int j = lane - R_ENT;
         rv = (j >= 0 && j < it.nblk) ? A.entry(it.b, it.blk0 + j) : -1;
-        run_item<G, false, NBUF, TT, HD, I8, false>(P, A, PV, it, rv, {-1, -1, -1}, kring, vring, sring);
+        dispatch_private<NBUF, TT, HD, I8, false>(P, A, PV, it, rv, {-1, -1, -1}, kring, vring, sring);
     }
 }
 
 // ---------------------------------------------------------------------------------------
 template <bool PLANNED, typename Addr>
-static kvp_status launch_f16(const DecodeParams &P, const Addr &A, const PlanView &PV, int group,
-                             long long grid, hipStream_t st)
+static kvp_status launch_f16(const DecodeParams &P, const Addr &A, const PlanView &PV, long long grid,
+                             hipStream_t st)
 {
     if (grid <= 0)
         return KVP_OK;
     if (grid > 0x7fffffffLL)
         return fail(KVP_ERR_UNSUPPORTED, "decode: %lld work items", grid);
     dim3 g((unsigned)grid), block(64);
-    if (group < 1 || group > MAXG)
-        return fail(KVP_ERR_UNSUPPORTED, "decode: %d query heads per KV head (1..8 supported)", group);
     if (P.dim != 64 && P.dim != 128)
         return fail(KVP_ERR_UNSUPPORTED, "decode: head_dim=%d (64 or 128)", P.dim);
+    if (!group_supported(P.group, P.dim))
+        return fail(KVP_ERR_UNSUPPORTED, "decode: %d query heads per KV head (1..16, or a multiple of 16 up to %d "
+                    "at head dim %d)", P.group, P.dim == 64 ? 64 : 32, P.dim);
     // head_dim 64: 64-token tiles; 128: 32-token tiles (the same 32 KB of LDS for the rings)
     if (P.kv_i8) {
         if constexpr (Addr::paged) {
-            switch (group * 1000 + P.dim) {
-#define KVP_G(GG)                                                                                  \
-    case GG * 1000 + 64:                                                                           \
-        hipLaunchKernelGGL((decode_f16_kernel<GG, DEC_NBUF, DEC_TT, 64, true, PLANNED, Addr>), g, block, 0, st, P, A, PV); \
-        break;                                                                                     \
-    case GG * 1000 + 128:                                                                          \
-        hipLaunchKernelGGL((decode_f16_kernel<GG, 2, 32, 128, true, PLANNED, Addr>), g, block, 0, st, P, A, PV); \
-        break;
-                KVP_G(1) KVP_G(2) KVP_G(3) KVP_G(4) KVP_G(5) KVP_G(6) KVP_G(7) KVP_G(8)
-#undef KVP_G
-            }
+            if (P.dim == 64)
+                hipLaunchKernelGGL((decode_f16_kernel<DEC_NBUF, DEC_TT, 64, true, PLANNED, Addr>), g, block, 0, st, P,
+                                   A, PV);
+            else
+                hipLaunchKernelGGL((decode_f16_kernel<2, 32, 128, true, PLANNED, Addr>), g, block, 0, st, P, A, PV);
         } else {
             return fail(KVP_ERR_UNSUPPORTED, "decode: int8 caches are paged only");
         }
     } else {
-        switch (group * 1000 + P.dim) {
-#define KVP_G(GG)                                                                                  \
-    case GG * 1000 + 64:                                                                           \
-        hipLaunchKernelGGL((decode_f16_kernel<GG, DEC_NBUF, DEC_TT, 64, false, PLANNED, Addr>), g, block, 0, st, P, A, PV); \
-        break;                                                                                     \
-    case GG * 1000 + 128:                                                                          \
-        hipLaunchKernelGGL((decode_f16_kernel<GG, 2, 32, 128, false, PLANNED, Addr>), g, block, 0, st, P, A, PV); \
-        break;
-            KVP_G(1) KVP_G(2) KVP_G(3) KVP_G(4) KVP_G(5) KVP_G(6) KVP_G(7) KVP_G(8)
-#undef KVP_G
-        }
+        if (P.dim == 64)
+            hipLaunchKernelGGL((decode_f16_kernel<DEC_NBUF, DEC_TT, 64, false, PLANNED, Addr>), g, block, 0, st, P, A,
+                               PV);
+        else
+            hipLaunchKernelGGL((decode_f16_kernel<2, 32, 128, false, PLANNED, Addr>), g, block, 0, st, P, A, PV);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
@@ -959,9 +1041,9 @@ int decode_f16_items_per_pair(int max_context, bool i8, int dim)
     return nb <= unsplit_blocks(i8, dim) ? 1 : (nb + split_blocks(i8, dim) - 1) / split_blocks(i8, dim);
 }
 
-size_t decode_f16_part_bytes(long long slots, int dim)
+size_t decode_f16_part_bytes(long long slots, int group, int dim)
 {
-    return (size_t)slots * MAXG * part_floats(dim) * sizeof(float);
+    return (size_t)slots * group * part_floats(dim) * sizeof(float);
 }
 
 kvp_status launch_decode_f16(const DecodeParams &P, const PagedAddr &A, int group, int max_context,
@@ -969,14 +1051,14 @@ kvp_status launch_decode_f16(const DecodeParams &P, const PagedAddr &A, int grou
 {
     PlanView PV{nullptr, nullptr, nullptr, nullptr, decode_f16_items_per_pair(max_context, P.kv_i8 != 0, P.dim), nullptr,
                 0};
-    return launch_f16<false>(P, A, PV, group, (long long)P.B * P.hkv * PV.ipp, st);
+    return launch_f16<false>(P, A, PV, (long long)P.B * P.hkv * PV.ipp, st);
 }
 kvp_status launch_decode_f16(const DecodeParams &P, const ContigAddr &A, int group, int max_context,
                              hipStream_t st)
 {
     PlanView PV{nullptr, nullptr, nullptr, nullptr, decode_f16_items_per_pair(max_context, P.kv_i8 != 0, P.dim), nullptr,
                 0};
-    return launch_f16<false>(P, A, PV, group, (long long)P.B * P.hkv * PV.ipp, st);
+    return launch_f16<false>(P, A, PV, (long long)P.B * P.hkv * PV.ipp, st);
 }
 kvp_status launch_decode_f16_planned(const DecodeParams &P, const PagedAddr &A, int group,
                                      const void *d_image, const kvp_decode_plan &plan, hipStream_t st)
@@ -985,7 +1067,7 @@ kvp_status launch_decode_f16_planned(const DecodeParams &P, const PagedAddr &A, 
     PlanView PV{(const int *)img, (const int *)(img + plan.off_pair_base),
                 (const int *)(img + plan.off_pair_nparts), (const int *)(img + plan.off_req_shared), 0,
                 (const int *)(img + plan.off_ids), plan.n_ids};
-    return launch_f16<true>(P, A, PV, group, plan.n_items, st);
+    return launch_f16<true>(P, A, PV, plan.n_items, st);
 }
 
 } // namespace kvp

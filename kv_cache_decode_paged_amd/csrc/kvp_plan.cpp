@@ -35,9 +35,9 @@ kvp_status check_plan_dims(const kvp_dims *d, const char *who)
     if (d->dtype != KVP_F16 && d->dtype != KVP_I8)
         return fail(d->dtype == KVP_F32 ? KVP_ERR_UNSUPPORTED : KVP_ERR_INVALID,
                     "%s: planned decode is implemented for fp16 and int8 (dtype=%d)", who, d->dtype);
-    if (d->num_q_heads / d->num_kv_heads > 8)
-        return fail(KVP_ERR_UNSUPPORTED, "%s: %d query heads per KV head (1..8 supported)", who,
-                    d->num_q_heads / d->num_kv_heads);
+    if (!group_supported(d->num_q_heads / d->num_kv_heads, d->head_dim))
+        return fail(KVP_ERR_UNSUPPORTED, "%s: %d query heads per KV head (1..16, or a multiple of 16 up to %d at head "
+                    "dim %d)", who, d->num_q_heads / d->num_kv_heads, 16 * max_col_blocks(d->head_dim), d->head_dim);
     return KVP_OK;
 }
 
@@ -47,9 +47,11 @@ constexpr int MAX_BUNDLE = 8; // shared items kept together on one XCD
 long long max_items(long long B, long long hkv, long long max_blocks, bool i8, int hd)
 {
     const long long ipp = std::max<long long>(1, (max_blocks + split_blocks(i8, hd) - 1) / split_blocks(i8, hd));
-    // private items: at most ipp per pair; shared items: at most one set per two requests;
-    // plus the padding that evens out the XCD queues and rounds them to whole CU rounds
-    const long long work = B * hkv * ipp + (B / 2) * hkv * ipp;
+    // private items: at most ipp per pair; shared items: a sub-run of n >= 2 members has at
+    // most 4 ipp parts when it takes 4 column blocks (then n >= 3), 2 ipp with 2 blocks and
+    // ipp with one, so fewer than 2 ipp per request; plus the padding that evens out the XCD
+    // queues and rounds them to whole CU rounds
+    const long long work = B * hkv * ipp + 2 * B * hkv * ipp;
     return XCDS * ((work + XCDS - 1) / XCDS + MAX_BUNDLE + CU_SLOTS - 1);
 }
 
@@ -79,6 +81,19 @@ struct SubRun {
     int a, n, shared_tokens, run;
 };
 
+// Parts of a shared range of nsb blocks read for n members at group size G: an item scores
+// each tile against ncb blocks of 16 query columns (ncb = 1, 2 or 4), so its work per tile
+// grows with ncb; its length is cut to BPI / ncb blocks to keep items of equal work.
+int shared_split(int nsb, int n, int G, int hd)
+{
+    const int mpb = G <= 16 ? 16 / G : 1;
+    int ncb = (n + mpb - 1) / mpb;
+    ncb = ncb <= 1 ? 1 : (ncb <= 2 ? 2 : 4);
+    ncb = std::min(ncb, max_col_blocks(hd));
+    const int len = BPI / ncb;
+    return nsb <= 0 ? 1 : (nsb + len - 1) / len;
+}
+
 } // namespace
 
 extern "C" {
@@ -106,8 +121,11 @@ kvp_status decode_plan_build(const kvp_dims *dims, const int32_t *table, int32_t
         return fail(KVP_ERR_INVALID, "%s: B=%d max_blocks=%d num_blocks=%d", who, B, max_blocks, num_blocks);
     if (!plan || !h_image || (B > 0 && (!table || !ctx_lens)))
         return fail(KVP_ERR_INVALID, "%s: NULL pointer argument", who);
-    if (flags & ~(KVP_PLAN_SHARE_PREFIX | KVP_PLAN_LONG_ITEMS))
+    if (flags & ~(KVP_PLAN_SHARE_PREFIX | KVP_PLAN_LONG_ITEMS | KVP_PLAN_SHARE_WIDE2 | KVP_PLAN_SHARE_WIDE4))
         return fail(KVP_ERR_INVALID, "%s: unknown flags 0x%x", who, flags);
+    if ((flags & KVP_PLAN_SHARE_WIDE2) && (flags & KVP_PLAN_SHARE_WIDE4))
+        return fail(KVP_ERR_INVALID, "%s: KVP_PLAN_SHARE_WIDE2 and KVP_PLAN_SHARE_WIDE4 together", who);
+    const int width = (flags & KVP_PLAN_SHARE_WIDE4) ? 4 : (flags & KVP_PLAN_SHARE_WIDE2) ? 2 : 1;
     if (pad_items < 0)
         return fail(KVP_ERR_INVALID, "%s: pad_items=%d", who, pad_items);
     if ((long long)max_blocks * BS > 0x7fffffffLL)
@@ -116,7 +134,7 @@ kvp_status decode_plan_build(const kvp_dims *dims, const int32_t *table, int32_t
     const bool i8 = dims->dtype == KVP_I8; // the int8 kernel's split sizes
     const int hd = dims->head_dim;
     const int G = dims->num_q_heads / hkv;
-    const int maxm = std::max(1, std::min(MAXM, 16 / G)); // members of a shared item (<= 16 rows)
+    const int maxm = shared_members(G, hd, width); // members of a shared item (1: no sharing)
     const long long npairs = (long long)B * hkv;
 
     std::vector<int> c(B), nbt(B), E(B, 0);
@@ -173,7 +191,7 @@ kvp_status decode_plan_build(const kvp_dims *dims, const int32_t *table, int32_t
     std::vector<int> shared_parts(B, 0);
     for (const SubRun &sr : subs) {
         const int nsb = sr.shared_tokens / BS;
-        const int ns = split_parts(nsb, true, i8, hd);
+        const int ns = shared_split(nsb, sr.n, G, hd);
         for (int m = sr.a; m < sr.a + sr.n; ++m)
             for (int k = 0; k < ns; ++k)
                 if (BS * split_start(nsb, ns, k) < E[m])
@@ -211,7 +229,7 @@ kvp_status decode_plan_build(const kvp_dims *dims, const int32_t *table, int32_t
         }
     long long n_shared = 0;
     for (const SubRun &s : subs)
-        n_shared += (long long)hkv * split_parts(s.shared_tokens / BS, true, i8, hd);
+        n_shared += (long long)hkv * shared_split(s.shared_tokens / BS, s.n, G, hd);
     n_items += n_shared;
     if (slots > 0x7fffffffLL || n_items > 0x7fffffffLL)
         return fail(KVP_ERR_UNSUPPORTED, "%s: plan too large", who);
@@ -257,7 +275,7 @@ kvp_status decode_plan_build(const kvp_dims *dims, const int32_t *table, int32_t
         std::vector<std::pair<long long, long long>> keyed; // (run * hkv + g, item)
         for (const SubRun &sr : subs) {
             const int nsb = sr.shared_tokens / BS;
-            const int ns = split_parts(nsb, true, i8, hd);
+            const int ns = shared_split(nsb, sr.n, G, hd);
             for (int g = 0; g < hkv; ++g)
                 for (int k = 0; k < ns; ++k) {
                     const int b0 = split_start(nsb, ns, k), b1 = split_start(nsb, ns, k + 1);

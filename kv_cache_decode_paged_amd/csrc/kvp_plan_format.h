@@ -64,7 +64,29 @@ constexpr int LONG_BPI = 192; // blocks of a long item (three ids per lane)
 // workgroups per CU, eight of the int8 kernel's 18 KB, on 256 CUs
 constexpr int LONG_TARGET_WAVES_F16 = 1024;
 constexpr int LONG_TARGET_WAVES_I8 = 2048;
-constexpr int MAXM = 16; // members of one shared item (and at most 16 query rows)
+constexpr int MAXM = 16; // members of one shared item
+// Query columns of an item: blocks of 16 MFMA columns, at most 4 per item at head dim 64 and
+// 2 at 128.  Group size G = Hq / Hkv: up to 16 (a block holds 16 / G members of G heads; a
+// shared item serves up to 16 / G members per block), or a multiple of 16 (a private item
+// of one request takes G / 16 blocks; no shared items).
+constexpr int max_col_blocks(int hd) { return hd == 64 ? 4 : 2; }
+constexpr bool group_supported(int G, int hd)
+{
+    return (G >= 1 && G <= 16) || (G % 16 == 0 && G / 16 <= max_col_blocks(hd));
+}
+// column blocks of a shared item: the plan's width (1, 2 or 4), at least 2 when a block
+// holds a single member, at most max_col_blocks(hd)
+constexpr int shared_col_blocks(int G, int hd, int width)
+{
+    const int w = G > 8 && width < 2 ? 2 : width;
+    return w < max_col_blocks(hd) ? w : max_col_blocks(hd);
+}
+// members of one shared item at group size G (1: no shared items)
+constexpr int shared_members(int G, int hd, int width)
+{
+    return G > 16 ? 1 : (16 / G * shared_col_blocks(G, hd, width) < MAXM ? 16 / G * shared_col_blocks(G, hd, width)
+                                                                        : MAXM);
+}
 constexpr int XCDS = 8;  // MI355X: workgroup i runs on XCD i % 8 (round-robin dispatch)
 // CUs per XCD: within an XCD, the dispatcher deals the queue positions of one launch
 // round-robin over its CUs, so positions p and p + CU_SLOTS of an XCD queue share a CU

@@ -53,7 +53,8 @@ class DecodeStepRunner:
     """
 
     def __init__(self, cache: PagedKVCache, pool: BlockPool, seqs, max_blocks, q, k_new, v_new, out,
-                 share_prefix=True, long_items=False, graph=True, spare_items=SPARE_ITEMS, grow_tokens=64):
+                 share_prefix=True, long_items=False, graph=True, spare_items=SPARE_ITEMS, grow_tokens=64,
+                 share_width=1):
         L, B = q.shape[0], q.shape[1]
         hq, hkv, d = cache.num_q_heads, cache.num_kv_heads, cache.head_dim
         if q.shape != (L, B, hq, d) or out.shape != q.shape:
@@ -67,6 +68,7 @@ class DecodeStepRunner:
         self.max_blocks = int(max_blocks)
         self.q, self.k_new, self.v_new, self.out = q, k_new, v_new, out
         self.share, self.long_items, self.use_graph = share_prefix, long_items, graph
+        self.share_width = share_width
         self.spare, self.grow = int(spare_items), int(grow_tokens)
         self.ids = torch.tensor([int(s) for s in seqs], dtype=torch.int32)
         self.cows = (kvp_copy * B)()
@@ -87,7 +89,8 @@ class DecodeStepRunner:
         table width), plus the spare items."""
         c1 = torch.clamp(ctx + 1 + self.grow, max=self.max_blocks * BLOCK)
         plan0, _ = decode_plan_build(self.hq, self.hkv, table, c1, self.cache.num_blocks, share_prefix=self.share,
-                                     head_dim=self.d, long_items=self.long_items, kv_dtype=self.cache.dtype)
+                                     head_dim=self.d, long_items=self.long_items, kv_dtype=self.cache.dtype,
+                                     share_width=self.share_width)
         pad = plan0.n_items + self.spare
         img_bytes = decode_plan_bytes(self.hq, self.hkv, self.B, self.max_blocks, pad, head_dim=self.d,
                                       kv_dtype=self.cache.dtype)
@@ -107,6 +110,7 @@ class DecodeStepRunner:
         self.layout = dict(pad=pad, img_bytes=img_bytes, slot_cap=slot_cap, launch=None)
         ws_plan = kvp_decode_plan()
         ws_plan.B, ws_plan.num_kv_heads, ws_plan.n_slots, ws_plan.head_dim = self.B, self.hkv, slot_cap, self.d
+        ws_plan.group = self.hq // self.hkv
         self.workspace = torch.zeros((max(decode_plan_workspace_bytes(ws_plan), 256),), dtype=torch.uint8,
                                      device=self.dev)
         self.graphs = [None, None]
@@ -161,7 +165,8 @@ class DecodeStepRunner:
         lay = self.layout
         plan, _ = decode_plan_build(self.hq, self.hkv, h["table"], h["ctx"], self.cache.num_blocks,
                                     share_prefix=self.share, image=h["image"], pad_items=lay["pad"], plan=h["plan"],
-                                    head_dim=self.d, long_items=self.long_items, kv_dtype=self.cache.dtype)
+                                    head_dim=self.d, long_items=self.long_items, kv_dtype=self.cache.dtype,
+                                    share_width=self.share_width)
         if lay["launch"] is None:
             # launch arguments shared by every step of this layout: the plan's offsets, the
             # workspace's slot capacity and the whole id area of the buffer

@@ -89,14 +89,20 @@ def test_device_calls_reject_bad_arguments_before_launch():
 def test_workspace_size():
     import kv_cache_decode_paged_amd as kvp
     # fp16: a pair longer than 32 blocks is cut into ceil(blocks / 32) parts, one partial per
-    # part (8 head slots x 68 floats) + one ticket per pair; 32768 tokens = 2048 blocks -> 64
+    # part (one 68-float record per query head of the group: 7 here) + one ticket per pair;
+    # 32768 tokens = 2048 blocks -> 64
     ws = kvp.decode_workspace_bytes(14, 2, torch.float16, 32, 32768)
-    assert ws == 32 * 2 * 64 * 8 * 68 * 4 + 256
+    assert ws == 32 * 2 * 64 * 7 * 68 * 4 + 256
     # contexts of at most 512 tokens are never split: no workspace
     assert kvp.decode_workspace_bytes(14, 2, torch.float16, 200, 512) == 0
-    assert kvp.decode_workspace_bytes(14, 2, torch.float16, 200, 513) == 1792 + 200 * 2 * 2 * 8 * 68 * 4
-    # head_dim 128: 132-float partial records
-    assert kvp.decode_workspace_bytes(32, 8, torch.float16, 4, 4096, head_dim=128) == 256 + 4 * 8 * 8 * 8 * 132 * 4
+    assert kvp.decode_workspace_bytes(14, 2, torch.float16, 200, 513) == 1792 + 200 * 2 * 2 * 7 * 68 * 4
+    # head_dim 128: 132-float partial records (group 4)
+    assert kvp.decode_workspace_bytes(32, 8, torch.float16, 4, 4096, head_dim=128) == 256 + 4 * 8 * 8 * 4 * 132 * 4
+    # multi-query: 14 and 32 query heads on one KV head
+    assert kvp.decode_workspace_bytes(14, 1, torch.float16, 2, 1024) == 256 + 2 * 1 * 2 * 14 * 68 * 4
+    assert kvp.decode_workspace_bytes(32, 1, torch.float16, 2, 1024, head_dim=128) == 256 + 2 * 1 * 2 * 32 * 132 * 4
+    # groups above 16 that are not a multiple of 16 are refused (no workspace)
+    assert kvp.decode_workspace_bytes(20, 1, torch.float16, 2, 1024) == 0
     # fp32 single head, short context: one split, no workspace needed
     assert kvp.decode_workspace_bytes(1, 1, torch.float32, 1, 88) == 0
     # 5000 tokens: at most 16 splits (256-token splits up to 4096 tokens, 512 beyond)

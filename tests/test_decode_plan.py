@@ -6,7 +6,8 @@ plan must guarantee, read independently from the image:
   member's block, which must be the same physical block);
 * a pair split into several parts has slots pbase .. pbase+nparts-1, each written once,
   in token order (the merge order), and single-part pairs are written directly;
-* shared items hold at most 16 query rows and a prefix's items run on one XCD;
+* shared items hold at most 16 / G members per block of 16 query columns (1, 2 or 4 blocks)
+  and a prefix's items run on one XCD;
 * each XCD's items are spread over its 32 CUs (queue indices 32 apart share a CU) so that
   no CU carries more than its share of the work plus one item;
 * without prefix sharing the plan is exactly the per-pair split (one item up to 32 blocks,
@@ -84,7 +85,9 @@ def check_plan(plan, image, table, ctx, num_blocks, hq, hkv, shared_expected=Non
                 want = ent(b, blk0 + j) if j < nblk else -1
                 assert int(r[R_ENT + j]) == want, (p, j)
         if fl == F_SHARED:
-            assert nmem * G <= 16 and slot >= 0
+            # a shared item serves at most 16 / G members per block of 16 query columns, 4
+            # blocks at head dim 64 (2 at 128); groups above 16 have no shared items
+            assert G <= 16 and nmem <= min(16, (16 // G) * (4 if plan.head_dim == 64 else 2)) and slot >= 0
             key = (run_of[b], g)  # one sharing run and KV head
             xs, n = bundles.get(key, (set(), 0))
             bundles[key] = (xs | {p % XCDS}, n + 1)
@@ -141,10 +144,11 @@ def check_plan(plan, image, table, ctx, num_blocks, hq, hkv, shared_expected=Non
     return items, pbase, nparts, req_shared
 
 
-def build(table, ctx, num_blocks, hq=14, hkv=2, share=True, long_items=False):
+def build(table, ctx, num_blocks, hq=14, hkv=2, share=True, long_items=False, share_width=1):
     t = torch.from_numpy(np.ascontiguousarray(table, dtype=np.int32))
     c = torch.from_numpy(np.ascontiguousarray(ctx, dtype=np.int32))
-    return kvp.decode_plan_build(hq, hkv, t, c, num_blocks, share_prefix=share, long_items=long_items)
+    return kvp.decode_plan_build(hq, hkv, t, c, num_blocks, share_prefix=share, long_items=long_items,
+                                 share_width=share_width)
 
 
 def c4_tables(B, steps_done=1, seed=42):
@@ -177,6 +181,10 @@ def test_plan_shared_prefix_workload(B):
     table, ctx, nb, _, _ = c4_tables(B)
     plan, image = build(table, ctx, nb)
     check_plan(plan, image, table, ctx, nb, 14, 2, shared_expected=True)
+    for w in (2, 4):  # wider shared items read each prefix through fewer block reads
+        wide, image_w = build(table, ctx, nb, share_width=w)
+        check_plan(wide, image_w, table, ctx, nb, 14, 2, shared_expected=True)
+        assert wide.kv_blocks_read < plan.kv_blocks_read
     # reading each shared prefix through fewer items than requests
     plain, image0 = build(table, ctx, nb, share=False)
     check_plan(plain, image0, table, ctx, nb, 14, 2, shared_expected=False)
@@ -213,9 +221,16 @@ def test_plan_members_without_shared_blocks():
     items, pbase, nparts, rs = check_plan(plan, image, table, ctx, 16, 4, 1)
     assert list(rs) == [32, 32, 16, 0]  # last member: its only block holds its last token
     assert list(nparts) == [2, 2, 2, 1]  # one shared part (if any) + one private part
-    plan, image = build(table, ctx, 16, hq=8, hkv=1)  # group 8: pairs of members
+    plan, image = build(table, ctx, 16, hq=8, hkv=1)  # group 8: one column block, pairs of members
     items, pbase, nparts, rs = check_plan(plan, image, table, ctx, 16, 8, 1)
     assert list(rs) == [32, 32, 0, 0]  # requests 2 and 3 share no whole block
+    for w in (2, 4):  # wider shared items: all four requests in one item again
+        plan, image = build(table, ctx, 16, hq=8, hkv=1, share_width=w)
+        items, pbase, nparts, rs = check_plan(plan, image, table, ctx, 16, 8, 1)
+        assert list(rs) == [32, 32, 16, 0]
+    plan, image = build(table, ctx, 16, hq=32, hkv=1)  # group 32: two blocks per member, no sharing
+    items, pbase, nparts, rs = check_plan(plan, image, table, ctx, 16, 32, 1)
+    assert list(rs) == [0, 0, 0, 0] and plan.n_shared == 0
 
 
 def test_plan_empty_and_unusable_entries():
@@ -267,8 +282,14 @@ def test_plan_validation():
         kvp.decode_plan_build(14, 2, table, ctx, 0)
     assert e.value.status == kvp.KVP_ERR_INVALID
     with pytest.raises(kvp.KvpError) as e:
-        kvp.decode_plan_build(18, 2, table, ctx, 8)  # group 9
+        kvp.decode_plan_build(40, 2, table, ctx, 8)  # group 20: above 16 and not a multiple of 16
     assert e.value.status == kvp.KVP_ERR_UNSUPPORTED
+    with pytest.raises(kvp.KvpError) as e:
+        kvp.decode_plan_build(96, 1, table, ctx, 8, head_dim=128)  # group 96: more than 2 blocks at d128
+    assert e.value.status == kvp.KVP_ERR_UNSUPPORTED
+    for hq, hkv in ((18, 2), (14, 1), (32, 1), (64, 1)):  # groups 9, 14, 32 and 64 are served
+        plan, _ = kvp.decode_plan_build(hq, hkv, table, ctx, 8)
+        assert plan.group == hq // hkv
     small = torch.empty((64,), dtype=torch.uint8)
     with pytest.raises(kvp.KvpError) as e:
         kvp.decode_plan_build(14, 2, table, ctx, 8, image=small)

@@ -152,7 +152,10 @@ def test_ragged_edges_and_tile_boundaries():
         assert err <= TOL[dtype]
 
 
-@pytest.mark.parametrize("hq,hkv", [(1, 1), (2, 1), (4, 2), (6, 2), (8, 1), (12, 4), (16, 2)])
+# groups 1..16 fill one block of 16 MFMA columns; 14 query heads on one KV head is the
+# chapter's model as multi-query attention, 32 and 64 take two and four column blocks
+@pytest.mark.parametrize("hq,hkv", [(1, 1), (2, 1), (4, 2), (6, 2), (8, 1), (12, 4), (16, 2), (18, 2), (14, 1),
+                                    (16, 1), (32, 1), (64, 2)])
 def test_head_groupings(hq, hkv):
     need_gpu()
     say("grouping", hq, hkv)
@@ -160,8 +163,22 @@ def test_head_groupings(hq, hkv):
     step = PagedStep(kvp, pb, layers=1, hq=hq, hkv=hkv, dtype=torch.float16, seed=5000 + hq)
     q = step.q(0).cuda()
     op = kvp.paged_decode_attention(step.cache, 0, q, step.table, step.ctx)
+    K, V = step.logical[0]
+    oc = kvp.contiguous_decode_attention(q, K.cuda(), V.cuda(), step.ctx)
     torch.cuda.synchronize()
-    assert max_abs(to64(op), step.oracle(0)) <= TOL[torch.float16]
+    assert torch.equal(_bits(op.cpu()), _bits(oc.cpu())), "paged != contiguous"
+    err = max_abs(to64(op), step.oracle(0))
+    say("grouping", hq, hkv, "max err", err)
+    assert err <= TOL[torch.float16]
+
+
+def test_groups_beyond_the_column_blocks_are_refused():
+    need_gpu()
+    pb = W.paged_batch(2, lo=10, hi=40, prefix=0, group_size=1, seed=32)
+    step = PagedStep(kvp, pb, layers=1, hq=20, hkv=1, dtype=torch.float16, seed=5100)
+    with pytest.raises(kvp.KvpError) as e:  # group 20: above 16 and not a multiple of 16
+        kvp.paged_decode_attention(step.cache, 0, step.q(0).cuda(), step.table, step.ctx)
+    assert e.value.status == kvp.KVP_ERR_UNSUPPORTED
 
 
 # ---------------------------------------------------------------------------------------

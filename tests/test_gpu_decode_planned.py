@@ -86,7 +86,10 @@ def test_planned_full_size_b200():
         assert err <= TOL[torch.float16]
 
 
-@pytest.mark.parametrize("hq,hkv", [(8, 8), (8, 2), (8, 1), (14, 2), (16, 2), (4, 4)])
+# shared items serve 16 / G members per column block (up to 4 blocks); groups above 16
+# (multi-query with 32 or 64 heads) read every request privately
+@pytest.mark.parametrize("hq,hkv", [(8, 8), (8, 2), (8, 1), (14, 2), (16, 2), (4, 4), (2, 2), (14, 1), (12, 1),
+                                    (32, 1), (64, 1)])
 def test_planned_head_groupings(hq, hkv):
     need_gpu()
     say("planned grouping", hq, hkv)

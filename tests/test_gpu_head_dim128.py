@@ -48,7 +48,7 @@ def test_append_gather_and_copy_on_write_are_bit_exact():
         assert torch.equal(_bits(vg.cpu()), _bits(V)), f"layer {l} V"
 
 
-@pytest.mark.parametrize("hq,hkv", [(32, 8), (32, 32), (8, 1), (14, 2)])
+@pytest.mark.parametrize("hq,hkv", [(32, 8), (32, 32), (8, 1), (14, 2), (14, 1), (32, 1)])
 def test_paged_decode_matches_oracle_and_contiguous(hq, hkv):
     need_gpu()
     pb = W.paged_batch(10)
@@ -83,11 +83,12 @@ def test_ragged_edges_and_tile_boundaries():
     assert err <= TOL[torch.float16]
 
 
-def test_planned_decode_bit_identical_without_sharing_and_oracle_with_sharing():
+@pytest.mark.parametrize("hq,hkv", [(32, 8), (14, 2)])
+def test_planned_decode_bit_identical_without_sharing_and_oracle_with_sharing(hq, hkv):
     need_gpu()
     pb = W.paged_batch(24, seed=91)
-    say("d128 planned", pb.batch)
-    step = PagedStep(kvp, pb, layers=1, hq=32, hkv=8, dtype=torch.float16, seed=22200, head_dim=D)
+    say("d128 planned", pb.batch, hq, hkv)
+    step = PagedStep(kvp, pb, layers=1, hq=hq, hkv=hkv, dtype=torch.float16, seed=22200, head_dim=D)
     q = step.q(0).cuda()
     o_plain = kvp.paged_decode_attention(step.cache, 0, q, step.table, step.ctx)
     plan0, dp0 = _plan(step, share=False)

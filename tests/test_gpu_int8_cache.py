@@ -84,7 +84,8 @@ def test_paged_decode_matches_oracle(B):
         assert err <= TOL[torch.float16]
 
 
-@pytest.mark.parametrize("hq,hkv,d", [(32, 8, 128), (32, 32, 128), (8, 1, 64), (4, 4, 64), (16, 2, 128)])
+@pytest.mark.parametrize("hq,hkv,d", [(32, 8, 128), (32, 32, 128), (8, 1, 64), (4, 4, 64), (16, 2, 128),
+                                      (14, 1, 64), (32, 1, 64), (32, 1, 128)])
 def test_head_shapes(hq, hkv, d):
     need_gpu()
     pb = W.paged_batch(6, lo=1, hi=900, prefix=0, group_size=1, seed=33)
