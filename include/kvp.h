@@ -335,6 +335,25 @@ kvp_status paged_decode_append_attention(const kvp_cache_desc *cache, int32_t la
                                          const int32_t *d_context_lens, int32_t B, float scale,
                                          void *workspace, size_t ws_bytes, kvp_stream stream);
 
+/* paged_decode_attention for callers that cannot allocate (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc): the same kernels, splits and
+ * results (bit for bit), but no workspace argument -- the split counters and partials live
+ * in a static device array of the library, KVP_NOALLOC_SCRATCH_BYTES per GPU (the first
+ * KVP_NOALLOC_MAX_PAIRS * 4 bytes hold the counters), held by each GPU the library runs on
+ * until the process ends.  The call itself allocates nothing.  INVALID (nothing launched)
+ * when B * H_kv exceeds KVP_NOALLOC_MAX_PAIRS or the split partials of B requests with
+ * contexts up to max_blocks * block_size tokens exceed the rest of the array (about 1000
+ * requests with tables of up to 2048 tokens, or 64 of 32768, at 14q / 2kv, d = 64).  The first call on a device zeroes the
+ * counters with a small kernel on `stream`; every call leaves them at zero.  Calls on one
+ * GPU share the array: calls that overlap in time on one GPU (other streams, other host
+ * threads) race and must not be issued; one stream at a time is fine. */
+#define KVP_NOALLOC_SCRATCH_BYTES (16u << 20)
+#define KVP_NOALLOC_MAX_PAIRS 65536
+kvp_status paged_decode_attention_noalloc(const kvp_cache_desc *cache, int32_t layer, void *out,
+                                          const void *q, const int32_t *d_block_table,
+                                          int32_t max_blocks, const int32_t *d_context_lens,
+                                          int32_t B, float scale, kvp_stream stream);
+
 /* The same decode over a contiguous cache k_cache / v_cache [B][H_kv][Lmax][d] (one layer;
  * the layout of the cache tensors in [CHAP]'s allocator check).  Same kernels, same split
  * policy and the same arithmetic order as the paged call, so the outputs of the two are

@@ -138,6 +138,8 @@ _sig("paged_decode_attention", _i32, [ctypes.POINTER(kvp_cache_desc), _i32, _p, 
                                       _i32, _f32, _p, _sz, _p])
 _sig("paged_decode_append_attention", _i32, [ctypes.POINTER(kvp_cache_desc), _i32, _p, _p, _p, _p, _p, _i32,
                                              _p, _i32, _f32, _p, _sz, _p])
+_sig("paged_decode_attention_noalloc", _i32, [ctypes.POINTER(kvp_cache_desc), _i32, _p, _p, _p, _i32, _p, _i32,
+                                              _f32, _p])
 _sig("decode_plan_bytes", _sz, [ctypes.POINTER(kvp_dims), _i32, _i32, _i32])
 _sig("decode_plan_build", _i32, [ctypes.POINTER(kvp_dims), _p, _i32, _p, _i32, _i32, ctypes.c_uint32, _i32, _p, _sz,
                                  ctypes.POINTER(kvp_decode_plan)])
@@ -437,6 +439,26 @@ def paged_decode_attention(cache: PagedKVCache, layer, q, block_table, context_l
                                        max_blocks, _dev(context_lens, "context_lens", torch.int32), B,
                                        float(scale), _dev(workspace, "workspace"), workspace.numel(),
                                        _stream(stream)))
+    return out
+
+
+def paged_decode_attention_noalloc(cache: PagedKVCache, layer, q, block_table, context_lens, out=None, scale=0.0,
+                                   stream=None):
+    """paged_decode_attention without a workspace (the library's static scratch holds the
+    split state; for callers that cannot allocate).  Same arguments and result."""
+    B, hq, d = q.shape
+    if hq != cache.num_q_heads or d != cache.head_dim:
+        raise ValueError("paged_decode_attention_noalloc: q shape does not match the cache")
+    max_blocks = block_table.shape[1]
+    if block_table.shape[0] != B or context_lens.shape != (B,):
+        raise ValueError("paged_decode_attention_noalloc: table / context_lens shape mismatch")
+    if out is None:
+        out = torch.empty_like(q)
+    _check(_lib.paged_decode_attention_noalloc(ctypes.byref(cache.desc), int(layer), _dev(out, "out", cache.io_dtype),
+                                               _dev(q, "q", cache.io_dtype),
+                                               _dev(block_table, "block_table", torch.int32), max_blocks,
+                                               _dev(context_lens, "context_lens", torch.int32), B, float(scale),
+                                               _stream(stream)))
     return out
 
 

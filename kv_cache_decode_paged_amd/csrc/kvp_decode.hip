@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <atomic>
+#include <mutex>
 
 #include <algorithm>
 #include <cmath>
@@ -42,6 +43,57 @@ static kvp_status check_dims(const kvp_dims *d, const char *who)
 
 static size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
+// ---------------------------------------------------------------------------------------
+// Static scratch of paged_decode_attention_noalloc: split counters (one int per request and
+// KV head, in a fixed region so that partials of a larger call never land on counters of a
+// later one) followed by the split partials.  Each GPU holds its own copy from the first
+// use until the process ends; its device address is looked up once per device.
+// ---------------------------------------------------------------------------------------
+constexpr int NOALLOC_MAX_PAIRS = KVP_NOALLOC_MAX_PAIRS;
+constexpr size_t NOALLOC_TICKET_BYTES = (size_t)KVP_NOALLOC_MAX_PAIRS * sizeof(int);
+constexpr size_t NOALLOC_PART_BYTES = (size_t)KVP_NOALLOC_SCRATCH_BYTES - NOALLOC_TICKET_BYTES;
+static_assert(NOALLOC_TICKET_BYTES % 256 == 0, "partials start 256-byte aligned");
+
+static __device__ __align__(256) char scratch[KVP_NOALLOC_SCRATCH_BYTES];
+
+constexpr int SCRATCH_MAX_DEVICES = 64;
+static std::mutex g_scratch_mu;
+static void *g_scratch_ptr[SCRATCH_MAX_DEVICES]; // device address of `scratch`, per device
+
+__global__ void clear_ints_kernel(int *p, int n)
+{
+    for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x)
+        p[i] = 0;
+}
+
+// The current device's scratch address.  On the first use on a device: look the array up
+// (hipGetSymbolAddress) and zero its counter region with a small kernel on `st` (stream-
+// ordered before the caller's decode; the array also starts zeroed when the code object
+// loads).  Every decode leaves the counters at zero again.
+static kvp_status scratch_for_device(char **out, hipStream_t st, const char *who)
+{
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return fail(KVP_ERR_HIP, "%s: hipGetDevice: %s", who, hipGetErrorString(e));
+    if (dev < 0 || dev >= SCRATCH_MAX_DEVICES)
+        return fail(KVP_ERR_UNSUPPORTED, "%s: device %d (at most %d devices)", who, dev, SCRATCH_MAX_DEVICES);
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p)
+            return fail(KVP_ERR_HIP, "%s: hipGetSymbolAddress(scratch): %s", who, hipGetErrorString(e));
+        hipLaunchKernelGGL(clear_ints_kernel, dim3(64), dim3(256), 0, st, (int *)p, NOALLOC_MAX_PAIRS);
+        e = hipGetLastError();
+        if (e != hipSuccess)
+            return fail(KVP_ERR_HIP, "%s: clearing the scratch counters: %s", who, hipGetErrorString(e));
+        g_scratch_ptr[dev] = p;
+    }
+    *out = (char *)g_scratch_ptr[dev];
+    return KVP_OK;
+}
+
 static size_t part_bytes(const kvp_dims *d, int B, int max_context)
 {
     if (d->dtype != KVP_F32) { // the fp16 kernel (fp16 or int8 caches)
@@ -65,12 +117,22 @@ static size_t workspace_bytes(const kvp_dims *d, int B, int max_context)
     return ticket_bytes(B, d->num_kv_heads) + pb;
 }
 
+// Where the split counters and partials live: the caller's workspace, or the library's
+// static scratch array (paged_decode_attention_noalloc: counters in a fixed region, partials
+// after it).  `dry` stops after the argument checks, before anything is launched.
+struct WsMode {
+    bool fixed = false;   // static scratch
+    bool dry = false;
+    int *tickets = nullptr;
+    float *part = nullptr;
+};
+
 template <typename Addr>
 static kvp_status decode_common(const kvp_dims *dims, void *out, const void *q, const void *kc,
                                 const void *vc, const void *ksc, const void *vsc, const void *k_new,
                                 const void *v_new, const Addr &A, int max_ctx, const int32_t *d_ctx,
                                 int32_t B, float scale, void *ws, size_t ws_bytes, kvp_stream stream,
-                                const char *who)
+                                const char *who, const WsMode &wm = WsMode())
 {
     kvp_status st = check_dims(dims, who);
     if (st != KVP_OK)
@@ -118,7 +180,14 @@ static kvp_status decode_common(const kvp_dims *dims, void *out, const void *q, 
     P.workers = dims->dtype != KVP_F32 ? 0 : decode_f32_max_splits(max_ctx);
     P.merge_polls = g_merge_polls.load(std::memory_order_relaxed);
     const size_t pb = part_bytes(dims, B, max_ctx);
-    if (pb > 0) {
+    if (wm.fixed) {
+        if ((long long)B * dims->num_kv_heads > NOALLOC_MAX_PAIRS || pb > NOALLOC_PART_BYTES)
+            return fail(KVP_ERR_INVALID, "%s: %d requests x %d KV heads with contexts up to %d tokens need %zu bytes "
+                        "of split partials; the static scratch holds %d (request, KV head) pairs and %zu bytes",
+                        who, B, dims->num_kv_heads, max_ctx, pb, NOALLOC_MAX_PAIRS, (size_t)NOALLOC_PART_BYTES);
+        P.tickets = wm.tickets;
+        P.part = wm.part;
+    } else if (pb > 0) {
         const size_t need = workspace_bytes(dims, B, max_ctx);
         if (!ws || ws_bytes < need)
             return fail(KVP_ERR_INVALID, "%s: workspace %zu bytes < %zu needed", who, ws_bytes, need);
@@ -127,6 +196,8 @@ static kvp_status decode_common(const kvp_dims *dims, void *out, const void *q, 
         P.tickets = (int *)ws;
         P.part = (float *)((char *)ws + ticket_bytes(B, dims->num_kv_heads));
     }
+    if (wm.dry)
+        return KVP_OK;
     const int group = P.hq / P.hkv;
     hipStream_t st_ = (hipStream_t)stream;
     return dims->dtype != KVP_F32 ? launch_decode_f16(P, A, group, max_ctx, st_)
@@ -137,7 +208,8 @@ static kvp_status paged_common(const kvp_cache_desc *cache, int32_t layer, void 
                                const void *q, const void *k_new, const void *v_new,
                                const int32_t *d_block_table, int32_t max_blocks,
                                const int32_t *d_context_lens, int32_t B, float scale,
-                               void *workspace, size_t ws_bytes, kvp_stream stream, const char *who)
+                               void *workspace, size_t ws_bytes, kvp_stream stream, const char *who,
+                               const WsMode &wm = WsMode())
 {
     if (!cache)
         return fail(KVP_ERR_INVALID, "%s: cache is NULL", who);
@@ -168,7 +240,7 @@ static kvp_status paged_common(const kvp_cache_desc *cache, int32_t layer, void 
     const char *vsc = i8 ? (const char *)cache->v_scale + (size_t)layer * layer_rows * 2 : nullptr;
     PagedAddr A{d_block_table, max_blocks, cache->dims.num_kv_heads, cache->num_blocks, cache->dims.head_dim};
     return decode_common(&cache->dims, out, q, kc, vc, ksc, vsc, k_new, v_new, A, max_blocks * BS,
-                         d_context_lens, B, scale, workspace, ws_bytes, stream, who);
+                         d_context_lens, B, scale, workspace, ws_bytes, stream, who, wm);
 }
 
 static size_t plan_workspace_bytes(const kvp_decode_plan *plan)
@@ -221,6 +293,29 @@ kvp_status paged_decode_append_attention(const kvp_cache_desc *cache, int32_t la
     return paged_common(cache, layer, out, q, k_new, v_new, d_block_table, max_blocks,
                         d_context_lens, B, scale, workspace, ws_bytes, stream,
                         "paged_decode_append_attention");
+}
+
+kvp_status paged_decode_attention_noalloc(const kvp_cache_desc *cache, int32_t layer, void *out, const void *q,
+                                          const int32_t *d_block_table, int32_t max_blocks,
+                                          const int32_t *d_context_lens, int32_t B, float scale, kvp_stream stream)
+{
+    const char *who = "paged_decode_attention_noalloc";
+    WsMode wm;
+    wm.fixed = true;
+    wm.dry = true; // every argument and size check first: on error nothing is launched
+    kvp_status st = paged_common(cache, layer, out, q, nullptr, nullptr, d_block_table, max_blocks, d_context_lens, B,
+                                 scale, nullptr, 0, stream, who, wm);
+    if (st != KVP_OK || B == 0)
+        return st;
+    char *base = nullptr;
+    st = scratch_for_device(&base, (hipStream_t)stream, who);
+    if (st != KVP_OK)
+        return st;
+    wm.dry = false;
+    wm.tickets = (int *)base;
+    wm.part = (float *)(base + NOALLOC_TICKET_BYTES);
+    return paged_common(cache, layer, out, q, nullptr, nullptr, d_block_table, max_blocks, d_context_lens, B, scale,
+                        nullptr, 0, stream, who, wm);
 }
 
 size_t decode_plan_workspace_bytes(const kvp_decode_plan *plan)
