@@ -62,6 +62,7 @@ SHAPES = {
 DEFAULT_SHAPE = "14q2kv_d64"
 
 KV_INT8 = False  # the cache holds int8 codes and one fp16 scale per row
+SCATTER = True   # block ids handed out from a shuffled free list (False: in order)
 
 
 def set_shape(name, kv_int8=False):
@@ -258,7 +259,8 @@ def build_state(kvp, torch, W, ctx_before, group, prefix, layers, total_steps, s
     num_blocks = need
     max_blocks = math.ceil((max(ctx_before) + total_steps + 1) / BLOCK)
     pool = kvp.BlockPool(num_blocks)
-    pool.set_free_order(W.free_list_permutation(num_blocks, seed + 1).tolist())
+    if SCATTER:  # block ids from a seeded shuffle of the free list: scattered tables
+        pool.set_free_order(W.free_list_permutation(num_blocks, seed + 1).tolist())
     cache = kvp.PagedKVCache(layers, num_blocks, HQ, HKV, torch.int8 if KV_INT8 else torch.float16, dev,
                              head_dim=D)
     for l in range(layers):  # cache contents: seeded N(0,1) in every slot
@@ -504,7 +506,8 @@ def decode_line(args, metric, B, L, ctx_before, group, prefix, long_items, share
         "dtype": "f16" if not KV_INT8 else "i8 cache (fp16 scales), f16 arithmetic",
         "data": "synthetic",
         "config": dict({"workload": workload_desc, "batch": B, "layers": L, "shape": args.shape,
-                        "kv_dtype": "int8" if KV_INT8 else "fp16", "graph": runner.graphs[0] is not None},
+                        "kv_dtype": "int8" if KV_INT8 else "fp16", "graph": runner.graphs[0] is not None,
+                        "scattered_blocks": SCATTER},
                        **extra_cfg),
         "steps_per_sec": round(1e3 / ms_per_step, 2),
         "hbm_pct": round(value / HBM_PEAK_GBPS * 100, 2),
@@ -994,6 +997,7 @@ def main():
                     help="decode workload: plans with long items (KVP_PLAN_LONG_ITEMS, which sizes parts to "
                          "one generation of waves when a batch's private blocks far exceed them and leaves "
                          "smaller batches' plans as they are); always on for long_context")
+    ap.add_argument("--no-scatter", action="store_true", help="hand out block ids in order (no free-list shuffle)")
     ap.add_argument("--seed", type=int, default=42)
     ap.add_argument("--workload", default="decode",
                     choices=["decode", "long_context", "batch1", "single_head", "varlen", "prefill",
@@ -1011,6 +1015,8 @@ def main():
               "Requests would be sharded across GPUs by whole sharing groups.", flush=True)
         sys.exit(2)
     set_shape(args.shape, args.kv_dtype == "int8")
+    global SCATTER
+    SCATTER = not args.no_scatter
     if args.kv_dtype == "int8" and args.workload not in ("decode", "long_context"):
         print("--kv-dtype int8 applies to the decode workloads", flush=True)
         sys.exit(2)
