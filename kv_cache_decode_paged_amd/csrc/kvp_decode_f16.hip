@@ -229,6 +229,7 @@ __device__ __forceinline__ void run_item(const DecodeParams &P, const Addr &A, c
     const char *kc = (const char *)P.kc;
     const char *vc = (const char *)P.vc;
     const float c = P.scale_log2;
+    const float inv_c = 1.f / c;
 
     // ---- this lane's query rows, one per column block: q operand, token limit, slots ----
     // Group size G = Hq / Hkv.  G <= 16: column block cb holds members cb mpb .. (mpb =
@@ -378,11 +379,12 @@ __device__ __forceinline__ void run_item(const DecodeParams &P, const Addr &A, c
 
     // running state of this lane's column in each block: reference max (scaled, log2 units),
     // output O^T rows 16 db + 4 grp + i, and the row sum (every entry of accl holds it)
-    float mref[NCB];
+    float mref[NCB], thr[NCB]; // thr: rescale_threshold of mref (raw-score units)
     f32x4 acc[NCB][NDB], accl[NCB];
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb) {
         mref[cb] = -INFINITY;
+        thr[cb] = -INFINITY;
         accl[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int db = 0; db < NDB; ++db)
@@ -708,20 +710,25 @@ __device__ __forceinline__ void run_item(const DecodeParams &P, const Addr &A, c
                 for (int i = kb == 0 ? 3 : 0; i < 4; ++i)
                     mt = max3(mt, sacc[kb][i], sacc[kb][i]);
         }
-        mt = group_max(mt) * c;
         // a column's reference max moves only when the column's own maximum passes it by more
         // than 2^8: between moves p = 2^(s c - mref) stays below 256, exact in fp16 range, and
         // the output and row sum need no rescaling.  Columns that do not move scale by exactly
-        // 1, so no query row depends on another's keys.
-        const bool need = mt > mref[cb] + RESCALE_LOG2;
-        if (__ballot(need) != 0) {
-            const float mn = need ? mt : mref[cb];
-            const float alpha = need ? (mref[cb] == -INFINITY ? 0.f : fast_exp2(mref[cb] - mn)) : 1.f;
+        // 1, so no query row depends on another's keys.  The lane's own maximum is first held
+        // against thr; only when some lane passes it does the wave reduce the columns' maxima
+        // across lanes and apply the exact test.
+        if (__ballot(mt > thr[cb]) != 0) {
+            mt = group_max(mt) * c;
+            const bool need = mt > mref[cb] + RESCALE_LOG2;
+            if (__ballot(need) != 0) {
+                const float mn = need ? mt : mref[cb];
+                const float alpha = need ? (mref[cb] == -INFINITY ? 0.f : fast_exp2(mref[cb] - mn)) : 1.f;
 #pragma unroll
-            for (int db = 0; db < NDB; ++db)
-                acc[cb][db] *= alpha;
-            accl[cb] *= alpha;
-            mref[cb] = mn;
+                for (int db = 0; db < NDB; ++db)
+                    acc[cb][db] *= alpha;
+                accl[cb] *= alpha;
+                mref[cb] = mn;
+                thr[cb] = rescale_threshold(mref[cb], c, inv_c);
+            }
         }
         const float mc = mref[cb] == -INFINITY ? 0.f : mref[cb];
         // P^T operand of k-step ks, slot s = sacc[2 ks + s / 4][s % 4] -- already in this lane

@@ -187,6 +187,17 @@ __device__ inline float group_max(float x)
 
 // growth of a column's maximum (log2 units) that moves its softmax reference
 constexpr float RESCALE_LOG2 = 8.f;
+// The per-lane pre-check of that growth compares raw scores (before the scale c > 0) with
+// the level (mref + RESCALE_LOG2) / c lowered by a relative 2e-5, far more than the few ulps
+// of rounding in that level, so it passes every tile the exact test (max * c > mref +
+// RESCALE_LOG2) would move; a scale <= 0 disables it (the exact test runs on every tile).
+__device__ inline float rescale_threshold(float mref, float c, float inv_c)
+{
+    if (!(c > 0.f) || mref == -INFINITY)
+        return -INFINITY;
+    const float x = (mref + RESCALE_LOG2) * inv_c;
+    return x - fabsf(x) * 2e-5f;
+}
 
 // workgroup execution barrier without a memory fence: the callers order their LDS and
 // LDS-DMA traffic with explicit counter waits, so the barrier must not also drain the

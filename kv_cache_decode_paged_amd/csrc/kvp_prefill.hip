@@ -132,6 +132,7 @@ __global__ __launch_bounds__(256) void prefill_mfma_f16_kernel(PrefillArgs P)
     const int col = lane & 15; // query row within a 16-row block (MFMA column)
     const int grp = lane >> 4; // lane group 0..3
     const float c = P.scale_log2;
+    const float inv_c = 1.f / c;
 
     // ---- this wave's query blocks: Q^T operands and each row's key limit ----
     f16x8 qop[NQB][KD];
@@ -214,10 +215,15 @@ __global__ __launch_bounds__(256) void prefill_mfma_f16_kernel(PrefillArgs P)
     // running state per block: reference max (scaled, log2 units), O^T rows 16 db + 4 grp + i
     // of column col, and the row sum (every entry of accl holds it)
     float mref[NQB];
+    // thr[nb]: raw-score level below which no key of a tile can move row block nb's reference
+    // (rescale_threshold: a little under (mref + 8) / c, so every tile the exact test would
+    // move is seen)
+    float thr[NQB];
     f32x4 acc[NQB][NDB], accl[NQB];
 #pragma unroll
     for (int nb = 0; nb < NQB; ++nb) {
         mref[nb] = -INFINITY;
+        thr[nb] = -INFINITY;
         accl[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int db = 0; db < NDB; ++db)
@@ -348,19 +354,25 @@ __global__ __launch_bounds__(256) void prefill_mfma_f16_kernel(PrefillArgs P)
                     for (int i = 0; i < 4; ++i)
                         sacc[kb][i] = (bok[kb] && k0 + 16 * kb + 4 * grp + i < lim[nb]) ? sacc[kb][i] : -INFINITY;
             }
-            const float mt = group_max(max_scores<KB>(sacc)) * c;
             // a row's reference max moves only when the row's own maximum passes it by more
             // than 2^8; between moves p = 2^(s c - mref) < 256 and nothing needs rescaling.
             // Rows that do not move scale by exactly 1, so no row depends on another's keys.
-            const bool need = mt > mref[nb] + RESCALE_LOG2;
-            if (__ballot(need) != 0) {
-                const float mn = need ? mt : mref[nb];
-                const float alpha = need ? (mref[nb] == -INFINITY ? 0.f : pf_exp2(mref[nb] - mn)) : 1.f;
+            // The lane's own maximum is first held against thr; only when some lane passes it
+            // does the wave reduce the rows' maxima across lanes and apply the exact test.
+            const float lmax = max_scores<KB>(sacc);
+            if (__ballot(lmax > thr[nb]) != 0) {
+                const float mt = group_max(lmax) * c;
+                const bool need = mt > mref[nb] + RESCALE_LOG2;
+                if (__ballot(need) != 0) {
+                    const float mn = need ? mt : mref[nb];
+                    const float alpha = need ? (mref[nb] == -INFINITY ? 0.f : pf_exp2(mref[nb] - mn)) : 1.f;
 #pragma unroll
-                for (int db = 0; db < NDB; ++db)
-                    acc[nb][db] *= alpha;
-                accl[nb] *= alpha;
-                mref[nb] = mn;
+                    for (int db = 0; db < NDB; ++db)
+                        acc[nb][db] *= alpha;
+                    accl[nb] *= alpha;
+                    mref[nb] = mn;
+                    thr[nb] = rescale_threshold(mref[nb], c, inv_c);
+                }
             }
             const float mc = mref[nb] == -INFINITY ? 0.f : mref[nb];
             // P^T operand of k-step ks, slot s: key 16 (2 ks + s / 4) + 4 grp + s % 4 =
