@@ -402,7 +402,9 @@ typedef struct {
     int32_t n_items;      /* work items (one wave each)                              */
     int32_t n_shared;     /* of which read a shared prefix for several requests      */
     int32_t head_dim;     /* head dim of the cache the plan is for (64 or 128)       */
-    int32_t reserved;     /* 0                                                       */
+    int32_t col_blocks;   /* widest item, in blocks of 16 query columns (1, 2 or 4);
+                           * launches of plans whose items are all one block wide use
+                           * a kernel built for that width (0: up to 4)              */
     int64_t n_slots;      /* partial slots the workspace must hold                   */
     int64_t bytes;        /* bytes of the plan image (device copy)                   */
     int64_t off_pair_base, off_pair_nparts, off_req_shared; /* offsets in the image  */

@@ -71,7 +71,7 @@ class kvp_pool_stats(ctypes.Structure):
 class kvp_decode_plan(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32), ("group", ctypes.c_int32),
                 ("num_blocks", ctypes.c_int32), ("n_items", ctypes.c_int32), ("n_shared", ctypes.c_int32),
-                ("head_dim", ctypes.c_int32), ("reserved", ctypes.c_int32), ("n_slots", ctypes.c_int64), ("bytes", ctypes.c_int64), ("off_pair_base", ctypes.c_int64),
+                ("head_dim", ctypes.c_int32), ("col_blocks", ctypes.c_int32), ("n_slots", ctypes.c_int64), ("bytes", ctypes.c_int64), ("off_pair_base", ctypes.c_int64),
                 ("off_pair_nparts", ctypes.c_int64), ("off_req_shared", ctypes.c_int64),
                 ("kv_blocks_read", ctypes.c_int64), ("off_ids", ctypes.c_int64), ("n_ids", ctypes.c_int64)]
 

@@ -893,7 +893,10 @@ __device__ __forceinline__ void run_private(const DecodeParams &P, const Addr &A
     run_item<NCB, false, NBUF, TT, HD, I8, LONGI>(P, A, PV, it, rv, rid, kring, vring, sring);
 }
 
-template <int NBUF, int TT, int HD, bool I8, bool LONGI, typename Addr>
+// MAXNCB: the widest item a kernel build serves (1, or 4): the wider paths hold more
+// accumulators, and a kernel carrying them allocates more registers for every item (fewer
+// resident waves), so launches whose items are all one block wide use the MAXNCB = 1 build.
+template <int MAXNCB, int NBUF, int TT, int HD, bool I8, bool LONGI, typename Addr>
 __device__ __forceinline__ void dispatch_private(const DecodeParams &P, const Addr &A, const PlanView &PV,
                                                  const Item &it, int rv, const int (&rid)[3], char *kring,
                                                  char *vring, char *sring)
@@ -901,15 +904,17 @@ __device__ __forceinline__ void dispatch_private(const DecodeParams &P, const Ad
     const int bpm = P.group <= 16 ? 1 : P.group >> 4;
     if (bpm == 1)
         run_private<1, NBUF, TT, HD, I8, LONGI>(P, A, PV, it, rv, rid, kring, vring, sring);
-    else if (bpm == 2)
-        run_private<2, NBUF, TT, HD, I8, LONGI>(P, A, PV, it, rv, rid, kring, vring, sring);
-    else if constexpr (HD == 64) {
-        if (bpm == 4)
-            run_private<4, NBUF, TT, HD, I8, LONGI>(P, A, PV, it, rv, rid, kring, vring, sring);
+    else if constexpr (MAXNCB >= 2) {
+        if (bpm == 2)
+            run_private<2, NBUF, TT, HD, I8, LONGI>(P, A, PV, it, rv, rid, kring, vring, sring);
+        else if constexpr (HD == 64 && MAXNCB >= 4) {
+            if (bpm == 4)
+                run_private<4, NBUF, TT, HD, I8, LONGI>(P, A, PV, it, rv, rid, kring, vring, sring);
+        }
     }
 }
 
-template <int NBUF, int TT, int HD, bool I8, bool PLANNED, typename Addr>
+template <int MAXNCB, int NBUF, int TT, int HD, bool I8, bool PLANNED, typename Addr>
 __global__ __launch_bounds__(64) void decode_f16_kernel(DecodeParams P, Addr A, PlanView PV)
 {
     static_assert(NBUF >= 2 && NBUF <= 4, "ring depth");
@@ -949,11 +954,14 @@ __global__ __launch_bounds__(64) void decode_f16_kernel(DecodeParams P, Addr A, 
             const int ncb = (it.nmem + mpb - 1) / mpb;
             if (ncb <= 1)
                 run_item<1, true, NBUF, TT, HD, I8, false>(P, A, PV, it, rv, {-1, -1, -1}, kring, vring, sring);
-            else if (ncb <= 2)
-                run_item<2, true, NBUF, TT, HD, I8, false>(P, A, PV, it, rv, {-1, -1, -1}, kring, vring, sring);
-            else if constexpr (HD == 64) {
-                if (ncb <= 4)
-                    run_item<4, true, NBUF, TT, HD, I8, false>(P, A, PV, it, rv, {-1, -1, -1}, kring, vring, sring);
+            else if constexpr (MAXNCB >= 2) {
+                if (ncb <= 2)
+                    run_item<2, true, NBUF, TT, HD, I8, false>(P, A, PV, it, rv, {-1, -1, -1}, kring, vring, sring);
+                else if constexpr (HD == 64 && MAXNCB >= 4) {
+                    if (ncb <= 4)
+                        run_item<4, true, NBUF, TT, HD, I8, false>(P, A, PV, it, rv, {-1, -1, -1}, kring, vring,
+                                                                   sring);
+                }
             }
             return;
         }
@@ -972,9 +980,9 @@ __global__ __launch_bounds__(64) void decode_f16_kernel(DecodeParams P, Addr A, 
                     rid[k] = PV.ids[off + 64 * k + lane];
         }
         if (longi)
-            dispatch_private<NBUF, TT, HD, I8, true>(P, A, PV, it, rv, rid, kring, vring, sring);
+            dispatch_private<MAXNCB, NBUF, TT, HD, I8, true>(P, A, PV, it, rv, rid, kring, vring, sring);
         else
-            dispatch_private<NBUF, TT, HD, I8, false>(P, A, PV, it, rv, rid, kring, vring, sring);
+            dispatch_private<MAXNCB, NBUF, TT, HD, I8, false>(P, A, PV, it, rv, rid, kring, vring, sring);
     } else {
         const int pair = blockIdx.x / PV.ipp;
         const int k = blockIdx.x - pair * PV.ipp;
@@ -999,43 +1007,56 @@ __global__ __launch_bounds__(64) void decode_f16_kernel(DecodeParams P, Addr A, 
         it.slot = it.pbase + k;
         const int j = lane - R_ENT;
         rv = (j >= 0 && j < it.nblk) ? A.entry(it.b, it.blk0 + j) : -1;
-        dispatch_private<NBUF, TT, HD, I8, false>(P, A, PV, it, rv, {-1, -1, -1}, kring, vring, sring);
+        dispatch_private<MAXNCB, NBUF, TT, HD, I8, false>(P, A, PV, it, rv, {-1, -1, -1}, kring, vring, sring);
     }
 }
 
 // ---------------------------------------------------------------------------------------
+template <int MAXNCB, bool PLANNED, typename Addr>
+static void launch_width(const DecodeParams &P, const Addr &A, const PlanView &PV, dim3 g, hipStream_t st)
+{
+    dim3 block(64);
+    // head_dim 64: 64-token tiles; 128: 32-token tiles (the same 32 KB of LDS for the rings)
+    if (P.kv_i8) {
+        if constexpr (Addr::paged) {
+            if (P.dim == 64)
+                hipLaunchKernelGGL((decode_f16_kernel<MAXNCB, DEC_NBUF, DEC_TT, 64, true, PLANNED, Addr>), g, block, 0,
+                                   st, P, A, PV);
+            else
+                hipLaunchKernelGGL((decode_f16_kernel<MAXNCB, 2, 32, 128, true, PLANNED, Addr>), g, block, 0, st, P, A,
+                                   PV);
+        }
+    } else {
+        if (P.dim == 64)
+            hipLaunchKernelGGL((decode_f16_kernel<MAXNCB, DEC_NBUF, DEC_TT, 64, false, PLANNED, Addr>), g, block, 0, st,
+                               P, A, PV);
+        else
+            hipLaunchKernelGGL((decode_f16_kernel<MAXNCB, 2, 32, 128, false, PLANNED, Addr>), g, block, 0, st, P, A,
+                               PV);
+    }
+}
+
+// width: the widest item of the launch in column blocks (1, 2 or 4)
 template <bool PLANNED, typename Addr>
-static kvp_status launch_f16(const DecodeParams &P, const Addr &A, const PlanView &PV, long long grid,
+static kvp_status launch_f16(const DecodeParams &P, const Addr &A, const PlanView &PV, long long grid, int width,
                              hipStream_t st)
 {
     if (grid <= 0)
         return KVP_OK;
     if (grid > 0x7fffffffLL)
         return fail(KVP_ERR_UNSUPPORTED, "decode: %lld work items", grid);
-    dim3 g((unsigned)grid), block(64);
+    dim3 g((unsigned)grid);
     if (P.dim != 64 && P.dim != 128)
         return fail(KVP_ERR_UNSUPPORTED, "decode: head_dim=%d (64 or 128)", P.dim);
     if (!group_supported(P.group, P.dim))
         return fail(KVP_ERR_UNSUPPORTED, "decode: %d query heads per KV head (1..16, or a multiple of 16 up to %d "
                     "at head dim %d)", P.group, P.dim == 64 ? 64 : 32, P.dim);
-    // head_dim 64: 64-token tiles; 128: 32-token tiles (the same 32 KB of LDS for the rings)
-    if (P.kv_i8) {
-        if constexpr (Addr::paged) {
-            if (P.dim == 64)
-                hipLaunchKernelGGL((decode_f16_kernel<DEC_NBUF, DEC_TT, 64, true, PLANNED, Addr>), g, block, 0, st, P,
-                                   A, PV);
-            else
-                hipLaunchKernelGGL((decode_f16_kernel<2, 32, 128, true, PLANNED, Addr>), g, block, 0, st, P, A, PV);
-        } else {
-            return fail(KVP_ERR_UNSUPPORTED, "decode: int8 caches are paged only");
-        }
-    } else {
-        if (P.dim == 64)
-            hipLaunchKernelGGL((decode_f16_kernel<DEC_NBUF, DEC_TT, 64, false, PLANNED, Addr>), g, block, 0, st, P, A,
-                               PV);
-        else
-            hipLaunchKernelGGL((decode_f16_kernel<2, 32, 128, false, PLANNED, Addr>), g, block, 0, st, P, A, PV);
-    }
+    if (P.kv_i8 && !Addr::paged)
+        return fail(KVP_ERR_UNSUPPORTED, "decode: int8 caches are paged only");
+    if (width <= 1)
+        launch_width<1, PLANNED>(P, A, PV, g, st);
+    else
+        launch_width<4, PLANNED>(P, A, PV, g, st);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return fail(KVP_ERR_HIP, "decode launch: %s", hipGetErrorString(e));
@@ -1058,14 +1079,14 @@ kvp_status launch_decode_f16(const DecodeParams &P, const PagedAddr &A, int grou
 {
     PlanView PV{nullptr, nullptr, nullptr, nullptr, decode_f16_items_per_pair(max_context, P.kv_i8 != 0, P.dim), nullptr,
                 0};
-    return launch_f16<false>(P, A, PV, (long long)P.B * P.hkv * PV.ipp, st);
+    return launch_f16<false>(P, A, PV, (long long)P.B * P.hkv * PV.ipp, P.group <= 16 ? 1 : P.group / 16, st);
 }
 kvp_status launch_decode_f16(const DecodeParams &P, const ContigAddr &A, int group, int max_context,
                              hipStream_t st)
 {
     PlanView PV{nullptr, nullptr, nullptr, nullptr, decode_f16_items_per_pair(max_context, P.kv_i8 != 0, P.dim), nullptr,
                 0};
-    return launch_f16<false>(P, A, PV, (long long)P.B * P.hkv * PV.ipp, st);
+    return launch_f16<false>(P, A, PV, (long long)P.B * P.hkv * PV.ipp, P.group <= 16 ? 1 : P.group / 16, st);
 }
 kvp_status launch_decode_f16_planned(const DecodeParams &P, const PagedAddr &A, int group,
                                      const void *d_image, const kvp_decode_plan &plan, hipStream_t st)
@@ -1074,7 +1095,8 @@ kvp_status launch_decode_f16_planned(const DecodeParams &P, const PagedAddr &A, 
     PlanView PV{(const int *)img, (const int *)(img + plan.off_pair_base),
                 (const int *)(img + plan.off_pair_nparts), (const int *)(img + plan.off_req_shared), 0,
                 (const int *)(img + plan.off_ids), plan.n_ids};
-    return launch_f16<true>(P, A, PV, plan.n_items, st);
+    // plans of an older layout carry 0: every width
+    return launch_f16<true>(P, A, PV, plan.n_items, plan.col_blocks > 0 ? plan.col_blocks : 4, st);
 }
 
 } // namespace kvp

@@ -402,7 +402,15 @@ kvp_status decode_plan_build(const kvp_dims *dims, const int32_t *table, int32_t
     plan->n_items = (int32_t)n_image;
     plan->n_shared = (int32_t)n_shared;
     plan->head_dim = dims->head_dim;
-    plan->reserved = 0;
+    // widest item: private items take G / 16 blocks when G > 16; shared items take
+    // ceil(members / (16 / G)) blocks rounded up to 1, 2 or 4
+    int widest = G <= 16 ? 1 : G / 16;
+    for (const SubRun &sr : subs) {
+        const int mpb = G <= 16 ? 16 / G : 1;
+        const int ncb = (sr.n + mpb - 1) / mpb;
+        widest = std::max(widest, ncb <= 1 ? 1 : (ncb <= 2 ? 2 : 4));
+    }
+    plan->col_blocks = std::min(widest, max_col_blocks(hd));
     plan->n_slots = slots;
     plan->bytes = (int64_t)bytes;
     plan->off_pair_base = (int64_t)off_pb;

@@ -173,8 +173,16 @@ class DecodeStepRunner:
             lp = kvp_decode_plan.from_buffer_copy(plan)
             lp.n_slots = lay["slot_cap"]
             lp.n_ids = (lay["img_bytes"] - plan.off_ids) // 4
+            # the widest item any step of this configuration can hold (the kernel build is
+            # chosen by it): G / 16 blocks above 16 heads per KV head, else the shared width
+            # (at least 2 when a block holds one member), at most 4 (2 at head dim 128)
+            G = self.hq // self.hkv
+            w = G // 16 if G > 16 else (max(self.share_width, 2 if G > 8 else 1) if self.share else 1)
+            lp.col_blocks = max(int(lp.col_blocks), min(w, 4 if self.d == 64 else 2))
             lay["launch"] = lp
         lp = lay["launch"]
+        if plan.col_blocks > lp.col_blocks:
+            raise RuntimeError("DecodeStepRunner: the step's plan holds wider items than the launch layout")
         if plan.n_slots > lp.n_slots:
             raise RuntimeError(f"DecodeStepRunner: step needs {plan.n_slots} partial slots, the workspace holds "
                                f"{lp.n_slots}")
