@@ -344,11 +344,13 @@ def logical_rows(snap, l, b, ctx_final, knew_h, vnew_h):
     return K, V
 
 
-def decode_check_and_baseline(torch, snap, rec, q, knew, vnew, out, layers, one_thread_reqs, total_layers):
+def decode_check_and_baseline(torch, snap, rec, q, knew, vnew, out, layers, one_thread_layers, total_layers):
     """The oracle on the bench's own data after the last step: every request of `layers`
-    on all host threads (timed: cpu_baseline), then `one_thread_reqs` requests of the first
-    of them on one thread (timed); the outputs of the last step are compared with it.  The
-    inputs of one layer are assembled (untimed) before that layer's oracle runs."""
+    on all host threads (timed: cpu_baseline), and every request of the first
+    `one_thread_layers` of them again on one thread (timed); the outputs of the last step are
+    compared with it.  The inputs of one layer are assembled (untimed) before that layer's
+    oracle runs.  Rates use the GPU line's unit: the step's unique K/V bytes per layer times
+    the layers computed, over the oracle's wall time."""
     import numpy as np
 
     import oracle
@@ -360,7 +362,7 @@ def decode_check_and_baseline(torch, snap, rec, q, knew, vnew, out, layers, one_
     threads = host_threads()
     secs = secs1 = 0.0
     err = 0.0
-    n1 = min(B, one_thread_reqs)
+    n1 = min(len(layers), one_thread_layers)
     for li, l in enumerate(layers):
         inputs = []
         for b in range(B):
@@ -374,29 +376,34 @@ def decode_check_and_baseline(torch, snap, rec, q, knew, vnew, out, layers, one_
         secs += dt
         for b, want in enumerate(res):
             err = max(err, float(np.abs(out_h[l, b].astype(np.float64) - want[0]).max()))
-        if li == 0:
-            _, secs1 = run_units(one, list(range(n1)), 1)
+        if li < n1:
+            _, dt1 = run_units(one, list(range(B)), 1)
+            secs1 += dt1
         del inputs
-    kv_bytes = sum(int(ctx[b]) for b in range(B)) * KV_TOKEN_LAYER_BYTES * len(layers)
-    kv1 = sum(int(ctx[b]) for b in range(n1)) * KV_TOKEN_LAYER_BYTES
+    _, uniq, logical = decode_call_bytes(rec.table, ctx, B)
+    uniq_b, logical_b = uniq * KV_TOKEN_LAYER_BYTES, logical * KV_TOKEN_LAYER_BYTES
     tol = 2e-3
     check = {"layers": list(layers), "requests": B, "max_abs_err": err, "tol": tol, "ok": bool(err <= tol),
              "reference": "fp64 oracle on the initial cache snapshot + the appended rows"}
-    cpu = {"value": round(kv_bytes / secs / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
-           "sample": f"{len(layers)} of {total_layers} layers x all {B} requests of the last timed step "
-                     f"(logical KV bytes / wall time, fp64 scalar C, {threads} threads)",
+    what = (f"all {total_layers} layers" if len(layers) == total_layers else
+            f"{len(layers)} of {total_layers} layers")
+    cpu = {"value": round(uniq_b * len(layers) / secs / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+           "sample": f"{what} x all {B} requests of the last timed step, fp64 scalar C on {threads} host threads "
+                     f"(unique K/V bytes of the layers computed / wall time, as the GPU value)",
            "seconds": round(secs, 3),
-           "one_thread": {"value": round(kv1 / secs1 / 1e9, 4), "unit": "GB/s", "cores": 1,
-                          "sample": f"layer {layers[0]}, {n1} requests, 1 thread",
+           "logical_GBps": round(logical_b * len(layers) / secs / 1e9, 4),
+           "one_thread": {"value": round(uniq_b * n1 / secs1 / 1e9, 4), "unit": "GB/s", "cores": 1,
+                          "sample": f"{n1} layer(s) x all {B} requests, 1 thread",
                           "seconds": round(secs1, 3)},
-           "step_seconds_scaled": {"all_cores": round(secs / len(layers) * total_layers, 3),
-                                   "one_thread": round(secs1 / n1 * B * total_layers, 3),
-                                   "note": f"scaled to all {B} requests x {total_layers} layers"}}
+           "step_seconds": {"all_cores": round(secs / len(layers) * total_layers, 3),
+                            "one_thread": round(secs1 / n1 * total_layers, 3),
+                            "note": f"all {B} requests x {total_layers} layers"
+                                    + ("" if len(layers) == total_layers else " (scaled from the sample)")}}
     return check, cpu
 
 
 def decode_line(args, metric, B, L, ctx_before, group, prefix, long_items, share, workload_desc, extra_cfg,
-                check_layers, one_thread_reqs):
+                check_layers, one_thread_layers):
     """Build the state, run the steps through DecodeStepRunner and return the JSON line."""
     import numpy as np
     import torch
@@ -490,7 +497,8 @@ def decode_line(args, metric, B, L, ctx_before, group, prefix, long_items, share
         print(f"[bench] read probe {probe}", file=sys.stderr, flush=True)
     check = cpu = None
     if want_cpu:
-        check, cpu = decode_check_and_baseline(torch, snap, last, q, knew, vnew, out, check_layers, one_thread_reqs, L)
+        check, cpu = decode_check_and_baseline(torch, snap, last, q, knew, vnew, out, check_layers,
+                                                one_thread_layers, L)
         print(f"[bench] check {check}\n[bench] cpu oracle {cpu}", file=sys.stderr, flush=True)
     line = {
         "metric": metric,
@@ -552,7 +560,8 @@ def bench_decode(args, B=None):
     metric = ("decode attention KV GB/s (% of HBM peak) + decode steps/sec at batch 200" if B == 200 else
               f"decode attention KV GB/s (% of HBM peak) + decode steps/sec at batch {B}")
     return decode_line(args, metric, B, L, pb.ctx_before, pb.group, pb.prefix, args.long_items, share, desc, {},
-                       check_layers=[0, 1, 2, 3] if L >= 4 else list(range(L)), one_thread_reqs=B)
+                       check_layers=list(range(L)) if args.shape == DEFAULT_SHAPE else list(range(min(L, 4))),
+                       one_thread_layers=2)
 
 
 def bench_long_context(args):
@@ -564,7 +573,7 @@ def bench_long_context(args):
             f", 16-token blocks, every context {LONG_CONTEXT} tokens (+1 per step), no sharing")
     return decode_line(args, "long-context split-K decode attention KV GB/s (% of HBM peak) + decode steps/sec", B,
                        L, [LONG_CONTEXT] * B, list(range(B)), 0, True, False, desc, {"context": LONG_CONTEXT},
-                       check_layers=[0], one_thread_reqs=2)
+                       check_layers=[0, 1], one_thread_layers=1)
 
 
 def bench_batch1(args, contexts=(16, 64, 256, 1024)):
@@ -576,7 +585,7 @@ def bench_batch1(args, contexts=(16, 64, 256, 1024)):
         desc = (f"batch-1 decode step, {L} layers x fused (append + paged decode), {HQ}q/{HKV}kv heads d{D} fp16, "
                 f"context {C} cached tokens (+1 per step)")
         line = decode_line(args, "batch-1 decode step latency (us per step) and KV GB/s", 1, L, [C], [0], 0, False,
-                           False, desc, {"context": C}, check_layers=list(range(min(L, 24))), one_thread_reqs=1)
+                           False, desc, {"context": C}, check_layers=list(range(min(L, 24))), one_thread_layers=24)
         # the latency regime: the headline figure is the step time
         line["latency_regime"] = True
         line["value_GBps"] = line["value"]
