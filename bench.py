@@ -425,7 +425,8 @@ def decode_line(args, metric, B, L, ctx_before, group, prefix, long_items, share
     snap = snapshot_state(torch, pool, cache, seqs, max_blocks, check_layers) if want_cpu else None
     runner = DecodeStepRunner(cache, pool, seqs, max_blocks, q, knew, vnew, out, share_prefix=share,
                               long_items=long_items, graph=not args.no_graph, grow_tokens=total_steps + 1,
-                              spare_items=8 * 32 if B >= 8 else 8, share_width=args.share_width)
+                              spare_items=8 * 32 if B >= 8 else 8, share_width=args.share_width,
+                              fill={"auto": "auto", "on": True, "off": False}[args.fill])
     stream = runner.stream
     runner.step()  # first step: eager launches (code objects load), the first copy-on-write; graphs captured
     torch.cuda.synchronize()
@@ -537,6 +538,7 @@ def decode_line(args, metric, B, L, ctx_before, group, prefix, long_items, share
         "hbm_read_probe": probe,
         "plan": {"items": int(last.n_items), "shared_items": int(last.n_shared),
                  "kv_block_reads": int(last.kv_blocks_read), "share_prefix": share, "long_items": long_items,
+                 "fill": bool(runner.fill),
                  "share_width": args.share_width},
         "check": check,
         "cpu_baseline": cpu,
@@ -1006,6 +1008,9 @@ def main():
                     help="decode workload: plans with long items (KVP_PLAN_LONG_ITEMS, which sizes parts to "
                          "one generation of waves when a batch's private blocks far exceed them and leaves "
                          "smaller batches' plans as they are); always on for long_context")
+    ap.add_argument("--fill", choices=["auto", "on", "off"], default="auto",
+                    help="plans with KVP_PLAN_FILL (parts shorter than 32 blocks while the batch leaves resident "
+                         "waves idle): on, off, or auto (batches of at most 8 request x KV-head pairs)")
     ap.add_argument("--no-scatter", action="store_true", help="hand out block ids in order (no free-list shuffle)")
     ap.add_argument("--seed", type=int, default=42)
     ap.add_argument("--workload", default="decode",

@@ -393,6 +393,16 @@ kvp_status contiguous_decode_attention(const kvp_dims *dims, void *out, const vo
  * no shared items. */
 #define KVP_PLAN_SHARE_WIDE2 4u
 #define KVP_PLAN_SHARE_WIDE4 8u
+/* Batches too small to fill the GPU (decode of one or a few requests): cut private ranges
+ * into parts shorter than the default 32 blocks, down to 8 -- the shortest part length, in
+ * whole 4-block tiles, at which the private items of every pair still fit the waves the GPU
+ * holds at once (about 1024 for fp16, 2048 for int8 caches) beside the plan's shared items.
+ * A split pair's parts are merged by the same rescale as any split (chatgpz.de
+ * "Aufmerksamkeit", FlashAttention post: block softmaxes combined through their maxima), so
+ * the chain of tiles one wave streams shortens while idle waves take the other parts.  A
+ * batch whose 32-block parts already fill the waves keeps its plan.  Changes the splits, so
+ * the result equals the unplanned call's up to the order of the fp32 sums only. */
+#define KVP_PLAN_FILL 16u
 
 typedef struct {
     int32_t B;            /* batch the plan was built for                            */

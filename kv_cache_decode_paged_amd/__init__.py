@@ -80,6 +80,7 @@ PLAN_SHARE_PREFIX = 1
 PLAN_LONG_ITEMS = 2
 PLAN_SHARE_WIDE2 = 4
 PLAN_SHARE_WIDE4 = 8
+PLAN_FILL = 16
 
 SCHED_STATIC, SCHED_CONTINUOUS = 0, 1
 ALLOC_PAGED, ALLOC_NAIVE = 0, 1
@@ -504,14 +505,15 @@ def _host_i32(t, name):
 
 def decode_plan_build(num_q_heads, num_kv_heads, block_table, context_lens, num_blocks, share_prefix=True,
                       image=None, pin=False, pad_items=0, plan=None, head_dim=HEAD_DIM, long_items=False,
-                      kv_dtype=torch.float16, share_width=1):
+                      kv_dtype=torch.float16, share_width=1, fill=False):
     """Build a decode plan on the host from the HOST block table [B, max_blocks] and context
     lengths [B] (int32 CPU tensors).  Returns (plan, image): plan is a kvp_decode_plan, image
     a uint8 CPU tensor whose first plan.bytes bytes are to be copied to the device.
     pad_items > 0 fixes the item count (see decode_plan_build in kvp.h); long_items asks for
     KVP_PLAN_LONG_ITEMS (fewer, longer parts for batches of long contexts), sized for the
     waves the kernel of kv_dtype's cache keeps resident; share_width (1, 2 or 4 blocks of 16
-    query columns) is the width of shared items (KVP_PLAN_SHARE_WIDE2 / 4).  kv_dtype (torch.float16 or
+    query columns) is the width of shared items (KVP_PLAN_SHARE_WIDE2 / 4); fill asks for
+    KVP_PLAN_FILL (shorter parts when the batch leaves resident waves idle).  kv_dtype (torch.float16 or
     torch.int8, the cache's) also sets the split size: an int8 cache at head dim 64 is cut
     into 16-block parts, as the unplanned call does, so pass it for int8 caches."""
     B, max_blocks = block_table.shape
@@ -529,7 +531,7 @@ def decode_plan_build(num_q_heads, num_kv_heads, block_table, context_lens, num_
     _check(_lib.decode_plan_build(ctypes.byref(dm), _host_i32(block_table, "block_table"), int(max_blocks),
                                   _host_i32(context_lens, "context_lens"), int(B), int(num_blocks),
                                   (PLAN_SHARE_PREFIX if share_prefix else 0) |
-                                  (PLAN_LONG_ITEMS if long_items else 0) |
+                                  (PLAN_LONG_ITEMS if long_items else 0) | (PLAN_FILL if fill else 0) |
                                   {1: 0, 2: PLAN_SHARE_WIDE2, 4: PLAN_SHARE_WIDE4}[share_width], int(pad_items),
                                   ctypes.c_void_p(image.data_ptr()), image.numel(), ctypes.byref(plan)))
     return plan, image

@@ -107,44 +107,49 @@ __device__ inline void coherent_store2(float *p, float a, float b)
     const float2 v = {a, b};
     asm volatile("global_store_dwordx2 %0, %1, off sc1" ::"v"(p), "v"(v) : "memory");
 }
-__device__ inline f32x4 coherent_load4_async(const float *p)
+// Device-coherent reads of partials other items stored (sc1: past this XCD's L2), as
+// relaxed agent-scope atomic loads of 8 bytes, so the compiler sees each load and waits for
+// it before the first use of its value.
+__device__ inline float2 coherent_load2(const float *p)
 {
-    f32x4 r;
-    asm volatile("global_load_dwordx4 %0, %1, off sc1" : "=v"(r) : "v"(p) : "memory");
-    return r;
+    const unsigned long long v =
+        __hip_atomic_load((const unsigned long long *)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return float2{__uint_as_float((unsigned)v), __uint_as_float((unsigned)(v >> 32))};
 }
-__device__ inline float2 coherent_load2_async(const float *p)
+__device__ inline f32x4 coherent_load4(const float *p)
 {
-    float2 r;
-    asm volatile("global_load_dwordx2 %0, %1, off sc1" : "=v"(r) : "v"(p) : "memory");
-    return r;
+    const float2 a = coherent_load2(p), b = coherent_load2(p + 2);
+    return f32x4{a.x, a.y, b.x, b.y};
 }
 
 // Merge, for this lane's column, the np partials of its pair (slots pbase .. pbase+np-1) in
 // slot order; the partial of slot own is this lane's registers (om, ol, oacc), the others are
 // read from memory.  Lane (col, grp) holds output dims 16 db + 4 grp + i as O[4 db + i].
-// Writes the normalised row to outp (this column's HD outputs).
+// Writes the normalised row to outp (this column's HD outputs).  The partials are read four
+// at a time, every load of a batch issued before the first is used, so a batch costs one
+// round trip.
 template <int HD>
 __device__ __forceinline__ void merge_column(const float *part, int G, int pbase, int np, int own, int hd, int grp,
                                              float om, float ol, const f32x4 (&oacc)[HD / 16], f16 *outp)
 {
     constexpr int NDB = HD / 16;
+    constexpr int NB = 4; // partials per batch (registers: NB (HD / 4 + 2))
     float M = -INFINITY, L = 0.f, O[4 * NDB];
 #pragma unroll
     for (int k = 0; k < 4 * NDB; ++k)
         O[k] = 0.f;
-    for (int j0 = 0; j0 < np; j0 += 4) {
-        f32x4 ov[4][NDB];
-        float2 ml[4];
+    for (int j0 = 0; j0 < np; j0 += NB) {
+        f32x4 ov[NB][NDB];
+        float2 ml[NB];
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
+        for (int jj = 0; jj < NB; ++jj) {
             const int j = j0 + jj;
             if (j < np && j != own) {
                 const float *src = part + ((size_t)(pbase + j) * G + hd) * part_floats(HD);
 #pragma unroll
                 for (int db = 0; db < NDB; ++db)
-                    ov[jj][db] = coherent_load4_async(src + 16 * db + 4 * grp);
-                ml[jj] = coherent_load2_async(src + HD);
+                    ov[jj][db] = coherent_load4(src + 16 * db + 4 * grp);
+                ml[jj] = coherent_load2(src + HD);
             } else {
 #pragma unroll
                 for (int db = 0; db < NDB; ++db)
@@ -152,14 +157,10 @@ __device__ __forceinline__ void merge_column(const float *part, int G, int pbase
                 ml[jj] = float2{om, ol};
             }
         }
-        wait_stores(); // the loads above have returned
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-#pragma unroll
-            for (int db = 0; db < NDB; ++db)
-                asm volatile("" : "+v"(ov[jj][db]));
-            asm volatile("" : "+v"(ml[jj]));
-            if (j0 + jj < np) {
+        for (int jj = 0; jj < NB; ++jj) {
+            const int j = j0 + jj;
+            if (j < np) {
                 float o[4 * NDB];
 #pragma unroll
                 for (int db = 0; db < NDB; ++db)

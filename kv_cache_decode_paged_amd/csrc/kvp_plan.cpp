@@ -51,7 +51,10 @@ long long max_items(long long B, long long hkv, long long max_blocks, bool i8, i
     // most 4 ipp parts when it takes 4 column blocks (then n >= 3), 2 ipp with 2 blocks and
     // ipp with one, so fewer than 2 ipp per request; plus the padding that evens out the XCD
     // queues and rounds them to whole CU rounds
-    const long long work = B * hkv * ipp + 2 * B * hkv * ipp;
+    // (KVP_PLAN_FILL: private items shorter than split_blocks only while they fit the
+    // resident waves)
+    const long long waves = i8 ? LONG_TARGET_WAVES_I8 : LONG_TARGET_WAVES_F16;
+    const long long work = std::max(B * hkv * ipp, waves) + 2 * B * hkv * ipp;
     return XCDS * ((work + XCDS - 1) / XCDS + MAX_BUNDLE + CU_SLOTS - 1);
 }
 
@@ -121,7 +124,8 @@ kvp_status decode_plan_build(const kvp_dims *dims, const int32_t *table, int32_t
         return fail(KVP_ERR_INVALID, "%s: B=%d max_blocks=%d num_blocks=%d", who, B, max_blocks, num_blocks);
     if (!plan || !h_image || (B > 0 && (!table || !ctx_lens)))
         return fail(KVP_ERR_INVALID, "%s: NULL pointer argument", who);
-    if (flags & ~(KVP_PLAN_SHARE_PREFIX | KVP_PLAN_LONG_ITEMS | KVP_PLAN_SHARE_WIDE2 | KVP_PLAN_SHARE_WIDE4))
+    if (flags & ~(KVP_PLAN_SHARE_PREFIX | KVP_PLAN_LONG_ITEMS | KVP_PLAN_SHARE_WIDE2 | KVP_PLAN_SHARE_WIDE4 |
+                  KVP_PLAN_FILL))
         return fail(KVP_ERR_INVALID, "%s: unknown flags 0x%x", who, flags);
     if ((flags & KVP_PLAN_SHARE_WIDE2) && (flags & KVP_PLAN_SHARE_WIDE4))
         return fail(KVP_ERR_INVALID, "%s: KVP_PLAN_SHARE_WIDE2 and KVP_PLAN_SHARE_WIDE4 together", who);
@@ -197,21 +201,43 @@ kvp_status decode_plan_build(const kvp_dims *dims, const int32_t *table, int32_t
                 if (BS * split_start(nsb, ns, k) < E[m])
                     ++shared_parts[m];
     }
+    long long n_shared = 0;
+    for (const SubRun &s : subs)
+        n_shared += (long long)hkv * shared_split(s.shared_tokens / BS, s.n, G, hd);
     // long items: parts of up to S blocks, S sized so the private blocks fill about one
     // generation of waves (whole tiles, between SPLIT_BLOCKS and LONG_BPI); S = SPLIT_BLOCKS
     // leaves the plan as without the flag
-    int S = split_blocks(i8, hd);
+    const long long waves = i8 ? LONG_TARGET_WAVES_I8 : LONG_TARGET_WAVES_F16;
+    const int S0 = split_blocks(i8, hd);
+    int S = S0;
     if (flags & KVP_PLAN_LONG_ITEMS) {
         long long priv_blocks = 0;
         for (int b = 0; b < B; ++b)
             priv_blocks += (long long)hkv * std::max(0, nbt[b] - E[b] / BS);
-        const long long waves = dims->dtype == KVP_I8 ? LONG_TARGET_WAVES_I8 : LONG_TARGET_WAVES_F16;
         const long long per_wave = (priv_blocks + waves - 1) / waves;
-        S = (int)std::min<long long>(LONG_BPI, std::max<long long>(split_blocks(i8, hd), (per_wave + 3) / 4 * 4));
+        S = (int)std::min<long long>(LONG_BPI, std::max<long long>(S0, (per_wave + 3) / 4 * 4));
+    }
+    // fill: the shortest parts (whole tiles, from FILL_MIN_BLOCKS) whose private items all
+    // fit the waves the shared items leave
+    if ((flags & KVP_PLAN_FILL) && S == S0) {
+        const long long avail = waves - n_shared;
+        for (int s = FILL_MIN_BLOCKS; s < S0; s += 4) {
+            long long items = 0;
+            for (int b = 0; b < B; ++b) {
+                const int nb = nbt[b] - E[b] / BS;
+                items += (long long)hkv * (nb <= 0 ? 1 : (nb + s - 1) / s);
+            }
+            if (items <= avail) {
+                S = s;
+                break;
+            }
+        }
     }
     auto private_items = [&](int b) -> int {
         const int nb = nbt[b] - E[b] / BS;
-        if (S == split_blocks(i8, hd) || nb <= unsplit_blocks(i8, hd))
+        if (S < S0) // fill
+            return nb <= 0 ? 1 : (nb + S - 1) / S;
+        if (S == S0 || nb <= unsplit_blocks(i8, hd))
             return split_parts(nb, E[b] > 0, i8, hd);
         return (nb + S - 1) / S;
     };
@@ -227,9 +253,6 @@ kvp_status decode_plan_build(const kvp_dims *dims, const int32_t *table, int32_t
             }
             n_items += private_items(b);
         }
-    long long n_shared = 0;
-    for (const SubRun &s : subs)
-        n_shared += (long long)hkv * shared_split(s.shared_tokens / BS, s.n, G, hd);
     n_items += n_shared;
     if (slots > 0x7fffffffLL || n_items > 0x7fffffffLL)
         return fail(KVP_ERR_UNSUPPORTED, "%s: plan too large", who);

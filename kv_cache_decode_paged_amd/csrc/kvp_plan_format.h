@@ -64,6 +64,8 @@ constexpr int LONG_BPI = 192; // blocks of a long item (three ids per lane)
 // workgroups per CU, eight of the int8 kernel's 18 KB, on 256 CUs
 constexpr int LONG_TARGET_WAVES_F16 = 1024;
 constexpr int LONG_TARGET_WAVES_I8 = 2048;
+// shortest private part of a KVP_PLAN_FILL plan (two tiles)
+constexpr int FILL_MIN_BLOCKS = 8;
 constexpr int MAXM = 16; // members of one shared item
 // Query columns of an item: blocks of 16 MFMA columns, at most 4 per item at head dim 64 and
 // 2 at 128.  Group size G = Hq / Hkv: up to 16 (a block holds 16 / G members of G heads; a

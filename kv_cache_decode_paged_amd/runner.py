@@ -29,6 +29,13 @@ import torch
 from . import (BLOCK, BlockPool, PagedKVCache, decode_plan_build, decode_plan_bytes, decode_plan_workspace_bytes,
                kv_copy_blocks, kvp_copy, kvp_decode_plan, paged_decode_attention_planned)
 
+# plans of at most this many (request, KV head) pairs use KVP_PLAN_FILL when fill="auto": a
+# lone request's context is then cut into 8-block parts across idle waves (one request of
+# 1024 tokens at 14q/2kv: 9.9 against 12.1 us per launch); for batches of 10 or more
+# requests the extra parts' partial stores, tickets and merge batches cost more than the
+# shorter tile chains save (batch 10: 15.8 against 14.0 us)
+FILL_AUTO_PAIRS = 8
+
 # spare items of the fixed launch size: one more round of CU slots per XCD queue (8 XCDs x
 # 32 CU slots), so plans of later steps (one token longer each) still fit
 SPARE_ITEMS = 8 * 32
@@ -49,12 +56,13 @@ class DecodeStepRunner:
     q [L, B, Hq, d], k_new / v_new [L, B, Hkv, d] (io dtype of the cache) and out
     [L, B, Hq, d] are device tensors read and written by every step.  max_blocks is the
     table width, large enough for the longest context of the last step to be run.
-    graph=False launches the layers eagerly.
+    graph=False launches the layers eagerly.  fill: True / False asks for / against
+    KVP_PLAN_FILL plans, "auto" uses them for batches of at most FILL_AUTO_PAIRS pairs.
     """
 
     def __init__(self, cache: PagedKVCache, pool: BlockPool, seqs, max_blocks, q, k_new, v_new, out,
                  share_prefix=True, long_items=False, graph=True, spare_items=SPARE_ITEMS, grow_tokens=64,
-                 share_width=1):
+                 share_width=1, fill="auto"):
         L, B = q.shape[0], q.shape[1]
         hq, hkv, d = cache.num_q_heads, cache.num_kv_heads, cache.head_dim
         if q.shape != (L, B, hq, d) or out.shape != q.shape:
@@ -68,7 +76,10 @@ class DecodeStepRunner:
         self.max_blocks = int(max_blocks)
         self.q, self.k_new, self.v_new, self.out = q, k_new, v_new, out
         self.share, self.long_items, self.use_graph = share_prefix, long_items, graph
+        if fill not in (True, False, "auto"):
+            raise ValueError("DecodeStepRunner: fill is True, False or 'auto'")
         self.share_width = share_width
+        self.fill = (B * hkv <= FILL_AUTO_PAIRS) if fill == "auto" else bool(fill)
         self.spare, self.grow = int(spare_items), int(grow_tokens)
         self.ids = torch.tensor([int(s) for s in seqs], dtype=torch.int32)
         self.cows = (kvp_copy * B)()
@@ -87,11 +98,15 @@ class DecodeStepRunner:
     def _make_layout(self, table, ctx):
         """Size the launch from a plan of the contexts grown by grow_tokens (capped by the
         table width), plus the spare items."""
-        c1 = torch.clamp(ctx + 1 + self.grow, max=self.max_blocks * BLOCK)
-        plan0, _ = decode_plan_build(self.hq, self.hkv, table, c1, self.cache.num_blocks, share_prefix=self.share,
-                                     head_dim=self.d, long_items=self.long_items, kv_dtype=self.cache.dtype,
-                                     share_width=self.share_width)
-        pad = plan0.n_items + self.spare
+        plans = []
+        # a fill plan's part length follows the batch's blocks: size for the first step too
+        for grow in ((self.grow, 0) if self.fill else (self.grow,)):
+            c1 = torch.clamp(ctx + 1 + grow, max=self.max_blocks * BLOCK)
+            plans.append(decode_plan_build(self.hq, self.hkv, table, c1, self.cache.num_blocks,
+                                           share_prefix=self.share, head_dim=self.d, long_items=self.long_items,
+                                           kv_dtype=self.cache.dtype, share_width=self.share_width,
+                                           fill=self.fill)[0])
+        pad = max(p.n_items for p in plans) + self.spare
         img_bytes = decode_plan_bytes(self.hq, self.hkv, self.B, self.max_blocks, pad, head_dim=self.d,
                                       kv_dtype=self.cache.dtype)
         self.host = [dict(table=torch.empty((self.B, self.max_blocks), dtype=torch.int32).pin_memory(),
@@ -105,8 +120,8 @@ class DecodeStepRunner:
         self.released = [torch.cuda.Event(), torch.cuda.Event()]
         self.done = [torch.cuda.Event(), torch.cuda.Event()]
         self.in_use = [False, False]
-        # partial slots: twice the first plan's, plus one per pair
-        slot_cap = 2 * plan0.n_slots + self.B * self.hkv
+        # partial slots: twice the sizing plans', plus one per pair
+        slot_cap = 2 * max(p.n_slots for p in plans) + self.B * self.hkv
         self.layout = dict(pad=pad, img_bytes=img_bytes, slot_cap=slot_cap, launch=None)
         ws_plan = kvp_decode_plan()
         ws_plan.B, ws_plan.num_kv_heads, ws_plan.n_slots, ws_plan.head_dim = self.B, self.hkv, slot_cap, self.d
@@ -166,7 +181,7 @@ class DecodeStepRunner:
         plan, _ = decode_plan_build(self.hq, self.hkv, h["table"], h["ctx"], self.cache.num_blocks,
                                     share_prefix=self.share, image=h["image"], pad_items=lay["pad"], plan=h["plan"],
                                     head_dim=self.d, long_items=self.long_items, kv_dtype=self.cache.dtype,
-                                    share_width=self.share_width)
+                                    share_width=self.share_width, fill=self.fill)
         if lay["launch"] is None:
             # launch arguments shared by every step of this layout: the plan's offsets, the
             # workspace's slot capacity and the whole id area of the buffer

@@ -144,11 +144,12 @@ def check_plan(plan, image, table, ctx, num_blocks, hq, hkv, shared_expected=Non
     return items, pbase, nparts, req_shared
 
 
-def build(table, ctx, num_blocks, hq=14, hkv=2, share=True, long_items=False, share_width=1):
+def build(table, ctx, num_blocks, hq=14, hkv=2, share=True, long_items=False, share_width=1, fill=False,
+          kv_dtype=torch.float16):
     t = torch.from_numpy(np.ascontiguousarray(table, dtype=np.int32))
     c = torch.from_numpy(np.ascontiguousarray(ctx, dtype=np.int32))
     return kvp.decode_plan_build(hq, hkv, t, c, num_blocks, share_prefix=share, long_items=long_items,
-                                 share_width=share_width)
+                                 share_width=share_width, fill=fill, kv_dtype=kv_dtype)
 
 
 def c4_tables(B, steps_done=1, seed=42):
@@ -425,3 +426,66 @@ def test_int8_plans_split_at_16_blocks():
         assert int(nparts[2 * b]) == want == int(nparts[2 * b + 1]), b
     live = items[items[:, 0] != F_EMPTY]
     assert live[:, 5].max() <= 16
+
+
+# ---- KVP_PLAN_FILL: shorter parts while the batch leaves resident waves idle ----
+
+def test_fill_cuts_a_lone_request_into_short_parts():
+    # one request of 1024 tokens, 2 KV heads: 64 blocks per pair; the default split is 2
+    # parts of 32 blocks, fill takes 8 parts of 8 blocks (16 items for 1024 waves)
+    table, ctx, nb = long_tables(1, 1024)
+    plain, image0 = build(table, ctx, nb, share=False)
+    items0, _, nparts0, _ = check_plan(plain, image0, table, ctx, nb, 14, 2)
+    assert (nparts0 == 2).all()
+    plan, image = build(table, ctx, nb, share=False, fill=True)
+    items, _, nparts, _ = check_plan(plan, image, table, ctx, nb, 14, 2)
+    live = items[items[:, 0] != F_EMPTY]
+    assert len(live) == 16 and (live[:, 5] == 8).all() and (nparts == 8).all()
+    # a short context: one 2-tile part per 8 blocks, the last part shorter
+    table, ctx, nb = long_tables(1, 200)
+    plan, image = build(table, ctx, nb, share=False, fill=True)
+    items, _, nparts, _ = check_plan(plan, image, table, ctx, nb, 14, 2)
+    assert (nparts == 2).all()
+
+
+@pytest.mark.parametrize("B", [10, 50, 100, 200])
+def test_fill_on_the_shared_prefix_workload(B):
+    table, ctx, nb, _, _ = c4_tables(B)
+    plain, image0 = build(table, ctx, nb)
+    items0, _, _, _ = check_plan(plain, image0, table, ctx, nb, 14, 2, shared_expected=True)
+    plan, image = build(table, ctx, nb, fill=True)
+    items, _, nparts, _ = check_plan(plan, image, table, ctx, nb, 14, 2, shared_expected=True)
+    live = items[items[:, 0] != F_EMPTY]
+    priv = live[live[:, 0] == 0]
+    if priv[:, 5].max() < BPI:
+        # shorter parts only while every item fits the 1024 waves at once
+        assert len(live) <= 1024 and priv[:, 5].max() >= 8
+        assert len(live) > len(items0[items0[:, 0] != F_EMPTY])
+    else:
+        # a batch whose 32-block parts fill the waves keeps its plan
+        assert plan.n_items == plain.n_items and plan.bytes == plain.bytes
+        assert torch.equal(image[: plan.bytes], image0[: plain.bytes])
+    if B <= 50:
+        assert priv[:, 5].max() == 8
+
+
+def test_fill_counts_the_int8_kernels_waves():
+    # 24 requests of 4096 tokens, 2 KV heads: 12288 private blocks.  fp16 (1024 waves) keeps
+    # 16-block parts or longer; the int8 kernel (2048 waves, 16-block default parts) takes
+    # 8-block parts only if they fit its waves
+    table, ctx, nb = long_tables(24, 4096)
+    for dt, waves in ((torch.float16, 1024), (torch.int8, 2048)):
+        plan, image = build(table, ctx, nb, share=False, fill=True, kv_dtype=dt)
+        items, _, _, _ = check_plan(plan, image, table, ctx, nb, 14, 2)
+        live = items[items[:, 0] != F_EMPTY]
+        default = 32 if dt == torch.float16 else 16
+        if live[:, 5].max() < default:
+            assert len(live) <= waves
+
+
+def test_fill_leaves_long_items_alone():
+    # the long-context batch: long items decide the parts, fill adds nothing
+    table, ctx, nb = long_tables(32, 32790)
+    a, ia = build(table, ctx, nb, share=False, long_items=True)
+    b, ib = build(table, ctx, nb, share=False, long_items=True, fill=True)
+    assert a.n_items == b.n_items and torch.equal(ia[: a.bytes], ib[: b.bytes])

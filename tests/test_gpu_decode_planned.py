@@ -21,10 +21,10 @@ def _bits(t):
     return t.contiguous().view(torch.int16)
 
 
-def _plan(step, share=True, long_items=False):
+def _plan(step, share=True, long_items=False, fill=False):
     plan, image = kvp.decode_plan_build(step.hq, step.hkv, step.table.cpu(), step.ctx.cpu(), step.num_blocks,
                                         share_prefix=share, head_dim=step.head_dim, long_items=long_items,
-                                        kv_dtype=step.dtype)
+                                        kv_dtype=step.dtype, fill=fill)
     return plan, kvp.upload_plan(plan, image)
 
 
@@ -159,4 +159,28 @@ def test_planned_long_items_match_oracle(dtype):
     assert torch.equal(_bits(o.cpu()), _bits(o2.cpu())), "repeat with the same workspace differs"
     err = max_abs(to64(o), step.oracle(0))
     say("planned long items", dtype, "items", plan.n_items, "ids", plan.n_ids, "max err", err)
+    assert err <= TOL[torch.float16]
+
+
+@pytest.mark.parametrize("B,dtype", [(1, torch.float16), (10, torch.float16), (100, torch.float16),
+                                     (10, torch.int8)])
+def test_planned_fill_matches_oracle(B, dtype):
+    # KVP_PLAN_FILL: batches that leave resident waves idle are cut into parts of 8 to 28
+    # blocks; the parts of a pair merge through the same rescale, so every request still
+    # matches the oracle (a lone request: every 8 blocks its own item)
+    need_gpu()
+    pb = W.paged_batch(B) if B > 1 else W.uniform_batch(1, 1500)
+    say("planned fill", dtype, "B", B)
+    step = PagedStep(kvp, pb, layers=1, hq=14, hkv=2, dtype=dtype, seed=9800 + B)
+    plan, dp = _plan(step, fill=True)
+    default, _ = _plan(step)
+    assert plan.n_slots > default.n_slots  # shorter parts: more of them
+    ws = kvp.make_plan_workspace(plan)
+    q = step.q(0).cuda()
+    o = kvp.paged_decode_attention_planned(step.cache, 0, q, plan, dp, workspace=ws)
+    o2 = kvp.paged_decode_attention_planned(step.cache, 0, q, plan, dp, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(_bits(o.cpu()), _bits(o2.cpu())), "repeat with the same workspace differs"
+    err = max_abs(to64(o), step.oracle(0))
+    say("planned fill B", B, dtype, "items", plan.n_items, "slots", plan.n_slots, "max err", err)
     assert err <= TOL[torch.float16]

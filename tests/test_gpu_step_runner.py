@@ -43,8 +43,8 @@ def oracle_decode_rows(q64, K64, V64, ctx):
         return np.stack(list(ex.map(one, range(B))))
 
 
-def _run_steps(B, n_steps, seed, check_layers, layers=24, graph=True, dtype=torch.float16):
-    pb = W.paged_batch(B)
+def _run_steps(B, n_steps, seed, check_layers, layers=24, graph=True, dtype=torch.float16, pb=None):
+    pb = W.paged_batch(B) if pb is None else pb
     say("step runner: batch", B, "layers", layers, "steps", n_steps, "graph", graph, "dtype", dtype)
     st = PagedStep(kvp, pb, layers=layers, hq=14, hkv=2, dtype=dtype, seed=seed, layers_with_data=check_layers,
                    take_step=False, extra_blocks=2 * B + 64)
@@ -58,7 +58,8 @@ def _run_steps(B, n_steps, seed, check_layers, layers=24, graph=True, dtype=torc
     vnew = torch.empty_like(knew)
     out = torch.empty_like(q)
     runner = DecodeStepRunner(st.cache, st.pool, st.seqs, max_blocks, q, knew, vnew, out, graph=graph,
-                              grow_tokens=n_steps + 1)
+                              grow_tokens=n_steps + 1, spare_items=256 if B >= 8 else 8)
+    say("step runner: fill plans", runner.fill)
     # the logical rows of the checked layers, extended by every step's appended row
     Lmax = max(pb.ctx_before) + n_steps
     logical = {}
@@ -86,7 +87,10 @@ def _run_steps(B, n_steps, seed, check_layers, layers=24, graph=True, dtype=torc
             say("step 0: copy-on-write pairs", cows, "plan items", rec.n_items, "shared", rec.n_shared)
             # members shorter than the prefix append into a shared block: it is copied first
             # (at most one copy per such member)
-            assert 0 < cows <= sum(1 for c in pb.ctx_before if c < pb.prefix and c % W.BLOCK != 0)
+            if pb.prefix > 0:
+                assert 0 < cows <= sum(1 for c in pb.ctx_before if c < pb.prefix and c % W.BLOCK != 0)
+            else:
+                assert cows == 0
         ctx = rec.ctx
         assert list(ctx) == [c + t + 1 for c in pb.ctx_before]
         for l in check_layers:
@@ -144,3 +148,12 @@ def test_runner_int8_cache_batch200():
     need_gpu()
     _, _, _, _, worst = _run_steps(200, 3, 9970, [0, 3], layers=4, dtype=torch.int8)
     say("runner b200 int8 worst err", worst)
+
+
+def test_runner_lone_request_fill_plans():
+    """One request of 1500 tokens: the runner's automatic fill plans cut its context into
+    8-block parts (12 per KV head, merged by the rescale); three graph-replayed steps."""
+    need_gpu()
+    _, runner, _, _, worst = _run_steps(1, 3, 9990, [0, 5], layers=6, pb=W.uniform_batch(1, 1500))
+    assert runner.fill
+    say("runner lone request worst err", worst)
