@@ -513,49 +513,51 @@ __device__ __forceinline__ void run_item(const DecodeParams &P, const Addr &A, c
             // exact fp16 integers and the row scales multiply the fp32 scores afterwards.
             // The lane's score rows 4 grp + i of block kb are the consecutive tile rows
             // 32 (kb/2) + 8 grp + 4 (kb%2) + i: their four scales are one 8-byte read.
-            u32x2 kraw[KB][KD];
-            u32x2 ksc4[KB];
+            constexpr int NK = KB * KD + KB; // K codes and their row scales: one group of reads
+            unsigned ka[NK];
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb) {
                 const int rt = 32 * (kb >> 1) + 8 * (col >> 2) + 4 * (kb & 1) + (col & 3);
 #pragma unroll
                 for (int ks = 0; ks < KD; ++ks)
-                    kraw[kb][ks] = lds_b64(kq + rt * RQ + swz8<HD>(2 * ks + (grp >> 1), rt) * 16 + (grp & 1) * 8);
-                ksc4[kb] = lds_b64(sq + 2 * (32 * (kb >> 1) + 8 * grp + 4 * (kb & 1)));
+                    ka[kb * KD + ks] = lds_addr(kq + rt * RQ + swz8<HD>(2 * ks + (grp >> 1), rt) * 16 + (grp & 1) * 8);
+                ka[KB * KD + kb] = lds_addr(sq + 2 * (32 * (kb >> 1) + 8 * grp + 4 * (kb & 1)));
             }
-            // V^T: lane (col, grp) of k-step ks reads dimension 16 db + col of tokens 32 ks +
-            // 8 grp .. + 7 (8 consecutive bytes of the dim-major block), and their 8 scales
-            u32x2 vraw8[KS][NDB];
-            i32x4 vsc[KS];
+            u32x2 kr[NK];
+            lds_read_b64<NK>(kr, ka);
+            u32x2 kraw[KB][KD];
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                vsc[ks] = lds_i128(sq + 32 * KB + 2 * (32 * ks + 8 * grp));
-#pragma unroll
-                for (int db = 0; db < NDB; ++db)
-                    vraw8[ks][db] = lds_b64(vq + (2 * ks + (grp >> 1)) * VBLK + (16 * db + col) * BS + 8 * (grp & 1));
-            }
-            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-#pragma unroll
-            for (int kb = 0; kb < KB; ++kb) {
+            for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
                 for (int ks = 0; ks < KD; ++ks)
-                    asm volatile("" : "+v"(kraw[kb][ks]));
-                asm volatile("" : "+v"(ksc4[kb]));
-            }
+                    kraw[kb][ks] = kr[kb * KD + ks];
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const unsigned w = ksc4[kb][i >> 1];
+                    const unsigned w = kr[KB * KD + kb][i >> 1];
                     kscale[kb][i] = (float)__builtin_bit_cast(f16, (unsigned short)(i & 1 ? w >> 16 : w & 0xffffu));
                 }
+            // V^T: lane (col, grp) of k-step ks reads dimension 16 db + col of tokens 32 ks +
+            // 8 grp .. + 7 (8 consecutive bytes of the dim-major block), and their 8 scales
+            static_assert(KS * NDB == 8, "8 V reads per int8 tile");
+            unsigned va[8], sa[KS];
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
-                asm volatile("" : "+v"(vsc[ks]));
+                sa[ks] = lds_addr(sq + 32 * KB + 2 * (32 * ks + 8 * grp));
 #pragma unroll
                 for (int db = 0; db < NDB; ++db)
-                    asm volatile("" : "+v"(vraw8[ks][db]));
+                    va[ks * NDB + db] = lds_addr(vq + (2 * ks + (grp >> 1)) * VBLK + (16 * db + col) * BS + 8 * (grp & 1));
             }
+            u32x2 vr[8];
+            i32x4 vsc[KS];
+            lds_read_v_i8<KS>(vr, vsc, va, sa);
+            u32x2 vraw8[KS][NDB];
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+                for (int db = 0; db < NDB; ++db)
+                    vraw8[ks][db] = vr[ks * NDB + db];
             // value rows no column may use: their scales (which can be anything) become 0
             if (!full) {
 #pragma unroll
@@ -623,14 +625,14 @@ __device__ __forceinline__ void run_item(const DecodeParams &P, const Addr &A, c
         } else {
         // K rows (A of the score MFMA): row 16 kb + col, dims 32 ks + 8 grp .. (chunk 4 ks + grp)
         const unsigned soff = (unsigned)((t % NBUF) * SLOT);
-        static_for<0, KD>([&](auto ks_) {
-            constexpr int ks = decltype(ks_)::value;
-            const unsigned base = kbase[ks] + soff;
-            static_for<0, KB>([&](auto kb_) {
-                constexpr int kb = decltype(kb_)::value;
-                kop[kb][ks] = lds_b128_at<16 * kb * RB>(base);
-            });
-        });
+        unsigned kb_t[KD], vb_t[NDB]; // the operand bases in this tile's ring slot
+#pragma unroll
+        for (int ks = 0; ks < KD; ++ks)
+            kb_t[ks] = kbase[ks] + soff;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+            vb_t[db] = vbase[db] + soff;
+        lds_read_k<KB, KD, 0, 16 * RB>(kop, kb_t);
         // V^T (A of the value MFMA) of k-step ks and dims 16 db ..: lane (col, grp) needs
         // V[token][16 db + col] for its k-slots s, token 16 (2 ks + s / 4) + 4 grp + s % 4.
         // A transposing read hands lane i of a 16-lane group half i % 4 of the 8 bytes
@@ -638,32 +640,12 @@ __device__ __forceinline__ void run_item(const DecodeParams &P, const Addr &A, c
         // token row 16 (2 ks + h) + 4 grp + L / 4, dims 16 db + 4 (L % 4) .. + 3, and the two
         // reads h = 0, 1 give slots 0-3 and 4-7.
         f16x4 vraw[KS][NDB][2];
-        static_for<0, NDB>([&](auto db_) {
-            constexpr int db = decltype(db_)::value;
-            const unsigned base = vbase[db] + soff;
-            static_for<0, KS>([&](auto ks_) {
-                constexpr int ks = decltype(ks_)::value;
-                static_for<0, 2>([&](auto h_) {
-                    constexpr int h = decltype(h_)::value;
-                    vraw[ks][db][h] = lds_tr16_b64_at<16 * (2 * ks + h) * RB>(base);
-                });
-            });
-        });
-        // every read has returned before any result is used (the empty statements tie each
-        // result to the wait)
-        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-            for (int ks = 0; ks < KD; ++ks)
-                asm volatile("" : "+v"(kop[kb][ks]));
+        lds_read_vt<KS, NDB, 0, 16 * RB>(vraw, vb_t);
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-            for (int db = 0; db < NDB; ++db) {
-                asm volatile("" : "+v"(vraw[ks][db][0]), "+v"(vraw[ks][db][1]));
+            for (int db = 0; db < NDB; ++db)
                 vop[ks][db] = __builtin_shufflevector(vraw[ks][db][0], vraw[ks][db][1], 0, 1, 2, 3, 4, 5, 6, 7);
-            }
         }
 
         // per column block: scores, softmax, values (the K and V operands serve every block)

@@ -32,46 +32,197 @@ __device__ inline int lane_int(int v, int l) { return __builtin_amdgcn_readlane(
 // LDS reads of the DMA-filled ring, issued as inline assembly.  The compiler's wait
 // insertion cannot tell these reads from reads of the slot a DMA is still filling, so for a
 // plain LDS read it waits for every outstanding vector-memory operation -- the prefetched
-// tiles included.  The ring is ordered by the explicit vmcnt waits instead; the results
-// are tied to an explicit lgkmcnt(0) before use.
+// tiles included.  The ring is ordered by the explicit vmcnt waits instead.
 __device__ inline unsigned lds_addr(const char *p)
 {
     return (unsigned)(uintptr_t)(const __attribute__((address_space(3))) char *)p;
 }
-__device__ inline f16x8 lds_b128(const char *p)
+// Groups of LDS reads issued back to back and waited for inside one asm statement, so that
+// every result is complete when the statement ends: the compiler never holds a register
+// that a read in flight is still to write (it takes an asm output as written when the
+// statement ends).  The outputs are early-clobber, so every address stays intact until
+// the group's last read has been issued.  (Reads of LDS through the compiler would each wait
+// for every load in flight, the LDS-DMA prefetch of the next tiles included.)
+// K operands of a tile: k[kb][ks] = the 16 bytes at LDS byte address base[ks] + OFF + kb STRIDE
+template <int KB, int KD, int OFF, int STRIDE>
+__device__ inline void lds_read_k(f16x8 (&k)[KB][KD], const unsigned (&base)[KD])
 {
-    f16x8 r;
-    asm volatile("ds_read_b128 %0, %1" : "=v"(r) : "v"(lds_addr(p)));
-    return r;
+    static_assert((KB == 4 && KD == 2) || (KB == 2 && KD == 4), "tile shapes of head dim 64 and 128");
+    static_assert(OFF >= 0 && OFF + (KB - 1) * STRIDE < 65536, "ds offset field");
+    if constexpr (KB == 4 && KD == 2)
+        asm volatile(
+            "ds_read_b128 %0, %8 offset:%10\n\t"
+            "ds_read_b128 %1, %8 offset:%11\n\t"
+            "ds_read_b128 %2, %8 offset:%12\n\t"
+            "ds_read_b128 %3, %8 offset:%13\n\t"
+            "ds_read_b128 %4, %9 offset:%10\n\t"
+            "ds_read_b128 %5, %9 offset:%11\n\t"
+            "ds_read_b128 %6, %9 offset:%12\n\t"
+            "ds_read_b128 %7, %9 offset:%13\n\t"
+            "s_waitcnt lgkmcnt(0)"
+            : "=&v"(k[0][0]), "=&v"(k[1][0]), "=&v"(k[2][0]), "=&v"(k[3][0]), "=&v"(k[0][1]), "=&v"(k[1][1]), "=&v"(k[2][1]), "=&v"(k[3][1])
+            : "v"(base[0]), "v"(base[1]), "i"(OFF + 0 * STRIDE), "i"(OFF + 1 * STRIDE), "i"(OFF + 2 * STRIDE), "i"(OFF + 3 * STRIDE));
+    if constexpr (KB == 2 && KD == 4)
+        asm volatile(
+            "ds_read_b128 %0, %8 offset:%12\n\t"
+            "ds_read_b128 %1, %8 offset:%13\n\t"
+            "ds_read_b128 %2, %9 offset:%12\n\t"
+            "ds_read_b128 %3, %9 offset:%13\n\t"
+            "ds_read_b128 %4, %10 offset:%12\n\t"
+            "ds_read_b128 %5, %10 offset:%13\n\t"
+            "ds_read_b128 %6, %11 offset:%12\n\t"
+            "ds_read_b128 %7, %11 offset:%13\n\t"
+            "s_waitcnt lgkmcnt(0)"
+            : "=&v"(k[0][0]), "=&v"(k[1][0]), "=&v"(k[0][1]), "=&v"(k[1][1]), "=&v"(k[0][2]), "=&v"(k[1][2]), "=&v"(k[0][3]), "=&v"(k[1][3])
+            : "v"(base[0]), "v"(base[1]), "v"(base[2]), "v"(base[3]), "i"(OFF + 0 * STRIDE), "i"(OFF + 1 * STRIDE));
 }
-__device__ inline int lds_b32(const void *p)
+
+// transposed V operands: v[ks][db][h] = ds_read_b64_tr_b16 at base[db] + OFF + (2 ks + h) STRIDE
+template <int KS, int NDB, int OFF, int STRIDE>
+__device__ inline void lds_read_vt(f16x4 (&v)[KS][NDB][2], const unsigned (&base)[NDB])
 {
-    int r;
-    asm volatile("ds_read_b32 %0, %1" : "=v"(r) : "v"(lds_addr((const char *)p)));
-    return r;
+    static_assert((KS == 2 && NDB == 4) || (KS == 1 && NDB == 8), "tile shapes of head dim 64 and 128");
+    static_assert(OFF >= 0 && OFF + (2 * KS - 1) * STRIDE < 65536, "ds offset field");
+    if constexpr (KS == 2 && NDB == 4)
+        asm volatile(
+            "ds_read_b64_tr_b16 %0, %16 offset:%20\n\t"
+            "ds_read_b64_tr_b16 %1, %16 offset:%21\n\t"
+            "ds_read_b64_tr_b16 %2, %16 offset:%22\n\t"
+            "ds_read_b64_tr_b16 %3, %16 offset:%23\n\t"
+            "ds_read_b64_tr_b16 %4, %17 offset:%20\n\t"
+            "ds_read_b64_tr_b16 %5, %17 offset:%21\n\t"
+            "ds_read_b64_tr_b16 %6, %17 offset:%22\n\t"
+            "ds_read_b64_tr_b16 %7, %17 offset:%23\n\t"
+            "ds_read_b64_tr_b16 %8, %18 offset:%20\n\t"
+            "ds_read_b64_tr_b16 %9, %18 offset:%21\n\t"
+            "ds_read_b64_tr_b16 %10, %18 offset:%22\n\t"
+            "ds_read_b64_tr_b16 %11, %18 offset:%23\n\t"
+            "ds_read_b64_tr_b16 %12, %19 offset:%20\n\t"
+            "ds_read_b64_tr_b16 %13, %19 offset:%21\n\t"
+            "ds_read_b64_tr_b16 %14, %19 offset:%22\n\t"
+            "ds_read_b64_tr_b16 %15, %19 offset:%23\n\t"
+            "s_waitcnt lgkmcnt(0)"
+            : "=&v"(v[0][0][0]), "=&v"(v[0][0][1]), "=&v"(v[1][0][0]), "=&v"(v[1][0][1]), "=&v"(v[0][1][0]), "=&v"(v[0][1][1]), "=&v"(v[1][1][0]), "=&v"(v[1][1][1]), "=&v"(v[0][2][0]), "=&v"(v[0][2][1]), "=&v"(v[1][2][0]), "=&v"(v[1][2][1]), "=&v"(v[0][3][0]), "=&v"(v[0][3][1]), "=&v"(v[1][3][0]), "=&v"(v[1][3][1])
+            : "v"(base[0]), "v"(base[1]), "v"(base[2]), "v"(base[3]), "i"(OFF + 0 * STRIDE), "i"(OFF + 1 * STRIDE), "i"(OFF + 2 * STRIDE), "i"(OFF + 3 * STRIDE));
+    if constexpr (KS == 1 && NDB == 8)
+        asm volatile(
+            "ds_read_b64_tr_b16 %0, %16 offset:%24\n\t"
+            "ds_read_b64_tr_b16 %1, %16 offset:%25\n\t"
+            "ds_read_b64_tr_b16 %2, %17 offset:%24\n\t"
+            "ds_read_b64_tr_b16 %3, %17 offset:%25\n\t"
+            "ds_read_b64_tr_b16 %4, %18 offset:%24\n\t"
+            "ds_read_b64_tr_b16 %5, %18 offset:%25\n\t"
+            "ds_read_b64_tr_b16 %6, %19 offset:%24\n\t"
+            "ds_read_b64_tr_b16 %7, %19 offset:%25\n\t"
+            "ds_read_b64_tr_b16 %8, %20 offset:%24\n\t"
+            "ds_read_b64_tr_b16 %9, %20 offset:%25\n\t"
+            "ds_read_b64_tr_b16 %10, %21 offset:%24\n\t"
+            "ds_read_b64_tr_b16 %11, %21 offset:%25\n\t"
+            "ds_read_b64_tr_b16 %12, %22 offset:%24\n\t"
+            "ds_read_b64_tr_b16 %13, %22 offset:%25\n\t"
+            "ds_read_b64_tr_b16 %14, %23 offset:%24\n\t"
+            "ds_read_b64_tr_b16 %15, %23 offset:%25\n\t"
+            "s_waitcnt lgkmcnt(0)"
+            : "=&v"(v[0][0][0]), "=&v"(v[0][0][1]), "=&v"(v[0][1][0]), "=&v"(v[0][1][1]), "=&v"(v[0][2][0]), "=&v"(v[0][2][1]), "=&v"(v[0][3][0]), "=&v"(v[0][3][1]), "=&v"(v[0][4][0]), "=&v"(v[0][4][1]), "=&v"(v[0][5][0]), "=&v"(v[0][5][1]), "=&v"(v[0][6][0]), "=&v"(v[0][6][1]), "=&v"(v[0][7][0]), "=&v"(v[0][7][1])
+            : "v"(base[0]), "v"(base[1]), "v"(base[2]), "v"(base[3]), "v"(base[4]), "v"(base[5]), "v"(base[6]), "v"(base[7]), "i"(OFF + 0 * STRIDE), "i"(OFF + 1 * STRIDE));
 }
-__device__ inline f16x4 lds_tr16_b64(const char *p)
+
+// N reads of 8 bytes: r[i] at LDS byte address a[i]
+template <int N> __device__ inline void lds_read_b64(u32x2 (&r)[N], const unsigned (&a)[N])
 {
-    f16x4 r;
-    asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(r) : "v"(lds_addr(p)));
-    return r;
+    static_assert(N == 10 || N == 12, "group sizes of the int8 tiles");
+    if constexpr (N == 10)
+        asm volatile(
+            "ds_read_b64 %0, %10\n\t"
+            "ds_read_b64 %1, %11\n\t"
+            "ds_read_b64 %2, %12\n\t"
+            "ds_read_b64 %3, %13\n\t"
+            "ds_read_b64 %4, %14\n\t"
+            "ds_read_b64 %5, %15\n\t"
+            "ds_read_b64 %6, %16\n\t"
+            "ds_read_b64 %7, %17\n\t"
+            "ds_read_b64 %8, %18\n\t"
+            "ds_read_b64 %9, %19\n\t"
+            "s_waitcnt lgkmcnt(0)"
+            : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]), "=&v"(r[7]), "=&v"(r[8]), "=&v"(r[9])
+            : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7]), "v"(a[8]), "v"(a[9]));
+    if constexpr (N == 12)
+        asm volatile(
+            "ds_read_b64 %0, %12\n\t"
+            "ds_read_b64 %1, %13\n\t"
+            "ds_read_b64 %2, %14\n\t"
+            "ds_read_b64 %3, %15\n\t"
+            "ds_read_b64 %4, %16\n\t"
+            "ds_read_b64 %5, %17\n\t"
+            "ds_read_b64 %6, %18\n\t"
+            "ds_read_b64 %7, %19\n\t"
+            "ds_read_b64 %8, %20\n\t"
+            "ds_read_b64 %9, %21\n\t"
+            "ds_read_b64 %10, %22\n\t"
+            "ds_read_b64 %11, %23\n\t"
+            "s_waitcnt lgkmcnt(0)"
+            : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]), "=&v"(r[7]), "=&v"(r[8]), "=&v"(r[9]), "=&v"(r[10]), "=&v"(r[11])
+            : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7]), "v"(a[8]), "v"(a[9]), "v"(a[10]), "v"(a[11]));
 }
-// the same reads at an LDS byte address plus an immediate offset (the instruction's own
-// 16-bit offset field): one base register serves every read that differs by a constant
-template <int OFF> __device__ inline f16x8 lds_b128_at(unsigned addr)
+
+// int8 V tile: r[i] = 8 bytes at a[i] (i < 8), s[j] = 16 bytes at b[j] (j < KS)
+template <int KS> __device__ inline void lds_read_v_i8(u32x2 (&r)[8], i32x4 (&s)[KS], const unsigned (&a)[8],
+                                                     const unsigned (&b)[KS])
 {
-    static_assert(OFF >= 0 && OFF < 65536, "ds offset field");
-    f16x8 r;
-    asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF));
-    return r;
+    static_assert(KS == 1 || KS == 2, "k-steps of an int8 tile");
+    if constexpr (KS == 1)
+        asm volatile(
+            "ds_read_b64 %0, %9\n\t"
+            "ds_read_b64 %1, %10\n\t"
+            "ds_read_b64 %2, %11\n\t"
+            "ds_read_b64 %3, %12\n\t"
+            "ds_read_b64 %4, %13\n\t"
+            "ds_read_b64 %5, %14\n\t"
+            "ds_read_b64 %6, %15\n\t"
+            "ds_read_b64 %7, %16\n\t"
+            "ds_read_b128 %8, %17\n\t"
+            "s_waitcnt lgkmcnt(0)"
+            : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]), "=&v"(r[7]), "=&v"(s[0])
+            : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7]), "v"(b[0]));
+    if constexpr (KS == 2)
+        asm volatile(
+            "ds_read_b64 %0, %10\n\t"
+            "ds_read_b64 %1, %11\n\t"
+            "ds_read_b64 %2, %12\n\t"
+            "ds_read_b64 %3, %13\n\t"
+            "ds_read_b64 %4, %14\n\t"
+            "ds_read_b64 %5, %15\n\t"
+            "ds_read_b64 %6, %16\n\t"
+            "ds_read_b64 %7, %17\n\t"
+            "ds_read_b128 %8, %18\n\t"
+            "ds_read_b128 %9, %19\n\t"
+            "s_waitcnt lgkmcnt(0)"
+            : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]), "=&v"(r[7]), "=&v"(s[0]), "=&v"(s[1])
+            : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7]), "v"(b[0]), "v"(b[1]));
 }
-template <int OFF> __device__ inline f16x4 lds_tr16_b64_at(unsigned addr)
+
+// N reads of 4 bytes: r[i] at LDS byte address a[i]
+template <int N> __device__ inline void lds_read_b32(int (&r)[N], const unsigned (&a)[N])
 {
-    static_assert(OFF >= 0 && OFF < 65536, "ds offset field");
-    f16x4 r;
-    asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF));
-    return r;
+    static_assert(N == 2 || N == 4, "group sizes of the block-id reads");
+    if constexpr (N == 2)
+        asm volatile(
+            "ds_read_b32 %0, %2\n\t"
+            "ds_read_b32 %1, %3\n\t"
+            "s_waitcnt lgkmcnt(0)"
+            : "=&v"(r[0]), "=&v"(r[1])
+            : "v"(a[0]), "v"(a[1]));
+    if constexpr (N == 4)
+        asm volatile(
+            "ds_read_b32 %0, %4\n\t"
+            "ds_read_b32 %1, %5\n\t"
+            "ds_read_b32 %2, %6\n\t"
+            "ds_read_b32 %3, %7\n\t"
+            "s_waitcnt lgkmcnt(0)"
+            : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3])
+            : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]));
 }
+
 // compile-time loop: f(integral_constant<int, I>) for I = B .. E - 1
 template <int B, int E, typename F> __device__ __forceinline__ void static_for(F &&f)
 {
@@ -95,24 +246,6 @@ __device__ inline void lds_store_b16(char *p, unsigned v)
 __device__ inline void lds_store_b8(char *p, unsigned v)
 {
     asm volatile("ds_write_b8 %0, %1" ::"v"(lds_addr(p)), "v"(v) : "memory");
-}
-__device__ inline u32x2 lds_b64(const char *p)
-{
-    u32x2 r;
-    asm volatile("ds_read_b64 %0, %1" : "=v"(r) : "v"(lds_addr(p)));
-    return r;
-}
-__device__ inline i32x4 lds_i128(const char *p)
-{
-    i32x4 r;
-    asm volatile("ds_read_b128 %0, %1" : "=v"(r) : "v"(lds_addr(p)));
-    return r;
-}
-__device__ inline unsigned lds_u16(const char *p)
-{
-    unsigned r;
-    asm volatile("ds_read_u16 %0, %1" : "=v"(r) : "v"(lds_addr(p)));
-    return r;
 }
 
 // maximum of three as one v_max3_f32 (fmaxf would first quiet each operand, a

@@ -181,20 +181,18 @@ __global__ __launch_bounds__(256) void prefill_mfma_f16_kernel(PrefillArgs P)
         char *kd = kring + (t % NBUF) * SLOT;
         char *vd = vring + (t % NBUF) * SLOT;
         int kk[LPW], e[LPW];
+        unsigned ea[LPW];
 #pragma unroll
         for (int ii = 0; ii < LPW; ++ii) {
             const int r = RPI * (LPW * wave + ii) + lane / CPR;
             kk[ii] = min(t * KT + r, kend - 1); // beyond kend every row of the workgroup masks the key
             e[ii] = 0;
+            ea[ii] = 0;
             if constexpr (PAGED)
-                e[ii] = lds_b32(&ids[kk[ii] >> 4]);
+                ea[ii] = lds_addr((const char *)&ids[kk[ii] >> 4]);
         }
-        if constexpr (PAGED) {
-            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-#pragma unroll
-            for (int ii = 0; ii < LPW; ++ii)
-                asm volatile("" : "+v"(e[ii]));
-        }
+        if constexpr (PAGED)
+            lds_read_b32<LPW>(e, ea);
 #pragma unroll
         for (int ii = 0; ii < LPW; ++ii) {
             const int i = LPW * wave + ii;
@@ -270,42 +268,21 @@ __global__ __launch_bounds__(256) void prefill_mfma_f16_kernel(PrefillArgs P)
         if (!any)
             continue;
         const unsigned soff = (unsigned)((t % NBUF) * SLOT);
+        unsigned kb_t[KD], vb_t[NDB]; // the operand bases in this tile's ring slot
+#pragma unroll
+        for (int ks = 0; ks < KD; ++ks)
+            kb_t[ks] = kbase[ks] + soff;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+            vb_t[db] = vbase[db] + soff;
         // K rows (A of the score MFMA): key 16 kb + col, dims 32 ks + 8 grp .. (chunk 4 ks + grp)
         f16x8 kop[KB][KD];
-        static_for<0, KD>([&](auto ks_) {
-            constexpr int ks = decltype(ks_)::value;
-            const unsigned base = kbase[ks] + soff;
-            static_for<0, KB>([&](auto kb_) {
-                constexpr int kb = decltype(kb_)::value;
-                kop[kb][ks] = lds_b128_at<16 * kb * RB>(base);
-            });
-        });
+        lds_read_k<KB, KD, 0, 16 * RB>(kop, kb_t);
         // V^T (A of the value MFMA), k-step ks, dims 16 db ..: lane L of group grp addresses
         // key row 16 (2 ks + h) + 4 grp + L / 4, dims 16 db + 4 (L % 4); the transposing
         // read hands lane i element j = half i % 4 of lane 4 j + i / 4's 8 bytes
         f16x4 vraw[KS][NDB][2];
-        static_for<0, NDB>([&](auto db_) {
-            constexpr int db = decltype(db_)::value;
-            const unsigned base = vbase[db] + soff;
-            static_for<0, KS>([&](auto ks_) {
-                constexpr int ks = decltype(ks_)::value;
-                static_for<0, 2>([&](auto hh_) {
-                    constexpr int hh = decltype(hh_)::value;
-                    vraw[ks][db][hh] = lds_tr16_b64_at<16 * (2 * ks + hh) * RB>(base);
-                });
-            });
-        });
-        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-            for (int ks = 0; ks < KD; ++ks)
-                asm volatile("" : "+v"(kop[kb][ks]));
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-            for (int db = 0; db < NDB; ++db)
-                asm volatile("" : "+v"(vraw[ks][db][0]), "+v"(vraw[ks][db][1]));
+        lds_read_vt<KS, NDB, 0, 16 * RB>(vraw, vb_t);
         f16x8 vop[KS][NDB];
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
@@ -337,15 +314,14 @@ __global__ __launch_bounds__(256) void prefill_mfma_f16_kernel(PrefillArgs P)
                 if constexpr (PAGED) {
                     if (!all_ok) { // keys of unusable blocks are masked
                         int e4[KB];
+                        unsigned a4[KB];
 #pragma unroll
                         for (int kb = 0; kb < KB; ++kb)
-                            e4[kb] = lds_b32(&ids[min((k0 >> 4) + kb, MAX_IDS - 1)]);
-                        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+                            a4[kb] = lds_addr((const char *)&ids[min((k0 >> 4) + kb, MAX_IDS - 1)]);
+                        lds_read_b32<KB>(e4, a4);
 #pragma unroll
-                        for (int kb = 0; kb < KB; ++kb) {
-                            asm volatile("" : "+v"(e4[kb]));
+                        for (int kb = 0; kb < KB; ++kb)
                             bok[kb] = e4[kb] >= 0;
-                        }
                     }
                 }
 #pragma unroll
