@@ -177,9 +177,34 @@ __global__ __launch_bounds__(256) void prefill_mfma_f16_kernel(PrefillArgs P)
     // swz(c, r) holds chunk c); rows past the workgroup's last visible key re-read that
     // key's row (they are masked; its block id is staged), an unusable block reads block 0
     // (masked too) ----
+    // lane part of an interior tile's packed K/V offsets: row r of the tile is key t KT + r,
+    // at element (a + t KT) hkv D + (r hkv + g) D + 8 chunk, whose first term is the same for
+    // every lane of the workgroup
+    int lane_off[LPW];
+#pragma unroll
+    for (int ii = 0; ii < LPW; ++ii) {
+        const int r = RPI * (LPW * wave + ii) + lane / CPR;
+        lane_off[ii] = (r * hkv + g_kv) * D + swz<D>(lane & (CPR - 1), r) * 8;
+    }
     auto issue = [&](int t) {
         char *kd = kring + (t % NBUF) * SLOT;
         char *vd = vring + (t % NBUF) * SLOT;
+        if (!PAGED && (t + 1) * KT <= kend) {
+            // every row of the tile is a key the workgroup sees: no clamp, no block ids
+            const size_t tb = (size_t)(a + t * KT) * hkv * D;
+            const f16 *kt = P.k + tb, *vt = P.v + tb;
+#pragma unroll
+            for (int ii = 0; ii < LPW; ++ii) {
+                const int i = LPW * wave + ii;
+                __builtin_amdgcn_global_load_lds((const void *)(kt + lane_off[ii]),
+                                                 (__attribute__((address_space(3))) void *)(kd + i * 1024), 16, 0,
+                                                 0);
+                __builtin_amdgcn_global_load_lds((const void *)(vt + lane_off[ii]),
+                                                 (__attribute__((address_space(3))) void *)(vd + i * 1024), 16, 0,
+                                                 0);
+            }
+            return;
+        }
         int kk[LPW], e[LPW];
         unsigned ea[LPW];
 #pragma unroll
