@@ -14,6 +14,10 @@ LIB = os.path.join(PKG, "libkvp.so")
 SOURCES = ["kvp_manager.cpp", "kvp_plan.cpp", "kvp_sched.cpp", "kvp_cache_ops.hip", "kvp_decode.hip", "kvp_decode_f16.hip",
            "kvp_decode_f32.hip", "kvp_prefill.hip", "kvp_probe.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+# per-source flags: the decode kernels take the plan-record pointer as their first argument
+# and have the dispatcher preload it (two SGPRs), so a wave's first instruction is its record
+# load rather than a kernel-argument fetch
+EXTRA_FLAGS = {"kvp_decode_f16.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=2"]}
 ARCH = "gfx950"
 
 
@@ -36,7 +40,7 @@ def build(verbose=False, jobs=4):
         obj = os.path.join(CSRC, "_build", src + ".o")
         os.makedirs(os.path.dirname(obj), exist_ok=True)
         lang = ["-x", "hip"] if src.endswith(".hip") else []
-        cmd = [HIPCC] + hip_flags() + lang + ["-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [HIPCC] + hip_flags() + EXTRA_FLAGS.get(src, []) + lang + ["-c", os.path.join(CSRC, src), "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
         procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)))

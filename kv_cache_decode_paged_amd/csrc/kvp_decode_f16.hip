@@ -261,40 +261,6 @@ __device__ __forceinline__ void run_item(const DecodeParams &P, const Addr &A, c
             qop[cb][ks] = cv[cb] ? qv : z;
         }
     }
-    // lim: tokens >= lim are masked for this row; rows whose results are not kept (padding
-    // columns, members that do not take part) have no limit -- their columns of the MFMA
-    // tiles are independent of the others and are never stored
-    int lim[NCB], pb[NCB], np[NCB];
-#pragma unroll
-    for (int cb = 0; cb < NCB; ++cb) {
-        if constexpr (SHARED) {
-            // a member takes part if its shared extent reaches into this item; its part index
-            // inside the pair's slot range is the item's R_SLOT
-            const int pair = bm[cb] * hkv + it.g;
-            const int l0 = PV.req_shared[bm[cb]], b0 = PV.pair_base[pair], n0 = PV.pair_nparts[pair];
-            const bool in = cv[cb] && l0 > BS * it.blk0;
-            lim[cb] = in ? l0 : 0x7fffffff;
-            pb[cb] = b0 + it.slot;
-            np[cb] = in ? n0 : 0;
-        } else {
-            lim[cb] = cv[cb] ? it.end : 0x7fffffff;
-            pb[cb] = it.slot;
-            np[cb] = it.nparts;
-        }
-    }
-    // tokens >= rend hold no data for any column of this item
-    const int rend = SHARED ? BS * (it.blk0 + it.nblk) : it.end;
-    // a tile ending at or before full_end needs no masking (when all its blocks are valid)
-    int full_end = rend;
-    if constexpr (SHARED) {
-        // member cb mpb + j's limit sits in block cb, lane j G
-#pragma unroll
-        for (int cb = 0; cb < NCB; ++cb)
-            for (int j = 0; j < mpb; ++j)
-                if (cb * mpb + j < it.nmem)
-                    full_end = min(full_end, lane_int(lim[cb], j * G));
-    }
-
     // the step's new K / V row (lanes 0 .. CPR-1: K chunks, CPR .. 2 CPR-1: V chunks)
     const bool app = !SHARED && P.k_new != nullptr;
     i32x4 nrow = {0, 0, 0, 0};
@@ -306,16 +272,6 @@ __device__ __forceinline__ void run_item(const DecodeParams &P, const Addr &A, c
         const size_t off = (((size_t)it.b * hkv + it.g) * HD + (lane & (CPR - 1)) * 8) * sizeof(f16);
         nrow = *(const __attribute__((address_space(1))) i32x4 *)(base + off);
     }
-    // int8: the new rows' codes and scales (lanes of one row exchange its maximum)
-    u32x2 ncodes = {0u, 0u};
-    unsigned nscale = 0;
-    if constexpr (I8) {
-        if (app) {
-            const f16 s16 = quantize_row_piece<CPR>(__builtin_bit_cast(f16x8, nrow), ncodes);
-            nscale = __builtin_bit_cast(unsigned short, s16);
-        }
-    }
-
     const int nt = (it.nblk + KB - 1) / KB;
     auto ent = [&](int j) -> int {
         if constexpr (LONGI) {
@@ -377,6 +333,76 @@ __device__ __forceinline__ void run_item(const DecodeParams &P, const Addr &A, c
                                              16, 0, 0);
         }
     };
+
+    // shared items: each member's shared extent and slot range (loaded before the first DMA,
+    // so that waiting for them does not also wait for the tile)
+    int l0v[NCB], b0v[NCB], n0v[NCB];
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) {
+        l0v[cb] = 0;
+        b0v[cb] = 0;
+        n0v[cb] = 0;
+        if constexpr (SHARED) {
+            const int pair = bm[cb] * hkv + it.g;
+            l0v[cb] = PV.req_shared[bm[cb]];
+            b0v[cb] = PV.pair_base[pair];
+            n0v[cb] = PV.pair_nparts[pair];
+        }
+    }
+    // The first NBUF tiles' DMA (one per ring slot) goes out as soon as the item's addresses
+    // are known, before anything waits for a load: the column limits and the new row's
+    // quantization are not needed before the first tile is computed.  The tiles are issued
+    // even past the item's end (their rows then come from the readable block and are unused),
+    // so that every path has the same loads in flight and one wait covers the loads issued
+    // before them (q operands, the new row, the members' extents) without waiting for a tile.
+#pragma unroll
+    for (int k = 0; k < NBUF; ++k)
+        issue(k);
+    wait_vm<NBUF * NDMA>();
+    __builtin_amdgcn_sched_barrier(0);
+
+    // lim: tokens >= lim are masked for this row; rows whose results are not kept (padding
+    // columns, members that do not take part) have no limit -- their columns of the MFMA
+    // tiles are independent of the others and are never stored
+    int lim[NCB], pb[NCB], np[NCB];
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) {
+        if constexpr (SHARED) {
+            // a member takes part if its shared extent reaches into this item; its part index
+            // inside the pair's slot range is the item's R_SLOT
+            const int l0 = l0v[cb], b0 = b0v[cb], n0 = n0v[cb];
+            const bool in = cv[cb] && l0 > BS * it.blk0;
+            lim[cb] = in ? l0 : 0x7fffffff;
+            pb[cb] = b0 + it.slot;
+            np[cb] = in ? n0 : 0;
+        } else {
+            lim[cb] = cv[cb] ? it.end : 0x7fffffff;
+            pb[cb] = it.slot;
+            np[cb] = it.nparts;
+        }
+    }
+    // tokens >= rend hold no data for any column of this item
+    const int rend = SHARED ? BS * (it.blk0 + it.nblk) : it.end;
+    // a tile ending at or before full_end needs no masking (when all its blocks are valid)
+    int full_end = rend;
+    if constexpr (SHARED) {
+        // member cb mpb + j's limit sits in block cb, lane j G
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb)
+            for (int j = 0; j < mpb; ++j)
+                if (cb * mpb + j < it.nmem)
+                    full_end = min(full_end, lane_int(lim[cb], j * G));
+    }
+
+    // int8: the new rows' codes and scales (lanes of one row exchange its maximum)
+    u32x2 ncodes = {0u, 0u};
+    unsigned nscale = 0;
+    if constexpr (I8) {
+        if (app) {
+            const f16 s16 = quantize_row_piece<CPR>(__builtin_bit_cast(f16x8, nrow), ncodes);
+            nscale = __builtin_bit_cast(unsigned short, s16);
+        }
+    }
 
     // running state of this lane's column in each block: reference max (scaled, log2 units),
     // output O^T rows 16 db + 4 grp + i, and the row sum (every entry of accl holds it)
@@ -740,13 +766,9 @@ __device__ __forceinline__ void run_item(const DecodeParams &P, const Addr &A, c
         wave_lds_sync();
     };
 
-    // ---- stream the item's tiles, NBUF-1 ahead ----
-#pragma unroll
-    for (int k = 0; k < NBUF - 1; ++k)
-        if (k < nt)
-            issue(k);
+    // ---- stream the item's tiles, NBUF-1 ahead (tiles 0 .. NBUF-1 are already issued) ----
     for (int t = 0; t < nt; ++t) {
-        if (t + NBUF - 1 < nt)
+        if (t >= 1 && t + NBUF - 1 < nt)
             issue(t + NBUF - 1);
         const int ahead = min(nt - 1 - t, NBUF - 1); // tiles issued after this one
         if (ahead >= 3)
@@ -759,6 +781,8 @@ __device__ __forceinline__ void run_item(const DecodeParams &P, const Addr &A, c
             wait_vm<0>();
         compute(t);
     }
+    if (nt == 0)
+        wait_vm<0>(); // the unused tiles have landed before the wave goes on
 
     // ---- results ----
     // Rows of an unsplit pair are normalised and written.  A pair split over several items
@@ -898,7 +922,9 @@ __device__ __forceinline__ void dispatch_private(const DecodeParams &P, const Ad
 }
 
 template <int MAXNCB, int NBUF, int TT, int HD, bool I8, bool PLANNED, typename Addr>
-__global__ __launch_bounds__(64) void decode_f16_kernel(DecodeParams P, Addr A, PlanView PV)
+// items0 = PV.items, passed first so that the dispatcher preloads it into SGPRs (built with
+// kernel-argument preloading): a wave's plan record load is its first instruction.
+__global__ __launch_bounds__(64) void decode_f16_kernel(const int *items0, DecodeParams P, Addr A, PlanView PV)
 {
     static_assert(NBUF >= 2 && NBUF <= 4, "ring depth");
     constexpr int EB = I8 ? 1 : 2; // bytes per cached value
@@ -910,8 +936,14 @@ __global__ __launch_bounds__(64) void decode_f16_kernel(DecodeParams P, Addr A, 
     Item it;
     int rv;
     if constexpr (PLANNED) {
-        const int *rec = PV.items + (size_t)blockIdx.x * REC;
-        rv = lane < REC ? rec[lane] : -1;
+        const int *rec = items0 + (size_t)blockIdx.x * REC;
+        rv = rec[min(lane, REC - 1)]; // every lane loads (no branch); lanes >= REC are unused
+        rv = lane < REC ? rv : -1;
+        // the scalar parameters the item needs before its first DMA, fetched while the record
+        // is in flight (the compiler would fetch each batch where it is first used, after the
+        // record has arrived)
+        asm volatile("" ::"s"(P.B), "s"(P.hkv), "s"(P.hq), "s"(P.group), "s"(P.q), "s"(P.kc), "s"(P.vc),
+                     "s"(P.k_new), "s"(P.v_new), "s"(A.num_blocks), "s"(A.hkv), "s"(P.scale_log2));
         const int flags = lane_int(rv, R_FLAGS);
         it.b = lane_int(rv, R_B);
         it.g = lane_int(rv, R_G);
@@ -1004,17 +1036,17 @@ static void launch_width(const DecodeParams &P, const Addr &A, const PlanView &P
         if constexpr (Addr::paged) {
             if (P.dim == 64)
                 hipLaunchKernelGGL((decode_f16_kernel<MAXNCB, DEC_NBUF, DEC_TT, 64, true, PLANNED, Addr>), g, block, 0,
-                                   st, P, A, PV);
+                                   st, PV.items, P, A, PV);
             else
-                hipLaunchKernelGGL((decode_f16_kernel<MAXNCB, 2, 32, 128, true, PLANNED, Addr>), g, block, 0, st, P, A,
+                hipLaunchKernelGGL((decode_f16_kernel<MAXNCB, 2, 32, 128, true, PLANNED, Addr>), g, block, 0, st, PV.items, P, A,
                                    PV);
         }
     } else {
         if (P.dim == 64)
             hipLaunchKernelGGL((decode_f16_kernel<MAXNCB, DEC_NBUF, DEC_TT, 64, false, PLANNED, Addr>), g, block, 0, st,
-                               P, A, PV);
+                               PV.items, P, A, PV);
         else
-            hipLaunchKernelGGL((decode_f16_kernel<MAXNCB, 2, 32, 128, false, PLANNED, Addr>), g, block, 0, st, P, A,
+            hipLaunchKernelGGL((decode_f16_kernel<MAXNCB, 2, 32, 128, false, PLANNED, Addr>), g, block, 0, st, PV.items, P, A,
                                PV);
     }
 }
