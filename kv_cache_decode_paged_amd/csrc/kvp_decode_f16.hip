@@ -817,7 +817,7 @@ __device__ __forceinline__ void run_item(const DecodeParams &P, const Addr &A, c
     int pbase[NCB], own;
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb)
-        pbase[cb] = SHARED ? PV.pair_base[bm[cb] * hkv + it.g] : it.pbase;
+        pbase[cb] = SHARED ? b0v[cb] : it.pbase; // shared: loaded with the member extents
     own = SHARED ? it.slot : it.slot - it.pbase;
     if constexpr (!SHARED) {
         if (P.merge_polls > 0 && own == np[0] - 1) {

@@ -42,6 +42,27 @@ def test_planned_without_sharing_is_bit_identical():
     assert torch.equal(_bits(o_plan.cpu()), _bits(o_plain.cpu()))
 
 
+@pytest.mark.parametrize("dtype", ["float16", "int8"])
+def test_planned_ragged_edges_are_bit_identical(dtype):
+    """Contexts at and around tile and part boundaries, an empty one included (its item has no
+    tile of its own to stream): a plan without sharing reproduces the unplanned call's splits,
+    so the outputs are equal bit for bit, and they match the oracle."""
+    need_gpu()
+    ctxs = [0, 1, 15, 16, 17, 63, 64, 65, 255, 256, 257, 511, 512, 513, 1025, 2049]
+    pb = W.PagedBatch(ctx_before=ctxs, group=list(range(len(ctxs))), prefix=0, group_size=1)
+    say("planned ragged edges", dtype, ctxs)
+    step = PagedStep(kvp, pb, layers=1, hq=14, hkv=2, dtype=getattr(torch, dtype), seed=9150)
+    plan, dp = _plan(step, share=False)
+    q = step.q(0).cuda()
+    o_plain = kvp.paged_decode_attention(step.cache, 0, q, step.table, step.ctx)
+    o_plan = kvp.paged_decode_attention_planned(step.cache, 0, q, plan, dp)
+    torch.cuda.synchronize()
+    assert torch.equal(_bits(o_plan.cpu()), _bits(o_plain.cpu()))
+    err = max_abs(to64(o_plan), step.oracle(0))
+    say("planned ragged", dtype, "max err", err)
+    assert err <= TOL[torch.float16]
+
+
 @pytest.mark.parametrize("B", [10, 50, 100])
 def test_planned_shared_prefix_matches_oracle(B):
     need_gpu()
