@@ -14,8 +14,10 @@
 // fp16: one workgroup = 4 wave64 = 64 NQB query rows of one (segment, query head).  Wave w
 // owns NQB blocks of 16 rows, rows q0 + 64 nb + 16 w, so the four waves reach the causal
 // diagonal together and share every K/V tile.  K and V tiles of KT keys stream HBM -> LDS
-// through global_load_lds into a 3-slot ring (one barrier per tile); each wave reads a
-// tile's K rows and its transposed V once and uses them for all of its blocks.  Head dim
+// through global_load_lds into a ring of 4 slots, two tiles ahead of the one computed (paged
+// keys: 3 slots, one ahead, since their staged block ids take LDS too; one barrier per
+// tile); each wave reads a tile's K rows and its transposed V once and uses them for all of
+// its blocks.  Head dim
 // 64: NQB = 4, KT = 64; head dim 128: NQB = 2, KT = 32 (the operands of twice the width in
 // the same register budget, and the same 8 KB K or V tile):
 //   scores  S^T = K Q^T       v_mfma_f32_16x16x32_f16, one query row per MFMA column
@@ -45,7 +47,6 @@ typedef int i32x2 __attribute__((ext_vector_type(2)));
 namespace pf {
 constexpr int D = 64;        // head dim of the fp32 kernel
 constexpr int BS = 16;       // tokens per cache block
-constexpr int NBUF = 3;      // ring slots for K and for V
 constexpr float LOG2E = 1.4426950408889634f;
 
 // tiling of the fp16 kernel by head dim HD
@@ -93,6 +94,7 @@ template <bool PAGED, int D>
 __global__ __launch_bounds__(256) void prefill_mfma_f16_kernel(PrefillArgs P)
 {
     using namespace pf;
+    constexpr int NB = PAGED ? 3 : 4; // ring slots (paged: the block ids take LDS too)
     using T_ = Tiles<D>;
     constexpr int NQB = T_::NQB, QB = T_::QB, KT = T_::KT, RB = T_::RB, SLOT = T_::SLOT;
     constexpr int LPW = T_::LPW, NDMA = T_::NDMA;
@@ -102,11 +104,12 @@ __global__ __launch_bounds__(256) void prefill_mfma_f16_kernel(PrefillArgs P)
     constexpr int KS = KT / 32;   // 32-key steps per tile (value product)
     constexpr int KD = D / 32;    // 32-dim steps (score product)
     constexpr int NDB = D / 16;   // 16-dim blocks of the output
-    // one barrier per tile: the DMA of tile t + 2 refills the slot of tile t - 1, so three
-    // slots are the minimum
-    static_assert(NBUF >= 3, "ring of at least three slots");
-    __shared__ __attribute__((aligned(16))) char kring[NBUF * SLOT];
-    __shared__ __attribute__((aligned(16))) char vring[NBUF * SLOT];
+    // one barrier per tile: the DMA of tile t + NB - 1 refills the slot of tile t - 1, so
+    // three slots are the minimum; four keep two tiles in flight (two workgroups of 64 KB fit
+    // a CU's LDS, which the paged kernel's staged block ids would overflow)
+    static_assert(NB >= 3 && NB <= 4, "ring of three or four slots");
+    __shared__ __attribute__((aligned(16))) char kring[NB * SLOT];
+    __shared__ __attribute__((aligned(16))) char vring[NB * SLOT];
     __shared__ int ids[PAGED ? MAX_IDS : 1];
     __shared__ int ids_bad;
 
@@ -172,7 +175,7 @@ __global__ __launch_bounds__(256) void prefill_mfma_f16_kernel(PrefillArgs P)
         all_ok = ids_bad == 0;
     }
 
-    // ---- DMA of tile t into ring slot t % NBUF: wave w loads the tile's 1 KB pieces
+    // ---- DMA of tile t into ring slot t % NB: wave w loads the tile's 1 KB pieces
     // LPW w .. LPW w + LPW - 1 of K and of V (RPI rows each; LDS row r, chunk slot
     // swz(c, r) holds chunk c); rows past the workgroup's last visible key re-read that
     // key's row (they are masked; its block id is staged), an unusable block reads block 0
@@ -187,8 +190,8 @@ __global__ __launch_bounds__(256) void prefill_mfma_f16_kernel(PrefillArgs P)
         lane_off[ii] = (r * hkv + g_kv) * D + swz<D>(lane & (CPR - 1), r) * 8;
     }
     auto issue = [&](int t) {
-        char *kd = kring + (t % NBUF) * SLOT;
-        char *vd = vring + (t % NBUF) * SLOT;
+        char *kd = kring + (t % NB) * SLOT;
+        char *vd = vring + (t % NB) * SLOT;
         if (!PAGED && (t + 1) * KT <= kend) {
             // every row of the tile is a key the workgroup sees: no clamp, no block ids
             const size_t tb = (size_t)(a + t * KT) * hkv * D;
@@ -272,19 +275,21 @@ __global__ __launch_bounds__(256) void prefill_mfma_f16_kernel(PrefillArgs P)
         vbase[db] = lds_addr(vring) + row * RB + swz<D>(ch, row) * 16 + (col & 1) * 8;
     }
 
-    issue(0);
-    if (nt > 1)
-        issue(1);
+    for (int k = 0; k < NB - 1 && k < nt; ++k)
+        issue(k);
     for (int t = 0; t < nt; ++t) {
         // this wave's loads of tile t have landed; after the barrier every wave's have, and
         // every wave has finished reading tile t - 1, whose slot the next DMA refills
-        if (t + 1 < nt)
+        const int ahead = min(nt - 1 - t, NB - 2); // tiles issued after tile t
+        if (ahead >= 2)
+            wait_vm<2 * NDMA>();
+        else if (ahead == 1)
             wait_vm<NDMA>();
         else
             wait_vm<0>();
         block_barrier();
-        if (t + 2 < nt)
-            issue(t + 2);
+        if (t + NB - 1 < nt)
+            issue(t + NB - 1);
         const int k0 = t * KT;
         bool any = false;
 #pragma unroll
@@ -292,7 +297,7 @@ __global__ __launch_bounds__(256) void prefill_mfma_f16_kernel(PrefillArgs P)
             any = any || (r0[nb] < n && (!causal || k0 <= off + r0[nb] + 15));
         if (!any)
             continue;
-        const unsigned soff = (unsigned)((t % NBUF) * SLOT);
+        const unsigned soff = (unsigned)((t % NB) * SLOT);
         unsigned kb_t[KD], vb_t[NDB]; // the operand bases in this tile's ring slot
 #pragma unroll
         for (int ks = 0; ks < KD; ++ks)
