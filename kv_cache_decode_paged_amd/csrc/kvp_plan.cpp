@@ -86,14 +86,15 @@ struct SubRun {
 
 // Parts of a shared range of nsb blocks read for n members at group size G: an item scores
 // each tile against ncb blocks of 16 query columns (ncb = 1, 2 or 4), so its work per tile
-// grows with ncb; its length is cut to BPI / ncb blocks to keep items of equal work.
-int shared_split(int nsb, int n, int G, int hd)
+// grows with ncb; its length is cut to split_blocks / ncb blocks (the private parts' length
+// over ncb) to keep items of equal work.
+int shared_split(int nsb, int n, int G, int hd, bool i8)
 {
     const int mpb = G <= 16 ? 16 / G : 1;
     int ncb = (n + mpb - 1) / mpb;
     ncb = ncb <= 1 ? 1 : (ncb <= 2 ? 2 : 4);
     ncb = std::min(ncb, max_col_blocks(hd));
-    const int len = BPI / ncb;
+    const int len = split_blocks(i8, hd) / ncb;
     return nsb <= 0 ? 1 : (nsb + len - 1) / len;
 }
 
@@ -195,7 +196,7 @@ kvp_status decode_plan_build(const kvp_dims *dims, const int32_t *table, int32_t
     std::vector<int> shared_parts(B, 0);
     for (const SubRun &sr : subs) {
         const int nsb = sr.shared_tokens / BS;
-        const int ns = shared_split(nsb, sr.n, G, hd);
+        const int ns = shared_split(nsb, sr.n, G, hd, i8);
         for (int m = sr.a; m < sr.a + sr.n; ++m)
             for (int k = 0; k < ns; ++k)
                 if (BS * split_start(nsb, ns, k) < E[m])
@@ -203,7 +204,7 @@ kvp_status decode_plan_build(const kvp_dims *dims, const int32_t *table, int32_t
     }
     long long n_shared = 0;
     for (const SubRun &s : subs)
-        n_shared += (long long)hkv * shared_split(s.shared_tokens / BS, s.n, G, hd);
+        n_shared += (long long)hkv * shared_split(s.shared_tokens / BS, s.n, G, hd, i8);
     // long items: parts of up to S blocks, S sized so the private blocks fill about one
     // generation of waves (whole tiles, between SPLIT_BLOCKS and LONG_BPI); S = SPLIT_BLOCKS
     // leaves the plan as without the flag
@@ -298,7 +299,7 @@ kvp_status decode_plan_build(const kvp_dims *dims, const int32_t *table, int32_t
         std::vector<std::pair<long long, long long>> keyed; // (run * hkv + g, item)
         for (const SubRun &sr : subs) {
             const int nsb = sr.shared_tokens / BS;
-            const int ns = shared_split(nsb, sr.n, G, hd);
+            const int ns = shared_split(nsb, sr.n, G, hd, i8);
             for (int g = 0; g < hkv; ++g)
                 for (int k = 0; k < ns; ++k) {
                     const int b0 = split_start(nsb, ns, k), b1 = split_start(nsb, ns, k + 1);
