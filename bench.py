@@ -436,12 +436,16 @@ def decode_line(args, metric, B, L, ctx_before, group, prefix, long_items, share
     # warm: steps back to back, the host planning of step k + 1 beside the device work of k
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
     records = []
+    host = np.zeros((args.steps, 2))  # host seconds of prepare() and launch() per step
     t0 = time.perf_counter()
     for s in range(args.steps):
+        ta = time.perf_counter()
         rec = runner.prepare(keep=True)
+        tb = time.perf_counter()
         evs[s][0].record(stream)
         runner.launch()
         evs[s][1].record(stream)
+        host[s] = (tb - ta, time.perf_counter() - tb)
         records.append(rec)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
@@ -456,6 +460,12 @@ def decode_line(args, metric, B, L, ctx_before, group, prefix, long_items, share
     print(f"[bench] {ms_per_step:.4f} ms/step (events: median {warm['median_ms']:.4f}, min {warm['min_ms']:.4f}, "
           f"max {warm['max_ms']:.4f}), unique {uniq_bytes_step / 1e9:.3f} GB/step -> {value:.1f} GB/s, logical "
           f"{logical_gbps:.1f} GB/s, COW blocks in timed steps {cow_blocks}", file=sys.stderr, flush=True)
+    host_us = {"prepare_median": round(float(np.median(host[:, 0])) * 1e6, 1),
+               "launch_median": round(float(np.median(host[:, 1])) * 1e6, 1),
+               "first_step": round(float(host[0].sum()) * 1e6, 1)}
+    print(f"[bench] host per step: prepare {host_us['prepare_median']} us, launch {host_us['launch_median']} us "
+          f"(medians; the first step's {host_us['first_step']} us run before any device work)", file=sys.stderr,
+          flush=True)
     # cold: each step alone after a 512 MB write, when the step's bytes could sit in the
     # on-die caches
     cold = None
@@ -524,6 +534,7 @@ def decode_line(args, metric, B, L, ctx_before, group, prefix, long_items, share
         "unique_GB_per_step": round(uniq_bytes_step / 1e9, 4),
         "logical_GB_per_step": round(logical_bytes_step / 1e9, 4),
         "step_time_warm": warm,
+        "host_us": host_us,
         "step_time_cold": cold,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4),

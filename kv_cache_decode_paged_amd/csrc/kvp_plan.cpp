@@ -80,6 +80,28 @@ int split_start(int nb, int n, int k, int slack = 0)
     return std::min(nb, 4 * part_tile_begin((nb + 3) / 4, n, k, slack));
 }
 
+// v in stable order of cost, highest first (cost: an item's tiles plus 2, at most
+// LONG_BPI + 2, so a counting sort; equal costs keep their order, as a stable sort would)
+void sort_by_cost_desc(std::vector<long long> &v, const std::vector<long long> &cost, std::vector<long long> &tmp)
+{
+    long long maxc = 0;
+    for (long long i : v)
+        maxc = std::max(maxc, cost[i]);
+    if (maxc > 4 * LONG_BPI) {
+        std::stable_sort(v.begin(), v.end(), [&](long long x, long long y) { return cost[x] > cost[y]; });
+        return;
+    }
+    std::vector<size_t> start((size_t)maxc + 2, 0);
+    for (long long i : v)
+        ++start[(size_t)(maxc - cost[i]) + 1];
+    for (size_t k = 1; k < start.size(); ++k)
+        start[k] += start[k - 1];
+    tmp.resize(v.size());
+    for (long long i : v)
+        tmp[start[(size_t)(maxc - cost[i])]++] = i;
+    v.swap(tmp);
+}
+
 struct SubRun {
     int a, n, shared_tokens, run;
 };
@@ -259,7 +281,7 @@ kvp_status decode_plan_build(const kvp_dims *dims, const int32_t *table, int32_t
         return fail(KVP_ERR_UNSUPPORTED, "%s: plan too large", who);
 
     // ---- records (built in plan order, placed into XCD queues below) ----
-    std::vector<int32_t> recs((size_t)n_items * REC, -1);
+    std::vector<int32_t> recs((size_t)n_items * REC); // every field of a record is written
     std::vector<int32_t> long_ids; // id area
     std::vector<long long> cost(n_items);
     long long idx = 0, blocks_read = 0;
@@ -286,8 +308,11 @@ kvp_status decode_plan_build(const kvp_dims *dims, const int32_t *table, int32_t
             for (int j = 0; j < nblk; ++j)
                 long_ids.push_back(ent(src_req, blk0 + j));
         } else {
-            for (int j = 0; j < BPI; ++j)
-                r[R_ENT + j] = j < nblk ? ent(src_req, blk0 + j) : -1;
+            const int32_t *row = table + (size_t)src_req * max_blocks + blk0;
+            for (int j = 0; j < nblk; ++j)
+                r[R_ENT + j] = (uint32_t)row[j] < (uint32_t)num_blocks ? row[j] : -1;
+            for (int j = std::max(nblk, 0); j < BPI; ++j)
+                r[R_ENT + j] = -1;
         }
         blocks_read += nblk;
         cost[idx] = nblk + 2; // a tile stream plus the fixed start / finish of a wave
@@ -333,55 +358,85 @@ kvp_status decode_plan_build(const kvp_dims *dims, const int32_t *table, int32_t
         }
     }
 
+    if (idx != n_items)
+        return fail(KVP_ERR_INVALID, "%s: internal error (%lld records for %lld items)", who, idx, n_items);
+
     // ---- XCD queues: item p of the image runs on XCD p % XCDS.  Bundles first, then private
     // items longest first, each to the least-loaded queue that stays within the length cap;
     // shorter queues are padded with empty items ----
     const long long cap = (n_items + XCDS - 1) / XCDS + MAX_BUNDLE;
     std::vector<std::vector<long long>> q(XCDS);
-    std::vector<long long> load(XCDS, 0);
-    auto place = [&](const std::vector<long long> &its) {
+    for (auto &v : q)
+        v.reserve((size_t)cap);
+    long long load[XCDS] = {};
+    // bundles: the least-loaded XCD (lowest index among equals) with room for the bundle
+    for (const auto &bd : bundles) {
         long long c = 0;
-        for (long long i : its)
+        for (long long i : bd)
             c += cost[i];
         int best = -1;
         for (int x = 0; x < XCDS; ++x)
-            if ((long long)(q[x].size() + its.size()) <= cap && (best < 0 || load[x] < load[best]))
+            if ((long long)(q[x].size() + bd.size()) <= cap && (best < 0 || load[x] < load[best]))
                 best = x;
-        for (long long i : its)
+        for (long long i : bd)
             q[best].push_back(i);
         load[best] += c;
-    };
-    for (const auto &bd : bundles)
-        place(bd);
+    }
+    // single items, longest first, the same rule: a min-heap of (load, XCD) over the XCDs
+    // with room (popping the least load, the lowest index among equal loads)
     std::vector<long long> priv(n_items - first_private);
     for (size_t i = 0; i < priv.size(); ++i)
         priv[i] = first_private + (long long)i;
-    std::stable_sort(priv.begin(), priv.end(), [&](long long x, long long y) { return cost[x] > cost[y]; });
-    for (long long i : priv)
-        place({i});
+    std::vector<long long> tmp;
+    sort_by_cost_desc(priv, cost, tmp);
+    typedef std::pair<long long, int> LoadIdx;
+    const auto after = [](const LoadIdx &a, const LoadIdx &b) { return a > b; }; // min-heap order
+    LoadIdx heap[XCDS > CU_SLOTS ? XCDS : CU_SLOTS];
+    int nh = 0;
+    for (int x = 0; x < XCDS; ++x)
+        if ((long long)q[x].size() < cap)
+            heap[nh++] = {load[x], x};
+    std::make_heap(heap, heap + nh, after);
+    for (long long i : priv) {
+        if (nh == 0) // cannot happen: the queues hold n_items + XCDS MAX_BUNDLE items
+            return fail(KVP_ERR_INVALID, "%s: internal error (XCD queues full)", who);
+        std::pop_heap(heap, heap + nh, after);
+        const int x = heap[nh - 1].second;
+        q[x].push_back(i);
+        load[x] += cost[i];
+        if ((long long)q[x].size() < cap) {
+            heap[nh - 1] = {load[x], x};
+            std::push_heap(heap, heap + nh, after);
+        } else {
+            --nh;
+        }
+    }
     // within each XCD: items to CU slots, longest first to the least-loaded slot that has
-    // fewer than K items (K = the XCD's items over its slots, rounded up); the k-th item of
-    // slot s takes queue position CU_SLOTS k + s
+    // fewer than K items (K = the XCD's items over its slots, rounded up; lowest slot among
+    // equal loads); the k-th item of slot s takes queue position CU_SLOTS k + s
     std::vector<std::vector<long long>> qpos(XCDS);
     size_t qlen = 0;
     for (int x = 0; x < XCDS; ++x) {
-        std::vector<long long> its = q[x];
-        std::stable_sort(its.begin(), its.end(), [&](long long a, long long b) { return cost[a] > cost[b]; });
+        std::vector<long long> &its = q[x];
+        sort_by_cost_desc(its, cost, tmp);
         const size_t K = (its.size() + CU_SLOTS - 1) / CU_SLOTS;
-        std::vector<std::vector<long long>> slot(CU_SLOTS);
-        std::vector<long long> sload(CU_SLOTS, 0);
-        for (long long i : its) {
-            int best = -1;
-            for (int c = 0; c < CU_SLOTS; ++c)
-                if (slot[c].size() < K && (best < 0 || sload[c] < sload[best]))
-                    best = c;
-            slot[best].push_back(i);
-            sload[best] += cost[i];
-        }
         qpos[x].assign(K * CU_SLOTS, -1);
+        int cnt[CU_SLOTS] = {};
+        nh = 0;
         for (int c = 0; c < CU_SLOTS; ++c)
-            for (size_t k = 0; k < slot[c].size(); ++k)
-                qpos[x][k * CU_SLOTS + c] = slot[c][k];
+            heap[nh++] = {0, c};
+        // all loads are 0: already a heap in (load, slot) order
+        for (long long i : its) {
+            std::pop_heap(heap, heap + nh, after);
+            const int c = heap[nh - 1].second;
+            qpos[x][(size_t)cnt[c] * CU_SLOTS + c] = i;
+            if ((size_t)++cnt[c] < K) {
+                heap[nh - 1] = {heap[nh - 1].first + cost[i], c};
+                std::push_heap(heap, heap + nh, after);
+            } else {
+                --nh;
+            }
+        }
         qlen = std::max(qlen, qpos[x].size());
     }
     if (pad_items > 0) {
@@ -401,7 +456,7 @@ kvp_status decode_plan_build(const kvp_dims *dims, const int32_t *table, int32_t
     if (image_bytes < bytes)
         return fail(KVP_ERR_INVALID, "%s: image buffer %zu bytes < %zu needed", who, image_bytes, bytes);
     int32_t *img = (int32_t *)h_image;
-    std::memset(h_image, 0, bytes);
+    std::memset((char *)h_image + off_pb, 0, bytes - off_pb); // records are written whole below
     for (size_t qi = 0; qi < qlen; ++qi)
         for (int x = 0; x < XCDS; ++x) {
             int32_t *dst = img + ((size_t)qi * XCDS + x) * REC;

@@ -24,6 +24,7 @@ code, the copies and attention its HIP kernels.  q, k_new, v_new and out are the
 caller's device tensors [layers, B, ...]; their contents may change between steps (the
 graphs read them in place).
 """
+import numpy as np
 import torch
 
 from . import (BLOCK, BlockPool, PagedKVCache, decode_plan_build, decode_plan_bytes, decode_plan_workspace_bytes,
@@ -83,6 +84,7 @@ class DecodeStepRunner:
         self.spare, self.grow = int(spare_items), int(grow_tokens)
         self.ids = torch.tensor([int(s) for s in seqs], dtype=torch.int32)
         self.cows = (kvp_copy * B)()
+        self.cows_np = np.frombuffer(self.cows, dtype=np.int32).reshape(B, 2)  # (src, dst) per request
         dev = q.device
         self.dev = dev
         self.stream = torch.cuda.current_stream(dev)
@@ -115,6 +117,8 @@ class DecodeStepRunner:
                           pairs=torch.empty((self.B, 2), dtype=torch.int32).pin_memory(),
                           image=torch.empty((img_bytes,), dtype=torch.uint8).pin_memory(),
                           plan=kvp_decode_plan()) for _ in range(2)]
+        for h in self.host:
+            h["pairs_np"] = h["pairs"].numpy()  # the same pinned memory
         self.plan_d = [torch.empty((img_bytes,), dtype=torch.uint8, device=self.dev) for _ in range(2)]
         self.uploaded = [torch.cuda.Event(), torch.cuda.Event()]
         self.released = [torch.cuda.Event(), torch.cuda.Event()]
@@ -170,12 +174,11 @@ class DecodeStepRunner:
         h = self.host[k % 2]
         self.done[k % 2].synchronize()  # the copies that last read these pinned buffers are done
         self.pool.append_slots_raw(self.ids.data_ptr(), B, h["slots"].data_ptr(), self.cows)
-        npairs = 0
-        for i in range(B):
-            if self.cows[i].src >= 0:
-                h["pairs"][npairs, 0] = self.cows[i].src
-                h["pairs"][npairs, 1] = self.cows[i].dst
-                npairs += 1
+        # the copy-on-write pairs of the requests that made one, in request order
+        sel = np.flatnonzero(self.cows_np[:, 0] >= 0)
+        npairs = int(sel.size)
+        if npairs:
+            h["pairs_np"][:npairs] = self.cows_np[sel]
         self.pool.export_raw(self.ids.data_ptr(), B, self.max_blocks, h["table"].data_ptr(), h["ctx"].data_ptr())
         lay = self.layout
         plan, _ = decode_plan_build(self.hq, self.hkv, h["table"], h["ctx"], self.cache.num_blocks,
