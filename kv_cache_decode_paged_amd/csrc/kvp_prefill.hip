@@ -13,11 +13,11 @@
 //
 // fp16: one workgroup = 4 wave64 = 64 NQB query rows of one (segment, query head).  Wave w
 // owns NQB blocks of 16 rows, rows q0 + 64 nb + 16 w, so the four waves reach the causal
-// diagonal together and share every K/V tile.  K and V tiles of KT keys stream HBM -> LDS
-// through global_load_lds into a ring of 4 slots, two tiles ahead of the one computed (paged
-// keys: 3 slots, one ahead, since their staged block ids take LDS too; one barrier per
-// tile); each wave reads a tile's K rows and its transposed V once and uses them for all of
-// its blocks.  Head dim
+// diagonal together and share every K/V tile.  K and V stream HBM -> LDS through
+// global_load_lds in ring tiles of two compute tiles of KT keys, 2 slots, the next ring tile
+// in flight while one is computed (paged keys: ring tiles of one compute tile in 3 slots,
+// since their staged block ids take LDS too); one barrier per ring tile.  Each wave reads a
+// compute tile's K rows and its transposed V once and uses them for all of its blocks.  Head dim
 // 64: NQB = 4, KT = 64; head dim 128: NQB = 2, KT = 32 (the operands of twice the width in
 // the same register budget, and the same 8 KB K or V tile):
 //   scores  S^T = K Q^T       v_mfma_f32_16x16x32_f16, one query row per MFMA column
@@ -94,22 +94,26 @@ template <bool PAGED, int D>
 __global__ __launch_bounds__(256) void prefill_mfma_f16_kernel(PrefillArgs P)
 {
     using namespace pf;
-    constexpr int NB = PAGED ? 3 : 4; // ring slots (paged: the block ids take LDS too)
     using T_ = Tiles<D>;
     constexpr int NQB = T_::NQB, QB = T_::QB, KT = T_::KT, RB = T_::RB, SLOT = T_::SLOT;
-    constexpr int LPW = T_::LPW, NDMA = T_::NDMA;
+    // ring: packed keys stream ring tiles of two compute tiles through 2 slots, paged keys
+    // single compute tiles through 3 (their staged block ids take LDS too)
+    constexpr int SUB = PAGED ? 1 : 2;  // compute tiles per ring tile
+    constexpr int NB = PAGED ? 3 : 2;   // ring slots
+    constexpr int RT = SUB * KT, RSLOT = SUB * SLOT; // keys and bytes (K or V) of a ring tile
+    constexpr int LPW = SUB * T_::LPW, NDMA = 2 * LPW; // 1 KB loads per wave per ring tile (K or V); both
     constexpr int CPR = D / 8;    // 16-byte chunks per row
     constexpr int RPI = 1024 / RB; // rows per 1 KB load
     constexpr int KB = KT / 16;   // 16-key blocks per tile
     constexpr int KS = KT / 32;   // 32-key steps per tile (value product)
     constexpr int KD = D / 32;    // 32-dim steps (score product)
     constexpr int NDB = D / 16;   // 16-dim blocks of the output
-    // one barrier per tile: the DMA of tile t + NB - 1 refills the slot of tile t - 1, so
-    // three slots are the minimum; four keep two tiles in flight (two workgroups of 64 KB fit
-    // a CU's LDS, which the paged kernel's staged block ids would overflow)
-    static_assert(NB >= 3 && NB <= 4, "ring of three or four slots");
-    __shared__ __attribute__((aligned(16))) char kring[NB * SLOT];
-    __shared__ __attribute__((aligned(16))) char vring[NB * SLOT];
+    // one barrier per ring tile: the DMA of ring tile t + NB - 1 refills the slot of ring tile
+    // t - 1, which every wave has finished at the barrier; either ring takes 64 KB of K and V
+    // (two workgroups per CU), the paged one 16 KB of block ids besides
+    static_assert(NB >= 2 && NB <= 4 && (SUB == 1 || SUB == 2), "ring shape");
+    __shared__ __attribute__((aligned(16))) char kring[NB * RSLOT];
+    __shared__ __attribute__((aligned(16))) char vring[NB * RSLOT];
     __shared__ int ids[PAGED ? MAX_IDS : 1];
     __shared__ int ids_bad;
 
@@ -154,7 +158,7 @@ __global__ __launch_bounds__(256) void prefill_mfma_f16_kernel(PrefillArgs P)
         lim[nb] = causal ? max(0, min(off + row + 1, nk)) : nk; // keys >= lim are masked for this row
     }
     const int kend = causal ? max(0, min(nk, off + q0 + QB)) : nk; // keys any row of the workgroup sees
-    const int nt = (kend + KT - 1) / KT;
+    const int nt = (kend + RT - 1) / RT;
     // paged: the request's block ids for keys < kend, an unusable entry (-1) masks its keys
     bool all_ok = true;
     if constexpr (PAGED) {
@@ -190,11 +194,11 @@ __global__ __launch_bounds__(256) void prefill_mfma_f16_kernel(PrefillArgs P)
         lane_off[ii] = (r * hkv + g_kv) * D + swz<D>(lane & (CPR - 1), r) * 8;
     }
     auto issue = [&](int t) {
-        char *kd = kring + (t % NB) * SLOT;
-        char *vd = vring + (t % NB) * SLOT;
-        if (!PAGED && (t + 1) * KT <= kend) {
+        char *kd = kring + (t % NB) * RSLOT;
+        char *vd = vring + (t % NB) * RSLOT;
+        if (!PAGED && (t + 1) * RT <= kend) {
             // every row of the tile is a key the workgroup sees: no clamp, no block ids
-            const size_t tb = (size_t)(a + t * KT) * hkv * D;
+            const size_t tb = (size_t)(a + t * RT) * hkv * D;
             const f16 *kt = P.k + tb, *vt = P.v + tb;
 #pragma unroll
             for (int ii = 0; ii < LPW; ++ii) {
@@ -213,7 +217,7 @@ __global__ __launch_bounds__(256) void prefill_mfma_f16_kernel(PrefillArgs P)
 #pragma unroll
         for (int ii = 0; ii < LPW; ++ii) {
             const int r = RPI * (LPW * wave + ii) + lane / CPR;
-            kk[ii] = min(t * KT + r, kend - 1); // beyond kend every row of the workgroup masks the key
+            kk[ii] = min(t * RT + r, kend - 1); // beyond kend every row of the workgroup masks the key
             e[ii] = 0;
             ea[ii] = 0;
             if constexpr (PAGED)
@@ -278,9 +282,9 @@ __global__ __launch_bounds__(256) void prefill_mfma_f16_kernel(PrefillArgs P)
     for (int k = 0; k < NB - 1 && k < nt; ++k)
         issue(k);
     for (int t = 0; t < nt; ++t) {
-        // this wave's loads of tile t have landed; after the barrier every wave's have, and
-        // every wave has finished reading tile t - 1, whose slot the next DMA refills
-        const int ahead = min(nt - 1 - t, NB - 2); // tiles issued after tile t
+        // this wave's loads of ring tile t have landed; after the barrier every wave's have,
+        // and every wave has finished reading ring tile t - 1, whose slot the next DMA refills
+        const int ahead = min(nt - 1 - t, NB - 2); // ring tiles issued after ring tile t
         if (ahead >= 2)
             wait_vm<2 * NDMA>();
         else if (ahead == 1)
@@ -290,111 +294,114 @@ __global__ __launch_bounds__(256) void prefill_mfma_f16_kernel(PrefillArgs P)
         block_barrier();
         if (t + NB - 1 < nt)
             issue(t + NB - 1);
-        const int k0 = t * KT;
-        bool any = false;
+#pragma unroll 1
+        for (int sub = 0; sub < SUB; ++sub) {
+            const int k0 = t * RT + sub * KT;
+            bool any = false;
 #pragma unroll
-        for (int nb = 0; nb < NQB; ++nb)
-            any = any || (r0[nb] < n && (!causal || k0 <= off + r0[nb] + 15));
-        if (!any)
-            continue;
-        const unsigned soff = (unsigned)((t % NB) * SLOT);
-        unsigned kb_t[KD], vb_t[NDB]; // the operand bases in this tile's ring slot
+            for (int nb = 0; nb < NQB; ++nb)
+                any = any || (r0[nb] < n && (!causal || k0 <= off + r0[nb] + 15));
+            if (!any)
+                continue;
+            const unsigned soff = (unsigned)((t % NB) * RSLOT + sub * SLOT);
+            unsigned kb_t[KD], vb_t[NDB]; // the operand bases in this tile's ring slot
 #pragma unroll
-        for (int ks = 0; ks < KD; ++ks)
-            kb_t[ks] = kbase[ks] + soff;
-#pragma unroll
-        for (int db = 0; db < NDB; ++db)
-            vb_t[db] = vbase[db] + soff;
-        // K rows (A of the score MFMA): key 16 kb + col, dims 32 ks + 8 grp .. (chunk 4 ks + grp)
-        f16x8 kop[KB][KD];
-        lds_read_k<KB, KD, 0, 16 * RB>(kop, kb_t);
-        // V^T (A of the value MFMA), k-step ks, dims 16 db ..: lane L of group grp addresses
-        // key row 16 (2 ks + h) + 4 grp + L / 4, dims 16 db + 4 (L % 4); the transposing
-        // read hands lane i element j = half i % 4 of lane 4 j + i / 4's 8 bytes
-        f16x4 vraw[KS][NDB][2];
-        lds_read_vt<KS, NDB, 0, 16 * RB>(vraw, vb_t);
-        f16x8 vop[KS][NDB];
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
+            for (int ks = 0; ks < KD; ++ks)
+                kb_t[ks] = kbase[ks] + soff;
 #pragma unroll
             for (int db = 0; db < NDB; ++db)
-                vop[ks][db] = __builtin_shufflevector(vraw[ks][db][0], vraw[ks][db][1], 0, 1, 2, 3, 4, 5, 6, 7);
-
-#pragma unroll
-        for (int nb = 0; nb < NQB; ++nb) {
-            if (!(r0[nb] < n && (!causal || k0 <= off + r0[nb] + 15)))
-                continue; // wave-uniform: no key of this tile is visible to the block
-            // scores: sacc[kb][i] = S[key k0 + 16 kb + 4 grp + i][row r0 + col] (unscaled)
-            f32x4 sacc[KB];
-#pragma unroll
-            for (int kb = 0; kb < KB; ++kb) {
-                f32x4 s = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop[kb][0], qop[nb][0], f32x4{0.f, 0.f, 0.f, 0.f},
-                                                                 0, 0, 0);
-#pragma unroll
-                for (int ks = 1; ks < KD; ++ks)
-                    s = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop[kb][ks], qop[nb][ks], s, 0, 0, 0);
-                sacc[kb] = s;
-            }
-            const bool full = all_ok && (!causal || k0 + KT - 1 <= off + r0[nb]) && k0 + KT <= nk;
-            if (!full) {
-                bool bok[KB];
-#pragma unroll
-                for (int kb = 0; kb < KB; ++kb)
-                    bok[kb] = true;
-                if constexpr (PAGED) {
-                    if (!all_ok) { // keys of unusable blocks are masked
-                        int e4[KB];
-                        unsigned a4[KB];
-#pragma unroll
-                        for (int kb = 0; kb < KB; ++kb)
-                            a4[kb] = lds_addr((const char *)&ids[min((k0 >> 4) + kb, MAX_IDS - 1)]);
-                        lds_read_b32<KB>(e4, a4);
-#pragma unroll
-                        for (int kb = 0; kb < KB; ++kb)
-                            bok[kb] = e4[kb] >= 0;
-                    }
-                }
-#pragma unroll
-                for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        sacc[kb][i] = (bok[kb] && k0 + 16 * kb + 4 * grp + i < lim[nb]) ? sacc[kb][i] : -INFINITY;
-            }
-            // a row's reference max moves only when the row's own maximum passes it by more
-            // than 2^8; between moves p = 2^(s c - mref) < 256 and nothing needs rescaling.
-            // Rows that do not move scale by exactly 1, so no row depends on another's keys.
-            // The lane's own maximum is first held against thr; only when some lane passes it
-            // does the wave reduce the rows' maxima across lanes and apply the exact test.
-            const float lmax = max_scores<KB>(sacc);
-            if (__ballot(lmax > thr[nb]) != 0) {
-                const float mt = group_max(lmax) * c;
-                const bool need = mt > mref[nb] + RESCALE_LOG2;
-                if (__ballot(need) != 0) {
-                    const float mn = need ? mt : mref[nb];
-                    const float alpha = need ? (mref[nb] == -INFINITY ? 0.f : pf_exp2(mref[nb] - mn)) : 1.f;
-#pragma unroll
-                    for (int db = 0; db < NDB; ++db)
-                        acc[nb][db] *= alpha;
-                    accl[nb] *= alpha;
-                    mref[nb] = mn;
-                    thr[nb] = rescale_threshold(mref[nb], c, inv_c);
-                }
-            }
-            const float mc = mref[nb] == -INFINITY ? 0.f : mref[nb];
-            // P^T operand of k-step ks, slot s: key 16 (2 ks + s / 4) + 4 grp + s % 4 =
-            // sacc[2 ks + s / 4][s % 4], rounded once to fp16
-            f16x8 pop[KS];
+                vb_t[db] = vbase[db] + soff;
+            // K rows (A of the score MFMA): key 16 kb + col, dims 32 ks + 8 grp .. (chunk 4 ks + grp)
+            f16x8 kop[KB][KD];
+            lds_read_k<KB, KD, 0, 16 * RB>(kop, kb_t);
+            // V^T (A of the value MFMA), k-step ks, dims 16 db ..: lane L of group grp addresses
+            // key row 16 (2 ks + h) + 4 grp + L / 4, dims 16 db + 4 (L % 4); the transposing
+            // read hands lane i element j = half i % 4 of lane 4 j + i / 4's 8 bytes
+            f16x4 vraw[KS][NDB][2];
+            lds_read_vt<KS, NDB, 0, 16 * RB>(vraw, vb_t);
+            f16x8 vop[KS][NDB];
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-                for (int s = 0; s < 8; ++s)
-                    pop[ks][s] = (f16)pf_exp2(fmaf(sacc[2 * ks + (s >> 2)][s & 3], c, -mc));
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-#pragma unroll
                 for (int db = 0; db < NDB; ++db)
-                    acc[nb][db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vop[ks][db], pop[ks], acc[nb][db], 0, 0, 0);
-                accl[nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, pop[ks], accl[nb], 0, 0, 0);
+                    vop[ks][db] = __builtin_shufflevector(vraw[ks][db][0], vraw[ks][db][1], 0, 1, 2, 3, 4, 5, 6, 7);
+
+#pragma unroll
+            for (int nb = 0; nb < NQB; ++nb) {
+                if (!(r0[nb] < n && (!causal || k0 <= off + r0[nb] + 15)))
+                    continue; // wave-uniform: no key of this tile is visible to the block
+                // scores: sacc[kb][i] = S[key k0 + 16 kb + 4 grp + i][row r0 + col] (unscaled)
+                f32x4 sacc[KB];
+#pragma unroll
+                for (int kb = 0; kb < KB; ++kb) {
+                    f32x4 s = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop[kb][0], qop[nb][0], f32x4{0.f, 0.f, 0.f, 0.f},
+                                                                     0, 0, 0);
+#pragma unroll
+                    for (int ks = 1; ks < KD; ++ks)
+                        s = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop[kb][ks], qop[nb][ks], s, 0, 0, 0);
+                    sacc[kb] = s;
+                }
+                const bool full = all_ok && (!causal || k0 + KT - 1 <= off + r0[nb]) && k0 + KT <= nk;
+                if (!full) {
+                    bool bok[KB];
+#pragma unroll
+                    for (int kb = 0; kb < KB; ++kb)
+                        bok[kb] = true;
+                    if constexpr (PAGED) {
+                        if (!all_ok) { // keys of unusable blocks are masked
+                            int e4[KB];
+                            unsigned a4[KB];
+#pragma unroll
+                            for (int kb = 0; kb < KB; ++kb)
+                                a4[kb] = lds_addr((const char *)&ids[min((k0 >> 4) + kb, MAX_IDS - 1)]);
+                            lds_read_b32<KB>(e4, a4);
+#pragma unroll
+                            for (int kb = 0; kb < KB; ++kb)
+                                bok[kb] = e4[kb] >= 0;
+                        }
+                    }
+#pragma unroll
+                    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+                            sacc[kb][i] = (bok[kb] && k0 + 16 * kb + 4 * grp + i < lim[nb]) ? sacc[kb][i] : -INFINITY;
+                }
+                // a row's reference max moves only when the row's own maximum passes it by more
+                // than 2^8; between moves p = 2^(s c - mref) < 256 and nothing needs rescaling.
+                // Rows that do not move scale by exactly 1, so no row depends on another's keys.
+                // The lane's own maximum is first held against thr; only when some lane passes it
+                // does the wave reduce the rows' maxima across lanes and apply the exact test.
+                const float lmax = max_scores<KB>(sacc);
+                if (__ballot(lmax > thr[nb]) != 0) {
+                    const float mt = group_max(lmax) * c;
+                    const bool need = mt > mref[nb] + RESCALE_LOG2;
+                    if (__ballot(need) != 0) {
+                        const float mn = need ? mt : mref[nb];
+                        const float alpha = need ? (mref[nb] == -INFINITY ? 0.f : pf_exp2(mref[nb] - mn)) : 1.f;
+#pragma unroll
+                        for (int db = 0; db < NDB; ++db)
+                            acc[nb][db] *= alpha;
+                        accl[nb] *= alpha;
+                        mref[nb] = mn;
+                        thr[nb] = rescale_threshold(mref[nb], c, inv_c);
+                    }
+                }
+                const float mc = mref[nb] == -INFINITY ? 0.f : mref[nb];
+                // P^T operand of k-step ks, slot s: key 16 (2 ks + s / 4) + 4 grp + s % 4 =
+                // sacc[2 ks + s / 4][s % 4], rounded once to fp16
+                f16x8 pop[KS];
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+                    for (int s = 0; s < 8; ++s)
+                        pop[ks][s] = (f16)pf_exp2(fmaf(sacc[2 * ks + (s >> 2)][s & 3], c, -mc));
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+                    for (int db = 0; db < NDB; ++db)
+                        acc[nb][db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vop[ks][db], pop[ks], acc[nb][db], 0, 0, 0);
+                    accl[nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, pop[ks], accl[nb], 0, 0, 0);
+                }
             }
         }
     }
