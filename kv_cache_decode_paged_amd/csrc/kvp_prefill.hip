@@ -15,9 +15,10 @@
 // owns NQB blocks of 16 rows, rows q0 + 64 nb + 16 w, so the four waves reach the causal
 // diagonal together and share every K/V tile.  K and V stream HBM -> LDS through
 // global_load_lds in ring tiles of two compute tiles of KT keys, 2 slots, the next ring tile
-// in flight while one is computed (paged keys: ring tiles of one compute tile in 3 slots,
-// since their staged block ids take LDS too); one barrier per ring tile.  Each wave reads a
-// compute tile's K rows and its transposed V once and uses them for all of its blocks.  Head dim
+// in flight while one is computed (paged keys whose block table is too wide for its staged
+// ids to fit beside that ring: ring tiles of one compute tile in 3 slots); one barrier per
+// ring tile.  Each wave reads a compute tile's K rows and its transposed V once and uses
+// them for all of its blocks.  Head dim
 // 64: NQB = 4, KT = 64; head dim 128: NQB = 2, KT = 32 (the operands of twice the width in
 // the same register budget, and the same 8 KB K or V tile):
 //   scores  S^T = K Q^T       v_mfma_f32_16x16x32_f16, one query row per MFMA column
@@ -88,18 +89,23 @@ struct PrefillArgs {
 
 // block ids of one request staged in LDS (paged): contexts of up to MAX_IDS blocks
 constexpr int MAX_IDS = 4096;
+// LDS of one workgroup when two share a CU (160 KB): the paged kernel takes the wide ring
+// (64 KB) when the staged ids of the table's width fit beside it
+constexpr int LDS_TWO_PER_CU = 80 * 1024;
+constexpr int WIDE_RING_LDS = 64 * 1024 + 16; // both rings + the bad-id flag
 
-// grid = (Hq, nseg, ceil(max query rows / QB)), block = 256
-template <bool PAGED, int D>
+// grid = (Hq, nseg, ceil(max query rows / QB)), block = 256; paged: dynamic LDS of
+// max_blocks ints for the staged block ids
+template <bool PAGED, int D, int SUB>
 __global__ __launch_bounds__(256) void prefill_mfma_f16_kernel(PrefillArgs P)
 {
     using namespace pf;
     using T_ = Tiles<D>;
     constexpr int NQB = T_::NQB, QB = T_::QB, KT = T_::KT, RB = T_::RB, SLOT = T_::SLOT;
-    // ring: packed keys stream ring tiles of two compute tiles through 2 slots, paged keys
-    // single compute tiles through 3 (their staged block ids take LDS too)
-    constexpr int SUB = PAGED ? 1 : 2;  // compute tiles per ring tile
-    constexpr int NB = PAGED ? 3 : 2;   // ring slots
+    // ring: ring tiles of SUB compute tiles; two compute tiles through 2 slots (64 KB of K
+    // and V), or, where a paged table's staged block ids leave no room for that beside a
+    // second workgroup, single compute tiles through 3 slots (48 KB)
+    constexpr int NB = SUB == 2 ? 2 : 3; // ring slots
     constexpr int RT = SUB * KT, RSLOT = SUB * SLOT; // keys and bytes (K or V) of a ring tile
     constexpr int LPW = SUB * T_::LPW, NDMA = 2 * LPW; // 1 KB loads per wave per ring tile (K or V); both
     constexpr int CPR = D / 8;    // 16-byte chunks per row
@@ -111,10 +117,10 @@ __global__ __launch_bounds__(256) void prefill_mfma_f16_kernel(PrefillArgs P)
     // one barrier per ring tile: the DMA of ring tile t + NB - 1 refills the slot of ring tile
     // t - 1, which every wave has finished at the barrier; either ring takes 64 KB of K and V
     // (two workgroups per CU), the paged one 16 KB of block ids besides
-    static_assert(NB >= 2 && NB <= 4 && (SUB == 1 || SUB == 2), "ring shape");
+    static_assert((SUB == 1 || SUB == 2) && (PAGED || SUB == 2), "ring shape");
     __shared__ __attribute__((aligned(16))) char kring[NB * RSLOT];
     __shared__ __attribute__((aligned(16))) char vring[NB * RSLOT];
-    __shared__ int ids[PAGED ? MAX_IDS : 1];
+    extern __shared__ int ids[]; // paged: [max_blocks] staged block ids (dynamic LDS)
     __shared__ int ids_bad;
 
     // the query tile is the slowest grid dimension: workgroups are dispatched x fastest, so
@@ -353,7 +359,7 @@ __global__ __launch_bounds__(256) void prefill_mfma_f16_kernel(PrefillArgs P)
                             unsigned a4[KB];
 #pragma unroll
                             for (int kb = 0; kb < KB; ++kb)
-                                a4[kb] = lds_addr((const char *)&ids[min((k0 >> 4) + kb, MAX_IDS - 1)]);
+                                a4[kb] = lds_addr((const char *)&ids[min((k0 >> 4) + kb, max(P.max_blocks - 1, 0))]);
                             lds_read_b32<KB>(e4, a4);
 #pragma unroll
                             for (int kb = 0; kb < KB; ++kb)
@@ -518,9 +524,9 @@ extern "C" kvp_status varlen_causal_prefill(const kvp_dims *dims, void *out, con
         PrefillArgs A{(const f16 *)q, (const f16 *)k, (const f16 *)v, (f16 *)out, d_cu_seqlens, nullptr, nullptr,
                       0, 0, dims->num_q_heads, dims->num_kv_heads, sl2, causal};
         if (hd == 64)
-            hipLaunchKernelGGL((prefill_mfma_f16_kernel<false, 64>), grid, dim3(256), 0, st, A);
+            hipLaunchKernelGGL((prefill_mfma_f16_kernel<false, 64, 2>), grid, dim3(256), 0, st, A);
         else
-            hipLaunchKernelGGL((prefill_mfma_f16_kernel<false, 128>), grid, dim3(256), 0, st, A);
+            hipLaunchKernelGGL((prefill_mfma_f16_kernel<false, 128, 2>), grid, dim3(256), 0, st, A);
     } else {
         dim3 grid(max_seqlen, dims->num_q_heads, nseg);
         hipLaunchKernelGGL(prefill_valu_f32_kernel, grid, dim3(64), 0, st, (const float *)q,
@@ -576,10 +582,17 @@ extern "C" kvp_status paged_prefill_attention(const kvp_cache_desc *cache, int32
                   d_block_table, max_blocks, cache->num_blocks, d.num_q_heads, d.num_kv_heads,
                   scale * pf::LOG2E, 1};
     dim3 grid(d.num_q_heads, B, (max_q + QB - 1) / QB);
-    if (hd == 64)
-        hipLaunchKernelGGL((prefill_mfma_f16_kernel<true, 64>), grid, dim3(256), 0, (hipStream_t)stream, A);
+    const size_t ids_bytes = 4 * (size_t)std::max(max_blocks, 1);
+    const bool wide = WIDE_RING_LDS + ids_bytes <= (size_t)LDS_TWO_PER_CU;
+    hipStream_t st = (hipStream_t)stream;
+    if (hd == 64 && wide)
+        hipLaunchKernelGGL((prefill_mfma_f16_kernel<true, 64, 2>), grid, dim3(256), ids_bytes, st, A);
+    else if (hd == 64)
+        hipLaunchKernelGGL((prefill_mfma_f16_kernel<true, 64, 1>), grid, dim3(256), ids_bytes, st, A);
+    else if (wide)
+        hipLaunchKernelGGL((prefill_mfma_f16_kernel<true, 128, 2>), grid, dim3(256), ids_bytes, st, A);
     else
-        hipLaunchKernelGGL((prefill_mfma_f16_kernel<true, 128>), grid, dim3(256), 0, (hipStream_t)stream, A);
+        hipLaunchKernelGGL((prefill_mfma_f16_kernel<true, 128, 1>), grid, dim3(256), ids_bytes, st, A);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return fail(KVP_ERR_HIP, "%s: launch failed: %s", who, hipGetErrorString(e));

@@ -95,3 +95,21 @@ def test_empty_calls_are_no_ops():
     kvp.paged_prefill_attention(st.cache, 0, st.q.cuda(), st.table, st.ctxd, st.cu.cuda(), 0, out=out)
     torch.cuda.synchronize()
     assert (out == 7.0).all()
+
+
+@pytest.mark.parametrize("head_dim", [64, 128])
+def test_wide_table_takes_the_narrow_ring_bit_identically(head_dim):
+    # a block table wider than the 2-slot ring leaves room for in LDS (its staged ids beside
+    # 64 KB of K / V ring, two workgroups per CU) runs the 3-slot ring of single compute
+    # tiles: the same compute tiles in the same order, so the outputs are bit-identical
+    need_gpu()
+    prefixes, chunks = [0, 300, 1000, 2047], [64, 257, 5, 300]
+    say("wide block table, head dim", head_dim)
+    st = ChunkStep(kvp, prefixes, chunks, seed=12600 + head_dim, head_dim=head_dim)
+    a = st.run()
+    wide = torch.full((st.B, 4096), -1, dtype=torch.int32, device="cuda")
+    wide[:, :st.max_blocks] = st.table
+    b = kvp.paged_prefill_attention(st.cache, 0, st.q.cuda(), wide, st.ctxd, st.cu.cuda(), max(st.m))
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+    assert max_abs(to64(b), st.oracle()) <= TOL[torch.float16]
