@@ -511,6 +511,7 @@ def decode_line(args, metric, B, L, ctx_before, group, prefix, long_items, share
         check, cpu = decode_check_and_baseline(torch, snap, last, q, knew, vnew, out, check_layers,
                                                 one_thread_layers, L)
         print(f"[bench] check {check}\n[bench] cpu oracle {cpu}", file=sys.stderr, flush=True)
+    part_rec = (HQ // HKV) * (D + 4) * 4  # one partial record: G rows of (o[d], m, l, 2 pad) fp32
     line = {
         "metric": metric,
         "value": round(value, 2),
@@ -547,6 +548,11 @@ def decode_line(args, metric, B, L, ctx_before, group, prefix, long_items, share
                      "bytes_per_launch": int(call_bytes), "avg_launch_us": round(launch_ms * 1e3, 3),
                      "avg_launch_from": f"graph replay of the {L} layers / {L}, median of {reps}"},
         "hbm_read_probe": probe,
+        "split_overhead": {"partials_per_launch": int(last.split_partials),
+                           "record_bytes": part_rec,
+                           "bytes_per_launch": 2 * int(last.split_partials) * part_rec,
+                           "note": "fp32 (m, l, o) partials of split pairs, stored and read back once each; "
+                                   "implementation overhead, not in bytes_per_launch"},
         "plan": {"items": int(last.n_items), "shared_items": int(last.n_shared),
                  "kv_block_reads": int(last.kv_blocks_read), "share_prefix": share, "long_items": long_items,
                  "fill": bool(runner.fill),

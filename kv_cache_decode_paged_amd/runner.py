@@ -44,11 +44,14 @@ SPARE_ITEMS = 8 * 32
 
 class StepRecord:
     """Host copies of what one step ran on: table [B, max_blocks], context lengths [B], the
-    copy-on-write pairs, and plan statistics."""
+    copy-on-write pairs, and plan statistics.  split_partials: partial records a layer's
+    split pairs exchange (all but one part of each split pair stores one, the merging part
+    reads them back)."""
 
-    def __init__(self, table, ctx, cow_pairs, n_items, n_shared, kv_blocks_read):
+    def __init__(self, table, ctx, cow_pairs, n_items, n_shared, kv_blocks_read, split_partials=0):
         self.table, self.ctx, self.cow_pairs = table, ctx, cow_pairs
         self.n_items, self.n_shared, self.kv_blocks_read = n_items, n_shared, kv_blocks_read
+        self.split_partials = split_partials
 
 
 class DecodeStepRunner:
@@ -211,9 +214,11 @@ class DecodeStepRunner:
             raise RuntimeError("DecodeStepRunner: plan image larger than its buffer")
         rec = None
         if keep:
+            npairs_kv = self.B * self.hkv
+            parts = h["image"][plan.off_pair_nparts:plan.off_pair_nparts + 4 * npairs_kv].numpy().view(np.int32)
             rec = StepRecord(h["table"].numpy().copy(), h["ctx"].numpy().copy(),
                              h["pairs"][:npairs].numpy().copy(), int(plan.n_items), int(plan.n_shared),
-                             int(plan.kv_blocks_read))
+                             int(plan.kv_blocks_read), int(np.maximum(parts - 1, 0).sum()))
         self._pending = (h, int(plan.bytes), npairs)
         return rec
 
