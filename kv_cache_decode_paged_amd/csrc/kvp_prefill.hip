@@ -31,6 +31,7 @@
 // fp32: a plain VALU kernel (wave = one query row), exact fp32 throughout.
 #include <hip/hip_runtime.h>
 
+#include <climits>
 #include <cmath>
 
 #include "kvp_gfx950.h"
@@ -164,6 +165,15 @@ __global__ __launch_bounds__(256) void prefill_mfma_f16_kernel(PrefillArgs P)
         lim[nb] = causal ? max(0, min(off + row + 1, nk)) : nk; // keys >= lim are masked for this row
     }
     const int kend = causal ? max(0, min(nk, off + q0 + QB)) : nk; // keys any row of the workgroup sees
+    // first key no row of block nb sees from (-1: the block holds no row; with causal masking
+    // its last row sees up to off + r0 + 15), and the largest over the wave's blocks: a
+    // compute tile starting at key k0 has work for block nb when k0 < kvis[nb]
+    int kvis[NQB], kvis_any = -1;
+#pragma unroll
+    for (int nb = 0; nb < NQB; ++nb) {
+        kvis[nb] = __builtin_amdgcn_readfirstlane(r0[nb] < n ? (causal ? off + r0[nb] + 16 : INT_MAX) : -1);
+        kvis_any = max(kvis_any, kvis[nb]);
+    }
     const int nt = (kend + RT - 1) / RT;
     // paged: the request's block ids for keys < kend, an unusable entry (-1) masks its keys
     bool all_ok = true;
@@ -303,12 +313,8 @@ __global__ __launch_bounds__(256) void prefill_mfma_f16_kernel(PrefillArgs P)
 #pragma unroll 1
         for (int sub = 0; sub < SUB; ++sub) {
             const int k0 = t * RT + sub * KT;
-            bool any = false;
-#pragma unroll
-            for (int nb = 0; nb < NQB; ++nb)
-                any = any || (r0[nb] < n && (!causal || k0 <= off + r0[nb] + 15));
-            if (!any)
-                continue;
+            if (k0 >= kvis_any)
+                continue; // no key of this tile is visible to any of the wave's blocks
             const unsigned soff = (unsigned)((t % NB) * RSLOT + sub * SLOT);
             unsigned kb_t[KD], vb_t[NDB]; // the operand bases in this tile's ring slot
 #pragma unroll
@@ -334,7 +340,7 @@ __global__ __launch_bounds__(256) void prefill_mfma_f16_kernel(PrefillArgs P)
 
 #pragma unroll
             for (int nb = 0; nb < NQB; ++nb) {
-                if (!(r0[nb] < n && (!causal || k0 <= off + r0[nb] + 15)))
+                if (k0 >= kvis[nb])
                     continue; // wave-uniform: no key of this tile is visible to the block
                 // scores: sacc[kb][i] = S[key k0 + 16 kb + 4 grp + i][row r0 + col] (unscaled)
                 f32x4 sacc[KB];
