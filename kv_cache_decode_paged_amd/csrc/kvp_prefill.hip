@@ -261,6 +261,9 @@ __global__ __launch_bounds__(256) void prefill_mfma_f16_kernel(PrefillArgs P)
     // running state per block: reference max (scaled, log2 units), O^T rows 16 db + 4 grp + i
     // of column col, and the row sum (every entry of accl holds it)
     float mref[NQB];
+    // nmc[nb]: the exponent offset -mref (0 while the row has no reference yet, so that
+    // masked scores give exp2(-inf) = 0 rather than NaN), kept beside mref
+    float nmc[NQB];
     // thr[nb]: raw-score level below which no key of a tile can move row block nb's reference
     // (rescale_threshold: a little under (mref + 8) / c, so every tile the exact test would
     // move is seen)
@@ -269,13 +272,15 @@ __global__ __launch_bounds__(256) void prefill_mfma_f16_kernel(PrefillArgs P)
 #pragma unroll
     for (int nb = 0; nb < NQB; ++nb) {
         mref[nb] = -INFINITY;
+        nmc[nb] = -0.f;
         thr[nb] = -INFINITY;
         accl[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int db = 0; db < NDB; ++db)
             acc[nb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
-    const f16x8 ones = {1, 1, 1, 1, 1, 1, 1, 1};
+    f16x8 ones = {1, 1, 1, 1, 1, 1, 1, 1};
+    asm volatile("" : "+v"(ones)); // held in registers, not rebuilt from scalars per block
 
     // LDS byte addresses of this lane's operand reads in ring slot 0.  The swizzle depends
     // on a row only through row % 8, which the 16-row steps leave alone, so K reads of one
@@ -395,10 +400,10 @@ __global__ __launch_bounds__(256) void prefill_mfma_f16_kernel(PrefillArgs P)
                             acc[nb][db] *= alpha;
                         accl[nb] *= alpha;
                         mref[nb] = mn;
+                        nmc[nb] = mn == -INFINITY ? -0.f : -mn;
                         thr[nb] = rescale_threshold(mref[nb], c, inv_c);
                     }
                 }
-                const float mc = mref[nb] == -INFINITY ? 0.f : mref[nb];
                 // P^T operand of k-step ks, slot s: key 16 (2 ks + s / 4) + 4 grp + s % 4 =
                 // sacc[2 ks + s / 4][s % 4], rounded once to fp16
                 f16x8 pop[KS];
@@ -406,7 +411,7 @@ __global__ __launch_bounds__(256) void prefill_mfma_f16_kernel(PrefillArgs P)
                 for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
                     for (int s = 0; s < 8; ++s)
-                        pop[ks][s] = (f16)pf_exp2(fmaf(sacc[2 * ks + (s >> 2)][s & 3], c, -mc));
+                        pop[ks][s] = (f16)pf_exp2(fmaf(sacc[2 * ks + (s >> 2)][s & 3], c, nmc[nb]));
 #pragma unroll
                 for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
