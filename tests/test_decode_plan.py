@@ -126,16 +126,24 @@ def check_plan(plan, image, table, ctx, num_blocks, hq, hkv, shared_expected=Non
     # per CU: position p runs on XCD p % 8 at queue index p // 8, and queue indices 32 apart
     # share a CU; the planner spreads each XCD's work over its 32 CUs longest first, so no
     # CU carries more than its share plus one item
+    # Each CU slot takes its items longest first (the k-th item of slot s sits at queue index
+    # 32 k + s) and at most ceil(items of the XCD / 32) of them.
     for x in range(XCDS):
         loads, costs = np.zeros(32), []
+        per_slot = [[] for _ in range(32)]
         for qi in range(plan.n_items // XCDS):
             r = items[qi * XCDS + x]
             if int(r[0]) != F_EMPTY:
                 cst = int(r[5]) + 2
                 loads[qi % 32] += cst
                 costs.append(cst)
+                per_slot[qi % 32].append(cst)
         if costs:
             assert loads.max() <= loads.sum() / 32 + max(costs), (x, loads.max(), loads.sum() / 32)
+            k_max = -(-len(costs) // 32)
+            for sl in per_slot:
+                assert len(sl) <= k_max, (x, len(sl), k_max)
+                assert all(a >= b for a, b in zip(sl, sl[1:])), (x, sl)
     for key, (xs, n) in bundles.items():
         if n <= 8:  # a run's shared items of one head (at most one bundle) share an XCD
             assert len(xs) == 1, f"shared items of run {key} spread over XCDs {xs}"
