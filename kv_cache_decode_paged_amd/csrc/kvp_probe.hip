@@ -48,8 +48,9 @@ extern "C" kvp_status kvp_read_bandwidth_probe(const void *d_buf, size_t bytes, 
         return fail(KVP_ERR_INVALID, "kvp_read_bandwidth_probe: bad arguments (buf %p, %zu bytes, %d waves)", d_buf,
                     bytes, waves);
     int dev = 0, cus = 256;
-    if (hipGetDevice(&dev) == hipSuccess)
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) !=
+                                                  hipSuccess)
+        cus = 256; // the MI355X's compute units
     const long long w = waves > 0 ? waves : 8LL * cus;
     const long long blocks = (w + 3) / 4; // 4 waves of 64 lanes per workgroup
     hipLaunchKernelGGL(read_probe_kernel, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream,
